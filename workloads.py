@@ -1,0 +1,209 @@
+"""Seeded synthetic inputs for the chunked linear recurrence (no method arithmetic).
+
+This module only draws random tensors. It is the one piece of code that both
+the oracle tests and the GPU path use, so it holds nothing of the recurrence
+itself: no decay, no state, no output. Every tensor is drawn in float32 on the
+CPU from numpy's PCG64 generator and, where the workload is bf16, cast once
+with torch (round to nearest even); both sides then receive exactly the same
+values (the oracle widens them to float64 exactly).
+
+The five named workloads follow the statement of the problem (shapes, value
+distributions, chunk sizes, segment counts); the readings taken where the
+statement is open are listed in the design doc:
+
+1. ``tiny_gdn``       B=1 T=256 H=2 K=V=64, float32, chunk 64.
+2. ``dense_gdn``      B=2 T=4096 H=16 K=V=128, bf16, initial state N(0, 0.02).
+3. ``varlen_gdn``     batch-one packed stream of 32768 tokens, 9 sequences
+                      (one empty, tails), H=32 K=V=128, bf16.
+4. ``long_gdn``       B=1 T=262144 H=16 K=V=128, bf16, 16 segments of 16384.
+5. ``ssd_gla``        scalar-gate linear attention, B=2 T=16384 H=64 HK=8,
+                      K=128 (dstate), V=64 (headdim), chunk 128, 8 segments per row.
+
+Draw order inside one workload: q, k, v, gate noise, beta noise, h0, A, dt,
+sequence lengths.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+SEEDS = {"tiny_gdn": 101, "dense_gdn": 102, "varlen_gdn": 103, "long_gdn": 104, "ssd_gla": 105}
+
+
+@dataclass
+class Workload:
+    name: str
+    kind: str                      # "gdn" or "gla"
+    q: torch.Tensor                # [B, T, HK, K]
+    k: torch.Tensor                # [B, T, HK, K]
+    v: torch.Tensor                # [B, T, H, V]
+    g: torch.Tensor                # [B, T, H] float32, natural-log gate
+    beta: Optional[torch.Tensor]   # [B, T, H] float32 (delta rule only)
+    h0: Optional[torch.Tensor]     # [N, H, V, K] float32 or None
+    cu_seqlens: Optional[torch.Tensor]  # int32 [N + 1] or None
+    scale: float
+    chunk: int
+    n_seg: int = 1                 # segments per batch row (1 = unsegmented)
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+    @property
+    def T(self):
+        return self.q.shape[1]
+
+    @property
+    def H(self):
+        return self.v.shape[2]
+
+    @property
+    def HK(self):
+        return self.q.shape[2]
+
+    @property
+    def K(self):
+        return self.q.shape[3]
+
+    @property
+    def V(self):
+        return self.v.shape[3]
+
+    @property
+    def N(self):
+        return self.B if self.cu_seqlens is None else self.cu_seqlens.numel() - 1
+
+    @property
+    def tokens(self) -> int:
+        """Active tokens (per the packed offsets when present)."""
+        if self.cu_seqlens is None:
+            return self.B * self.T
+        return int(self.cu_seqlens[-1])
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def _l2rows(x):
+    # unit rows over the last axis, in float32, no epsilon (N(0,1) rows are never zero)
+    return (x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32))).astype(np.float32)
+
+
+def _softplus(x):
+    return np.logaddexp(np.float32(0.0), x).astype(np.float32)
+
+
+def _sigmoid(x):
+    return (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
+
+
+def _cast(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(dtype) if dtype != torch.float32 else t
+
+
+def delta_rule_inputs(*, B, T, H, K, V, HK=None, dtype=torch.bfloat16, seed=0,
+                      gate_shift=0.0, h0_std=None, N=None, normalize_qk=True,
+                      beta_scale=1.0):
+    """q, k (unit rows), v ~ N(0,1); g = -softplus(N(0,1) + gate_shift); beta = sigmoid(N(0,1))."""
+    HK = HK or H
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (B, T, HK, K))
+    k = _normal(rng, (B, T, HK, K))
+    if normalize_qk:
+        q, k = _l2rows(q), _l2rows(k)
+    v = _normal(rng, (B, T, H, V))
+    g = -_softplus(_normal(rng, (B, T, H)) + np.float32(gate_shift))
+    beta = (_sigmoid(_normal(rng, (B, T, H))) * np.float32(beta_scale)).astype(np.float32)
+    h0 = None
+    if h0_std is not None:
+        h0 = torch.from_numpy(_normal(rng, (N or B, H, V, K)) * np.float32(h0_std))
+    return dict(q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype),
+                g=torch.from_numpy(g), beta=torch.from_numpy(beta), h0=h0, rng=rng)
+
+
+def scalar_gate_inputs(*, B, T, H, HK, K, V, dtype=torch.bfloat16, seed=0):
+    """q, k, v ~ N(0,1) (not normalised); per-head A = -softplus(N(0,1)) [H];
+    dt = softplus(N(0,1)) [B, T, H]; g = A * dt."""
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (B, T, HK, K))
+    k = _normal(rng, (B, T, HK, K))
+    v = _normal(rng, (B, T, H, V))
+    A = -_softplus(_normal(rng, (H,)))
+    dt = _softplus(_normal(rng, (B, T, H)))
+    g = (A[None, None, :] * dt).astype(np.float32)
+    return dict(q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype),
+                g=torch.from_numpy(g), A=A, rng=rng)
+
+
+def varlen_lengths(rng, total, n_long=7, min_ragged=3, chunk=64):
+    """Sequence lengths of the packed workload: one short sequence (1..63 tokens),
+    n_long more from distinct random cuts, then one empty sequence at a random slot.
+    All lengths sum to ``total``; at least ``min_ragged`` of the nonempty ones are
+    not multiples of ``chunk``."""
+    short = int(rng.integers(1, chunk))
+    while True:
+        cuts = np.sort(rng.choice(np.arange(1, total - short), size=n_long - 1, replace=False))
+        edges = np.concatenate([[0], cuts, [total - short]])
+        longs = np.diff(edges).astype(np.int64)
+        lens = np.concatenate([[short], longs])
+        if np.count_nonzero(lens % chunk) >= min_ragged and np.all(lens > 0):
+            break
+    rng.shuffle(lens)
+    pos = int(rng.integers(0, len(lens) + 1))
+    lens = np.insert(lens, pos, 0)
+    assert lens.sum() == total
+    return lens
+
+
+def cu_from_lengths(lens):
+    return torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+
+
+def tiny_gdn(seed=SEEDS["tiny_gdn"]):
+    d = delta_rule_inputs(B=1, T=256, H=2, K=64, V=64, dtype=torch.float32, seed=seed)
+    return Workload("tiny_gdn", "gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], None, None,
+                    scale=1.0 / 8.0, chunk=64)
+
+
+def dense_gdn(seed=SEEDS["dense_gdn"], *, B=2, T=4096, H=16, D=128):
+    d = delta_rule_inputs(B=B, T=T, H=H, K=D, V=D, dtype=torch.bfloat16, seed=seed,
+                          gate_shift=2.0, h0_std=0.02)
+    return Workload("dense_gdn", "gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], None,
+                    scale=1.0 / np.sqrt(D), chunk=64)
+
+
+def varlen_gdn(seed=SEEDS["varlen_gdn"], *, T=32768, H=32, D=128, n_long=7):
+    d = delta_rule_inputs(B=1, T=T, H=H, K=D, V=D, dtype=torch.bfloat16, seed=seed, gate_shift=2.0)
+    lens = varlen_lengths(d["rng"], T, n_long=n_long)
+    return Workload("varlen_gdn", "gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], None,
+                    cu_from_lengths(lens), scale=1.0 / np.sqrt(D), chunk=64,
+                    meta={"lengths": [int(x) for x in lens]})
+
+
+def long_gdn(seed=SEEDS["long_gdn"], *, T=262144, H=16, D=128, n_seg=16):
+    d = delta_rule_inputs(B=1, T=T, H=H, K=D, V=D, dtype=torch.bfloat16, seed=seed, gate_shift=4.0)
+    return Workload("long_gdn", "gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], None, None,
+                    scale=1.0 / np.sqrt(D), chunk=64, n_seg=n_seg)
+
+
+def ssd_gla(seed=SEEDS["ssd_gla"], *, B=2, T=16384, H=64, HK=8, K=128, V=64, n_seg=8):
+    d = scalar_gate_inputs(B=B, T=T, H=H, HK=HK, K=K, V=V, seed=seed)
+    return Workload("ssd_gla", "gla", d["q"], d["k"], d["v"], d["g"], None, None, None,
+                    scale=1.0, chunk=128, n_seg=n_seg, meta={"A": d["A"]})
+
+
+CONFIGS = {"tiny_gdn": tiny_gdn, "dense_gdn": dense_gdn, "varlen_gdn": varlen_gdn,
+           "long_gdn": long_gdn, "ssd_gla": ssd_gla}
+
+
+def to_f32(t):
+    """Exact float32 numpy copy of a CPU tensor (bf16 widens exactly)."""
+    if t is None:
+        return None
+    return t.detach().to("cpu").to(torch.float32).numpy()
