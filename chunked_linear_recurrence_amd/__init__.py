@@ -1,0 +1,292 @@
+"""Chunk-parallel linear recurrences on MI355X (gfx950): Python binding.
+
+This module only marshals arguments: it checks tensor shapes and dtypes,
+allocates outputs and workspaces with PyTorch (which is used here for device
+memory and streams only) and calls the C ABI of ``libsf.so`` (include/sf.h)
+on the current HIP stream. Every step of the computation runs in the HIP
+kernels of that library; there is no CPU or PyTorch fallback, and a missing
+library is an error.
+
+Functions (same names as the C entry points, without the ``sf_`` prefix):
+
+* ``gdn_chunk_fwd``     Gated Delta Rule forward, 64-token chunks
+                        (attention-gym "Linear Attention", "Gated Delta Rule").
+* ``gla_chunk_fwd``     scalar-gated linear attention forward
+                        (StateFlow Eq. (1), scalar-identity transition).
+* ``segment_summary``   affine summary per segment row (attention-gym
+                        "Context Parallelism"; Megatron-LM "Mamba2 state-passing
+                        context parallelism").
+* ``state_scan``        exclusive scan over segment summaries.
+* ``segmented_gdn_fwd`` / ``segmented_gla_fwd``: one long sequence cut into
+  segments laid along the batch axis: summary -> scan -> chunk forward.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsf.so")
+
+SF_OK, SF_ERR_INVALID, SF_ERR_UNSUPPORTED, SF_ERR_HIP, SF_ERR_WORKSPACE = range(5)
+SF_F32, SF_BF16 = 0, 1
+SF_KIND_GDN, SF_KIND_GLA = 0, 1
+KINDS = {"gdn": SF_KIND_GDN, "gla": SF_KIND_GLA}
+
+EXPORTED = (
+    "sf_version", "sf_last_error", "sf_gdn_chunk_fwd_workspace", "sf_gdn_chunk_fwd",
+    "sf_gla_chunk_fwd", "sf_segment_summary_workspace", "sf_segment_summary",
+    "sf_state_scan", "sf_timing_enable", "sf_timing_collect",
+)
+
+
+class SfError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sf status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsf.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m chunked_linear_recurrence_amd.build` "
+            "(there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.sf_version.restype = ctypes.c_char_p
+    L.sf_last_error.restype = ctypes.c_char_p
+    L.sf_gdn_chunk_fwd_workspace.restype = Z
+    L.sf_gdn_chunk_fwd_workspace.argtypes = [I, I, I, I, I, I, I, I]
+    L.sf_gdn_chunk_fwd.restype = I
+    L.sf_gdn_chunk_fwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, Z, P]
+    L.sf_gla_chunk_fwd.restype = I
+    L.sf_gla_chunk_fwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, P, P]
+    L.sf_segment_summary_workspace.restype = Z
+    L.sf_segment_summary_workspace.argtypes = [I, I, I, I, I, I, I, I]
+    L.sf_segment_summary.restype = I
+    L.sf_segment_summary.argtypes = [I, I, P, P, P, P, I, I, I, I, I, I, I, P, P, P, Z, P]
+    L.sf_state_scan.restype = I
+    L.sf_state_scan.argtypes = [I, P, P, P, I, I, I, I, I, P, P, P]
+    L.sf_timing_enable.restype = I
+    L.sf_timing_enable.argtypes = [I]
+    L.sf_timing_collect.restype = I
+    L.sf_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int), I]
+    _lib = L
+    return L
+
+
+def version() -> str:
+    return lib().sf_version().decode()
+
+
+def _check(status: int):
+    if status != SF_OK:
+        raise SfError(status, lib().sf_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SF_BF16
+    if t.dtype == torch.float32:
+        return SF_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t, name, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns blocks aligned to at least 512 bytes
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _token_args(q, k, v, g, beta, initial_state, cu_seqlens):
+    _need(q, "q", ndim=4)
+    dev = q.device
+    _need(k, "k", dtype=q.dtype, ndim=4, device=dev)
+    _need(v, "v", dtype=q.dtype, ndim=4, device=dev)
+    _need(g, "g", dtype=torch.float32, ndim=3, device=dev)
+    if beta is not None:
+        _need(beta, "beta", dtype=torch.float32, ndim=3, device=dev)
+    B, T, HK, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, H):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)} g {tuple(g.shape)}")
+    if beta is not None and beta.shape != g.shape:
+        raise ValueError("beta must have the shape of g")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1, device=dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", dtype=torch.float32, ndim=4, device=dev)
+        if tuple(initial_state.shape) != (N, H, V, K):
+            raise ValueError(f"initial_state must be [{N}, {H}, {V}, {K}], got {tuple(initial_state.shape)}")
+    return B, T, H, HK, K, V, N
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, scale=None,
+                  output_final_state=False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated Delta Rule chunk forward. q, k [B,T,HK,K]; v [B,T,H,V]; g, beta [B,T,H] float32;
+    initial_state [N,H,V,K] float32. Returns (output [B,T,H,V] in q.dtype, final state or None).
+    Output rows at or past cu_seqlens[-1] are left uninitialised."""
+    B, T, H, HK, K, V, N = _token_args(q, k, v, g, beta, initial_state, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    dev = q.device
+    out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+    ht = torch.empty((N, H, V, K), dtype=torch.float32, device=dev) if output_final_state else None
+    dt = _dt(q)
+    nbytes = lib().sf_gdn_chunk_fwd_workspace(dt, B, T, H, K, V, N, int(cu_seqlens is not None))
+    ws = _workspace(nbytes, dev)
+    _check(lib().sf_gdn_chunk_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                  _ptr(cu_seqlens), N, B, T, H, HK, K, V, float(scale), _ptr(out), _ptr(ht),
+                                  _ptr(ws), nbytes, _stream()))
+    return out, ht
+
+
+def gla_chunk_fwd(q, k, v, g, initial_state=None, *, cu_seqlens=None, scale=1.0, chunk=64,
+                  output_final_state=False):
+    """Scalar-gated linear attention forward: S_t = exp(g_t) S_{t-1} + v_t k_t^T,
+    o_t = scale S_t q_t. Returns (output, final state or None)."""
+    B, T, H, HK, K, V, N = _token_args(q, k, v, g, None, initial_state, cu_seqlens)
+    dev = q.device
+    out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+    ht = torch.empty((N, H, V, K), dtype=torch.float32, device=dev) if output_final_state else None
+    _check(lib().sf_gla_chunk_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state),
+                                  _ptr(cu_seqlens), N, B, T, H, HK, K, V, int(chunk), float(scale), _ptr(out),
+                                  _ptr(ht), _stream()))
+    return out, ht
+
+
+def segment_summary(kind, k, v, g, beta=None, *, chunk=None):
+    """Affine summary of each row of [n_rows, L_seg, ...] inputs.
+    kind "gdn": returns (M [n_rows,H,K,K], S_ext [n_rows,H,V,K]);
+    kind "gla": returns (a_block [n_rows,H], S_ext)."""
+    kd = KINDS[kind]
+    _need(k, "k", ndim=4)
+    dev = k.device
+    _need(v, "v", dtype=k.dtype, ndim=4, device=dev)
+    _need(g, "g", dtype=torch.float32, ndim=3, device=dev)
+    R, L, HK, K = k.shape
+    H, V = v.shape[2], v.shape[3]
+    if v.shape[:2] != (R, L) or g.shape != (R, L, H):
+        raise ValueError("shape mismatch between k, v and g")
+    if kd == SF_KIND_GDN:
+        _need(beta, "beta", dtype=torch.float32, ndim=3, device=dev)
+        if beta.shape != g.shape:
+            raise ValueError("beta must have the shape of g")
+    chunk = chunk or 64
+    dt = _dt(k)
+    M = torch.empty((R, H, K, K) if kd == SF_KIND_GDN else (R, H), dtype=torch.float32, device=dev)
+    S_ext = torch.empty((R, H, V, K), dtype=torch.float32, device=dev)
+    nbytes = lib().sf_segment_summary_workspace(kd, dt, R, L, H, K, V, chunk)
+    ws = _workspace(nbytes, dev) if nbytes else None
+    _check(lib().sf_segment_summary(kd, dt, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), R, L, H, HK, K, V, chunk,
+                                    _ptr(M), _ptr(S_ext), _ptr(ws), nbytes, _stream()))
+    return M, S_ext
+
+
+def state_scan(kind, M, S_ext, h0=None, *, B, n_seg, final_state=True):
+    """Exclusive scan over segment rows s = b*n_seg + j. Returns (S_in, S_final or None)."""
+    kd = KINDS[kind]
+    _need(S_ext, "S_ext", dtype=torch.float32, ndim=4)
+    dev = S_ext.device
+    _need(M, "M", dtype=torch.float32, device=dev)
+    R, H, V, K = S_ext.shape
+    if R != B * n_seg:
+        raise ValueError(f"S_ext has {R} rows, expected B*n_seg = {B * n_seg}")
+    want_M = (R, H, K, K) if kd == SF_KIND_GDN else (R, H)
+    if tuple(M.shape) != want_M:
+        raise ValueError(f"M must be {want_M}, got {tuple(M.shape)}")
+    if h0 is not None:
+        _need(h0, "h0", dtype=torch.float32, ndim=4, device=dev)
+        if tuple(h0.shape) != (B, H, V, K):
+            raise ValueError("h0 must be [B, H, V, K]")
+    S_in = torch.empty_like(S_ext)
+    S_final = torch.empty((B, H, V, K), dtype=torch.float32, device=dev) if final_state else None
+    _check(lib().sf_state_scan(kd, _ptr(M), _ptr(S_ext), _ptr(h0), B, n_seg, H, K, V, _ptr(S_in), _ptr(S_final),
+                               _stream()))
+    return S_in, S_final
+
+
+def segment_view(x: torch.Tensor, n_seg: int) -> torch.Tensor:
+    """[B, T, ...] -> [B*n_seg, T/n_seg, ...] (a view; row s = b*n_seg + j)."""
+    B, T = x.shape[:2]
+    if T % n_seg:
+        raise ValueError(f"T={T} is not a multiple of n_seg={n_seg}")
+    return x.view(B * n_seg, T // n_seg, *x.shape[2:])
+
+
+def segmented_gdn_fwd(q, k, v, g, beta, n_seg, initial_state=None, *, scale=None, output_final_state=False):
+    """One long Gated Delta Rule run cut into n_seg segments per batch row (summary -> scan -> forward).
+    Equals gdn_chunk_fwd on the whole rows up to floating-point order."""
+    B, T = q.shape[:2]
+    if (T // n_seg) % 64:
+        raise ValueError("segment length must be a multiple of the 64-token chunk")
+    sv = lambda x: segment_view(x, n_seg)
+    M, S_ext = segment_summary("gdn", sv(k), sv(v), sv(g), sv(beta), chunk=64)
+    S_in, S_final = state_scan("gdn", M, S_ext, initial_state, B=B, n_seg=n_seg, final_state=output_final_state)
+    o, _ = gdn_chunk_fwd(sv(q), sv(k), sv(v), sv(g), sv(beta), S_in, scale=scale)
+    return o.view(q.shape[0], T, *o.shape[2:]), S_final
+
+
+def segmented_gla_fwd(q, k, v, g, n_seg, initial_state=None, *, scale=1.0, chunk=64, output_final_state=False):
+    """Scalar-gate counterpart of segmented_gdn_fwd (a_block summaries)."""
+    B, T = q.shape[:2]
+    if (T // n_seg) % chunk:
+        raise ValueError("segment length must be a multiple of the chunk")
+    sv = lambda x: segment_view(x, n_seg)
+    a, S_ext = segment_summary("gla", sv(k), sv(v), sv(g), chunk=chunk)
+    S_in, S_final = state_scan("gla", a, S_ext, initial_state, B=B, n_seg=n_seg, final_state=output_final_state)
+    o, _ = gla_chunk_fwd(sv(q), sv(k), sv(v), sv(g), S_in, scale=scale, chunk=chunk)
+    return o.view(B, T, *o.shape[2:]), S_final
+
+
+def timing_enable(max_pairs: int = 4096):
+    """Bracket every library launch with HIP events (0 disables)."""
+    _check(lib().sf_timing_enable(int(max_pairs)))
+
+
+def timing_collect(max_kernels: int = 32):
+    """{kernel name: (launches, total ms)} since the last collect (synchronises on the events)."""
+    names = (ctypes.c_char_p * max_kernels)()
+    ms = (ctypes.c_double * max_kernels)()
+    cnt = (ctypes.c_int * max_kernels)()
+    n = lib().sf_timing_collect(names, ms, cnt, max_kernels)
+    if n < 0:
+        raise SfError(SF_ERR_HIP, "timing collect failed")
+    return {names[i].decode(): (cnt[i], ms[i]) for i in range(n)}

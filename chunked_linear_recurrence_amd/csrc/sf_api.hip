@@ -1,0 +1,248 @@
+// Host entry points of the C ABI declared in include/sf.h: argument
+// validation, workspace carve-up and kernel dispatch. No allocation, no
+// synchronisation on the enqueue path.
+#include "../../include/sf.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "sf_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sf_status fail(sf_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+sf_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return SF_OK;
+    return fail(SF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr long kMaxElems = 0x7fffffffL;
+
+bool fits(long a) { return a >= 0 && a <= kMaxElems; }
+
+int elem_bytes(sf_dtype dt) { return dt == SF_BF16 ? 2 : 4; }
+
+// Common shape checks for token-major inputs.
+sf_status check_tokens(sf_dtype dt, int B, int T, int H, int HK, int K, int V, int N,
+                       bool packed) {
+    if (dt != SF_F32 && dt != SF_BF16) return fail(SF_ERR_INVALID, "dtype must be SF_F32 or SF_BF16");
+    if (B < 0 || T < 0 || H <= 0 || HK <= 0 || K <= 0 || V <= 0 || N < 0)
+        return fail(SF_ERR_INVALID, "sizes must be positive (B=%d T=%d H=%d HK=%d K=%d V=%d N=%d)", B, T, H,
+                    HK, K, V, N);
+    if (H % HK != 0) return fail(SF_ERR_INVALID, "HK=%d must divide H=%d", HK, H);
+    if (packed && B != 1) return fail(SF_ERR_INVALID, "cu_seqlens needs batch-one inputs (B=%d)", B);
+    if (!packed && N != B) return fail(SF_ERR_INVALID, "without cu_seqlens N (%d) must equal B (%d)", N, B);
+    if (!fits((long)B * T * HK * K) || !fits((long)B * T * H * V) || !fits((long)N * H * V * K) ||
+        !fits((long)B * T * H))
+        return fail(SF_ERR_UNSUPPORTED, "a tensor has 2^31 or more elements (int64 offsets are not supported)");
+    return SF_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// timing hook
+// ---------------------------------------------------------------------------
+namespace sf {
+namespace {
+struct TimingRec {
+    const char* name;
+    int pair;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<hipEvent_t> g_ev;  // 2 * pairs
+std::vector<TimingRec> g_recs;
+int g_next = 0;
+const char* g_pending = nullptr;
+}  // namespace
+
+void timing_begin(const char* name, hipStream_t s) {
+    if (!g_timing) return;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_pending = nullptr;
+    if (2 * (g_next + 1) > (int)g_ev.size()) return;
+    if (hipEventRecord(g_ev[2 * g_next], s) != hipSuccess) return;
+    g_pending = name;
+}
+
+void timing_end(hipStream_t s) {
+    if (!g_timing) return;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (!g_pending) return;
+    if (hipEventRecord(g_ev[2 * g_next + 1], s) == hipSuccess) g_recs.push_back({g_pending, g_next++});
+    g_pending = nullptr;
+}
+}  // namespace sf
+
+extern "C" {
+
+const char* sf_version(void) { return "sf 0.1.0 gfx950"; }
+
+const char* sf_last_error(void) { return g_err; }
+
+sf_status sf_timing_enable(int max_pairs) {
+    std::lock_guard<std::mutex> lk(sf::g_tmu);
+    for (hipEvent_t e : sf::g_ev) (void)hipEventDestroy(e);
+    sf::g_ev.clear();
+    sf::g_recs.clear();
+    sf::g_next = 0;
+    sf::g_timing = false;
+    if (max_pairs <= 0) return SF_OK;
+    sf::g_ev.resize(2 * (size_t)max_pairs);
+    for (auto& e : sf::g_ev) {
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return hip_status(err, "hipEventCreate");
+    }
+    sf::g_timing = true;
+    return SF_OK;
+}
+
+int sf_timing_collect(const char** names, double* total_ms, int* launches, int max_kernels) {
+    std::lock_guard<std::mutex> lk(sf::g_tmu);
+    int nk = 0;
+    for (const auto& r : sf::g_recs) {
+        if (hipEventSynchronize(sf::g_ev[2 * r.pair + 1]) != hipSuccess) return -1;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, sf::g_ev[2 * r.pair], sf::g_ev[2 * r.pair + 1]) != hipSuccess) return -1;
+        int i = 0;
+        while (i < nk && strcmp(names[i], r.name) != 0) ++i;
+        if (i == nk) {
+            if (nk == max_kernels) continue;
+            names[nk] = r.name;
+            total_ms[nk] = 0.0;
+            launches[nk] = 0;
+            ++nk;
+        }
+        total_ms[i] += ms;
+        launches[i] += 1;
+    }
+    sf::g_recs.clear();
+    sf::g_next = 0;
+    return nk;
+}
+
+size_t sf_gdn_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N, int packed) {
+    (void)K;
+    (void)V;
+    if ((dt != SF_F32 && dt != SF_BF16) || B < 0 || T < 0 || H <= 0 || N < 0) return 0;
+    return sf::gdn_workspace_layout(nullptr, elem_bytes(dt), B, T, H, N, packed != 0).bytes;
+}
+
+sf_status sf_gdn_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B,
+                           int T, int H, int HK, int K, int V, float scale, void* out, float* ht,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
+    if (st != SF_OK) return st;
+    if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
+    if (K != V || (K != 64 && K != 128))
+        return fail(SF_ERR_UNSUPPORTED, "delta-rule kernels are built for K == V in {64, 128} (K=%d V=%d)", K, V);
+    const sf::GdnWorkspace need = sf::gdn_workspace_layout(nullptr, elem_bytes(dt), B, T, H, N, packed);
+    if (!workspace || workspace_bytes < need.bytes)
+        return fail(SF_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                    need.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(SF_ERR_INVALID, "workspace must be 256-byte aligned");
+    const sf::GdnWorkspace ws = sf::gdn_workspace_layout(workspace, elem_bytes(dt), B, T, H, N, packed);
+    hipError_t e = sf::launch_gdn(dt == SF_BF16, 0, q, k, v, g, beta, h0, cu_seqlens, ws, N, B, T, H, HK, K, V,
+                                  scale, out, ht, nullptr, static_cast<hipStream_t>(stream));
+    return hip_status(e, "sf_gdn_chunk_fwd launch");
+}
+
+sf_status sf_gla_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                           const float* h0, const int32_t* cu_seqlens, int N, int B, int T, int H, int HK,
+                           int K, int V, int chunk, float scale, void* out, float* ht, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
+    if (st != SF_OK) return st;
+    if (!q || !k || !v || !g || !out) return fail(SF_ERR_INVALID, "q, k, v, g and out must not be NULL");
+    if (chunk != 64 && chunk != 128) return fail(SF_ERR_UNSUPPORTED, "chunk must be 64 or 128 (got %d)", chunk);
+    if (dt == SF_F32 && chunk != 64) return fail(SF_ERR_UNSUPPORTED, "float32 inputs use chunk 64");
+    if ((K != 64 && K != 128) || (V != 64 && V != 128))
+        return fail(SF_ERR_UNSUPPORTED, "scalar-gate kernels are built for K, V in {64, 128} (K=%d V=%d)", K, V);
+    hipError_t e = sf::launch_gla(dt == SF_BF16, 0, q, k, v, g, h0, cu_seqlens, N, B, T, H, HK, K, V, chunk, scale,
+                                  out, ht, nullptr, static_cast<hipStream_t>(stream));
+    return hip_status(e, "sf_gla_chunk_fwd launch");
+}
+
+size_t sf_segment_summary_workspace(sf_kind kind, sf_dtype dt, int n_rows, int L_seg, int H, int K, int V,
+                                    int chunk) {
+    (void)K;
+    (void)V;
+    (void)chunk;
+    if (kind == SF_KIND_GLA) return 0;
+    if (kind != SF_KIND_GDN || (dt != SF_F32 && dt != SF_BF16) || n_rows < 0 || L_seg < 0 || H <= 0) return 0;
+    return sf::gdn_workspace_layout(nullptr, elem_bytes(dt), n_rows, L_seg, H, n_rows, false).bytes;
+}
+
+sf_status sf_segment_summary(sf_kind kind, sf_dtype dt, const void* k, const void* v, const float* g,
+                             const float* beta, int n_rows, int L_seg, int H, int HK, int K, int V, int chunk,
+                             float* M, float* S_ext, void* workspace, size_t workspace_bytes, void* stream) {
+    sf_status st = check_tokens(dt, n_rows, L_seg, H, HK, K, V, n_rows, false);
+    if (st != SF_OK) return st;
+    if (!k || !v || !g || !M || !S_ext) return fail(SF_ERR_INVALID, "k, v, g, M and S_ext must not be NULL");
+    if (!fits((long)n_rows * H * K * K)) return fail(SF_ERR_UNSUPPORTED, "M has 2^31 or more elements");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kind == SF_KIND_GDN) {
+        if (!beta) return fail(SF_ERR_INVALID, "beta must not be NULL for SF_KIND_GDN");
+        if (chunk != 64) return fail(SF_ERR_UNSUPPORTED, "delta-rule chunk is 64 (got %d)", chunk);
+        if (K != V || (K != 64 && K != 128))
+            return fail(SF_ERR_UNSUPPORTED, "delta-rule kernels are built for K == V in {64, 128} (K=%d V=%d)", K, V);
+        const sf::GdnWorkspace need = sf::gdn_workspace_layout(nullptr, elem_bytes(dt), n_rows, L_seg, H, n_rows, false);
+        if (!workspace || workspace_bytes < need.bytes)
+            return fail(SF_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                        need.bytes);
+        if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(SF_ERR_INVALID, "workspace must be 256-byte aligned");
+        const sf::GdnWorkspace ws = sf::gdn_workspace_layout(workspace, elem_bytes(dt), n_rows, L_seg, H, n_rows, false);
+        hipError_t e = sf::launch_gdn(dt == SF_BF16, 1, nullptr, k, v, g, beta, nullptr, nullptr, ws, n_rows, n_rows,
+                                      L_seg, H, HK, K, V, 1.f, nullptr, S_ext, M, s);
+        return hip_status(e, "sf_segment_summary launch");
+    }
+    if (kind == SF_KIND_GLA) {
+        if (chunk != 64 && chunk != 128) return fail(SF_ERR_UNSUPPORTED, "chunk must be 64 or 128 (got %d)", chunk);
+        if (dt == SF_F32 && chunk != 64) return fail(SF_ERR_UNSUPPORTED, "float32 inputs use chunk 64");
+        if ((K != 64 && K != 128) || (V != 64 && V != 128))
+            return fail(SF_ERR_UNSUPPORTED, "scalar-gate kernels are built for K, V in {64, 128} (K=%d V=%d)", K, V);
+        hipError_t e = sf::launch_gla(dt == SF_BF16, 1, nullptr, k, v, g, nullptr, nullptr, n_rows, n_rows, L_seg, H,
+                                      HK, K, V, chunk, 1.f, nullptr, S_ext, M, s);
+        return hip_status(e, "sf_segment_summary launch");
+    }
+    return fail(SF_ERR_INVALID, "kind must be SF_KIND_GDN or SF_KIND_GLA");
+}
+
+sf_status sf_state_scan(sf_kind kind, const float* M, const float* S_ext, const float* h0, int B, int n_seg,
+                        int H, int K, int V, float* S_in, float* S_final, void* stream) {
+    if (kind != SF_KIND_GDN && kind != SF_KIND_GLA) return fail(SF_ERR_INVALID, "kind must be SF_KIND_GDN or SF_KIND_GLA");
+    if (B < 0 || n_seg < 0 || H <= 0 || K <= 0 || V <= 0) return fail(SF_ERR_INVALID, "sizes must be positive");
+    if (!M || !S_ext || !S_in) return fail(SF_ERR_INVALID, "M, S_ext and S_in must not be NULL");
+    if (!fits((long)B * n_seg * H * V * K) || !fits((long)B * n_seg * H * K * K))
+        return fail(SF_ERR_UNSUPPORTED, "a tensor has 2^31 or more elements");
+    if (kind == SF_KIND_GDN) {
+        if ((K != 64 && K != 128) || V % 16 != 0)
+            return fail(SF_ERR_UNSUPPORTED, "delta-rule scan is built for K in {64, 128} and V a multiple of 16 (K=%d V=%d)",
+                        K, V);
+    } else if ((V * K) % 4 != 0) {
+        return fail(SF_ERR_UNSUPPORTED, "V * K must be a multiple of 4");
+    }
+    hipError_t e = sf::launch_scan(kind == SF_KIND_GDN ? 0 : 1, M, S_ext, h0, B, n_seg, H, K, V, S_in, S_final,
+                                   static_cast<hipStream_t>(stream));
+    return hip_status(e, "sf_state_scan launch");
+}
+
+}  // extern "C"

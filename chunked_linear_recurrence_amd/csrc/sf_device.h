@@ -1,0 +1,114 @@
+// Device-side building blocks for the gfx950 kernels: element types, the
+// 16x16 MFMA block product, LDS fragment loads and bf16 conversion.
+//
+// Block product convention (one 64-lane wavefront):
+//   lane = 16 * lg + ln  (ln in 0..15, lg in 0..3)
+//   A fragment of a 16x16 block A[m][r]:  lane holds A[ln][4*lg + j], j = 0..3
+//   B fragment of a 16x16 block B[r][n]:  lane holds B[4*lg + j][ln], j = 0..3
+//   C/D tile of a 16x16 block C[m][n]:    lane holds C[4*lg + j][ln], j = 0..3
+// so the C tile of one product is, unchanged, the B fragment of a product
+// that reduces over the C tile's row index, and (as C^T) the A fragment of a
+// product whose rows are the C tile's columns. For bf16 storage one block
+// product is one v_mfma_f32_16x16x16_bf16; for float32 it is four
+// v_mfma_f32_16x16x4_f32 issued over the four reduction slots j.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sf {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+// float32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+template <typename ST> struct Elem;
+
+template <> struct Elem<bf16_t> {
+    typedef i16x4 frag;
+    static __device__ __forceinline__ float to_f(bf16_t x) { return bf2f(x); }
+    static __device__ __forceinline__ bf16_t from_f(float x) { return f2bf(x); }
+    static __device__ __forceinline__ f32x4 mma(f32x4 acc, frag a, frag b) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag pack(f32x4 x) {
+        frag r;
+        r[0] = (short)f2bf(x[0]);
+        r[1] = (short)f2bf(x[1]);
+        r[2] = (short)f2bf(x[2]);
+        r[3] = (short)f2bf(x[3]);
+        return r;
+    }
+    static __device__ __forceinline__ f32x4 unpack(frag x) {
+        f32x4 r;
+        r[0] = bf2f((bf16_t)x[0]);
+        r[1] = bf2f((bf16_t)x[1]);
+        r[2] = bf2f((bf16_t)x[2]);
+        r[3] = bf2f((bf16_t)x[3]);
+        return r;
+    }
+};
+
+template <> struct Elem<float> {
+    typedef f32x4 frag;
+    static __device__ __forceinline__ float to_f(float x) { return x; }
+    static __device__ __forceinline__ float from_f(float x) { return x; }
+    static __device__ __forceinline__ f32x4 mma(f32x4 acc, frag a, frag b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+        return acc;
+    }
+    static __device__ __forceinline__ frag pack(f32x4 x) { return x; }
+    static __device__ __forceinline__ f32x4 unpack(frag x) { return x; }
+};
+
+// Fragment of rows [r0, r0+16) x columns [c0 + 4*lg, +4) of a row-major
+// LDS matrix with leading dimension ld. Serves as the A fragment of
+// X[r0.., c0..] and as the B fragment of (Y[r0.., c0..])^T.
+template <typename ST>
+__device__ __forceinline__ typename Elem<ST>::frag frag_rows(const ST* m, int ld, int r0, int c0) {
+    const int ln = lane_id() & 15, lg = lane_id() >> 4;
+    return *reinterpret_cast<const typename Elem<ST>::frag*>(m + (r0 + ln) * ld + c0 + 4 * lg);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// 16-byte vector unit used for staging copies.
+typedef uint4 u128;
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// blockIdx -> (chain, sub-block) so that all sub-blocks of one chain run on
+// the same XCD (workgroups are dispatched round-robin over the 8 XCDs, so
+// consecutive linear ids land on different XCDs; each XCD has its own L2).
+// The grid must hold ceil(chains / 8) * 8 * nsub workgroups.
+__device__ __forceinline__ void xcd_split(int L, int nsub, int& chain, int& sub) {
+    const int xcd = L & 7, idx = L >> 3;
+    chain = (idx / nsub) * 8 + xcd;
+    sub = idx % nsub;
+}
+
+}  // namespace sf

@@ -1,0 +1,76 @@
+// Internal interface between the host entry points (sf_api.hip) and the
+// kernel launchers (gdn.hip, gla.hip, scan.hip). Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sf {
+
+constexpr int kGdnChunk = 64;
+
+// Bytes of one per-(chunk, head) factor record of the delta-rule "Pre" stage:
+// the 64x64 solve factor T, the 64x64 decay-masked query-key block P (both in
+// the q/k/v element type) and 256 float coefficients.
+__host__ __device__ inline size_t gdn_factor_bytes(int elem_bytes) {
+    return (size_t)2 * kGdnChunk * kGdnChunk * elem_bytes + 256 * sizeof(float);
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace carve-up for the delta-rule path (packed: chunk offsets + table).
+struct GdnWorkspace {
+    int* chunk_off;      // [N + 1] (packed only)
+    int2* table;         // [cap]   (packed only)
+    uint8_t* factors;    // [slots, H] records
+    size_t bytes;
+};
+
+// Number of chunk slots: dense B * ceil(T/64); packed ceil(T/64) + N.
+inline long gdn_slots(int B, int T, int N, bool packed) {
+    const long nc = (T + kGdnChunk - 1) / kGdnChunk;
+    return packed ? nc + N : (long)B * nc;
+}
+
+inline GdnWorkspace gdn_workspace_layout(void* base, int elem_bytes, int B, int T, int H, int N,
+                                         bool packed) {
+    GdnWorkspace w{};
+    size_t off = 0;
+    uint8_t* p = static_cast<uint8_t*>(base);
+    const long slots = gdn_slots(B, T, N, packed);
+    if (packed) {
+        w.chunk_off = reinterpret_cast<int*>(p ? p + off : nullptr);
+        off += align256(sizeof(int) * (size_t)(N + 1));
+        w.table = reinterpret_cast<int2*>(p ? p + off : nullptr);
+        off += align256(sizeof(int2) * (size_t)slots);
+    }
+    w.factors = p ? p + off : nullptr;
+    off += align256(gdn_factor_bytes(elem_bytes) * (size_t)slots * H);
+    w.bytes = off;
+    return w;
+}
+
+// Measurement hook (see sf_timing_enable): brackets one launch with events.
+void timing_begin(const char* name, hipStream_t s);
+void timing_end(hipStream_t s);
+
+// ---- launchers (return the HIP error of the launch) ----
+hipError_t launch_chunk_table(const int32_t* cu, int N, int chunk, long cap, int* chunk_off,
+                              int2* table, hipStream_t s);
+
+// mode: 0 = forward (writes out/ht), 1 = summary (writes S_ext into ht, M into Mout)
+hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const float* h0, const int32_t* cu,
+                      const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int K, int V,
+                      float scale, void* out, float* ht, float* Mout, hipStream_t s);
+
+hipError_t launch_gla(bool bf16, int mode, const void* q, const void* k, const void* v,
+                      const float* g, const float* h0, const int32_t* cu, int N, int B, int T,
+                      int H, int HK, int K, int V, int chunk, float scale, void* out, float* ht,
+                      float* a_out, hipStream_t s);
+
+hipError_t launch_scan(int kind, const float* M, const float* S_ext, const float* h0, int B,
+                       int n_seg, int H, int K, int V, float* S_in, float* S_final, hipStream_t s);
+
+}  // namespace sf

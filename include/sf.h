@@ -1,0 +1,185 @@
+/*
+ * sf.h -- C ABI of the chunk-parallel linear recurrence library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library runs the forward pass of two linear recurrences on one GPU,
+ * chunk by chunk, with hand-written HIP kernels:
+ *
+ *  - the Gated Delta Rule (attention-gym "Linear Attention" page, section
+ *    "Gated Delta Rule"): per token, the state is decayed by exp(gate), the
+ *    beta-scaled residual of the value against the decayed state read at the
+ *    key is added as an outer product with the key, and the output is the
+ *    scaled updated state read at the query;
+ *  - scalar-gated linear attention (StateFlow, Section 2.1, Eq. (1), with the
+ *    Mamba-2 scalar-identity transition; the SSD form of the Megatron-LM page
+ *    "Mamba2 state-passing context parallelism"): S_t = exp(g_t) S_{t-1} +
+ *    v_t k_t^T, o_t = scale * S_t q_t;
+ *
+ * plus the boundary-state passing that lets one long sequence be cut into
+ * segments laid along the batch axis: every segment is an affine map of its
+ * entry state (attention-gym "Context Parallelism"; the Megatron-LM page),
+ * summarised independently, and the true entry states are recovered with an
+ * exclusive scan over the summaries.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer to memory the caller owns
+ *    (allocated with hipMalloc or by PyTorch). The library never allocates,
+ *    frees or synchronises; it validates arguments on the host, enqueues its
+ *    kernels on `stream` (a hipStream_t; NULL is the null stream) and returns.
+ *  - Layouts are dense, row-major, token-major, with no padding:
+ *      q, k  [B, T, HK, K]      v, out [B, T, H, V]
+ *      g, beta [B, T, H] float32 (g is the natural-log decay, finite, <= 0)
+ *      states [N, H, V, K] float32 (V-major: row v, column k)
+ *    Value head h uses q/k head h / (H / HK); HK must divide H.
+ *  - `dt` is the element type of q, k, v and out (SF_F32 or SF_BF16). Gates,
+ *    beta, states and summaries are always float32; the recurrence is carried
+ *    in float32.
+ *  - cu_seqlens (optional, int32 [N + 1], device) packs N sequences into a
+ *    batch-one stream: it starts at 0, never decreases and ends at or before
+ *    T. Chunking restarts at every sequence start and a sequence's last chunk
+ *    may be partial. An empty sequence returns its initial state as its final
+ *    state. Output rows at or past cu_seqlens[N] are not written. These value
+ *    constraints are the caller's responsibility and are not checked on the
+ *    host (reading device memory would synchronise).
+ *  - Inputs must not alias outputs.
+ *  - Return value: SF_OK, or an error status with a message available from
+ *    sf_last_error() (thread-local, valid until the next call on the same
+ *    thread). Invalid shapes or pointers give SF_ERR_INVALID; shapes the
+ *    kernels are not built for give SF_ERR_UNSUPPORTED (there is no fallback);
+ *    a failed HIP launch gives SF_ERR_HIP. Nothing is enqueued when a call
+ *    returns an error.
+ *  - Sizes: every tensor must have fewer than 2^31 elements.
+ */
+#ifndef SF_H
+#define SF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SF_OK = 0,
+    SF_ERR_INVALID = 1,
+    SF_ERR_UNSUPPORTED = 2,
+    SF_ERR_HIP = 3,
+    SF_ERR_WORKSPACE = 4
+} sf_status;
+
+typedef enum { SF_F32 = 0, SF_BF16 = 1 } sf_dtype;
+
+typedef enum { SF_KIND_GDN = 0, SF_KIND_GLA = 1 } sf_kind;
+
+/* Library version string, e.g. "sf 0.1.0 gfx950". */
+const char *sf_version(void);
+
+/* Message of the last non-OK status returned on this thread. */
+const char *sf_last_error(void);
+
+/*
+ * Workspace bytes needed by sf_gdn_chunk_fwd for these sizes (packed != 0
+ * when cu_seqlens is passed; then B must be 1). The workspace holds the
+ * per-chunk factors of the chunk decomposition (StateFlow Section 2.2,
+ * Eq. (2), "Pre"): the unit-lower-triangular WY/UT solve factor, the
+ * decay-masked query-key block and the per-token decay coefficients, plus
+ * the device chunk table of packed inputs. Returns 0 for invalid sizes.
+ */
+size_t sf_gdn_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N,
+                                  int packed);
+
+/*
+ * Gated Delta Rule chunk forward (attention-gym "Linear Attention", section
+ * "Gated Delta Rule": chunk_gdn with a 64-token chunk).
+ *   q, k   [B, T, HK, K] dt          v [B, T, H, V] dt
+ *   g, beta [B, T, H] float32
+ *   h0     [N, H, V, K] float32 initial states, or NULL for zeros
+ *   cu_seqlens  int32 [N + 1] or NULL; without it N must equal B
+ *   scale  query scale (the usual choice is 1 / sqrt(K), chosen by the caller)
+ *   out    [B, T, H, V] dt           ht [N, H, V, K] float32 final states, or NULL
+ *   workspace  at least sf_gdn_chunk_fwd_workspace(...) bytes, 256-byte aligned
+ * Supported: K == V, K in {64, 128}.
+ */
+sf_status sf_gdn_chunk_fwd(sf_dtype dt, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const float *h0,
+                           const int32_t *cu_seqlens, int N, int B, int T, int H, int HK,
+                           int K, int V, float scale, void *out, float *ht,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Scalar-gated linear attention chunk forward (StateFlow Section 2.1, Eq. (1)
+ * with F_t = exp(g_t) I; the Megatron-LM "Mamba2 state-passing context
+ * parallelism" SSD core): S_t = exp(g_t) S_{t-1} + v_t k_t^T,
+ * o_t = scale * S_t q_t. Same layouts as sf_gdn_chunk_fwd without beta.
+ * chunk is 64 or 128 (64 only for SF_F32). Supported: K, V in {64, 128}.
+ * Needs no workspace.
+ */
+sf_status sf_gla_chunk_fwd(sf_dtype dt, const void *q, const void *k, const void *v,
+                           const float *g, const float *h0, const int32_t *cu_seqlens,
+                           int N, int B, int T, int H, int HK, int K, int V, int chunk,
+                           float scale, void *out, float *ht, void *stream);
+
+/* Workspace bytes needed by sf_segment_summary (0 for SF_KIND_GLA). */
+size_t sf_segment_summary_workspace(sf_kind kind, sf_dtype dt, int n_rows, int L_seg, int H,
+                                    int K, int V, int chunk);
+
+/*
+ * Affine summary of each segment row (attention-gym "Context Parallelism":
+ * a token range is the map S_out = S_in @ M + S_ext; its sub-section "cuDNN
+ * local execution": S_ext is the exit state from a zero entry state and M
+ * the exit state from the identity entry with the value term disabled;
+ * Megatron-LM "Mamba2 state-passing context parallelism": for the scalar
+ * gate, S_out = a_block * S_in + S_ext).
+ *   k [n_rows, L_seg, HK, K] dt, v [n_rows, L_seg, H, V] dt, g and beta
+ *   [n_rows, L_seg, H] float32 (beta NULL for SF_KIND_GLA). A long sequence
+ *   [B, T, ...] is passed as its segment view [B * n_seg, T / n_seg, ...]
+ *   (a reshape: row s = b * n_seg + j covers tokens [j L_seg, (j+1) L_seg)).
+ *   M: SF_KIND_GDN  [n_rows, H, K, K] float32 transition
+ *      SF_KIND_GLA  [n_rows, H] float32 a_block = exp(sum of the row's gates)
+ *   S_ext [n_rows, H, V, K] float32.
+ *   chunk: 64 for SF_KIND_GDN, 64 or 128 for SF_KIND_GLA; L_seg need not be
+ *   a multiple of it (the last chunk may be partial).
+ */
+sf_status sf_segment_summary(sf_kind kind, sf_dtype dt, const void *k, const void *v,
+                             const float *g, const float *beta, int n_rows, int L_seg, int H,
+                             int HK, int K, int V, int chunk, float *M, float *S_ext,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Exclusive state scan over segment summaries (Megatron-LM "Mamba2
+ * state-passing context parallelism": exclusive causal scan; attention-gym
+ * "Context Parallelism": composition of range maps). For every batch row b
+ * and segment j (row s = b * n_seg + j):
+ *   S_in[b*n_seg]       = h0[b] (zeros if h0 is NULL)
+ *   S_in[b*n_seg + j+1] = S_in[b*n_seg + j] @ M[s] + S_ext[s]     (SF_KIND_GDN)
+ *                       = M[s] * S_in[b*n_seg + j] + S_ext[s]     (SF_KIND_GLA, M = a_block)
+ *   S_final[b]          = the same step applied after the last segment
+ *   M: [B*n_seg, H, K, K] (GDN) or [B*n_seg, H] (GLA); S_ext, S_in
+ *   [B*n_seg, H, V, K]; h0, S_final [B, H, V, K] (S_final may be NULL).
+ *   All float32. The products are carried in float32.
+ */
+sf_status sf_state_scan(sf_kind kind, const float *M, const float *S_ext, const float *h0,
+                        int B, int n_seg, int H, int K, int V, float *S_in, float *S_final,
+                        void *stream);
+
+/*
+ * Kernel timing hook for measurement. While enabled, every kernel the
+ * library enqueues is bracketed by a pair of HIP events recorded on the same
+ * stream (events come from a pool created by sf_timing_enable, so no
+ * allocation happens in the enqueue path). sf_timing_collect synchronises
+ * on the recorded events and returns, per kernel name, the number of
+ * launches and the summed elapsed milliseconds, then clears the records.
+ *   max_pairs: capacity of the pool (enable), 0 disables and frees the pool.
+ *   names/total_ms/launches: arrays of length max_kernels; returns the number
+ *   of distinct kernels written, or -1 on error.
+ */
+sf_status sf_timing_enable(int max_pairs);
+int sf_timing_collect(const char **names, double *total_ms, int *launches, int max_kernels);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SF_H */

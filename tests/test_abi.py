@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes its workspaces, and rejects invalid arguments on the
+host before anything is enqueued (attention-gym "Linear Attention": unsupported
+choices fail instead of falling back)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_linear_recurrence_amd as sf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sf.h")
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sf.LIB_PATH):
+        from chunked_linear_recurrence_amd import build
+        build.build(verbose=False)
+    return sf.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sf_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("sf_gdn_chunk_fwd", "sf_segment_summary", "sf_state_scan", "sf_gla_chunk_fwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"{n} is declared in sf.h but not exported"
+    assert set(names) == set(sf.EXPORTED)
+
+
+def test_version(L):
+    assert sf.version().startswith("sf ") and "gfx950" in sf.version()
+
+
+def test_workspace_sizes(L):
+    rec = 2 * 64 * 64 * 2 + 1024  # bf16 factor record
+    dense = L.sf_gdn_chunk_fwd_workspace(sf.SF_BF16, 2, 4096, 16, 128, 128, 2, 0)
+    assert dense == 2 * 64 * 16 * rec
+    # packed: chunk offsets (N+1 ints) and table (cap int2), each 256-aligned, then factors
+    N, T, H = 9, 32768, 32
+    cap = (T + 63) // 64 + N
+    al = lambda x: (x + 255) // 256 * 256
+    packed = L.sf_gdn_chunk_fwd_workspace(sf.SF_BF16, 1, T, H, 128, 128, N, 1)
+    assert packed == al(4 * (N + 1)) + al(8 * cap) + al(cap * H * rec)
+    assert L.sf_gdn_chunk_fwd_workspace(sf.SF_F32, 1, 256, 2, 64, 64, 1, 0) == 4 * 2 * (2 * 64 * 64 * 4 + 1024)
+    assert L.sf_segment_summary_workspace(sf.SF_KIND_GLA, sf.SF_BF16, 16, 2048, 64, 128, 64, 128) == 0
+    assert L.sf_gdn_chunk_fwd_workspace(7, 1, 1, 1, 64, 64, 1, 0) == 0
+
+
+def gdn_call(L, **kw):
+    a = dict(dt=sf.SF_BF16, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, N=2, B=2, T=64,
+             H=4, HK=4, K=128, V=128, scale=0.1, out=FAKE, ht=None, ws=FAKE * 256, wsb=1 << 40, s=None)
+    a.update(kw)
+    st = L.sf_gdn_chunk_fwd(a["dt"], a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["N"], a["B"],
+                            a["T"], a["H"], a["HK"], a["K"], a["V"], a["scale"], a["out"], a["ht"], a["ws"],
+                            a["wsb"], a["s"])
+    return st, L.sf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(HK=3), sf.SF_ERR_INVALID, "divide"),
+    (dict(q=None), sf.SF_ERR_INVALID, "NULL"),
+    (dict(beta=None), sf.SF_ERR_INVALID, "NULL"),
+    (dict(dt=5), sf.SF_ERR_INVALID, "dtype"),
+    (dict(N=3), sf.SF_ERR_INVALID, "N (3) must equal B"),
+    (dict(cu=FAKE, B=2), sf.SF_ERR_INVALID, "batch-one"),
+    (dict(K=96, V=96), sf.SF_ERR_UNSUPPORTED, "K == V"),
+    (dict(K=128, V=64), sf.SF_ERR_UNSUPPORTED, "K == V"),
+    (dict(wsb=16), sf.SF_ERR_WORKSPACE, "smaller"),
+    (dict(ws=None), sf.SF_ERR_WORKSPACE, "smaller"),
+    (dict(ws=FAKE * 256 + 8), sf.SF_ERR_INVALID, "aligned"),
+    (dict(T=1 << 20, H=128, HK=128, B=2, N=2), sf.SF_ERR_UNSUPPORTED, "2^31"),
+    (dict(H=-1), sf.SF_ERR_INVALID, "positive"),
+])
+def test_gdn_rejects_invalid_arguments(L, kw, status, msg):
+    st, err = gdn_call(L, **kw)
+    assert st == status, err
+    assert msg in err
+
+
+def test_gla_rejects_invalid_arguments(L):
+    call = lambda dt=sf.SF_BF16, K=128, V=64, chunk=128, H=64, HK=8: L.sf_gla_chunk_fwd(
+        dt, FAKE, FAKE, FAKE, FAKE, None, None, 2, 2, 128, H, HK, K, V, chunk, 1.0, FAKE, None, None)
+    assert call(chunk=32) == sf.SF_ERR_UNSUPPORTED
+    assert call(dt=sf.SF_F32, chunk=128) == sf.SF_ERR_UNSUPPORTED
+    assert call(K=96) == sf.SF_ERR_UNSUPPORTED
+    assert call(HK=7) == sf.SF_ERR_INVALID
+
+
+def test_summary_and_scan_reject_invalid_arguments(L):
+    st = L.sf_segment_summary(sf.SF_KIND_GDN, sf.SF_BF16, FAKE, FAKE, FAKE, None, 16, 256, 4, 4, 128, 128, 64,
+                              FAKE, FAKE, FAKE * 256, 1 << 40, None)
+    assert st == sf.SF_ERR_INVALID and "beta" in L.sf_last_error().decode()
+    st = L.sf_segment_summary(sf.SF_KIND_GDN, sf.SF_BF16, FAKE, FAKE, FAKE, FAKE, 16, 256, 4, 4, 128, 128, 128,
+                              FAKE, FAKE, FAKE * 256, 1 << 40, None)
+    assert st == sf.SF_ERR_UNSUPPORTED
+    st = L.sf_segment_summary(9, sf.SF_BF16, FAKE, FAKE, FAKE, FAKE, 16, 256, 4, 4, 128, 128, 64,
+                              FAKE, FAKE, FAKE * 256, 1 << 40, None)
+    assert st == sf.SF_ERR_INVALID
+    st = L.sf_state_scan(sf.SF_KIND_GDN, FAKE, FAKE, None, 1, 4, 4, 96, 128, FAKE, None, None)
+    assert st == sf.SF_ERR_UNSUPPORTED
+    st = L.sf_state_scan(sf.SF_KIND_GDN, None, FAKE, None, 1, 4, 4, 128, 128, FAKE, None, None)
+    assert st == sf.SF_ERR_INVALID
+    st = L.sf_state_scan(3, FAKE, FAKE, None, 1, 4, 4, 128, 128, FAKE, None, None)
+    assert st == sf.SF_ERR_INVALID
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 64, 2, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sf.gdn_chunk_fwd(q, q, q, torch.zeros(1, 64, 2), torch.zeros(1, 64, 2))
+
+
+def test_segment_view_indexing():
+    """Row s = b*n_seg + j of the segment view covers tokens [j*L, (j+1)*L) of batch row b."""
+    import torch
+    B, T, n_seg = 3, 48, 4
+    x = torch.arange(B * T * 2).view(B, T, 2)
+    sv = sf.segment_view(x, n_seg)
+    L = T // n_seg
+    for b in range(B):
+        for j in range(n_seg):
+            assert torch.equal(sv[b * n_seg + j], x[b, j * L:(j + 1) * L])
+            assert sv[b * n_seg + j].data_ptr() == x[b, j * L].data_ptr()

@@ -1,0 +1,391 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (from the statement of the problem): float32 inputs, max |x - oracle|
+<= 1e-4 on outputs and final states; bf16 inputs with float32 state,
+rel_rms(x, oracle) = ||x - oracle||_2 / ||oracle||_2 <= 2e-2 per tensor over the
+active rows. Integer work (chunk table, segment indexing) and the packing
+invariants are bit-exact.
+
+Full-size configurations run the GPU exactly as bench.py does and compare every
+sequence of a sample of heads against the oracle (each (sequence, head) chain is
+independent, so the sample is exact for those heads).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_linear_recurrence_amd as sf
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+FP32_ATOL = 1e-4
+BF16_RTOL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_rms(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def maxabs(x, ref):
+    return float(np.max(np.abs(np.asarray(x, np.float64) - ref))) if np.size(ref) else 0.0
+
+
+def f32(t):
+    return None if t is None else t.detach().float().cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sf.lib()
+    return torch.device("cuda:0")
+
+
+def cuda(t, dev):
+    return None if t is None else t.to(dev).contiguous()
+
+
+def heads_subset(w, heads):
+    """Slice a workload's tensors to the given value heads (q/k follow their groups)."""
+    grp = w.H // w.HK
+    groups = sorted({h // grp for h in heads})
+    assert all(h // grp in groups for h in heads)
+    # keep whole groups so the grouping stays H/HK
+    hs = [g * grp + i for g in groups for i in range(grp)]
+    sub = lambda x, idx: None if x is None else x[:, :, idx]
+    return dict(q=f32(sub(w.q, groups)), k=f32(sub(w.k, groups)), v=f32(sub(w.v, hs)), g=f32(sub(w.g, hs)),
+                beta=f32(sub(w.beta, hs)), h0=None if w.h0 is None else f32(w.h0[:, hs]), hs=hs)
+
+
+def check_bf16(name, o, ro, ht, rh):
+    eo, eh = rel_rms(o, ro), rel_rms(ht, rh)
+    say(f"  {name}: rel_rms(o)={eo:.3e} rel_rms(ht)={eh:.3e}")
+    assert eo <= BF16_RTOL and eh <= BF16_RTOL, (name, eo, eh)
+
+
+# ---------------------------------------------------------------------------
+# Gated Delta Rule
+# ---------------------------------------------------------------------------
+
+def test_tiny_gdn_fp32(dev, oracle):
+    say("case: tiny GDN fp32 B=1 T=256 H=2 K=V=64")
+    w = wl.tiny_gdn()
+    o, ht = sf.gdn_chunk_fwd(cuda(w.q, dev), cuda(w.k, dev), cuda(w.v, dev), cuda(w.g, dev), cuda(w.beta, dev),
+                             scale=w.scale, output_final_state=True)
+    ro, rh = oracle.gdn_forward(f32(w.q), f32(w.k), f32(w.v), f32(w.g), f32(w.beta), scale=w.scale)
+    eo, eh = maxabs(f32(o), ro), maxabs(f32(ht), rh)
+    say(f"  max|o-ref|={eo:.3e} max|ht-ref|={eh:.3e}")
+    assert eo <= FP32_ATOL and eh <= FP32_ATOL
+
+
+@pytest.mark.parametrize("T,D,HK,B", [(1, 64, 2, 2), (63, 64, 1, 2), (64, 128, 2, 1), (65, 64, 2, 2),
+                                      (200, 128, 1, 2), (333, 64, 2, 1)])
+def test_gdn_fp32_sweep(dev, oracle, T, D, HK, B):
+    say(f"case: GDN fp32 T={T} K=V={D} H=2 HK={HK} B={B} with h0")
+    d = wl.delta_rule_inputs(B=B, T=T, H=2, HK=HK, K=D, V=D, dtype=torch.float32, seed=T + D, h0_std=0.5)
+    o, ht = sf.gdn_chunk_fwd(cuda(d["q"], dev), cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev),
+                             cuda(d["beta"], dev), cuda(d["h0"], dev), scale=0.3, output_final_state=True)
+    ro, rh = oracle.gdn_forward(f32(d["q"]), f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(d["beta"]), f32(d["h0"]),
+                                scale=0.3)
+    eo, eh = maxabs(f32(o), ro), maxabs(f32(ht), rh)
+    say(f"  max|o-ref|={eo:.3e} max|ht-ref|={eh:.3e}")
+    assert eo <= FP32_ATOL and eh <= FP32_ATOL
+
+
+@pytest.mark.parametrize("T,D,shift", [(600, 128, 2.0), (257, 64, 0.0), (128, 128, -3.0)])
+def test_gdn_bf16_reduced(dev, oracle, T, D, shift):
+    say(f"case: GDN bf16 B=2 T={T} H=4 K=V={D} gate shift {shift} h0 N(0,0.02)")
+    d = wl.delta_rule_inputs(B=2, T=T, H=4, K=D, V=D, dtype=torch.bfloat16, seed=11 + T, gate_shift=shift,
+                             h0_std=0.02)
+    o, ht = sf.gdn_chunk_fwd(cuda(d["q"], dev), cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev),
+                             cuda(d["beta"], dev), cuda(d["h0"], dev), output_final_state=True)
+    ro, rh = oracle.gdn_forward(f32(d["q"]), f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(d["beta"]), f32(d["h0"]))
+    check_bf16("reduced", f32(o), ro, f32(ht), rh)
+
+
+def test_dense_gdn_full_size(dev, oracle):
+    say("case: dense GDN prefill B=2 T=4096 H=16 K=V=128 bf16 (full size, heads 0, 7, 15 vs oracle)")
+    w = wl.dense_gdn()
+    o, ht = sf.gdn_chunk_fwd(cuda(w.q, dev), cuda(w.k, dev), cuda(w.v, dev), cuda(w.g, dev), cuda(w.beta, dev),
+                             cuda(w.h0, dev), scale=w.scale, output_final_state=True)
+    torch.cuda.synchronize()
+    o, ht = f32(o), f32(ht)
+    assert np.isfinite(o).all() and np.isfinite(ht).all()
+    heads = [0, 7, 15]
+    s = heads_subset(w, heads)
+    ro, rh = oracle.gdn_forward(s["q"], s["k"], s["v"], s["g"], s["beta"], s["h0"], scale=w.scale)
+    check_bf16("dense heads", o[:, :, s["hs"]], ro, ht[:, s["hs"]], rh)
+
+
+def host_chunk_table(cu, C=64):
+    lens = np.diff(cu)
+    nch = (lens + C - 1) // C
+    off = np.concatenate([[0], np.cumsum(nch)]).astype(np.int32)
+    table = [(n, c) for n in range(len(lens)) for c in range(nch[n])]
+    return off, table
+
+
+def test_varlen_gdn_full_size(dev, oracle):
+    w = wl.varlen_gdn()
+    lens = w.meta["lengths"]
+    say(f"case: packed varlen GDN T=32768 H=32 K=V=128 bf16 lengths={lens}")
+    cu = cuda(w.cu_seqlens, dev)
+    h0 = torch.randn(w.N, w.H, w.V, w.K, generator=torch.Generator().manual_seed(5)) * 0.02
+    q, k, v, g, beta = (cuda(x, dev) for x in (w.q, w.k, w.v, w.g, w.beta))
+    o, ht = sf.gdn_chunk_fwd(q, k, v, g, beta, cuda(h0, dev), cu_seqlens=cu, scale=w.scale, output_final_state=True)
+    torch.cuda.synchronize()
+    o, ht = f32(o), f32(ht)
+    heads = [0, 13, 31]
+    s = heads_subset(w, heads)
+    ro, rh = oracle.gdn_forward(s["q"], s["k"], s["v"], s["g"], s["beta"], f32(h0[:, s["hs"]]),
+                                cu_seqlens=w.cu_seqlens.numpy(), scale=w.scale)
+    end = int(w.cu_seqlens[-1])
+    check_bf16("varlen heads", o[:, :end, s["hs"]], ro[:, :end], ht[:, s["hs"]], rh)
+    # an empty sequence returns its initial state bitwise
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(ht[n], f32(h0[n])), "empty sequence must pass its state through"
+
+
+def test_varlen_chunk_table_is_exact(dev):
+    say("case: device chunk table vs host table (bit-exact)")
+    lens = [0, 5, 64, 0, 130, 1, 63, 700, 0]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1]) + 37
+    N, H = len(lens), 2
+    d = wl.delta_rule_inputs(B=1, T=T, H=H, K=64, V=64, dtype=torch.bfloat16, seed=3)
+    L = sf.lib()
+    nbytes = L.sf_gdn_chunk_fwd_workspace(sf.SF_BF16, 1, T, H, 64, 64, N, 1)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    q, k, v, g, beta = (cuda(d[x], dev) for x in ("q", "k", "v", "g", "beta"))
+    out = torch.empty_like(v)
+    cu_d = torch.from_numpy(cu).to(dev)
+    import ctypes
+    st = L.sf_gdn_chunk_fwd(sf.SF_BF16, *(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, g, beta)), None,
+                            ctypes.c_void_p(cu_d.data_ptr()), N, 1, T, H, H, 64, 64, 0.125,
+                            ctypes.c_void_p(out.data_ptr()), None, ctypes.c_void_p(ws.data_ptr()), nbytes,
+                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, L.sf_last_error()
+    torch.cuda.synchronize()
+    cap = (T + 63) // 64 + N
+    raw = ws.cpu().numpy()
+    off_dev = raw[:4 * (N + 1)].view(np.int32)
+    tab_base = (4 * (N + 1) + 255) // 256 * 256
+    tab_dev = raw[tab_base:tab_base + 8 * cap].view(np.int32).reshape(cap, 2)
+    off, table = host_chunk_table(cu)
+    assert np.array_equal(off_dev, off)
+    assert [tuple(x) for x in tab_dev[:len(table)]] == table
+    assert (tab_dev[len(table):, 0] == -1).all()
+
+
+def test_packed_equals_alone_bitwise(dev):
+    say("case: packed sequences equal separate dense calls bitwise; rows past the end untouched")
+    lens = [130, 0, 64, 7, 300]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1]) + 20
+    d = wl.delta_rule_inputs(B=1, T=T, H=4, K=128, V=128, dtype=torch.bfloat16, seed=21, gate_shift=-1.0)
+    h0 = torch.randn(len(lens), 4, 128, 128, generator=torch.Generator().manual_seed(1)) * 0.1
+    q, k, v, g, beta = (cuda(d[x], dev) for x in ("q", "k", "v", "g", "beta"))
+    h0d = cuda(h0, dev)
+    o, ht = sf.gdn_chunk_fwd(q, k, v, g, beta, h0d, cu_seqlens=torch.from_numpy(cu).to(dev),
+                             output_final_state=True)
+    for n, L in enumerate(lens):
+        a, b_ = int(cu[n]), int(cu[n + 1])
+        if L == 0:
+            assert torch.equal(ht[n], h0d[n])
+            continue
+        sl = lambda x: x[:, a:b_].contiguous()
+        o1, h1 = sf.gdn_chunk_fwd(sl(q), sl(k), sl(v), sl(g), sl(beta), h0d[n:n + 1].contiguous(),
+                                  output_final_state=True)
+        assert torch.equal(o[:, a:b_], o1), f"sequence {n} differs from its separate run"
+        assert torch.equal(ht[n], h1[0])
+    # GLA: same packing invariant
+    o2, h2 = sf.gla_chunk_fwd(q, k, v, g, h0d, cu_seqlens=torch.from_numpy(cu).to(dev), chunk=64,
+                              output_final_state=True)
+    for n, L in enumerate(lens):
+        a, b_ = int(cu[n]), int(cu[n + 1])
+        if L == 0:
+            assert torch.equal(h2[n], h0d[n])
+            continue
+        sl = lambda x: x[:, a:b_].contiguous()
+        o3, h3 = sf.gla_chunk_fwd(sl(q), sl(k), sl(v), sl(g), h0d[n:n + 1].contiguous(), chunk=64,
+                                  output_final_state=True)
+        assert torch.equal(o2[:, a:b_], o3)
+        assert torch.equal(h2[n], h3[0])
+
+
+def test_rows_past_terminal_offset_are_not_written(dev):
+    say("case: output rows past cu_seqlens[-1] keep their contents")
+    import ctypes
+    lens = [70, 30]
+    cu = torch.tensor([0, 70, 100], dtype=torch.int32)
+    T, H = 160, 2
+    d = wl.delta_rule_inputs(B=1, T=T, H=H, K=64, V=64, dtype=torch.bfloat16, seed=4)
+    q, k, v, g, beta = (cuda(d[x], dev) for x in ("q", "k", "v", "g", "beta"))
+    for kind in ("gdn", "gla"):
+        out = torch.full_like(v, 3.0)
+        L = sf.lib()
+        cu_d = cu.to(dev)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if kind == "gdn":
+            nb = L.sf_gdn_chunk_fwd_workspace(sf.SF_BF16, 1, T, H, 64, 64, 2, 1)
+            ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+            st = L.sf_gdn_chunk_fwd(sf.SF_BF16, P(q), P(k), P(v), P(g), P(beta), None, P(cu_d), 2, 1, T, H, H, 64, 64,
+                                    0.125, P(out), None, P(ws), nb, s)
+        else:
+            st = L.sf_gla_chunk_fwd(sf.SF_BF16, P(q), P(k), P(v), P(g), None, P(cu_d), 2, 1, T, H, H, 64, 64, 64, 1.0,
+                                    P(out), None, s)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert (out[:, 100:] == 3.0).all()
+        assert not (out[:, :100] == 3.0).all()
+
+
+def test_resume_from_final_state_is_bitwise(dev):
+    say("case: one call on [0,T) equals [0,t) then [t,T) with the state passed (t a multiple of 64)")
+    d = wl.delta_rule_inputs(B=2, T=448, H=2, K=128, V=128, dtype=torch.bfloat16, seed=9, gate_shift=-2.0,
+                             h0_std=0.1)
+    x = {n: cuda(d[n], dev) for n in ("q", "k", "v", "g", "beta", "h0")}
+    o, ht = sf.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], output_final_state=True)
+    t = 192
+    a = {n: x[n][:, :t].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    b = {n: x[n][:, t:].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    o1, h1 = sf.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], x["h0"], output_final_state=True)
+    o2, h2 = sf.gdn_chunk_fwd(b["q"], b["k"], b["v"], b["g"], b["beta"], h1, output_final_state=True)
+    assert torch.equal(o[:, :t], o1) and torch.equal(o[:, t:], o2) and torch.equal(ht, h2)
+
+
+# ---------------------------------------------------------------------------
+# Summaries and the scan
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.bfloat16, 128), (torch.bfloat16, 64)])
+def test_gdn_summary_vs_oracle(dev, oracle, dtype, D):
+    say(f"case: GDN summary {dtype} K=V={D}, rows with tails")
+    R, L = 3, 200
+    d = wl.delta_rule_inputs(B=R, T=L, H=2, K=D, V=D, dtype=dtype, seed=D + 3, gate_shift=-5.0,
+                             beta_scale=0.3)
+    M, E = sf.segment_summary("gdn", cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev), cuda(d["beta"], dev))
+    rM, rE = oracle.gdn_summary(f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(d["beta"]))
+    assert np.abs(rM).max() > 0.1  # the transition is far from zero here
+    if dtype == torch.float32:
+        eM, eE = maxabs(f32(M), rM), maxabs(f32(E), rE)
+        say(f"  max|M-ref|={eM:.3e} max|S_ext-ref|={eE:.3e}")
+        assert eM <= FP32_ATOL and eE <= FP32_ATOL
+    else:
+        eM, eE = rel_rms(f32(M), rM), rel_rms(f32(E), rE)
+        say(f"  rel_rms(M)={eM:.3e} rel_rms(S_ext)={eE:.3e}")
+        assert eM <= BF16_RTOL and eE <= BF16_RTOL
+
+
+@pytest.mark.parametrize("dtype,chunk", [(torch.float32, 64), (torch.bfloat16, 128), (torch.bfloat16, 64)])
+def test_gla_summary_vs_oracle(dev, oracle, dtype, chunk):
+    say(f"case: GLA summary {dtype} chunk {chunk}")
+    d = wl.scalar_gate_inputs(B=3, T=300, H=4, HK=2, K=128, V=64, dtype=dtype, seed=chunk)
+    a, E = sf.segment_summary("gla", cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev), chunk=chunk)
+    ra, rE = oracle.gla_summary(f32(d["k"]), f32(d["v"]), f32(d["g"]))
+    ea = float(np.max(np.abs(f32(a) - ra) / ra))
+    say(f"  max rel|a-ref|={ea:.3e} rel_rms(S_ext)={rel_rms(f32(E), rE):.3e}")
+    assert ea <= 1e-4
+    if dtype == torch.float32:
+        assert maxabs(f32(E), rE) <= FP32_ATOL * max(1.0, np.abs(rE).max())
+    else:
+        assert rel_rms(f32(E), rE) <= BF16_RTOL
+
+
+@pytest.mark.parametrize("kind,D", [("gdn", 128), ("gdn", 64), ("gla", 128)])
+def test_state_scan_vs_oracle(dev, oracle, kind, D):
+    say(f"case: state scan {kind} K=V={D}")
+    B, n_seg, H = 2, 5, 3
+    rng = np.random.default_rng(D)
+    if kind == "gdn":
+        M = (rng.standard_normal((B * n_seg, H, D, D)) / np.sqrt(D)).astype(np.float32)
+    else:
+        M = rng.uniform(0.2, 1.0, (B * n_seg, H)).astype(np.float32)
+    E = rng.standard_normal((B * n_seg, H, D, D)).astype(np.float32)
+    h0 = rng.standard_normal((B, H, D, D)).astype(np.float32)
+    S_in, S_f = sf.state_scan(kind, torch.from_numpy(M).to(dev), torch.from_numpy(E).to(dev),
+                              torch.from_numpy(h0).to(dev), B=B, n_seg=n_seg)
+    rS, rF = oracle.state_scan(kind, M, E, h0, B=B, n_seg=n_seg)
+    e1, e2 = maxabs(f32(S_in), rS), maxabs(f32(S_f), rF)
+    say(f"  max|S_in-ref|={e1:.3e} max|S_final-ref|={e2:.3e} (|ref| max {np.abs(rF).max():.2f})")
+    assert np.array_equal(f32(S_in)[0::n_seg], h0)  # exclusive: first segment starts at h0 exactly
+    assert e1 <= 1e-4 * max(1.0, np.abs(rS).max()) and e2 <= 1e-4 * max(1.0, np.abs(rF).max())
+
+
+def test_segmented_gdn_nonzero_transitions(dev, oracle):
+    say("case: segmented GDN B=1 T=4096 H=4 K=V=64, 16 segments of 256, slow gates (M far from 0)")
+    d = wl.delta_rule_inputs(B=1, T=4096, H=4, K=64, V=64, dtype=torch.bfloat16, seed=77, gate_shift=-6.0,
+                             beta_scale=0.1, h0_std=0.1)
+    x = {n: cuda(d[n], dev) for n in ("q", "k", "v", "g", "beta", "h0")}
+    o, hf = sf.segmented_gdn_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], 16, x["h0"], output_final_state=True)
+    ro, rh = oracle.gdn_forward(f32(d["q"]), f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(d["beta"]), f32(d["h0"]))
+    check_bf16("segmented vs unsegmented oracle", f32(o), ro, f32(hf), rh)
+    M, _ = sf.segment_summary("gdn", *(sf.segment_view(x[n], 16) for n in ("k", "v", "g", "beta")))
+    assert f32(M).std() > 0.05
+
+
+# ---------------------------------------------------------------------------
+# Scalar-gated linear attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,chunk,T,HK", [(torch.float32, 64, 200, 2), (torch.bfloat16, 64, 129, 1),
+                                              (torch.bfloat16, 128, 300, 2), (torch.bfloat16, 128, 1, 4)])
+def test_gla_vs_oracle(dev, oracle, dtype, chunk, T, HK):
+    say(f"case: GLA {dtype} chunk {chunk} T={T} H=4 HK={HK} K=128 V=64 with h0")
+    d = wl.scalar_gate_inputs(B=2, T=T, H=4, HK=HK, K=128, V=64, dtype=dtype, seed=T)
+    h0 = (torch.randn(2, 4, 64, 128, generator=torch.Generator().manual_seed(T))).float()
+    o, ht = sf.gla_chunk_fwd(cuda(d["q"], dev), cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev),
+                             cuda(h0, dev), chunk=chunk, scale=0.5, output_final_state=True)
+    ro, rh = oracle.gla_forward(f32(d["q"]), f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(h0), scale=0.5)
+    if dtype == torch.float32:
+        # unnormalised q/k: outputs reach ~1e2, so the float32 bound scales with them
+        eo, eh = maxabs(f32(o), ro), maxabs(f32(ht), rh)
+        so, sh = max(1.0, np.abs(ro).max()), max(1.0, np.abs(rh).max())
+        say(f"  max|o-ref|/max(1,|ref|)={eo / so:.3e} max|ht-ref|/max(1,|ref|)={eh / sh:.3e}")
+        assert eo <= FP32_ATOL * so and eh <= FP32_ATOL * sh
+    else:
+        check_bf16("gla", f32(o), ro, f32(ht), rh)
+
+
+def test_ssd_gla_full_size_segmented(dev, oracle):
+    say("case: SSD-shaped GLA B=2 T=16384 H=64 HK=8 K=128 V=64 chunk 128, 8 segments per row (full size)")
+    w = wl.ssd_gla()
+    x = {n: cuda(getattr(w, n), dev) for n in ("q", "k", "v", "g")}
+    o, hf = sf.segmented_gla_fwd(x["q"], x["k"], x["v"], x["g"], w.n_seg, scale=w.scale, chunk=w.chunk,
+                                 output_final_state=True)
+    ou, hu = sf.gla_chunk_fwd(x["q"], x["k"], x["v"], x["g"], scale=w.scale, chunk=w.chunk,
+                              output_final_state=True)
+    torch.cuda.synchronize()
+    heads = [0, 1, 37, 63]
+    s = heads_subset(w, heads)
+    ro, rh = oracle.gla_forward(s["q"], s["k"], s["v"], s["g"], scale=w.scale)
+    hs = s["hs"]
+    check_bf16("segmented", f32(o)[:, :, hs], ro, f32(hf)[:, hs], rh)
+    check_bf16("unsegmented", f32(ou)[:, :, hs], ro, f32(hu)[:, hs], rh)
+
+
+def test_long_gdn_full_size_segmented(dev, oracle):
+    say("case: long GDN B=1 T=262144 H=16 K=V=128 bf16, 16 segments of 16384 (full size; head 3 vs oracle)")
+    w = wl.long_gdn()
+    x = {n: cuda(getattr(w, n), dev) for n in ("q", "k", "v", "g", "beta")}
+    o, hf = sf.segmented_gdn_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], w.n_seg, scale=w.scale,
+                                 output_final_state=True)
+    torch.cuda.synchronize()
+    say("  GPU done; oracle on head 3 over 262144 tokens")
+    s = heads_subset(w, [3])
+    ro, rh = oracle.gdn_forward(s["q"], s["k"], s["v"], s["g"], s["beta"], scale=w.scale)
+    hs = s["hs"]
+    check_bf16("segmented head 3", f32(o[:, :, hs]), ro, f32(hf[:, hs]), rh)
