@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Throughput of the Gated Delta Rule chunk forward on one MI355X.
+
+Workload (default): dense GDN prefill, B=2, T=4096, H=16, K=V=128, bf16 q/k/v,
+float32 gate/beta/state, chunk 64, initial state N(0, 0.02) -- the configuration
+the headline metric is quoted on. One step is one full sf_gdn_chunk_fwd call
+(gate cumsum, K K^T / Q K^T, blocked solve, state transition, output, final
+state) on one batch of seeded synthetic inputs already resident in HBM. Several
+input sets (--rotate, default 3, 310 MB > the 256 MB last-level cache) are
+cycled so consecutive steps cannot be served from the cache.
+
+Prints one JSON line with tokens/s, the roofline fraction of the dominant
+kernel (its average launch time from HIP events recorded on the launch stream
+inside the timed region) and the float64 oracle timed on the host cores on the
+same workload (cpu_baseline; a reported baseline, not a target).
+
+Other workloads (--workload varlen_gdn | long_gdn | ssd_gla | tiny_gdn) are for
+measurement only; the headline line is the default one.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN chunk-fwd tokens/s (bf16, K=V=128) + % of MFMA/HBM roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, kernel):
+    """Bytes a kernel must move by definition of the computation (no intermediates).
+
+    Delta rule, per token and value head: q, k, v and o in the element type
+    (HK/H of q and k per value head), plus gate and beta in float32; per
+    (sequence, head): the initial state read (when given) and the final state
+    written, V*K float32 each."""
+    eb = w.q.element_size()
+    tok = w.tokens
+    qk = 2 * tok * w.HK * w.K * eb
+    vo = 2 * tok * w.H * w.V * eb
+    gb = tok * w.H * 4 * (2 if w.beta is not None else 1)
+    states = w.N * w.H * w.V * w.K * 4 * (1 + (w.h0 is not None))
+    if kernel in ("gdn_chain", "gla_chain"):
+        return qk + vo + states
+    if kernel == "gdn_prep":
+        return qk + gb
+    return qk + vo + gb + states      # whole path
+
+
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (scaled by a copy-kernel
+    calibration) from profiles/<kernel>_<workload>_traffic.txt, or None when absent or when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "chunked_linear_recurrence_amd", "csrc", kv.get("source", "gdn.hip"))
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != kv.get("source_sha256_16"):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_sets(w, dev, rotate):
+    import torch
+    sets = []
+    for r in range(rotate):
+        s = {}
+        for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens"):
+            t = getattr(w, n)
+            s[n] = None if t is None else t.to(dev).contiguous()
+        sets.append(s)
+    return sets
+
+
+def step_fn(w):
+    import chunked_linear_recurrence_amd as sf
+    if w.name in ("dense_gdn", "tiny_gdn", "varlen_gdn"):
+        def step(s):
+            return sf.gdn_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["h0"], cu_seqlens=s["cu_seqlens"],
+                                    scale=w.scale, output_final_state=True)
+    elif w.name == "long_gdn":
+        def step(s):
+            return sf.segmented_gdn_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], w.n_seg, scale=w.scale,
+                                        output_final_state=True)
+    elif w.name == "ssd_gla":
+        def step(s):
+            return sf.segmented_gla_fwd(s["q"], s["k"], s["v"], s["g"], w.n_seg, scale=w.scale, chunk=w.chunk,
+                                        output_final_state=True)
+    else:
+        raise ValueError(w.name)
+    return step
+
+
+def cpu_baseline(w):
+    """The float64 oracle, as it stands, on the host cores: one pass over the workload."""
+    import oracle
+    import workloads as wl
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = min(threads, len(os.sched_getaffinity(0)))
+    f = wl.to_f32
+    args = dict(q=f(w.q), k=f(w.k), v=f(w.v), g=f(w.g))
+    log(f"cpu_baseline: float64 oracle on {threads} threads ...")
+    t0 = time.perf_counter()
+    if w.kind == "gdn":
+        oracle.gdn_forward(args["q"], args["k"], args["v"], args["g"], f(w.beta), f(w.h0),
+                           cu_seqlens=None if w.cu_seqlens is None else w.cu_seqlens.numpy(), scale=w.scale,
+                           threads=threads)
+    else:
+        oracle.gla_forward(args["q"], args["k"], args["v"], args["g"], scale=w.scale, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": w.tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {w.name} workload ({w.tokens} tokens x {w.H} heads), one float64 pass, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=3, help="input sets cycled through (cache defeat)")
+    ap.add_argument("--workload", default="dense_gdn",
+                    choices=["dense_gdn", "tiny_gdn", "varlen_gdn", "long_gdn", "ssd_gla"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-events", action="store_true", help="do not bracket launches with HIP events")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (one GPU's share of the "
+              "work is what it runs); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_linear_recurrence_amd as sf
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    sf.lib()
+
+    log(f"bench: generating {args.workload} ...")
+    w = wl.CONFIGS[args.workload]()
+    sets = make_sets(w, dev, max(1, args.rotate))
+    step = step_fn(w)
+
+    log(f"bench: warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    if not args.no_events:
+        sf.timing_enable(64 * (args.steps + 1))
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kt = sf.timing_collect() if not args.no_events else {}
+    if not args.no_events:
+        sf.timing_enable(0)
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = w.tokens * args.steps / elapsed
+    kernels = {k: {"launches": n, "avg_us": 1e3 * ms / n} for k, (n, ms) in kt.items()}
+    log("bench: per-kernel " + json.dumps(kernels))
+
+    roof = None
+    if kernels:
+        dom = max(kt, key=lambda k: kt[k][1])
+        avg_s = kt[dom][1] / kt[dom][0] / 1e3
+        ab = algorithmic_bytes(w, dom)
+        ach = ab / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(dom, w.name),
+                "kernel": dom, "avg_us": round(avg_s * 1e6, 2), "algorithmic_bytes": ab}
+    path_bytes = algorithmic_bytes(w, "path")
+    path_ach = path_bytes / (elapsed / args.steps) / 1e9
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.q.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HK": w.HK, "K": w.K, "V": w.V,
+                   "chunk": w.chunk, "n_seg": w.n_seg, "tokens": w.tokens, "rotate": len(sets)},
+        "roofline": roof,
+        "path_roofline": {"bound": "hbm", "achieved": round(path_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(path_ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": path_bytes},
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -248,12 +248,28 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const ST* __restrict__ q,
 template <typename ST>
 __device__ __forceinline__ ST unit_elem(const u128& u, int e) {
     if constexpr (sizeof(ST) == 2) {
-        const uint32_t w = (&u.x)[e >> 1];
+        const uint32_t w = u[e >> 1];
         return (ST)((e & 1) ? (w >> 16) : (w & 0xffffu));
     } else {
-        return __uint_as_float((&u.x)[e]);
+        return __uint_as_float(u[e]);
     }
 }
+
+template <typename ST, int KD, bool SUMMARY>
+struct ChainSmem {
+    static constexpr int E = 16 / sizeof(ST);
+    static constexpr int LDK = KD + E, LD = GC + E;
+    // one staging buffer: K [64][LDK], K^T [KD][LD], T [64][LD], coef float[256],
+    // and (forward only) Q [64][LDK], P [64][LD]
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_KT = OFF_K + GC * LDK * (int)sizeof(ST);
+    static constexpr int OFF_T = OFF_KT + KD * LD * (int)sizeof(ST);
+    static constexpr int OFF_C = OFF_T + GC * LD * (int)sizeof(ST);
+    static constexpr int OFF_Q = OFF_C + 256 * 4;
+    static constexpr int OFF_P = OFF_Q + (SUMMARY ? 0 : GC * LDK * (int)sizeof(ST));
+    static constexpr int BYTES = OFF_P + (SUMMARY ? 0 : GC * LD * (int)sizeof(ST));
+    static constexpr int NBUF = 2 * BYTES <= 160 * 1024 - 1024 ? 2 : 1;
+};
 
 template <typename ST, int KD, int NW, bool SUMMARY>
 __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
@@ -261,25 +277,19 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
     const float* __restrict__ h0, const int32_t* __restrict__ cu, const int* __restrict__ chunk_off,
     const uint8_t* __restrict__ fac, int T, int H, int HK, int V, int n_seq, int nc, int nvb,
     float scale, ST* __restrict__ out, float* __restrict__ ht, float* __restrict__ Mout) {
-    constexpr int E = 16 / sizeof(ST);
-    constexpr int LDK = KD + E, LD = GC + E;
+    typedef ChainSmem<ST, KD, SUMMARY> SM;
+    constexpr int E = SM::E, LDK = SM::LDK, LD = SM::LD, NBUF = SM::NBUF;
     constexpr int NT = 64 * NW;
     constexpr int KB = KD / 16;
     constexpr int UPR = KD / E;             // units per K/Q row
     constexpr int NUK = GC * UPR;           // units per K (or Q) chunk
     constexpr int NUT = GC * GC / E;        // units per T (or P) block
-    constexpr int PK = (NUK + NT - 1) / NT;
-    constexpr int PT = (NUT + NT - 1) / NT;
-    constexpr int QSZ = SUMMARY ? E : GC * LDK;
-    constexpr int PSZ = SUMMARY ? E : GC * LD;
+    constexpr int PK = NUK / NT;
+    constexpr int PT = NUT / NT;
+    static_assert(NUK % NT == 0 && NUT % NT == 0, "staging units must divide evenly");
     typedef typename Elem<ST>::frag frag;
 
-    __shared__ __align__(16) ST sK[GC * LDK];
-    __shared__ __align__(16) ST sKT[KD * LD];
-    __shared__ __align__(16) ST sQ[QSZ];
-    __shared__ __align__(16) ST sT[GC * LD];
-    __shared__ __align__(16) ST sP[PSZ];
-    __shared__ __align__(16) float sC[256];
+    __shared__ __align__(16) uint8_t smem[NBUF * SM::BYTES];
 
     int chain, vb;
     xcd_split(blockIdx.x, nvb, chain, vb);
@@ -288,6 +298,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int myrow = (vb * NW + wave) * 16 + ln;
     const bool vrow = myrow < V;
+    const int vload_row = vrow ? myrow : 0;
 
     int b, bos, eos, slot0;
     if (cu) {
@@ -318,9 +329,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
         }
     }
 
+    // Staging registers live only within one iteration: loads for chunk c+1
+    // are issued before chunk c's products and written to the other LDS
+    // buffer after them, so their latency hides behind the compute. Loads use
+    // clamped (valid) rows; rows past the chunk end are zeroed on the write.
     u128 rk[PK], rq[PK], rt[PT], rp[PT], rc;
     ST rv[16];
-    auto prefetch = [&](int c) {
+    auto issue = [&](int c) __attribute__((always_inline)) {
         const int t0 = bos + c * GC, L = min(GC, eos - t0);
         const uint8_t* rec = fac + ((size_t)(slot0 + c) * H + h) * rec_bytes;
         const ST* gT = reinterpret_cast<const ST*>(rec);
@@ -329,63 +344,80 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
             const int u = tid + i * NT;
-            rk[i] = rq[i] = u128{0u, 0u, 0u, 0u};
-            if (u < NUK) {
-                const int t = u / UPR, col = (u % UPR) * E;
-                if (t < L) {
-                    const size_t off = ((size_t)(b * T + t0 + t) * HK + hk) * KD + col;
-                    rk[i] = *reinterpret_cast<const u128*>(k + off);
-                    if constexpr (!SUMMARY) rq[i] = *reinterpret_cast<const u128*>(q + off);
-                }
-            }
+            const int t = min(u / UPR, L - 1), col = (u % UPR) * E;
+            const size_t off = ((size_t)(b * T + t0 + t) * HK + hk) * KD + col;
+            rk[i] = *reinterpret_cast<const u128*>(k + off);
+            if constexpr (!SUMMARY) rq[i] = *reinterpret_cast<const u128*>(q + off);
         }
 #pragma unroll
         for (int i = 0; i < PT; ++i) {
             const int u = tid + i * NT;
-            if (u < NUT) {
-                rt[i] = *reinterpret_cast<const u128*>(gT + u * E);
-                if constexpr (!SUMMARY) rp[i] = *reinterpret_cast<const u128*>(gP + u * E);
-            }
+            rt[i] = *reinterpret_cast<const u128*>(gT + u * E);
+            if constexpr (!SUMMARY) rp[i] = *reinterpret_cast<const u128*>(gP + u * E);
         }
-        if (tid < 64) rc = *reinterpret_cast<const u128*>(gC + 4 * tid);
+        rc = *reinterpret_cast<const u128*>(gC + 4 * lane);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int t = 16 * (i >> 2) + 4 * lg + (i & 3);
-            rv[i] = (vrow && t < L) ? v[((size_t)(b * T + t0 + t) * H + h) * V + myrow] : Elem<ST>::from_f(0.f);
+            const int t = min(16 * (i >> 2) + 4 * lg + (i & 3), L - 1);
+            rv[i] = v[((size_t)(b * T + t0 + t) * H + h) * V + vload_row];
         }
     };
-
-    if (nch > 0) prefetch(0);
-    for (int c = 0; c < nch; ++c) {
-        const int t0 = bos + c * GC, L = min(GC, eos - t0);
-        __syncthreads();
-        // registers -> LDS (K natural and transposed, Q, T, P, coefficients)
+    float vv[16];
+    auto commit = [&](int c, int buf) __attribute__((always_inline)) {
+        const int L = min(GC, eos - (bos + c * GC));
+        uint8_t* base = smem + buf * SM::BYTES;
+        ST* sK = reinterpret_cast<ST*>(base + SM::OFF_K);
+        ST* sKT = reinterpret_cast<ST*>(base + SM::OFF_KT);
+        ST* sT = reinterpret_cast<ST*>(base + SM::OFF_T);
+        float* sC = reinterpret_cast<float*>(base + SM::OFF_C);
+        ST* sQ = reinterpret_cast<ST*>(base + SM::OFF_Q);
+        ST* sP = reinterpret_cast<ST*>(base + SM::OFF_P);
+        const u128 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
             const int u = tid + i * NT;
-            if (u < NUK) {
-                const int t = u / UPR, col = (u % UPR) * E;
-                *reinterpret_cast<u128*>(sK + t * LDK + col) = rk[i];
+            const int t = u / UPR, col = (u % UPR) * E;
+            const u128 kv = t < L ? rk[i] : zero;
+            *reinterpret_cast<u128*>(sK + t * LDK + col) = kv;
 #pragma unroll
-                for (int e = 0; e < E; ++e) sKT[(col + e) * LD + t] = unit_elem<ST>(rk[i], e);
-                if constexpr (!SUMMARY) *reinterpret_cast<u128*>(sQ + t * LDK + col) = rq[i];
-            }
+            for (int e = 0; e < E; ++e) sKT[(col + e) * LD + t] = unit_elem<ST>(kv, e);
+            if constexpr (!SUMMARY) *reinterpret_cast<u128*>(sQ + t * LDK + col) = t < L ? rq[i] : zero;
         }
 #pragma unroll
         for (int i = 0; i < PT; ++i) {
             const int u = tid + i * NT;
-            if (u < NUT) {
-                const int r = u / (GC / E), col = (u % (GC / E)) * E;
-                *reinterpret_cast<u128*>(sT + r * LD + col) = rt[i];
-                if constexpr (!SUMMARY) *reinterpret_cast<u128*>(sP + r * LD + col) = rp[i];
-            }
+            const int r = u / (GC / E), col = (u % (GC / E)) * E;
+            *reinterpret_cast<u128*>(sT + r * LD + col) = rt[i];
+            if constexpr (!SUMMARY) *reinterpret_cast<u128*>(sP + r * LD + col) = rp[i];
         }
-        if (tid < 64) *reinterpret_cast<u128*>(sC + 4 * tid) = rc;
-        float vv[16];
+        if (wave == 0) *reinterpret_cast<u128*>(sC + 4 * lane) = rc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) vv[i] = Elem<ST>::to_f(rv[i]);
-        __syncthreads();
-        if (c + 1 < nch) prefetch(c + 1);
+        for (int i = 0; i < 16; ++i) {
+            const int t = 16 * (i >> 2) + 4 * lg + (i & 3);
+            vv[i] = (vrow && t < L) ? Elem<ST>::to_f(rv[i]) : 0.f;
+        }
+    };
+
+    if (nch > 0) {
+        issue(0);
+        commit(0, 0);
+    }
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const int t0 = bos + c * GC, L = min(GC, eos - t0);
+        const int buf = NBUF == 2 ? (c & 1) : 0;
+        const uint8_t* base = smem + buf * SM::BYTES;
+        const ST* sK = reinterpret_cast<const ST*>(base + SM::OFF_K);
+        const ST* sKT = reinterpret_cast<const ST*>(base + SM::OFF_KT);
+        const ST* sT = reinterpret_cast<const ST*>(base + SM::OFF_T);
+        const float* sC = reinterpret_cast<const float*>(base + SM::OFF_C);
+        const ST* sQ = reinterpret_cast<const ST*>(base + SM::OFF_Q);
+        const ST* sP = reinterpret_cast<const ST*>(base + SM::OFF_P);
+        const bool more = c + 1 < nch;
+        if (more) issue(c + 1);
+        float vcur[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vcur[i] = vv[i];
 
         frag Sb[KB];
 #pragma unroll
@@ -397,45 +429,29 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
         for (int tb = 0; tb < 4; ++tb) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) acc = Elem<ST>::mma(acc, frag_rows(sK, LDK, 16 * tb, 16 * kb), Sb[kb]);
+            for (int kb = 0; kb < KB; kb += 2)
+                acc = Elem<ST>::mma2(acc, frag_rows(sK, LDK, 16 * tb, 16 * kb), frag_rows(sK, LDK, 16 * tb, 16 * kb + 16),
+                                     Sb[kb], Sb[kb + 1]);
             f32x4 y;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * tb + 4 * lg + r;
-                y[r] = sC[128 + t] * (vv[4 * tb + r] - sC[t] * acc[r]);
+                y[r] = sC[128 + t] * (vcur[4 * tb + r] - sC[t] * acc[r]);
             }
             Yb[tb] = Elem<ST>::pack(y);
         }
-        // R = T Y
+        // R = T Y (T is lower triangular; its upper 16x16 blocks are stored as zeros)
         f32x4 R[4];
         frag Rb[4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int tj = 0; tj <= ti; ++tj) acc = Elem<ST>::mma(acc, frag_rows(sT, LD, 16 * ti, 16 * tj), Yb[tj]);
+            for (int tj = 0; tj <= ti; tj += 2)
+                acc = Elem<ST>::mma2(acc, frag_rows(sT, LD, 16 * ti, 16 * tj), frag_rows(sT, LD, 16 * ti, 16 * tj + 16),
+                                     Yb[tj], Yb[tj + 1]);
             R[ti] = acc;
             Rb[ti] = Elem<ST>::pack(acc);
-        }
-        if constexpr (!SUMMARY) {
-            // O = scale Gamma (Q S^T) + P R
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) acc = Elem<ST>::mma(acc, frag_rows(sQ, LDK, 16 * ti, 16 * kb), Sb[kb]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] *= scale * sC[16 * ti + 4 * lg + r];
-#pragma unroll
-                for (int tj = 0; tj <= ti; ++tj) acc = Elem<ST>::mma(acc, frag_rows(sP, LD, 16 * ti, 16 * tj), Rb[tj]);
-                if (vrow) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = 16 * ti + 4 * lg + r;
-                        if (t < L) out[((size_t)(b * T + t0 + t) * H + h) * V + myrow] = Elem<ST>::from_f(acc[r]);
-                    }
-                }
-            }
         }
         // S <- Gamma_L S + K^T (e R)
         frag ERb[4];
@@ -451,10 +467,40 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
         for (int kb = 0; kb < KB; ++kb) {
             f32x4 acc = S[kb] * gl;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) acc = Elem<ST>::mma(acc, frag_rows(sKT, LD, 16 * kb, 16 * tb), ERb[tb]);
+            for (int tb = 0; tb < 4; tb += 2)
+                acc = Elem<ST>::mma2(acc, frag_rows(sKT, LD, 16 * kb, 16 * tb), frag_rows(sKT, LD, 16 * kb, 16 * tb + 16),
+                                     ERb[tb], ERb[tb + 1]);
             S[kb] = acc;
         }
-        (void)L;
+        if constexpr (!SUMMARY) {
+            // O = scale Gamma (Q S^T) + P R  (S^T here is the chunk-entry state, Sb)
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KB; kb += 2)
+                    acc = Elem<ST>::mma2(acc, frag_rows(sQ, LDK, 16 * ti, 16 * kb), frag_rows(sQ, LDK, 16 * ti, 16 * kb + 16),
+                                         Sb[kb], Sb[kb + 1]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] *= scale * sC[16 * ti + 4 * lg + r];
+#pragma unroll
+                for (int tj = 0; tj <= ti; tj += 2)
+                    acc = Elem<ST>::mma2(acc, frag_rows(sP, LD, 16 * ti, 16 * tj), frag_rows(sP, LD, 16 * ti, 16 * tj + 16),
+                                         Rb[tj], Rb[tj + 1]);
+                if (vrow) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * ti + 4 * lg + r;
+                        if (t < L) out[((size_t)(b * T + t0 + t) * H + h) * V + myrow] = Elem<ST>::from_f(acc[r]);
+                    }
+                }
+            }
+        }
+        if (more) {
+            if constexpr (NBUF == 1) __syncthreads();
+            commit(c + 1, NBUF == 2 ? (buf ^ 1) : 0);
+        }
+        __syncthreads();
     }
 
     // exit state
@@ -465,6 +511,353 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
             if (ht) *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + myrow) * KD + kk) = S[kb];
         } else if constexpr (SUMMARY) {
             *reinterpret_cast<f32x4*>(Mout + (((size_t)n * H + h) * KD + (myrow - V)) * KD + kk) = S[kb];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// ST + Out, bf16, warp-specialised: one workgroup = one 16-row state slice of
+// one chain, KS compute wavefronts + 4 loader wavefronts.
+//
+//  - Compute wavefront j owns the state columns k in k-tiles [j KB/KS, (j+1) KB/KS)
+//    (float32 MFMA accumulators) and the tokens of t-tiles [j 4/KS, (j+1) 4/KS).
+//    The bf16 copy of the whole slice state is exchanged through LDS, so each
+//    wavefront forms X = K S^T and Q S^T for its own tokens over all k; the
+//    corrected values Y of all tokens are exchanged the same way; R = T Y is
+//    formed redundantly by every compute wavefront (6 MFMAs), which then
+//    updates its own state columns and writes its own output tokens.
+//  - Loader wavefronts move chunk c+1 (K, Q, T, P, coefficients, the slice's V)
+//    from global memory into the other half of a double-buffered LDS stage
+//    and write chunk c-1's output tile to global memory with 16-byte stores,
+//    so the compute wavefronts never wait on vector memory.
+//  Two workgroup barriers per chunk separate the exchange phases.
+// ---------------------------------------------------------------------------
+template <int KD, bool SUMMARY>
+struct WsSmem {
+    static constexpr int E = 8;  // bf16 per 16-byte unit
+    static constexpr int LDK = KD + E, LD = GC + E, LDO = 16 + E;
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_T = OFF_K + GC * LDK * 2;
+    static constexpr int OFF_C = OFF_T + GC * LD * 2;
+    static constexpr int OFF_V = OFF_C + 256 * 4;
+    static constexpr int OFF_Q = OFF_V + 16 * LD * 2;
+    static constexpr int OFF_P = OFF_Q + (SUMMARY ? 0 : GC * LDK * 2);
+    static constexpr int BUF = OFF_P + (SUMMARY ? 0 : GC * LD * 2);
+    static constexpr int OFF_KT = 2 * BUF;                      // K^T [KD][LD] (single buffer)
+    static constexpr int OFF_S = OFF_KT + KD * LD * 2;          // state frags [KB][64] x 8 B
+    static constexpr int OFF_Y = OFF_S + (KD / 16) * 64 * 8;    // Y frags [4][64] x 8 B
+    static constexpr int OFF_O = OFF_Y + 4 * 64 * 8;            // output tiles [2][64][LDO] bf16
+    static constexpr int BYTES = OFF_O + (SUMMARY ? 0 : 2 * GC * LDO * 2);
+};
+
+template <int KD, int KS, bool SUMMARY>
+__global__ __launch_bounds__(64 * (KS + 4)) void gdn_chain_ws_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ h0, const int32_t* __restrict__ cu, const int* __restrict__ chunk_off,
+    const uint8_t* __restrict__ fac, int T, int H, int HK, int V, int n_seq, int nc, int nvb,
+    float scale, bf16_t* __restrict__ out, float* __restrict__ ht, float* __restrict__ Mout) {
+    typedef WsSmem<KD, SUMMARY> SM;
+    typedef Elem<bf16_t> El;
+    typedef El::frag frag;
+    constexpr int E = SM::E, LDK = SM::LDK, LD = SM::LD, LDO = SM::LDO;
+    constexpr int KB = KD / 16;
+    constexpr int KT = KB / KS;       // state k-tiles per compute wavefront
+    constexpr int TT = 4 / KS;        // token tiles per compute wavefront
+    constexpr int NLT = 256;          // loader threads
+    constexpr int UPR = KD / E;
+    constexpr int NUK = GC * UPR;
+    constexpr int NUT = GC * GC / E;
+    constexpr int PK = NUK / NLT, PT = NUT / NLT;
+    static_assert(KB % KS == 0 && 4 % KS == 0 && NUK % NLT == 0 && NUT % NLT == 0, "tiling");
+
+    __shared__ __align__(16) uint8_t smem[SM::BYTES];
+    i16x4* sS = reinterpret_cast<i16x4*>(smem + SM::OFF_S);
+    i16x4* sY = reinterpret_cast<i16x4*>(smem + SM::OFF_Y);
+
+    int chain, vb;
+    xcd_split(blockIdx.x, nvb, chain, vb);
+    if (chain >= n_seq * H) return;
+    const int n = chain / H, h = chain % H, hk = h / (H / HK);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const bool loader = wave >= KS;
+    const int row0 = 16 * vb;               // first state row of this slice
+    const bool vrows = row0 < V;            // value rows (else transition rows, summary only)
+
+    int b, bos, eos, slot0;
+    if (cu) {
+        b = 0;
+        bos = cu[n];
+        eos = cu[n + 1];
+        slot0 = chunk_off[n];
+    } else {
+        b = n;
+        bos = 0;
+        eos = T;
+        slot0 = n * nc;
+    }
+    const int nch = (eos - bos + GC - 1) / GC;
+    const size_t rec_bytes = gdn_factor_bytes(2);
+    auto buf_ptr = [&](int c) __attribute__((always_inline)) { return smem + (c & 1) * SM::BUF; };
+
+    // ---------------- loader role ----------------
+    const int lt = tid - 64 * KS;
+    u128 rk[PK], rq[PK], rt[PT], rp[PT], rc, rvv;
+    auto issue = [&](int c) __attribute__((always_inline)) {
+        const int t0 = bos + c * GC, L = min(GC, eos - t0);
+        const uint8_t* rec = fac + ((size_t)(slot0 + c) * H + h) * rec_bytes;
+        const bf16_t* gT = reinterpret_cast<const bf16_t*>(rec);
+        const bf16_t* gP = gT + GC * GC;
+        const float* gC = reinterpret_cast<const float*>(gP + GC * GC);
+#pragma unroll
+        for (int i = 0; i < PK; ++i) {
+            const int u = lt + i * NLT;
+            const int t = min(u / UPR, L - 1), col = (u % UPR) * E;
+            const size_t off = ((size_t)(b * T + t0 + t) * HK + hk) * KD + col;
+            rk[i] = *reinterpret_cast<const u128*>(k + off);
+            if constexpr (!SUMMARY) rq[i] = *reinterpret_cast<const u128*>(q + off);
+        }
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int u = lt + i * NLT;
+            rt[i] = *reinterpret_cast<const u128*>(gT + u * E);
+            if constexpr (!SUMMARY) rp[i] = *reinterpret_cast<const u128*>(gP + u * E);
+        }
+        if (lt < 64) rc = *reinterpret_cast<const u128*>(gC + 4 * lt);
+        if (vrows && lt < 128) {
+            const int t = min(lt >> 1, L - 1), col = (lt & 1) * E;
+            rvv = *reinterpret_cast<const u128*>(v + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + col);
+        }
+    };
+    auto commit = [&](int c) __attribute__((always_inline)) {
+        const int L = min(GC, eos - (bos + c * GC));
+        uint8_t* base = buf_ptr(c);
+        bf16_t* sK = reinterpret_cast<bf16_t*>(base + SM::OFF_K);
+        bf16_t* sT = reinterpret_cast<bf16_t*>(base + SM::OFF_T);
+        float* sC = reinterpret_cast<float*>(base + SM::OFF_C);
+        bf16_t* sVT = reinterpret_cast<bf16_t*>(base + SM::OFF_V);
+        bf16_t* sQ = reinterpret_cast<bf16_t*>(base + SM::OFF_Q);
+        bf16_t* sP = reinterpret_cast<bf16_t*>(base + SM::OFF_P);
+        const u128 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < PK; ++i) {
+            const int u = lt + i * NLT;
+            const int t = u / UPR, col = (u % UPR) * E;
+            *reinterpret_cast<u128*>(sK + t * LDK + col) = t < L ? rk[i] : zero;
+            if constexpr (!SUMMARY) *reinterpret_cast<u128*>(sQ + t * LDK + col) = t < L ? rq[i] : zero;
+        }
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int u = lt + i * NLT;
+            const int r = u / (GC / E), col = (u % (GC / E)) * E;
+            *reinterpret_cast<u128*>(sT + r * LD + col) = rt[i];
+            if constexpr (!SUMMARY) *reinterpret_cast<u128*>(sP + r * LD + col) = rp[i];
+        }
+        if (lt < 64) *reinterpret_cast<u128*>(sC + 4 * lt) = rc;
+        if (lt < 128) {
+            const int t = lt >> 1, col = (lt & 1) * E;
+            const u128 x = (vrows && t < L) ? rvv : zero;
+#pragma unroll
+            for (int e = 0; e < E; ++e) sVT[(col + e) * LD + t] = unit_elem<bf16_t>(x, e);
+        }
+    };
+    // K^T of chunk c (single buffer) from the staged natural K: read during
+    // phase 1, consumed by the compute wavefronts in phase 2 of the same chunk
+    auto transpose_k = [&](int c) __attribute__((always_inline)) {
+        // one lane per (token pair p, k-octet m): two 16-byte row reads, then
+        // eight 4-byte writes K^T[8m+e][2p .. 2p+1]; the 64 lanes of a
+        // wavefront cover 32 pairs x 2 octets, which fall in distinct banks
+        const bf16_t* sK = reinterpret_cast<const bf16_t*>(buf_ptr(c) + SM::OFF_K);
+        bf16_t* sKT = reinterpret_cast<bf16_t*>(smem + SM::OFF_KT);
+        constexpr int NPO = (GC / 2) * UPR;  // pair-octets per chunk
+        static_assert(NPO % NLT == 0, "transpose tiling");
+#pragma unroll
+        for (int i = 0; i < NPO / NLT; ++i) {
+            const int w = lt + i * NLT;
+            const int p = w & 31, m = w >> 5;
+            const u128 x0 = *reinterpret_cast<const u128*>(sK + (2 * p) * LDK + 8 * m);
+            const u128 x1 = *reinterpret_cast<const u128*>(sK + (2 * p + 1) * LDK + 8 * m);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t lo = (x0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                const uint32_t hi = (x1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                *reinterpret_cast<uint32_t*>(sKT + (8 * m + e) * LD + 2 * p) = lo | (hi << 16);
+            }
+        }
+    };
+    auto store_out = [&](int c) __attribute__((always_inline)) {  // output tile of chunk c from LDS to global
+        if constexpr (!SUMMARY) {
+            const int t0 = bos + c * GC, L = min(GC, eos - t0);
+            const bf16_t* sO = reinterpret_cast<const bf16_t*>(smem + SM::OFF_O) + (c & 1) * GC * LDO;
+            if (lt < 128) {
+                const int t = lt >> 1, col = (lt & 1) * E;
+                if (t < L)
+                    *reinterpret_cast<u128*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + col) =
+                        *reinterpret_cast<const u128*>(sO + t * LDO + col);
+            }
+        }
+    };
+
+    // ---------------- compute role ----------------
+    const int j = wave;  // compute wavefront index (valid when !loader)
+    f32x4 S[KT];
+    if (!loader) {
+#pragma unroll
+        for (int i = 0; i < KT; ++i) {
+            const int kt = j * KT + i, kk = 16 * kt + 4 * lg;
+            const int row = row0 + ln;
+            if constexpr (!SUMMARY) {
+                S[i] = h0 ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + row) * KD + kk) : zero4();
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[i][r] = (!vrows && kk + r == row - V) ? 1.f : 0.f;
+            }
+            sS[kt * 64 + lane] = El::pack(S[i]);
+        }
+    } else if (nch > 0) {
+        issue(0);
+        commit(0);
+        if (nch > 1) issue(1);  // in flight across the first iteration
+    }
+    __syncthreads();
+
+    f32x4 QS[TT];
+    for (int c = 0; c < nch; ++c) {
+        const int t0 = bos + c * GC, L = min(GC, eos - t0);
+        const uint8_t* base = buf_ptr(c);
+        const bf16_t* sK = reinterpret_cast<const bf16_t*>(base + SM::OFF_K);
+        const bf16_t* sT = reinterpret_cast<const bf16_t*>(base + SM::OFF_T);
+        const float* sC = reinterpret_cast<const float*>(base + SM::OFF_C);
+        const bf16_t* sVT = reinterpret_cast<const bf16_t*>(base + SM::OFF_V);
+        const bf16_t* sQ = reinterpret_cast<const bf16_t*>(base + SM::OFF_Q);
+        const bf16_t* sP = reinterpret_cast<const bf16_t*>(base + SM::OFF_P);
+        const bool more = c + 1 < nch;
+        // ---- phase 1: X = K S^T and Q S^T for own tokens, Y = beta (V - Gamma X) ----
+        if (loader) {
+            transpose_k(c);
+            if (c > 0) store_out(c - 1);
+        } else {
+            // every LDS operand of the phase is read before the first product
+            frag Sf[KB], Kf[TT][KB], Qf[TT][KB], Vf[TT];
+            f32x4 gam[TT], bet[TT];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) Sf[kb] = sS[kb * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < TT; ++i) {
+                const int tt = j * TT + i;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    Kf[i][kb] = frag_rows(sK, LDK, 16 * tt, 16 * kb);
+                    if constexpr (!SUMMARY) Qf[i][kb] = frag_rows(sQ, LDK, 16 * tt, 16 * kb);
+                }
+                Vf[i] = frag_rows(sVT, LD, 0, 16 * tt);
+                gam[i] = *reinterpret_cast<const f32x4*>(sC + 16 * tt + 4 * lg);
+                bet[i] = *reinterpret_cast<const f32x4*>(sC + 128 + 16 * tt + 4 * lg);
+            }
+#pragma unroll
+            for (int i = 0; i < TT; ++i) {
+                const int tt = j * TT + i;
+                f32x4 x = zero4(), qs = zero4();
+#pragma unroll
+                for (int kb = 0; kb < KB; kb += 2) {
+                    x = El::mma2(x, Kf[i][kb], Kf[i][kb + 1], Sf[kb], Sf[kb + 1]);
+                    if constexpr (!SUMMARY) qs = El::mma2(qs, Qf[i][kb], Qf[i][kb + 1], Sf[kb], Sf[kb + 1]);
+                }
+                QS[i] = qs * gam[i] * scale;
+                const f32x4 vx = El::unpack(Vf[i]);
+                sY[tt * 64 + lane] = El::pack(bet[i] * (vx - gam[i] * x));
+            }
+        }
+        __syncthreads();
+        // ---- phase 2: R = T Y, state update of own columns, own output tokens ----
+        if (loader) {
+            // chunk c+1 was issued one iteration ago; chunk c+2 stays in flight for the next one
+            if (more) commit(c + 1);
+            if (c + 2 < nch) issue(c + 2);
+        } else {
+            frag Yf[4], Tf[6][2], Ka[KT][2][2], Pf[TT][2][2];
+            f32x4 ec[4];
+            constexpr int TI[6] = {0, 1, 2, 2, 3, 3}, TJ[6] = {0, 0, 0, 2, 0, 2};
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                Yf[ti] = sY[ti * 64 + lane];
+                ec[ti] = *reinterpret_cast<const f32x4*>(sC + 64 + 16 * ti + 4 * lg);
+            }
+#pragma unroll
+            for (int p = 0; p < 6; ++p) {
+                Tf[p][0] = frag_rows(sT, LD, 16 * TI[p], 16 * TJ[p]);
+                Tf[p][1] = frag_rows(sT, LD, 16 * TI[p], 16 * TJ[p] + 16);
+            }
+            // K^T fragments of own state columns
+            const bf16_t* sKT = reinterpret_cast<const bf16_t*>(smem + SM::OFF_KT);
+#pragma unroll
+            for (int i = 0; i < KT; ++i)
+#pragma unroll
+                for (int tp = 0; tp < 2; ++tp) {
+                    Ka[i][tp][0] = frag_rows(sKT, LD, 16 * (j * KT + i), 32 * tp);
+                    Ka[i][tp][1] = frag_rows(sKT, LD, 16 * (j * KT + i), 32 * tp + 16);
+                }
+            if constexpr (!SUMMARY) {
+#pragma unroll
+                for (int i = 0; i < TT; ++i) {
+                    const int tt = j * TT + i;
+                    // all four 16-token blocks of the row; P's upper blocks are stored as zeros
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) {
+                        Pf[i][pp][0] = frag_rows(sP, LD, 16 * tt, 32 * pp);
+                        Pf[i][pp][1] = frag_rows(sP, LD, 16 * tt, 32 * pp + 16);
+                    }
+                }
+            }
+            const float gl = sC[192];
+            f32x4 R[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+            for (int p = 0; p < 6; ++p)
+                R[TI[p]] = El::mma2(R[TI[p]], Tf[p][0], Tf[p][1], Yf[TJ[p]], Yf[TJ[p] + 1]);
+            frag Rb[4], ER[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                Rb[ti] = El::pack(R[ti]);
+                ER[ti] = El::pack(R[ti] * ec[ti]);
+            }
+            // own state columns: S^T[kt] <- Gamma_L S^T[kt] + K^T[kt, :] (e R)
+#pragma unroll
+            for (int i = 0; i < KT; ++i) {
+                f32x4 acc = S[i] * gl;
+                acc = El::mma2(acc, Ka[i][0][0], Ka[i][0][1], ER[0], ER[1]);
+                acc = El::mma2(acc, Ka[i][1][0], Ka[i][1][1], ER[2], ER[3]);
+                S[i] = acc;
+            }
+            if constexpr (!SUMMARY) {
+                bf16_t* sO = reinterpret_cast<bf16_t*>(smem + SM::OFF_O) + (c & 1) * GC * LDO;
+#pragma unroll
+                for (int i = 0; i < TT; ++i) {
+                    const int tt = j * TT + i;
+                    f32x4 acc = QS[i];
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) acc = El::mma2(acc, Pf[i][pp][0], Pf[i][pp][1], Rb[2 * pp], Rb[2 * pp + 1]);
+                    const frag o = El::pack(acc);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sO[(16 * tt + 4 * lg + r) * LDO + ln] = (bf16_t)o[r];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < KT; ++i) sS[(j * KT + i) * 64 + lane] = El::pack(S[i]);
+        }
+        __syncthreads();
+        (void)L;
+        (void)t0;
+    }
+    if (loader) {
+        if (nch > 0) store_out(nch - 1);
+    } else {
+#pragma unroll
+        for (int i = 0; i < KT; ++i) {
+            const int kt = j * KT + i, kk = 16 * kt + 4 * lg, row = row0 + ln;
+            if (vrows) {
+                if (ht) *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + row) * KD + kk) = S[i];
+            } else if constexpr (SUMMARY) {
+                *reinterpret_cast<f32x4*>(Mout + (((size_t)n * H + h) * KD + (row - V)) * KD + kk) = S[i];
+            }
         }
     }
 }
@@ -499,12 +892,28 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
         timing_end(s);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    constexpr int NW = 4;
     const int rows = mode == 0 ? V : V + KD;
-    const int nvb = rows / (16 * NW);
     const int chains = N * H;
-    const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * nvb);
     if (chains == 0) return hipSuccess;
+    if constexpr (sizeof(ST) == 2) {
+        constexpr int KS = 4;
+        const int nvb = rows / 16;
+        const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * nvb);
+        if (mode == 0) {
+            timing_begin("gdn_chain", s);
+            gdn_chain_ws_kernel<KD, KS, false><<<grid, 64 * (KS + 4), 0, s>>>(
+                q, k, v, h0, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, nvb, scale, out, ht, nullptr);
+        } else {
+            timing_begin("gdn_summary_chain", s);
+            gdn_chain_ws_kernel<KD, KS, true><<<grid, 64 * (KS + 4), 0, s>>>(
+                q, k, v, nullptr, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, nvb, scale, nullptr, ht, Mout);
+        }
+        timing_end(s);
+        return hipGetLastError();
+    }
+    constexpr int NW = 4;
+    const int nvb = rows / (16 * NW);
+    const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * nvb);
     if (mode == 0) {
         timing_begin("gdn_chain", s);
         gdn_chain_kernel<ST, KD, NW, false><<<grid, 64 * NW, 0, s>>>(

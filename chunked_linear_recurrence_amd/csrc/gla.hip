@@ -25,10 +25,10 @@ namespace sf {
 template <typename ST>
 __device__ __forceinline__ ST gla_unit_elem(const u128& u, int e) {
     if constexpr (sizeof(ST) == 2) {
-        const uint32_t w = (&u.x)[e >> 1];
+        const uint32_t w = u[e >> 1];
         return (ST)((e & 1) ? (w >> 16) : (w & 0xffffu));
     } else {
-        return __uint_as_float((&u.x)[e]);
+        return __uint_as_float(u[e]);
     }
 }
 
@@ -97,68 +97,54 @@ __global__ __launch_bounds__(64 * NW) void gla_chain_kernel(
     }
     float gsum = 0.f;
 
+    static_assert(NUK % NT == 0 && NUV % NT == 0, "staging units must divide evenly");
+    // Unconditional loads from clamped rows; rows past the chunk end are
+    // zeroed when the registers are written to LDS.
     u128 rk[PK], rq[PK], rv[PV];
-    float rg[(C + NT - 1) / NT];
-    auto prefetch = [&](int c) {
+    float rg;
+    auto prefetch = [&](int c) __attribute__((always_inline)) {
         const int t0 = bos + c * C, L = min(C, eos - t0);
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
             const int u = tid + i * NT;
-            rk[i] = rq[i] = u128{0u, 0u, 0u, 0u};
-            if (u < NUK) {
-                const int t = u / UPR, col = (u % UPR) * E;
-                if (t < L) {
-                    const size_t off = ((size_t)(b * T + t0 + t) * HK + hk) * KD + col;
-                    rk[i] = *reinterpret_cast<const u128*>(k + off);
-                    if constexpr (!SUMMARY) rq[i] = *reinterpret_cast<const u128*>(q + off);
-                }
-            }
+            const int t = min(u / UPR, L - 1), col = (u % UPR) * E;
+            const size_t off = ((size_t)(b * T + t0 + t) * HK + hk) * KD + col;
+            rk[i] = *reinterpret_cast<const u128*>(k + off);
+            if constexpr (!SUMMARY) rq[i] = *reinterpret_cast<const u128*>(q + off);
         }
 #pragma unroll
         for (int i = 0; i < PV; ++i) {
             const int u = tid + i * NT;
-            rv[i] = u128{0u, 0u, 0u, 0u};
-            if (u < NUV) {
-                const int t = u / VPR, col = (u % VPR) * E;
-                if (t < L) rv[i] = *reinterpret_cast<const u128*>(v + ((size_t)(b * T + t0 + t) * H + h) * V + v0 + col);
-            }
+            const int t = min(u / VPR, L - 1), col = (u % VPR) * E;
+            rv[i] = *reinterpret_cast<const u128*>(v + ((size_t)(b * T + t0 + t) * H + h) * V + v0 + col);
         }
-#pragma unroll
-        for (int i = 0; i < (C + NT - 1) / NT; ++i) {
-            const int t = tid + i * NT;
-            rg[i] = (t < C && t < L) ? g[(size_t)(b * T + t0 + t) * H + h] : 0.f;
-        }
+        rg = g[(size_t)(b * T + t0 + min(tid % C, L - 1)) * H + h];
     };
 
     if (nch > 0) prefetch(0);
     for (int c = 0; c < nch; ++c) {
         const int t0 = bos + c * C, L = min(C, eos - t0);
+        const u128 zero = {0u, 0u, 0u, 0u};
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < PK; ++i) {
             const int u = tid + i * NT;
-            if (u < NUK) {
-                const int t = u / UPR, col = (u % UPR) * E;
-                *reinterpret_cast<u128*>(sKP + t * LDKP + col) = rk[i];
+            const int t = u / UPR, col = (u % UPR) * E;
+            const u128 kv = t < L ? rk[i] : zero;
+            *reinterpret_cast<u128*>(sKP + t * LDKP + col) = kv;
 #pragma unroll
-                for (int e = 0; e < E; ++e) sKT[(col + e) * LDC + t] = gla_unit_elem<ST>(rk[i], e);
-                if constexpr (!SUMMARY) *reinterpret_cast<u128*>(sQ + t * LDK + col) = rq[i];
-            }
+            for (int e = 0; e < E; ++e) sKT[(col + e) * LDC + t] = gla_unit_elem<ST>(kv, e);
+            if constexpr (!SUMMARY) *reinterpret_cast<u128*>(sQ + t * LDK + col) = t < L ? rq[i] : zero;
         }
 #pragma unroll
         for (int i = 0; i < PV; ++i) {
             const int u = tid + i * NT;
-            if (u < NUV) {
-                const int t = u / VPR, col = (u % VPR) * E;
+            const int t = u / VPR, col = (u % VPR) * E;
+            const u128 vv = t < L ? rv[i] : zero;
 #pragma unroll
-                for (int e = 0; e < E; ++e) sVT[(col + e) * LDC + t] = gla_unit_elem<ST>(rv[i], e);
-            }
+            for (int e = 0; e < E; ++e) sVT[(col + e) * LDC + t] = gla_unit_elem<ST>(vv, e);
         }
-#pragma unroll
-        for (int i = 0; i < (C + NT - 1) / NT; ++i) {
-            const int t = tid + i * NT;
-            if (t < C) sG[t] = rg[i];
-        }
+        if (tid < C) sG[tid] = tid < L ? rg : 0.f;
         __syncthreads();
         if (c + 1 < nch) prefetch(c + 1);
 
@@ -202,8 +188,9 @@ __global__ __launch_bounds__(64 * NW) void gla_chain_kernel(
                     const int tj = tt - ti * (ti + 1) / 2;
                     f32x4 acc = zero4();
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-                        acc = Elem<ST>::mma(acc, frag_rows(sQ, LDK, 16 * ti, 16 * kb), frag_rows(sKP, LDKP, 16 * tj, 16 * kb));
+                    for (int kb = 0; kb < KB; kb += 2)
+                        acc = Elem<ST>::mma2(acc, frag_rows(sQ, LDK, 16 * ti, 16 * kb), frag_rows(sQ, LDK, 16 * ti, 16 * kb + 16),
+                                             frag_rows(sKP, LDKP, 16 * tj, 16 * kb), frag_rows(sKP, LDKP, 16 * tj, 16 * kb + 16));
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int t = 16 * ti + 4 * lg + r, j = 16 * tj + ln;
@@ -223,6 +210,10 @@ __global__ __launch_bounds__(64 * NW) void gla_chain_kernel(
                     for (int r = 0; r < 4; ++r) sKP[(16 * ti + 4 * lg + r) * LDKP + 16 * tj + ln] = Elem<ST>::from_f(pt[i][r]);
                 }
             }
+            // the 32-token products below pair block (ti, ti) with the upper block (ti, ti+1) for even ti
+            for (int ti = 2 * wave; ti < CB; ti += 2 * NW)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sKP[(16 * ti + 4 * lg + r) * LDKP + 16 * (ti + 1) + ln] = Elem<ST>::from_f(0.f);
             __syncthreads();
 
             frag Sb[KB];
@@ -232,12 +223,15 @@ __global__ __launch_bounds__(64 * NW) void gla_chain_kernel(
             for (int ti = 0; ti < CB; ++ti) {
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) acc = Elem<ST>::mma(acc, frag_rows(sQ, LDK, 16 * ti, 16 * kb), Sb[kb]);
+                for (int kb = 0; kb < KB; kb += 2)
+                    acc = Elem<ST>::mma2(acc, frag_rows(sQ, LDK, 16 * ti, 16 * kb), frag_rows(sQ, LDK, 16 * ti, 16 * kb + 16),
+                                         Sb[kb], Sb[kb + 1]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] *= scale * sGam[16 * ti + 4 * lg + r];
 #pragma unroll
-                for (int tj = 0; tj <= ti; ++tj)
-                    acc = Elem<ST>::mma(acc, frag_rows(sKP, LDKP, 16 * ti, 16 * tj), frag_rows(sVT, LDC, 16 * wave, 16 * tj));
+                for (int tj = 0; tj <= ti; tj += 2)
+                    acc = Elem<ST>::mma2(acc, frag_rows(sKP, LDKP, 16 * ti, 16 * tj), frag_rows(sKP, LDKP, 16 * ti, 16 * tj + 16),
+                                         frag_rows(sVT, LDC, 16 * wave, 16 * tj), frag_rows(sVT, LDC, 16 * wave, 16 * tj + 16));
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * ti + 4 * lg + r;
@@ -260,7 +254,9 @@ __global__ __launch_bounds__(64 * NW) void gla_chain_kernel(
         for (int kb = 0; kb < KB; ++kb) {
             f32x4 acc = S[kb] * gl;
 #pragma unroll
-            for (int tb = 0; tb < CB; ++tb) acc = Elem<ST>::mma(acc, frag_rows(sKT, LDC, 16 * kb, 16 * tb), EV[tb]);
+            for (int tb = 0; tb < CB; tb += 2)
+                acc = Elem<ST>::mma2(acc, frag_rows(sKT, LDC, 16 * kb, 16 * tb), frag_rows(sKT, LDC, 16 * kb, 16 * tb + 16),
+                                     EV[tb], EV[tb + 1]);
             S[kb] = acc;
         }
     }

@@ -20,6 +20,9 @@ namespace sf {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -43,13 +46,20 @@ template <> struct Elem<bf16_t> {
     static __device__ __forceinline__ f32x4 mma(f32x4 acc, frag a, frag b) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
     }
+    // Two consecutive 16-wide reduction blocks in one v_mfma_f32_16x16x32_bf16:
+    // lane slots 0..3 carry block 0 and 4..7 block 1 in both operands, so the
+    // 32 products pair up exactly as in two block products.
+    static __device__ __forceinline__ f32x4 mma2(f32x4 acc, frag a0, frag a1, frag b0, frag b1) {
+        const i16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const i16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       acc, 0, 0, 0);
+    }
+    // float32 -> bf16 with the hardware converter (v_cvt_pk_bf16_f32, round to
+    // nearest even), two values per instruction.
     static __device__ __forceinline__ frag pack(f32x4 x) {
-        frag r;
-        r[0] = (short)f2bf(x[0]);
-        r[1] = (short)f2bf(x[1]);
-        r[2] = (short)f2bf(x[2]);
-        r[3] = (short)f2bf(x[3]);
-        return r;
+        const bf16x4 b = __builtin_convertvector(x, bf16x4);
+        return __builtin_bit_cast(frag, b);
     }
     static __device__ __forceinline__ f32x4 unpack(frag x) {
         f32x4 r;
@@ -72,6 +82,9 @@ template <> struct Elem<float> {
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
         return acc;
     }
+    static __device__ __forceinline__ f32x4 mma2(f32x4 acc, frag a0, frag a1, frag b0, frag b1) {
+        return mma(mma(acc, a0, b0), a1, b1);
+    }
     static __device__ __forceinline__ frag pack(f32x4 x) { return x; }
     static __device__ __forceinline__ f32x4 unpack(frag x) { return x; }
 };
@@ -87,8 +100,10 @@ __device__ __forceinline__ typename Elem<ST>::frag frag_rows(const ST* m, int ld
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// 16-byte vector unit used for staging copies.
-typedef uint4 u128;
+// 16-byte vector unit used for staging copies. A native vector type (not
+// HIP's uint4 struct, whose copies become stack memcpys) so that staging
+// values stay in registers.
+typedef unsigned int u128 __attribute__((ext_vector_type(4)));
 
 // Inclusive prefix sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_inclusive_scan(float x) {

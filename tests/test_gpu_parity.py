@@ -294,11 +294,13 @@ def test_gdn_summary_vs_oracle(dev, oracle, dtype, D):
 def test_gla_summary_vs_oracle(dev, oracle, dtype, chunk):
     say(f"case: GLA summary {dtype} chunk {chunk}")
     d = wl.scalar_gate_inputs(B=3, T=300, H=4, HK=2, K=128, V=64, dtype=dtype, seed=chunk)
+    # slow the gates so that a_block = exp(sum g) stays in the float32 range (sum g ~ -3)
+    d["g"] = d["g"] * 0.02
     a, E = sf.segment_summary("gla", cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev), chunk=chunk)
     ra, rE = oracle.gla_summary(f32(d["k"]), f32(d["v"]), f32(d["g"]))
     ea = float(np.max(np.abs(f32(a) - ra) / ra))
     say(f"  max rel|a-ref|={ea:.3e} rel_rms(S_ext)={rel_rms(f32(E), rE):.3e}")
-    assert ea <= 1e-4
+    assert ra.min() > 1e-6 and ea <= 1e-4
     if dtype == torch.float32:
         assert maxabs(f32(E), rE) <= FP32_ATOL * max(1.0, np.abs(rE).max())
     else:
@@ -334,7 +336,8 @@ def test_segmented_gdn_nonzero_transitions(dev, oracle):
     ro, rh = oracle.gdn_forward(f32(d["q"]), f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(d["beta"]), f32(d["h0"]))
     check_bf16("segmented vs unsegmented oracle", f32(o), ro, f32(hf), rh)
     M, _ = sf.segment_summary("gdn", *(sf.segment_view(x[n], 16) for n in ("k", "v", "g", "beta")))
-    assert f32(M).std() > 0.05
+    diag = np.einsum("shii->shi", f32(M))
+    assert diag.mean() > 0.1  # the transitions are far from zero, so the scan matters
 
 
 # ---------------------------------------------------------------------------
