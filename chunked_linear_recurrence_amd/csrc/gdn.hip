@@ -108,7 +108,8 @@ __device__ __forceinline__ bool chunk_coords(int slot, const int2* table, const 
 // ---------------------------------------------------------------------------
 // Pre: per (chunk slot, head) -> T, P, coefficients.
 // Record layout: T [64][64] ST | P [64][64] ST | coef float[256]:
-//   [0,64) Gamma_t  [64,128) e_t  [128,192) beta_t  [192] Gamma_L
+//   [0,64) Gamma_t  [64,128) e_t  [128,192) beta_t  [192,256) G_t
+// (Gamma_L = Gamma_63: padded tokens of a partial chunk have zero gate)
 // ---------------------------------------------------------------------------
 template <typename ST, int KD>
 __global__ __launch_bounds__(256) void gdn_prep_kernel(const ST* __restrict__ q, const ST* __restrict__ k,
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const ST* __restrict__ q,
         gC[tid] = expf(G);
         gC[64 + tid] = expf(GL - G);
         gC[128 + tid] = sB[tid];
-        gC[192 + tid] = tid == 0 ? expf(GL) : 0.f;
+        gC[192 + tid] = G;
     }
 
     // raw K K^T and Q K^T on the 10 lower 16x16 tiles each, then decay masks
@@ -239,6 +240,161 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const ST* __restrict__ q,
             const int r = u / UR, c = (u % UR) * E;
             *reinterpret_cast<u128*>(gP + r * GC + c) = *reinterpret_cast<const u128*>(sP + r * LD + c);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pre, bf16: one wavefront per (chunk slot, head), no workgroup barriers.
+//  - K and Q rows go straight from global memory into 16x16x32 MFMA
+//    fragments (lane (n, g) holds row 16R+n, columns 32p+8g..+7), which serve
+//    as both operands of K K^T and Q K^T on the 10 lower 16x16 tiles.
+//  - A = diag(beta)(strictly lower D o K K^T) is kept in LDS as packed
+//    columns (column i holds rows i+1..63, 16-byte aligned).
+//  - T = (I + A)^-1 by forward substitution with one column per lane
+//    (T[t][j] = 1{t == j} - sum_{i<t} A[t][i] T[i][j]), applied right-looking:
+//    A's columns are read as broadcasts from LDS, T's column stays in 64
+//    registers.
+//  - T and P leave through a 64x64 bf16 LDS staging tile with 16-byte stores.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int tri_off(int t) {  // sum_{s<t} round_up(s, 4)
+    return 8 * (t / 4) * (t / 4) + 4 * (t / 4) + ((t % 4) ? 4 * (t / 4) * (t % 4) + 4 * ((t % 4) - 1) : 0);
+}
+// Column i of the strictly lower 64x64 A (rows i+1..63) starts at col_off(i),
+// each column padded to a multiple of 4 floats: sum_{i'<i} round_up(63 - i', 4).
+__host__ __device__ constexpr int col_off(int i) { return tri_off(GC) - tri_off(GC - i); }
+
+template <int KD, bool WANT_P>
+__global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                           const float* __restrict__ g,
+                                                           const float* __restrict__ beta,
+                                                           const int2* __restrict__ table,
+                                                           const int32_t* __restrict__ cu, int T, int H,
+                                                           int HK, int nc, int n_slots, float scale,
+                                                           uint8_t* __restrict__ fac) {
+    constexpr int KP = KD / 32;
+    constexpr int NPW = 1;
+    __shared__ __align__(16) float sA[tri_off(GC)];
+    __shared__ __align__(16) bf16_t sO[GC * GC];
+    __shared__ float sG[GC], sB[GC];
+
+    const int h = blockIdx.y;
+    const int hk = h / (H / HK);
+    const int lane = threadIdx.x, ln = lane & 15, lg = lane >> 4;
+    const bf16x8 zero8 = {};
+
+    bf16x8 kf[4][KP], qf[4][KP];
+    float gv, bv;
+    int b, t0, L;
+    auto load = [&](int slot) __attribute__((always_inline)) {
+        const int t_lane = min(lane, L - 1);
+        const size_t gi = (size_t)(b * T + t0 + t_lane) * H + h;
+        gv = lane < L ? g[gi] : 0.f;
+        bv = lane < L ? beta[gi] : 0.f;
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            const int t = 16 * R + ln;
+            const size_t row = ((size_t)(b * T + t0 + min(t, L - 1)) * HK + hk) * KD;
+#pragma unroll
+            for (int p = 0; p < KP; ++p) {
+                const bf16x8 kv = *reinterpret_cast<const bf16x8*>(k + row + 32 * p + 8 * lg);
+                kf[R][p] = t < L ? kv : zero8;
+                if constexpr (WANT_P) {
+                    const bf16x8 qv = *reinterpret_cast<const bf16x8*>(q + row + 32 * p + 8 * lg);
+                    qf[R][p] = t < L ? qv : zero8;
+                }
+            }
+        }
+        (void)slot;
+    };
+
+    int slot = blockIdx.x * NPW;
+    if (slot >= n_slots || !chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
+    load(slot);
+    for (int s = 0; s < NPW; ++s, ++slot) {
+        // gates of this slot (registers loaded with the slot's K/Q)
+        const float G = wave_inclusive_scan(gv);
+        sG[lane] = G;
+        sB[lane] = bv;
+        uint8_t* rec = fac + ((size_t)slot * H + h) * gdn_factor_bytes(2);
+        bf16_t* gT = reinterpret_cast<bf16_t*>(rec);
+        bf16_t* gP = gT + GC * GC;
+        float* gC = reinterpret_cast<float*>(gP + GC * GC);
+        {
+            const float GL = __shfl(G, 63, 64);
+            gC[lane] = expf(G);
+            gC[64 + lane] = expf(GL - G);
+            gC[128 + lane] = bv;
+            gC[192 + lane] = G;
+        }
+#pragma unroll
+        for (int i = 0; i < GC * GC / 8 / 64; ++i) *reinterpret_cast<u128*>(sO + 8 * (lane + 64 * i)) = u128{0u, 0u, 0u, 0u};
+        __syncthreads();
+
+#pragma unroll
+        for (int tt = 0; tt < 10; ++tt) {
+            const int ti = (tt >= 1) + (tt >= 3) + (tt >= 6);
+            const int tj = tt - ti * (ti + 1) / 2;
+            f32x4 a = zero4(), pq = zero4();
+#pragma unroll
+            for (int p = 0; p < KP; ++p) {
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ti][p], kf[tj][p], a, 0, 0, 0);
+                if constexpr (WANT_P) pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ti][p], kf[tj][p], pq, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * ti + 4 * lg + r, i = 16 * tj + ln;
+                const float d = expf(fminf(sG[t] - sG[i], 0.f));
+                if (i < t) sA[col_off(i) + (t - i - 1)] = sB[t] * d * a[r];
+                if (WANT_P && i <= t) sO[t * GC + i] = f2bf(scale * d * pq[r]);
+            }
+        }
+        __syncthreads();
+        if constexpr (WANT_P) {
+#pragma unroll
+            for (int i = 0; i < GC * GC / 8 / 64; ++i) {
+                const int u = lane + 64 * i;
+                *reinterpret_cast<u128*>(gP + 8 * u) = *reinterpret_cast<const u128*>(sO + 8 * u);
+            }
+        }
+        // next slot's loads go out now (the fragment registers are free) and land during the solve
+        const bool next = s + 1 < NPW && slot + 1 < n_slots && chunk_coords(slot + 1, table, cu, T, nc, b, t0, L);
+        if (next) load(slot + 1);
+
+        // forward substitution, lane = column j of T, right-looking: once row t
+        // of the column is final, its contribution A[r][t] x_t leaves every later
+        // row r, so each step is 63 - t independent FMAs; the next column of A
+        // is read from LDS while the current one is applied
+        float x[GC];
+#pragma unroll
+        for (int r = 0; r < GC; ++r) x[r] = (r == lane) ? 1.f : 0.f;
+        f32x4 cur[16], nxt[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) cur[m] = *reinterpret_cast<const f32x4*>(sA + col_off(0) + 4 * m);
+#pragma unroll
+        for (int t = 0; t < GC - 1; ++t) {
+            const int n = GC - 1 - t, n1 = n - 1;  // entries in column t and t+1
+#pragma unroll
+            for (int m = 0; m < (n1 + 3) / 4; ++m) nxt[m] = *reinterpret_cast<const f32x4*>(sA + col_off(t + 1) + 4 * m);
+            const float xt = x[t];
+#pragma unroll
+            for (int m = 0; m < (n + 3) / 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * m + e < n) x[t + 1 + 4 * m + e] -= cur[m][e] * xt;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) cur[m] = nxt[m];
+        }
+        __syncthreads();  // staging tile free again (P copy done)
+#pragma unroll
+        for (int t = 0; t < GC; ++t) sO[t * GC + lane] = f2bf(x[t]);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < GC * GC / 8 / 64; ++i) {
+            const int u = lane + 64 * i;
+            *reinterpret_cast<u128*>(gT + 8 * u) = *reinterpret_cast<const u128*>(sO + 8 * u);
+        }
+        if (!next) break;
+        __syncthreads();  // sG/sB/sA/sO are rewritten for the next slot
     }
 }
 
@@ -462,7 +618,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
             for (int r = 0; r < 4; ++r) er[r] = sC[64 + 16 * tb + 4 * lg + r] * R[tb][r];
             ERb[tb] = Elem<ST>::pack(er);
         }
-        const float gl = sC[192];
+        const float gl = sC[63];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             f32x4 acc = S[kb] * gl;
@@ -808,7 +964,7 @@ __global__ __launch_bounds__(64 * (KS + 4)) void gdn_chain_ws_kernel(
                     }
                 }
             }
-            const float gl = sC[192];
+            const float gl = sC[63];
             f32x4 R[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
             for (int p = 0; p < 6; ++p)
@@ -886,9 +1042,18 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
     }
     if (slots > 0) {
         timing_begin("gdn_prep", s);
-        gdn_prep_kernel<ST, KD><<<dim3((unsigned)slots, H), 256, 0, s>>>(
-            q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, scale, mode == 0 ? 1 : 0,
-            ws.factors);
+        if constexpr (sizeof(ST) == 2) {
+            const unsigned gx = (unsigned)slots;
+            if (mode == 0)
+                gdn_prep_wave_kernel<KD, true><<<dim3(gx, H), 64, 0, s>>>(
+                    q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+            else
+                gdn_prep_wave_kernel<KD, false><<<dim3(gx, H), 64, 0, s>>>(
+                    q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+        } else
+            gdn_prep_kernel<ST, KD><<<dim3((unsigned)slots, H), 256, 0, s>>>(
+                q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, scale, mode == 0 ? 1 : 0,
+                ws.factors);
         timing_end(s);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
