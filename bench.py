@@ -142,6 +142,9 @@ def main():
                     choices=["dense_gdn", "tiny_gdn", "varlen_gdn", "long_gdn", "ssd_gla"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="do not bracket launches with HIP events")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a plain 512 MiB device-to-device copy three times (reference dispatches "
+                         "that scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -211,6 +214,16 @@ def main():
         "kernels": kernels,
         "cpu_baseline": None,
     }
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": n, "write": n}
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
