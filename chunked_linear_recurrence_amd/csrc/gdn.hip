@@ -685,7 +685,9 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
 //  - Loader wavefronts move chunk c+1 (K, Q, T, P, coefficients, the slice's V)
 //    from global memory into the other half of a double-buffered LDS stage
 //    and write chunk c-1's output tile to global memory with 16-byte stores,
-//    so the compute wavefronts never wait on vector memory.
+//    so the compute wavefronts never wait on vector memory. K^T fragments for
+//    the state update are read from the natural K tile with the transposing
+//    LDS read.
 //  Two workgroup barriers per chunk separate the exchange phases.
 // ---------------------------------------------------------------------------
 template <int KD, bool SUMMARY>
@@ -699,8 +701,7 @@ struct WsSmem {
     static constexpr int OFF_Q = OFF_V + 16 * LD * 2;
     static constexpr int OFF_P = OFF_Q + (SUMMARY ? 0 : GC * LDK * 2);
     static constexpr int BUF = OFF_P + (SUMMARY ? 0 : GC * LD * 2);
-    static constexpr int OFF_KT = 2 * BUF;                      // K^T [KD][LD] (single buffer)
-    static constexpr int OFF_S = OFF_KT + KD * LD * 2;          // state frags [KB][64] x 8 B
+    static constexpr int OFF_S = 2 * BUF;                       // state frags [KB][64] x 8 B
     static constexpr int OFF_Y = OFF_S + (KD / 16) * 64 * 8;    // Y frags [4][64] x 8 B
     static constexpr int OFF_O = OFF_Y + 4 * 64 * 8;            // output tiles [2][64][LDO] bf16
     static constexpr int BYTES = OFF_O + (SUMMARY ? 0 : 2 * GC * LDO * 2);
@@ -816,30 +817,6 @@ __global__ __launch_bounds__(64 * (KS + 4)) void gdn_chain_ws_kernel(
             for (int e = 0; e < E; ++e) sVT[(col + e) * LD + t] = unit_elem<bf16_t>(x, e);
         }
     };
-    // K^T of chunk c (single buffer) from the staged natural K: read during
-    // phase 1, consumed by the compute wavefronts in phase 2 of the same chunk
-    auto transpose_k = [&](int c) __attribute__((always_inline)) {
-        // one lane per (token pair p, k-octet m): two 16-byte row reads, then
-        // eight 4-byte writes K^T[8m+e][2p .. 2p+1]; the 64 lanes of a
-        // wavefront cover 32 pairs x 2 octets, which fall in distinct banks
-        const bf16_t* sK = reinterpret_cast<const bf16_t*>(buf_ptr(c) + SM::OFF_K);
-        bf16_t* sKT = reinterpret_cast<bf16_t*>(smem + SM::OFF_KT);
-        constexpr int NPO = (GC / 2) * UPR;  // pair-octets per chunk
-        static_assert(NPO % NLT == 0, "transpose tiling");
-#pragma unroll
-        for (int i = 0; i < NPO / NLT; ++i) {
-            const int w = lt + i * NLT;
-            const int p = w & 31, m = w >> 5;
-            const u128 x0 = *reinterpret_cast<const u128*>(sK + (2 * p) * LDK + 8 * m);
-            const u128 x1 = *reinterpret_cast<const u128*>(sK + (2 * p + 1) * LDK + 8 * m);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (x0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                const uint32_t hi = (x1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                *reinterpret_cast<uint32_t*>(sKT + (8 * m + e) * LD + 2 * p) = lo | (hi << 16);
-            }
-        }
-    };
     auto store_out = [&](int c) __attribute__((always_inline)) {  // output tile of chunk c from LDS to global
         if constexpr (!SUMMARY) {
             const int t0 = bos + c * GC, L = min(GC, eos - t0);
@@ -889,7 +866,6 @@ __global__ __launch_bounds__(64 * (KS + 4)) void gdn_chain_ws_kernel(
         const bool more = c + 1 < nch;
         // ---- phase 1: X = K S^T and Q S^T for own tokens, Y = beta (V - Gamma X) ----
         if (loader) {
-            transpose_k(c);
             if (c > 0) store_out(c - 1);
         } else {
             // every LDS operand of the phase is read before the first product
@@ -943,14 +919,13 @@ __global__ __launch_bounds__(64 * (KS + 4)) void gdn_chain_ws_kernel(
                 Tf[p][0] = frag_rows(sT, LD, 16 * TI[p], 16 * TJ[p]);
                 Tf[p][1] = frag_rows(sT, LD, 16 * TI[p], 16 * TJ[p] + 16);
             }
-            // K^T fragments of own state columns
-            const bf16_t* sKT = reinterpret_cast<const bf16_t*>(smem + SM::OFF_KT);
+            // K^T fragments of own state columns, read transposed from the natural K tile
 #pragma unroll
             for (int i = 0; i < KT; ++i)
 #pragma unroll
                 for (int tp = 0; tp < 2; ++tp) {
-                    Ka[i][tp][0] = frag_rows(sKT, LD, 16 * (j * KT + i), 32 * tp);
-                    Ka[i][tp][1] = frag_rows(sKT, LD, 16 * (j * KT + i), 32 * tp + 16);
+                    Ka[i][tp][0] = frag_rows_t(sK, LDK, 32 * tp, 16 * (j * KT + i));
+                    Ka[i][tp][1] = frag_rows_t(sK, LDK, 32 * tp + 16, 16 * (j * KT + i));
                 }
             if constexpr (!SUMMARY) {
 #pragma unroll
