@@ -263,6 +263,31 @@ __host__ __device__ constexpr int tri_off(int t) {  // sum_{s<t} round_up(s, 4)
 // each column padded to a multiple of 4 floats: sum_{i'<i} round_up(63 - i', 4).
 __host__ __device__ constexpr int col_off(int i) { return tri_off(GC) - tri_off(GC - i); }
 
+// Fragment order of a lower-triangular 64x64 bf16 block M (T or P), as the
+// MFMA operand the chain reads it in. Fragment f = FRAG_BASE[ti] + p covers
+// rows 16 ti .. 16 ti + 15 and columns 32 p .. 32 p + 31 (p <= ti / 2, the
+// blocks right of the diagonal tile being zero); lane (ln, lg) holds 16 bytes:
+// M[16 ti + ln][32 p + 4 lg + j] then M[16 ti + ln][32 p + 16 + 4 lg + j],
+// j = 0..3. That is the A operand of a 32-deep product reducing over the
+// block's columns against a right operand made of two consecutive 16-row
+// C tiles, and equally the B operand of the transposed product. Six
+// fragments, 6 KB.
+constexpr int kTriFrags = 6;
+__host__ __device__ constexpr int tri_frag(int ti, int p) { return (ti == 0 ? 0 : ti == 1 ? 1 : ti == 2 ? 2 : 4) + p; }
+
+// Write the six fragments of the row-major staged block m (row stride ld) to g.
+__device__ __forceinline__ void store_tri_frags(const bf16_t* m, int ld, bf16_t* g) {
+    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+        for (int p = 0; p <= ti / 2; ++p) {
+            const bf16_t* r = m + (16 * ti + ln) * ld + 32 * p + 4 * lg;
+            const uint2 lo = *reinterpret_cast<const uint2*>(r), hi = *reinterpret_cast<const uint2*>(r + 16);
+            *reinterpret_cast<u128*>(g + (tri_frag(ti, p) * 64 + lane) * 8) = u128{lo.x, lo.y, hi.x, hi.y};
+        }
+}
+
 template <int KD, bool WANT_P>
 __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                            const float* __restrict__ g,
@@ -273,8 +298,9 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
                                                            uint8_t* __restrict__ fac) {
     constexpr int KP = KD / 32;
     constexpr int NPW = 1;
+    constexpr int LO = GC + 8;  // staging tile row stride (bf16)
     __shared__ __align__(16) float sA[tri_off(GC)];
-    __shared__ __align__(16) bf16_t sO[GC * GC];
+    __shared__ __align__(16) bf16_t sO[GC * LO];
     __shared__ float sG[GC], sB[GC];
 
     const int h = blockIdx.y;
@@ -327,7 +353,7 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
             gC[192 + lane] = G;
         }
 #pragma unroll
-        for (int i = 0; i < GC * GC / 8 / 64; ++i) *reinterpret_cast<u128*>(sO + 8 * (lane + 64 * i)) = u128{0u, 0u, 0u, 0u};
+        for (int i = 0; i < GC * LO / 8 / 64; ++i) *reinterpret_cast<u128*>(sO + 8 * (lane + 64 * i)) = u128{0u, 0u, 0u, 0u};
         __syncthreads();
 
 #pragma unroll
@@ -345,17 +371,11 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
                 const int t = 16 * ti + 4 * lg + r, i = 16 * tj + ln;
                 const float d = expf(fminf(sG[t] - sG[i], 0.f));
                 if (i < t) sA[col_off(i) + (t - i - 1)] = sB[t] * d * a[r];
-                if (WANT_P && i <= t) sO[t * GC + i] = f2bf(scale * d * pq[r]);
+                if (WANT_P && i <= t) sO[t * LO + i] = f2bf(scale * d * pq[r]);
             }
         }
         __syncthreads();
-        if constexpr (WANT_P) {
-#pragma unroll
-            for (int i = 0; i < GC * GC / 8 / 64; ++i) {
-                const int u = lane + 64 * i;
-                *reinterpret_cast<u128*>(gP + 8 * u) = *reinterpret_cast<const u128*>(sO + 8 * u);
-            }
-        }
+        if constexpr (WANT_P) store_tri_frags(sO, LO, gP);
         // next slot's loads go out now (the fragment registers are free) and land during the solve
         const bool next = s + 1 < NPW && slot + 1 < n_slots && chunk_coords(slot + 1, table, cu, T, nc, b, t0, L);
         if (next) load(slot + 1);
@@ -385,14 +405,11 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
             for (int m = 0; m < 16; ++m) cur[m] = nxt[m];
         }
         __syncthreads();  // staging tile free again (P copy done)
+        // stored as T diag(beta): column j scaled by beta_j (zero past the chunk's end)
 #pragma unroll
-        for (int t = 0; t < GC; ++t) sO[t * GC + lane] = f2bf(x[t]);
+        for (int t = 0; t < GC; ++t) sO[t * LO + lane] = f2bf(x[t] * bv);
         __syncthreads();
-#pragma unroll
-        for (int i = 0; i < GC * GC / 8 / 64; ++i) {
-            const int u = lane + 64 * i;
-            *reinterpret_cast<u128*>(gT + 8 * u) = *reinterpret_cast<const u128*>(sO + 8 * u);
-        }
+        store_tri_frags(sO, LO, gT);
         if (!next) break;
         __syncthreads();  // sG/sB/sA/sO are rewritten for the next slot
     }
@@ -672,73 +689,87 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// ST + Out, bf16, warp-specialised: one workgroup = one 16-row state slice of
-// one chain, KS compute wavefronts + 4 loader wavefronts.
+// ST + Out, bf16: one workgroup = one 16-row state slice of one chain, four
+// wavefronts (one per SIMD).
 //
-//  - Compute wavefront j owns the state columns k in k-tiles [j KB/KS, (j+1) KB/KS)
-//    (float32 MFMA accumulators) and the tokens of t-tiles [j 4/KS, (j+1) 4/KS).
-//    The bf16 copy of the whole slice state is exchanged through LDS, so each
-//    wavefront forms X = K S^T and Q S^T for its own tokens over all k; the
-//    corrected values Y of all tokens are exchanged the same way; R = T Y is
-//    formed redundantly by every compute wavefront (6 MFMAs), which then
-//    updates its own state columns and writes its own output tokens.
-//  - Loader wavefronts move chunk c+1 (K, Q, T, P, coefficients, the slice's V)
-//    from global memory into the other half of a double-buffered LDS stage
-//    and write chunk c-1's output tile to global memory with 16-byte stores,
-//    so the compute wavefronts never wait on vector memory. K^T fragments for
-//    the state update are read from the natural K tile with the transposing
-//    LDS read.
-//  Two workgroup barriers per chunk separate the exchange phases.
+//  - Wavefront 0 runs the state recurrence alone, the slice state held in
+//    float32 MFMA accumulators for the whole chain: per chunk X = K S^T,
+//    Y = diag(beta) (V - diag(Gamma) X), R = T Y and S <- Gamma_L S + (e R)^T K,
+//    with no exchange between wavefronts on that path. The C tile of each
+//    product is the operand of the next as it stands (sf_device.h); beta is
+//    carried by the stored T (T diag(beta)), so Y = V - diag(Gamma) X here.
+//  - Wavefront 3 feeds it: it moves chunk c+3 (K, T, the slice's V, the
+//    coefficients) from global memory straight into LDS with 16-byte direct
+//    loads (no register staging) while the chain works on chunk c, four
+//    chunk buffers deep.
+//  - Wavefronts 1 and 2 form chunk c-1's output
+//    O^T = scale diag(Gamma) (S Q^T) + R^T P^T, two token tiles each, from
+//    the bf16 state and residual fragments wavefront 0 leaves in LDS, with
+//    Q and P fetched into registers one chunk ahead, and store it with
+//    8-byte row stores.
+//  One workgroup barrier per chunk.
+//
+// State tiles: S[kt], kt = 2p + h, is the C tile of S^T whose row 4 lg + j
+// stands for key column k = 32 p + 8 lg + 4 h + j and whose column ln for
+// state row row0 + ln. The pairs (S[2p], S[2p+1]) then give lane group lg the
+// eight consecutive columns 32 p + 8 lg .. + 7, so K and Q rows enter the
+// products as plain 16-byte row loads.
+//
+// K in LDS: fragment (u, p) (u = token tile, p = 32-column pair) is 1 KB,
+// slot 16 lg + (ln ^ 4 lg) holding K[16 u + ln][32 p + 8 lg .. + 7]. Row
+// fragments read one slot per lane; the transposed reads that build K^T
+// fragments for the state update take 8 bytes from 16 different slots per
+// 16 lanes. The XOR swizzle keeps both patterns free of bank conflicts.
 // ---------------------------------------------------------------------------
 template <int KD, bool SUMMARY>
-struct WsSmem {
-    static constexpr int E = 8;  // bf16 per 16-byte unit
-    static constexpr int LDK = KD + E, LD = GC + E, LDO = 16 + E;
-    static constexpr int OFF_K = 0;
-    static constexpr int OFF_T = OFF_K + GC * LDK * 2;
-    static constexpr int OFF_C = OFF_T + GC * LD * 2;
-    static constexpr int OFF_V = OFF_C + 256 * 4;
-    static constexpr int OFF_Q = OFF_V + 16 * LD * 2;
-    static constexpr int OFF_P = OFF_Q + (SUMMARY ? 0 : GC * LDK * 2);
-    static constexpr int BUF = OFF_P + (SUMMARY ? 0 : GC * LD * 2);
-    static constexpr int OFF_S = 2 * BUF;                       // state frags [KB][64] x 8 B
-    static constexpr int OFF_Y = OFF_S + (KD / 16) * 64 * 8;    // Y frags [4][64] x 8 B
-    static constexpr int OFF_O = OFF_Y + 4 * 64 * 8;            // output tiles [2][64][LDO] bf16
-    static constexpr int BYTES = OFF_O + (SUMMARY ? 0 : 2 * GC * LDO * 2);
+struct ChainLds {
+    static constexpr int KP = KD / 32, KB = KD / 16;
+    static constexpr int NBUF = 4;                                   // chunks c .. c+3 resident
+    static constexpr int OFF_K = 0;                                  // 4 KP fragments of 1 KB
+    static constexpr int OFF_T = OFF_K + 4 * KP * 1024;              // kTriFrags fragments of 1 KB
+    static constexpr int OFF_V = OFF_T + kTriFrags * 1024;           // V slice [64][16] bf16
+    static constexpr int OFF_C = OFF_V + GC * 16 * 2;                // coefficients float[256]
+    static constexpr int BUF = OFF_C + 256 * 4;
+    static constexpr int NLOAD = 4 * KP + kTriFrags + 2 + 1;         // direct-load instructions per chunk
+    static constexpr int OFF_SF = NBUF * BUF;                        // [2][KB][64] x 8 B  bf16 state
+    static constexpr int OFF_RB = OFF_SF + (SUMMARY ? 0 : 2 * KB * 512);  // [2][4][64] x 8 B  bf16 R
+    static constexpr int BYTES = OFF_RB + (SUMMARY ? 0 : 2 * 4 * 512);
 };
 
-template <int KD, int KS, bool SUMMARY>
-__global__ __launch_bounds__(64 * (KS + 4)) void gdn_chain_ws_kernel(
+__device__ __forceinline__ int kslot(int ln, int lg) { return 16 * lg + (ln ^ (4 * lg)); }
+
+// 16-byte direct load global -> LDS: lane l's 16 bytes land at dst + 16 l.
+__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 cat8(i16x4 x, i16x4 y) {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int KD, bool SUMMARY>
+__global__ __launch_bounds__(256) void gdn_chain_1w_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ h0, const int32_t* __restrict__ cu, const int* __restrict__ chunk_off,
     const uint8_t* __restrict__ fac, int T, int H, int HK, int V, int n_seq, int nc, int nvb,
     float scale, bf16_t* __restrict__ out, float* __restrict__ ht, float* __restrict__ Mout) {
-    typedef WsSmem<KD, SUMMARY> SM;
+    typedef ChainLds<KD, SUMMARY> SM;
     typedef Elem<bf16_t> El;
-    typedef El::frag frag;
-    constexpr int E = SM::E, LDK = SM::LDK, LD = SM::LD, LDO = SM::LDO;
-    constexpr int KB = KD / 16;
-    constexpr int KT = KB / KS;       // state k-tiles per compute wavefront
-    constexpr int TT = 4 / KS;        // token tiles per compute wavefront
-    constexpr int NLT = 256;          // loader threads
-    constexpr int UPR = KD / E;
-    constexpr int NUK = GC * UPR;
-    constexpr int NUT = GC * GC / E;
-    constexpr int PK = NUK / NLT, PT = NUT / NLT;
-    static_assert(KB % KS == 0 && 4 % KS == 0 && NUK % NLT == 0 && NUT % NLT == 0, "tiling");
+    constexpr int KP = SM::KP, KB = SM::KB;
 
     __shared__ __align__(16) uint8_t smem[SM::BYTES];
-    i16x4* sS = reinterpret_cast<i16x4*>(smem + SM::OFF_S);
-    i16x4* sY = reinterpret_cast<i16x4*>(smem + SM::OFF_Y);
 
     int chain, vb;
     xcd_split(blockIdx.x, nvb, chain, vb);
     if (chain >= n_seq * H) return;
     const int n = chain / H, h = chain % H, hk = h / (H / HK);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
-    const bool loader = wave >= KS;
-    const int row0 = 16 * vb;               // first state row of this slice
-    const bool vrows = row0 < V;            // value rows (else transition rows, summary only)
+    const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row0 = 16 * vb;       // first state row of this slice
+    const bool vrows = row0 < V;    // value rows (else transition rows, summary only)
 
     int b, bos, eos, slot0;
     if (cu) {
@@ -754,241 +785,246 @@ __global__ __launch_bounds__(64 * (KS + 4)) void gdn_chain_ws_kernel(
     }
     const int nch = (eos - bos + GC - 1) / GC;
     const size_t rec_bytes = gdn_factor_bytes(2);
-    auto buf_ptr = [&](int c) __attribute__((always_inline)) { return smem + (c & 1) * SM::BUF; };
+    auto buf = [&](int c) __attribute__((always_inline)) { return smem + (c % SM::NBUF) * SM::BUF; };
+    auto record = [&](int c) __attribute__((always_inline)) {
+        return fac + ((size_t)(slot0 + c) * H + h) * rec_bytes;
+    };
+    // Each role below runs its own loop with exactly one barrier per chunk (plus one before the
+    // first chunk), so the roles' registers never overlap; every wavefront's own memory traffic
+    // is complete (explicit waits) before it reaches a barrier.
+    auto barrier = [] __attribute__((always_inline)) () { asm volatile("s_barrier" ::: "memory"); };
 
-    // ---------------- loader role ----------------
-    const int lt = tid - 64 * KS;
-    u128 rk[PK], rq[PK], rt[PT], rp[PT], rc, rvv;
-    auto issue = [&](int c) __attribute__((always_inline)) {
-        const int t0 = bos + c * GC, L = min(GC, eos - t0);
-        const uint8_t* rec = fac + ((size_t)(slot0 + c) * H + h) * rec_bytes;
-        const bf16_t* gT = reinterpret_cast<const bf16_t*>(rec);
-        const bf16_t* gP = gT + GC * GC;
-        const float* gC = reinterpret_cast<const float*>(gP + GC * GC);
+    if (wave == 0) {
+        // ================= the state recurrence =================
+        f32x4 S[KB];
 #pragma unroll
-        for (int i = 0; i < PK; ++i) {
-            const int u = lt + i * NLT;
-            const int t = min(u / UPR, L - 1), col = (u % UPR) * E;
-            const size_t off = ((size_t)(b * T + t0 + t) * HK + hk) * KD + col;
-            rk[i] = *reinterpret_cast<const u128*>(k + off);
-            if constexpr (!SUMMARY) rq[i] = *reinterpret_cast<const u128*>(q + off);
-        }
-#pragma unroll
-        for (int i = 0; i < PT; ++i) {
-            const int u = lt + i * NLT;
-            rt[i] = *reinterpret_cast<const u128*>(gT + u * E);
-            if constexpr (!SUMMARY) rp[i] = *reinterpret_cast<const u128*>(gP + u * E);
-        }
-        if (lt < 64) rc = *reinterpret_cast<const u128*>(gC + 4 * lt);
-        if (vrows && lt < 128) {
-            const int t = min(lt >> 1, L - 1), col = (lt & 1) * E;
-            rvv = *reinterpret_cast<const u128*>(v + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + col);
-        }
-    };
-    auto commit = [&](int c) __attribute__((always_inline)) {
-        const int L = min(GC, eos - (bos + c * GC));
-        uint8_t* base = buf_ptr(c);
-        bf16_t* sK = reinterpret_cast<bf16_t*>(base + SM::OFF_K);
-        bf16_t* sT = reinterpret_cast<bf16_t*>(base + SM::OFF_T);
-        float* sC = reinterpret_cast<float*>(base + SM::OFF_C);
-        bf16_t* sVT = reinterpret_cast<bf16_t*>(base + SM::OFF_V);
-        bf16_t* sQ = reinterpret_cast<bf16_t*>(base + SM::OFF_Q);
-        bf16_t* sP = reinterpret_cast<bf16_t*>(base + SM::OFF_P);
-        const u128 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < PK; ++i) {
-            const int u = lt + i * NLT;
-            const int t = u / UPR, col = (u % UPR) * E;
-            *reinterpret_cast<u128*>(sK + t * LDK + col) = t < L ? rk[i] : zero;
-            if constexpr (!SUMMARY) *reinterpret_cast<u128*>(sQ + t * LDK + col) = t < L ? rq[i] : zero;
-        }
-#pragma unroll
-        for (int i = 0; i < PT; ++i) {
-            const int u = lt + i * NLT;
-            const int r = u / (GC / E), col = (u % (GC / E)) * E;
-            *reinterpret_cast<u128*>(sT + r * LD + col) = rt[i];
-            if constexpr (!SUMMARY) *reinterpret_cast<u128*>(sP + r * LD + col) = rp[i];
-        }
-        if (lt < 64) *reinterpret_cast<u128*>(sC + 4 * lt) = rc;
-        if (lt < 128) {
-            const int t = lt >> 1, col = (lt & 1) * E;
-            const u128 x = (vrows && t < L) ? rvv : zero;
-#pragma unroll
-            for (int e = 0; e < E; ++e) sVT[(col + e) * LD + t] = unit_elem<bf16_t>(x, e);
-        }
-    };
-    auto store_out = [&](int c) __attribute__((always_inline)) {  // output tile of chunk c from LDS to global
-        if constexpr (!SUMMARY) {
-            const int t0 = bos + c * GC, L = min(GC, eos - t0);
-            const bf16_t* sO = reinterpret_cast<const bf16_t*>(smem + SM::OFF_O) + (c & 1) * GC * LDO;
-            if (lt < 128) {
-                const int t = lt >> 1, col = (lt & 1) * E;
-                if (t < L)
-                    *reinterpret_cast<u128*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + col) =
-                        *reinterpret_cast<const u128*>(sO + t * LDO + col);
-            }
-        }
-    };
-
-    // ---------------- compute role ----------------
-    const int j = wave;  // compute wavefront index (valid when !loader)
-    f32x4 S[KT];
-    if (!loader) {
-#pragma unroll
-        for (int i = 0; i < KT; ++i) {
-            const int kt = j * KT + i, kk = 16 * kt + 4 * lg;
-            const int row = row0 + ln;
+        for (int kt = 0; kt < KB; ++kt) {
+            const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
             if constexpr (!SUMMARY) {
-                S[i] = h0 ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + row) * KD + kk) : zero4();
+                S[kt] = h0 ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + row) * KD + kk) : zero4();
             } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[i][r] = (!vrows && kk + r == row - V) ? 1.f : 0.f;
-            }
-            sS[kt * 64 + lane] = El::pack(S[i]);
-        }
-    } else if (nch > 0) {
-        issue(0);
-        commit(0);
-        if (nch > 1) issue(1);  // in flight across the first iteration
-    }
-    __syncthreads();
-
-    f32x4 QS[TT];
-    for (int c = 0; c < nch; ++c) {
-        const int t0 = bos + c * GC, L = min(GC, eos - t0);
-        const uint8_t* base = buf_ptr(c);
-        const bf16_t* sK = reinterpret_cast<const bf16_t*>(base + SM::OFF_K);
-        const bf16_t* sT = reinterpret_cast<const bf16_t*>(base + SM::OFF_T);
-        const float* sC = reinterpret_cast<const float*>(base + SM::OFF_C);
-        const bf16_t* sVT = reinterpret_cast<const bf16_t*>(base + SM::OFF_V);
-        const bf16_t* sQ = reinterpret_cast<const bf16_t*>(base + SM::OFF_Q);
-        const bf16_t* sP = reinterpret_cast<const bf16_t*>(base + SM::OFF_P);
-        const bool more = c + 1 < nch;
-        // ---- phase 1: X = K S^T and Q S^T for own tokens, Y = beta (V - Gamma X) ----
-        if (loader) {
-            if (c > 0) store_out(c - 1);
-        } else {
-            // every LDS operand of the phase is read before the first product
-            frag Sf[KB], Kf[TT][KB], Qf[TT][KB], Vf[TT];
-            f32x4 gam[TT], bet[TT];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) Sf[kb] = sS[kb * 64 + lane];
-#pragma unroll
-            for (int i = 0; i < TT; ++i) {
-                const int tt = j * TT + i;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    Kf[i][kb] = frag_rows(sK, LDK, 16 * tt, 16 * kb);
-                    if constexpr (!SUMMARY) Qf[i][kb] = frag_rows(sQ, LDK, 16 * tt, 16 * kb);
-                }
-                Vf[i] = frag_rows(sVT, LD, 0, 16 * tt);
-                gam[i] = *reinterpret_cast<const f32x4*>(sC + 16 * tt + 4 * lg);
-                bet[i] = *reinterpret_cast<const f32x4*>(sC + 128 + 16 * tt + 4 * lg);
-            }
-#pragma unroll
-            for (int i = 0; i < TT; ++i) {
-                const int tt = j * TT + i;
-                f32x4 x = zero4(), qs = zero4();
-#pragma unroll
-                for (int kb = 0; kb < KB; kb += 2) {
-                    x = El::mma2(x, Kf[i][kb], Kf[i][kb + 1], Sf[kb], Sf[kb + 1]);
-                    if constexpr (!SUMMARY) qs = El::mma2(qs, Qf[i][kb], Qf[i][kb + 1], Sf[kb], Sf[kb + 1]);
-                }
-                QS[i] = qs * gam[i] * scale;
-                const f32x4 vx = El::unpack(Vf[i]);
-                sY[tt * 64 + lane] = El::pack(bet[i] * (vx - gam[i] * x));
+                for (int r = 0; r < 4; ++r) S[kt][r] = (!vrows && kk + r == row - V) ? 1.f : 0.f;
             }
         }
-        __syncthreads();
-        // ---- phase 2: R = T Y, state update of own columns, own output tokens ----
-        if (loader) {
-            // chunk c+1 was issued one iteration ago; chunk c+2 stays in flight for the next one
-            if (more) commit(c + 1);
-            if (c + 2 < nch) issue(c + 2);
-        } else {
-            frag Yf[4], Tf[6][2], Ka[KT][2][2], Pf[TT][2][2];
-            f32x4 ec[4];
-            constexpr int TI[6] = {0, 1, 2, 2, 3, 3}, TJ[6] = {0, 0, 0, 2, 0, 2};
+        // chunk operands, read from LDS one barrier ahead of use
+        bf16x8 Kf[4][KP], Tf[kTriFrags];
+        f32x4 gam[4], ec[4];
+        i16x4 Vf[4];
+        float gl;
+        auto prefetch = [&](int c) __attribute__((always_inline)) {
+            const uint8_t* B = buf(c);
+            const float* sC = reinterpret_cast<const float*>(B + SM::OFF_C);
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                Yf[ti] = sY[ti * 64 + lane];
-                ec[ti] = *reinterpret_cast<const f32x4*>(sC + 64 + 16 * ti + 4 * lg);
+            for (int u = 0; u < 4; ++u) {
+                gam[u] = *reinterpret_cast<const f32x4*>(sC + 16 * u + 4 * lg);
+                ec[u] = *reinterpret_cast<const f32x4*>(sC + 64 + 16 * u + 4 * lg);
+                Vf[u] = vrows ? frag_rows_t(B + SM::OFF_V, 16, 16 * u, 0) : i16x4{0, 0, 0, 0};
             }
+            gl = sC[63];
 #pragma unroll
-            for (int p = 0; p < 6; ++p) {
-                Tf[p][0] = frag_rows(sT, LD, 16 * TI[p], 16 * TJ[p]);
-                Tf[p][1] = frag_rows(sT, LD, 16 * TI[p], 16 * TJ[p] + 16);
+            for (int f = 0; f < kTriFrags; ++f)
+                Tf[f] = *reinterpret_cast<const bf16x8*>(B + SM::OFF_T + f * 1024 + lane * 16);
+            // K row fragments last: X waits on them first
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int p = 0; p < KP; ++p)
+                    Kf[u][p] = *reinterpret_cast<const bf16x8*>(B + SM::OFF_K + (u * KP + p) * 1024 + kslot(ln, lg) * 16);
+        };
+        barrier();
+        if (nch > 0) prefetch(0);
+        for (int c = 0; c < nch; ++c) {
+            const uint8_t* B = buf(c);
+            // bf16 copy of the entry state: B operand of X, and left for the output wavefronts
+            i16x4 Sf[KB];
+#pragma unroll
+            for (int kt = 0; kt < KB; ++kt) Sf[kt] = El::pack(S[kt]);
+            // X = K S^T
+            f32x4 X[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                X[u] = zero4();
+#pragma unroll
+                for (int p = 0; p < KP; ++p) X[u] = mma32(Kf[u][p], cat8(Sf[2 * p], Sf[2 * p + 1]), X[u]);
             }
-            // K^T fragments of own state columns, read transposed from the natural K tile
+            // K^T fragments for the state update: transposed reads of the swizzled K fragments;
+            // lane i of group g points at token 16 u + 4 g + i/4, columns 32 p + 8 (i%4) + 4 h
+            i16x4 Ka[KB][4];
+            {
+                const uint8_t* BK = B + SM::OFF_K;
+                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 #pragma unroll
-            for (int i = 0; i < KT; ++i)
+                for (int kt = 0; kt < KB; ++kt)
 #pragma unroll
-                for (int tp = 0; tp < 2; ++tp) {
-                    Ka[i][tp][0] = frag_rows_t(sK, LDK, 32 * tp, 16 * (j * KT + i));
-                    Ka[i][tp][1] = frag_rows_t(sK, LDK, 32 * tp + 16, 16 * (j * KT + i));
-                }
+                    for (int u = 0; u < 4; ++u) {
+                        const int p = kt >> 1, hh = kt & 1;
+                        const int tl = 4 * lg + (ln >> 2), cl = ln & 3;
+                        const uint8_t* ptr = BK + (u * KP + p) * 1024 + kslot(tl, cl) * 16 + 8 * hh;
+                        Ka[kt][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ptr));
+                    }
+            }
             if constexpr (!SUMMARY) {
+                i16x4* sSf = reinterpret_cast<i16x4*>(smem + SM::OFF_SF) + (c & 1) * KB * 64;
 #pragma unroll
-                for (int i = 0; i < TT; ++i) {
-                    const int tt = j * TT + i;
-                    // all four 16-token blocks of the row; P's upper blocks are stored as zeros
+                for (int kt = 0; kt < KB; ++kt) sSf[kt * 64 + lane] = Sf[kt];
+            }
+            // Y = V - Gamma X (beta is folded into the stored T)
+            i16x4 Yf[4];
 #pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) {
-                        Pf[i][pp][0] = frag_rows(sP, LD, 16 * tt, 32 * pp);
-                        Pf[i][pp][1] = frag_rows(sP, LD, 16 * tt, 32 * pp + 16);
+            for (int u = 0; u < 4; ++u) Yf[u] = El::pack(El::unpack(Vf[u]) - gam[u] * X[u]);
+            // R = T diag(beta) Y (T lower triangular, fragment pairs of 32 columns)
+            f32x4 R[4];
+            const bf16x8 Y01 = cat8(Yf[0], Yf[1]), Y23 = cat8(Yf[2], Yf[3]);
+            R[0] = mma32(Tf[tri_frag(0, 0)], Y01, zero4());
+            R[1] = mma32(Tf[tri_frag(1, 0)], Y01, zero4());
+            R[2] = mma32(Tf[tri_frag(2, 1)], Y23, mma32(Tf[tri_frag(2, 0)], Y01, zero4()));
+            R[3] = mma32(Tf[tri_frag(3, 1)], Y23, mma32(Tf[tri_frag(3, 0)], Y01, zero4()));
+            i16x4 ER[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) ER[ti] = El::pack(R[ti] * ec[ti]);
+            if constexpr (!SUMMARY) {
+                i16x4* sRb = reinterpret_cast<i16x4*>(smem + SM::OFF_RB) + (c & 1) * 4 * 64;
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) sRb[ti * 64 + lane] = El::pack(R[ti]);
+            }
+            // S^T <- Gamma_L S^T + K^T (e R)
+            const bf16x8 E01 = cat8(ER[0], ER[1]), E23 = cat8(ER[2], ER[3]);
+#pragma unroll
+            for (int kt = 0; kt < KB; ++kt) {
+                f32x4 acc = S[kt] * gl;
+                acc = mma32(cat8(Ka[kt][0], Ka[kt][1]), E01, acc);
+                acc = mma32(cat8(Ka[kt][2], Ka[kt][3]), E23, acc);
+                S[kt] = acc;
+            }
+            // this chunk's LDS writes are complete before the barrier; the next chunk's operands
+            // (filled before the previous barrier) are read now and land while the barrier is waited on
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (c + 1 < nch) prefetch(c + 1);
+            barrier();
+        }
+#pragma unroll
+        for (int kt = 0; kt < KB; ++kt) {
+            const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
+            if (vrows) {
+                if (ht) *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + row) * KD + kk) = S[kt];
+            } else if constexpr (SUMMARY) {
+                *reinterpret_cast<f32x4*>(Mout + (((size_t)n * H + h) * KD + (row - V)) * KD + kk) = S[kt];
+            }
+        }
+    } else if (wave == 3) {
+        // ================= feeder: direct loads, chunk c+3 while the chain is on chunk c =================
+        // padded rows of a partial chunk repeat its last token (finite values that the stored
+        // T diag(beta) and e = 0 keep out of every result)
+        auto feed = [&](int c) __attribute__((always_inline)) {
+            const int t0 = bos + c * GC, L = min(GC, eos - t0);
+            uint8_t* B = buf(c);
+            const uint8_t* rec = record(c);
+#pragma unroll
+            for (int m = 0; m < SM::NLOAD; ++m) {
+                if (m < 4 * KP) {
+                    const int u = m / KP, p = m % KP;
+                    const int t = min(16 * u + (ln ^ (4 * lg)), L - 1);
+                    load_lds16(k + ((size_t)(b * T + t0 + t) * HK + hk) * KD + 32 * p + 8 * lg, B + SM::OFF_K + m * 1024);
+                } else if (m < 4 * KP + kTriFrags) {
+                    const int f = m - 4 * KP;
+                    load_lds16(rec + f * 1024 + lane * 16, B + SM::OFF_T + f * 1024);
+                } else if (m < 4 * KP + kTriFrags + 2) {
+                    // transition-row slices (summary mode) never read it: they load value rows 0..15
+                    // so that every chunk issues the same number of loads
+                    const int hv = m - 4 * KP - kTriFrags;
+                    const int t = min(32 * hv + (lane >> 1), L - 1);
+                    load_lds16(v + ((size_t)(b * T + t0 + t) * H + h) * V + (vrows ? row0 : 0) + 8 * (lane & 1),
+                               B + SM::OFF_V + hv * 1024);
+                } else {
+                    load_lds16(rec + 2 * GC * GC * 2 + lane * 16, B + SM::OFF_C);
+                }
+            }
+        };
+        // chunks 0 and 1 must have landed before the first barrier, chunk 2 before the second
+        for (int c = 0; c < min(nch, 3); ++c) feed(c);
+        if (nch > 2)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SM::NLOAD) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier();
+        for (int c = 0; c < nch; ++c) {
+            // this wavefront issues no other vector memory operation, so the count is exact
+            if (c + 3 < nch) {
+                feed(c + 3);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SM::NLOAD) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            barrier();
+        }
+    } else {
+        // ================= output: wavefront 1 tiles {0, 3}, wavefront 2 tiles {1, 2} =================
+        barrier();
+        if constexpr (!SUMMARY) {
+            struct OutRegs {
+                bf16x8 Qf[2][KP], Pf[2][2];
+                float gq[2];
+            };
+            auto tile_of = [&](int i) __attribute__((always_inline)) { return wave == 1 ? 3 * i : 1 + i; };
+            auto fetch_out = [&](int c, OutRegs& R) __attribute__((always_inline)) {  // Q, P, Gamma of chunk c
+                const int t0 = bos + c * GC, L = min(GC, eos - t0);
+                const uint8_t* rec = record(c);
+                const bf16_t* gP = reinterpret_cast<const bf16_t*>(rec + GC * GC * 2);
+                const float* gC = reinterpret_cast<const float*>(rec + 2 * GC * GC * 2);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int tt = tile_of(i);
+                    const int t = min(16 * tt + ln, L - 1);
+#pragma unroll
+                    for (int p = 0; p < KP; ++p)
+                        R.Qf[i][p] = *reinterpret_cast<const bf16x8*>(q + ((size_t)(b * T + t0 + t) * HK + hk) * KD + 32 * p + 8 * lg);
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+                        if (p <= tt / 2) R.Pf[i][p] = *reinterpret_cast<const bf16x8*>(gP + (tri_frag(tt, p) * 64 + lane) * 8);
+                    R.gq[i] = gC[16 * tt + ln];
+                }
+            };
+            auto emit_out = [&](int c, const OutRegs& R) __attribute__((always_inline)) {  // O of chunk c
+                const int t0 = bos + c * GC, L = min(GC, eos - t0);
+                const i16x4* sSf = reinterpret_cast<const i16x4*>(smem + SM::OFF_SF) + (c & 1) * KB * 64;
+                const i16x4* sRb = reinterpret_cast<const i16x4*>(smem + SM::OFF_RB) + (c & 1) * 4 * 64;
+                i16x4 Sf[KB], Rb[4];
+#pragma unroll
+                for (int kt = 0; kt < KB; ++kt) Sf[kt] = sSf[kt * 64 + lane];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) Rb[ti] = sRb[ti * 64 + lane];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int tt = tile_of(i);
+                    f32x4 qs = zero4();
+#pragma unroll
+                    for (int p = 0; p < KP; ++p) qs = mma32(cat8(Sf[2 * p], Sf[2 * p + 1]), R.Qf[i][p], qs);
+                    f32x4 o = qs * (R.gq[i] * scale);
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+                        if (p <= tt / 2) o = mma32(cat8(Rb[2 * p], Rb[2 * p + 1]), R.Pf[i][p], o);
+                    const int t = 16 * tt + ln;
+                    if (t < L) {
+                        const i16x4 ob = El::pack(o);
+                        *reinterpret_cast<i16x4*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + 4 * lg) = ob;
                     }
                 }
+            };
+            // chunk c: fetch chunk c's Q/P into F, emit chunk c-1 from E (register sets alternate)
+            auto step = [&](int c, OutRegs& F, const OutRegs& E) __attribute__((always_inline)) {
+                fetch_out(c, F);
+                if (c > 0) emit_out(c - 1, E);
+                barrier();
+            };
+            OutRegs RA, RB;
+            for (int c = 0; c < nch; c += 2) {
+                step(c, RA, RB);
+                if (c + 1 < nch) step(c + 1, RB, RA);
             }
-            const float gl = sC[63];
-            f32x4 R[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-            for (int p = 0; p < 6; ++p)
-                R[TI[p]] = El::mma2(R[TI[p]], Tf[p][0], Tf[p][1], Yf[TJ[p]], Yf[TJ[p] + 1]);
-            frag Rb[4], ER[4];
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                Rb[ti] = El::pack(R[ti]);
-                ER[ti] = El::pack(R[ti] * ec[ti]);
-            }
-            // own state columns: S^T[kt] <- Gamma_L S^T[kt] + K^T[kt, :] (e R)
-#pragma unroll
-            for (int i = 0; i < KT; ++i) {
-                f32x4 acc = S[i] * gl;
-                acc = El::mma2(acc, Ka[i][0][0], Ka[i][0][1], ER[0], ER[1]);
-                acc = El::mma2(acc, Ka[i][1][0], Ka[i][1][1], ER[2], ER[3]);
-                S[i] = acc;
-            }
-            if constexpr (!SUMMARY) {
-                bf16_t* sO = reinterpret_cast<bf16_t*>(smem + SM::OFF_O) + (c & 1) * GC * LDO;
-#pragma unroll
-                for (int i = 0; i < TT; ++i) {
-                    const int tt = j * TT + i;
-                    f32x4 acc = QS[i];
-#pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) acc = El::mma2(acc, Pf[i][pp][0], Pf[i][pp][1], Rb[2 * pp], Rb[2 * pp + 1]);
-                    const frag o = El::pack(acc);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sO[(16 * tt + 4 * lg + r) * LDO + ln] = (bf16_t)o[r];
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < KT; ++i) sS[(j * KT + i) * 64 + lane] = El::pack(S[i]);
-        }
-        __syncthreads();
-        (void)L;
-        (void)t0;
-    }
-    if (loader) {
-        if (nch > 0) store_out(nch - 1);
-    } else {
-#pragma unroll
-        for (int i = 0; i < KT; ++i) {
-            const int kt = j * KT + i, kk = 16 * kt + 4 * lg, row = row0 + ln;
-            if (vrows) {
-                if (ht) *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + row) * KD + kk) = S[i];
-            } else if constexpr (SUMMARY) {
-                *reinterpret_cast<f32x4*>(Mout + (((size_t)n * H + h) * KD + (row - V)) * KD + kk) = S[i];
-            }
+            if (nch > 0) emit_out(nch - 1, (nch - 1) & 1 ? RB : RA);
+        } else {
+            for (int c = 0; c < nch; ++c) barrier();
         }
     }
 }
@@ -1036,16 +1072,15 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
     const int chains = N * H;
     if (chains == 0) return hipSuccess;
     if constexpr (sizeof(ST) == 2) {
-        constexpr int KS = 4;
         const int nvb = rows / 16;
         const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * nvb);
         if (mode == 0) {
             timing_begin("gdn_chain", s);
-            gdn_chain_ws_kernel<KD, KS, false><<<grid, 64 * (KS + 4), 0, s>>>(
+            gdn_chain_1w_kernel<KD, false><<<grid, 256, 0, s>>>(
                 q, k, v, h0, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, nvb, scale, out, ht, nullptr);
         } else {
             timing_begin("gdn_summary_chain", s);
-            gdn_chain_ws_kernel<KD, KS, true><<<grid, 64 * (KS + 4), 0, s>>>(
+            gdn_chain_1w_kernel<KD, true><<<grid, 256, 0, s>>>(
                 q, k, v, nullptr, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, nvb, scale, nullptr, ht, Mout);
         }
         timing_end(s);
