@@ -88,21 +88,29 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
     }
 }
 
-// Locate chunk `slot`: batch row, first token, length. false past the end.
+// Locate chunk `slot`: batch row, first token, length, index of the chunk in
+// its sequence. false past the end.
 __device__ __forceinline__ bool chunk_coords(int slot, const int2* table, const int32_t* cu, int T,
-                                             int nc, int& b, int& t0, int& L) {
+                                             int nc, int& b, int& t0, int& L, int& ci) {
     if (table) {
         const int2 e = table[slot];
         if (e.x < 0) return false;
         b = 0;
         t0 = cu[e.x] + GC * e.y;
         L = min(GC, cu[e.x + 1] - t0);
+        ci = e.y;
     } else {
         b = slot / nc;
-        t0 = (slot % nc) * GC;
+        ci = slot % nc;
+        t0 = ci * GC;
         L = min(GC, T - t0);
     }
     return true;
+}
+__device__ __forceinline__ bool chunk_coords(int slot, const int2* table, const int32_t* cu, int T,
+                                             int nc, int& b, int& t0, int& L) {
+    int ci;
+    return chunk_coords(slot, table, cu, T, nc, b, t0, L, ci);
 }
 
 // ---------------------------------------------------------------------------
@@ -308,9 +316,9 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
     const int lane = threadIdx.x, ln = lane & 15, lg = lane >> 4;
     const bf16x8 zero8 = {};
 
-    bf16x8 kf[4][KP], qf[4][KP];
+    bf16x8 kf[4][KP], qf[4][KP], kp[4][KP];
     float gv, bv;
-    int b, t0, L;
+    int b, t0, L, ci;
     auto load = [&](int slot) __attribute__((always_inline)) {
         const int t_lane = min(lane, L - 1);
         const size_t gi = (size_t)(b * T + t0 + t_lane) * H + h;
@@ -328,13 +336,18 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
                     const bf16x8 qv = *reinterpret_cast<const bf16x8*>(q + row + 32 * p + 8 * lg);
                     qf[R][p] = t < L ? qv : zero8;
                 }
+                // rows of the preceding (always full) chunk of the same sequence, for W
+                // (a sequence's first chunk loads its own first row and discards it)
+                const int pt = ci > 0 ? t0 - GC + t : t0;
+                const bf16x8 pv = *reinterpret_cast<const bf16x8*>(k + ((size_t)(b * T + pt) * HK + hk) * KD + 32 * p + 8 * lg);
+                kp[R][p] = ci > 0 ? pv : zero8;
             }
         }
         (void)slot;
     };
 
     int slot = blockIdx.x * NPW;
-    if (slot >= n_slots || !chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
+    if (slot >= n_slots || !chunk_coords(slot, table, cu, T, nc, b, t0, L, ci)) return;
     load(slot);
     for (int s = 0; s < NPW; ++s, ++slot) {
         // gates of this slot (registers loaded with the slot's K/Q)
@@ -374,10 +387,32 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
                 if (WANT_P && i <= t) sO[t * LO + i] = f2bf(scale * d * pq[r]);
             }
         }
+        // W = K_c K_{c-1}^T (zero for a sequence's first chunk and for padded rows), as the A
+        // operand of W (e R)_{c-1}: fragment (u, p) holds, for lane (ln, lg), W[16 u + ln][32 p + 4 lg + j]
+        // then W[16 u + ln][32 p + 16 + 4 lg + j]. The C tile of K_{c-1} K_c^T (rows s, columns t) is
+        // exactly that lane content, so each fragment pairs two of those tiles without any shuffle.
+        {
+            bf16_t* gW = reinterpret_cast<bf16_t*>(rec + kGdnWOffset);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                f32x4 wt[4];
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) {
+                    wt[sb] = zero4();
+#pragma unroll
+                    for (int p = 0; p < KP; ++p) wt[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kp[sb][p], kf[u][p], wt[sb], 0, 0, 0);
+                }
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const i16x4 lo = Elem<bf16_t>::pack(wt[2 * p]), hi = Elem<bf16_t>::pack(wt[2 * p + 1]);
+                    *reinterpret_cast<i16x8*>(gW + ((2 * u + p) * 64 + lane) * 8) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            }
+        }
         __syncthreads();
         if constexpr (WANT_P) store_tri_frags(sO, LO, gP);
         // next slot's loads go out now (the fragment registers are free) and land during the solve
-        const bool next = s + 1 < NPW && slot + 1 < n_slots && chunk_coords(slot + 1, table, cu, T, nc, b, t0, L);
+        const bool next = s + 1 < NPW && slot + 1 < n_slots && chunk_coords(slot + 1, table, cu, T, nc, b, t0, L, ci);
         if (next) load(slot + 1);
 
         // forward substitution, lane = column j of T, right-looking: once row t
@@ -689,54 +724,92 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// ST + Out, bf16: one workgroup = one 16-row state slice of one chain, four
-// wavefronts (one per SIMD).
+// ST + Out, bf16: one workgroup = one 16-row state slice of one chain, eight
+// wavefronts.
 //
-//  - Wavefront 0 runs the state recurrence alone, the slice state held in
-//    float32 MFMA accumulators for the whole chain: per chunk X = K S^T,
-//    Y = diag(beta) (V - diag(Gamma) X), R = T Y and S <- Gamma_L S + (e R)^T K,
-//    with no exchange between wavefronts on that path. The C tile of each
-//    product is the operand of the next as it stands (sf_device.h); beta is
-//    carried by the stored T (T diag(beta)), so Y = V - diag(Gamma) X here.
-//  - Wavefront 3 feeds it: it moves chunk c+3 (K, T, the slice's V, the
-//    coefficients) from global memory straight into LDS with 16-byte direct
-//    loads (no register staging) while the chain works on chunk c, four
-//    chunk buffers deep.
-//  - Wavefronts 1 and 2 form chunk c-1's output
-//    O^T = scale diag(Gamma) (S Q^T) + R^T P^T, two token tiles each, from
-//    the bf16 state and residual fragments wavefront 0 leaves in LDS, with
-//    Q and P fetched into registers one chunk ahead, and store it with
-//    8-byte row stores.
+//  With S_c the entry state of chunk c, the key-state product is split as
+//        X_c = K_c S_c^T = Gamma_L(c-1) Z_c + W_c (e R)_{c-1},
+//        Z_c = K_c S_{c-1}^T,   W_c = K_c K_{c-1}^T  (from the Pre stage),
+//  so one chunk step is two independent streams, each on its own SIMD:
+//  - wavefront 0, residual:  X_c -> Y_c = V_c - diag(Gamma) X_c
+//                            -> R_c = T_c diag(beta) Y_c -> (e R)_c
+//  - wavefronts 1 and 2, state, one half of the key columns each:
+//                            S_c = Gamma_L S_{c-1} + K_{c-1}^T (e R)_{c-1}
+//                            -> Z_{c+1} = K_{c+1} S_c^T (each its half of the sum over k),
+//    the slice state held in float32 MFMA accumulators for the whole chain.
+//  Each step needs only (e R)_{c-1} and Z_c from the previous one; the
+//  wavefronts swap them through LDS once per chunk. Within a wavefront the
+//  C tile of each product is the operand of the next as it stands
+//  (sf_device.h).
+//  - Wavefronts 3 and 7 form the output, two token tiles each: in step c they
+//    build P_c^T = scale (D o K_c Q_c^T)^T from K and Q in LDS and keep it,
+//    with their Q_c fragments, in registers; in step c+1 they emit
+//    O_c^T = scale diag(Gamma) (S_c Q_c^T) + R_c^T P_c^T from the bf16 state
+//    and residual fragments the chain leaves in LDS (8-byte row stores).
+//  - Wavefronts 4, 5 and 6 feed everyone with 16-byte direct loads into LDS
+//    (no register staging; one wavefront alone issues them too slowly): in
+//    step c they move K of chunk c+2, Q, T, W, V and coefficients of chunk
+//    c+1. K and Q rows go four whole rows per load.
 //  One workgroup barrier per chunk.
 //
 // State tiles: S[kt], kt = 2p + h, is the C tile of S^T whose row 4 lg + j
 // stands for key column k = 32 p + 8 lg + 4 h + j and whose column ln for
 // state row row0 + ln. The pairs (S[2p], S[2p+1]) then give lane group lg the
 // eight consecutive columns 32 p + 8 lg .. + 7, so K and Q rows enter the
-// products as plain 16-byte row loads.
+// products as plain 16-byte row fragments.
 //
-// K in LDS: fragment (u, p) (u = token tile, p = 32-column pair) is 1 KB,
-// slot 16 lg + (ln ^ 4 lg) holding K[16 u + ln][32 p + 8 lg .. + 7]. Row
-// fragments read one slot per lane; the transposed reads that build K^T
-// fragments for the state update take 8 bytes from 16 different slots per
-// 16 lanes. The XOR swizzle keeps both patterns free of bank conflicts.
+// K and Q in LDS (RowBlock): 1 KB blocks of whole rows; the 16-byte piece b of
+// row r sits at piece b ^ swz(r) of its row. The row-fragment reads (16 rows,
+// one piece) and the transposed reads that build K^T fragments (4 rows x 4
+// pieces per 16 lanes) both hit 16 different bank groups.
 // ---------------------------------------------------------------------------
-template <int KD, bool SUMMARY>
-struct ChainLds {
-    static constexpr int KP = KD / 32, KB = KD / 16;
-    static constexpr int NBUF = 4;                                   // chunks c .. c+3 resident
-    static constexpr int OFF_K = 0;                                  // 4 KP fragments of 1 KB
-    static constexpr int OFF_T = OFF_K + 4 * KP * 1024;              // kTriFrags fragments of 1 KB
-    static constexpr int OFF_V = OFF_T + kTriFrags * 1024;           // V slice [64][16] bf16
-    static constexpr int OFF_C = OFF_V + GC * 16 * 2;                // coefficients float[256]
-    static constexpr int BUF = OFF_C + 256 * 4;
-    static constexpr int NLOAD = 4 * KP + kTriFrags + 2 + 1;         // direct-load instructions per chunk
-    static constexpr int OFF_SF = NBUF * BUF;                        // [2][KB][64] x 8 B  bf16 state
-    static constexpr int OFF_RB = OFF_SF + (SUMMARY ? 0 : 2 * KB * 512);  // [2][4][64] x 8 B  bf16 R
-    static constexpr int BYTES = OFF_RB + (SUMMARY ? 0 : 2 * 4 * 512);
+template <int KD>
+struct RowBlock {
+    static constexpr int RB = 2 * KD;          // bytes per row
+    static constexpr int RPB = 1024 / RB;      // rows per 1 KB block
+    static constexpr int PCS = RB / 16;        // 16-byte pieces per row
+    static constexpr int BYTES = 64 * RB;      // one 64-row chunk
+    static constexpr int NLOAD = BYTES / 1024; // direct-load instructions per chunk
+    __device__ static int swz(int r) {
+        return KD == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    }
+    __device__ static int off(int r, int b) { return (r / RPB) * 1024 + (r % RPB) * RB + ((b ^ swz(r)) * 16); }
 };
 
-__device__ __forceinline__ int kslot(int ln, int lg) { return 16 * lg + (ln ^ (4 * lg)); }
+template <int KD, bool SUMMARY>
+struct ChainLds {
+    typedef RowBlock<KD> RBk;
+    static constexpr int KP = KD / 32, KB = KD / 16;
+    // K of chunk c: row fragments in step c-1 (Z_c), transposed in step c (for the update with
+    // (e R)_c); loaded in step c-2
+    static constexpr int NK = 3;
+    static constexpr int KBUF = RBk::BYTES;
+    // Q of chunk c: read in step c (the Q fragments kept for O_c); loaded in step c-1
+    static constexpr int NQ = 2;
+    // T, W, V, coefficients and P of chunk c: step c; loaded in step c-1
+    static constexpr int NT = 2;
+    static constexpr int OFF_T = 0;                                  // kTriFrags fragments of 1 KB
+    static constexpr int OFF_W = OFF_T + kTriFrags * 1024;           // 8 fragments of 1 KB
+    static constexpr int OFF_V = OFF_W + 8 * 1024;                   // V slice [64][16] bf16
+    static constexpr int OFF_C = OFF_V + GC * 16 * 2;                // coefficients float[256]
+    static constexpr int OFF_P = OFF_C + 256 * 4;                    // kTriFrags fragments of 1 KB
+    static constexpr int TBUF = OFF_P + (SUMMARY ? 0 : kTriFrags * 1024);
+    static constexpr int OFF_KR = 0;
+    static constexpr int OFF_QR = OFF_KR + NK * KBUF;
+    static constexpr int OFF_TR = OFF_QR + (SUMMARY ? 0 : NQ * KBUF);
+    static constexpr int OFF_Z = OFF_TR + NT * TBUF;                 // [2 halves][2][4][64] x 16 B  float Z
+    static constexpr int ZHALF = 2 * 4 * 1024;
+    static constexpr int OFF_ER = OFF_Z + 2 * ZHALF;                 // [2][4][64] x 8 B   bf16 e R
+    static constexpr int OFF_SF = OFF_ER + 2 * 4 * 512;              // [2][KB][64] x 8 B  bf16 state
+    static constexpr int OFF_RB = OFF_SF + (SUMMARY ? 0 : 2 * KB * 512);  // [2][4][64] x 8 B  bf16 R
+    static constexpr int OFF_JUNK = OFF_RB + (SUMMARY ? 0 : 2 * 4 * 512);  // 256 B sink of cache warm-up loads
+    static constexpr int BYTES = OFF_JUNK + 256;
+    static_assert(BYTES <= 160 * 1024, "chain LDS plan exceeds the CU's 160 KB");
+};
+
+// s_waitcnt immediate for lgkmcnt(0) with the vector-memory and export counts left alone (gfx9
+// encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitLgkm0 = 0xC07F;
 
 // 16-byte direct load global -> LDS: lane l's 16 bytes land at dst + 16 l.
 __device__ __forceinline__ void load_lds16(const void* src, void* dst) {
@@ -751,23 +824,35 @@ __device__ __forceinline__ bf16x8 cat8(i16x4 x, i16x4 y) {
 }
 
 template <int KD, bool SUMMARY>
-__global__ __launch_bounds__(256) void gdn_chain_1w_kernel(
+__global__ __launch_bounds__(512) void gdn_chain_1w_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ h0, const int32_t* __restrict__ cu, const int* __restrict__ chunk_off,
     const uint8_t* __restrict__ fac, int T, int H, int HK, int V, int n_seq, int nc, int nvb,
     float scale, bf16_t* __restrict__ out, float* __restrict__ ht, float* __restrict__ Mout) {
     typedef ChainLds<KD, SUMMARY> SM;
+    typedef RowBlock<KD> RBk;
     typedef Elem<bf16_t> El;
     constexpr int KP = SM::KP, KB = SM::KB;
+    constexpr int UST = (16 / RBk::RPB) * 1024;  // byte step of one 16-row token tile in a row block
 
     __shared__ __align__(16) uint8_t smem[SM::BYTES];
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    lds_u8* const lds0 = (lds_u8*)smem;
+    auto opaque = [](lds_u8* p) __attribute__((always_inline)) { asm volatile("" : "+v"(p)); return p; };
 
     int chain, vb;
     xcd_split(blockIdx.x, nvb, chain, vb);
     if (chain >= n_seq * H) return;
     const int n = chain / H, h = chain % H, hk = h / (H / HK);
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Role numbers below: the CU places wavefront w of a workgroup on SIMD w % 4, so the two output
+    // roles (3 and 7), the heaviest in issued instructions, run as wavefronts 3 and 5, each beside a
+    // light role on its SIMD (role 5 runs as wavefront 7).
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wid == 5 ? 7 : wid == 7 ? 5 : wid;
     const int row0 = 16 * vb;       // first state row of this slice
     const bool vrows = row0 < V;    // value rows (else transition rows, summary only)
 
@@ -785,89 +870,63 @@ __global__ __launch_bounds__(256) void gdn_chain_1w_kernel(
     }
     const int nch = (eos - bos + GC - 1) / GC;
     const size_t rec_bytes = gdn_factor_bytes(2);
-    auto buf = [&](int c) __attribute__((always_inline)) { return smem + (c % SM::NBUF) * SM::BUF; };
+    auto kbuf = [&](int c) __attribute__((always_inline)) { return lds0 + SM::OFF_KR + (c % SM::NK) * SM::KBUF; };
+    auto qbuf = [&](int c) __attribute__((always_inline)) { return lds0 + SM::OFF_QR + (c % SM::NQ) * SM::KBUF; };
+    auto tbuf = [&](int c) __attribute__((always_inline)) { return lds0 + SM::OFF_TR + (c % SM::NT) * SM::TBUF; };
     auto record = [&](int c) __attribute__((always_inline)) {
         return fac + ((size_t)(slot0 + c) * H + h) * rec_bytes;
     };
-    // Each role below runs its own loop with exactly one barrier per chunk (plus one before the
-    // first chunk), so the roles' registers never overlap; every wavefront's own memory traffic
-    // is complete (explicit waits) before it reaches a barrier.
+    // lane offsets of row fragment (0, p) (16 rows, one 16-byte piece) and of the transposed-read
+    // pointer for column pair p (token 4 lg + ln/4, piece 4 p + ln%4) in a row block
+    auto roff_row = [&](int p) __attribute__((always_inline)) { return RBk::off(ln, 4 * p + lg); };
+    auto roff_tr = [&](int p) __attribute__((always_inline)) { return RBk::off(4 * lg + (ln >> 2), 4 * p + (ln & 3)); };
+    // Each role below runs its own loop with two barriers before the first chunk and one per
+    // chunk, so the roles' registers never overlap; every wavefront's own memory traffic is
+    // complete (explicit waits) before it reaches a barrier.
     auto barrier = [] __attribute__((always_inline)) () { asm volatile("s_barrier" ::: "memory"); };
 
     if (wave == 0) {
-        // ================= the state recurrence =================
-        f32x4 S[KB];
-#pragma unroll
-        for (int kt = 0; kt < KB; ++kt) {
-            const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
-            if constexpr (!SUMMARY) {
-                S[kt] = h0 ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + row) * KD + kk) : zero4();
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) S[kt][r] = (!vrows && kk + r == row - V) ? 1.f : 0.f;
-            }
-        }
-        // chunk operands, read from LDS one barrier ahead of use
-        bf16x8 Kf[4][KP], Tf[kTriFrags];
-        f32x4 gam[4], ec[4];
-        i16x4 Vf[4];
-        float gl;
-        auto prefetch = [&](int c) __attribute__((always_inline)) {
-            const uint8_t* B = buf(c);
-            const float* sC = reinterpret_cast<const float*>(B + SM::OFF_C);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                gam[u] = *reinterpret_cast<const f32x4*>(sC + 16 * u + 4 * lg);
-                ec[u] = *reinterpret_cast<const f32x4*>(sC + 64 + 16 * u + 4 * lg);
-                Vf[u] = vrows ? frag_rows_t(B + SM::OFF_V, 16, 16 * u, 0) : i16x4{0, 0, 0, 0};
-            }
-            gl = sC[63];
-#pragma unroll
-            for (int f = 0; f < kTriFrags; ++f)
-                Tf[f] = *reinterpret_cast<const bf16x8*>(B + SM::OFF_T + f * 1024 + lane * 16);
-            // K row fragments last: X waits on them first
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int p = 0; p < KP; ++p)
-                    Kf[u][p] = *reinterpret_cast<const bf16x8*>(B + SM::OFF_K + (u * KP + p) * 1024 + kslot(ln, lg) * 16);
-        };
+        // ================= residual stream =================
+        const int off_frag = lane * 16;                                             // W, T fragments
+        const int off_coef = 16 * lg;                                               // coefficient rows
+        const int off_v = ((4 * lg + (ln >> 2)) * 16 + 4 * (ln & 3)) * 2;           // V read transposed
+        const uint32_t vmask = vrows ? 0xffffffffu : 0u;  // transition rows (summary) carry no values
         barrier();
-        if (nch > 0) prefetch(0);
+        barrier();
+        float glp = 1.f;    // Gamma_L of chunk c-1
+        i16x4 ERp[4];       // (e R)_{c-1}
         for (int c = 0; c < nch; ++c) {
-            const uint8_t* B = buf(c);
-            // bf16 copy of the entry state: B operand of X, and left for the output wavefronts
-            i16x4 Sf[KB];
-#pragma unroll
-            for (int kt = 0; kt < KB; ++kt) Sf[kt] = El::pack(S[kt]);
-            // X = K S^T
+            lds_u8* tb = tbuf(c);
+            lds_u8* xb = lds0 + SM::OFF_Z + (c & 1) * 4 * 1024 + off_frag;            // Z halves, 16 B / lane
+            lds_u8* eb = lds0 + SM::OFF_ER + (c & 1) * 4 * 512 + lane * 8;            // e R, R fragments
+            lds_u8* fb = tb + off_frag;
+            lds_u8* cb = tb + SM::OFF_C + off_coef;
+            lds_u8* vb_ = tb + SM::OFF_V + off_v;
+            asm volatile("" : "+v"(xb), "+v"(eb), "+v"(fb), "+v"(cb), "+v"(vb_));
             f32x4 X[4];
 #pragma unroll
+            for (int u = 0; u < 4; ++u) X[u] = *(const lds_f32x4*)(xb + u * 1024) + *(const lds_f32x4*)(xb + SM::ZHALF + u * 1024);
+            bf16x8 Wf[8], Tf[kTriFrags];
+            f32x4 gam[4], ec[4];
+            i16x4 Vf[4];
+#pragma unroll
+            for (int f = 0; f < 8; ++f) Wf[f] = *(const lds_bf16x8*)(fb + SM::OFF_W + f * 1024);
+#pragma unroll
+            for (int f = 0; f < kTriFrags; ++f) Tf[f] = *(const lds_bf16x8*)(fb + SM::OFF_T + f * 1024);
+#pragma unroll
             for (int u = 0; u < 4; ++u) {
-                X[u] = zero4();
-#pragma unroll
-                for (int p = 0; p < KP; ++p) X[u] = mma32(Kf[u][p], cat8(Sf[2 * p], Sf[2 * p + 1]), X[u]);
+                gam[u] = *(const lds_f32x4*)(cb + 64 * u);
+                ec[u] = *(const lds_f32x4*)(cb + 256 + 64 * u);
+                const i16x4 vx = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_ + 16 * u * 16 * 2));
+                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                Vf[u] = __builtin_bit_cast(i16x4, __builtin_bit_cast(u32x2, vx) & vmask);
             }
-            // K^T fragments for the state update: transposed reads of the swizzled K fragments;
-            // lane i of group g points at token 16 u + 4 g + i/4, columns 32 p + 8 (i%4) + 4 h
-            i16x4 Ka[KB][4];
-            {
-                const uint8_t* BK = B + SM::OFF_K;
-                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const float gl = *(const __attribute__((address_space(3))) float*)(tb + SM::OFF_C + 63 * 4);
+            // X_c = Gamma_L(c-1) Z_c + W_c (e R)_{c-1}
+            if (c > 0) {
+                const bf16x8 E01 = cat8(ERp[0], ERp[1]), E23 = cat8(ERp[2], ERp[3]);
 #pragma unroll
-                for (int kt = 0; kt < KB; ++kt)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int p = kt >> 1, hh = kt & 1;
-                        const int tl = 4 * lg + (ln >> 2), cl = ln & 3;
-                        const uint8_t* ptr = BK + (u * KP + p) * 1024 + kslot(tl, cl) * 16 + 8 * hh;
-                        Ka[kt][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ptr));
-                    }
-            }
-            if constexpr (!SUMMARY) {
-                i16x4* sSf = reinterpret_cast<i16x4*>(smem + SM::OFF_SF) + (c & 1) * KB * 64;
-#pragma unroll
-                for (int kt = 0; kt < KB; ++kt) sSf[kt * 64 + lane] = Sf[kt];
+                for (int u = 0; u < 4; ++u) X[u] = mma32(Wf[2 * u + 1], E23, mma32(Wf[2 * u], E01, X[u] * glp));
             }
             // Y = V - Gamma X (beta is folded into the stored T)
             i16x4 Yf[4];
@@ -880,130 +939,350 @@ __global__ __launch_bounds__(256) void gdn_chain_1w_kernel(
             R[1] = mma32(Tf[tri_frag(1, 0)], Y01, zero4());
             R[2] = mma32(Tf[tri_frag(2, 1)], Y23, mma32(Tf[tri_frag(2, 0)], Y01, zero4()));
             R[3] = mma32(Tf[tri_frag(3, 1)], Y23, mma32(Tf[tri_frag(3, 0)], Y01, zero4()));
-            i16x4 ER[4];
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) ER[ti] = El::pack(R[ti] * ec[ti]);
+            for (int ti = 0; ti < 4; ++ti) {
+                ERp[ti] = El::pack(R[ti] * ec[ti]);
+                *(lds_i16x4*)(eb + ti * 512) = ERp[ti];
+            }
             if constexpr (!SUMMARY) {
-                i16x4* sRb = reinterpret_cast<i16x4*>(smem + SM::OFF_RB) + (c & 1) * 4 * 64;
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) sRb[ti * 64 + lane] = El::pack(R[ti]);
+                for (int ti = 0; ti < 4; ++ti) *(lds_i16x4*)(eb + (SM::OFF_RB - SM::OFF_ER) + ti * 512) = El::pack(R[ti]);
             }
-            // S^T <- Gamma_L S^T + K^T (e R)
-            const bf16x8 E01 = cat8(ER[0], ER[1]), E23 = cat8(ER[2], ER[3]);
-#pragma unroll
-            for (int kt = 0; kt < KB; ++kt) {
-                f32x4 acc = S[kt] * gl;
-                acc = mma32(cat8(Ka[kt][0], Ka[kt][1]), E01, acc);
-                acc = mma32(cat8(Ka[kt][2], Ka[kt][3]), E23, acc);
-                S[kt] = acc;
-            }
-            // this chunk's LDS writes are complete before the barrier; the next chunk's operands
-            // (filled before the previous barrier) are read now and land while the barrier is waited on
+            glp = gl;
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (c + 1 < nch) prefetch(c + 1);
             barrier();
         }
+    } else if (wave == 1 || wave == 2) {
+        // ================= state stream, one half of the key columns per wavefront =================
+        // wavefront 1 holds key tiles [0, KB/2), wavefront 2 [KB/2, KB): each updates its half of the
+        // state and forms its half of the sum over k in Z; the residual stream adds the two halves
+        constexpr int KH = KB / 2, KPH = KP / 2;
+        const int half = wave - 1, kt0 = half * KH, p0 = half * KPH;
+        f32x4 S[KH];
 #pragma unroll
-        for (int kt = 0; kt < KB; ++kt) {
+        for (int i = 0; i < KH; ++i) {
+            const int kt = kt0 + i;
             const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
-            if (vrows) {
-                if (ht) *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + row) * KD + kk) = S[kt];
-            } else if constexpr (SUMMARY) {
-                *reinterpret_cast<f32x4*>(Mout + (((size_t)n * H + h) * KD + (row - V)) * KD + kk) = S[kt];
+            if constexpr (!SUMMARY) {
+                S[i] = h0 ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + row) * KD + kk) : zero4();
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[i][r] = (!vrows && kk + r == row - V) ? 1.f : 0.f;
             }
         }
-    } else if (wave == 3) {
-        // ================= feeder: direct loads, chunk c+3 while the chain is on chunk c =================
-        // padded rows of a partial chunk repeat its last token (finite values that the stored
-        // T diag(beta) and e = 0 keep out of every result)
-        auto feed = [&](int c) __attribute__((always_inline)) {
-            const int t0 = bos + c * GC, L = min(GC, eos - t0);
-            uint8_t* B = buf(c);
-            const uint8_t* rec = record(c);
+        int orow[KPH], otr[KPH];
 #pragma unroll
-            for (int m = 0; m < SM::NLOAD; ++m) {
-                if (m < 4 * KP) {
-                    const int u = m / KP, p = m % KP;
-                    const int t = min(16 * u + (ln ^ (4 * lg)), L - 1);
-                    load_lds16(k + ((size_t)(b * T + t0 + t) * HK + hk) * KD + 32 * p + 8 * lg, B + SM::OFF_K + m * 1024);
-                } else if (m < 4 * KP + kTriFrags) {
-                    const int f = m - 4 * KP;
-                    load_lds16(rec + f * 1024 + lane * 16, B + SM::OFF_T + f * 1024);
-                } else if (m < 4 * KP + kTriFrags + 2) {
-                    // transition-row slices (summary mode) never read it: they load value rows 0..15
-                    // so that every chunk issues the same number of loads
-                    const int hv = m - 4 * KP - kTriFrags;
-                    const int t = min(32 * hv + (lane >> 1), L - 1);
-                    load_lds16(v + ((size_t)(b * T + t0 + t) * H + h) * V + (vrows ? row0 : 0) + 8 * (lane & 1),
-                               B + SM::OFF_V + hv * 1024);
-                } else {
-                    load_lds16(rec + 2 * GC * GC * 2 + lane * 16, B + SM::OFF_C);
+        for (int i = 0; i < KPH; ++i) {
+            orow[i] = roff_row(p0 + i);
+            otr[i] = roff_tr(p0 + i);
+        }
+        bf16x8 Kf[4][KPH];
+        auto read_krow = [&](int c) __attribute__((always_inline)) {  // K_c rows, own column pairs
+#pragma unroll
+            for (int i = 0; i < KPH; ++i) {
+                lds_u8* B = opaque(kbuf(c) + orow[i]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) Kf[u][i] = *(lds_bf16x8*)(B + u * UST);
+            }
+        };
+        // K^T fragments of chunk c, own key tiles: transposed reads of the row blocks; lane i of
+        // group g points at token 16 u + 4 g + i/4, columns 32 p + 8 (i%4) + 4 h
+        i16x4 Ka[KH][4];
+        auto read_kt = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < KPH; ++i) {
+                lds_u8* B = opaque(kbuf(c) + otr[i]);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        Ka[2 * i + hh][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(B + u * UST + 8 * hh));
+            }
+        };
+        i16x4 ER[4];
+        auto read_er = [&](int c) __attribute__((always_inline)) {  // (e R)_c from the residual stream
+            lds_u8* B = opaque(lds0 + SM::OFF_ER + (c & 1) * 4 * 512 + lane * 8);
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) ER[ti] = *(lds_i16x4*)(B + ti * 512);
+        };
+        auto update = [&](float glp) __attribute__((always_inline)) {  // S <- glp S + K^T (e R)
+            const bf16x8 E01 = cat8(ER[0], ER[1]), E23 = cat8(ER[2], ER[3]);
+#pragma unroll
+            for (int i = 0; i < KH; ++i) {
+                f32x4 acc = S[i] * glp;
+                acc = mma32(cat8(Ka[i][0], Ka[i][1]), E01, acc);
+                acc = mma32(cat8(Ka[i][2], Ka[i][3]), E23, acc);
+                S[i] = acc;
+            }
+        };
+        auto pack_state = [&](int c, i16x4 (&Sf)[KH]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < KH; ++i) Sf[i] = El::pack(S[i]);
+            if constexpr (!SUMMARY) {
+                lds_u8* B = opaque(lds0 + SM::OFF_SF + (c & 1) * KB * 512 + kt0 * 512 + lane * 8);
+#pragma unroll
+                for (int i = 0; i < KH; ++i) *(lds_i16x4*)(B + i * 512) = Sf[i];
+            }
+        };
+        // partial Z_c = K_c[:, own columns] S[:, own columns]^T, left for the residual stream
+        auto z_of = [&](const i16x4 (&Sf)[KH], f32x4 (&Zn)[4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                Zn[u] = zero4();
+#pragma unroll
+                for (int i = 0; i < KPH; ++i) Zn[u] = mma32(Kf[u][i], cat8(Sf[2 * i], Sf[2 * i + 1]), Zn[u]);
+            }
+        };
+        auto store_z = [&](int c, const f32x4 (&Zn)[4]) __attribute__((always_inline)) {
+            lds_u8* zb = opaque(lds0 + SM::OFF_Z + half * SM::ZHALF + (c & 1) * 4 * 1024 + lane * 16);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) *(lds_f32x4*)(zb + u * 1024) = Zn[u];
+        };
+        barrier();
+        if (nch > 0) {
+            read_krow(0);
+            i16x4 Sf[KH];
+#pragma unroll
+            for (int i = 0; i < KH; ++i) Sf[i] = El::pack(S[i]);
+            f32x4 Zn[4];
+            z_of(Sf, Zn);
+            store_z(0, Zn);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        barrier();
+        float glp = 1.f;
+        // The LDS wait counter holds at most 15 operations in flight and counts them in issue order,
+        // so the phases below are pinned (sched_barrier) such that each wait is on the newest group:
+        // e R -> (K_{c+1} rows out) -> update -> bf16 state out -> Z (waits on K rows only)
+        // -> (K_c^T out) -> Z out.
+        for (int c = 0; c < nch; ++c) {
+            const bool more = c + 1 < nch;
+            const float gl = *(const __attribute__((address_space(3))) float*)(tbuf(c) + SM::OFF_C + 63 * 4);
+            if (c > 0) read_er(c - 1);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // (the compiler's counter model sees this form)
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) read_krow(c + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // S_c = Gamma_L(c-1) S_{c-1} + K_{c-1}^T (e R)_{c-1}
+            if (c > 0) update(glp);
+            i16x4 Sf[KH];
+            pack_state(c, Sf);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) {
+                // Z_{c+1} = K_{c+1} S_c^T (own half of the sum)
+                f32x4 Zn[4];
+                z_of(Sf, Zn);
+                __builtin_amdgcn_sched_barrier(0);
+                // K^T of chunk c for the next update: lands while Z finishes and the barrier is waited on
+                read_kt(c);
+                store_z(c + 1, Zn);
+            } else {
+                read_kt(c);
+            }
+            glp = gl;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            barrier();
+        }
+        // exit state S_nch = Gamma_L S_{nch-1} + K_{nch-1}^T (e R)_{nch-1}
+        if (nch > 0) {
+            read_er(nch - 1);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            update(glp);
+        }
+#pragma unroll
+        for (int i = 0; i < KH; ++i) {
+            const int kt = kt0 + i;
+            const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
+            if (vrows) {
+                if (ht) *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + row) * KD + kk) = S[i];
+            } else if constexpr (SUMMARY) {
+                *reinterpret_cast<f32x4*>(Mout + (((size_t)n * H + h) * KD + (row - V)) * KD + kk) = S[i];
+            }
+        }
+    } else if (wave >= 4 && wave <= 6) {
+        // ================= feeders: direct loads into LDS, three wavefronts =================
+        // One wavefront issues these loads at a fraction of the rate several do, so the chunk's loads
+        // are split by kind: wavefront 4 the K rows (and a cache warm-up), 5 the Q rows and the P part
+        // of the record, 6 the other record parts (T, W, coefficients) and the V slice. Every lane offset is computed once; a load is
+        // then a scalar base, an LDS destination and the load itself. Rows past the end of a partial
+        // chunk repeat its last token (finite values that the stored T diag(beta), W and e = 0 keep out
+        // of every result, and that the output never stores).
+        const int fi = wave - 4;
+        constexpr int NPAT = 16 / RBk::RPB;  // the swizzle repeats every 16 rows = NPAT row blocks
+        const size_t krs = (size_t)HK * KD * 2, vrs = (size_t)H * V * 2;  // token strides (bytes)
+        // row-block loads: instruction m, lane l -> row m RPB + l / PCS, piece (l % PCS) ^ swz(row)
+        uint32_t rowoff[NPAT];
+#pragma unroll
+        for (int j = 0; j < NPAT; ++j) {
+            const int r = j * RBk::RPB + lane / RBk::PCS;
+            rowoff[j] = (uint32_t)((lane / RBk::PCS) * krs) + 16u * (uint32_t)((lane % RBk::PCS) ^ RBk::swz(r));
+        }
+        auto feed_rows = [&](const bf16_t* src, int c, lds_u8* dst) __attribute__((always_inline)) {
+            const int t0 = bos + c * GC, L = min(GC, eos - t0);
+            const uint8_t* base = reinterpret_cast<const uint8_t*>(src + ((size_t)(b * T + t0) * HK + hk) * KD);
+            if (L == GC) {
+#pragma unroll
+                for (int m = 0; m < RBk::NLOAD; ++m)
+                    load_lds16(base + (size_t)(m * RBk::RPB) * krs + rowoff[m % NPAT], (uint8_t*)(dst + m * 1024));
+            } else {
+#pragma unroll
+                for (int m = 0; m < RBk::NLOAD; ++m) {
+                    const int r = m * RBk::RPB + lane / RBk::PCS, pc = lane % RBk::PCS;
+                    const int t = min(r, L - 1);
+                    load_lds16(base + (size_t)t * krs + 16 * (pc ^ RBk::swz(r)), (uint8_t*)(dst + m * 1024));
                 }
             }
         };
-        // chunks 0 and 1 must have landed before the first barrier, chunk 2 before the second
-        for (int c = 0; c < min(nch, 3); ++c) feed(c);
-        if (nch > 2)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SM::NLOAD) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const uint32_t voff = (uint32_t)((lane >> 1) * vrs) + (uint32_t)(((vrows ? row0 : 0) + 8 * (lane & 1)) * 2);
+        auto feed_t = [&](int c) __attribute__((always_inline)) {
+            const int t0 = bos + c * GC, L = min(GC, eos - t0);
+            lds_u8* B = tbuf(c);
+            const uint8_t* rec = record(c) + lane * 16;
+#pragma unroll
+            for (int f = 0; f < kTriFrags; ++f) load_lds16(rec + f * 1024, (uint8_t*)(B + SM::OFF_T + f * 1024));
+#pragma unroll
+            for (int f = 0; f < 8; ++f) load_lds16(rec + kGdnWOffset + f * 1024, (uint8_t*)(B + SM::OFF_W + f * 1024));
+            load_lds16(rec + 2 * GC * GC * 2, (uint8_t*)(B + SM::OFF_C));
+            // V slice [64][16]; transition-row slices (summary mode) never read it: they load value rows 0..15
+            const uint8_t* vb0 = reinterpret_cast<const uint8_t*>(v + (size_t)(b * T + t0) * H * V + (size_t)h * V);
+#pragma unroll
+            for (int hv = 0; hv < 2; ++hv) {
+                if (L == GC) {
+                    load_lds16(vb0 + (size_t)(32 * hv) * vrs + voff, (uint8_t*)(B + SM::OFF_V + hv * 1024));
+                } else {
+                    const int t = min(32 * hv + (lane >> 1), L - 1);
+                    load_lds16(vb0 + (size_t)t * vrs + ((vrows ? row0 : 0) + 8 * (lane & 1)) * 2,
+                               (uint8_t*)(B + SM::OFF_V + hv * 1024));
+                }
+            }
+        };
+        auto feed_p = [&](int c) __attribute__((always_inline)) {
+            const uint8_t* rec = record(c) + GC * GC * 2 + lane * 16;
+#pragma unroll
+            for (int f = 0; f < kTriFrags; ++f) load_lds16(rec + f * 1024, (uint8_t*)(tbuf(c) + SM::OFF_P + f * 1024));
+        };
+        // Cache warm-up (wavefront 4): the direct loads run one step ahead, so the lines of chunk c+4 are
+        // touched now (one 4-byte load per 128-byte line: the rows of K, Q and V of the head, the T, W,
+        // coefficient and P parts of the record) and sit in this XCD's L2 when their loads come. The
+        // head's slices share the lines: slice vb touches line li = (64 vb + lane) mod (list length) and,
+        // with P, line min(li + 512, last) of the chunk's list (duplicates are harmless).
+        constexpr int NLINES = 504 + (SUMMARY ? 0 : 48);
+        constexpr int NWARM = NLINES > 512 ? 2 : 1;
+        auto warm_line = [&](int c, int li) __attribute__((always_inline)) {
+            const int t0 = bos + c * GC, L = min(GC, eos - t0);
+            const uint8_t* a;
+            if (li < 256) {        // K rows (0..127), Q rows (128..255): two 128-byte lines per row
+                const int t = min((li & 127) >> 1, L - 1);
+                const bf16_t* base = li < 128 ? k : (SUMMARY ? k : q);
+                a = reinterpret_cast<const uint8_t*>(base + ((size_t)(b * T + t0 + t) * HK + hk) * KD) + (li & 1) * (KD >= 128 ? 128 : 0);
+            } else if (li < 384) { // V rows of the head (two lines per token)
+                const int t = min((li - 256) >> 1, L - 1);
+                a = reinterpret_cast<const uint8_t*>(v + ((size_t)(b * T + t0 + t) * H + h) * V) + (li & 1) * (V >= 128 ? 128 : 0);
+            } else {               // record: T (48 lines), coefficients (8), W (64), P (48)
+                const int r = li - 384;
+                const size_t off = r < 48    ? (size_t)r * 128
+                                   : r < 56  ? (size_t)2 * GC * GC * 2 + (r - 48) * 128
+                                   : r < 120 ? kGdnWOffset + (size_t)(r - 56) * 128
+                                             : (size_t)GC * GC * 2 + (r - 120) * 128;
+                a = record(c) + off;
+            }
+            __builtin_amdgcn_global_load_lds(a, (__attribute__((address_space(3))) void*)(smem + SM::OFF_JUNK), 4, 0, 0);
+        };
+        const int li = (64 * vb + lane) % NLINES;
+        auto warm = [&](int c) __attribute__((always_inline)) {
+            warm_line(c, li);
+            if constexpr (NWARM == 2) warm_line(c, min(li + 512, NLINES - 1));
+        };
+        // one step of this wavefront's share: chunk c+2 of K, chunk c+1 of Q and of the record/V
+        auto feed = [&](int cK, int cR) __attribute__((always_inline)) {
+            if (fi == 0) {
+                if (cK < nch) feed_rows(k, cK, kbuf(cK));
+            } else if (fi == 1) {
+                if constexpr (!SUMMARY)
+                    if (cR < nch) {
+                        feed_rows(q, cR, qbuf(cR));
+                        feed_p(cR);
+                    }
+            } else {
+                if (cR < nch) feed_t(cR);
+            }
+        };
+        // everything read before the first chunk step and in it has landed before the first barrier
+        if (fi == 0) {
+            for (int c = 2; c < min(nch, 4); ++c) warm(c);
+            if (nch > 1) feed_rows(k, 1, kbuf(1));
+        }
+        feed(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier();
         barrier();
         for (int c = 0; c < nch; ++c) {
-            // this wavefront issues no other vector memory operation, so the count is exact
-            if (c + 3 < nch) {
-                feed(c + 3);
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SM::NLOAD) : "memory");
+            feed(c + 2, c + 1);
+            if (fi == 0 && c + 4 < nch) {
+                // issued after this step's loads: the wait below leaves only the warm-up in flight
+                // (loads complete in issue order)
+                warm(c + 4);
+                if constexpr (NWARM == 2)
+                    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
             } else {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             barrier();
         }
     } else {
-        // ================= output: wavefront 1 tiles {0, 3}, wavefront 2 tiles {1, 2} =================
+        // ================= output: wavefront 3 tiles {0, 3}, wavefront 7 tiles {1, 2} =================
+        barrier();
         barrier();
         if constexpr (!SUMMARY) {
             struct OutRegs {
                 bf16x8 Qf[2][KP], Pf[2][2];
                 float gq[2];
             };
-            auto tile_of = [&](int i) __attribute__((always_inline)) { return wave == 1 ? 3 * i : 1 + i; };
-            auto fetch_out = [&](int c, OutRegs& R) __attribute__((always_inline)) {  // Q, P, Gamma of chunk c
-                const int t0 = bos + c * GC, L = min(GC, eos - t0);
-                const uint8_t* rec = record(c);
-                const bf16_t* gP = reinterpret_cast<const bf16_t*>(rec + GC * GC * 2);
-                const float* gC = reinterpret_cast<const float*>(rec + 2 * GC * GC * 2);
+            auto tile_of = [&](int i) __attribute__((always_inline)) { return wave == 3 ? 3 * i : 1 + i; };
+            int orow[KP];
+#pragma unroll
+            for (int p = 0; p < KP; ++p) orow[p] = roff_row(p);
+            // chunk c's Q fragments and P fragments of own tiles, from LDS. The stored P fragment (tt, p)
+            // is, per lane, P[16 tt + ln][32 p + 4 lg + j] then P[16 tt + ln][32 p + 16 + 4 lg + j]: the
+            // B operand of the product with the R fragment pair p of the same tokens.
+            auto build = [&](int c, OutRegs& F) __attribute__((always_inline)) {
+                lds_u8* cb = tbuf(c) + SM::OFF_C;
+                lds_u8* pb = opaque(tbuf(c) + SM::OFF_P + lane * 16);
+                lds_u8* qb[KP];
+#pragma unroll
+                for (int p = 0; p < KP; ++p) qb[p] = opaque(qbuf(c) + orow[p]);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int tt = tile_of(i);
-                    const int t = min(16 * tt + ln, L - 1);
 #pragma unroll
-                    for (int p = 0; p < KP; ++p)
-                        R.Qf[i][p] = *reinterpret_cast<const bf16x8*>(q + ((size_t)(b * T + t0 + t) * HK + hk) * KD + 32 * p + 8 * lg);
+                    for (int p = 0; p < KP; ++p) F.Qf[i][p] = *(lds_bf16x8*)(qb[p] + tt * UST);
+                    F.gq[i] = *(const __attribute__((address_space(3))) float*)(cb + (16 * tt + ln) * 4);
 #pragma unroll
                     for (int p = 0; p < 2; ++p)
-                        if (p <= tt / 2) R.Pf[i][p] = *reinterpret_cast<const bf16x8*>(gP + (tri_frag(tt, p) * 64 + lane) * 8);
-                    R.gq[i] = gC[16 * tt + ln];
+                        if (p <= tt / 2) F.Pf[i][p] = *(lds_bf16x8*)(pb + tri_frag(tt, p) * 1024);
                 }
             };
-            auto emit_out = [&](int c, const OutRegs& R) __attribute__((always_inline)) {  // O of chunk c
+            auto emit = [&](int c, const OutRegs& E) __attribute__((always_inline)) {  // O of chunk c
                 const int t0 = bos + c * GC, L = min(GC, eos - t0);
-                const i16x4* sSf = reinterpret_cast<const i16x4*>(smem + SM::OFF_SF) + (c & 1) * KB * 64;
-                const i16x4* sRb = reinterpret_cast<const i16x4*>(smem + SM::OFF_RB) + (c & 1) * 4 * 64;
+                lds_u8* sb = opaque(lds0 + SM::OFF_SF + (c & 1) * KB * 512 + lane * 8);
+                lds_u8* rb = opaque(lds0 + SM::OFF_RB + (c & 1) * 4 * 512 + lane * 8);
                 i16x4 Sf[KB], Rb[4];
 #pragma unroll
-                for (int kt = 0; kt < KB; ++kt) Sf[kt] = sSf[kt * 64 + lane];
+                for (int kt = 0; kt < KB; ++kt) Sf[kt] = *(lds_i16x4*)(sb + kt * 512);
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) Rb[ti] = sRb[ti * 64 + lane];
+                for (int ti = 0; ti < 4; ++ti) Rb[ti] = *(lds_i16x4*)(rb + ti * 512);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int tt = tile_of(i);
                     f32x4 qs = zero4();
 #pragma unroll
-                    for (int p = 0; p < KP; ++p) qs = mma32(cat8(Sf[2 * p], Sf[2 * p + 1]), R.Qf[i][p], qs);
-                    f32x4 o = qs * (R.gq[i] * scale);
+                    for (int p = 0; p < KP; ++p) qs = mma32(cat8(Sf[2 * p], Sf[2 * p + 1]), E.Qf[i][p], qs);
+                    f32x4 o = qs * (E.gq[i] * scale);
 #pragma unroll
                     for (int p = 0; p < 2; ++p)
-                        if (p <= tt / 2) o = mma32(cat8(Rb[2 * p], Rb[2 * p + 1]), R.Pf[i][p], o);
+                        if (p <= tt / 2) o = mma32(cat8(Rb[2 * p], Rb[2 * p + 1]), E.Pf[i][p], o);
                     const int t = 16 * tt + ln;
                     if (t < L) {
                         const i16x4 ob = El::pack(o);
@@ -1011,10 +1290,11 @@ __global__ __launch_bounds__(256) void gdn_chain_1w_kernel(
                     }
                 }
             };
-            // chunk c: fetch chunk c's Q/P into F, emit chunk c-1 from E (register sets alternate)
+            // step c: build chunk c's operands into F (K_c, Q_c resident now), emit chunk c-1 from E
             auto step = [&](int c, OutRegs& F, const OutRegs& E) __attribute__((always_inline)) {
-                fetch_out(c, F);
-                if (c > 0) emit_out(c - 1, E);
+                build(c, F);
+                if (c > 0) emit(c - 1, E);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 barrier();
             };
             OutRegs RA, RB;
@@ -1022,7 +1302,7 @@ __global__ __launch_bounds__(256) void gdn_chain_1w_kernel(
                 step(c, RA, RB);
                 if (c + 1 < nch) step(c + 1, RB, RA);
             }
-            if (nch > 0) emit_out(nch - 1, (nch - 1) & 1 ? RB : RA);
+            if (nch > 0) emit(nch - 1, (nch - 1) & 1 ? RB : RA);
         } else {
             for (int c = 0; c < nch; ++c) barrier();
         }
@@ -1054,6 +1334,7 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
     if (slots > 0) {
         timing_begin("gdn_prep", s);
         if constexpr (sizeof(ST) == 2) {
+            // the decay-masked query-key block P only feeds the output
             const unsigned gx = (unsigned)slots;
             if (mode == 0)
                 gdn_prep_wave_kernel<KD, true><<<dim3(gx, H), 64, 0, s>>>(
@@ -1076,11 +1357,11 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
         const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * nvb);
         if (mode == 0) {
             timing_begin("gdn_chain", s);
-            gdn_chain_1w_kernel<KD, false><<<grid, 256, 0, s>>>(
+            gdn_chain_1w_kernel<KD, false><<<grid, 512, 0, s>>>(
                 q, k, v, h0, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, nvb, scale, out, ht, nullptr);
         } else {
             timing_begin("gdn_summary_chain", s);
-            gdn_chain_1w_kernel<KD, true><<<grid, 256, 0, s>>>(
+            gdn_chain_1w_kernel<KD, true><<<grid, 512, 0, s>>>(
                 q, k, v, nullptr, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, nvb, scale, nullptr, ht, Mout);
         }
         timing_end(s);

@@ -12,10 +12,15 @@ constexpr int kGdnChunk = 64;
 
 // Bytes of one per-(chunk, head) factor record of the delta-rule "Pre" stage:
 // the 64x64 solve factor T, the 64x64 decay-masked query-key block P (both in
-// the q/k/v element type) and 256 float coefficients.
+// the q/k/v element type) and 256 float coefficients; for bf16 also the 64x64
+// key-key block W = K_c K_{c-1}^T of the chunk and its predecessor, which lets
+// the chain form K_c S_c^T without waiting for the state update of chunk c-1.
 __host__ __device__ inline size_t gdn_factor_bytes(int elem_bytes) {
-    return (size_t)2 * kGdnChunk * kGdnChunk * elem_bytes + 256 * sizeof(float);
+    return (size_t)2 * kGdnChunk * kGdnChunk * elem_bytes + 256 * sizeof(float) +
+           (elem_bytes == 2 ? (size_t)kGdnChunk * kGdnChunk * 2 : 0);
 }
+// byte offset of W in a bf16 record (after T, P and the coefficients)
+constexpr size_t kGdnWOffset = (size_t)2 * kGdnChunk * kGdnChunk * 2 + 256 * sizeof(float);
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

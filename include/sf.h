@@ -84,8 +84,10 @@ const char *sf_last_error(void);
  * when cu_seqlens is passed; then B must be 1). The workspace holds the
  * per-chunk factors of the chunk decomposition (StateFlow Section 2.2,
  * Eq. (2), "Pre"): the unit-lower-triangular WY/UT solve factor, the
- * decay-masked query-key block and the per-token decay coefficients, plus
- * the device chunk table of packed inputs. Returns 0 for invalid sizes.
+ * decay-masked query-key block and the per-token decay coefficients (for
+ * bf16 also the key-key block of each chunk with its predecessor, which
+ * lets the chain overlap consecutive chunk steps), plus the device chunk
+ * table of packed inputs. Returns 0 for invalid sizes.
  */
 size_t sf_gdn_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N,
                                   int packed);

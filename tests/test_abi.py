@@ -49,7 +49,7 @@ def test_version(L):
 
 
 def test_workspace_sizes(L):
-    rec = 2 * 64 * 64 * 2 + 1024  # bf16 factor record
+    rec = 3 * 64 * 64 * 2 + 1024  # bf16 factor record: T, P, coefficients, W
     dense = L.sf_gdn_chunk_fwd_workspace(sf.SF_BF16, 2, 4096, 16, 128, 128, 2, 0)
     assert dense == 2 * 64 * 16 * rec
     # packed: chunk offsets (N+1 ints) and table (cap int2), each 256-aligned, then factors
