@@ -271,6 +271,287 @@ __global__ __launch_bounds__(64 * NW) void gla_chain_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, V = 64: one workgroup of four wavefronts per (sequence, head) chain,
+// two workgroups per CU (65.5 KB of LDS for K = 128, chunk 128).
+//
+// Per chunk, with K and V of the chunk in LDS (RowBlock layout, sf_device.h)
+// and the bf16 entry state S_c in LDS:
+//  - wavefront w forms, for its own token tiles (w and C/16-1-w for chunk 128,
+//    w for chunk 64), P^T = scale (D o K Q^T)^T tile by tile from K rows in LDS
+//    and its Q rows (registers, loaded during the previous chunk), and emits
+//    O^T = scale diag(Gamma) (S_c Q^T) + V^T P^T for all 64 value rows;
+//  - wavefront w updates the key columns it owns (KD/4 of them) of the float32
+//    state, S <- Gamma_L S + (diag(e) V)^T K, from transposed reads of K and V.
+// Then, after a barrier, the next chunk's K and V go straight into LDS with
+// 16-byte direct loads, the gates are summed and the new bf16 state is
+// written; a second barrier starts the next chunk. The other workgroup on the
+// CU computes while one waits for its loads.
+//
+// Value rows inside a 16-row value tile vt follow the transposed V reads, which
+// hand lane n the column v(vt, n) = 32 (vt / 2) + 8 (n / 4) + 4 (vt % 2) + n % 4;
+// so lane group lg of an output tile holds the four consecutive rows
+// 32 (vt / 2) + 8 lg + 4 (vt % 2) + r. State tiles: for key tile kt = 2p + h and
+// value tile vt, lane (n, lg) holds S[v(vt, n)][32 p + 8 lg + 4 h + r], r = 0..3.
+// ---------------------------------------------------------------------------
+template <int KD, int C, bool SUMMARY>
+__global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ h0, const int32_t* __restrict__ cu,
+    int T, int H, int HK, int n_seq, float scale, bf16_t* __restrict__ out, float* __restrict__ ht,
+    float* __restrict__ a_out) {
+    constexpr int V = 64, NVT = V / 16;
+    constexpr int KP = KD / 32, KB = KD / 16, KTW = KB / 4;  // key tiles of the state per wavefront
+    constexpr int NTT = C / 16;                              // token tiles per chunk
+    constexpr int NOT = C == 128 ? 2 : 1;                    // output token tiles per wavefront
+    typedef RowBlock<KD> RBk;
+    typedef RowBlock<V> RBv;
+    constexpr int UK = (16 / RBk::RPB) * 1024, UV = (16 / RBv::RPB) * 1024;  // bytes per 16 rows
+    constexpr int OFF_K = 0;
+    constexpr int OFF_V = OFF_K + C * RBk::RB;
+    constexpr int OFF_SF = OFF_V + C * RBv::RB;          // [KB][NVT][64 lanes] x 8 B bf16 state
+    constexpr int OFF_G = OFF_SF + KB * NVT * 512;       // G[C], Gamma[C], e[C], then G_L, Gamma_L
+    constexpr int BYTES = OFF_G + 3 * C * 4 + 16;
+    constexpr int NKI = C * RBk::RB / 1024 / 4, NVI = C * RBv::RB / 1024 / 4;  // direct loads per wavefront
+    static_assert(NKI * 4 * 1024 == C * RBk::RB && NVI * 4 * 1024 == C * RBv::RB, "loads must divide evenly");
+    static_assert(BYTES <= 80 * 1024, "two workgroups per CU");
+
+    __shared__ __align__(16) uint8_t smem[BYTES];
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    typedef __attribute__((address_space(3))) float lds_f32;
+    lds_u8* const lds0 = (lds_u8*)smem;
+    lds_f32* const sG = (lds_f32*)(lds0 + OFF_G);
+    lds_f32* const sGam = sG + C;
+    lds_f32* const sE = sG + 2 * C;
+
+    // the heads of one key group share K and Q rows: they run on one XCD
+    const int GH = H / HK;
+    int grp, j;
+    xcd_split(blockIdx.x, GH, grp, j);
+    if (grp >= n_seq * HK) return;
+    const int n = grp / HK, hk = grp % HK, h = hk * GH + j;
+    const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    int b, bos, eos;
+    if (cu) {
+        b = 0;
+        bos = cu[n];
+        eos = cu[n + 1];
+    } else {
+        b = n;
+        bos = 0;
+        eos = T;
+    }
+    const int nch = (eos - bos + C - 1) / C;
+    auto vrow = [&](int vt, int m) __attribute__((always_inline)) { return 32 * (vt >> 1) + 8 * (m >> 2) + 4 * (vt & 1) + (m & 3); };
+    auto tile_of = [&](int i) __attribute__((always_inline)) { return i == 0 ? w : NTT - 1 - w; };
+
+    // float32 state, own key tiles kt = w KTW + i
+    f32x4 S[KTW][NVT];
+#pragma unroll
+    for (int i = 0; i < KTW; ++i)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+            const int kt = w * KTW + i, kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1);
+            S[i][vt] = (!SUMMARY && h0) ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + vrow(vt, ln)) * KD + kk)
+                                        : zero4();
+        }
+
+    // ---- chunk c's K and V rows into LDS (rows past the end repeat the last token; their e = 0
+    // keeps them out of the state and their outputs are not stored) and its gates into registers
+    float rg[C / 64];
+    auto load_chunk = [&](int c) __attribute__((always_inline)) {
+        const int t0 = bos + c * C, L = min(C, eos - t0);
+#pragma unroll
+        for (int i = 0; i < NKI; ++i) {
+            const int m = w * NKI + i, r = m * RBk::RPB + lane / RBk::PCS;
+            const int bb = (lane % RBk::PCS) ^ RBk::swz(r);
+            load_lds16(k + ((size_t)(b * T + t0 + min(r, L - 1)) * HK + hk) * KD + 8 * bb, (uint8_t*)(lds0 + OFF_K + m * 1024));
+        }
+#pragma unroll
+        for (int i = 0; i < NVI; ++i) {
+            const int m = w * NVI + i, r = m * RBv::RPB + lane / RBv::PCS;
+            const int bb = (lane % RBv::PCS) ^ RBv::swz(r);
+            load_lds16(v + ((size_t)(b * T + t0 + min(r, L - 1)) * H + h) * V + 8 * bb, (uint8_t*)(lds0 + OFF_V + m * 1024));
+        }
+        if (w == 0) {
+#pragma unroll
+            for (int i = 0; i < C / 64; ++i) {
+                const int t = (C / 64) * lane + i;
+                rg[i] = t < L ? g[(size_t)(b * T + t0 + t) * H + h] : 0.f;
+            }
+        }
+    };
+    // cumulative gate of the chunk (wavefront 0, after its loads landed); padded gates are 0, so
+    // the total is G at the last token
+    auto gates = [&](int c) __attribute__((always_inline)) {
+        const int t0 = bos + c * C, L = min(C, eos - t0);
+        constexpr int PER = C / 64;
+        float x[PER], part = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            part += rg[i];
+            x[i] = part;
+        }
+        const float incl = wave_inclusive_scan(part), base = incl - part;
+        const float GL = __shfl(incl, 63, 64);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int t = PER * lane + i;
+            const float G = base + x[i];
+            sG[t] = G;
+            sGam[t] = __expf(G);
+            sE[t] = t < L ? __expf(GL - G) : 0.f;
+        }
+        if (lane == 0) {
+            sG[3 * C] = GL;
+            sG[3 * C + 1] = __expf(GL);
+        }
+    };
+    auto store_state = [&]() __attribute__((always_inline)) {  // bf16 copy of own state tiles
+        lds_u8* B = lds0 + OFF_SF + lane * 8;
+#pragma unroll
+        for (int i = 0; i < KTW; ++i)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt)
+                *(lds_i16x4*)(B + ((w * KTW + i) * NVT + vt) * 512) = Elem<bf16_t>::pack(S[i][vt]);
+    };
+    // Q rows of own output tiles: lane (ln, lg) <- Q[16 tt + ln][32 p + 8 lg + j]
+    bf16x8 Q[NOT][KP];
+    auto load_q = [&](int c) __attribute__((always_inline)) {
+        const int t0 = bos + c * C, L = min(C, eos - t0);
+#pragma unroll
+        for (int i = 0; i < NOT; ++i) {
+            const bf16_t* qr = q + ((size_t)(b * T + t0 + min(16 * tile_of(i) + ln, L - 1)) * HK + hk) * KD + 8 * lg;
+#pragma unroll
+            for (int p = 0; p < KP; ++p) Q[i][p] = *reinterpret_cast<const bf16x8*>(qr + 32 * p);
+        }
+    };
+    auto prologue_sync = [&](int c) __attribute__((always_inline)) {  // loads of chunk c landed -> gates
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (w == 0) gates(c);
+    };
+
+    float gsum = 0.f;
+    if (nch > 0) {
+        load_chunk(0);
+        if constexpr (!SUMMARY) {
+            load_q(0);
+            store_state();
+        }
+        prologue_sync(0);
+    }
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const int t0 = bos + c * C, L = min(C, eos - t0);
+        if constexpr (SUMMARY) gsum += sG[3 * C];
+        // ---- output tiles: P^T fragments of own token tiles
+        bf16x8 Pf[NOT][NTT / 2];
+        float gam[NOT];
+        if constexpr (!SUMMARY) {
+#pragma unroll
+            for (int i = 0; i < NOT; ++i) {
+                const int tt = tile_of(i);
+                const float Gt = sG[16 * tt + ln];
+                gam[i] = sGam[16 * tt + ln] * scale;
+                f32x4 PT[NTT];
+#pragma unroll
+                for (int si = 0; si < NTT; ++si) {
+                    PT[si] = zero4();
+                    if (si <= tt) {
+#pragma unroll
+                        for (int p = 0; p < KP; ++p)
+                            PT[si] = mma32(*(lds_bf16x8*)(lds0 + OFF_K + RBk::off(ln, 4 * p + lg) + si * UK), Q[i][p], PT[si]);
+                        const f32x4 Gs = *(lds_f32x4*)(sG + 16 * si + 4 * lg);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            // token s = 16 si + 4 lg + r against t = 16 tt + ln: only s <= t, where G_t - G_s <= 0
+                            const bool keep = si < tt || 4 * lg + r <= ln;
+                            PT[si][r] = keep ? PT[si][r] * (scale * __expf(fminf(Gt - Gs[r], 0.f))) : 0.f;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int pp = 0; pp < NTT / 2; ++pp) Pf[i][pp] = cat8(Elem<bf16_t>::pack(PT[2 * pp]), Elem<bf16_t>::pack(PT[2 * pp + 1]));
+            }
+        }
+        // ---- own key tiles of K^T: lane (n, lg) <- K[16 u + 4 lg + r][32 p + 8 (n/4) + 4 h + n%4]
+        i16x4 Ka[KTW][NTT];
+#pragma unroll
+        for (int i = 0; i < KTW; ++i) {
+            const int kt = w * KTW + i;
+            const int ktr = RBk::off(4 * lg + (ln >> 2), 4 * (kt >> 1) + (ln & 3)) + 8 * (kt & 1);
+#pragma unroll
+            for (int u = 0; u < NTT; ++u) Ka[i][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds0 + OFF_K + ktr + u * UK));
+        }
+        const float gamL = sG[3 * C + 1];
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+            // V^T fragments of value tile vt: lane (n, lg) <- V[16 u + 4 lg + r][v(vt, n)]
+            const int vtr = RBv::off(4 * lg + (ln >> 2), 4 * (vt >> 1) + (ln & 3)) + 8 * (vt & 1);
+            i16x4 Vt[NTT];
+#pragma unroll
+            for (int u = 0; u < NTT; ++u) Vt[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds0 + OFF_V + vtr + u * UV));
+            if constexpr (!SUMMARY) {
+                // bf16 entry state of value tile vt, all key columns (A operand: rows v, columns k)
+                bf16x8 Sq[KP];
+                lds_u8* sb = lds0 + OFF_SF + lane * 8 + vt * 512;
+#pragma unroll
+                for (int p = 0; p < KP; ++p)
+                    Sq[p] = cat8(*(lds_i16x4*)(sb + (2 * p) * NVT * 512), *(lds_i16x4*)(sb + (2 * p + 1) * NVT * 512));
+#pragma unroll
+                for (int i = 0; i < NOT; ++i) {
+                    const int tt = tile_of(i), t = 16 * tt + ln;
+                    f32x4 o = zero4();
+#pragma unroll
+                    for (int p = 0; p < KP; ++p) o = mma32(Sq[p], Q[i][p], o);
+                    o = o * gam[i];
+#pragma unroll
+                    for (int pp = 0; pp < NTT / 2; ++pp)
+                        if (pp <= tt / 2) o = mma32(cat8(Vt[2 * pp], Vt[2 * pp + 1]), Pf[i][pp], o);
+                    if (t < L)
+                        *reinterpret_cast<i16x4*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + vrow(vt, 4 * lg)) = Elem<bf16_t>::pack(o);
+                }
+            }
+            // S[:, own keys] of tile vt <- Gamma_L S + (e V)^T K
+            i16x4 E[NTT];
+#pragma unroll
+            for (int u = 0; u < NTT; ++u) E[u] = Elem<bf16_t>::pack(Elem<bf16_t>::unpack(Vt[u]) * *(lds_f32x4*)(sE + 16 * u + 4 * lg));
+#pragma unroll
+            for (int i = 0; i < KTW; ++i) {
+                f32x4 acc = S[i][vt] * gamL;
+#pragma unroll
+                for (int uu = 0; uu < NTT / 2; ++uu) acc = mma32(cat8(Ka[i][2 * uu], Ka[i][2 * uu + 1]), cat8(E[2 * uu], E[2 * uu + 1]), acc);
+                S[i][vt] = acc;
+            }
+        }
+        const bool more = c + 1 < nch;
+        if constexpr (!SUMMARY)
+            if (more) load_q(c + 1);  // lands during the exchange below
+        __syncthreads();
+        if (more) {
+            load_chunk(c + 1);
+            if constexpr (!SUMMARY) store_state();
+            prologue_sync(c + 1);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < KTW; ++i)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+            const int kt = w * KTW + i, kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1);
+            if (ht) *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + vrow(vt, ln)) * KD + kk) = S[i][vt];
+        }
+    if constexpr (SUMMARY) {
+        if (tid == 0) a_out[(size_t)n * H + h] = expf(gsum);
+    }
+}
+
 template <typename ST, int KD, int C>
 static hipError_t run_gla(int mode, const ST* q, const ST* k, const ST* v, const float* g,
                           const float* h0, const int32_t* cu, int N, int T, int H, int HK, int V,
@@ -291,6 +572,24 @@ static hipError_t run_gla(int mode, const ST* q, const ST* k, const ST* v, const
     return hipGetLastError();
 }
 
+template <int KD, int C>
+static hipError_t run_gla_bf16(int mode, const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* g,
+                               const float* h0, const int32_t* cu, int N, int T, int H, int HK, float scale,
+                               bf16_t* out, float* ht, float* a_out, hipStream_t s) {
+    const int groups = N * HK;
+    if (groups == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(((groups + 7) / 8) * 8 * (H / HK));
+    if (mode == 0) {
+        timing_begin("gla_chain", s);
+        gla_bf16_kernel<KD, C, false><<<grid, 256, 0, s>>>(q, k, v, g, h0, cu, T, H, HK, N, scale, out, ht, nullptr);
+    } else {
+        timing_begin("gla_summary_chain", s);
+        gla_bf16_kernel<KD, C, true><<<grid, 256, 0, s>>>(q, k, v, g, nullptr, cu, T, H, HK, N, scale, nullptr, ht, a_out);
+    }
+    timing_end(s);
+    return hipGetLastError();
+}
+
 template <typename ST>
 static hipError_t gla_dispatch(int mode, const void* q, const void* k, const void* v, const float* g,
                                const float* h0, const int32_t* cu, int N, int T, int H, int HK, int K,
@@ -299,6 +598,12 @@ static hipError_t gla_dispatch(int mode, const void* q, const void* k, const voi
     const ST *qq = (const ST*)q, *kk = (const ST*)k, *vv = (const ST*)v;
     ST* oo = (ST*)out;
     if constexpr (sizeof(ST) == 2) {
+        if (V == 64 && (K == 128 || K == 64) && (chunk == 128 || chunk == 64)) {
+            if (K == 128 && chunk == 128) return run_gla_bf16<128, 128>(mode, qq, kk, vv, g, h0, cu, N, T, H, HK, scale, oo, ht, a_out, s);
+            if (K == 128) return run_gla_bf16<128, 64>(mode, qq, kk, vv, g, h0, cu, N, T, H, HK, scale, oo, ht, a_out, s);
+            if (chunk == 128) return run_gla_bf16<64, 128>(mode, qq, kk, vv, g, h0, cu, N, T, H, HK, scale, oo, ht, a_out, s);
+            return run_gla_bf16<64, 64>(mode, qq, kk, vv, g, h0, cu, N, T, H, HK, scale, oo, ht, a_out, s);
+        }
         if (K == 128 && chunk == 128) return run_gla<ST, 128, 128>(mode, qq, kk, vv, g, h0, cu, N, T, H, HK, V, scale, oo, ht, a_out, s);
         if (K == 64 && chunk == 128) return run_gla<ST, 64, 128>(mode, qq, kk, vv, g, h0, cu, N, T, H, HK, V, scale, oo, ht, a_out, s);
     }

@@ -135,4 +135,36 @@ __device__ __forceinline__ void xcd_split(int L, int nsub, int& chain, int& sub)
     sub = idx % nsub;
 }
 
+// 16-byte direct load global -> LDS: lane l's 16 bytes land at dst + 16 l.
+__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// One v_mfma_f32_16x16x32_bf16: lane (ln, lg) brings A[ln][8 lg + j] and B[8 lg + j][ln], j = 0..7
+// (any pairing of the 32 reduction slots works as long as both operands use the same one).
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 cat8(i16x4 x, i16x4 y) {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Rows of KD 16-bit elements in LDS (K, Q, V tiles): 1 KB blocks of whole rows; the 16-byte piece b
+// of row r sits at piece b ^ swz(r) of its row (KD = 64 or 128). The row-fragment reads (16 rows,
+// one piece) and the transposed reads that build transposed fragments (4 rows x 4 pieces per 16
+// lanes) both hit 16 different bank groups. The swizzle repeats every 16 rows, so a tile of 16 more
+// rows sits (16 / RPB) KB further on.
+template <int KD>
+struct RowBlock {
+    static constexpr int RB = 2 * KD;          // bytes per row
+    static constexpr int RPB = 1024 / RB;      // rows per 1 KB block
+    static constexpr int PCS = RB / 16;        // 16-byte pieces per row
+    static constexpr int BYTES = 64 * RB;      // one 64-row chunk
+    static constexpr int NLOAD = BYTES / 1024; // direct-load instructions per chunk
+    __device__ static int swz(int r) {
+        return KD == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    }
+    __device__ static int off(int r, int b) { return (r / RPB) * 1024 + (r % RPB) * RB + ((b ^ swz(r)) * 16); }
+};
+
 }  // namespace sf
