@@ -296,6 +296,9 @@ __device__ __forceinline__ void store_tri_frags(const bf16_t* m, int ld, bf16_t*
         }
 }
 
+// chunk slots per Pre wavefront: the next slot's rows are loaded while this one's solve runs
+constexpr int kPrepSlotsPerWave = 1;
+
 template <int KD, bool WANT_P>
 __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                            const float* __restrict__ g,
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
                                                            int HK, int nc, int n_slots, float scale,
                                                            uint8_t* __restrict__ fac) {
     constexpr int KP = KD / 32;
-    constexpr int NPW = 1;
+    constexpr int NPW = kPrepSlotsPerWave;
     constexpr int LO = GC + 8;  // staging tile row stride (bf16)
     __shared__ __align__(16) float sA[tri_off(GC)];
     __shared__ __align__(16) bf16_t sO[GC * LO];
@@ -411,7 +414,9 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
         }
         __syncthreads();
         if constexpr (WANT_P) store_tri_frags(sO, LO, gP);
-        // next slot's loads go out now (the fragment registers are free) and land during the solve
+        // next slot's loads go out now (the fragment registers are free) and land during the solve;
+        // they replace gv/bv too, so this slot's beta is kept
+        const float bcur = bv;
         const bool next = s + 1 < NPW && slot + 1 < n_slots && chunk_coords(slot + 1, table, cu, T, nc, b, t0, L, ci);
         if (next) load(slot + 1);
 
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
         __syncthreads();  // staging tile free again (P copy done)
         // stored as T diag(beta): column j scaled by beta_j (zero past the chunk's end)
 #pragma unroll
-        for (int t = 0; t < GC; ++t) sO[t * LO + lane] = f2bf(x[t] * bv);
+        for (int t = 0; t < GC; ++t) sO[t * LO + lane] = f2bf(x[t] * bcur);
         __syncthreads();
         store_tri_frags(sO, LO, gT);
         if (!next) break;
@@ -1309,7 +1314,7 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
         timing_begin("gdn_prep", s);
         if constexpr (sizeof(ST) == 2) {
             // the decay-masked query-key block P only feeds the output
-            const unsigned gx = (unsigned)slots;
+            const unsigned gx = (unsigned)((slots + kPrepSlotsPerWave - 1) / kPrepSlotsPerWave);
             if (mode == 0)
                 gdn_prep_wave_kernel<KD, true><<<dim3(gx, H), 64, 0, s>>>(
                     q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
