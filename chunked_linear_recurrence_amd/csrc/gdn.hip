@@ -298,6 +298,13 @@ __device__ __forceinline__ void store_tri_frags(const bf16_t* m, int ld, bf16_t*
 
 // chunk slots per Pre wavefront: the next slot's rows are loaded while this one's solve runs
 constexpr int kPrepSlotsPerWave = 1;
+// Pre work units (head, slot group) in runs of this many consecutive slots of one head per XCD:
+// neighbouring chunks read each other's key rows (W), which then come from that XCD's L2
+constexpr int kPrepXcdRun = 64;
+inline unsigned prep_grid(int H, long n_slots) {
+    const long units = (long)H * ((n_slots + kPrepSlotsPerWave - 1) / kPrepSlotsPerWave);
+    return (unsigned)(((units + 8 * kPrepXcdRun - 1) / (8 * kPrepXcdRun)) * (8 * kPrepXcdRun));
+}
 
 template <int KD, bool WANT_P>
 __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -312,9 +319,16 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
     constexpr int LO = GC + 8;  // staging tile row stride (bf16)
     __shared__ __align__(16) float sA[tri_off(GC)];
     __shared__ __align__(16) bf16_t sO[GC * LO];
+    __shared__ __align__(16) float sD[GC * 16];  // diagonal blocks of T, row-major per block
     __shared__ float sG[GC], sB[GC];
 
-    const int h = blockIdx.y;
+    // blockIdx -> unit u = h * groups + group, in runs of kPrepXcdRun units per XCD (workgroups go
+    // round-robin over the 8 XCDs)
+    const int ngrp = (n_slots + NPW - 1) / NPW;
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int u = (idx / kPrepXcdRun) * (8 * kPrepXcdRun) + xcd * kPrepXcdRun + idx % kPrepXcdRun;
+    if (u >= H * ngrp) return;
+    const int h = u / ngrp;
     const int hk = h / (H / HK);
     const int lane = threadIdx.x, ln = lane & 15, lg = lane >> 4;
     const bf16x8 zero8 = {};
@@ -349,7 +363,7 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
         (void)slot;
     };
 
-    int slot = blockIdx.x * NPW;
+    int slot = (u % ngrp) * NPW;
     if (slot >= n_slots || !chunk_coords(slot, table, cu, T, nc, b, t0, L, ci)) return;
     load(slot);
     for (int s = 0; s < NPW; ++s, ++slot) {
@@ -420,34 +434,66 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
         const bool next = s + 1 < NPW && slot + 1 < n_slots && chunk_coords(slot + 1, table, cu, T, nc, b, t0, L, ci);
         if (next) load(slot + 1);
 
-        // forward substitution, lane = column j of T, right-looking: once row t
-        // of the column is final, its contribution A[r][t] x_t leaves every later
-        // row r, so each step is 63 - t independent FMAs; the next column of A
-        // is read from LDS while the current one is applied
-        float x[GC];
+        // T = (I + A)^-1 by 16x16 blocks (A strictly lower, float32). The diagonal blocks
+        // D_b = (I + A_bb)^-1 come from forward substitution, lane (b, jj) holding column jj of D_b
+        // (15 steps for all four blocks at once); the others from block row i of (I + A) T = I,
+        //   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj  (T_jj = D_j),
+        // one block diagonal i - j at a time, as float32 MFMA block products (sf_device.h).
+        const int db = lane >> 4, dj = lane & 15;
+        float x[16];
 #pragma unroll
-        for (int r = 0; r < GC; ++r) x[r] = (r == lane) ? 1.f : 0.f;
-        f32x4 cur[16], nxt[16];
+        for (int r = 0; r < 16; ++r) x[r] = (r == dj) ? 1.f : 0.f;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) cur[m] = *reinterpret_cast<const f32x4*>(sA + col_off(0) + 4 * m);
-#pragma unroll
-        for (int t = 0; t < GC - 1; ++t) {
-            const int n = GC - 1 - t, n1 = n - 1;  // entries in column t and t+1
-#pragma unroll
-            for (int m = 0; m < (n1 + 3) / 4; ++m) nxt[m] = *reinterpret_cast<const f32x4*>(sA + col_off(t + 1) + 4 * m);
+        for (int t = 0; t < 15; ++t) {
+            const float* col = sA + col_off(16 * db + t);  // rows 16 db + t + 1 .. of column 16 db + t
             const float xt = x[t];
 #pragma unroll
-            for (int m = 0; m < (n + 3) / 4; ++m)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * m + e < n) x[t + 1 + 4 * m + e] -= cur[m][e] * xt;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) cur[m] = nxt[m];
+            for (int r = t + 1; r < 16; ++r) x[r] -= col[r - t - 1] * xt;
         }
-        __syncthreads();  // staging tile free again (P copy done)
-        // stored as T diag(beta): column j scaled by beta_j (zero past the chunk's end)
 #pragma unroll
-        for (int t = 0; t < GC; ++t) sO[t * LO + lane] = f2bf(x[t] * bcur);
+        for (int r = 0; r < 16; ++r) sD[(16 * db + r) * 16 + dj] = x[r];
+        __syncthreads();
+        // fragments: A operand lane (ln, lg) <- M[ln][4 lg + q], B operand <- M[4 lg + q][ln]
+        auto d_a = [&](int i) __attribute__((always_inline)) { return *reinterpret_cast<const f32x4*>(sD + (16 * i + ln) * 16 + 4 * lg); };
+        auto d_b = [&](int j) __attribute__((always_inline)) {
+            f32x4 r;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) r[q] = sD[(16 * j + 4 * lg + q) * 16 + ln];
+            return r;
+        };
+        auto a_a = [&](int i, int j) __attribute__((always_inline)) {  // block A_ij, i > j
+            f32x4 r;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = 16 * j + 4 * lg + q;
+                r[q] = sA[col_off(c) + (16 * i + ln) - c - 1];
+            }
+            return r;
+        };
+        f32x4 Tb[4][4];  // Tb[i][j], i > j, C tile: lane (ln, lg) holds T[16 i + 4 lg + r][16 j + ln]
+#pragma unroll
+        for (int dd = 1; dd < 4; ++dd)
+#pragma unroll
+            for (int j = 0; j + dd < 4; ++j) {
+                const int i = j + dd;
+                f32x4 u = Elem<float>::mma(zero4(), a_a(i, j), d_b(j));
+#pragma unroll
+                for (int kk = j + 1; kk < i; ++kk) u = Elem<float>::mma(u, a_a(i, kk), Tb[kk][j]);
+                Tb[i][j] = Elem<float>::mma(zero4(), d_a(i), u) * -1.f;
+            }
+        __syncthreads();  // staging tile free again (P copy done)
+        // stored as T diag(beta): column j scaled by beta_j (zero past the chunk's end); blocks above
+        // the diagonal stay zero from the clear at the start of the slot
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sO[(16 * db + r) * LO + 16 * db + dj] = f2bf(x[r] * bcur);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float bj = sB[16 * j + ln];
+#pragma unroll
+            for (int i = j + 1; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sO[(16 * i + 4 * lg + r) * LO + 16 * j + ln] = f2bf(Tb[i][j][r] * bj);
+        }
         __syncthreads();
         store_tri_frags(sO, LO, gT);
         if (!next) break;
@@ -1314,12 +1360,12 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
         timing_begin("gdn_prep", s);
         if constexpr (sizeof(ST) == 2) {
             // the decay-masked query-key block P only feeds the output
-            const unsigned gx = (unsigned)((slots + kPrepSlotsPerWave - 1) / kPrepSlotsPerWave);
+            const unsigned gx = prep_grid(H, slots);
             if (mode == 0)
-                gdn_prep_wave_kernel<KD, true><<<dim3(gx, H), 64, 0, s>>>(
+                gdn_prep_wave_kernel<KD, true><<<gx, 64, 0, s>>>(
                     q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
             else
-                gdn_prep_wave_kernel<KD, false><<<dim3(gx, H), 64, 0, s>>>(
+                gdn_prep_wave_kernel<KD, false><<<gx, 64, 0, s>>>(
                     q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
         } else
             gdn_prep_kernel<ST, KD><<<dim3((unsigned)slots, H), 256, 0, s>>>(
