@@ -252,17 +252,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const ST* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// Pre, bf16: one wavefront per (chunk slot, head), no workgroup barriers.
-//  - K and Q rows go straight from global memory into 16x16x32 MFMA
-//    fragments (lane (n, g) holds row 16R+n, columns 32p+8g..+7), which serve
-//    as both operands of K K^T and Q K^T on the 10 lower 16x16 tiles.
-//  - A = diag(beta)(strictly lower D o K K^T) is kept in LDS as packed
-//    columns (column i holds rows i+1..63, 16-byte aligned).
-//  - T = (I + A)^-1 by forward substitution with one column per lane
-//    (T[t][j] = 1{t == j} - sum_{i<t} A[t][i] T[i][j]), applied right-looking:
-//    A's columns are read as broadcasts from LDS, T's column stays in 64
-//    registers.
-//  - T and P leave through a 64x64 bf16 LDS staging tile with 16-byte stores.
+// Pre, bf16: shared pieces of the two kernels below.
 // ---------------------------------------------------------------------------
 __host__ __device__ constexpr int tri_off(int t) {  // sum_{s<t} round_up(s, 4)
     return 8 * (t / 4) * (t / 4) + 4 * (t / 4) + ((t % 4) ? 4 * (t / 4) * (t % 4) + 4 * ((t % 4) - 1) : 0);
@@ -296,39 +286,41 @@ __device__ __forceinline__ void store_tri_frags(const bf16_t* m, int ld, bf16_t*
         }
 }
 
-// chunk slots per Pre wavefront: the next slot's rows are loaded while this one's solve runs
-constexpr int kPrepSlotsPerWave = 1;
-// Pre work units (head, slot group) in runs of this many consecutive slots of one head per XCD:
+// Pre work units (head, slot) in runs of this many consecutive slots of one head per XCD:
 // neighbouring chunks read each other's key rows (W), which then come from that XCD's L2
 constexpr int kPrepXcdRun = 64;
 inline unsigned prep_grid(int H, long n_slots) {
-    const long units = (long)H * ((n_slots + kPrepSlotsPerWave - 1) / kPrepSlotsPerWave);
+    const long units = (long)H * n_slots;
     return (unsigned)(((units + 8 * kPrepXcdRun - 1) / (8 * kPrepXcdRun)) * (8 * kPrepXcdRun));
 }
 
+// ---------------------------------------------------------------------------
+// Pre, bf16, one wavefront per (chunk slot, head), for launches with more units than the GPU
+// holds at once (there the instructions spent per chunk count more than each chunk's latency):
+// the same steps as the two-wavefront kernel below, in one wavefront, with the P and T blocks
+// leaving through a 64x64 bf16 LDS staging tile.
+// ---------------------------------------------------------------------------
 template <int KD, bool WANT_P>
-__global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                           const float* __restrict__ g,
-                                                           const float* __restrict__ beta,
-                                                           const int2* __restrict__ table,
-                                                           const int32_t* __restrict__ cu, int T, int H,
-                                                           int HK, int nc, int n_slots, float scale,
-                                                           uint8_t* __restrict__ fac) {
+__global__ __launch_bounds__(64) void gdn_prep_1w_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                         const float* __restrict__ g,
+                                                         const float* __restrict__ beta,
+                                                         const int2* __restrict__ table,
+                                                         const int32_t* __restrict__ cu, int T, int H,
+                                                         int HK, int nc, int n_slots, float scale,
+                                                         uint8_t* __restrict__ fac) {
     constexpr int KP = KD / 32;
-    constexpr int NPW = kPrepSlotsPerWave;
     constexpr int LO = GC + 8;  // staging tile row stride (bf16)
     __shared__ __align__(16) float sA[tri_off(GC)];
     __shared__ __align__(16) bf16_t sO[GC * LO];
     __shared__ __align__(16) float sD[GC * 16];  // diagonal blocks of T, row-major per block
     __shared__ float sG[GC], sB[GC];
 
-    // blockIdx -> unit u = h * groups + group, in runs of kPrepXcdRun units per XCD (workgroups go
+    // blockIdx -> unit u = h * n_slots + slot, in runs of kPrepXcdRun units per XCD (workgroups go
     // round-robin over the 8 XCDs)
-    const int ngrp = (n_slots + NPW - 1) / NPW;
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int u = (idx / kPrepXcdRun) * (8 * kPrepXcdRun) + xcd * kPrepXcdRun + idx % kPrepXcdRun;
-    if (u >= H * ngrp) return;
-    const int h = u / ngrp;
+    if (u >= H * n_slots) return;
+    const int h = u / n_slots;
     const int hk = h / (H / HK);
     const int lane = threadIdx.x, ln = lane & 15, lg = lane >> 4;
     const bf16x8 zero8 = {};
@@ -336,7 +328,7 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
     bf16x8 kf[4][KP], qf[4][KP], kp[4][KP];
     float gv, bv;
     int b, t0, L, ci;
-    auto load = [&](int slot) __attribute__((always_inline)) {
+    auto load = [&]() __attribute__((always_inline)) {
         const int t_lane = min(lane, L - 1);
         const size_t gi = (size_t)(b * T + t0 + t_lane) * H + h;
         gv = lane < L ? g[gi] : 0.f;
@@ -360,14 +352,13 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
                 kp[R][p] = ci > 0 ? pv : zero8;
             }
         }
-        (void)slot;
     };
 
-    int slot = (u % ngrp) * NPW;
-    if (slot >= n_slots || !chunk_coords(slot, table, cu, T, nc, b, t0, L, ci)) return;
-    load(slot);
-    for (int s = 0; s < NPW; ++s, ++slot) {
-        // gates of this slot (registers loaded with the slot's K/Q)
+    const int slot = u % n_slots;
+    if (!chunk_coords(slot, table, cu, T, nc, b, t0, L, ci)) return;
+    load();
+    {
+        // gates of this slot
         const float G = wave_inclusive_scan(gv);
         sG[lane] = G;
         sB[lane] = bv;
@@ -428,11 +419,6 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
         }
         __syncthreads();
         if constexpr (WANT_P) store_tri_frags(sO, LO, gP);
-        // next slot's loads go out now (the fragment registers are free) and land during the solve;
-        // they replace gv/bv too, so this slot's beta is kept
-        const float bcur = bv;
-        const bool next = s + 1 < NPW && slot + 1 < n_slots && chunk_coords(slot + 1, table, cu, T, nc, b, t0, L, ci);
-        if (next) load(slot + 1);
 
         // T = (I + A)^-1 by 16x16 blocks (A strictly lower, float32). The diagonal blocks
         // D_b = (I + A_bb)^-1 come from forward substitution, lane (b, jj) holding column jj of D_b
@@ -485,7 +471,7 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
         // stored as T diag(beta): column j scaled by beta_j (zero past the chunk's end); blocks above
         // the diagonal stay zero from the clear at the start of the slot
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sO[(16 * db + r) * LO + 16 * db + dj] = f2bf(x[r] * bcur);
+        for (int r = 0; r < 16; ++r) sO[(16 * db + r) * LO + 16 * db + dj] = f2bf(x[r] * bv);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float bj = sB[16 * j + ln];
@@ -496,8 +482,245 @@ __global__ __launch_bounds__(64) void gdn_prep_wave_kernel(const bf16_t* __restr
         }
         __syncthreads();
         store_tri_frags(sO, LO, gT);
-        if (!next) break;
-        __syncthreads();  // sG/sB/sA/sO are rewritten for the next slot
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// Pre, bf16: one workgroup of two wavefronts per (chunk slot, head); the two never wait for
+// each other (each orders its own LDS traffic).
+//  - K and Q rows go straight from global memory into 16x16x32 MFMA fragments (lane (n, g)
+//    holds row 16R+n, columns 32p+8g..+7).
+//  - Wavefront 0: the within-chunk gates and coefficients; A = diag(beta)(strictly lower
+//    D o K K^T) in LDS as packed columns (column i holds rows i+1..63, 16-byte aligned);
+//    T = (I + A)^-1 by 16x16 blocks; T diag(beta) out through a 64x64 bf16 staging tile that
+//    reuses the A area, in fragment order.
+//  - Wavefront 1: its own copy of the gates; P^T = scale (D o K Q^T)^T tile by tile, whose C
+//    tiles are already the lane contents of P's fragments, so P goes out from registers.
+//  - The key-key block W = K_c K_{c-1}^T from the previous chunk's rows: each wavefront forms
+//    half of its fragments (wavefront 0 before its solve, wavefront 1 after P).
+// ---------------------------------------------------------------------------
+template <int KD, bool WANT_P>
+__global__ __launch_bounds__(128, 4) void gdn_prep_2w_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                            const float* __restrict__ g,
+                                                            const float* __restrict__ beta,
+                                                            const int2* __restrict__ table,
+                                                            const int32_t* __restrict__ cu, int T, int H,
+                                                            int HK, int nc, int n_slots, float scale,
+                                                            uint8_t* __restrict__ fac) {
+    constexpr int KP = KD / 32;
+    static_assert(tri_off(GC) * 4 >= GC * GC * 2, "the T staging tile reuses the A area");
+    __shared__ __align__(16) float sA[tri_off(GC)];  // A packed columns; then T diag(beta), bf16 [64][64]
+    __shared__ __align__(16) float sD[GC * 16];      // diagonal blocks of T, row-major per block
+    __shared__ float sG[2][GC], sB[GC];
+    // wavefront-local order of LDS traffic: later LDS reads see the lanes' earlier writes
+    auto wave_sync = [] __attribute__((always_inline)) () { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+
+    // blockIdx -> unit u = h * n_slots + slot, in runs of kPrepXcdRun units per XCD (workgroups go
+    // round-robin over the 8 XCDs)
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int u = (idx / kPrepXcdRun) * (8 * kPrepXcdRun) + xcd * kPrepXcdRun + idx % kPrepXcdRun;
+    if (u >= H * n_slots) return;
+    const int h = u / n_slots, slot = u % n_slots;
+    const int hk = h / (H / HK);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+    const bf16x8 zero8 = {};
+    int b, t0, L, ci;
+    if (!chunk_coords(slot, table, cu, T, nc, b, t0, L, ci)) return;
+
+    // gates of the chunk (both wavefronts; padded tokens get g = 0)
+    const size_t gi = (size_t)(b * T + t0 + min(lane, L - 1)) * H + h;
+    const float G = wave_inclusive_scan(lane < L ? g[gi] : 0.f);
+    float* sGw = sG[wave];
+    sGw[lane] = G;
+    uint8_t* rec = fac + ((size_t)slot * H + h) * gdn_factor_bytes(2);
+    bf16_t* gT = reinterpret_cast<bf16_t*>(rec);
+    bf16_t* gP = gT + GC * GC;
+    float* gC = reinterpret_cast<float*>(gP + GC * GC);
+    // K rows of the chunk (rows past its end are zero)
+    bf16x8 kf[4][KP];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        const int t = 16 * R + ln;
+        const bf16_t* row = k + ((size_t)(b * T + t0 + min(t, L - 1)) * HK + hk) * KD + 8 * lg;
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            const bf16x8 kv = *reinterpret_cast<const bf16x8*>(row + 32 * p);
+            kf[R][p] = t < L ? kv : zero8;
+        }
+    }
+
+    // W = K_c K_{c-1}^T (zero for a sequence's first chunk and for padded rows), as the A
+    // operand of W (e R)_{c-1}: fragment (u, p) holds, for lane (ln, lg), W[16 u + ln][32 p + 4 lg + j]
+    // then W[16 u + ln][32 p + 16 + 4 lg + j]. The C tile of K_{c-1} K_c^T (rows s, columns t) is
+    // exactly that lane content, so each fragment pairs two of those tiles without any shuffle.
+    // Wavefront pp forms the fragments (u, pp) from the row tiles 2 pp, 2 pp + 1 of the preceding
+    // (always full) chunk of the same sequence (a sequence's first chunk loads its own first row
+    // and discards it).
+    auto make_w = [&](int pp) __attribute__((always_inline)) {
+        bf16_t* gW = reinterpret_cast<bf16_t*>(rec + kGdnWOffset);
+        bf16x8 kq[2][KP];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int t = 16 * (2 * pp + s2) + ln;
+            const int pt = ci > 0 ? t0 - GC + t : t0;
+            const bf16_t* row = k + ((size_t)(b * T + pt) * HK + hk) * KD + 8 * lg;
+#pragma unroll
+            for (int p = 0; p < KP; ++p) {
+                const bf16x8 pv = *reinterpret_cast<const bf16x8*>(row + 32 * p);
+                kq[s2][p] = ci > 0 ? pv : zero8;
+            }
+        }
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+            f32x4 w0 = zero4(), w1 = zero4();
+#pragma unroll
+            for (int p = 0; p < KP; ++p) {
+                w0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[0][p], kf[uu][p], w0, 0, 0, 0);
+                w1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[1][p], kf[uu][p], w1, 0, 0, 0);
+            }
+            const i16x4 lo = Elem<bf16_t>::pack(w0), hi = Elem<bf16_t>::pack(w1);
+            *reinterpret_cast<i16x8*>(gW + ((2 * uu + pp) * 64 + lane) * 8) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+
+    if (wave == 0) {
+        const float bv = lane < L ? beta[gi] : 0.f;
+        sB[lane] = bv;
+        {
+            const float GL = __shfl(G, 63, 64);
+            gC[lane] = expf(G);
+            gC[64 + lane] = expf(GL - G);
+            gC[128 + lane] = bv;
+            gC[192 + lane] = G;
+        }
+        wave_sync();
+        // A on the 10 lower tiles: C tile lane (ln, lg) holds (K K^T)[16 ti + 4 lg + r][16 tj + ln]
+#pragma unroll
+        for (int tt = 0; tt < 10; ++tt) {
+            const int ti = (tt >= 1) + (tt >= 3) + (tt >= 6);
+            const int tj = tt - ti * (ti + 1) / 2;
+            f32x4 a = zero4();
+#pragma unroll
+            for (int p = 0; p < KP; ++p) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ti][p], kf[tj][p], a, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * ti + 4 * lg + r, i = 16 * tj + ln;
+                const float d = expf(fminf(sGw[t] - sGw[i], 0.f));
+                if (i < t) sA[col_off(i) + (t - i - 1)] = sB[t] * d * a[r];
+            }
+        }
+        make_w(0);
+        wave_sync();
+        // T = (I + A)^-1 by 16x16 blocks (A strictly lower, float32). The diagonal blocks
+        // D_b = (I + A_bb)^-1 come from forward substitution, lane (b, jj) holding column jj of D_b
+        // (15 steps for all four blocks at once); the others from block row i of (I + A) T = I,
+        //   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj  (T_jj = D_j),
+        // one block diagonal i - j at a time, as float32 MFMA block products (sf_device.h).
+        const int db = lane >> 4, dj = lane & 15;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == dj) ? 1.f : 0.f;
+#pragma unroll
+        for (int t = 0; t < 15; ++t) {
+            const float* col = sA + col_off(16 * db + t);  // rows 16 db + t + 1 .. of column 16 db + t
+            const float xt = x[t];
+#pragma unroll
+            for (int r = t + 1; r < 16; ++r) x[r] -= col[r - t - 1] * xt;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sD[(16 * db + r) * 16 + dj] = x[r];
+        wave_sync();
+        // fragments: A operand lane (ln, lg) <- M[ln][4 lg + q], B operand <- M[4 lg + q][ln]
+        auto d_a = [&](int i) __attribute__((always_inline)) { return *reinterpret_cast<const f32x4*>(sD + (16 * i + ln) * 16 + 4 * lg); };
+        auto d_b = [&](int j) __attribute__((always_inline)) {
+            f32x4 r;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) r[qq] = sD[(16 * j + 4 * lg + qq) * 16 + ln];
+            return r;
+        };
+        auto a_a = [&](int i, int j) __attribute__((always_inline)) {  // block A_ij, i > j
+            f32x4 r;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int c = 16 * j + 4 * lg + qq;
+                r[qq] = sA[col_off(c) + (16 * i + ln) - c - 1];
+            }
+            return r;
+        };
+        f32x4 Tb[4][4];  // Tb[i][j], i > j, C tile: lane (ln, lg) holds T[16 i + 4 lg + r][16 j + ln]
+#pragma unroll
+        for (int dd = 1; dd < 4; ++dd)
+#pragma unroll
+            for (int j = 0; j + dd < 4; ++j) {
+                const int i = j + dd;
+                f32x4 uu = Elem<float>::mma(zero4(), a_a(i, j), d_b(j));
+#pragma unroll
+                for (int kk = j + 1; kk < i; ++kk) uu = Elem<float>::mma(uu, a_a(i, kk), Tb[kk][j]);
+                Tb[i][j] = Elem<float>::mma(zero4(), d_a(i), uu) * -1.f;
+            }
+        wave_sync();
+        // T diag(beta) (column j scaled by beta_j, zero past the chunk's end) into the staging tile
+        // over the A area; the two blocks right of the diagonal that the fragments cover are zero
+        bf16_t* sS = reinterpret_cast<bf16_t*>(sA);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sS[(16 * db + r) * GC + 16 * db + dj] = f2bf(x[r] * bv);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float bj = sB[16 * j + ln];
+#pragma unroll
+            for (int i = j + 1; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sS[(16 * i + 4 * lg + r) * GC + 16 * j + ln] = f2bf(Tb[i][j][r] * bj);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sS[(4 * lg + r) * GC + 16 + ln] = 0;
+            sS[(32 + 4 * lg + r) * GC + 48 + ln] = 0;
+        }
+        wave_sync();
+        store_tri_frags(sS, GC, gT);
+    } else {
+        wave_sync();
+        if constexpr (WANT_P) {
+            // P^T tiles, K rows (A operand, rows s) against Q rows (B operand, columns t): C tile lane
+            // (ln, lg) holds P[16 ti + ln][16 tj + 4 lg + r], which is fragment (ti, tj / 2)'s lane
+            // content (first or second half)
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                const int t = 16 * ti + ln;
+                bf16x8 qf[KP];
+                const bf16_t* row = q + ((size_t)(b * T + t0 + min(t, L - 1)) * HK + hk) * KD + 8 * lg;
+#pragma unroll
+                for (int p = 0; p < KP; ++p) {
+                    const bf16x8 qv = *reinterpret_cast<const bf16x8*>(row + 32 * p);
+                    qf[p] = t < L ? qv : zero8;
+                }
+                const float Gt = sGw[t];
+                f32x4 PT[4];
+#pragma unroll
+                for (int tj = 0; tj < 4; ++tj) {
+                    PT[tj] = zero4();
+                    if (tj <= ti) {
+#pragma unroll
+                        for (int p = 0; p < KP; ++p) PT[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tj][p], qf[p], PT[tj], 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int i = 16 * tj + 4 * lg + r;
+                            const float d = expf(fminf(Gt - sGw[i], 0.f));
+                            PT[tj][r] = i <= t ? scale * d * PT[tj][r] : 0.f;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p <= ti / 2; ++p) {
+                    const i16x4 lo = Elem<bf16_t>::pack(PT[2 * p]), hi = Elem<bf16_t>::pack(PT[2 * p + 1]);
+                    *reinterpret_cast<i16x8*>(gP + (tri_frag(ti, p) * 64 + lane) * 8) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            }
+        }
+        make_w(1);
     }
 }
 
@@ -1343,6 +1566,19 @@ hipError_t launch_chunk_table(const int32_t* cu, int N, int chunk, long cap, int
     return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 template <typename ST, int KD>
 static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const float* g,
                           const float* beta, const float* h0, const int32_t* cu,
@@ -1359,14 +1595,24 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
     if (slots > 0) {
         timing_begin("gdn_prep", s);
         if constexpr (sizeof(ST) == 2) {
-            // the decay-masked query-key block P only feeds the output
+            // the decay-masked query-key block P only feeds the output. When every unit fits on the
+            // GPU at once (8 two-wavefront workgroups per CU), the chunk's latency is the launch's
+            // and two wavefronts per chunk halve it; otherwise one wavefront per chunk spends fewer
+            // instructions per chunk.
             const unsigned gx = prep_grid(H, slots);
-            if (mode == 0)
-                gdn_prep_wave_kernel<KD, true><<<gx, 64, 0, s>>>(
-                    q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
-            else
-                gdn_prep_wave_kernel<KD, false><<<gx, 64, 0, s>>>(
-                    q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+            const int2* tab = packed ? ws.table : nullptr;
+            const bool two = (long)H * slots <= 8L * device_cus();
+            if (two) {
+                if (mode == 0)
+                    gdn_prep_2w_kernel<KD, true><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+                else
+                    gdn_prep_2w_kernel<KD, false><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+            } else {
+                if (mode == 0)
+                    gdn_prep_1w_kernel<KD, true><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+                else
+                    gdn_prep_1w_kernel<KD, false><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+            }
         } else
             gdn_prep_kernel<ST, KD><<<dim3((unsigned)slots, H), 256, 0, s>>>(
                 q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, scale, mode == 0 ? 1 : 0,
