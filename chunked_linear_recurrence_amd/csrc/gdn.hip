@@ -1558,6 +1558,304 @@ __global__ __launch_bounds__(512) void gdn_chain_1w_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// ST + Out, bf16, one workgroup per (sequence, head) and group of eight 16-row slices, for
+// launches with many more slices than CUs. There every CU runs slice after slice, and what
+// bounds a step is how many bytes each CU must pull from L2 per chunk: the per-slice kernel
+// above loads the chunk's K, Q and factor record once per slice, this one once per eight.
+//  - Wavefronts 0..7 each run one slice's whole chunk step with its state in registers, as the
+//    chunk algebra states it (no look-ahead, so the key-key block of the record is not read):
+//    X = K S^T, Y = V - Gamma X, R = T diag(beta) Y, O = scale Gamma Q S^T + P R,
+//    S <- Gamma_L S + K^T (e R).
+//  - Wavefronts 8 and 9 move chunk c+1 (K and Q rows, T, P, coefficients, the eight V slices)
+//    into the other of two LDS buffers with 16-byte direct loads while chunk c computes, and
+//    touch the lines of chunk c+2 so that those loads find them in L2.
+// One workgroup barrier per chunk.
+// ---------------------------------------------------------------------------
+template <int KD, bool SUMMARY>
+struct HeadLds {
+    typedef RowBlock<KD> RBk;
+    static constexpr int KP = KD / 32, KB = KD / 16;
+    static constexpr int NS = 8;                                       // slices per workgroup
+    static constexpr int OFF_K = 0;                                    // K rows (RowBlock)
+    static constexpr int OFF_Q = OFF_K + RBk::BYTES;                   // Q rows (RowBlock)
+    static constexpr int OFF_T = OFF_Q + (SUMMARY ? 0 : RBk::BYTES);   // kTriFrags fragments of 1 KB
+    static constexpr int OFF_P = OFF_T + kTriFrags * 1024;             // kTriFrags fragments of 1 KB
+    static constexpr int OFF_C = OFF_P + (SUMMARY ? 0 : kTriFrags * 1024);  // coefficients float[256]
+    static constexpr int OFF_V = OFF_C + 256 * 4;                      // [NS][64][16] bf16 V slices
+    static constexpr int BUF = OFF_V + NS * GC * 16 * 2;
+    static constexpr int OFF_JUNK = 2 * BUF;                           // sink of cache warm-up loads
+    static constexpr int BYTES = OFF_JUNK + 128 * 4;
+    static_assert(BYTES <= 160 * 1024, "LDS plan exceeds the CU's 160 KB");
+};
+
+template <int KD, bool SUMMARY>
+__global__ __launch_bounds__(640) void gdn_chain_head_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ h0, const int32_t* __restrict__ cu, const int* __restrict__ chunk_off,
+    const uint8_t* __restrict__ fac, int T, int H, int HK, int V, int n_seq, int nc, int ngrp,
+    float scale, bf16_t* __restrict__ out, float* __restrict__ ht, float* __restrict__ Mout) {
+    typedef HeadLds<KD, SUMMARY> SM;
+    typedef RowBlock<KD> RBk;
+    typedef Elem<bf16_t> El;
+    constexpr int KP = SM::KP, KB = SM::KB, NS = SM::NS;
+    constexpr int UST = (16 / RBk::RPB) * 1024;  // byte step of one 16-row token tile in a row block
+
+    __shared__ __align__(16) uint8_t smem[SM::BYTES];
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    typedef __attribute__((address_space(3))) float lds_f32;
+    lds_u8* const lds0 = (lds_u8*)smem;
+
+    int chain, grp;
+    xcd_split(blockIdx.x, ngrp, chain, grp);
+    if (chain >= n_seq * H) return;
+    const int n = chain / H, h = chain % H, hk = h / (H / HK);
+    const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rows = SUMMARY ? V + KD : V;
+
+    int b, bos, eos, slot0;
+    if (cu) {
+        b = 0;
+        bos = cu[n];
+        eos = cu[n + 1];
+        slot0 = chunk_off[n];
+    } else {
+        b = n;
+        bos = 0;
+        eos = T;
+        slot0 = n * nc;
+    }
+    const int nch = (eos - bos + GC - 1) / GC;
+    const size_t rec_bytes = gdn_factor_bytes(2);
+    auto buf = [&](int c) __attribute__((always_inline)) { return lds0 + (c & 1) * SM::BUF; };
+    auto record = [&](int c) __attribute__((always_inline)) {
+        return fac + ((size_t)(slot0 + c) * H + h) * rec_bytes;
+    };
+    auto barrier = [] __attribute__((always_inline)) () { asm volatile("s_barrier" ::: "memory"); };
+
+    if (wave < NS) {
+        // ================= one slice: the state recurrence and the output =================
+        const int vb = grp * NS + wave, row0 = 16 * vb;
+        const bool active = row0 < rows;
+        const bool vrows = row0 < V;                       // value rows (else transition rows, summary only)
+        const uint32_t vmask = vrows ? 0xffffffffu : 0u;
+        f32x4 S[KB];
+#pragma unroll
+        for (int kt = 0; kt < KB; ++kt) {
+            const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
+            if constexpr (!SUMMARY) {
+                S[kt] = (active && h0) ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + row) * KD + kk) : zero4();
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[kt][r] = (!vrows && kk + r == row - V) ? 1.f : 0.f;
+            }
+        }
+        int orow[KP], otr[KP];
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            orow[p] = RBk::off(ln, 4 * p + lg);                             // row fragment (0, p)
+            otr[p] = RBk::off(4 * lg + (ln >> 2), 4 * p + (ln & 3));        // transposed read, column pair p
+        }
+        const int off_v = SM::OFF_V + (wave * GC * 16 + (4 * lg + (ln >> 2)) * 16 + 4 * (ln & 3)) * 2;
+        barrier();
+        for (int c = 0; c < nch; ++c) {
+            if (active) {
+                lds_u8* B = buf(c);
+                const lds_f32* cf = (const lds_f32*)(B + SM::OFF_C);
+                // bf16 entry state: B operand of X and A operand of the output
+                i16x4 Sf[KB];
+#pragma unroll
+                for (int kt = 0; kt < KB; ++kt) Sf[kt] = El::pack(S[kt]);
+                // X = K S^T
+                f32x4 X[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    X[u] = zero4();
+#pragma unroll
+                    for (int p = 0; p < KP; ++p) X[u] = mma32(*(lds_bf16x8*)(B + SM::OFF_K + orow[p] + u * UST), cat8(Sf[2 * p], Sf[2 * p + 1]), X[u]);
+                }
+                // Y = V - Gamma X (beta is folded into the stored T)
+                i16x4 Yf[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const i16x4 vx = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(B + off_v + 16 * u * 16 * 2));
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    const i16x4 Vf = __builtin_bit_cast(i16x4, __builtin_bit_cast(u32x2, vx) & vmask);
+                    const f32x4 gam = *(const lds_f32x4*)(cf + 16 * u + 4 * lg);
+                    Yf[u] = El::pack(El::unpack(Vf) - gam * X[u]);
+                }
+                // R = T diag(beta) Y (T lower triangular, fragment pairs of 32 columns)
+                bf16x8 Tf[kTriFrags];
+#pragma unroll
+                for (int f = 0; f < kTriFrags; ++f) Tf[f] = *(lds_bf16x8*)(B + SM::OFF_T + f * 1024 + lane * 16);
+                f32x4 R[4];
+                const bf16x8 Y01 = cat8(Yf[0], Yf[1]), Y23 = cat8(Yf[2], Yf[3]);
+                R[0] = mma32(Tf[tri_frag(0, 0)], Y01, zero4());
+                R[1] = mma32(Tf[tri_frag(1, 0)], Y01, zero4());
+                R[2] = mma32(Tf[tri_frag(2, 1)], Y23, mma32(Tf[tri_frag(2, 0)], Y01, zero4()));
+                R[3] = mma32(Tf[tri_frag(3, 1)], Y23, mma32(Tf[tri_frag(3, 0)], Y01, zero4()));
+                i16x4 ER[4];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) ER[ti] = El::pack(R[ti] * *(const lds_f32x4*)(cf + 64 + 16 * ti + 4 * lg));
+                if constexpr (!SUMMARY) {
+                    // O^T = scale Gamma (S Q^T) + R^T P^T, token tile by token tile
+                    const int t0 = bos + c * GC, L = min(GC, eos - t0);
+                    i16x4 Rb[4];
+#pragma unroll
+                    for (int ti = 0; ti < 4; ++ti) Rb[ti] = El::pack(R[ti]);
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        f32x4 o = zero4();
+#pragma unroll
+                        for (int p = 0; p < KP; ++p)
+                            o = mma32(cat8(Sf[2 * p], Sf[2 * p + 1]), *(lds_bf16x8*)(B + SM::OFF_Q + orow[p] + tt * UST), o);
+                        o = o * (cf[16 * tt + ln] * scale);
+#pragma unroll
+                        for (int pp = 0; pp <= tt / 2; ++pp)
+                            o = mma32(cat8(Rb[2 * pp], Rb[2 * pp + 1]), *(lds_bf16x8*)(B + SM::OFF_P + tri_frag(tt, pp) * 1024 + lane * 16), o);
+                        const int t = 16 * tt + ln;
+                        if (t < L) *reinterpret_cast<i16x4*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + 4 * lg) = El::pack(o);
+                    }
+                }
+                // S^T <- Gamma_L S^T + K^T (e R)
+                const float gl = cf[63];
+                const bf16x8 E01 = cat8(ER[0], ER[1]), E23 = cat8(ER[2], ER[3]);
+#pragma unroll
+                for (int kt = 0; kt < KB; ++kt) {
+                    const int p = kt >> 1, hh = kt & 1;
+                    i16x4 Ka[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        Ka[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(B + SM::OFF_K + otr[p] + 8 * hh + u * UST));
+                    f32x4 acc = S[kt] * gl;
+                    acc = mma32(cat8(Ka[0], Ka[1]), E01, acc);
+                    acc = mma32(cat8(Ka[2], Ka[3]), E23, acc);
+                    S[kt] = acc;
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            barrier();
+        }
+        if (active) {
+#pragma unroll
+            for (int kt = 0; kt < KB; ++kt) {
+                const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
+                if (vrows) {
+                    if (ht) *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + row) * KD + kk) = S[kt];
+                } else if constexpr (SUMMARY) {
+                    *reinterpret_cast<f32x4*>(Mout + (((size_t)n * H + h) * KD + (row - V)) * KD + kk) = S[kt];
+                }
+            }
+        }
+    } else {
+        // ================= feeders: direct loads into LDS, two wavefronts =================
+        // wavefront 8: K rows, T, coefficients, V slices 0..3; wavefront 9: Q rows, P, V slices 4..7.
+        // Rows past the end of a partial chunk repeat its last token (finite values that the
+        // stored T diag(beta) and e = 0 keep out of the state, and whose outputs are not stored).
+        const int fi = wave - NS;
+        const size_t krs = (size_t)HK * KD * 2, vrs = (size_t)H * V * 2;  // token strides (bytes)
+        auto feed_rows = [&](const bf16_t* src, int c, lds_u8* dst) __attribute__((always_inline)) {
+            const int t0 = bos + c * GC, L = min(GC, eos - t0);
+            const uint8_t* base = reinterpret_cast<const uint8_t*>(src + ((size_t)(b * T + t0) * HK + hk) * KD);
+#pragma unroll
+            for (int m = 0; m < RBk::NLOAD; ++m) {
+                const int r = m * RBk::RPB + lane / RBk::PCS, pc = lane % RBk::PCS;
+                load_lds16(base + (size_t)min(r, L - 1) * krs + 16 * (pc ^ RBk::swz(r)), (uint8_t*)(dst + m * 1024));
+            }
+        };
+        // V slice j [64][16]: instruction hv, lane l -> token 32 hv + l/2, values 16 j + 8 (l%2) .. + 7
+        auto feed_v = [&](int c, int j) __attribute__((always_inline)) {
+            const int t0 = bos + c * GC, L = min(GC, eos - t0);
+            const uint8_t* vb0 = reinterpret_cast<const uint8_t*>(v + (size_t)(b * T + t0) * H * V + (size_t)h * V);
+#pragma unroll
+            for (int hv = 0; hv < 2; ++hv) {
+                const int t = min(32 * hv + (lane >> 1), L - 1);
+                load_lds16(vb0 + (size_t)t * vrs + (16 * (grp * NS + j) + 8 * (lane & 1)) * 2,
+                           (uint8_t*)(buf(c) + SM::OFF_V + j * GC * 16 * 2 + hv * 1024));
+            }
+        };
+        // the V slices this group holds (summary transition rows have none)
+        const int vslices = max(0, min(NS, V / 16 - grp * NS));
+        auto issue = [&](int c) __attribute__((always_inline)) {  // returns load instructions issued
+            lds_u8* B = buf(c);
+            const uint8_t* rec = record(c) + lane * 16;
+            int nl = 0;
+            if (fi == 0) {
+                feed_rows(k, c, B + SM::OFF_K);
+#pragma unroll
+                for (int f = 0; f < kTriFrags; ++f) load_lds16(rec + f * 1024, (uint8_t*)(B + SM::OFF_T + f * 1024));
+                load_lds16(rec + 2 * GC * GC * 2, (uint8_t*)(B + SM::OFF_C));
+                nl = RBk::NLOAD + kTriFrags + 1;
+                for (int j = 0; j < min(vslices, NS / 2); ++j) {
+                    feed_v(c, j);
+                    nl += 2;
+                }
+            } else {
+                if constexpr (!SUMMARY) {
+                    feed_rows(q, c, B + SM::OFF_Q);
+#pragma unroll
+                    for (int f = 0; f < kTriFrags; ++f) load_lds16(rec + GC * GC * 2 + f * 1024, (uint8_t*)(B + SM::OFF_P + f * 1024));
+                    nl = RBk::NLOAD + kTriFrags;
+                }
+                for (int j = NS / 2; j < vslices; ++j) {
+                    feed_v(c, j);
+                    nl += 2;
+                }
+            }
+            return nl;
+        };
+        // Cache warm-up: one 4-byte load per 128-byte line of chunk c, from the list K rows [0, 128),
+        // Q rows [128, 256) (K again in summary mode), the head's V rows [256, 384) (two lines per
+        // token each), then the record's T [384, 432), P [432, 480) and coefficient [480, 488) lines;
+        // lane l of wavefront fi touches lines 4 (64 fi + l) .. + 3 (past the end: the last line).
+        constexpr int NLINES = 488;
+        auto warm = [&](int c) __attribute__((always_inline)) {
+            const int t0 = bos + c * GC, L = min(GC, eos - t0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int li = min(4 * (64 * fi + lane) + e, NLINES - 1);
+                const uint8_t* a;
+                if (li < 256) {
+                    const int t = min((li & 127) >> 1, L - 1);
+                    const bf16_t* base = (li < 128 || SUMMARY) ? k : q;
+                    a = reinterpret_cast<const uint8_t*>(base + ((size_t)(b * T + t0 + t) * HK + hk) * KD) + (li & 1) * (KD >= 128 ? 128 : 0);
+                } else if (li < 384) {
+                    const int t = min((li - 256) >> 1, L - 1);
+                    a = reinterpret_cast<const uint8_t*>(v + ((size_t)(b * T + t0 + t) * H + h) * V) + (li & 1) * (V >= 128 ? 128 : 0);
+                } else {
+                    const int r = li - 384;
+                    const size_t off = r < 48 ? (size_t)r * 128 : r < 96 ? (size_t)GC * GC * 2 + (r - 48) * 128
+                                                                         : (size_t)2 * GC * GC * 2 + (r - 96) * 128;
+                    a = record(c) + off;
+                }
+                __builtin_amdgcn_global_load_lds(a, (__attribute__((address_space(3))) void*)(smem + SM::OFF_JUNK + fi * 256), 4, 0, 0);
+            }
+        };
+        // (loads complete in issue order: the wait after a step's loads and its warm-up leaves only
+        // the warm-up in flight)
+        if (nch > 0) issue(0);
+        if (nch > 1) warm(1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier();
+        for (int c = 0; c < nch; ++c) {
+            if (c + 1 < nch) {
+                issue(c + 1);
+                if (c + 2 < nch) {
+                    warm(c + 2);
+                    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+            }
+            barrier();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 hipError_t launch_chunk_table(const int32_t* cu, int N, int chunk, long cap, int* chunk_off,
                               int2* table, hipStream_t s) {
     timing_begin("chunk_table", s);
@@ -1625,6 +1923,23 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
     if (chains == 0) return hipSuccess;
     if constexpr (sizeof(ST) == 2) {
         const int nvb = rows / 16;
+        // more 16-row slices than two per CU: the CUs run slice after slice, and one workgroup per
+        // eight slices loads each chunk's shared operands once for them
+        if ((long)chains * nvb > 2L * device_cus()) {
+            const int ngrp = (nvb + HeadLds<KD, false>::NS - 1) / HeadLds<KD, false>::NS;
+            const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * ngrp);
+            if (mode == 0) {
+                timing_begin("gdn_chain", s);
+                gdn_chain_head_kernel<KD, false><<<grid, 640, 0, s>>>(
+                    q, k, v, h0, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, ngrp, scale, out, ht, nullptr);
+            } else {
+                timing_begin("gdn_summary_chain", s);
+                gdn_chain_head_kernel<KD, true><<<grid, 640, 0, s>>>(
+                    q, k, v, nullptr, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, ngrp, scale, nullptr, ht, Mout);
+            }
+            timing_end(s);
+            return hipGetLastError();
+        }
         const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * nvb);
         if (mode == 0) {
             timing_begin("gdn_chain", s);

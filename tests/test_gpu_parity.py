@@ -114,6 +114,32 @@ def test_gdn_bf16_reduced(dev, oracle, T, D, shift):
     check_bf16("reduced", f32(o), ro, f32(ht), rh)
 
 
+# Launches with more 16-row slices than two per CU (256 CUs on MI355X) take the per-head chain
+# kernel (one workgroup per eight slices of a head); these cases reach it at small sizes, with a
+# ragged last chunk, h0, grouped heads and summary mode.
+@pytest.mark.parametrize("D,H,HK", [(128, 40, 40), (64, 72, 72), (128, 40, 10)])
+def test_gdn_bf16_many_heads(dev, oracle, D, H, HK):
+    say(f"case: GDN bf16 B=2 T=200 H={H} HK={HK} K=V={D} (more slices than two per CU) h0 N(0,0.02)")
+    d = wl.delta_rule_inputs(B=2, T=200, H=H, HK=HK, K=D, V=D, dtype=torch.bfloat16, seed=D + H + HK,
+                             gate_shift=1.0, h0_std=0.02)
+    o, ht = sf.gdn_chunk_fwd(cuda(d["q"], dev), cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev),
+                             cuda(d["beta"], dev), cuda(d["h0"], dev), output_final_state=True)
+    ro, rh = oracle.gdn_forward(f32(d["q"]), f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(d["beta"]), f32(d["h0"]))
+    check_bf16("many heads", f32(o), ro, f32(ht), rh)
+
+
+def test_gdn_summary_many_rows(dev, oracle):
+    say("case: GDN bf16 summary, 8 rows x H=8 K=V=128 (more slices than two per CU), rows with tails")
+    d = wl.delta_rule_inputs(B=8, T=200, H=8, K=128, V=128, dtype=torch.bfloat16, seed=77, gate_shift=-5.0,
+                             beta_scale=0.3)
+    M, E = sf.segment_summary("gdn", cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev), cuda(d["beta"], dev))
+    rM, rE = oracle.gdn_summary(f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(d["beta"]))
+    assert np.abs(rM).max() > 0.1  # the transition is far from zero here
+    eM, eE = rel_rms(f32(M), rM), rel_rms(f32(E), rE)
+    say(f"  rel_rms(M)={eM:.3e} rel_rms(S_ext)={eE:.3e}")
+    assert eM <= BF16_RTOL and eE <= BF16_RTOL
+
+
 def test_dense_gdn_full_size(dev, oracle):
     say("case: dense GDN prefill B=2 T=4096 H=16 K=V=128 bf16 (full size, heads 0, 7, 15 vs oracle)")
     w = wl.dense_gdn()
