@@ -40,7 +40,8 @@ KINDS = {"gdn": SF_KIND_GDN, "gla": SF_KIND_GLA}
 EXPORTED = (
     "sf_version", "sf_last_error", "sf_gdn_chunk_fwd_workspace", "sf_gdn_chunk_fwd",
     "sf_gla_chunk_fwd", "sf_segment_summary_workspace", "sf_segment_summary",
-    "sf_state_scan", "sf_timing_enable", "sf_timing_collect",
+    "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_timing_enable",
+    "sf_timing_collect",
 )
 
 
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
     L.sf_segment_summary.argtypes = [I, I, P, P, P, P, I, I, I, I, I, I, I, P, P, P, Z, P]
     L.sf_state_scan.restype = I
     L.sf_state_scan.argtypes = [I, P, P, P, I, I, I, I, I, P, P, P]
+    L.sf_gdn_segmented_fwd_workspace.restype = Z
+    L.sf_gdn_segmented_fwd_workspace.argtypes = [I, I, I, I, I, I, I]
+    L.sf_gdn_segmented_fwd.restype = I
+    L.sf_gdn_segmented_fwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, Z, P]
     L.sf_timing_enable.restype = I
     L.sf_timing_enable.argtypes = [I]
     L.sf_timing_collect.restype = I
@@ -252,16 +257,23 @@ def segment_view(x: torch.Tensor, n_seg: int) -> torch.Tensor:
 
 
 def segmented_gdn_fwd(q, k, v, g, beta, n_seg, initial_state=None, *, scale=None, output_final_state=False):
-    """One long Gated Delta Rule run cut into n_seg segments per batch row (summary -> scan -> forward).
-    Equals gdn_chunk_fwd on the whole rows up to floating-point order."""
-    B, T = q.shape[:2]
-    if (T // n_seg) % 64:
-        raise ValueError("segment length must be a multiple of the 64-token chunk")
-    sv = lambda x: segment_view(x, n_seg)
-    M, S_ext = segment_summary("gdn", sv(k), sv(v), sv(g), sv(beta), chunk=64)
-    S_in, S_final = state_scan("gdn", M, S_ext, initial_state, B=B, n_seg=n_seg, final_state=output_final_state)
-    o, _ = gdn_chunk_fwd(sv(q), sv(k), sv(v), sv(g), sv(beta), S_in, scale=scale)
-    return o.view(q.shape[0], T, *o.shape[2:]), S_final
+    """One long Gated Delta Rule run cut into n_seg segments per batch row (summary -> scan -> forward,
+    one sf_gdn_segmented_fwd call). Equals gdn_chunk_fwd on the whole rows up to floating-point order."""
+    B, T, H, HK, K, V, N = _token_args(q, k, v, g, beta, initial_state, None)
+    if n_seg <= 0 or T % n_seg or (T // n_seg) % 64:
+        raise ValueError("T must split into n_seg segments whose length is a multiple of the 64-token chunk")
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    dev = q.device
+    out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+    ht = torch.empty((B, H, V, K), dtype=torch.float32, device=dev) if output_final_state else None
+    dt = _dt(q)
+    nbytes = lib().sf_gdn_segmented_fwd_workspace(dt, B, n_seg, T, H, K, V)
+    ws = _workspace(nbytes, dev)
+    _check(lib().sf_gdn_segmented_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), B,
+                                      n_seg, T, H, HK, K, V, float(scale), _ptr(out), _ptr(ht), _ptr(ws), nbytes,
+                                      _stream()))
+    return out, ht
 
 
 def segmented_gla_fwd(q, k, v, g, n_seg, initial_state=None, *, scale=1.0, chunk=64, output_final_state=False):

@@ -1881,16 +1881,16 @@ template <typename ST, int KD>
 static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const float* g,
                           const float* beta, const float* h0, const int32_t* cu,
                           const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int V,
-                          float scale, ST* out, float* ht, float* Mout, hipStream_t s) {
+                          float scale, ST* out, float* ht, float* Mout, hipStream_t s, int stages) {
     const bool packed = cu != nullptr;
     const long slots = gdn_slots(B, T, N, packed);
     const int nc = (T + GC - 1) / GC;
     hipError_t err;
-    if (packed) {
+    if (packed && (stages & 1)) {
         err = launch_chunk_table(cu, N, GC, slots, ws.chunk_off, ws.table, s);
         if (err != hipSuccess) return err;
     }
-    if (slots > 0) {
+    if (slots > 0 && (stages & 1)) {
         timing_begin("gdn_prep", s);
         if constexpr (sizeof(ST) == 2) {
             // the decay-masked query-key block P only feeds the output. When every unit fits on the
@@ -1918,6 +1918,7 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
         timing_end(s);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
+    if (!(stages & 2)) return hipSuccess;
     const int rows = mode == 0 ? V : V + KD;
     const int chains = N * H;
     if (chains == 0) return hipSuccess;
@@ -1972,15 +1973,15 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
 hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const float* h0, const int32_t* cu,
                       const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int K, int V,
-                      float scale, void* out, float* ht, float* Mout, hipStream_t s) {
+                      float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages) {
     if (bf16) {
         const bf16_t *qq = (const bf16_t*)q, *kk = (const bf16_t*)k, *vv = (const bf16_t*)v;
-        if (K == 128) return run_gdn<bf16_t, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s);
-        return run_gdn<bf16_t, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s);
+        if (K == 128) return run_gdn<bf16_t, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s, stages);
+        return run_gdn<bf16_t, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s, stages);
     }
     const float *qq = (const float*)q, *kk = (const float*)k, *vv = (const float*)v;
-    if (K == 128) return run_gdn<float, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s);
-    return run_gdn<float, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s);
+    if (K == 128) return run_gdn<float, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s, stages);
+    return run_gdn<float, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s, stages);
 }
 
 }  // namespace sf

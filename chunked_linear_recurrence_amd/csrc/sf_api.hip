@@ -226,6 +226,74 @@ sf_status sf_segment_summary(sf_kind kind, sf_dtype dt, const void* k, const voi
     return fail(SF_ERR_INVALID, "kind must be SF_KIND_GDN or SF_KIND_GLA");
 }
 
+namespace {
+// Segmented delta-rule workspace: the per-segment Pre records, then M, S_ext and the entry states.
+struct SegWorkspace {
+    sf::GdnWorkspace pre;
+    float *M, *S_ext, *S_in;
+    size_t bytes;
+};
+SegWorkspace seg_layout(void* base, int eb, int n_rows, int L_seg, int H, int K, int V) {
+    SegWorkspace w{};
+    w.pre = sf::gdn_workspace_layout(base, eb, n_rows, L_seg, H, n_rows, false);
+    size_t off = w.pre.bytes;
+    uint8_t* p = static_cast<uint8_t*>(base);
+    auto take = [&](size_t n) {
+        float* r = reinterpret_cast<float*>(p ? p + off : nullptr);
+        off += sf::align256(n * sizeof(float));
+        return r;
+    };
+    w.M = take((size_t)n_rows * H * K * K);
+    w.S_ext = take((size_t)n_rows * H * V * K);
+    w.S_in = take((size_t)n_rows * H * V * K);
+    w.bytes = off;
+    return w;
+}
+}  // namespace
+
+size_t sf_gdn_segmented_fwd_workspace(sf_dtype dt, int B, int n_seg, int T, int H, int K, int V) {
+    if ((dt != SF_F32 && dt != SF_BF16) || B < 0 || n_seg <= 0 || T < 0 || T % n_seg || H <= 0 || K <= 0 || V <= 0)
+        return 0;
+    return seg_layout(nullptr, elem_bytes(dt), B * n_seg, T / n_seg, H, K, V).bytes;
+}
+
+sf_status sf_gdn_segmented_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* h0, int B, int n_seg, int T, int H, int HK,
+                               int K, int V, float scale, void* out, float* ht, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (n_seg <= 0 || T % (n_seg > 0 ? n_seg : 1) != 0)
+        return fail(SF_ERR_INVALID, "T=%d must be a positive multiple of n_seg=%d", T, n_seg);
+    const int L_seg = T / n_seg, n_rows = B * n_seg;
+    if (L_seg % sf::kGdnChunk != 0)
+        return fail(SF_ERR_INVALID, "the segment length %d must be a multiple of the chunk (%d)", L_seg, sf::kGdnChunk);
+    sf_status st = check_tokens(dt, n_rows, L_seg, H, HK, K, V, n_rows, false);
+    if (st != SF_OK) return st;
+    if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
+    if (K != V || (K != 64 && K != 128))
+        return fail(SF_ERR_UNSUPPORTED, "delta-rule kernels are built for K == V in {64, 128} (K=%d V=%d)", K, V);
+    if (!fits((long)n_rows * H * K * K)) return fail(SF_ERR_UNSUPPORTED, "M has 2^31 or more elements");
+    const SegWorkspace need = seg_layout(nullptr, elem_bytes(dt), n_rows, L_seg, H, K, V);
+    if (!workspace || workspace_bytes < need.bytes)
+        return fail(SF_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                    need.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(SF_ERR_INVALID, "workspace must be 256-byte aligned");
+    const SegWorkspace ws = seg_layout(workspace, elem_bytes(dt), n_rows, L_seg, H, K, V);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf = dt == SF_BF16;
+    // Pre once on the segment view (with P, so the records serve both passes), then the summary
+    // pass, the exclusive scan and the forward pass from the true entry states
+    hipError_t e = sf::launch_gdn(bf, 0, q, k, v, g, beta, nullptr, nullptr, ws.pre, n_rows, n_rows, L_seg, H, HK, K, V,
+                                  scale, nullptr, nullptr, nullptr, s, 1);
+    if (e == hipSuccess)
+        e = sf::launch_gdn(bf, 1, nullptr, k, v, g, beta, nullptr, nullptr, ws.pre, n_rows, n_rows, L_seg, H, HK, K, V,
+                           1.f, nullptr, ws.S_ext, ws.M, s, 2);
+    if (e == hipSuccess) e = sf::launch_scan(0, ws.M, ws.S_ext, h0, B, n_seg, H, K, V, ws.S_in, ht, s);
+    if (e == hipSuccess)
+        e = sf::launch_gdn(bf, 0, q, k, v, g, beta, ws.S_in, nullptr, ws.pre, n_rows, n_rows, L_seg, H, HK, K, V,
+                           scale, out, nullptr, nullptr, s, 2);
+    return hip_status(e, "sf_gdn_segmented_fwd launch");
+}
+
 sf_status sf_state_scan(sf_kind kind, const float* M, const float* S_ext, const float* h0, int B, int n_seg,
                         int H, int K, int V, float* S_in, float* S_final, void* stream) {
     if (kind != SF_KIND_GDN && kind != SF_KIND_GLA) return fail(SF_ERR_INVALID, "kind must be SF_KIND_GDN or SF_KIND_GLA");

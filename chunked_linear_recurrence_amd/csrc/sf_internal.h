@@ -64,11 +64,13 @@ void timing_end(hipStream_t s);
 hipError_t launch_chunk_table(const int32_t* cu, int N, int chunk, long cap, int* chunk_off,
                               int2* table, hipStream_t s);
 
-// mode: 0 = forward (writes out/ht), 1 = summary (writes S_ext into ht, M into Mout)
+// mode: 0 = forward (writes out/ht), 1 = summary (writes S_ext into ht, M into Mout).
+// stages: 1 = Pre (and the chunk table) into the workspace, 2 = the chain from the workspace's
+// records, 3 = both. Pre of mode 0 also forms P, so its records serve both modes.
 hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const float* h0, const int32_t* cu,
                       const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int K, int V,
-                      float scale, void* out, float* ht, float* Mout, hipStream_t s);
+                      float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages = 3);
 
 hipError_t launch_gla(bool bf16, int mode, const void* q, const void* k, const void* v,
                       const float* g, const float* h0, const int32_t* cu, int N, int B, int T,

@@ -166,6 +166,32 @@ sf_status sf_state_scan(sf_kind kind, const float *M, const float *S_ext, const 
                         int B, int n_seg, int H, int K, int V, float *S_in, float *S_final,
                         void *stream);
 
+/* Workspace bytes needed by sf_gdn_segmented_fwd (0 for invalid sizes). */
+size_t sf_gdn_segmented_fwd_workspace(sf_dtype dt, int B, int n_seg, int T, int H, int K, int V);
+
+/*
+ * Gated Delta Rule forward of B long sequences, each cut into n_seg contiguous
+ * segments laid along the batch axis (Megatron-LM "Mamba2 state-passing
+ * context parallelism": summarise every segment, recover the true entry
+ * states with an exclusive scan, then finish each segment from its entry
+ * state; attention-gym "Context Parallelism" for the delta rule's affine
+ * range maps). The same result as sf_segment_summary, sf_state_scan and
+ * sf_gdn_chunk_fwd on the segment view, with the chunk factors of every
+ * segment formed once for both passes.
+ *   q, k [B, T, HK, K] dt, v [B, T, H, V] dt, g and beta [B, T, H] float32;
+ *   T a multiple of n_seg and T / n_seg a multiple of 64.
+ *   h0 [B, H, V, K] float32 or NULL for zeros; out [B, T, H, V] dt;
+ *   ht [B, H, V, K] float32 final states, or NULL.
+ *   workspace at least sf_gdn_segmented_fwd_workspace(...) bytes, 256-byte
+ *   aligned (it holds the factors, the summaries and the entry states).
+ * Supported: K == V, K in {64, 128}.
+ */
+sf_status sf_gdn_segmented_fwd(sf_dtype dt, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *h0, int B,
+                               int n_seg, int T, int H, int HK, int K, int V, float scale,
+                               void *out, float *ht, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 /*
  * Kernel timing hook for measurement. While enabled, every kernel the
  * library enqueues is bracketed by a pair of HIP events recorded on the same

@@ -63,6 +63,36 @@ def test_workspace_sizes(L):
     assert L.sf_gdn_chunk_fwd_workspace(7, 1, 1, 1, 64, 64, 1, 0) == 0
 
 
+def test_segmented_workspace_size(L):
+    # per segment row: the Pre records, then M [rows, H, K, K], S_ext and S_in [rows, H, V, K], float32,
+    # each 256-aligned
+    rec = 3 * 64 * 64 * 2 + 1024
+    al = lambda x: (x + 255) // 256 * 256
+    B, n_seg, T, H, K = 1, 16, 262144, 16, 128
+    rows, L_seg = B * n_seg, T // n_seg
+    want = al(rows * (L_seg // 64) * H * rec) + al(4 * rows * H * K * K) + 2 * al(4 * rows * H * K * K)
+    assert L.sf_gdn_segmented_fwd_workspace(sf.SF_BF16, B, n_seg, T, H, K, K) == want
+    assert L.sf_gdn_segmented_fwd_workspace(sf.SF_BF16, 1, 3, 1000, 4, 64, 64) == 0  # T not a multiple of n_seg
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(T=1000, n_seg=8), sf.SF_ERR_INVALID, "multiple of the chunk"),
+    (dict(T=999, n_seg=8), sf.SF_ERR_INVALID, "multiple of n_seg"),
+    (dict(n_seg=0), sf.SF_ERR_INVALID, "multiple of n_seg"),
+    (dict(q=None), sf.SF_ERR_INVALID, "NULL"),
+    (dict(K=96, V=96), sf.SF_ERR_UNSUPPORTED, "K == V"),
+    (dict(wsb=16), sf.SF_ERR_WORKSPACE, "workspace"),
+])
+def test_segmented_rejects_before_enqueue(L, kw, status, msg):
+    a = dict(dt=sf.SF_BF16, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, B=1, n_seg=4, T=1024, H=4, HK=4,
+             K=128, V=128, scale=0.1, out=FAKE, ht=None, ws=FAKE * 256, wsb=1 << 40, s=None)
+    a.update(kw)
+    st = L.sf_gdn_segmented_fwd(a["dt"], a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["B"], a["n_seg"],
+                                a["T"], a["H"], a["HK"], a["K"], a["V"], a["scale"], a["out"], a["ht"], a["ws"],
+                                a["wsb"], a["s"])
+    assert st == status and msg in L.sf_last_error().decode()
+
+
 def gdn_call(L, **kw):
     a = dict(dt=sf.SF_BF16, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, N=2, B=2, T=64,
              H=4, HK=4, K=128, V=128, scale=0.1, out=FAKE, ht=None, ws=FAKE * 256, wsb=1 << 40, s=None)
