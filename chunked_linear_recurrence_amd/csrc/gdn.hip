@@ -295,198 +295,6 @@ inline unsigned prep_grid(int H, long n_slots) {
 }
 
 // ---------------------------------------------------------------------------
-// Pre, bf16, one wavefront per (chunk slot, head), for launches with more units than the GPU
-// holds at once (there the instructions spent per chunk count more than each chunk's latency):
-// the same steps as the two-wavefront kernel below, in one wavefront, with the P and T blocks
-// leaving through a 64x64 bf16 LDS staging tile.
-// ---------------------------------------------------------------------------
-template <int KD, bool WANT_P>
-__global__ __launch_bounds__(64) void gdn_prep_1w_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                         const float* __restrict__ g,
-                                                         const float* __restrict__ beta,
-                                                         const int2* __restrict__ table,
-                                                         const int32_t* __restrict__ cu, int T, int H,
-                                                         int HK, int nc, int n_slots, float scale,
-                                                         uint8_t* __restrict__ fac) {
-    constexpr int KP = KD / 32;
-    constexpr int LO = GC + 8;  // staging tile row stride (bf16)
-    __shared__ __align__(16) float sA[tri_off(GC)];
-    __shared__ __align__(16) bf16_t sO[GC * LO];
-    __shared__ __align__(16) float sD[GC * 16];  // diagonal blocks of T, row-major per block
-    __shared__ float sG[GC], sB[GC];
-
-    // blockIdx -> unit u = h * n_slots + slot, in runs of kPrepXcdRun units per XCD (workgroups go
-    // round-robin over the 8 XCDs)
-    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-    const int u = (idx / kPrepXcdRun) * (8 * kPrepXcdRun) + xcd * kPrepXcdRun + idx % kPrepXcdRun;
-    if (u >= H * n_slots) return;
-    const int h = u / n_slots;
-    const int hk = h / (H / HK);
-    const int lane = threadIdx.x, ln = lane & 15, lg = lane >> 4;
-    const bf16x8 zero8 = {};
-
-    bf16x8 kf[4][KP], qf[4][KP], kp[4][KP];
-    float gv, bv;
-    int b, t0, L, ci;
-    auto load = [&]() __attribute__((always_inline)) {
-        const int t_lane = min(lane, L - 1);
-        const size_t gi = (size_t)(b * T + t0 + t_lane) * H + h;
-        gv = lane < L ? g[gi] : 0.f;
-        bv = lane < L ? beta[gi] : 0.f;
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-            const int t = 16 * R + ln;
-            const size_t row = ((size_t)(b * T + t0 + min(t, L - 1)) * HK + hk) * KD;
-#pragma unroll
-            for (int p = 0; p < KP; ++p) {
-                const bf16x8 kv = *reinterpret_cast<const bf16x8*>(k + row + 32 * p + 8 * lg);
-                kf[R][p] = t < L ? kv : zero8;
-                if constexpr (WANT_P) {
-                    const bf16x8 qv = *reinterpret_cast<const bf16x8*>(q + row + 32 * p + 8 * lg);
-                    qf[R][p] = t < L ? qv : zero8;
-                }
-                // rows of the preceding (always full) chunk of the same sequence, for W
-                // (a sequence's first chunk loads its own first row and discards it)
-                const int pt = ci > 0 ? t0 - GC + t : t0;
-                const bf16x8 pv = *reinterpret_cast<const bf16x8*>(k + ((size_t)(b * T + pt) * HK + hk) * KD + 32 * p + 8 * lg);
-                kp[R][p] = ci > 0 ? pv : zero8;
-            }
-        }
-    };
-
-    const int slot = u % n_slots;
-    if (!chunk_coords(slot, table, cu, T, nc, b, t0, L, ci)) return;
-    load();
-    {
-        // gates of this slot
-        const float G = wave_inclusive_scan(gv);
-        sG[lane] = G;
-        sB[lane] = bv;
-        uint8_t* rec = fac + ((size_t)slot * H + h) * gdn_factor_bytes(2);
-        bf16_t* gT = reinterpret_cast<bf16_t*>(rec);
-        bf16_t* gP = gT + GC * GC;
-        float* gC = reinterpret_cast<float*>(gP + GC * GC);
-        {
-            const float GL = __shfl(G, 63, 64);
-            gC[lane] = expf(G);
-            gC[64 + lane] = expf(GL - G);
-            gC[128 + lane] = bv;
-            gC[192 + lane] = G;
-        }
-#pragma unroll
-        for (int i = 0; i < GC * LO / 8 / 64; ++i) *reinterpret_cast<u128*>(sO + 8 * (lane + 64 * i)) = u128{0u, 0u, 0u, 0u};
-        __syncthreads();
-
-#pragma unroll
-        for (int tt = 0; tt < 10; ++tt) {
-            const int ti = (tt >= 1) + (tt >= 3) + (tt >= 6);
-            const int tj = tt - ti * (ti + 1) / 2;
-            f32x4 a = zero4(), pq = zero4();
-#pragma unroll
-            for (int p = 0; p < KP; ++p) {
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ti][p], kf[tj][p], a, 0, 0, 0);
-                if constexpr (WANT_P) pq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ti][p], kf[tj][p], pq, 0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * ti + 4 * lg + r, i = 16 * tj + ln;
-                const float d = expf(fminf(sG[t] - sG[i], 0.f));
-                if (i < t) sA[col_off(i) + (t - i - 1)] = sB[t] * d * a[r];
-                if (WANT_P && i <= t) sO[t * LO + i] = f2bf(scale * d * pq[r]);
-            }
-        }
-        // W = K_c K_{c-1}^T (zero for a sequence's first chunk and for padded rows), as the A
-        // operand of W (e R)_{c-1}: fragment (u, p) holds, for lane (ln, lg), W[16 u + ln][32 p + 4 lg + j]
-        // then W[16 u + ln][32 p + 16 + 4 lg + j]. The C tile of K_{c-1} K_c^T (rows s, columns t) is
-        // exactly that lane content, so each fragment pairs two of those tiles without any shuffle.
-        {
-            bf16_t* gW = reinterpret_cast<bf16_t*>(rec + kGdnWOffset);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                f32x4 wt[4];
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) {
-                    wt[sb] = zero4();
-#pragma unroll
-                    for (int p = 0; p < KP; ++p) wt[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kp[sb][p], kf[u][p], wt[sb], 0, 0, 0);
-                }
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    const i16x4 lo = Elem<bf16_t>::pack(wt[2 * p]), hi = Elem<bf16_t>::pack(wt[2 * p + 1]);
-                    *reinterpret_cast<i16x8*>(gW + ((2 * u + p) * 64 + lane) * 8) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
-            }
-        }
-        __syncthreads();
-        if constexpr (WANT_P) store_tri_frags(sO, LO, gP);
-
-        // T = (I + A)^-1 by 16x16 blocks (A strictly lower, float32). The diagonal blocks
-        // D_b = (I + A_bb)^-1 come from forward substitution, lane (b, jj) holding column jj of D_b
-        // (15 steps for all four blocks at once); the others from block row i of (I + A) T = I,
-        //   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj  (T_jj = D_j),
-        // one block diagonal i - j at a time, as float32 MFMA block products (sf_device.h).
-        const int db = lane >> 4, dj = lane & 15;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == dj) ? 1.f : 0.f;
-#pragma unroll
-        for (int t = 0; t < 15; ++t) {
-            const float* col = sA + col_off(16 * db + t);  // rows 16 db + t + 1 .. of column 16 db + t
-            const float xt = x[t];
-#pragma unroll
-            for (int r = t + 1; r < 16; ++r) x[r] -= col[r - t - 1] * xt;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sD[(16 * db + r) * 16 + dj] = x[r];
-        __syncthreads();
-        // fragments: A operand lane (ln, lg) <- M[ln][4 lg + q], B operand <- M[4 lg + q][ln]
-        auto d_a = [&](int i) __attribute__((always_inline)) { return *reinterpret_cast<const f32x4*>(sD + (16 * i + ln) * 16 + 4 * lg); };
-        auto d_b = [&](int j) __attribute__((always_inline)) {
-            f32x4 r;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) r[q] = sD[(16 * j + 4 * lg + q) * 16 + ln];
-            return r;
-        };
-        auto a_a = [&](int i, int j) __attribute__((always_inline)) {  // block A_ij, i > j
-            f32x4 r;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = 16 * j + 4 * lg + q;
-                r[q] = sA[col_off(c) + (16 * i + ln) - c - 1];
-            }
-            return r;
-        };
-        f32x4 Tb[4][4];  // Tb[i][j], i > j, C tile: lane (ln, lg) holds T[16 i + 4 lg + r][16 j + ln]
-#pragma unroll
-        for (int dd = 1; dd < 4; ++dd)
-#pragma unroll
-            for (int j = 0; j + dd < 4; ++j) {
-                const int i = j + dd;
-                f32x4 u = Elem<float>::mma(zero4(), a_a(i, j), d_b(j));
-#pragma unroll
-                for (int kk = j + 1; kk < i; ++kk) u = Elem<float>::mma(u, a_a(i, kk), Tb[kk][j]);
-                Tb[i][j] = Elem<float>::mma(zero4(), d_a(i), u) * -1.f;
-            }
-        __syncthreads();  // staging tile free again (P copy done)
-        // stored as T diag(beta): column j scaled by beta_j (zero past the chunk's end); blocks above
-        // the diagonal stay zero from the clear at the start of the slot
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sO[(16 * db + r) * LO + 16 * db + dj] = f2bf(x[r] * bv);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float bj = sB[16 * j + ln];
-#pragma unroll
-            for (int i = j + 1; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sO[(16 * i + 4 * lg + r) * LO + 16 * j + ln] = f2bf(Tb[i][j][r] * bj);
-        }
-        __syncthreads();
-        store_tri_frags(sO, LO, gT);
-    }
-}
-
-
-// ---------------------------------------------------------------------------
 // Pre, bf16: one workgroup of two wavefronts per (chunk slot, head); the two never wait for
 // each other (each orders its own LDS traffic).
 //  - K and Q rows go straight from global memory into 16x16x32 MFMA fragments (lane (n, g)
@@ -497,17 +305,20 @@ __global__ __launch_bounds__(64) void gdn_prep_1w_kernel(const bf16_t* __restric
 //    reuses the A area, in fragment order.
 //  - Wavefront 1: its own copy of the gates; P^T = scale (D o K Q^T)^T tile by tile, whose C
 //    tiles are already the lane contents of P's fragments, so P goes out from registers.
-//  - The key-key block W = K_c K_{c-1}^T from the previous chunk's rows: each wavefront forms
-//    half of its fragments (wavefront 0 before its solve, wavefront 1 after P).
+//  - The key-key block W = K_c K_{c-1}^T from the previous chunk's rows, when a chain kernel that
+//    reads it runs on these records (want_w): each wavefront forms half of its fragments
+//    (wavefront 0 before its solve, wavefront 1 after P).
+//  With one wavefront (NW = 1, for launches larger than the GPU holds at once) the two parts run
+//  one after the other.
 // ---------------------------------------------------------------------------
-template <int KD, bool WANT_P>
-__global__ __launch_bounds__(128, 4) void gdn_prep_2w_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+template <int KD, bool WANT_P, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 2 ? 4 : 1) void gdn_prep_wave_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                             const float* __restrict__ g,
                                                             const float* __restrict__ beta,
                                                             const int2* __restrict__ table,
                                                             const int32_t* __restrict__ cu, int T, int H,
                                                             int HK, int nc, int n_slots, float scale,
-                                                            uint8_t* __restrict__ fac) {
+                                                            uint8_t* __restrict__ fac, int want_w) {
     constexpr int KP = KD / 32;
     static_assert(tri_off(GC) * 4 >= GC * GC * 2, "the T staging tile reuses the A area");
     __shared__ __align__(16) float sA[tri_off(GC)];  // A packed columns; then T diag(beta), bf16 [64][64]
@@ -585,7 +396,7 @@ __global__ __launch_bounds__(128, 4) void gdn_prep_2w_kernel(const bf16_t* __res
         }
     };
 
-    if (wave == 0) {
+    auto role0 = [&]() __attribute__((always_inline)) {
         const float bv = lane < L ? beta[gi] : 0.f;
         sB[lane] = bv;
         {
@@ -611,7 +422,7 @@ __global__ __launch_bounds__(128, 4) void gdn_prep_2w_kernel(const bf16_t* __res
                 if (i < t) sA[col_off(i) + (t - i - 1)] = sB[t] * d * a[r];
             }
         }
-        make_w(0);
+        if (want_w) make_w(0);
         wave_sync();
         // T = (I + A)^-1 by 16x16 blocks (A strictly lower, float32). The diagonal blocks
         // D_b = (I + A_bb)^-1 come from forward substitution, lane (b, jj) holding column jj of D_b
@@ -681,7 +492,8 @@ __global__ __launch_bounds__(128, 4) void gdn_prep_2w_kernel(const bf16_t* __res
         }
         wave_sync();
         store_tri_frags(sS, GC, gT);
-    } else {
+    };
+    auto role1 = [&]() __attribute__((always_inline)) {
         wave_sync();
         if constexpr (WANT_P) {
             // P^T tiles, K rows (A operand, rows s) against Q rows (B operand, columns t): C tile lane
@@ -720,7 +532,16 @@ __global__ __launch_bounds__(128, 4) void gdn_prep_2w_kernel(const bf16_t* __res
                 }
             }
         }
-        make_w(1);
+        if (want_w) make_w(1);
+    };
+    if constexpr (NW == 2) {
+        if (wave == 0)
+            role0();
+        else
+            role1();
+    } else {
+        role0();
+        role1();
     }
 }
 
@@ -1865,7 +1686,7 @@ hipError_t launch_chunk_table(const int32_t* cu, int N, int chunk, long cap, int
 }
 
 // Compute units of the current device (cached per device).
-static int device_cus() {
+int device_cus() {
     static int cache[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -1877,11 +1698,18 @@ static int device_cus() {
     return cache[dev];
 }
 
+// The bf16 chain runs one workgroup per 16-row state slice (gdn_chain_1w_kernel) unless the launch
+// has more than two slices per CU; then one workgroup per eight slices of a head
+// (gdn_chain_head_kernel), which loads each chunk's shared operands once for them.
+bool gdn_chain_per_slice(long chains, int rows) { return chains * (rows / 16) <= 2L * device_cus(); }
+
 template <typename ST, int KD>
 static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const float* g,
                           const float* beta, const float* h0, const int32_t* cu,
                           const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int V,
-                          float scale, ST* out, float* ht, float* Mout, hipStream_t s, int stages) {
+                          float scale, ST* out, float* ht, float* Mout, hipStream_t s, int stages, int pre_w) {
+    // the key-key block W is read only by the per-slice bf16 chain kernel
+    const int want_w = pre_w >= 0 ? pre_w : (gdn_chain_per_slice(N * H, mode == 0 ? V : V + KD) ? 1 : 0);
     const bool packed = cu != nullptr;
     const long slots = gdn_slots(B, T, N, packed);
     const int nc = (T + GC - 1) / GC;
@@ -1902,14 +1730,14 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
             const bool two = (long)H * slots <= 8L * device_cus();
             if (two) {
                 if (mode == 0)
-                    gdn_prep_2w_kernel<KD, true><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+                    gdn_prep_wave_kernel<KD, true, 2><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
                 else
-                    gdn_prep_2w_kernel<KD, false><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+                    gdn_prep_wave_kernel<KD, false, 2><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
             } else {
                 if (mode == 0)
-                    gdn_prep_1w_kernel<KD, true><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+                    gdn_prep_wave_kernel<KD, true, 1><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
                 else
-                    gdn_prep_1w_kernel<KD, false><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors);
+                    gdn_prep_wave_kernel<KD, false, 1><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
             }
         } else
             gdn_prep_kernel<ST, KD><<<dim3((unsigned)slots, H), 256, 0, s>>>(
@@ -1926,7 +1754,7 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
         const int nvb = rows / 16;
         // more 16-row slices than two per CU: the CUs run slice after slice, and one workgroup per
         // eight slices loads each chunk's shared operands once for them
-        if ((long)chains * nvb > 2L * device_cus()) {
+        if (!gdn_chain_per_slice(chains, rows)) {
             const int ngrp = (nvb + HeadLds<KD, false>::NS - 1) / HeadLds<KD, false>::NS;
             const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * ngrp);
             if (mode == 0) {
@@ -1973,15 +1801,15 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
 hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const float* h0, const int32_t* cu,
                       const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int K, int V,
-                      float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages) {
+                      float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages, int pre_w) {
     if (bf16) {
         const bf16_t *qq = (const bf16_t*)q, *kk = (const bf16_t*)k, *vv = (const bf16_t*)v;
-        if (K == 128) return run_gdn<bf16_t, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s, stages);
-        return run_gdn<bf16_t, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s, stages);
+        if (K == 128) return run_gdn<bf16_t, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s, stages, pre_w);
+        return run_gdn<bf16_t, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s, stages, pre_w);
     }
     const float *qq = (const float*)q, *kk = (const float*)k, *vv = (const float*)v;
-    if (K == 128) return run_gdn<float, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s, stages);
-    return run_gdn<float, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s, stages);
+    if (K == 128) return run_gdn<float, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s, stages, pre_w);
+    return run_gdn<float, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s, stages, pre_w);
 }
 
 }  // namespace sf

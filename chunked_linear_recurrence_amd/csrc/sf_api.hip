@@ -282,8 +282,10 @@ sf_status sf_gdn_segmented_fwd(sf_dtype dt, const void* q, const void* k, const 
     const bool bf = dt == SF_BF16;
     // Pre once on the segment view (with P, so the records serve both passes), then the summary
     // pass, the exclusive scan and the forward pass from the true entry states
+    // (the key-key block W only if one of the two chain passes runs per 16-row slice)
+    const int pre_w = (sf::gdn_chain_per_slice((long)n_rows * H, V + K) || sf::gdn_chain_per_slice((long)n_rows * H, V)) ? 1 : 0;
     hipError_t e = sf::launch_gdn(bf, 0, q, k, v, g, beta, nullptr, nullptr, ws.pre, n_rows, n_rows, L_seg, H, HK, K, V,
-                                  scale, nullptr, nullptr, nullptr, s, 1);
+                                  scale, nullptr, nullptr, nullptr, s, 1, pre_w);
     if (e == hipSuccess)
         e = sf::launch_gdn(bf, 1, nullptr, k, v, g, beta, nullptr, nullptr, ws.pre, n_rows, n_rows, L_seg, H, HK, K, V,
                            1.f, nullptr, ws.S_ext, ws.M, s, 2);

@@ -66,11 +66,19 @@ hipError_t launch_chunk_table(const int32_t* cu, int N, int chunk, long cap, int
 
 // mode: 0 = forward (writes out/ht), 1 = summary (writes S_ext into ht, M into Mout).
 // stages: 1 = Pre (and the chunk table) into the workspace, 2 = the chain from the workspace's
-// records, 3 = both. Pre of mode 0 also forms P, so its records serve both modes.
+// records, 3 = both. Pre of mode 0 also forms P, so its records serve both modes. pre_w: whether
+// Pre forms the key-key block W (read only by the per-slice chain kernel); -1 = as this call's
+// chain needs.
 hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const float* h0, const int32_t* cu,
                       const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int K, int V,
-                      float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages = 3);
+                      float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages = 3,
+                      int pre_w = -1);
+
+// Compute units of the current device, and whether a bf16 delta-rule chain over `chains`
+// (sequence, head) pairs of `rows` state rows runs per 16-row slice (else per head).
+int device_cus();
+bool gdn_chain_per_slice(long chains, int rows);
 
 hipError_t launch_gla(bool bf16, int mode, const void* q, const void* k, const void* v,
                       const float* g, const float* h0, const int32_t* cu, int N, int B, int T,
