@@ -17,6 +17,8 @@
 // Summary mode (Megatron-LM page: S_out = a_block S_in + S_ext): the state
 // runs from zero without outputs; S_ext is its exit value and
 // a_block = exp(sum of the gates).
+#include <type_traits>
+
 #include "sf_device.h"
 #include "sf_internal.h"
 
@@ -364,24 +366,28 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
     // ---- chunk c's K and V rows into LDS (rows past the end repeat the last token; their e = 0
     // keeps them out of the state and their outputs are not stored) and its gates into registers
     float rg[C / 64];
+    // (the lane index is laundered through an empty asm so that the per-lane address terms are
+    // formed here each time instead of being hoisted out of the chunk loop and kept live across it)
     auto load_chunk = [&](int c) __attribute__((always_inline)) {
         const int t0 = bos + c * C, L = min(C, eos - t0);
+        int lo = lane;
+        asm volatile("" : "+v"(lo));
 #pragma unroll
         for (int i = 0; i < NKI; ++i) {
-            const int m = w * NKI + i, r = m * RBk::RPB + lane / RBk::PCS;
-            const int bb = (lane % RBk::PCS) ^ RBk::swz(r);
+            const int m = w * NKI + i, r = m * RBk::RPB + lo / RBk::PCS;
+            const int bb = (lo % RBk::PCS) ^ RBk::swz(r);
             load_lds16(k + ((size_t)(b * T + t0 + min(r, L - 1)) * HK + hk) * KD + 8 * bb, (uint8_t*)(lds0 + OFF_K + m * 1024));
         }
 #pragma unroll
         for (int i = 0; i < NVI; ++i) {
-            const int m = w * NVI + i, r = m * RBv::RPB + lane / RBv::PCS;
-            const int bb = (lane % RBv::PCS) ^ RBv::swz(r);
+            const int m = w * NVI + i, r = m * RBv::RPB + lo / RBv::PCS;
+            const int bb = (lo % RBv::PCS) ^ RBv::swz(r);
             load_lds16(v + ((size_t)(b * T + t0 + min(r, L - 1)) * H + h) * V + 8 * bb, (uint8_t*)(lds0 + OFF_V + m * 1024));
         }
         if (w == 0) {
 #pragma unroll
             for (int i = 0; i < C / 64; ++i) {
-                const int t = (C / 64) * lane + i;
+                const int t = (C / 64) * lo + i;
                 rg[i] = t < L ? g[(size_t)(b * T + t0 + t) * H + h] : 0.f;
             }
         }
@@ -424,9 +430,11 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
     bf16x8 Q[NOT][KP];
     auto load_q = [&](int c) __attribute__((always_inline)) {
         const int t0 = bos + c * C, L = min(C, eos - t0);
+        int lo = lane;
+        asm volatile("" : "+v"(lo));
 #pragma unroll
         for (int i = 0; i < NOT; ++i) {
-            const bf16_t* qr = q + ((size_t)(b * T + t0 + min(16 * tile_of(i) + ln, L - 1)) * HK + hk) * KD + 8 * lg;
+            const bf16_t* qr = q + ((size_t)(b * T + t0 + min(16 * tile_of(i) + (lo & 15), L - 1)) * HK + hk) * KD + 8 * (lo >> 4);
 #pragma unroll
             for (int p = 0; p < KP; ++p) Q[i][p] = *reinterpret_cast<const bf16x8*>(qr + 32 * p);
         }
@@ -449,85 +457,100 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
     for (int c = 0; c < nch; ++c) {
         const int t0 = bos + c * C, L = min(C, eos - t0);
         if constexpr (SUMMARY) gsum += sG[3 * C];
-        // ---- output tiles: P^T fragments of own token tiles
-        bf16x8 Pf[NOT][NTT / 2];
-        float gam[NOT];
-        if constexpr (!SUMMARY) {
-#pragma unroll
-            for (int i = 0; i < NOT; ++i) {
-                const int tt = tile_of(i);
-                const float Gt = sG[16 * tt + ln];
-                gam[i] = sGam[16 * tt + ln] * scale;
-                f32x4 PT[NTT];
-#pragma unroll
-                for (int si = 0; si < NTT; ++si) {
-                    PT[si] = zero4();
-                    if (si <= tt) {
-#pragma unroll
-                        for (int p = 0; p < KP; ++p)
-                            PT[si] = mma32(*(lds_bf16x8*)(lds0 + OFF_K + RBk::off(ln, 4 * p + lg) + si * UK), Q[i][p], PT[si]);
-                        const f32x4 Gs = *(lds_f32x4*)(sG + 16 * si + 4 * lg);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            // token s = 16 si + 4 lg + r against t = 16 tt + ln: only s <= t, where G_t - G_s <= 0
-                            const bool keep = si < tt || 4 * lg + r <= ln;
-                            PT[si][r] = keep ? PT[si][r] * (scale * __expf(fminf(Gt - Gs[r], 0.f))) : 0.f;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int pp = 0; pp < NTT / 2; ++pp) Pf[i][pp] = cat8(Elem<bf16_t>::pack(PT[2 * pp]), Elem<bf16_t>::pack(PT[2 * pp + 1]));
-            }
-        }
-        // ---- own key tiles of K^T: lane (n, lg) <- K[16 u + 4 lg + r][32 p + 8 (n/4) + 4 h + n%4]
-        i16x4 Ka[KTW][NTT];
-#pragma unroll
-        for (int i = 0; i < KTW; ++i) {
-            const int kt = w * KTW + i;
-            const int ktr = RBk::off(4 * lg + (ln >> 2), 4 * (kt >> 1) + (ln & 3)) + 8 * (kt & 1);
-#pragma unroll
-            for (int u = 0; u < NTT; ++u) Ka[i][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds0 + OFF_K + ktr + u * UK));
-        }
-        const float gamL = sG[3 * C + 1];
-#pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) {
-            // V^T fragments of value tile vt: lane (n, lg) <- V[16 u + 4 lg + r][v(vt, n)]
-            const int vtr = RBv::off(4 * lg + (ln >> 2), 4 * (vt >> 1) + (ln & 3)) + 8 * (vt & 1);
-            i16x4 Vt[NTT];
-#pragma unroll
-            for (int u = 0; u < NTT; ++u) Vt[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds0 + OFF_V + vtr + u * UV));
+        // ---- compute phase, specialised per wavefront so that every tile bound is a constant
+        auto compute = [&](auto WC) __attribute__((always_inline)) {
+            constexpr int WV = decltype(WC)::value;
+            // lane-dependent LDS offsets are formed here each chunk (laundered lane index) rather than
+            // kept live across the chunk loop
+            int lo = lane;
+            asm volatile("" : "+v"(lo));
+            const int ln = lo & 15, lg = lo >> 4;
+            // ---- output tiles: P^T fragments of own token tiles
+            bf16x8 Pf[NOT][NTT / 2];
+            float gam[NOT];
             if constexpr (!SUMMARY) {
-                // bf16 entry state of value tile vt, all key columns (A operand: rows v, columns k)
-                bf16x8 Sq[KP];
-                lds_u8* sb = lds0 + OFF_SF + lane * 8 + vt * 512;
-#pragma unroll
-                for (int p = 0; p < KP; ++p)
-                    Sq[p] = cat8(*(lds_i16x4*)(sb + (2 * p) * NVT * 512), *(lds_i16x4*)(sb + (2 * p + 1) * NVT * 512));
 #pragma unroll
                 for (int i = 0; i < NOT; ++i) {
-                    const int tt = tile_of(i), t = 16 * tt + ln;
-                    f32x4 o = zero4();
+                    const int tt = i == 0 ? WV : NTT - 1 - WV;
+                    const float Gt = sG[16 * tt + ln];
+                    gam[i] = sGam[16 * tt + ln] * scale;
+                    f32x4 PT[NTT];
 #pragma unroll
-                    for (int p = 0; p < KP; ++p) o = mma32(Sq[p], Q[i][p], o);
-                    o = o * gam[i];
+                    for (int si = 0; si < NTT; ++si) {
+                        PT[si] = zero4();
+                        if (si <= tt) {
 #pragma unroll
-                    for (int pp = 0; pp < NTT / 2; ++pp)
-                        if (pp <= tt / 2) o = mma32(cat8(Vt[2 * pp], Vt[2 * pp + 1]), Pf[i][pp], o);
-                    if (t < L)
-                        *reinterpret_cast<i16x4*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + vrow(vt, 4 * lg)) = Elem<bf16_t>::pack(o);
+                            for (int p = 0; p < KP; ++p)
+                                PT[si] = mma32(*(lds_bf16x8*)(lds0 + OFF_K + RBk::off(ln, 4 * p + lg) + si * UK), Q[i][p], PT[si]);
+                            const f32x4 Gs = *(lds_f32x4*)(sG + 16 * si + 4 * lg);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                // token s = 16 si + 4 lg + r against t = 16 tt + ln: only s <= t, where G_t - G_s <= 0
+                                const bool keep = si < tt || 4 * lg + r <= ln;
+                                PT[si][r] = keep ? PT[si][r] * (scale * __expf(fminf(Gt - Gs[r], 0.f))) : 0.f;
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int pp = 0; pp < NTT / 2; ++pp) Pf[i][pp] = cat8(Elem<bf16_t>::pack(PT[2 * pp]), Elem<bf16_t>::pack(PT[2 * pp + 1]));
                 }
             }
-            // S[:, own keys] of tile vt <- Gamma_L S + (e V)^T K
-            i16x4 E[NTT];
-#pragma unroll
-            for (int u = 0; u < NTT; ++u) E[u] = Elem<bf16_t>::pack(Elem<bf16_t>::unpack(Vt[u]) * *(lds_f32x4*)(sE + 16 * u + 4 * lg));
+            // ---- own key tiles of K^T: lane (n, lg) <- K[16 u + 4 lg + r][32 p + 8 (n/4) + 4 h + n%4]
+            i16x4 Ka[KTW][NTT];
 #pragma unroll
             for (int i = 0; i < KTW; ++i) {
-                f32x4 acc = S[i][vt] * gamL;
+                const int kt = WV * KTW + i;
+                const int ktr = RBk::off(4 * lg + (ln >> 2), 4 * (kt >> 1) + (ln & 3)) + 8 * (kt & 1);
 #pragma unroll
-                for (int uu = 0; uu < NTT / 2; ++uu) acc = mma32(cat8(Ka[i][2 * uu], Ka[i][2 * uu + 1]), cat8(E[2 * uu], E[2 * uu + 1]), acc);
-                S[i][vt] = acc;
+                for (int u = 0; u < NTT; ++u) Ka[i][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds0 + OFF_K + ktr + u * UK));
             }
+            const float gamL = sG[3 * C + 1];
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) {
+                // V^T fragments of value tile vt: lane (n, lg) <- V[16 u + 4 lg + r][v(vt, n)]
+                const int vtr = RBv::off(4 * lg + (ln >> 2), 4 * (vt >> 1) + (ln & 3)) + 8 * (vt & 1);
+                i16x4 Vt[NTT];
+#pragma unroll
+                for (int u = 0; u < NTT; ++u) Vt[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds0 + OFF_V + vtr + u * UV));
+                if constexpr (!SUMMARY) {
+                    // bf16 entry state of value tile vt, all key columns (A operand: rows v, columns k)
+                    bf16x8 Sq[KP];
+                    lds_u8* sb = lds0 + OFF_SF + lane * 8 + vt * 512;
+#pragma unroll
+                    for (int p = 0; p < KP; ++p)
+                        Sq[p] = cat8(*(lds_i16x4*)(sb + (2 * p) * NVT * 512), *(lds_i16x4*)(sb + (2 * p + 1) * NVT * 512));
+#pragma unroll
+                    for (int i = 0; i < NOT; ++i) {
+                        const int tt = i == 0 ? WV : NTT - 1 - WV, t = 16 * tt + ln;
+                        f32x4 o = zero4();
+#pragma unroll
+                        for (int p = 0; p < KP; ++p) o = mma32(Sq[p], Q[i][p], o);
+                        o = o * gam[i];
+#pragma unroll
+                        for (int pp = 0; pp < NTT / 2; ++pp)
+                            if (pp <= tt / 2) o = mma32(cat8(Vt[2 * pp], Vt[2 * pp + 1]), Pf[i][pp], o);
+                        if (t < L)
+                            *reinterpret_cast<i16x4*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + vrow(vt, 4 * lg)) = Elem<bf16_t>::pack(o);
+                    }
+                }
+                // S[:, own keys] of tile vt <- Gamma_L S + (e V)^T K
+                i16x4 E[NTT];
+#pragma unroll
+                for (int u = 0; u < NTT; ++u) E[u] = Elem<bf16_t>::pack(Elem<bf16_t>::unpack(Vt[u]) * *(lds_f32x4*)(sE + 16 * u + 4 * lg));
+#pragma unroll
+                for (int i = 0; i < KTW; ++i) {
+                    f32x4 acc = S[i][vt] * gamL;
+#pragma unroll
+                    for (int uu = 0; uu < NTT / 2; ++uu) acc = mma32(cat8(Ka[i][2 * uu], Ka[i][2 * uu + 1]), cat8(E[2 * uu], E[2 * uu + 1]), acc);
+                    S[i][vt] = acc;
+                }
+            }
+        };
+        switch (w) {
+            case 0: compute(std::integral_constant<int, 0>{}); break;
+            case 1: compute(std::integral_constant<int, 1>{}); break;
+            case 2: compute(std::integral_constant<int, 2>{}); break;
+            default: compute(std::integral_constant<int, 3>{}); break;
         }
         const bool more = c + 1 < nch;
         if constexpr (!SUMMARY)
