@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
     auto load_chunk = [&](int c) __attribute__((always_inline)) {
         const int t0 = bos + c * C, L = min(C, eos - t0);
         int lo = lane;
-        asm volatile("" : "+v"(lo));
+        if constexpr (!SUMMARY) asm volatile("" : "+v"(lo));
 #pragma unroll
         for (int i = 0; i < NKI; ++i) {
             const int m = w * NKI + i, r = m * RBk::RPB + lo / RBk::PCS;
@@ -463,8 +463,11 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
             // lane-dependent LDS offsets are formed here each chunk (laundered lane index) rather than
             // kept live across the chunk loop
             int lo = lane;
-            asm volatile("" : "+v"(lo));
+            if constexpr (!SUMMARY) asm volatile("" : "+v"(lo));
             const int ln = lo & 15, lg = lo >> 4;
+            // key tiles depend on the wavefront only through kw; the summary pass has no output tiles
+            // and keeps one body with the runtime index (four copies cost more than they save there)
+            const int kw = SUMMARY ? w : WV;
             // ---- output tiles: P^T fragments of own token tiles
             bf16x8 Pf[NOT][NTT / 2];
             float gam[NOT];
@@ -499,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
             i16x4 Ka[KTW][NTT];
 #pragma unroll
             for (int i = 0; i < KTW; ++i) {
-                const int kt = WV * KTW + i;
+                const int kt = kw * KTW + i;
                 const int ktr = RBk::off(4 * lg + (ln >> 2), 4 * (kt >> 1) + (ln & 3)) + 8 * (kt & 1);
 #pragma unroll
                 for (int u = 0; u < NTT; ++u) Ka[i][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds0 + OFF_K + ktr + u * UK));
@@ -546,7 +549,8 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
                 }
             }
         };
-        switch (w) {
+        if constexpr (SUMMARY) compute(std::integral_constant<int, 0>{});
+        else switch (w) {
             case 0: compute(std::integral_constant<int, 0>{}); break;
             case 1: compute(std::integral_constant<int, 1>{}); break;
             case 2: compute(std::integral_constant<int, 2>{}); break;
