@@ -336,7 +336,6 @@ __global__ __launch_bounds__(64 * NW, NW == 2 ? 4 : 1) void gdn_prep_wave_kernel
     const int hk = h / (H / HK);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
-    const bf16x8 zero8 = {};
     int b, t0, L, ci;
     if (!chunk_coords(slot, table, cu, T, nc, b, t0, L, ci)) return;
 
@@ -349,26 +348,24 @@ __global__ __launch_bounds__(64 * NW, NW == 2 ? 4 : 1) void gdn_prep_wave_kernel
     bf16_t* gT = reinterpret_cast<bf16_t*>(rec);
     bf16_t* gP = gT + GC * GC;
     float* gC = reinterpret_cast<float*>(gP + GC * GC);
-    // K rows of the chunk (rows past its end are zero)
+    // K rows of the chunk. Rows past a partial chunk's end repeat its last token: they only reach
+    // entries that are never read or are cancelled exactly (rows of A scaled by beta = 0; columns of
+    // P and W that meet padded tokens only, whose e and T diag(beta) columns are zero)
     bf16x8 kf[4][KP];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
         const int t = 16 * R + ln;
         const bf16_t* row = k + ((size_t)(b * T + t0 + min(t, L - 1)) * HK + hk) * KD + 8 * lg;
 #pragma unroll
-        for (int p = 0; p < KP; ++p) {
-            const bf16x8 kv = *reinterpret_cast<const bf16x8*>(row + 32 * p);
-            kf[R][p] = t < L ? kv : zero8;
-        }
+        for (int p = 0; p < KP; ++p) kf[R][p] = *reinterpret_cast<const bf16x8*>(row + 32 * p);
     }
 
-    // W = K_c K_{c-1}^T (zero for a sequence's first chunk and for padded rows), as the A
-    // operand of W (e R)_{c-1}: fragment (u, p) holds, for lane (ln, lg), W[16 u + ln][32 p + 4 lg + j]
+    // W = K_c K_{c-1}^T, as the A operand of W (e R)_{c-1} (a sequence's first chunk has no
+    // predecessor: its W is formed from its own first row and never read): fragment (u, p) holds, for lane (ln, lg), W[16 u + ln][32 p + 4 lg + j]
     // then W[16 u + ln][32 p + 16 + 4 lg + j]. The C tile of K_{c-1} K_c^T (rows s, columns t) is
     // exactly that lane content, so each fragment pairs two of those tiles without any shuffle.
     // Wavefront pp forms the fragments (u, pp) from the row tiles 2 pp, 2 pp + 1 of the preceding
-    // (always full) chunk of the same sequence (a sequence's first chunk loads its own first row
-    // and discards it).
+    // (always full) chunk of the same sequence.
     auto make_w = [&](int pp) __attribute__((always_inline)) {
         bf16_t* gW = reinterpret_cast<bf16_t*>(rec + kGdnWOffset);
         bf16x8 kq[2][KP];
@@ -378,10 +375,7 @@ __global__ __launch_bounds__(64 * NW, NW == 2 ? 4 : 1) void gdn_prep_wave_kernel
             const int pt = ci > 0 ? t0 - GC + t : t0;
             const bf16_t* row = k + ((size_t)(b * T + pt) * HK + hk) * KD + 8 * lg;
 #pragma unroll
-            for (int p = 0; p < KP; ++p) {
-                const bf16x8 pv = *reinterpret_cast<const bf16x8*>(row + 32 * p);
-                kq[s2][p] = ci > 0 ? pv : zero8;
-            }
+            for (int p = 0; p < KP; ++p) kq[s2][p] = *reinterpret_cast<const bf16x8*>(row + 32 * p);
         }
 #pragma unroll
         for (int uu = 0; uu < 4; ++uu) {
@@ -418,7 +412,7 @@ __global__ __launch_bounds__(64 * NW, NW == 2 ? 4 : 1) void gdn_prep_wave_kernel
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * ti + 4 * lg + r, i = 16 * tj + ln;
-                const float d = expf(fminf(sGw[t] - sGw[i], 0.f));
+                const float d = __expf(fminf(sGw[t] - sGw[i], 0.f));
                 if (i < t) sA[col_off(i) + (t - i - 1)] = sB[t] * d * a[r];
             }
         }
@@ -505,10 +499,7 @@ __global__ __launch_bounds__(64 * NW, NW == 2 ? 4 : 1) void gdn_prep_wave_kernel
                 bf16x8 qf[KP];
                 const bf16_t* row = q + ((size_t)(b * T + t0 + min(t, L - 1)) * HK + hk) * KD + 8 * lg;
 #pragma unroll
-                for (int p = 0; p < KP; ++p) {
-                    const bf16x8 qv = *reinterpret_cast<const bf16x8*>(row + 32 * p);
-                    qf[p] = t < L ? qv : zero8;
-                }
+                for (int p = 0; p < KP; ++p) qf[p] = *reinterpret_cast<const bf16x8*>(row + 32 * p);
                 const float Gt = sGw[t];
                 f32x4 PT[4];
 #pragma unroll
@@ -520,7 +511,7 @@ __global__ __launch_bounds__(64 * NW, NW == 2 ? 4 : 1) void gdn_prep_wave_kernel
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int i = 16 * tj + 4 * lg + r;
-                            const float d = expf(fminf(Gt - sGw[i], 0.f));
+                            const float d = __expf(fminf(Gt - sGw[i], 0.f));
                             PT[tj][r] = i <= t ? scale * d * PT[tj][r] : 0.f;
                         }
                     }
