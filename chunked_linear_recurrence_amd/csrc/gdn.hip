@@ -1378,10 +1378,13 @@ __global__ __launch_bounds__(512) void gdn_chain_1w_kernel(
 //    chunk algebra states it (no look-ahead, so the key-key block of the record is not read):
 //    X = K S^T, Y = V - Gamma X, R = T diag(beta) Y, O = scale Gamma Q S^T + P R,
 //    S <- Gamma_L S + K^T (e R).
-//  - Wavefronts 8 and 9 move chunk c+1 (K and Q rows, T, P, coefficients, the eight V slices)
-//    into the other of two LDS buffers with 16-byte direct loads while chunk c computes, and
-//    touch the lines of chunk c+2 so that those loads find them in L2.
-// One workgroup barrier per chunk.
+//  - Wavefronts 8 and 9 move chunk c+1 (K and Q rows, T, coefficients, the eight V slices) into
+//    the other of two LDS buffers with 16-byte direct loads while chunk c computes, and touch the
+//    lines of chunk c+2 so that those loads find them in L2.
+//  - Wavefront 10 (output pass only) forms P_c = scale (D o Q_c K_c^T) from the K and Q rows in
+//    LDS while the slice wavefronts form X, Y and R, once for the eight slices: Pre then neither
+//    reads Q nor writes P, and the chain does not read P back.
+// One workgroup barrier per chunk (two in the output pass: P_c is complete before the outputs).
 // ---------------------------------------------------------------------------
 template <int KD, bool SUMMARY>
 struct HeadLds {
@@ -1401,7 +1404,7 @@ struct HeadLds {
 };
 
 template <int KD, bool SUMMARY>
-__global__ __launch_bounds__(640) void gdn_chain_head_kernel(
+__global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ h0, const int32_t* __restrict__ cu, const int* __restrict__ chunk_off,
     const uint8_t* __restrict__ fac, int T, int H, int HK, int V, int n_seq, int nc, int ngrp,
@@ -1513,6 +1516,7 @@ __global__ __launch_bounds__(640) void gdn_chain_head_kernel(
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) ER[ti] = El::pack(R[ti] * *(const lds_f32x4*)(cf + 64 + 16 * ti + 4 * lg));
                 if constexpr (!SUMMARY) {
+                    barrier();  // P_c complete (wavefront 10)
                     // O^T = scale Gamma (S Q^T) + R^T P^T, token tile by token tile
                     const int t0 = bos + c * GC, L = min(GC, eos - t0);
                     i16x4 Rb[4];
@@ -1547,6 +1551,8 @@ __global__ __launch_bounds__(640) void gdn_chain_head_kernel(
                     acc = mma32(cat8(Ka[2], Ka[3]), E23, acc);
                     S[kt] = acc;
                 }
+            } else {
+                if constexpr (!SUMMARY) barrier();  // the P_c barrier of the active slices
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             barrier();
@@ -1562,9 +1568,9 @@ __global__ __launch_bounds__(640) void gdn_chain_head_kernel(
                 }
             }
         }
-    } else {
+    } else if (wave < NS + 2) {
         // ================= feeders: direct loads into LDS, two wavefronts =================
-        // wavefront 8: K rows, T, coefficients, V slices 0..3; wavefront 9: Q rows, P, V slices 4..7.
+        // wavefront 8: K rows, T, coefficients, V slices 0..3; wavefront 9: Q rows, V slices 4..7.
         // Rows past the end of a partial chunk repeat its last token (finite values that the
         // stored T diag(beta) and e = 0 keep out of the state, and whose outputs are not stored).
         const int fi = wave - NS;
@@ -1608,9 +1614,7 @@ __global__ __launch_bounds__(640) void gdn_chain_head_kernel(
             } else {
                 if constexpr (!SUMMARY) {
                     feed_rows(q, c, B + SM::OFF_Q);
-#pragma unroll
-                    for (int f = 0; f < kTriFrags; ++f) load_lds16(rec + GC * GC * 2 + f * 1024, (uint8_t*)(B + SM::OFF_P + f * 1024));
-                    nl = RBk::NLOAD + kTriFrags;
+                    nl = RBk::NLOAD;
                 }
                 for (int j = NS / 2; j < vslices; ++j) {
                     feed_v(c, j);
@@ -1621,9 +1625,9 @@ __global__ __launch_bounds__(640) void gdn_chain_head_kernel(
         };
         // Cache warm-up: one 4-byte load per 128-byte line of chunk c, from the list K rows [0, 128),
         // Q rows [128, 256) (K again in summary mode), the head's V rows [256, 384) (two lines per
-        // token each), then the record's T [384, 432), P [432, 480) and coefficient [480, 488) lines;
-        // lane l of wavefront fi touches lines 4 (64 fi + l) .. + 3 (past the end: the last line).
-        constexpr int NLINES = 488;
+        // token each), then the record's T [384, 432) and coefficient [432, 440) lines; lane l of
+        // wavefront fi touches lines 4 (64 fi + l) .. + 3 (past the end: the last line).
+        constexpr int NLINES = 440;
         auto warm = [&](int c) __attribute__((always_inline)) {
             const int t0 = bos + c * GC, L = min(GC, eos - t0);
 #pragma unroll
@@ -1639,8 +1643,7 @@ __global__ __launch_bounds__(640) void gdn_chain_head_kernel(
                     a = reinterpret_cast<const uint8_t*>(v + ((size_t)(b * T + t0 + t) * H + h) * V) + (li & 1) * (V >= 128 ? 128 : 0);
                 } else {
                     const int r = li - 384;
-                    const size_t off = r < 48 ? (size_t)r * 128 : r < 96 ? (size_t)GC * GC * 2 + (r - 48) * 128
-                                                                         : (size_t)2 * GC * GC * 2 + (r - 96) * 128;
+                    const size_t off = r < 48 ? (size_t)r * 128 : (size_t)2 * GC * GC * 2 + (r - 48) * 128;
                     a = record(c) + off;
                 }
                 __builtin_amdgcn_global_load_lds(a, (__attribute__((address_space(3))) void*)(smem + SM::OFF_JUNK + fi * 256), 4, 0, 0);
@@ -1655,14 +1658,66 @@ __global__ __launch_bounds__(640) void gdn_chain_head_kernel(
         for (int c = 0; c < nch; ++c) {
             if (c + 1 < nch) {
                 issue(c + 1);
-                if (c + 2 < nch) {
-                    warm(c + 2);
+                if (c + 2 < nch) warm(c + 2);
+            }
+            if constexpr (!SUMMARY) barrier();  // the P_c barrier
+            if (c + 1 < nch) {
+                if (c + 2 < nch)
                     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-                } else {
+                else
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                }
             }
             barrier();
+        }
+    } else {
+        // ================= P_c for the output pass: one wavefront =================
+        // P^T tiles with K rows as A (rows s) and Q rows as B (columns t): the C tile holds, for lane
+        // (ln, lg), P[16 ti + ln][16 tj + 4 lg + r], which is fragment (ti, tj / 2)'s lane content
+        // (first or second half), the B operand that pairs with the R fragments of the same tokens.
+        // The cumulative gates G are the coefficient block's last quarter.
+        if constexpr (!SUMMARY) {
+            int orow[KP];
+#pragma unroll
+            for (int p = 0; p < KP; ++p) orow[p] = RBk::off(ln, 4 * p + lg);
+            barrier();
+            for (int c = 0; c < nch; ++c) {
+                lds_u8* B = buf(c);
+                const lds_f32* cf = (const lds_f32*)(B + SM::OFF_C);
+                bf16x8 kf[4][KP];
+#pragma unroll
+                for (int R = 0; R < 4; ++R)
+#pragma unroll
+                    for (int p = 0; p < KP; ++p) kf[R][p] = *(lds_bf16x8*)(B + SM::OFF_K + orow[p] + R * UST);
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    bf16x8 qf[KP];
+#pragma unroll
+                    for (int p = 0; p < KP; ++p) qf[p] = *(lds_bf16x8*)(B + SM::OFF_Q + orow[p] + ti * UST);
+                    const float Gt = cf[192 + 16 * ti + ln];
+                    f32x4 PT[4];
+#pragma unroll
+                    for (int tj = 0; tj < 4; ++tj) {
+                        PT[tj] = zero4();
+                        if (tj <= ti) {
+#pragma unroll
+                            for (int p = 0; p < KP; ++p) PT[tj] = mma32(kf[tj][p], qf[p], PT[tj]);
+                            const f32x4 Gs = *(const lds_f32x4*)(cf + 192 + 16 * tj + 4 * lg);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                // token s = 16 tj + 4 lg + r against t = 16 ti + ln: only s <= t, where G_t - G_s <= 0
+                                const bool keep = tj < ti || 4 * lg + r <= ln;
+                                PT[tj][r] = keep ? PT[tj][r] * (scale * __expf(fminf(Gt - Gs[r], 0.f))) : 0.f;
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int p = 0; p <= ti / 2; ++p)
+                        *(lds_bf16x8*)(B + SM::OFF_P + tri_frag(ti, p) * 1024 + lane * 16) = cat8(El::pack(PT[2 * p]), El::pack(PT[2 * p + 1]));
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                barrier();  // P_c complete
+                barrier();  // end of the step
+            }
         }
     }
 }
@@ -1699,8 +1754,10 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
                           const float* beta, const float* h0, const int32_t* cu,
                           const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int V,
                           float scale, ST* out, float* ht, float* Mout, hipStream_t s, int stages, int pre_w) {
-    // the key-key block W is read only by the per-slice bf16 chain kernel
+    // the key-key block W and the decay-masked query-key block P are read only by the per-slice bf16
+    // chain kernel (the per-head one forms P itself from the K and Q rows it holds)
     const int want_w = pre_w >= 0 ? pre_w : (gdn_chain_per_slice(N * H, mode == 0 ? V : V + KD) ? 1 : 0);
+    const bool want_p = mode == 0 && gdn_chain_per_slice(N * H, V);
     const bool packed = cu != nullptr;
     const long slots = gdn_slots(B, T, N, packed);
     const int nc = (T + GC - 1) / GC;
@@ -1712,20 +1769,19 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
     if (slots > 0 && (stages & 1)) {
         timing_begin("gdn_prep", s);
         if constexpr (sizeof(ST) == 2) {
-            // the decay-masked query-key block P only feeds the output. When every unit fits on the
-            // GPU at once (8 two-wavefront workgroups per CU), the chunk's latency is the launch's
-            // and two wavefronts per chunk halve it; otherwise one wavefront per chunk spends fewer
-            // instructions per chunk.
+            // When every unit fits on the GPU at once (8 two-wavefront workgroups per CU), the
+            // chunk's latency is the launch's and two wavefronts per chunk halve it; otherwise one
+            // wavefront per chunk spends fewer instructions per chunk.
             const unsigned gx = prep_grid(H, slots);
             const int2* tab = packed ? ws.table : nullptr;
             const bool two = (long)H * slots <= 8L * device_cus();
             if (two) {
-                if (mode == 0)
+                if (want_p)
                     gdn_prep_wave_kernel<KD, true, 2><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
                 else
                     gdn_prep_wave_kernel<KD, false, 2><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
             } else {
-                if (mode == 0)
+                if (want_p)
                     gdn_prep_wave_kernel<KD, true, 1><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
                 else
                     gdn_prep_wave_kernel<KD, false, 1><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
@@ -1750,7 +1806,7 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
             const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * ngrp);
             if (mode == 0) {
                 timing_begin("gdn_chain", s);
-                gdn_chain_head_kernel<KD, false><<<grid, 640, 0, s>>>(
+                gdn_chain_head_kernel<KD, false><<<grid, 704, 0, s>>>(
                     q, k, v, h0, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, ngrp, scale, out, ht, nullptr);
             } else {
                 timing_begin("gdn_summary_chain", s);
