@@ -286,8 +286,10 @@ __device__ __forceinline__ void store_tri_frags(const bf16_t* m, int ld, bf16_t*
         }
 }
 
-// Pre work units (head, slot) in runs of this many consecutive slots of one head per XCD:
-// neighbouring chunks read each other's key rows (W), which then come from that XCD's L2
+// Pre work units u = slot * H + head (heads fastest) in runs of this many units per XCD. The gates
+// and beta are [token][head] rows of H floats, so the heads of a chunk read the same lines: in one
+// run they come from that XCD's L2 once (a run of one head's chunks would fetch every line on every
+// XCD). Neighbouring chunks of a head (the key rows W reads) mostly share a run too.
 constexpr int kPrepXcdRun = 64;
 inline unsigned prep_grid(int H, long n_slots) {
     const long units = (long)H * n_slots;
@@ -327,12 +329,12 @@ __global__ __launch_bounds__(64 * NW, NW == 2 ? 4 : 1) void gdn_prep_wave_kernel
     // wavefront-local order of LDS traffic: later LDS reads see the lanes' earlier writes
     auto wave_sync = [] __attribute__((always_inline)) () { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
 
-    // blockIdx -> unit u = h * n_slots + slot, in runs of kPrepXcdRun units per XCD (workgroups go
+    // blockIdx -> unit u = slot * H + h, in runs of kPrepXcdRun units per XCD (workgroups go
     // round-robin over the 8 XCDs)
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int u = (idx / kPrepXcdRun) * (8 * kPrepXcdRun) + xcd * kPrepXcdRun + idx % kPrepXcdRun;
     if (u >= H * n_slots) return;
-    const int h = u / n_slots, slot = u % n_slots;
+    const int slot = u / H, h = u % H;
     const int hk = h / (H / HK);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
