@@ -10,7 +10,8 @@
 // Delta rule: one workgroup per (batch row, head, 16 state rows). The 16 x K
 // slice of the running state lives in LDS in float32; each step is a
 // [16 x K] @ [K x K] float32 MFMA product (v_mfma_f32_16x16x4_f32), the
-// four wavefronts splitting the output columns.
+// four wavefronts splitting the output columns. A step's M and S_ext
+// fragments are loaded during the step before.
 // Scalar gate: elementwise, one thread per four state elements.
 #include "sf_device.h"
 #include "sf_internal.h"
@@ -25,6 +26,7 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(const float* __restrict__
                                                        float* __restrict__ S_final) {
     constexpr int LD = KD + 4;
     constexpr int NTW = KD / 16 / 4;  // output column tiles per wavefront
+    constexpr int KBN = KD / 16;      // 16-row blocks of M
     __shared__ __align__(16) float sS[16 * LD];
     const int nvs = V / 16;
     const int vs = blockIdx.x % nvs, h = (blockIdx.x / nvs) % H, b = blockIdx.x / (nvs * H);
@@ -32,32 +34,52 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(const float* __restrict__
     const int r0 = vs * 16;
     const size_t VK = (size_t)V * KD;
 
+    // Operands of step j (this wavefront's column tiles): the B fragments of M_j and the S_ext_j
+    // tile that starts the accumulator. They do not depend on the running state, so step j+1's are
+    // loaded while step j's products run.
+    typedef f32x4 StepM[NTW][KBN];
+    typedef f32x4 StepE[NTW];
+    auto load_step = [&](int j, StepM& bm, StepE& e) __attribute__((always_inline)) {
+        const size_t sh = ((size_t)(b * n_seg + j) * H + h);
+        const float* Mj = M + sh * KD * KD;
+        const float* Ej = E + sh * VK;
+#pragma unroll
+        for (int w = 0; w < NTW; ++w) {
+            const int n0 = (wave * NTW + w) * 16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e[w][r] = Ej[(size_t)(r0 + 4 * lg + r) * KD + n0 + ln];
+#pragma unroll
+            for (int kb = 0; kb < KBN; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bm[w][kb][r] = Mj[(size_t)(16 * kb + 4 * lg + r) * KD + n0 + ln];
+        }
+    };
+
     for (int i = tid; i < 16 * KD; i += 256) {
         const int r = i / KD, c = i % KD;
         sS[r * LD + c] = h0 ? h0[((size_t)b * H + h) * VK + (size_t)(r0 + r) * KD + c] : 0.f;
     }
+    StepM bm;
+    StepE e;
+    if (n_seg > 0) load_step(0, bm, e);
     for (int j = 0; j < n_seg; ++j) {
+        StepM bmn;
+        StepE en;
+        if (j + 1 < n_seg) load_step(j + 1, bmn, en);
         const size_t sh = ((size_t)(b * n_seg + j) * H + h);
         __syncthreads();
         for (int i = tid; i < 16 * KD; i += 256) {
             const int r = i / KD, c = i % KD;
             S_in[sh * VK + (size_t)(r0 + r) * KD + c] = sS[r * LD + c];
         }
-        const float* Mj = M + sh * KD * KD;
-        const float* Ej = E + sh * VK;
         f32x4 acc[NTW];
 #pragma unroll
         for (int w = 0; w < NTW; ++w) {
-            const int n0 = (wave * NTW + w) * 16;
+            acc[w] = e[w];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[w][r] = Ej[(size_t)(r0 + 4 * lg + r) * KD + n0 + ln];
-#pragma unroll 4
-            for (int kb = 0; kb < KD / 16; ++kb) {
+            for (int kb = 0; kb < KBN; ++kb) {
                 const f32x4 a = *reinterpret_cast<const f32x4*>(&sS[ln * LD + 16 * kb + 4 * lg]);
-                f32x4 bm;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) bm[r] = Mj[(size_t)(16 * kb + 4 * lg + r) * KD + n0 + ln];
-                acc[w] = Elem<float>::mma(acc[w], a, bm);
+                acc[w] = Elem<float>::mma(acc[w], a, bm[w][kb]);
             }
         }
         __syncthreads();
@@ -66,6 +88,14 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(const float* __restrict__
             const int n0 = (wave * NTW + w) * 16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) sS[(4 * lg + r) * LD + n0 + ln] = acc[w][r];
+        }
+        if (j + 1 < n_seg) {
+#pragma unroll
+            for (int w = 0; w < NTW; ++w) {
+                e[w] = en[w];
+#pragma unroll
+                for (int kb = 0; kb < KBN; ++kb) bm[w][kb] = bmn[w][kb];
+            }
         }
     }
     __syncthreads();
