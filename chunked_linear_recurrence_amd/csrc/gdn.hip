@@ -1372,14 +1372,16 @@ __global__ __launch_bounds__(512) void gdn_chain_1w_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// ST + Out, bf16, one workgroup per (sequence, head) and group of eight 16-row slices, for
-// launches with many more slices than CUs. There every CU runs slice after slice, and what
-// bounds a step is how many bytes each CU must pull from L2 per chunk: the per-slice kernel
-// above loads the chunk's K, Q and factor record once per slice, this one once per eight.
-//  - Wavefronts 0..7 each run one slice's whole chunk step with its state in registers, as the
-//    chunk algebra states it (no look-ahead, so the key-key block of the record is not read):
-//    X = K S^T, Y = V - Gamma X, R = T diag(beta) Y, O = scale Gamma Q S^T + P R,
-//    S <- Gamma_L S + K^T (e R).
+// ST + Out, bf16, one workgroup per (sequence, head) and group of 16-row slices (the output pass's
+// 8 value slices; the summary pass's 16, value and transition rows), for launches with many more
+// slices than CUs. There every CU runs slice after slice, and what bounds a step is how many
+// bytes each CU must pull from L2 per chunk: the per-slice kernel above loads the chunk's K, Q and
+// factor record once per slice, this one once per group.
+//  - Wavefronts 0..7 each run SPW slices' whole chunk step (one in the output pass, two in the
+//    summary pass) with the states in registers, as the chunk algebra states it (no look-ahead, so
+//    the key-key block of the record is not read): X = K S^T, Y = V - Gamma X,
+//    R = T diag(beta) Y, O = scale Gamma Q S^T + P R, S <- Gamma_L S + K^T (e R). Each fragment of
+//    the shared operands read from LDS feeds the wavefront's SPW slices.
 //  - Wavefronts 8 and 9 move chunk c+1 (K and Q rows, T, coefficients, the eight V slices) into
 //    the other of two LDS buffers with 16-byte direct loads while chunk c computes, and touch the
 //    lines of chunk c+2 so that those loads find them in L2.
@@ -1392,14 +1394,17 @@ template <int KD, bool SUMMARY>
 struct HeadLds {
     typedef RowBlock<KD> RBk;
     static constexpr int KP = KD / 32, KB = KD / 16;
-    static constexpr int NS = 8;                                       // slices per workgroup
+    static constexpr int SPW = SUMMARY ? 2 : 1;                        // slices per slice wavefront
+    static constexpr int NCW = 8;                                      // slice wavefronts
+    static constexpr int NS = NCW * SPW;                               // slices per workgroup
+    static constexpr int NVS = 8;                                      // V slices held (V <= 128)
     static constexpr int OFF_K = 0;                                    // K rows (RowBlock)
     static constexpr int OFF_Q = OFF_K + RBk::BYTES;                   // Q rows (RowBlock)
     static constexpr int OFF_T = OFF_Q + (SUMMARY ? 0 : RBk::BYTES);   // kTriFrags fragments of 1 KB
     static constexpr int OFF_P = OFF_T + kTriFrags * 1024;             // kTriFrags fragments of 1 KB
     static constexpr int OFF_C = OFF_P + (SUMMARY ? 0 : kTriFrags * 1024);  // coefficients float[256]
-    static constexpr int OFF_V = OFF_C + 256 * 4;                      // [NS][64][16] bf16 V slices
-    static constexpr int BUF = OFF_V + NS * GC * 16 * 2;
+    static constexpr int OFF_V = OFF_C + 256 * 4;                      // [NVS][64][16] bf16 V slices
+    static constexpr int BUF = OFF_V + NVS * GC * 16 * 2;
     static constexpr int OFF_JUNK = 2 * BUF;                           // sink of cache warm-up loads
     static constexpr int BYTES = OFF_JUNK + 128 * 4;
     static_assert(BYTES <= 160 * 1024, "LDS plan exceeds the CU's 160 KB");
@@ -1414,7 +1419,7 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
     typedef HeadLds<KD, SUMMARY> SM;
     typedef RowBlock<KD> RBk;
     typedef Elem<bf16_t> El;
-    constexpr int KP = SM::KP, KB = SM::KB, NS = SM::NS;
+    constexpr int KP = SM::KP, KB = SM::KB, NS = SM::NS, SPW = SM::SPW, NCW = SM::NCW;
     constexpr int UST = (16 / RBk::RPB) * 1024;  // byte step of one 16-row token tile in a row block
 
     __shared__ __align__(16) uint8_t smem[SM::BYTES];
@@ -1453,105 +1458,151 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
     };
     auto barrier = [] __attribute__((always_inline)) () { asm volatile("s_barrier" ::: "memory"); };
 
-    if (wave < NS) {
-        // ================= one slice: the state recurrence and the output =================
-        const int vb = grp * NS + wave, row0 = 16 * vb;
+    if (wave < NCW) {
+        // ================= SPW slices: the state recurrence and the output =================
+        // rows is a multiple of 16 SPW, so the wavefront's slices are all active or all not, and all
+        // value rows or all transition rows
+        const int row0 = 16 * (grp * NS + SPW * wave);
         const bool active = row0 < rows;
-        const bool vrows = row0 < V;                       // value rows (else transition rows, summary only)
+        const bool vrows = row0 < V;  // value rows (else transition rows, summary only)
         const uint32_t vmask = vrows ? 0xffffffffu : 0u;
-        f32x4 S[KB];
+        f32x4 S[SPW][KB];
 #pragma unroll
-        for (int kt = 0; kt < KB; ++kt) {
-            const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
-            if constexpr (!SUMMARY) {
-                S[kt] = (active && h0) ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + row) * KD + kk) : zero4();
-            } else {
+        for (int sl = 0; sl < SPW; ++sl)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[kt][r] = (!vrows && kk + r == row - V) ? 1.f : 0.f;
+            for (int kt = 0; kt < KB; ++kt) {
+                const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + 16 * sl + ln;
+                if constexpr (!SUMMARY) {
+                    S[sl][kt] = (active && h0) ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + row) * KD + kk) : zero4();
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[sl][kt][r] = (!vrows && kk + r == row - V) ? 1.f : 0.f;
+                }
             }
-        }
         int orow[KP], otr[KP];
 #pragma unroll
         for (int p = 0; p < KP; ++p) {
             orow[p] = RBk::off(ln, 4 * p + lg);                             // row fragment (0, p)
             otr[p] = RBk::off(4 * lg + (ln >> 2), 4 * p + (ln & 3));        // transposed read, column pair p
         }
-        const int off_v = SM::OFF_V + (wave * GC * 16 + (4 * lg + (ln >> 2)) * 16 + 4 * (ln & 3)) * 2;
+        // V slice (row0 / 16 + sl) read transposed; transition rows read slice 0 and mask it
+        const int off_v = SM::OFF_V + ((vrows ? row0 - 16 * grp * NS : 0) * GC + (4 * lg + (ln >> 2)) * 16 + 4 * (ln & 3)) * 2;
         barrier();
         for (int c = 0; c < nch; ++c) {
             if (active) {
                 lds_u8* B = buf(c);
+                lds_u8* KR = B + SM::OFF_K;
                 const lds_f32* cf = (const lds_f32*)(B + SM::OFF_C);
-                // bf16 entry state: B operand of X and A operand of the output
-                i16x4 Sf[KB];
+                // bf16 entry states: B operands of X and A operands of the output
+                i16x4 Sf[SPW][KB];
 #pragma unroll
-                for (int kt = 0; kt < KB; ++kt) Sf[kt] = El::pack(S[kt]);
+                for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+                    for (int kt = 0; kt < KB; ++kt) Sf[sl][kt] = El::pack(S[sl][kt]);
                 // X = K S^T
-                f32x4 X[4];
+                f32x4 X[SPW][4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    X[u] = zero4();
 #pragma unroll
-                    for (int p = 0; p < KP; ++p) X[u] = mma32(*(lds_bf16x8*)(B + SM::OFF_K + orow[p] + u * UST), cat8(Sf[2 * p], Sf[2 * p + 1]), X[u]);
+                    for (int sl = 0; sl < SPW; ++sl) X[sl][u] = zero4();
+#pragma unroll
+                    for (int p = 0; p < KP; ++p) {
+                        const bf16x8 kr = *(lds_bf16x8*)(KR + orow[p] + u * UST);
+#pragma unroll
+                        for (int sl = 0; sl < SPW; ++sl) X[sl][u] = mma32(kr, cat8(Sf[sl][2 * p], Sf[sl][2 * p + 1]), X[sl][u]);
+                    }
                 }
-                // Y = V - Gamma X (beta is folded into the stored T)
-                i16x4 Yf[4];
+                // Y = V - Gamma X (beta is folded into T)
+                i16x4 Yf[SPW][4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const i16x4 vx = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(B + off_v + 16 * u * 16 * 2));
-                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                    const i16x4 Vf = __builtin_bit_cast(i16x4, __builtin_bit_cast(u32x2, vx) & vmask);
                     const f32x4 gam = *(const lds_f32x4*)(cf + 16 * u + 4 * lg);
-                    Yf[u] = El::pack(El::unpack(Vf) - gam * X[u]);
+#pragma unroll
+                    for (int sl = 0; sl < SPW; ++sl) {
+                        const i16x4 vx = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(B + off_v + sl * GC * 16 * 2 + 16 * u * 16 * 2));
+                        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                        const i16x4 Vf = __builtin_bit_cast(i16x4, __builtin_bit_cast(u32x2, vx) & vmask);
+                        Yf[sl][u] = El::pack(El::unpack(Vf) - gam * X[sl][u]);
+                    }
                 }
                 // R = T diag(beta) Y (T lower triangular, fragment pairs of 32 columns)
                 bf16x8 Tf[kTriFrags];
 #pragma unroll
                 for (int f = 0; f < kTriFrags; ++f) Tf[f] = *(lds_bf16x8*)(B + SM::OFF_T + f * 1024 + lane * 16);
-                f32x4 R[4];
-                const bf16x8 Y01 = cat8(Yf[0], Yf[1]), Y23 = cat8(Yf[2], Yf[3]);
-                R[0] = mma32(Tf[tri_frag(0, 0)], Y01, zero4());
-                R[1] = mma32(Tf[tri_frag(1, 0)], Y01, zero4());
-                R[2] = mma32(Tf[tri_frag(2, 1)], Y23, mma32(Tf[tri_frag(2, 0)], Y01, zero4()));
-                R[3] = mma32(Tf[tri_frag(3, 1)], Y23, mma32(Tf[tri_frag(3, 0)], Y01, zero4()));
-                i16x4 ER[4];
+                f32x4 R[SPW][4];
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) ER[ti] = El::pack(R[ti] * *(const lds_f32x4*)(cf + 64 + 16 * ti + 4 * lg));
+                for (int sl = 0; sl < SPW; ++sl) {
+                    const bf16x8 Y01 = cat8(Yf[sl][0], Yf[sl][1]), Y23 = cat8(Yf[sl][2], Yf[sl][3]);
+                    R[sl][0] = mma32(Tf[tri_frag(0, 0)], Y01, zero4());
+                    R[sl][1] = mma32(Tf[tri_frag(1, 0)], Y01, zero4());
+                    R[sl][2] = mma32(Tf[tri_frag(2, 1)], Y23, mma32(Tf[tri_frag(2, 0)], Y01, zero4()));
+                    R[sl][3] = mma32(Tf[tri_frag(3, 1)], Y23, mma32(Tf[tri_frag(3, 0)], Y01, zero4()));
+                }
+                i16x4 ER[SPW][4];
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti) {
+                    const f32x4 ec = *(const lds_f32x4*)(cf + 64 + 16 * ti + 4 * lg);
+#pragma unroll
+                    for (int sl = 0; sl < SPW; ++sl) ER[sl][ti] = El::pack(R[sl][ti] * ec);
+                }
                 if constexpr (!SUMMARY) {
                     barrier();  // P_c complete (wavefront 10)
                     // O^T = scale Gamma (S Q^T) + R^T P^T, token tile by token tile
                     const int t0 = bos + c * GC, L = min(GC, eos - t0);
-                    i16x4 Rb[4];
+                    i16x4 Rb[SPW][4];
 #pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) Rb[ti] = El::pack(R[ti]);
+                    for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+                        for (int ti = 0; ti < 4; ++ti) Rb[sl][ti] = El::pack(R[sl][ti]);
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) {
-                        f32x4 o = zero4();
+                        f32x4 o[SPW];
 #pragma unroll
-                        for (int p = 0; p < KP; ++p)
-                            o = mma32(cat8(Sf[2 * p], Sf[2 * p + 1]), *(lds_bf16x8*)(B + SM::OFF_Q + orow[p] + tt * UST), o);
-                        o = o * (cf[16 * tt + ln] * scale);
+                        for (int sl = 0; sl < SPW; ++sl) o[sl] = zero4();
 #pragma unroll
-                        for (int pp = 0; pp <= tt / 2; ++pp)
-                            o = mma32(cat8(Rb[2 * pp], Rb[2 * pp + 1]), *(lds_bf16x8*)(B + SM::OFF_P + tri_frag(tt, pp) * 1024 + lane * 16), o);
+                        for (int p = 0; p < KP; ++p) {
+                            const bf16x8 qf = *(lds_bf16x8*)(B + SM::OFF_Q + orow[p] + tt * UST);
+#pragma unroll
+                            for (int sl = 0; sl < SPW; ++sl) o[sl] = mma32(cat8(Sf[sl][2 * p], Sf[sl][2 * p + 1]), qf, o[sl]);
+                        }
+                        const float gq = cf[16 * tt + ln] * scale;
+#pragma unroll
+                        for (int pp = 0; pp <= tt / 2; ++pp) {
+                            const bf16x8 pf = *(lds_bf16x8*)(B + SM::OFF_P + tri_frag(tt, pp) * 1024 + lane * 16);
+#pragma unroll
+                            for (int sl = 0; sl < SPW; ++sl) o[sl] = mma32(cat8(Rb[sl][2 * pp], Rb[sl][2 * pp + 1]), pf, pp == 0 ? o[sl] * gq : o[sl]);
+                        }
                         const int t = 16 * tt + ln;
-                        if (t < L) *reinterpret_cast<i16x4*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + 4 * lg) = El::pack(o);
+                        if (t < L) {
+#pragma unroll
+                            for (int sl = 0; sl < SPW; ++sl)
+                                *reinterpret_cast<i16x4*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + 16 * sl + 4 * lg) = El::pack(o[sl]);
+                        }
                     }
                 }
                 // S^T <- Gamma_L S^T + K^T (e R)
                 const float gl = cf[63];
-                const bf16x8 E01 = cat8(ER[0], ER[1]), E23 = cat8(ER[2], ER[3]);
+                bf16x8 E01[SPW], E23[SPW];
+#pragma unroll
+                for (int sl = 0; sl < SPW; ++sl) {
+                    E01[sl] = cat8(ER[sl][0], ER[sl][1]);
+                    E23[sl] = cat8(ER[sl][2], ER[sl][3]);
+                }
 #pragma unroll
                 for (int kt = 0; kt < KB; ++kt) {
                     const int p = kt >> 1, hh = kt & 1;
                     i16x4 Ka[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        Ka[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(B + SM::OFF_K + otr[p] + 8 * hh + u * UST));
-                    f32x4 acc = S[kt] * gl;
-                    acc = mma32(cat8(Ka[0], Ka[1]), E01, acc);
-                    acc = mma32(cat8(Ka[2], Ka[3]), E23, acc);
-                    S[kt] = acc;
+                        Ka[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(KR + otr[p] + 8 * hh + u * UST));
+                    const bf16x8 K01 = cat8(Ka[0], Ka[1]), K23 = cat8(Ka[2], Ka[3]);
+#pragma unroll
+                    for (int sl = 0; sl < SPW; ++sl) {
+                        f32x4 acc = S[sl][kt] * gl;
+                        acc = mma32(K01, E01[sl], acc);
+                        acc = mma32(K23, E23[sl], acc);
+                        S[sl][kt] = acc;
+                    }
                 }
             } else {
                 if constexpr (!SUMMARY) barrier();  // the P_c barrier of the active slices
@@ -1561,21 +1612,23 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
         }
         if (active) {
 #pragma unroll
-            for (int kt = 0; kt < KB; ++kt) {
-                const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
-                if (vrows) {
-                    if (ht) *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + row) * KD + kk) = S[kt];
-                } else if constexpr (SUMMARY) {
-                    *reinterpret_cast<f32x4*>(Mout + (((size_t)n * H + h) * KD + (row - V)) * KD + kk) = S[kt];
+            for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+                for (int kt = 0; kt < KB; ++kt) {
+                    const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + 16 * sl + ln;
+                    if (vrows) {
+                        if (ht) *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + row) * KD + kk) = S[sl][kt];
+                    } else if constexpr (SUMMARY) {
+                        *reinterpret_cast<f32x4*>(Mout + (((size_t)n * H + h) * KD + (row - V)) * KD + kk) = S[sl][kt];
+                    }
                 }
-            }
         }
-    } else if (wave < NS + 2) {
+    } else if (wave < NCW + 2) {
         // ================= feeders: direct loads into LDS, two wavefronts =================
         // wavefront 8: K rows, T, coefficients, V slices 0..3; wavefront 9: Q rows, V slices 4..7.
         // Rows past the end of a partial chunk repeat its last token (finite values that the
         // stored T diag(beta) and e = 0 keep out of the state, and whose outputs are not stored).
-        const int fi = wave - NS;
+        const int fi = wave - NCW;
         const size_t krs = (size_t)HK * KD * 2, vrs = (size_t)H * V * 2;  // token strides (bytes)
         auto feed_rows = [&](const bf16_t* src, int c, lds_u8* dst) __attribute__((always_inline)) {
             const int t0 = bos + c * GC, L = min(GC, eos - t0);
@@ -1598,7 +1651,7 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
             }
         };
         // the V slices this group holds (summary transition rows have none)
-        const int vslices = max(0, min(NS, V / 16 - grp * NS));
+        const int vslices = max(0, min(SM::NVS, V / 16 - grp * NS));
         auto issue = [&](int c) __attribute__((always_inline)) {  // returns load instructions issued
             lds_u8* B = buf(c);
             const uint8_t* rec = record(c) + lane * 16;
@@ -1609,7 +1662,7 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
                 for (int f = 0; f < kTriFrags; ++f) load_lds16(rec + f * 1024, (uint8_t*)(B + SM::OFF_T + f * 1024));
                 load_lds16(rec + 2 * GC * GC * 2, (uint8_t*)(B + SM::OFF_C));
                 nl = RBk::NLOAD + kTriFrags + 1;
-                for (int j = 0; j < min(vslices, NS / 2); ++j) {
+                for (int j = 0; j < min(vslices, SM::NVS / 2); ++j) {
                     feed_v(c, j);
                     nl += 2;
                 }
@@ -1618,7 +1671,7 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
                     feed_rows(q, c, B + SM::OFF_Q);
                     nl = RBk::NLOAD;
                 }
-                for (int j = NS / 2; j < vslices; ++j) {
+                for (int j = SM::NVS / 2; j < vslices; ++j) {
                     feed_v(c, j);
                     nl += 2;
                 }
@@ -1804,7 +1857,9 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
         // more 16-row slices than two per CU: the CUs run slice after slice, and one workgroup per
         // eight slices loads each chunk's shared operands once for them
         if (!gdn_chain_per_slice(chains, rows)) {
-            const int ngrp = (nvb + HeadLds<KD, false>::NS - 1) / HeadLds<KD, false>::NS;
+            // slices per workgroup: the output pass's 8, the summary pass's 16 (all of a head's V + K rows)
+            const int ns = mode == 0 ? HeadLds<KD, false>::NS : HeadLds<KD, true>::NS;
+            const int ngrp = (nvb + ns - 1) / ns;
             const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * ngrp);
             if (mode == 0) {
                 timing_begin("gdn_chain", s);
