@@ -115,8 +115,9 @@ def test_gdn_bf16_reduced(dev, oracle, T, D, shift):
 
 
 # Launches with more 16-row slices than two per CU (256 CUs on MI355X) take the per-head chain
-# kernel (one workgroup per eight slices of a head); these cases reach it at small sizes, with a
-# ragged last chunk, h0, grouped heads and summary mode.
+# kernel (one workgroup per head: its 8 value slices, or in summary mode all its value and
+# transition slices); these cases reach it at small sizes, with a ragged last chunk, h0, grouped
+# heads and summary mode at both key sizes.
 @pytest.mark.parametrize("D,H,HK", [(128, 40, 40), (64, 72, 72), (128, 40, 10)])
 def test_gdn_bf16_many_heads(dev, oracle, D, H, HK):
     say(f"case: GDN bf16 B=2 T=200 H={H} HK={HK} K=V={D} (more slices than two per CU) h0 N(0,0.02)")
@@ -128,9 +129,10 @@ def test_gdn_bf16_many_heads(dev, oracle, D, H, HK):
     check_bf16("many heads", f32(o), ro, f32(ht), rh)
 
 
-def test_gdn_summary_many_rows(dev, oracle):
-    say("case: GDN bf16 summary, 8 rows x H=8 K=V=128 (more slices than two per CU), rows with tails")
-    d = wl.delta_rule_inputs(B=8, T=200, H=8, K=128, V=128, dtype=torch.bfloat16, seed=77, gate_shift=-5.0,
+@pytest.mark.parametrize("D,H", [(128, 8), (64, 24)])
+def test_gdn_summary_many_rows(dev, oracle, D, H):
+    say(f"case: GDN bf16 summary, 8 rows x H={H} K=V={D} (more slices than two per CU), rows with tails")
+    d = wl.delta_rule_inputs(B=8, T=200, H=H, K=D, V=D, dtype=torch.bfloat16, seed=77 + D, gate_shift=-5.0,
                              beta_scale=0.3)
     M, E = sf.segment_summary("gdn", cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev), cuda(d["beta"], dev))
     rM, rE = oracle.gdn_summary(f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(d["beta"]))
