@@ -142,6 +142,32 @@ def test_gdn_summary_many_rows(dev, oracle, D, H):
     assert eM <= BF16_RTOL and eE <= BF16_RTOL
 
 
+# Degenerate gates in both bf16 chain kernels (4 heads: one workgroup per 16-row slice; 40 heads:
+# one per head): beta = 0 leaves the initial state's pure decay (weak gates, so that it stays
+# representable in float32); g = 0 with beta = 1 overwrites along each unit key without decay;
+# g = -60 per token underflows every decay factor past the diagonal, and the carried state, to zero
+# in float32.
+@pytest.mark.parametrize("case", ["beta0", "nodecay", "strongdecay"])
+@pytest.mark.parametrize("H", [4, 40])
+def test_gdn_bf16_degenerate_gates(dev, oracle, case, H):
+    say(f"case: GDN bf16 B=2 T=200 H={H} K=V=128 h0 N(0,0.02), {case}")
+    d = wl.delta_rule_inputs(B=2, T=200, H=H, K=128, V=128, dtype=torch.bfloat16, seed=300 + H,
+                             gate_shift=-5.0, h0_std=0.02)
+    if case == "beta0":
+        d["beta"] = torch.zeros_like(d["beta"])
+    elif case == "nodecay":
+        d["g"] = torch.zeros_like(d["g"])
+        d["beta"] = torch.ones_like(d["beta"])
+    else:
+        d["g"] = torch.full_like(d["g"], -60.0)
+    o, ht = sf.gdn_chunk_fwd(cuda(d["q"], dev), cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev),
+                             cuda(d["beta"], dev), cuda(d["h0"], dev), output_final_state=True)
+    o, ht = f32(o), f32(ht)
+    assert np.isfinite(o).all() and np.isfinite(ht).all()
+    ro, rh = oracle.gdn_forward(f32(d["q"]), f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(d["beta"]), f32(d["h0"]))
+    check_bf16(case, o, ro, ht, rh)
+
+
 def test_dense_gdn_full_size(dev, oracle):
     say("case: dense GDN prefill B=2 T=4096 H=16 K=V=128 bf16 (full size, heads 0, 7, 15 vs oracle)")
     w = wl.dense_gdn()
@@ -403,6 +429,22 @@ def test_gla_vs_oracle(dev, oracle, dtype, chunk, T, HK):
         assert eo <= FP32_ATOL * so and eh <= FP32_ATOL * sh
     else:
         check_bf16("gla", f32(o), ro, f32(ht), rh)
+
+
+# Degenerate scalar gates: g = 0 is causal linear attention (no decay, the state grows), g = -60
+# per token underflows every decay past the diagonal and the carried state.
+@pytest.mark.parametrize("case", ["nodecay", "strongdecay"])
+def test_gla_bf16_degenerate_gates(dev, oracle, case):
+    say(f"case: GLA bf16 chunk 128 T=300 H=4 HK=2 K=128 V=64 with h0, {case}")
+    d = wl.scalar_gate_inputs(B=2, T=300, H=4, HK=2, K=128, V=64, dtype=torch.bfloat16, seed=31)
+    d["g"] = torch.zeros_like(d["g"]) if case == "nodecay" else torch.full_like(d["g"], -60.0)
+    h0 = (torch.randn(2, 4, 64, 128, generator=torch.Generator().manual_seed(31))).float()
+    o, ht = sf.gla_chunk_fwd(cuda(d["q"], dev), cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev),
+                             cuda(h0, dev), chunk=128, scale=0.05, output_final_state=True)
+    o, ht = f32(o), f32(ht)
+    assert np.isfinite(o).all() and np.isfinite(ht).all()
+    ro, rh = oracle.gla_forward(f32(d["q"]), f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(h0), scale=0.05)
+    check_bf16(case, o, ro, ht, rh)
 
 
 def test_ssd_gla_full_size_segmented(dev, oracle):
