@@ -507,6 +507,15 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
 #pragma unroll
                 for (int u = 0; u < NTT; ++u) Ka[i][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds0 + OFF_K + ktr + u * UK));
             }
+            // the update's factor e_t scales token t's key row here, once per chunk (the wavefront's
+            // own key tiles only), rather than its value row in every value tile: sum_t (e_t k_t) v_t^T
+            // is the same sum, and the output keeps the unscaled V
+#pragma unroll
+            for (int u = 0; u < NTT; ++u) {
+                const f32x4 eu = *(lds_f32x4*)(sE + 16 * u + 4 * lg);
+#pragma unroll
+                for (int i = 0; i < KTW; ++i) Ka[i][u] = Elem<bf16_t>::pack(Elem<bf16_t>::unpack(Ka[i][u]) * eu);
+            }
             const float gamL = sG[3 * C + 1];
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) {
@@ -536,15 +545,12 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
                             *reinterpret_cast<i16x4*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + vrow(vt, 4 * lg)) = Elem<bf16_t>::pack(o);
                     }
                 }
-                // S[:, own keys] of tile vt <- Gamma_L S + (e V)^T K
-                i16x4 E[NTT];
-#pragma unroll
-                for (int u = 0; u < NTT; ++u) E[u] = Elem<bf16_t>::pack(Elem<bf16_t>::unpack(Vt[u]) * *(lds_f32x4*)(sE + 16 * u + 4 * lg));
+                // S[:, own keys] of tile vt <- Gamma_L S + V^T (e K)
 #pragma unroll
                 for (int i = 0; i < KTW; ++i) {
                     f32x4 acc = S[i][vt] * gamL;
 #pragma unroll
-                    for (int uu = 0; uu < NTT / 2; ++uu) acc = mma32(cat8(Ka[i][2 * uu], Ka[i][2 * uu + 1]), cat8(E[2 * uu], E[2 * uu + 1]), acc);
+                    for (int uu = 0; uu < NTT / 2; ++uu) acc = mma32(cat8(Ka[i][2 * uu], Ka[i][2 * uu + 1]), cat8(Vt[2 * uu], Vt[2 * uu + 1]), acc);
                     S[i][vt] = acc;
                 }
             }
