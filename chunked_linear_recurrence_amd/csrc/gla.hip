@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
     constexpr int OFF_K = 0;
     constexpr int OFF_V = OFF_K + C * RBk::RB;
     constexpr int OFF_SF = OFF_V + C * RBv::RB;          // [KB][NVT][64 lanes] x 8 B bf16 state
-    constexpr int OFF_G = OFF_SF + KB * NVT * 512;       // G[C], Gamma[C], e[C], then G_L, Gamma_L
+    constexpr int OFF_G = OFF_SF + KB * NVT * 512;       // G[C] (log2 units), Gamma[C], e[C], then G_L, Gamma_L
     constexpr int BYTES = OFF_G + 3 * C * 4 + 16;
     constexpr int NKI = C * RBk::RB / 1024 / 4, NVI = C * RBv::RB / 1024 / 4;  // direct loads per wavefront
     static_assert(NKI * 4 * 1024 == C * RBk::RB && NVI * 4 * 1024 == C * RBv::RB, "loads must divide evenly");
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
         for (int i = 0; i < PER; ++i) {
             const int t = PER * lane + i;
             const float G = base + x[i];
-            sG[t] = G;
+            sG[t] = G * 1.4426950408889634f;  // log2 units: the decay masks use the hardware exp2
             sGam[t] = __expf(G);
             sE[t] = t < L ? __expf(GL - G) : 0.f;
         }
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(256, 2) void gla_bf16_kernel(
                             for (int r = 0; r < 4; ++r) {
                                 // token s = 16 si + 4 lg + r against t = 16 tt + ln: only s <= t, where G_t - G_s <= 0
                                 const bool keep = si < tt || 4 * lg + r <= ln;
-                                PT[si][r] = keep ? PT[si][r] * (scale * __expf(fminf(Gt - Gs[r], 0.f))) : 0.f;
+                                PT[si][r] = keep ? PT[si][r] * (scale * __builtin_amdgcn_exp2f(fminf(Gt - Gs[r], 0.f))) : 0.f;
                             }
                         }
                     }
