@@ -1800,8 +1800,8 @@ int device_cus() {
 }
 
 // The bf16 chain runs one workgroup per 16-row state slice (gdn_chain_1w_kernel) unless the launch
-// has more than two slices per CU; then one workgroup per eight slices of a head
-// (gdn_chain_head_kernel), which loads each chunk's shared operands once for them.
+// has more than two slices per CU; then one workgroup per head (gdn_chain_head_kernel), which
+// loads each chunk's shared operands once for all the head's slices.
 bool gdn_chain_per_slice(long chains, int rows) { return chains * (rows / 16) <= 2L * device_cus(); }
 
 template <typename ST, int KD>
@@ -1855,7 +1855,7 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
     if constexpr (sizeof(ST) == 2) {
         const int nvb = rows / 16;
         // more 16-row slices than two per CU: the CUs run slice after slice, and one workgroup per
-        // eight slices loads each chunk's shared operands once for them
+        // head loads each chunk's shared operands once for all its slices
         if (!gdn_chain_per_slice(chains, rows)) {
             // slices per workgroup: the output pass's 8, the summary pass's 16 (all of a head's V + K rows)
             const int ns = mode == 0 ? HeadLds<KD, false>::NS : HeadLds<KD, true>::NS;
