@@ -84,10 +84,13 @@ const char *sf_last_error(void);
  * when cu_seqlens is passed; then B must be 1). The workspace holds the
  * per-chunk factors of the chunk decomposition (StateFlow Section 2.2,
  * Eq. (2), "Pre"): the unit-lower-triangular WY/UT solve factor, the
- * decay-masked query-key block and the per-token decay coefficients (for
- * bf16 also the key-key block of each chunk with its predecessor, which
- * lets the chain overlap consecutive chunk steps), plus the device chunk
- * table of packed inputs. Returns 0 for invalid sizes.
+ * per-token decay coefficients and the decay-masked query-key block, plus
+ * for bf16 the key-key block of each chunk with its predecessor, which lets
+ * the chain overlap consecutive chunk steps (for bf16 launches with more
+ * 16-row state slices than the GPU runs at once, the chain forms the
+ * query-key block itself and does without the key-key block, so those two
+ * parts are left unwritten), and the device chunk table of packed inputs.
+ * The size does not depend on that choice. Returns 0 for invalid sizes.
  */
 size_t sf_gdn_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N,
                                   int packed);
