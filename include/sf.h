@@ -87,7 +87,7 @@ const char *sf_last_error(void);
  * per-token decay coefficients and the decay-masked query-key block, plus
  * for bf16 the key-key block of each chunk with its predecessor, which lets
  * the chain overlap consecutive chunk steps (for bf16 launches with more
- * 16-row state slices than the GPU runs at once, the chain forms the
+ * than two 16-row state slices per compute unit, the chain forms the
  * query-key block itself and does without the key-key block, so those two
  * parts are left unwritten), and the device chunk table of packed inputs.
  * The size does not depend on that choice. Returns 0 for invalid sizes.
