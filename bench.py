@@ -152,7 +152,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (one GPU's share of the "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (one GPU's share of the "
               "work is what it runs); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -8,8 +8,8 @@ with torch (round to nearest even); both sides then receive exactly the same
 values (the oracle widens them to float64 exactly).
 
 The five named workloads follow the statement of the problem (shapes, value
-distributions, chunk sizes, segment counts); the readings taken where the
-statement is open are listed in the design doc:
+distributions, chunk sizes, segment counts), with the readings taken where it
+is open noted in the workload functions below:
 
 1. ``tiny_gdn``       B=1 T=256 H=2 K=V=64, float32, chunk 64.
 2. ``dense_gdn``      B=2 T=4096 H=16 K=V=128, bf16, initial state N(0, 0.02).
