@@ -166,12 +166,15 @@ def cu_from_lengths(lens):
 
 
 def tiny_gdn(seed=SEEDS["tiny_gdn"]):
+    """float32 delta rule; scale 1/sqrt(64) = 1/8, zero initial state."""
     d = delta_rule_inputs(B=1, T=256, H=2, K=64, V=64, dtype=torch.float32, seed=seed)
     return Workload("tiny_gdn", "gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], None, None,
                     scale=1.0 / 8.0, chunk=64)
 
 
 def dense_gdn(seed=SEEDS["dense_gdn"], *, B=2, T=4096, H=16, D=128):
+    """bf16 delta rule; g = -softplus(N(0,1) + 2); initial state N(0, 0.02) read as standard deviation
+    0.02; scale 1/sqrt(D)."""
     d = delta_rule_inputs(B=B, T=T, H=H, K=D, V=D, dtype=torch.bfloat16, seed=seed,
                           gate_shift=2.0, h0_std=0.02)
     return Workload("dense_gdn", "gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], None,
@@ -179,6 +182,9 @@ def dense_gdn(seed=SEEDS["dense_gdn"], *, B=2, T=4096, H=16, D=128):
 
 
 def varlen_gdn(seed=SEEDS["varlen_gdn"], *, T=32768, H=32, D=128, n_long=7):
+    """bf16 delta rule on one packed stream; lengths from varlen_lengths (one short length, the others
+    from random cuts with at least three not multiples of 64, one empty sequence inserted); gates and
+    distributions as dense_gdn; zero initial states."""
     d = delta_rule_inputs(B=1, T=T, H=H, K=D, V=D, dtype=torch.bfloat16, seed=seed, gate_shift=2.0)
     lens = varlen_lengths(d["rng"], T, n_long=n_long)
     return Workload("varlen_gdn", "gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], None,
@@ -187,12 +193,16 @@ def varlen_gdn(seed=SEEDS["varlen_gdn"], *, T=32768, H=32, D=128, n_long=7):
 
 
 def long_gdn(seed=SEEDS["long_gdn"], *, T=262144, H=16, D=128, n_seg=16):
+    """bf16 delta rule on one long row cut into n_seg segments; g = -softplus(N(0,1) + 4) as the
+    formula gives it (its decay is fast, whatever the label says); zero initial state; scale 1/sqrt(D)."""
     d = delta_rule_inputs(B=1, T=T, H=H, K=D, V=D, dtype=torch.bfloat16, seed=seed, gate_shift=4.0)
     return Workload("long_gdn", "gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], None, None,
                     scale=1.0 / np.sqrt(D), chunk=64, n_seg=n_seg)
 
 
 def ssd_gla(seed=SEEDS["ssd_gla"], *, B=2, T=16384, H=64, HK=8, K=128, V=64, n_seg=8):
+    """bf16 scalar-gated recurrence; A = -softplus(N(0,1)) once per head, dt = softplus(N(0,1)) per
+    token, g = A dt; q, k, v ~ N(0,1) unnormalised and v used as given; zero initial state; scale 1."""
     d = scalar_gate_inputs(B=B, T=T, H=H, HK=HK, K=K, V=V, seed=seed)
     return Workload("ssd_gla", "gla", d["q"], d["k"], d["v"], d["g"], None, None, None,
                     scale=1.0, chunk=128, n_seg=n_seg, meta={"A": d["A"]})
