@@ -15,7 +15,9 @@ events recorded on the launch stream around every launch, in a second timed
 pass over the same steps; the events add gaps between launches, so that pass's
 step time is reported apart as events_pass_ms_per_step) and the float64 oracle
 timed on the host cores on the same workload (cpu_baseline; a reported
-baseline, not a target).
+baseline, not a target). Beside the published HBM peak, the roofline objects
+carry measured_peak: the bandwidth a plain 1 GiB device-to-device copy reaches
+on the same GPU (read plus write bytes), and the fraction of that.
 
 Other workloads (--workload varlen_gdn | long_gdn | ssd_gla | tiny_gdn) are for
 measurement only; the headline line is the default one.
@@ -135,6 +137,26 @@ def cpu_baseline(w):
                       f"{dt:.2f} s wall"}
 
 
+def measured_copy_gbs(dev, nbytes=1 << 30, reps=10):
+    """HBM bandwidth a plain device-to-device copy reaches here (bytes read plus bytes written per
+    second), for a buffer far larger than the caches: the practical ceiling next to the spec peak.
+    Timed with events on torch's current stream, which is where the copy runs."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    return round(gbs, 1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +168,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the second pass, whose launches are bracketed with HIP events")
+    ap.add_argument("--no-copy-peak", action="store_true",
+                    help="skip the measured-copy bandwidth reported beside the spec peak")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 512 MiB device-to-device copy three times (reference dispatches "
                          "that scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes)")
@@ -215,6 +239,10 @@ def main():
                 "kernel": dom, "avg_us": round(avg_s * 1e6, 2), "algorithmic_bytes": ab}
     path_bytes = algorithmic_bytes(w, "path")
     path_ach = path_bytes / (elapsed / args.steps) / 1e9
+    copy_gbs = None if args.no_copy_peak else measured_copy_gbs(dev)
+    if roof is not None and copy_gbs:
+        roof["measured_peak"] = copy_gbs
+        roof["frac_of_measured"] = round(roof["achieved"] / copy_gbs, 4)
 
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -224,7 +252,9 @@ def main():
                    "chunk": w.chunk, "n_seg": w.n_seg, "tokens": w.tokens, "rotate": len(sets)},
         "roofline": roof,
         "path_roofline": {"bound": "hbm", "achieved": round(path_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(path_ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": path_bytes},
+                          "frac": round(path_ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": path_bytes,
+                          "measured_peak": copy_gbs,
+                          "frac_of_measured": None if not copy_gbs else round(path_ach / copy_gbs, 4)},
         "kernels": kernels,
         "events_pass_ms_per_step": None if ev_elapsed is None else 1e3 * ev_elapsed / args.steps,
         "cpu_baseline": None,
