@@ -243,13 +243,16 @@ def test_varlen_chunk_table_is_exact(dev):
     assert (tab_dev[len(table):, 0] == -1).all()
 
 
-def test_packed_equals_alone_bitwise(dev):
-    say("case: packed sequences equal separate dense calls bitwise; rows past the end untouched")
+# Both launches of a comparison take the same bf16 chain kernel: with 4 heads the per-slice one,
+# with 72 heads (576 slices even for one sequence, more than two per CU) the per-head one.
+@pytest.mark.parametrize("H", [4, 72])
+def test_packed_equals_alone_bitwise(dev, H):
+    say(f"case: packed sequences equal separate dense calls bitwise, H={H} K=V=128")
     lens = [130, 0, 64, 7, 300]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu[-1]) + 20
-    d = wl.delta_rule_inputs(B=1, T=T, H=4, K=128, V=128, dtype=torch.bfloat16, seed=21, gate_shift=-1.0)
-    h0 = torch.randn(len(lens), 4, 128, 128, generator=torch.Generator().manual_seed(1)) * 0.1
+    d = wl.delta_rule_inputs(B=1, T=T, H=H, K=128, V=128, dtype=torch.bfloat16, seed=21, gate_shift=-1.0)
+    h0 = torch.randn(len(lens), H, 128, 128, generator=torch.Generator().manual_seed(1)) * 0.1
     q, k, v, g, beta = (cuda(d[x], dev) for x in ("q", "k", "v", "g", "beta"))
     h0d = cuda(h0, dev)
     o, ht = sf.gdn_chunk_fwd(q, k, v, g, beta, h0d, cu_seqlens=torch.from_numpy(cu).to(dev),
