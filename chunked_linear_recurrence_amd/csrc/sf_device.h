@@ -96,19 +96,6 @@ __device__ __forceinline__ typename Elem<ST>::frag frag_rows(const ST* m, int ld
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// A fragment of the transpose of a row-major LDS matrix X (16-bit elements):
-// the block X^T[c0.., r0..] as A operand, i.e. lane (n, g) receives
-// X[r0 + 4g + q][c0 + n] for q = 0..3. Uses the gfx950 transposing LDS read:
-// within each 16-lane group, lane i points at 4 consecutive elements M[i][0..3]
-// and lane j receives M[4q + j/4][j%4] (q = 0..3), so lane 4q + r of group g
-// points at X[r0 + 4g + q][c0 + 4r].
-__device__ __forceinline__ i16x4 frag_rows_t(const void* m, int ld, int r0, int c0) {
-    const int ln = lane_id() & 15, lg = lane_id() >> 4;
-    const short* p = reinterpret_cast<const short*>(m) + (r0 + 4 * lg + (ln >> 2)) * ld + c0 + 4 * (ln & 3);
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-}
-
 // 16-byte vector unit used for staging copies. A native vector type (not
 // HIP's uint4 struct, whose copies become stack memcpys) so that staging
 // values stay in registers.
