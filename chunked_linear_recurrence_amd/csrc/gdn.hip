@@ -830,10 +830,12 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
 //  C tile of each product is the operand of the next as it stands
 //  (sf_device.h).
 //  - Wavefronts 3 and 7 form the output, two token tiles each: in step c they
-//    build P_c^T = scale (D o K_c Q_c^T)^T from K and Q in LDS and keep it,
-//    with their Q_c fragments, in registers; in step c+1 they emit
+//    read their Q_c and P_c fragments (P from the Pre stage) from LDS into
+//    registers; in step c+1 they form
 //    O_c^T = scale diag(Gamma) (S_c Q_c^T) + R_c^T P_c^T from the bf16 state
-//    and residual fragments the chain leaves in LDS (8-byte row stores).
+//    and residual fragments the chain leaves in LDS, and store it (8-byte row
+//    pieces) at the start of step c+2: stores issued mid-step, while the
+//    feeders' loads are in flight, stretch the step more.
 //  - Wavefronts 4, 5 and 6 feed everyone with 16-byte direct loads into LDS
 //    (no register staging; one wavefront alone issues them too slowly): in
 //    step c they move K of chunk c+2, Q, T, W, V and coefficients of chunk
@@ -1326,7 +1328,17 @@ __global__ __launch_bounds__(512) void gdn_chain_1w_kernel(
                         if (p <= tt / 2) F.Pf[i][p] = *(lds_bf16x8*)(pb + tri_frag(tt, p) * 1024);
                 }
             };
-            auto emit = [&](int c, const OutRegs& E) __attribute__((always_inline)) {  // O of chunk c
+            // O pieces formed in one step and stored at the start of the next
+            i16x4 pend_o[2];
+            bf16_t* pend_at[2];
+            bool pend[2] = {false, false};
+            auto flush = [&]() __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    if (pend[i]) *reinterpret_cast<i16x4*>(pend_at[i]) = pend_o[i];
+            };
+            // O of chunk c: stored now (last chunk) or left pending
+            auto emit = [&](int c, const OutRegs& E, bool now) __attribute__((always_inline)) {
                 const int t0 = bos + c * GC, L = min(GC, eos - t0);
                 lds_u8* sb = opaque(lds0 + SM::OFF_SF + (c & 1) * KB * 512 + lane * 8);
                 lds_u8* rb = opaque(lds0 + SM::OFF_RB + (c & 1) * 4 * 512 + lane * 8);
@@ -1346,16 +1358,22 @@ __global__ __launch_bounds__(512) void gdn_chain_1w_kernel(
                     for (int p = 0; p < 2; ++p)
                         if (p <= tt / 2) o = mma32(cat8(Rb[2 * p], Rb[2 * p + 1]), E.Pf[i][p], o);
                     const int t = 16 * tt + ln;
-                    if (t < L) {
-                        const i16x4 ob = El::pack(o);
-                        *reinterpret_cast<i16x4*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + 4 * lg) = ob;
+                    bf16_t* at = out + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + 4 * lg;
+                    if (now) {
+                        if (t < L) *reinterpret_cast<i16x4*>(at) = El::pack(o);
+                    } else {
+                        pend_o[i] = El::pack(o);
+                        pend_at[i] = at;
+                        pend[i] = t < L;
                     }
                 }
             };
-            // step c: build chunk c's operands into F (K_c, Q_c resident now), emit chunk c-1 from E
+            // step c: store chunk c-2, read chunk c's operands into F (Q_c, P_c resident now),
+            // form chunk c-1 from E
             auto step = [&](int c, OutRegs& F, const OutRegs& E) __attribute__((always_inline)) {
+                flush();
                 build(c, F);
-                if (c > 0) emit(c - 1, E);
+                if (c > 0) emit(c - 1, E, false);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 barrier();
             };
@@ -1364,7 +1382,8 @@ __global__ __launch_bounds__(512) void gdn_chain_1w_kernel(
                 step(c, RA, RB);
                 if (c + 1 < nch) step(c + 1, RB, RA);
             }
-            if (nch > 0) emit(nch - 1, (nch - 1) & 1 ? RB : RA);
+            flush();
+            if (nch > 0) emit(nch - 1, (nch - 1) & 1 ? RB : RA, true);
         } else {
             for (int c = 0; c < nch; ++c) barrier();
         }
