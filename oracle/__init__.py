@@ -21,6 +21,8 @@ What each function follows (pages by title and section):
 * ``state_scan``    the exclusive causal scan of the same page.
 * ``chunked_forward``  StateFlow Section 2.2 Eq. (2) chunk split, used only to
   check that the chunk algebra reproduces the token recurrence.
+* ``gdn_decode``    attention-gym "Linear Attention", the ``recurrent_gdn_decode``
+  entry and the section "Gate Transforms" (``decode.py``, numpy float64).
 
 Pins: tests/test_oracle.py checks every function against closed forms,
 brute-force products or invariants that do not reuse this code.
@@ -188,3 +190,6 @@ def chunked_forward(kind, q, k, v, g, beta=None, h0=None, cu_seqlens=None, scale
                                 _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu), N, B, T,
                                 H, HK, K, V, float(scale), _ptr(out), _ptr(ht), int(threads))
     return out, ht
+
+
+from .decode import gdn_decode  # noqa: E402  (numpy float64, no C part)

@@ -1,0 +1,88 @@
+"""One-token paged delta-rule decode, float64 (test infrastructure; same rules as the rest of
+``oracle/``: only tests, the smoke check and the bench's CPU baseline may use it).
+
+Follows attention-gym "Linear Attention": the API entry of ``recurrent_gdn_decode`` (the
+packed post-convolution [Q | K | V] row per token, grouped q/k heads, the paged state pool
+advanced in place through slot indices, null slots, the fresh-slot mask) and the section
+"Gate Transforms" (the softplus convention for the decay). The recurrence step is the token
+rule of the section "Gated Delta Rule".
+
+Readings where the pages leave a step open:
+* L2 normalisation is x / sqrt(sum x^2 + eps) with eps = 1e-6 (the pages give no epsilon;
+  some guard is needed for a zero row, and this one moves a unit-scale row by about 1e-6).
+* raw gate and raw beta come in the same element type as the packed row.
+* slot index 0 and negative indices are null rows: zero output, pool untouched.
+
+Everything runs in float64 on the values as given (bf16 inputs arrive already rounded).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+L2_EPS = 1e-6
+
+
+def softplus(x):
+    """log(1 + exp(x)) without overflow."""
+    return np.logaddexp(0.0, x)
+
+
+def decay_gate(raw_gate, A_log, dt_bias):
+    """Natural-log decay of the softplus convention: -exp(A_log) * softplus(raw + dt_bias)."""
+    return -np.exp(A_log) * softplus(raw_gate + dt_bias)
+
+
+def write_gate(raw_beta):
+    """Logistic sigmoid."""
+    return 1.0 / (1.0 + np.exp(-raw_beta))
+
+
+def l2_normalise(x, eps=L2_EPS):
+    return x / np.sqrt(np.dot(x, x) + eps)
+
+
+def gdn_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_pool, state_indices,
+               has_initial_state=None, *, H, HK, K, V, scale=None):
+    """One decode step for B sequences.
+
+    packed_qkv [B, 2*HK*K + H*V]: per token the query heads, then the key heads, then the
+    value heads, each head's row contiguous. raw_gate, raw_beta [B, H] (or [1, B, H]);
+    A_log, dt_bias [H]; state_pool [num_slots, H, V, K]; state_indices [B] int;
+    has_initial_state [B] bool or None (all True).
+
+    Returns (out [B, H, V], pool [num_slots, H, V, K]), both float64; ``pool`` is a copy of
+    ``state_pool`` with the selected slots advanced.
+    """
+    x = np.asarray(packed_qkv, dtype=np.float64)
+    B = x.shape[0]
+    assert x.shape[1] == 2 * HK * K + H * V and H % HK == 0
+    rg = np.asarray(raw_gate, dtype=np.float64).reshape(B, H)
+    rb = np.asarray(raw_beta, dtype=np.float64).reshape(B, H)
+    A_log = np.asarray(A_log, dtype=np.float64)
+    dt_bias = np.asarray(dt_bias, dtype=np.float64)
+    pool = np.array(state_pool, dtype=np.float64, copy=True)
+    idx = np.asarray(state_indices).astype(np.int64)
+    init = np.ones(B, dtype=bool) if has_initial_state is None else np.asarray(has_initial_state, dtype=bool)
+    if scale is None:
+        scale = 1.0 / np.sqrt(K)
+    out = np.zeros((B, H, V), dtype=np.float64)
+    group = H // HK
+    for b in range(B):
+        slot = int(idx[b])
+        if slot <= 0:
+            continue
+        for h in range(H):
+            hk = h // group
+            q = l2_normalise(x[b, hk * K:(hk + 1) * K])
+            k = l2_normalise(x[b, HK * K + hk * K:HK * K + (hk + 1) * K])
+            v = x[b, 2 * HK * K + h * V:2 * HK * K + (h + 1) * V]
+            g = decay_gate(rg[b, h], A_log[h], dt_bias[h])
+            beta = write_gate(rb[b, h])
+            S = pool[slot, h].copy() if init[b] else np.zeros((V, K))
+            # token rule: decay, delta correction against the decayed state, then read with q
+            S = np.exp(g) * S
+            r = beta * (v - S @ k)
+            S = S + np.outer(r, k)
+            out[b, h] = scale * (S @ q)
+            pool[slot, h] = S
+    return out, pool

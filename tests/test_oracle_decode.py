@@ -1,0 +1,153 @@
+"""Pins of the float64 decode oracle (oracle/decode.py) against facts that do not reuse its code.
+
+Each check would fail for a plausible slip in it: the decay with the wrong sign or without
+exp(A_log), softplus or sigmoid swapped, a missing L2 normalisation, the residual taken against
+the undecayed state, the output read before the update, the wrong q/k head for a value head,
+sections of the packed row in the wrong order, a null slot written, a fresh slot read.
+
+* closed forms of the gate transforms (attention-gym "Linear Attention", "Gate Transforms"):
+  softplus(0) = ln 2, so A_log = ln 3 with a zero pre-activation decays by exactly 2^-3;
+  sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4;
+* single steps with a closed-form result: pure decay (beta -> 0) and a write into a fresh slot
+  with q = k along one axis;
+* invariance of the output under positive rescaling of q and k (the normalisation);
+* T decode steps against the token-by-token float64 recurrence of oracle.c, which has pins of
+  its own (tests/test_oracle.py), with grouped heads and a permuted set of slots.
+"""
+import math
+
+import numpy as np
+
+import oracle
+from oracle import decode as dec
+
+H, HK, K, V = 4, 2, 8, 6
+
+
+def packed(q, k, v):
+    """[B, HK, K], [B, HK, K], [B, H, V] -> [B, 2 HK K + H V]."""
+    B = q.shape[0]
+    return np.concatenate([q.reshape(B, -1), k.reshape(B, -1), v.reshape(B, -1)], axis=1)
+
+
+def test_gate_transform_closed_forms():
+    assert math.isclose(dec.decay_gate(0.0, 0.0, 0.0), -math.log(2.0), rel_tol=1e-15)
+    assert math.isclose(dec.decay_gate(0.0, math.log(3.0), 0.0), -3 * math.log(2.0), rel_tol=1e-15)
+    # the bias adds to the raw projection before softplus: softplus(ln 3 - ln 3 + 0) = ln 2
+    assert math.isclose(dec.decay_gate(math.log(3.0), 0.0, -math.log(3.0)), -math.log(2.0), rel_tol=1e-15)
+    # softplus(ln(e - 1)) = 1
+    assert math.isclose(dec.softplus(math.log(math.e - 1.0)), 1.0, rel_tol=1e-15)
+    assert math.isclose(dec.softplus(60.0), 60.0, rel_tol=1e-15)
+    assert dec.softplus(-60.0) > 0.0
+    assert dec.write_gate(0.0) == 0.5
+    assert math.isclose(dec.write_gate(math.log(3.0)), 0.75, rel_tol=1e-15)
+
+
+def _single(rng, B=2):
+    q = rng.standard_normal((B, HK, K))
+    k = rng.standard_normal((B, HK, K))
+    v = rng.standard_normal((B, H, V))
+    return q, k, v
+
+
+def test_pure_decay_step():
+    """beta -> 0: the state decays by exp(g) = 1/8 and the output reads the decayed state."""
+    rng = np.random.default_rng(1)
+    B, j = 2, 3
+    q = np.zeros((B, HK, K))
+    q[..., j] = 5.0                       # q-hat = e_j up to the normalisation guard
+    _, k, v = _single(rng, B)
+    pool = rng.standard_normal((4, H, V, K))
+    idx = np.array([3, 1])
+    out, new = oracle.gdn_decode(packed(q, k, v), np.zeros((B, H)), np.full((B, H), -80.0),
+                                 np.full(H, math.log(3.0)), np.zeros(H), pool, idx,
+                                 H=H, HK=HK, K=K, V=V, scale=0.5)
+    shrink = 5.0 / math.sqrt(25.0 + dec.L2_EPS)
+    for b in range(B):
+        np.testing.assert_allclose(new[idx[b]], pool[idx[b]] / 8.0, rtol=1e-12, atol=1e-30)
+        np.testing.assert_allclose(out[b], 0.5 * shrink * pool[idx[b]][:, :, j] / 8.0, rtol=1e-12)
+    # untouched slots stay bit-identical
+    for s in (0, 2):
+        assert np.array_equal(new[s], pool[s])
+
+
+def test_fresh_slot_write():
+    """Fresh slot (garbage ignored), beta = 1/2, q = k = c e_j: S = v k-hat^T / 2, o = scale v/2 (k-hat.q-hat)."""
+    rng = np.random.default_rng(2)
+    B, j = 1, 5
+    q = np.zeros((B, HK, K))
+    q[..., j] = 3.0
+    k = q.copy()
+    v = rng.standard_normal((B, H, V))
+    pool = np.full((2, H, V, K), np.nan)
+    out, new = oracle.gdn_decode(packed(q, k, v), rng.standard_normal((B, H)), np.zeros((B, H)),
+                                 rng.standard_normal(H), rng.standard_normal(H), pool, np.array([1]),
+                                 np.array([False]), H=H, HK=HK, K=K, V=V, scale=0.25)
+    c = 3.0 / math.sqrt(9.0 + dec.L2_EPS)
+    expect_S = np.zeros((H, V, K))
+    expect_S[:, :, j] = 0.5 * v[0] * c
+    np.testing.assert_allclose(new[1], expect_S, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(out[0], 0.25 * 0.5 * v[0] * c * c, rtol=1e-14)
+    assert np.all(np.isnan(new[0]))
+
+
+def test_null_slots():
+    rng = np.random.default_rng(3)
+    B = 3
+    q, k, v = _single(rng, B)
+    pool = rng.standard_normal((3, H, V, K))
+    pool[0] = np.nan
+    out, new = oracle.gdn_decode(packed(q, k, v), rng.standard_normal((B, H)), rng.standard_normal((B, H)),
+                                 rng.standard_normal(H), rng.standard_normal(H), pool,
+                                 np.array([0, -4, 2]), H=H, HK=HK, K=K, V=V)
+    assert np.all(out[0] == 0) and np.all(out[1] == 0)
+    assert np.all(np.isnan(new[0])) and np.array_equal(new[1], pool[1])
+    assert not np.array_equal(new[2], pool[2])
+
+
+def test_rescaled_q_k_leave_the_output():
+    rng = np.random.default_rng(4)
+    B = 2
+    q, k, v = _single(rng, B)
+    args = (rng.standard_normal((B, H)), rng.standard_normal((B, H)), rng.standard_normal(H),
+            rng.standard_normal(H), rng.standard_normal((3, H, V, K)), np.array([2, 1]))
+    o1, p1 = oracle.gdn_decode(packed(q, k, v), *args, H=H, HK=HK, K=K, V=V)
+    o2, p2 = oracle.gdn_decode(packed(7.0 * q, 0.5 * k, v), *args, H=H, HK=HK, K=K, V=V)
+    # the guard eps = 1e-6 in the norm moves a row of squared norm n by about eps / (2 n)
+    np.testing.assert_allclose(o2, o1, rtol=1e-5, atol=2e-6)
+    np.testing.assert_allclose(p2, p1, rtol=1e-5, atol=2e-6)
+    # an unnormalised variant would differ by the scale factors themselves
+    assert np.abs(o2 - o1).max() < 1e-3 * np.abs(o1).max()
+
+
+def test_steps_match_token_recurrence():
+    """T decode steps on slots [2, 5, 1] equal oracle.gdn_forward run on the normalised q, k and the
+    transformed gates, started from the same slots."""
+    rng = np.random.default_rng(5)
+    B, T = 3, 6
+    q = rng.standard_normal((B, T, HK, K))
+    k = rng.standard_normal((B, T, HK, K))
+    v = rng.standard_normal((B, T, H, V))
+    rg = rng.standard_normal((B, T, H))
+    rb = rng.standard_normal((B, T, H))
+    A_log = rng.standard_normal(H) * 0.5
+    dt_bias = rng.standard_normal(H) * 0.5
+    pool = rng.standard_normal((6, H, V, K)) * 0.3
+    idx = np.array([2, 5, 1])
+    cur = pool
+    outs = []
+    for t in range(T):
+        o, cur = oracle.gdn_decode(packed(q[:, t], k[:, t], v[:, t]), rg[:, t], rb[:, t], A_log, dt_bias,
+                                   cur, idx, H=H, HK=HK, K=K, V=V, scale=0.3)
+        outs.append(o)
+    outs = np.stack(outs, axis=1)
+    qn = q / np.sqrt((q * q).sum(-1, keepdims=True) + dec.L2_EPS)
+    kn = k / np.sqrt((k * k).sum(-1, keepdims=True) + dec.L2_EPS)
+    g = -np.exp(A_log) * np.logaddexp(0.0, rg + dt_bias)
+    beta = 1.0 / (1.0 + np.exp(-rb))
+    ref_o, ref_ht = oracle.gdn_forward(qn, kn, v, g, beta, h0=pool[idx], scale=0.3)
+    # oracle.gdn_forward takes float32 inputs: the comparison is at float32 input rounding
+    np.testing.assert_allclose(outs, ref_o, rtol=2e-5, atol=2e-6)
+    np.testing.assert_allclose(cur[idx], ref_ht, rtol=2e-5, atol=2e-6)
+    for s in (0, 3, 4):
+        assert np.array_equal(cur[s], pool[s])
