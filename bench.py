@@ -19,8 +19,10 @@ baseline, not a target). Beside the published HBM peak, the roofline objects
 carry measured_peak: the bandwidth a plain 1 GiB device-to-device copy reaches
 on the same GPU (read plus write bytes), and the fraction of that.
 
-Other workloads (--workload varlen_gdn | long_gdn | ssd_gla | tiny_gdn) are for
-measurement only; the headline line is the default one.
+Other workloads (--workload varlen_gdn | long_gdn | ssd_gla | tiny_gdn | decode_gdn) are for
+measurement only; the headline line is the default one. decode_gdn times one sf_gdn_decode call
+(one token for each of 256 sequences against a 514 MB float32 state pool, which is larger than
+the last-level cache, so it runs on one input set).
 """
 from __future__ import annotations
 
@@ -43,6 +45,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def decode_bytes(w):
+    """One decode step: every active row reads (unless fresh) and writes its H states of V*K pool
+    elements, reads its packed row and its 2 H raw gates, writes H*V outputs; A_log and dt_bias."""
+    import torch
+    eb = w.packed_qkv.element_size()
+    pe = w.pool.element_size()
+    active = w.state_indices > 0
+    loaded = active if w.has_initial_state is None else active & w.has_initial_state
+    states = (int(active.sum()) + int(loaded.sum())) * w.H * w.V * w.K * pe
+    rows = w.B * (w.packed_qkv.shape[1] + 2 * w.H) * eb + w.B * w.H * w.V * eb
+    return states + rows + 2 * w.H * 4 + w.B * 4
+
+
 def algorithmic_bytes(w, kernel):
     """Bytes a kernel must move by definition of the computation (no intermediates).
 
@@ -50,6 +65,8 @@ def algorithmic_bytes(w, kernel):
     (HK/H of q and k per value head), plus gate and beta in float32; per
     (sequence, head): the initial state read (when given) and the final state
     written, V*K float32 each."""
+    if kernel in ("gdn_decode", "decode_path"):
+        return decode_bytes(w)
     eb = w.q.element_size()
     tok = w.tokens
     qk = 2 * tok * w.HK * w.K * eb
@@ -86,6 +103,13 @@ def traffic_from_profile(kernel, workload):
 
 def make_sets(w, dev, rotate):
     import torch
+    import workloads as wl
+    if isinstance(w, wl.DecodeWorkload):
+        s = {n: (None if getattr(w, n) is None else getattr(w, n).to(dev).contiguous())
+             for n in ("packed_qkv", "raw_gate", "raw_beta", "A_log", "dt_bias", "pool", "state_indices",
+                       "has_initial_state")}
+        s["out"] = torch.empty((1, w.B, w.H, w.V), dtype=w.packed_qkv.dtype, device=dev)
+        return [s]
     sets = []
     for r in range(rotate):
         s = {}
@@ -98,7 +122,12 @@ def make_sets(w, dev, rotate):
 
 def step_fn(w):
     import chunked_linear_recurrence_amd as sf
-    if w.name in ("dense_gdn", "tiny_gdn", "varlen_gdn"):
+    if w.name == "decode_gdn":
+        def step(s):
+            return sf.gdn_decode(s["packed_qkv"], s["raw_gate"], s["raw_beta"], s["A_log"], s["dt_bias"], s["pool"],
+                                 s["state_indices"], has_initial_state=s["has_initial_state"], scale=w.scale,
+                                 out=s["out"])
+    elif w.name in ("dense_gdn", "tiny_gdn", "varlen_gdn"):
         def step(s):
             return sf.gdn_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["h0"], cu_seqlens=s["cu_seqlens"],
                                     scale=w.scale, output_final_state=True)
@@ -122,6 +151,16 @@ def cpu_baseline(w):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     threads = min(threads, len(os.sched_getaffinity(0)))
     f = wl.to_f32
+    if isinstance(w, wl.DecodeWorkload):
+        log("cpu_baseline: float64 decode oracle (numpy, one step) ...")
+        t0 = time.perf_counter()
+        oracle.gdn_decode(f(w.packed_qkv), f(w.raw_gate), f(w.raw_beta), f(w.A_log), f(w.dt_bias), f(w.pool),
+                          w.state_indices.numpy(), None if w.has_initial_state is None else w.has_initial_state.numpy(),
+                          H=w.H, HK=w.HK, K=w.K, V=w.V, scale=w.scale)
+        dt = time.perf_counter() - t0
+        return {"value": w.tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole {w.name} step ({w.tokens} rows x {w.H} heads), one float64 pass, "
+                          f"{dt:.2f} s wall"}
     args = dict(q=f(w.q), k=f(w.k), v=f(w.v), g=f(w.g))
     log(f"cpu_baseline: float64 oracle on {threads} threads ...")
     t0 = time.perf_counter()
@@ -164,7 +203,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=3, help="input sets cycled through (cache defeat)")
     ap.add_argument("--workload", default="dense_gdn",
-                    choices=["dense_gdn", "tiny_gdn", "varlen_gdn", "long_gdn", "ssd_gla"])
+                    choices=["dense_gdn", "tiny_gdn", "varlen_gdn", "long_gdn", "ssd_gla", "decode_gdn"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the second pass, whose launches are bracketed with HIP events")
@@ -237,7 +276,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(dom, w.name),
                 "kernel": dom, "avg_us": round(avg_s * 1e6, 2), "algorithmic_bytes": ab}
-    path_bytes = algorithmic_bytes(w, "path")
+    decode = isinstance(w, wl.DecodeWorkload)
+    path_bytes = algorithmic_bytes(w, "decode_path" if decode else "path")
     path_ach = path_bytes / (elapsed / args.steps) / 1e9
     copy_gbs = None if args.no_copy_peak else measured_copy_gbs(dev)
     if roof is not None and copy_gbs:
@@ -247,9 +287,14 @@ def main():
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if w.q.dtype == torch.bfloat16 else "f32", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HK": w.HK, "K": w.K, "V": w.V,
-                   "chunk": w.chunk, "n_seg": w.n_seg, "tokens": w.tokens, "rotate": len(sets)},
+        "vs_baseline": None,
+        "dtype": "bf16" if (w.packed_qkv if decode else w.q).dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": ({"workload": w.name, "B": w.B, "H": w.H, "HK": w.HK, "K": w.K, "V": w.V,
+                    "pool": "f32" if w.pool.dtype == torch.float32 else "bf16", "num_slots": w.pool.shape[0],
+                    "tokens": w.tokens, "rotate": len(sets)} if decode else
+                   {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HK": w.HK, "K": w.K, "V": w.V,
+                    "chunk": w.chunk, "n_seg": w.n_seg, "tokens": w.tokens, "rotate": len(sets)}),
         "roofline": roof,
         "path_roofline": {"bound": "hbm", "achieved": round(path_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(path_ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": path_bytes,

@@ -19,6 +19,8 @@ Functions (same names as the C entry points, without the ``sf_`` prefix):
 * ``state_scan``        exclusive scan over segment summaries.
 * ``segmented_gdn_fwd`` / ``segmented_gla_fwd``: one long sequence cut into
   segments laid along the batch axis: summary -> scan -> chunk forward.
+* ``gdn_decode``        one-token paged Gated Delta Rule decode (attention-gym
+                        "Linear Attention", recurrent_gdn_decode).
 """
 from __future__ import annotations
 
@@ -40,8 +42,8 @@ KINDS = {"gdn": SF_KIND_GDN, "gla": SF_KIND_GLA}
 EXPORTED = (
     "sf_version", "sf_last_error", "sf_gdn_chunk_fwd_workspace", "sf_gdn_chunk_fwd",
     "sf_gla_chunk_fwd", "sf_segment_summary_workspace", "sf_segment_summary",
-    "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_timing_enable",
-    "sf_timing_collect",
+    "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_gdn_decode",
+    "sf_timing_enable", "sf_timing_collect",
 )
 
 
@@ -83,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.sf_gdn_segmented_fwd_workspace.argtypes = [I, I, I, I, I, I, I]
     L.sf_gdn_segmented_fwd.restype = I
     L.sf_gdn_segmented_fwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, Z, P]
+    L.sf_gdn_decode.restype = I
+    L.sf_gdn_decode.argtypes = [I, P, P, P, P, P, P, I, I, ctypes.c_longlong, P, P, I, I, I, I, I, F, P, P]
     L.sf_timing_enable.restype = I
     L.sf_timing_enable.argtypes = [I]
     L.sf_timing_collect.restype = I
@@ -286,6 +290,62 @@ def segmented_gla_fwd(q, k, v, g, n_seg, initial_state=None, *, scale=1.0, chunk
     S_in, S_final = state_scan("gla", a, S_ext, initial_state, B=B, n_seg=n_seg, final_state=output_final_state)
     o, _ = gla_chunk_fwd(sv(q), sv(k), sv(v), sv(g), S_in, scale=scale, chunk=chunk)
     return o.view(B, T, *o.shape[2:]), S_final
+
+
+def gdn_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_cache, state_indices, *,
+               has_initial_state=None, scale=None, out=None):
+    """One decode token per sequence; advances ``state_cache`` in place.
+
+    packed_qkv [B, 2*HK*K + H*V] (bf16 or float32): per row the query heads, key heads, value heads;
+    raw_gate, raw_beta [1, B, H] or [B, H] in packed_qkv's dtype; A_log, dt_bias [H] float32;
+    state_cache [num_slots, H, V, K] float32 or bf16 (each slot dense; padding between slots allowed);
+    state_indices [B] int32 (<= 0: null row, zero output, cache untouched); has_initial_state [B]
+    bool or None. Returns out [1, B, H, V] in packed_qkv's dtype (``out`` itself when given)."""
+    _need(packed_qkv, "packed_qkv", ndim=2)
+    dev = packed_qkv.device
+    B, W = packed_qkv.shape
+    if not isinstance(state_cache, torch.Tensor) or not state_cache.is_cuda or state_cache.dim() != 4:
+        raise ValueError("state_cache must be a [num_slots, H, V, K] GPU tensor")
+    if state_cache.device != dev:
+        raise ValueError(f"state_cache is on {state_cache.device}, expected {dev}")
+    if state_cache.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"state_cache must be float32 or bfloat16, got {state_cache.dtype}")
+    NS, H, V, K = state_cache.shape
+    st = state_cache.stride()
+    if st[3] != 1 or st[2] != K or st[1] != V * K or (NS > 1 and st[0] < H * V * K):
+        raise ValueError("each [H, V, K] slot of state_cache must be dense")
+    if (W - H * V) <= 0 or (W - H * V) % (2 * K):
+        raise ValueError(f"packed_qkv width {W} does not match 2*HK*{K} + {H}*{V}")
+    HK = (W - H * V) // (2 * K)
+    for name, t in (("raw_gate", raw_gate), ("raw_beta", raw_beta)):
+        _need(t, name, dtype=packed_qkv.dtype, device=dev)
+        if t.numel() != B * H:
+            raise ValueError(f"{name} must hold [1, {B}, {H}] values, got shape {tuple(t.shape)}")
+    _need(A_log, "A_log", dtype=torch.float32, ndim=1, device=dev)
+    _need(dt_bias, "dt_bias", dtype=torch.float32, ndim=1, device=dev)
+    if A_log.numel() != H or dt_bias.numel() != H:
+        raise ValueError(f"A_log and dt_bias must have {H} entries")
+    _need(state_indices, "state_indices", dtype=torch.int32, ndim=1, device=dev)
+    if state_indices.numel() != B:
+        raise ValueError(f"state_indices must have {B} entries")
+    if has_initial_state is not None:
+        _need(has_initial_state, "has_initial_state", dtype=torch.bool, ndim=1, device=dev)
+        if has_initial_state.numel() != B:
+            raise ValueError(f"has_initial_state must have {B} entries")
+    if out is None:
+        out = torch.empty((1, B, H, V), dtype=packed_qkv.dtype, device=dev)
+    else:
+        _need(out, "out", dtype=packed_qkv.dtype, device=dev)
+        if out.numel() != B * H * V:
+            raise ValueError(f"out must hold [1, {B}, {H}, {V}] values")
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    pool_dt = SF_BF16 if state_cache.dtype == torch.bfloat16 else SF_F32
+    stride0 = st[0] if NS > 1 else H * V * K
+    _check(lib().sf_gdn_decode(_dt(packed_qkv), _ptr(packed_qkv), _ptr(raw_gate), _ptr(raw_beta), _ptr(A_log),
+                               _ptr(dt_bias), _ptr(state_cache), pool_dt, NS, stride0, _ptr(state_indices),
+                               _ptr(has_initial_state), B, H, HK, K, V, float(scale), _ptr(out), _stream()))
+    return out
 
 
 def timing_enable(max_pairs: int = 4096):

@@ -315,4 +315,37 @@ sf_status sf_state_scan(sf_kind kind, const float* M, const float* S_ext, const 
     return hip_status(e, "sf_state_scan launch");
 }
 
+sf_status sf_gdn_decode(sf_dtype dt, const void* packed_qkv, const void* raw_gate, const void* raw_beta,
+                        const float* A_log, const float* dt_bias, void* state_pool, sf_dtype pool_dt,
+                        int num_slots, long long slot_stride, const int32_t* state_indices,
+                        const uint8_t* has_initial_state, int B, int H, int HK, int K, int V, float scale,
+                        void* out, void* stream) {
+    if (dt != SF_F32 && dt != SF_BF16) return fail(SF_ERR_INVALID, "dtype must be SF_F32 or SF_BF16");
+    if (pool_dt != SF_F32 && pool_dt != SF_BF16) return fail(SF_ERR_INVALID, "pool dtype must be SF_F32 or SF_BF16");
+    if (B < 0 || H <= 0 || HK <= 0 || K <= 0 || V <= 0 || num_slots < 0)
+        return fail(SF_ERR_INVALID, "sizes must be positive (B=%d H=%d HK=%d K=%d V=%d num_slots=%d)", B, H, HK, K, V,
+                    num_slots);
+    if (H % HK != 0) return fail(SF_ERR_INVALID, "HK=%d must divide H=%d", HK, H);
+    if (K != 64 && K != 128 && K != 256)
+        return fail(SF_ERR_UNSUPPORTED, "decode is built for K in {64, 128, 256} (K=%d)", K);
+    if (V % 16 != 0) return fail(SF_ERR_UNSUPPORTED, "V must be a multiple of 16 (V=%d)", V);
+    const long long block = (long long)H * V * K;
+    if (slot_stride < block || slot_stride % 4 != 0)
+        return fail(SF_ERR_INVALID, "slot_stride %lld must be a multiple of 4 and at least H*V*K = %lld", slot_stride,
+                    block);
+    if (!fits((long)B * (2L * HK * K + (long)H * V)) || !fits((long)B * H * V) || B > kMaxElems / H)
+        return fail(SF_ERR_UNSUPPORTED, "a tensor has 2^31 or more elements (int64 offsets are not supported)");
+    if (B == 0) return SF_OK;
+    if (!packed_qkv || !raw_gate || !raw_beta || !A_log || !dt_bias || !state_pool || !state_indices || !out)
+        return fail(SF_ERR_INVALID, "packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_pool, state_indices and out "
+                                    "must not be NULL");
+    if (reinterpret_cast<uintptr_t>(state_pool) % 16 != 0 || reinterpret_cast<uintptr_t>(packed_qkv) % 16 != 0)
+        return fail(SF_ERR_INVALID, "state_pool and packed_qkv must be 16-byte aligned");
+    hipError_t e = sf::launch_gdn_decode(dt == SF_BF16, pool_dt == SF_BF16, packed_qkv, raw_gate, raw_beta, A_log,
+                                         dt_bias, state_pool, slot_stride, num_slots, state_indices,
+                                         has_initial_state, B, H, HK, K, V, scale, out,
+                                         static_cast<hipStream_t>(stream));
+    return hip_status(e, "sf_gdn_decode launch");
+}
+
 }  // extern "C"

@@ -75,6 +75,13 @@ hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const v
                       float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages = 3,
                       int pre_w = -1);
 
+// One-token paged delta-rule decode (decode.hip). pool_bf16: the pool's element type.
+hipError_t launch_gdn_decode(bool bf16, bool pool_bf16, const void* qkv, const void* raw_gate,
+                             const void* raw_beta, const float* A_log, const float* dt_bias, void* pool,
+                             long long slot_stride, int num_slots, const int32_t* state_indices,
+                             const uint8_t* has_init, int B, int H, int HK, int K, int V, float scale,
+                             void* out, hipStream_t s);
+
 // Compute units of the current device, and whether a bf16 delta-rule chain over `chains`
 // (sequence, head) pairs of `rows` state rows runs per 16-row slice (else per head).
 int device_cus();

@@ -196,6 +196,39 @@ sf_status sf_gdn_segmented_fwd(sf_dtype dt, const void *q, const void *k, const 
                                void *stream);
 
 /*
+ * One-token paged Gated Delta Rule decode (attention-gym "Linear Attention":
+ * the recurrent_gdn_decode entry; section "Gate Transforms" for the gate).
+ * For every sequence b < B and value head h < H, in float32:
+ *   slot = state_indices[b]; a slot <= 0 (null row) or >= num_slots gives a
+ *   zero output row and no state access;
+ *   q, k = the row's query and key heads h / (H / HK), each L2-normalised as
+ *   x / sqrt(|x|^2 + 1e-6); v = the row's value head h;
+ *   g = -exp(A_log[h]) * softplus(raw_gate[b, h] + dt_bias[h]);
+ *   beta = sigmoid(raw_beta[b, h]);
+ *   S = state_pool[slot, h] (zeros when has_initial_state[b] == 0);
+ *   S <- exp(g) S; r = beta (v - S k); S <- S + r k^T; o = scale S q;
+ *   state_pool[slot, h] = S (rounded to pool_dt); out[b, h] = o (in dt).
+ * Arguments (all device pointers):
+ *   packed_qkv [B, 2*HK*K + H*V] dt, per row the HK query heads, the HK key
+ *   heads, then the H value heads, each head's K or V elements contiguous;
+ *   raw_gate, raw_beta [B, H] dt (the [1, B, H] projections);
+ *   A_log, dt_bias [H] float32;
+ *   state_pool: num_slots slots, slot s at state_pool + s * slot_stride
+ *   elements of pool_dt (SF_F32 or SF_BF16), each a dense [H, V, K] block;
+ *   slot_stride >= H*V*K and a multiple of 4; 16-byte aligned base;
+ *   state_indices [B] int32; has_initial_state [B] uint8 or NULL (all set);
+ *   out [B, H, V] dt, must not alias an input.
+ * The pool is advanced in place: two rows naming the same positive slot race
+ * (the caller keeps active slots unique). K in {64, 128, 256}; V a positive
+ * multiple of 16; HK divides H.
+ */
+sf_status sf_gdn_decode(sf_dtype dt, const void *packed_qkv, const void *raw_gate,
+                        const void *raw_beta, const float *A_log, const float *dt_bias,
+                        void *state_pool, sf_dtype pool_dt, int num_slots, long long slot_stride,
+                        const int32_t *state_indices, const uint8_t *has_initial_state, int B,
+                        int H, int HK, int K, int V, float scale, void *out, void *stream);
+
+/*
  * Kernel timing hook for measurement. While enabled, every kernel the
  * library enqueues is bracketed by a pair of HIP events recorded on the same
  * stream (events come from a pool created by sf_timing_enable, so no

@@ -151,6 +151,29 @@ def test_summary_and_scan_reject_invalid_arguments(L):
     assert st == sf.SF_ERR_INVALID
 
 
+def test_decode_rejects_invalid_arguments(L):
+    def call(dt=sf.SF_BF16, pool_dt=sf.SF_F32, B=4, H=8, HK=4, K=128, V=128, slots=9, stride=None, pool=FAKE * 16,
+             qkv=FAKE * 16, idx=FAKE):
+        stride = H * V * K if stride is None else stride
+        st = L.sf_gdn_decode(dt, qkv, FAKE, FAKE, FAKE, FAKE, pool, pool_dt, slots, stride, idx, None, B, H, HK, K, V,
+                             1.0, FAKE, None)
+        return st, L.sf_last_error().decode()
+    assert call(K=96)[0] == sf.SF_ERR_UNSUPPORTED
+    assert call(K=512)[0] == sf.SF_ERR_UNSUPPORTED
+    assert call(V=72)[0] == sf.SF_ERR_UNSUPPORTED
+    assert call(HK=3)[0] == sf.SF_ERR_INVALID
+    assert call(dt=5)[0] == sf.SF_ERR_INVALID
+    assert call(pool_dt=5)[0] == sf.SF_ERR_INVALID
+    st, err = call(stride=8 * 128 * 128 - 4)
+    assert st == sf.SF_ERR_INVALID and "slot_stride" in err
+    assert call(stride=8 * 128 * 128 + 2)[0] == sf.SF_ERR_INVALID
+    st, err = call(pool=FAKE * 16 + 8)
+    assert st == sf.SF_ERR_INVALID and "aligned" in err
+    st, err = call(idx=None)
+    assert st == sf.SF_ERR_INVALID and "NULL" in err
+    assert call(B=0, idx=None)[0] == sf.SF_OK  # nothing to do, nothing enqueued
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 64, 2, 64)

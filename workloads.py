@@ -19,6 +19,12 @@ is open noted in the workload functions below:
 5. ``ssd_gla``        scalar-gate linear attention, B=2 T=16384 H=64 HK=8,
                       K=128 (dstate), V=64 (headdim), chunk 128, 8 segments per row.
 
+and one decode workload (one token per sequence against a paged state pool):
+
+6. ``decode_gdn``     B=256 sequences, H=HK=32, K=V=128 (the packed workload's
+                      heads), bf16 packed [Q | K | V] rows, float32 pool of 257
+                      slots (slot 0 the null slot), every row active.
+
 Draw order inside one workload: q, k, v, gate noise, beta noise, h0, A, dt,
 sequence lengths.
 """
@@ -30,7 +36,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-SEEDS = {"tiny_gdn": 101, "dense_gdn": 102, "varlen_gdn": 103, "long_gdn": 104, "ssd_gla": 105}
+SEEDS = {"tiny_gdn": 101, "dense_gdn": 102, "varlen_gdn": 103, "long_gdn": 104, "ssd_gla": 105,
+         "decode_gdn": 106}
 
 
 @dataclass
@@ -208,8 +215,70 @@ def ssd_gla(seed=SEEDS["ssd_gla"], *, B=2, T=16384, H=64, HK=8, K=128, V=64, n_s
                     scale=1.0, chunk=128, n_seg=n_seg, meta={"A": d["A"]})
 
 
+@dataclass
+class DecodeWorkload:
+    name: str
+    packed_qkv: torch.Tensor       # [B, 2*HK*K + H*V]: query heads, key heads, value heads
+    raw_gate: torch.Tensor         # [1, B, H], element type of packed_qkv
+    raw_beta: torch.Tensor         # [1, B, H]
+    A_log: torch.Tensor            # [H] float32
+    dt_bias: torch.Tensor          # [H] float32
+    pool: torch.Tensor             # [num_slots, H, V, K] float32 or bf16
+    state_indices: torch.Tensor    # [B] int32; <= 0 marks a null row
+    has_initial_state: Optional[torch.Tensor]  # [B] bool or None (all loaded)
+    H: int
+    HK: int
+    K: int
+    V: int
+    scale: float
+
+    @property
+    def B(self):
+        return self.packed_qkv.shape[0]
+
+    @property
+    def tokens(self) -> int:
+        """Rows that advance a slot (one token each)."""
+        return int((self.state_indices > 0).sum())
+
+
+def decode_inputs(*, B, H, HK, K, V, dtype=torch.bfloat16, pool_dtype=torch.float32, seed=0,
+                  num_slots=None, n_null=0, n_fresh=0, pool_std=0.02):
+    """packed rows, raw gate and raw beta ~ N(0,1); A_log = log U(1, 16) per head; dt_bias ~
+    N(-3, 1) per head; pool ~ N(0, pool_std^2); slots a random permutation of 1..num_slots-1, then
+    n_null rows set to the null indices 0 and -1 (alternating) and n_fresh other rows marked fresh."""
+    rng = np.random.default_rng(seed)
+    num_slots = num_slots or B + 1
+    assert num_slots - 1 >= B and n_null + n_fresh <= B
+    packed = _normal(rng, (B, 2 * HK * K + H * V))
+    raw_gate = _normal(rng, (1, B, H))
+    raw_beta = _normal(rng, (1, B, H))
+    A_log = np.log(rng.uniform(1.0, 16.0, size=H)).astype(np.float32)
+    dt_bias = (rng.standard_normal(H) - 3.0).astype(np.float32)
+    pool = _normal(rng, (num_slots, H, V, K)) * np.float32(pool_std)
+    idx = rng.permutation(np.arange(1, num_slots))[:B].astype(np.int32)
+    rows = rng.permutation(B)
+    for i, r in enumerate(rows[:n_null]):
+        idx[r] = 0 if i % 2 == 0 else -1
+    fresh = None
+    if n_fresh:
+        fresh = np.ones(B, dtype=bool)
+        fresh[rows[n_null:n_null + n_fresh]] = False
+    return dict(packed_qkv=_cast(packed, dtype), raw_gate=_cast(raw_gate, dtype), raw_beta=_cast(raw_beta, dtype),
+                A_log=torch.from_numpy(A_log), dt_bias=torch.from_numpy(dt_bias), pool=_cast(pool, pool_dtype),
+                state_indices=torch.from_numpy(idx),
+                has_initial_state=None if fresh is None else torch.from_numpy(fresh))
+
+
+def decode_gdn(seed=SEEDS["decode_gdn"], *, B=256, H=32, HK=32, D=128):
+    """One decode token for each of B sequences; every row active and loaded; scale 1/sqrt(D). The
+    pages give no decode batch: 256 rows of the packed workload's heads is the reading taken."""
+    d = decode_inputs(B=B, H=H, HK=HK, K=D, V=D, seed=seed)
+    return DecodeWorkload("decode_gdn", H=H, HK=HK, K=D, V=D, scale=1.0 / np.sqrt(D), **d)
+
+
 CONFIGS = {"tiny_gdn": tiny_gdn, "dense_gdn": dense_gdn, "varlen_gdn": varlen_gdn,
-           "long_gdn": long_gdn, "ssd_gla": ssd_gla}
+           "long_gdn": long_gdn, "ssd_gla": ssd_gla, "decode_gdn": decode_gdn}
 
 
 def to_f32(t):
