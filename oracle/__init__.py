@@ -23,6 +23,8 @@ What each function follows (pages by title and section):
   check that the chunk algebra reproduces the token recurrence.
 * ``gdn_decode``    attention-gym "Linear Attention", the ``recurrent_gdn_decode``
   entry and the section "Gate Transforms" (``decode.py``, numpy float64).
+* ``gdn_recurrent_paged``  the ``recurrent_gdn`` entry with a paged state pool:
+  slot gather and scatter around ``gdn_forward`` (``decode.py``).
 
 Pins: tests/test_oracle.py checks every function against closed forms,
 brute-force products or invariants that do not reuse this code.
@@ -192,4 +194,4 @@ def chunked_forward(kind, q, k, v, g, beta=None, h0=None, cu_seqlens=None, scale
     return out, ht
 
 
-from .decode import gdn_decode  # noqa: E402  (numpy float64, no C part)
+from .decode import gdn_decode, gdn_recurrent_paged  # noqa: E402  (numpy float64, no C part)

@@ -1,7 +1,15 @@
-"""One-token paged delta-rule decode, float64 (test infrastructure; same rules as the rest of
-``oracle/``: only tests, the smoke check and the bench's CPU baseline may use it).
+"""Recurrent (token-by-token) delta rule with a paged state pool, and the one-token paged decode,
+float64 (test infrastructure; same rules as the rest of ``oracle/``: only tests, the smoke check
+and the bench's CPU baseline may use it).
 
-Follows attention-gym "Linear Attention": the API entry of ``recurrent_gdn_decode`` (the
+``gdn_recurrent_paged`` follows the ``recurrent_gdn`` entry of attention-gym "Linear Attention"
+with ``state_indices``: every sequence starts from its slot of the pool (or from zero when its
+``has_initial_state`` entry is false), runs the token rule over its tokens, and its final state
+overwrites the slot; a non-positive index gives zero output and leaves the pool untouched. The
+token recurrence itself is ``oracle.gdn_forward`` (oracle.c); this function only gathers and
+scatters the slots around it.
+
+``gdn_decode`` follows attention-gym "Linear Attention": the API entry of ``recurrent_gdn_decode`` (the
 packed post-convolution [Q | K | V] row per token, grouped q/k heads, the paged state pool
 advanced in place through slot indices, null slots, the fresh-slot mask) and the section
 "Gate Transforms" (the softplus convention for the decay). The recurrence step is the token
@@ -86,3 +94,35 @@ def gdn_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_pool, state
             out[b, h] = scale * (S @ q)
             pool[slot, h] = S
     return out, pool
+
+
+def gdn_recurrent_paged(q, k, v, g, beta, state_pool, state_indices, has_initial_state=None,
+                        cu_seqlens=None, scale=None):
+    """q, k [B, T, HK, K]; v [B, T, H, V]; g, beta [B, T, H] (g the natural-log decay, beta the
+    write gate, both as given); state_pool [num_slots, H, V, K]; state_indices [N] (N = B, or the
+    number of packed sequences). Returns (out [B, T, H, V], pool), float64; rows of null sequences
+    are zero, rows outside every sequence are NaN."""
+    from . import gdn_forward
+    q = np.asarray(q, dtype=np.float64)
+    B, T, HK, K = q.shape
+    H, V = np.shape(v)[2], np.shape(v)[3]
+    idx = np.asarray(state_indices).astype(np.int64)
+    N = idx.shape[0]
+    init = np.ones(N, dtype=bool) if has_initial_state is None else np.asarray(has_initial_state, dtype=bool)
+    pool = np.array(state_pool, dtype=np.float64, copy=True)
+    h0 = np.zeros((N, H, V, K))
+    for n in range(N):
+        if idx[n] > 0 and init[n]:
+            h0[n] = pool[idx[n]]
+    out, ht = gdn_forward(q, k, v, g, beta, h0=h0, cu_seqlens=cu_seqlens, scale=scale)
+    cu = np.arange(B + 1) * T if cu_seqlens is None else np.asarray(cu_seqlens)
+    for n in range(N):
+        if idx[n] > 0:
+            pool[idx[n]] = ht[n]
+        else:  # a null sequence: zero output rows
+            if cu_seqlens is None:
+                out[n] = 0.0
+            else:
+                out[0, cu[n]:cu[n + 1]] = 0.0
+    return out, pool
+

@@ -13,6 +13,10 @@ sections of the packed row in the wrong order, a null slot written, a fresh slot
 * invariance of the output under positive rescaling of q and k (the normalisation);
 * T decode steps against the token-by-token float64 recurrence of oracle.c, which has pins of
   its own (tests/test_oracle.py), with grouped heads and a permuted set of slots.
+
+The paged recurrent form (``gdn_recurrent_paged``: slot gather, ``gdn_forward``, slot scatter)
+is pinned against the decode oracle run token by token (its q, k and gates prepared with the
+decode module's own pinned helpers), and for null, fresh and empty sequences in a packed stream.
 """
 import math
 
@@ -151,3 +155,71 @@ def test_steps_match_token_recurrence():
     np.testing.assert_allclose(cur[idx], ref_ht, rtol=2e-5, atol=2e-6)
     for s in (0, 3, 4):
         assert np.array_equal(cur[s], pool[s])
+
+
+def _prepared(rng, B, T):
+    """Raw decode inputs for T tokens and the recurrent form's inputs made from them with the decode
+    module's helpers (each pinned above)."""
+    q = rng.standard_normal((B, T, HK, K))
+    k = rng.standard_normal((B, T, HK, K))
+    v = rng.standard_normal((B, T, H, V))
+    rg = rng.standard_normal((B, T, H))
+    rb = rng.standard_normal((B, T, H))
+    A_log = rng.standard_normal(H) * 0.5
+    dt_bias = rng.standard_normal(H) * 0.5
+    qn = np.apply_along_axis(dec.l2_normalise, -1, q)
+    kn = np.apply_along_axis(dec.l2_normalise, -1, k)
+    g = dec.decay_gate(rg, A_log, dt_bias)
+    beta = dec.write_gate(rb)
+    return (q, k, v, rg, rb, A_log, dt_bias), (qn, kn, v, g, beta)
+
+
+def test_paged_recurrent_equals_decode_steps():
+    rng = np.random.default_rng(6)
+    B, T = 4, 5
+    raw, prep = _prepared(rng, B, T)
+    pool = rng.standard_normal((7, H, V, K)) * 0.3
+    idx = np.array([3, 0, 6, 1])
+    fresh = np.array([True, True, False, True])
+    out, new = oracle.gdn_recurrent_paged(*prep, pool, idx, fresh, scale=0.3)
+    cur, outs = pool, []
+    for t in range(T):
+        o, cur = oracle.gdn_decode(packed(raw[0][:, t], raw[1][:, t], raw[2][:, t]), raw[3][:, t], raw[4][:, t],
+                                   raw[5], raw[6], cur, idx, fresh if t == 0 else None, H=H, HK=HK, K=K, V=V,
+                                   scale=0.3)
+        outs.append(o)
+    outs = np.stack(outs, axis=1)
+    np.testing.assert_allclose(out, outs, rtol=2e-5, atol=2e-6)   # gdn_forward reads float32 inputs
+    np.testing.assert_allclose(new, cur, rtol=2e-5, atol=2e-6)
+    assert np.all(out[1] == 0)                                     # the null sequence
+    for s in (0, 2, 4, 5):
+        assert np.array_equal(new[s], pool[s])
+
+
+def test_paged_recurrent_packed_edge_cases():
+    """Packed stream: an empty loaded sequence keeps its slot, an empty fresh one zeroes it, a null
+    sequence writes nothing and outputs zeros; the others equal separate unpaged runs."""
+    rng = np.random.default_rng(7)
+    lens = [3, 0, 4, 0, 2]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    _, (qn, kn, v, g, beta) = _prepared(rng, 1, T)
+    # float32 values: gdn_forward takes its inputs (h0 included) in float32
+    pool = (rng.standard_normal((8, H, V, K)) * 0.3).astype(np.float32).astype(np.float64)
+    idx = np.array([5, 2, 0, 7, 1])
+    fresh = np.array([True, True, True, False, False])
+    out, new = oracle.gdn_recurrent_paged(qn, kn, v, g, beta, pool, idx, fresh, cu_seqlens=cu, scale=0.5)
+    assert np.array_equal(new[2], pool[2])                 # empty, loaded: unchanged
+    assert np.all(new[7] == 0)                             # empty, fresh: zeroed
+    assert np.all(out[0, cu[2]:cu[3]] == 0)                # null sequence
+    for s in (0, 3, 4, 6):
+        assert np.array_equal(new[s], pool[s])
+    for n, (slot, init) in enumerate(zip(idx, fresh)):
+        if slot <= 0 or lens[n] == 0:
+            continue
+        sl = slice(cu[n], cu[n + 1])
+        h0 = pool[slot][None] if init else np.zeros((1, H, V, K))
+        o1, h1 = oracle.gdn_forward(qn[:, sl], kn[:, sl], v[:, sl], g[:, sl], beta[:, sl], h0=h0, scale=0.5)
+        np.testing.assert_allclose(out[:, sl], o1, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(new[slot], h1[0], rtol=1e-12, atol=1e-14)
+
