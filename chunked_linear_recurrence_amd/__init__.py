@@ -21,6 +21,9 @@ Functions (same names as the C entry points, without the ``sf_`` prefix):
   segments laid along the batch axis: summary -> scan -> chunk forward.
 * ``gdn_decode``        one-token paged Gated Delta Rule decode (attention-gym
                         "Linear Attention", recurrent_gdn_decode).
+* ``gdn_recurrent_fwd`` token-by-token Gated Delta Rule forward, optionally on a
+                        paged state pool (attention-gym "Linear Attention",
+                        recurrent_gdn).
 """
 from __future__ import annotations
 
@@ -42,7 +45,7 @@ KINDS = {"gdn": SF_KIND_GDN, "gla": SF_KIND_GLA}
 EXPORTED = (
     "sf_version", "sf_last_error", "sf_gdn_chunk_fwd_workspace", "sf_gdn_chunk_fwd",
     "sf_gla_chunk_fwd", "sf_segment_summary_workspace", "sf_segment_summary",
-    "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_gdn_decode",
+    "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_gdn_decode", "sf_gdn_recurrent_fwd",
     "sf_timing_enable", "sf_timing_collect",
 )
 
@@ -87,6 +90,9 @@ def lib() -> ctypes.CDLL:
     L.sf_gdn_segmented_fwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, Z, P]
     L.sf_gdn_decode.restype = I
     L.sf_gdn_decode.argtypes = [I, P, P, P, P, P, P, I, I, ctypes.c_longlong, P, P, I, I, I, I, I, F, P, P]
+    L.sf_gdn_recurrent_fwd.restype = I
+    L.sf_gdn_recurrent_fwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, I, I,
+                                       ctypes.c_longlong, P, P, P]
     L.sf_timing_enable.restype = I
     L.sf_timing_enable.argtypes = [I]
     L.sf_timing_collect.restype = I
@@ -290,6 +296,63 @@ def segmented_gla_fwd(q, k, v, g, n_seg, initial_state=None, *, scale=1.0, chunk
     S_in, S_final = state_scan("gla", a, S_ext, initial_state, B=B, n_seg=n_seg, final_state=output_final_state)
     o, _ = gla_chunk_fwd(sv(q), sv(k), sv(v), sv(g), S_in, scale=scale, chunk=chunk)
     return o.view(B, T, *o.shape[2:]), S_final
+
+
+def _pool_layout(pool, H, V, K, dev):
+    if not isinstance(pool, torch.Tensor) or not pool.is_cuda or pool.dim() != 4:
+        raise ValueError("the state pool must be a [num_slots, H, V, K] GPU tensor")
+    if pool.device != dev:
+        raise ValueError(f"the state pool is on {pool.device}, expected {dev}")
+    if pool.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"the state pool must be float32 or bfloat16, got {pool.dtype}")
+    NS = pool.shape[0]
+    if tuple(pool.shape[1:]) != (H, V, K):
+        raise ValueError(f"the state pool must be [num_slots, {H}, {V}, {K}], got {tuple(pool.shape)}")
+    st = pool.stride()
+    if st[3] != 1 or st[2] != K or st[1] != V * K or (NS > 1 and st[0] < H * V * K):
+        raise ValueError("each [H, V, K] slot of the state pool must be dense")
+    pool_dt = SF_BF16 if pool.dtype == torch.bfloat16 else SF_F32
+    return NS, (st[0] if NS > 1 else H * V * K), pool_dt
+
+
+def gdn_recurrent_fwd(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, scale=None,
+                      output_final_state=False, state_indices=None, has_initial_state=None):
+    """Token-by-token Gated Delta Rule forward. q, k [B,T,HK,K]; v [B,T,H,V]; g, beta [B,T,H] float32.
+    Without state_indices: initial_state [N,H,V,K] float32 or None; returns (output, final state or None).
+    With state_indices [N] int32: initial_state is a [num_slots,H,V,K] float32 or bf16 pool advanced in
+    place (each sequence's final state overwrites its slot; indices <= 0 give zero output and leave the
+    pool alone); has_initial_state [N] bool marks slots to load; output_final_state must be False."""
+    if state_indices is None:
+        B, T, H, HK, K, V, N = _token_args(q, k, v, g, beta, initial_state, cu_seqlens)
+        if has_initial_state is not None:
+            raise ValueError("has_initial_state needs state_indices")
+    else:
+        B, T, H, HK, K, V, N = _token_args(q, k, v, g, beta, None, cu_seqlens)
+        if output_final_state:
+            raise ValueError("output_final_state is rejected with state_indices: the pool is advanced in place")
+        _need(state_indices, "state_indices", dtype=torch.int32, ndim=1, device=q.device)
+        if state_indices.numel() != N:
+            raise ValueError(f"state_indices must have {N} entries")
+        if has_initial_state is not None:
+            _need(has_initial_state, "has_initial_state", dtype=torch.bool, ndim=1, device=q.device)
+            if has_initial_state.numel() != N:
+                raise ValueError(f"has_initial_state must have {N} entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    dev = q.device
+    out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+    if state_indices is None:
+        ht = torch.empty((N, H, V, K), dtype=torch.float32, device=dev) if output_final_state else None
+        _check(lib().sf_gdn_recurrent_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                          _ptr(cu_seqlens), N, B, T, H, HK, K, V, float(scale), _ptr(out), _ptr(ht),
+                                          None, SF_F32, 0, 0, None, None, _stream()))
+        return out, ht
+    NS, stride0, pool_dt = _pool_layout(initial_state, H, V, K, dev)
+    _check(lib().sf_gdn_recurrent_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), None,
+                                      _ptr(cu_seqlens), N, B, T, H, HK, K, V, float(scale), _ptr(out), None,
+                                      _ptr(initial_state), pool_dt, NS, stride0, _ptr(state_indices),
+                                      _ptr(has_initial_state), _stream()))
+    return out, None
 
 
 def gdn_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_cache, state_indices, *,

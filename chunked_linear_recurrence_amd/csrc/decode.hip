@@ -1,4 +1,5 @@
-// One-token paged Gated Delta Rule decode for gfx950.
+// Token-by-token Gated Delta Rule kernels for gfx950: the one-token paged decode and the
+// multi-token recurrent forward.
 //
 // attention-gym "Linear Attention": the recurrent_gdn_decode entry (one token per sequence, the
 // packed post-convolution row [Q heads | K heads | V heads], grouped q/k heads, an FP32 or BF16
@@ -17,6 +18,17 @@
 // consecutive key columns per lane (16-byte loads and stores of the float32 pool), and the two
 // row sums (S k^ and S q^) are butterfly sums over the group. Eight row iterations of loads are
 // issued before any arithmetic so that each wavefront keeps 8 KB in flight.
+//
+// Recurrent forward (attention-gym "Linear Attention", the recurrent_gdn entry): the same token
+// rule over a whole sequence, with g and beta as given and q, k used as given. The state stays
+// in registers from the first token to the last: a workgroup of four wavefronts owns 32 state
+// rows of one (sequence, head), eight lanes per row with K/8 consecutive key columns each, so
+// each row sum is a lane's own dot product plus three DPP lane permutations. The token operands
+// (q, k, the 32 values, the two gates) come in blocks of 16 tokens, moved into LDS with direct
+// loads one block ahead, so a token step waits on LDS, not on memory; outputs leave once per
+// block, 16 bytes per token and wavefront.
+// The state comes from h0 (or zero) and goes to ht, or, with slot indices, from and back to a
+// paged pool.
 #include "sf_device.h"
 #include "sf_internal.h"
 
@@ -115,6 +127,203 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gdn_decode_kernel(
     }
 }
 
+constexpr int kRecLpr = 8;     // lanes per state row in the recurrent kernel
+constexpr int kRecWaves = 4;   // wavefronts per recurrent workgroup
+constexpr int kRecRows = kRecWaves * 64 / kRecLpr;  // state rows per workgroup (32)
+constexpr int kRecTok = 16;    // tokens per block staged in LDS
+
+// raw (unconverted) four-element vectors of the token operands, converted when used
+template <typename T> struct Raw;
+template <> struct Raw<float> {
+    typedef f32x4 type;
+    static __device__ __forceinline__ f32x4 cvt(type x) { return x; }
+};
+template <> struct Raw<bf16_t> {
+    typedef i16x4 type;
+    static __device__ __forceinline__ f32x4 cvt(type x) { return Elem<bf16_t>::unpack(x); }
+};
+
+// sum over the eight lanes of a row group with DPP: quad permutations (lane i reads lane i^1, then
+// i^2), then the half-row mirror (lane i reads lane 7-i of its eight)
+__device__ __forceinline__ float row_group_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    return x;
+}
+
+// LDS plan of one recurrent workgroup: two buffers of one token block each
+template <typename ET, int K>
+struct RecLds {
+    static constexpr int RB = K * (int)sizeof(ET);           // bytes of one q or k row
+    static constexpr int QK = kRecTok * RB;                  // q (or k) rows of a block
+    static constexpr int VB = kRecTok * kRecRows * (int)sizeof(ET);  // the block's values of the 32 rows
+    static constexpr int OFF_Q = 0, OFF_K = QK, OFF_V = 2 * QK, OFF_G = OFF_V + VB;
+    static constexpr int BUF = OFF_G + 256;                  // g at +0, beta at +64 (floats)
+    static constexpr int OFF_O = 2 * BUF;                    // outputs of a block, per wavefront [16][8]
+    static constexpr int BYTES = OFF_O + kRecWaves * kRecTok * 8 * (int)sizeof(ET);
+    static_assert(QK % 1024 == 0 && VB % 1024 == 0, "block parts are whole 1 KB loads");
+};
+
+template <typename ET, typename PT, int K>
+__global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
+    const ET* __restrict__ q, const ET* __restrict__ k, const ET* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, const float* __restrict__ h0, float* __restrict__ ht, PT* __restrict__ pool,
+    long long slot_stride, int num_slots, const int32_t* __restrict__ state_indices,
+    const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cu, int T, int H, int HK, int V, float scale,
+    ET* __restrict__ out) {
+    typedef RecLds<ET, K> SM;
+    constexpr int CPL = K / kRecLpr;  // key columns per lane: lanes 8r .. 8r+7 hold state row r of the wavefront
+    constexpr int NV = CPL / 4;       // four-column vectors per lane
+    constexpr int EB = (int)sizeof(ET);
+    typedef typename Raw<ET>::type RawT;
+    __shared__ __align__(16) uint8_t smem[SM::BYTES];
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    lds_u8* const lds = (lds_u8*)smem;
+
+    const int nvb = V / kRecRows;
+    const int vb = blockIdx.x % nvb, nh = blockIdx.x / nvb;
+    const int n = nh / H, h = nh - n * H, hk = h / (H / HK);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int rl = 8 * w + lane / kRecLpr;     // row within the workgroup's 32
+    const int r0 = kRecRows * vb, row = r0 + rl;
+    const int c0 = CPL * (lane % kRecLpr);
+    int b, bos, eos;
+    if (cu) {
+        b = 0;
+        bos = cu[n];
+        eos = cu[n + 1];
+    } else {
+        b = n;
+        bos = 0;
+        eos = T;
+    }
+    PT* slot_p = nullptr;
+    if (pool) {
+        const int slot = state_indices[n];
+        if (slot <= 0 || slot >= num_slots) {  // null sequence: zero output rows, no state access
+            for (int t = bos + (int)threadIdx.x / kRecRows; t < eos; t += 64 * kRecWaves / kRecRows)
+                Io<ET>::store1(out + ((size_t)(b * T + t) * H + h) * V + r0 + threadIdx.x % kRecRows, 0.f);
+            return;
+        }
+        slot_p = pool + (size_t)slot * (size_t)slot_stride + (size_t)h * V * K;
+    }
+    const float* h0p = h0 ? h0 + ((size_t)n * H + h) * V * K : nullptr;
+    float* htp = ht ? ht + ((size_t)n * H + h) * V * K : nullptr;
+    const bool load_slot = slot_p && (has_init == nullptr || has_init[n] != 0);
+    const size_t soff = (size_t)row * K + c0;
+
+    f32x4 S[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        S[i] = load_slot ? Io<PT>::load4(slot_p + soff + 4 * i)
+                         : (h0p ? Io<float>::load4(h0p + soff + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f});
+
+    // one token block [t0, t0 + 16) into buffer bf with 16-byte direct loads (4-byte for the gates);
+    // tokens past the sequence's end repeat its last token (their results are never stored)
+    auto load_block = [&](int t0, int bf) __attribute__((always_inline)) {
+        lds_u8* B = lds + bf * SM::BUF;
+        const int last = eos - 1;
+        for (int m = w; m < SM::QK / 1024; m += kRecWaves) {
+            const int off = 1024 * m + 16 * lane, tt = min(t0 + off / SM::RB, last), pc = off % SM::RB;
+            const size_t src = ((size_t)(b * T + tt) * HK + hk) * K * EB + pc;
+            load_lds16(reinterpret_cast<const uint8_t*>(q) + src, (uint8_t*)(B + SM::OFF_Q + 1024 * m));
+            load_lds16(reinterpret_cast<const uint8_t*>(k) + src, (uint8_t*)(B + SM::OFF_K + 1024 * m));
+        }
+        constexpr int VROW = kRecRows * EB;  // bytes of the 32 values of one token
+        for (int m = w; m * 1024 < SM::VB; m += kRecWaves) {
+            const int off = 1024 * m + 16 * lane, tt = min(t0 + off / VROW, last), pc = off % VROW;
+            load_lds16(reinterpret_cast<const uint8_t*>(v) + ((size_t)(b * T + tt) * H + h) * V * EB + r0 * EB + pc,
+                       (uint8_t*)(B + SM::OFF_V + 1024 * m));
+        }
+        if (w == 0) {  // lanes 0..15 the gates, 16..31 beta, the rest repeat them
+            const int tt = min(t0 + (lane & 15), last);
+            const float* src = ((lane >> 4) & 1 ? beta : g) + (size_t)(b * T + tt) * H + h;
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(B + SM::OFF_G), 4, 0, 0);
+        }
+    };
+    const int nblk = (eos - bos + kRecTok - 1) / kRecTok;
+    if (nblk > 0) load_block(bos, 0);
+    lds_u8* const obuf = lds + SM::OFF_O + w * (kRecTok * 8 * EB);
+    for (int blk = 0; blk < nblk; ++blk) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // block blk landed for every wavefront; block blk-1's buffer is free again
+        const int t0 = bos + blk * kRecTok, nt = min(kRecTok, eos - t0);
+        if (blk + 1 < nblk) load_block(t0 + kRecTok, (blk + 1) & 1);
+        const lds_u8* B = lds + (blk & 1) * SM::BUF;
+        for (int tt = 0; tt < nt; ++tt) {
+            const lds_u8* qr = B + SM::OFF_Q + tt * SM::RB + c0 * EB;
+            const lds_u8* kr = B + SM::OFF_K + tt * SM::RB + c0 * EB;
+            const float gamma = expf(*(const __attribute__((address_space(3))) float*)(B + SM::OFF_G + 4 * tt));
+            const float bt = *(const __attribute__((address_space(3))) float*)(B + SM::OFF_G + 64 + 4 * tt);
+            const lds_u8* vp = B + SM::OFF_V + (tt * kRecRows + rl) * EB;
+            const float vv = EB == 2 ? bf2f(*(const __attribute__((address_space(3))) bf16_t*)vp)
+                                     : *(const __attribute__((address_space(3))) float*)vp;
+            f32x4 kf[NV];
+            float sk = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                kf[i] = Raw<ET>::cvt(*(const __attribute__((address_space(3))) RawT*)(kr + 4 * i * EB));
+                sk += dot4(S[i], kf[i]);
+            }
+            const float r = bt * (vv - gamma * row_group_sum(sk));
+            float so = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                S[i] = S[i] * gamma + kf[i] * r;
+                so += dot4(S[i], Raw<ET>::cvt(*(const __attribute__((address_space(3))) RawT*)(qr + 4 * i * EB)));
+            }
+            so = row_group_sum(so);
+            if (lane % kRecLpr == 0) {
+                const float ov = scale * so;
+                if constexpr (EB == 2)
+                    *(__attribute__((address_space(3))) bf16_t*)(obuf + (tt * 8 + lane / kRecLpr) * EB) = f2bf(ov);
+                else
+                    *(__attribute__((address_space(3))) float*)(obuf + (tt * 8 + lane / kRecLpr) * EB) = ov;
+            }
+        }
+        // the wavefront's 8 outputs of each token of the block: one row piece per lane
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane < nt) {
+            ET* dst = out + ((size_t)(b * T + t0 + lane) * H + h) * V + r0 + 8 * w;
+            if constexpr (EB == 2)
+                *reinterpret_cast<u128*>(dst) = *(const __attribute__((address_space(3))) u128*)(obuf + lane * 16);
+            else {
+                *reinterpret_cast<u128*>(dst) = *(const __attribute__((address_space(3))) u128*)(obuf + lane * 32);
+                *reinterpret_cast<u128*>(dst + 4) = *(const __attribute__((address_space(3))) u128*)(obuf + lane * 32 + 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        if (slot_p)
+            Io<PT>::store4(slot_p + soff + 4 * i, S[i]);
+        else if (htp)
+            Io<float>::store4(htp + soff + 4 * i, S[i]);
+    }
+}
+
+template <typename ET, typename PT>
+hipError_t launch_rec_typed(int K, const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            const float* h0, float* ht, void* pool, long long slot_stride, int num_slots,
+                            const int32_t* idx, const uint8_t* has_init, const int32_t* cu, int N, int T, int H,
+                            int HK, int V, float scale, void* out, hipStream_t s) {
+    const dim3 grid((unsigned)N * (unsigned)H * (unsigned)(V / kRecRows)), block(64 * kRecWaves);
+    const ET *qq = static_cast<const ET*>(q), *kk = static_cast<const ET*>(k), *vv = static_cast<const ET*>(v);
+    PT* p = static_cast<PT*>(pool);
+    ET* o = static_cast<ET*>(out);
+    if (K == 64)
+        gdn_recurrent_kernel<ET, PT, 64><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride, num_slots,
+                                                                idx, has_init, cu, T, H, HK, V, scale, o);
+    else if (K == 128)
+        gdn_recurrent_kernel<ET, PT, 128><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride,
+                                                                 num_slots, idx, has_init, cu, T, H, HK, V, scale, o);
+    else
+        gdn_recurrent_kernel<ET, PT, 256><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride,
+                                                                 num_slots, idx, has_init, cu, T, H, HK, V, scale, o);
+    return hipGetLastError();
+}
+
 template <typename ET, typename PT>
 hipError_t launch_typed(int K, const void* qkv, const void* rg, const void* rb, const float* A_log,
                         const float* dt_bias, void* pool, long long slot_stride, int num_slots,
@@ -139,6 +348,28 @@ hipError_t launch_typed(int K, const void* qkv, const void* rg, const void* rb, 
 }
 
 }  // namespace
+
+hipError_t launch_gdn_recurrent(bool bf16, bool pool_bf16, const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, const float* h0, float* ht, void* pool,
+                                long long slot_stride, int num_slots, const int32_t* state_indices,
+                                const uint8_t* has_init, const int32_t* cu, int N, int T, int H, int HK, int K,
+                                int V, float scale, void* out, hipStream_t s) {
+    if (N == 0) return hipSuccess;
+    timing_begin("gdn_recurrent", s);
+    hipError_t e;
+    if (bf16)
+        e = pool_bf16 ? launch_rec_typed<bf16_t, bf16_t>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
+                                                         state_indices, has_init, cu, N, T, H, HK, V, scale, out, s)
+                      : launch_rec_typed<bf16_t, float>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
+                                                        state_indices, has_init, cu, N, T, H, HK, V, scale, out, s);
+    else
+        e = pool_bf16 ? launch_rec_typed<float, bf16_t>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
+                                                        state_indices, has_init, cu, N, T, H, HK, V, scale, out, s)
+                      : launch_rec_typed<float, float>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
+                                                       state_indices, has_init, cu, N, T, H, HK, V, scale, out, s);
+    timing_end(s);
+    return e;
+}
 
 hipError_t launch_gdn_decode(bool bf16, bool pool_bf16, const void* qkv, const void* raw_gate,
                              const void* raw_beta, const float* A_log, const float* dt_bias, void* pool,

@@ -315,6 +315,43 @@ sf_status sf_state_scan(sf_kind kind, const float* M, const float* S_ext, const 
     return hip_status(e, "sf_state_scan launch");
 }
 
+sf_status sf_gdn_recurrent_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B, int T,
+                               int H, int HK, int K, int V, float scale, void* out, float* ht, void* state_pool,
+                               sf_dtype pool_dt, int num_slots, long long slot_stride, const int32_t* state_indices,
+                               const uint8_t* has_initial_state, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
+    if (st != SF_OK) return st;
+    if (K != 64 && K != 128 && K != 256)
+        return fail(SF_ERR_UNSUPPORTED, "the recurrent kernel is built for K in {64, 128, 256} (K=%d)", K);
+    if (V % 32 != 0) return fail(SF_ERR_UNSUPPORTED, "V must be a multiple of 32 (V=%d)", V);
+    if (!fits((long)N * H * (V / 32))) return fail(SF_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+    const bool paged = state_indices != nullptr;
+    if (paged) {
+        if (h0 || ht) return fail(SF_ERR_INVALID, "with state_indices the pool holds the states: h0 and ht must be NULL");
+        if (pool_dt != SF_F32 && pool_dt != SF_BF16) return fail(SF_ERR_INVALID, "pool dtype must be SF_F32 or SF_BF16");
+        if (num_slots < 0) return fail(SF_ERR_INVALID, "num_slots must not be negative");
+        const long long block = (long long)H * V * K;
+        if (slot_stride < block || slot_stride % 4 != 0)
+            return fail(SF_ERR_INVALID, "slot_stride %lld must be a multiple of 4 and at least H*V*K = %lld",
+                        slot_stride, block);
+        if (!state_pool) return fail(SF_ERR_INVALID, "state_pool must not be NULL with state_indices");
+        if (reinterpret_cast<uintptr_t>(state_pool) % 16 != 0) return fail(SF_ERR_INVALID, "state_pool must be 16-byte aligned");
+    } else if (state_pool || has_initial_state) {
+        return fail(SF_ERR_INVALID, "state_pool and has_initial_state need state_indices");
+    }
+    if (N == 0) return SF_OK;
+    if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
+    if ((h0 && reinterpret_cast<uintptr_t>(h0) % 16 != 0) || (ht && reinterpret_cast<uintptr_t>(ht) % 16 != 0))
+        return fail(SF_ERR_INVALID, "h0 and ht must be 16-byte aligned");
+    hipError_t e = sf::launch_gdn_recurrent(dt == SF_BF16, paged && pool_dt == SF_BF16, q, k, v, g, beta, h0, ht,
+                                            paged ? state_pool : nullptr, slot_stride, num_slots, state_indices,
+                                            has_initial_state, cu_seqlens, N, T, H, HK, K, V, scale, out,
+                                            static_cast<hipStream_t>(stream));
+    return hip_status(e, "sf_gdn_recurrent_fwd launch");
+}
+
 sf_status sf_gdn_decode(sf_dtype dt, const void* packed_qkv, const void* raw_gate, const void* raw_beta,
                         const float* A_log, const float* dt_bias, void* state_pool, sf_dtype pool_dt,
                         int num_slots, long long slot_stride, const int32_t* state_indices,

@@ -196,6 +196,38 @@ sf_status sf_gdn_segmented_fwd(sf_dtype dt, const void *q, const void *k, const 
                                void *stream);
 
 /*
+ * Token-by-token Gated Delta Rule forward (attention-gym "Linear Attention":
+ * the recurrent_gdn entry; the token rule of the section "Gated Delta Rule").
+ * The same result as sf_gdn_chunk_fwd up to floating-point order, computed one
+ * token after another with the state in registers: meant for decoding and for
+ * short prefills (a few tokens per sequence), where the chunk path's per-chunk
+ * factors do not pay.
+ *   q, k [B, T, HK, K] dt, v [B, T, H, V] dt, g and beta [B, T, H] float32
+ *   (g the natural-log decay, beta the write gate, both used as given);
+ *   cu_seqlens [N+1] (batch-one packed input) or NULL (then N == B);
+ *   out [B, T, H, V] dt (rows at or past cu_seqlens[N] are not written).
+ * State, one of two modes:
+ *   - state_indices == NULL: h0 [N, H, V, K] float32 or NULL (zeros); ht
+ *     [N, H, V, K] float32 or NULL; state_pool must be NULL;
+ *   - state_indices [N] int32: sequence n starts from slot state_indices[n]
+ *     of state_pool (zeros when has_initial_state[n] == 0) and its final
+ *     state overwrites that slot, even for an empty sequence; an index <= 0 or
+ *     >= num_slots gives zero output rows and no state access; h0 and ht must
+ *     be NULL. The pool layout is as for sf_gdn_decode (pool_dt SF_F32 or
+ *     SF_BF16, slot_stride elements between slots, each slot a dense
+ *     [H, V, K] block, 16-byte aligned base); two sequences naming the same
+ *     positive slot race.
+ * K in {64, 128, 256}; V a positive multiple of 32; HK divides H.
+ */
+sf_status sf_gdn_recurrent_fwd(sf_dtype dt, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *h0,
+                               const int32_t *cu_seqlens, int N, int B, int T, int H, int HK, int K,
+                               int V, float scale, void *out, float *ht, void *state_pool,
+                               sf_dtype pool_dt, int num_slots, long long slot_stride,
+                               const int32_t *state_indices, const uint8_t *has_initial_state,
+                               void *stream);
+
+/*
  * One-token paged Gated Delta Rule decode (attention-gym "Linear Attention":
  * the recurrent_gdn_decode entry; section "Gate Transforms" for the gate).
  * For every sequence b < B and value head h < H, in float32:

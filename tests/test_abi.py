@@ -174,6 +174,28 @@ def test_decode_rejects_invalid_arguments(L):
     assert call(B=0, idx=None)[0] == sf.SF_OK  # nothing to do, nothing enqueued
 
 
+def test_recurrent_rejects_invalid_arguments(L):
+    def call(K=128, V=128, H=4, HK=2, h0=None, ht=None, pool=None, idx=None, fresh=None, stride=0, B=2, N=2, cu=None,
+             dt=sf.SF_BF16, q=FAKE):
+        st = L.sf_gdn_recurrent_fwd(dt, q, FAKE, FAKE, FAKE, FAKE, h0, cu, N, B, 16, H, HK, K, V, 1.0, FAKE, ht, pool,
+                                    sf.SF_F32, 9, stride, idx, fresh, None)
+        return st, L.sf_last_error().decode()
+    assert call(K=96)[0] == sf.SF_ERR_UNSUPPORTED
+    assert call(V=48)[0] == sf.SF_ERR_UNSUPPORTED
+    assert call(HK=3)[0] == sf.SF_ERR_INVALID
+    assert call(N=3)[0] == sf.SF_ERR_INVALID            # N != B without cu_seqlens
+    st, err = call(idx=FAKE, h0=FAKE * 16, pool=FAKE * 16, stride=4 * 128 * 128)
+    assert st == sf.SF_ERR_INVALID and "NULL" in err    # h0 with a pool
+    st, err = call(idx=FAKE, pool=FAKE * 16, stride=4 * 128 * 128 - 4)
+    assert st == sf.SF_ERR_INVALID and "slot_stride" in err
+    st, err = call(idx=FAKE, pool=None, stride=4 * 128 * 128)
+    assert st == sf.SF_ERR_INVALID and "state_pool" in err
+    st, err = call(pool=FAKE * 16)
+    assert st == sf.SF_ERR_INVALID and "state_indices" in err
+    st, err = call(q=None)
+    assert st == sf.SF_ERR_INVALID and "NULL" in err
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 64, 2, 64)

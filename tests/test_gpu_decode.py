@@ -145,3 +145,122 @@ def test_decode_full_size(dev):
     out, pool = run_gpu(d, dev, w.scale)
     ref_out, ref_pool = run_oracle(d, w.H, w.HK, w.K, w.V, w.scale)
     check(out, pool.cpu().numpy(), ref_out, ref_pool, d, False, "decode_gdn")
+
+
+# ---------------------------------------------------------------------------------------------
+# token-by-token forward (sf_gdn_recurrent_fwd)
+# ---------------------------------------------------------------------------------------------
+
+REC_CASES = [
+    # name, dtype, B, T, H, HK, K, V, h0, lengths (packed) or None
+    ("f32-k64-h0", torch.float32, 2, 37, 4, 2, 64, 64, True, None),
+    ("bf16-k128-h0", torch.bfloat16, 2, 50, 4, 4, 128, 128, True, None),
+    ("f32-k256-v32", torch.float32, 1, 9, 2, 1, 256, 32, False, None),
+    ("bf16-packed", torch.bfloat16, 1, 0, 4, 2, 128, 64, True, [5, 0, 17, 1, 30]),
+]
+
+
+@pytest.mark.parametrize("case", REC_CASES, ids=[c[0] for c in REC_CASES])
+def test_recurrent_vs_oracle(dev, case):
+    name, dt, B, T, H, HK, K, V, with_h0, lens = case
+    cu = None
+    if lens is not None:
+        T = int(sum(lens)) + 3                       # three rows past the terminal offset stay unwritten
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    N = B if lens is None else len(lens)
+    say(f"recurrent {name}: B={B} T={T} H={H} HK={HK} K={K} V={V} N={N}")
+    d = wl.delta_rule_inputs(B=B, T=T, H=H, HK=HK, K=K, V=V, dtype=dt, seed=zlib.crc32(name.encode()) % 1000,
+                             gate_shift=1.0, h0_std=0.3 if with_h0 else None, N=N)
+    g = {n: (None if d[n] is None else d[n].to(dev).contiguous()) for n in ("q", "k", "v", "g", "beta", "h0")}
+    o, ht = sf.gdn_recurrent_fwd(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"],
+                                 cu_seqlens=None if cu is None else cu.to(dev), scale=0.3, output_final_state=True)
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    ref_o, ref_ht = oracle.gdn_forward(f(d["q"]), f(d["k"]), f(d["v"]), f(d["g"]), f(d["beta"]), f(d["h0"]),
+                                       cu_seqlens=None if cu is None else cu.numpy(), scale=0.3)
+    o = o.float().cpu().numpy()
+    ht = ht.cpu().numpy()
+    if cu is not None:
+        end = int(cu[-1])
+        o, ref_o = o[:, :end], ref_o[:, :end]
+    if dt == torch.float32:
+        eo, eh = float(np.max(np.abs(o - ref_o))), float(np.max(np.abs(ht - ref_ht)))
+        say(f"{name}: max|o|err {eo:.3g}  max|ht|err {eh:.3g}")
+        assert eo <= FP32_ATOL and eh <= FP32_ATOL
+    else:
+        eo, eh = rel_rms(o, ref_o), rel_rms(ht, ref_ht)
+        say(f"{name}: rel_rms o {eo:.3g}  ht {eh:.3g}")
+        assert eo <= BF16_RTOL and eh <= BF16_RTOL
+
+
+PAGED_CASES = [
+    # name, dtype, pool dtype, B, T, lengths or None, nulls, fresh
+    ("f32-dense", torch.float32, torch.float32, 6, 12, None, 1, 2),
+    ("bf16-bf16pool", torch.bfloat16, torch.bfloat16, 5, 20, None, 1, 1),
+    ("bf16-packed-empty", torch.bfloat16, torch.float32, 1, 0, [7, 0, 0, 13, 4, 0], 1, 2),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[c[0] for c in PAGED_CASES])
+def test_recurrent_paged_vs_oracle(dev, case):
+    name, dt, pdt, B, T, lens, nulls, fresh_n = case
+    H, HK, K, V = 4, 2, 128, 128
+    cu = None
+    if lens is not None:
+        T = int(sum(lens))
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    N = B if lens is None else len(lens)
+    say(f"recurrent paged {name}: N={N} T={T}")
+    seed = zlib.crc32(name.encode()) % 1000
+    d = wl.delta_rule_inputs(B=B, T=T, H=H, HK=HK, K=K, V=V, dtype=dt, seed=seed, gate_shift=1.0)
+    p = wl.decode_inputs(B=N, H=H, HK=HK, K=K, V=V, dtype=dt, pool_dtype=pdt, seed=seed + 1, num_slots=N + 4,
+                         n_null=nulls, n_fresh=fresh_n, pool_std=0.3)
+    pool = p["pool"].to(dev).contiguous()
+    g = {n: d[n].to(dev).contiguous() for n in ("q", "k", "v", "g", "beta")}
+    fresh = p["has_initial_state"]
+    o, none = sf.gdn_recurrent_fwd(g["q"], g["k"], g["v"], g["g"], g["beta"], pool,
+                                   cu_seqlens=None if cu is None else cu.to(dev), scale=0.25,
+                                   state_indices=p["state_indices"].to(dev),
+                                   has_initial_state=None if fresh is None else fresh.to(dev))
+    assert none is None
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    ref_o, ref_pool = oracle.gdn_recurrent_paged(f(d["q"]), f(d["k"]), f(d["v"]), f(d["g"]), f(d["beta"]),
+                                                 f(p["pool"]), p["state_indices"].numpy(),
+                                                 None if fresh is None else fresh.numpy(),
+                                                 cu_seqlens=None if cu is None else cu.numpy(), scale=0.25)
+    o = o.float().cpu().numpy()
+    got_pool = pool.float().cpu().numpy()
+    idx = p["state_indices"].numpy()
+    active = sorted(int(s) for s in idx if s > 0)
+    p0 = f(p["pool"])
+    for s in range(got_pool.shape[0]):
+        if s not in active:
+            assert np.array_equal(got_pool[s], p0[s]), f"slot {s} was written"
+    if dt == torch.float32 and pdt == torch.float32:
+        eo, ep = float(np.max(np.abs(o - ref_o))), float(np.max(np.abs(got_pool[active] - ref_pool[active])))
+        say(f"{name}: max|o|err {eo:.3g}  max|S|err {ep:.3g}")
+        assert eo <= FP32_ATOL and ep <= FP32_ATOL
+    else:
+        eo, ep = rel_rms(o, ref_o), rel_rms(got_pool[active], ref_pool[active])
+        say(f"{name}: rel_rms o {eo:.3g}  S {ep:.3g}")
+        assert eo <= BF16_RTOL and ep <= BF16_RTOL
+
+
+def test_recurrent_full_size(dev):
+    """The bench's recurrent workload (64 sequences of 16 tokens, H=32, K=V=128, bf16, float32 pool),
+    every sequence and head against the oracle."""
+    w = wl.recurrent_gdn()
+    say("recurrent: full-size workload")
+    pool = w.meta["pool"].to(dev).contiguous()
+    o, _ = sf.gdn_recurrent_fwd(w.q.to(dev), w.k.to(dev), w.v.to(dev), w.g.to(dev), w.beta.to(dev), pool,
+                                state_indices=w.meta["state_indices"].to(dev), scale=w.scale)
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    ref_o, ref_pool = oracle.gdn_recurrent_paged(f(w.q), f(w.k), f(w.v), f(w.g), f(w.beta), f(w.meta["pool"]),
+                                                 w.meta["state_indices"].numpy(), scale=w.scale)
+    eo = rel_rms(o.float().cpu().numpy(), ref_o)
+    ep = rel_rms(pool.cpu().numpy()[1:], ref_pool[1:])
+    say(f"recurrent_gdn: rel_rms o {eo:.3g}  S {ep:.3g}")
+    assert eo <= BF16_RTOL and ep <= BF16_RTOL
+    assert np.array_equal(pool[0].cpu().numpy(), f(w.meta["pool"])[0])

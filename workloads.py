@@ -24,6 +24,8 @@ and one decode workload (one token per sequence against a paged state pool):
 6. ``decode_gdn``     B=256 sequences, H=HK=32, K=V=128 (the packed workload's
                       heads), bf16 packed [Q | K | V] rows, float32 pool of 257
                       slots (slot 0 the null slot), every row active.
+7. ``recurrent_gdn``  64 sequences of 16 tokens, H=HK=32, K=V=128, bf16, on a
+                      float32 pool of 65 slots (token-by-token forward).
 
 Draw order inside one workload: q, k, v, gate noise, beta noise, h0, A, dt,
 sequence lengths.
@@ -37,7 +39,7 @@ import numpy as np
 import torch
 
 SEEDS = {"tiny_gdn": 101, "dense_gdn": 102, "varlen_gdn": 103, "long_gdn": 104, "ssd_gla": 105,
-         "decode_gdn": 106}
+         "decode_gdn": 106, "recurrent_gdn": 107}
 
 
 @dataclass
@@ -277,8 +279,23 @@ def decode_gdn(seed=SEEDS["decode_gdn"], *, B=256, H=32, HK=32, D=128):
     return DecodeWorkload("decode_gdn", H=H, HK=HK, K=D, V=D, scale=1.0 / np.sqrt(D), **d)
 
 
+def recurrent_gdn(seed=SEEDS["recurrent_gdn"], *, B=64, T=16, H=32, D=128):
+    """A short multi-token step for each of B sequences on a paged float32 pool (B + 1 slots, every
+    sequence loaded): q, k unit rows, v ~ N(0,1), g and beta as dense_gdn, pool ~ N(0, 0.02^2), slots
+    a random permutation of 1..B. The pages give no such batch: 64 sequences of 16 tokens with the
+    packed workload's heads is the reading taken."""
+    d = delta_rule_inputs(B=B, T=T, H=H, K=D, V=D, dtype=torch.bfloat16, seed=seed, gate_shift=2.0)
+    rng = d["rng"]
+    pool = _normal(rng, (B + 1, H, D, D)) * np.float32(0.02)
+    idx = rng.permutation(np.arange(1, B + 1)).astype(np.int32)
+    return Workload("recurrent_gdn", "gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], None, None,
+                    scale=1.0 / np.sqrt(D), chunk=0,
+                    meta={"pool": torch.from_numpy(pool), "state_indices": torch.from_numpy(idx)})
+
+
 CONFIGS = {"tiny_gdn": tiny_gdn, "dense_gdn": dense_gdn, "varlen_gdn": varlen_gdn,
-           "long_gdn": long_gdn, "ssd_gla": ssd_gla, "decode_gdn": decode_gdn}
+           "long_gdn": long_gdn, "ssd_gla": ssd_gla, "decode_gdn": decode_gdn,
+           "recurrent_gdn": recurrent_gdn}
 
 
 def to_f32(t):
