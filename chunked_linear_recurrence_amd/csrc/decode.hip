@@ -24,9 +24,10 @@
 // in registers from the first token to the last: a workgroup of four wavefronts owns 32 state
 // rows of one (sequence, head), eight lanes per row with K/8 consecutive key columns each, so
 // each row sum is a lane's own dot product plus three DPP lane permutations. The token operands
-// (q, k, the 32 values, the two gates) come in blocks of 16 tokens, moved into LDS with direct
-// loads one block ahead, so a token step waits on LDS, not on memory; outputs leave once per
-// block, 16 bytes per token and wavefront.
+// (q, k, the 32 values, the two gates) come in blocks of 16 tokens: the workgroup loads the next
+// block into registers while it computes the current one, then widens it to float32 in LDS once
+// for all 32 rows, so a token step waits on LDS, not on memory, and converts nothing; outputs
+// leave once per block, one row piece per token and wavefront.
 // The state comes from h0 (or zero) and goes to ht, or, with slot indices, from and back to a
 // paged pool.
 #include "sf_device.h"
@@ -132,37 +133,43 @@ constexpr int kRecWaves = 4;   // wavefronts per recurrent workgroup
 constexpr int kRecRows = kRecWaves * 64 / kRecLpr;  // state rows per workgroup (32)
 constexpr int kRecTok = 16;    // tokens per block staged in LDS
 
-// raw (unconverted) four-element vectors of the token operands, converted when used
+// raw (unconverted) four-element vectors of the token operands
 template <typename T> struct Raw;
 template <> struct Raw<float> {
     typedef f32x4 type;
+    static __device__ __forceinline__ type load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
     static __device__ __forceinline__ f32x4 cvt(type x) { return x; }
 };
 template <> struct Raw<bf16_t> {
     typedef i16x4 type;
+    static __device__ __forceinline__ type load(const bf16_t* p) { return *reinterpret_cast<const i16x4*>(p); }
     static __device__ __forceinline__ f32x4 cvt(type x) { return Elem<bf16_t>::unpack(x); }
 };
 
 // sum over the eight lanes of a row group with DPP: quad permutations (lane i reads lane i^1, then
 // i^2), then the half-row mirror (lane i reads lane 7-i of its eight)
+// (every source lane exists, so bound_ctrl changes nothing and lets each move fold into its add)
 __device__ __forceinline__ float row_group_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
     return x;
 }
 
-// LDS plan of one recurrent workgroup: two buffers of one token block each
-template <typename ET, int K>
+// a + x . y as four fused multiply-adds
+__device__ __forceinline__ float fma4(f32x4 x, f32x4 y, float a) {
+    return fmaf(x[3], y[3], fmaf(x[2], y[2], fmaf(x[1], y[1], fmaf(x[0], y[0], a))));
+}
+
+// LDS plan of one recurrent workgroup: one token block, widened to float32 once for all rows
+template <int K>
 struct RecLds {
-    static constexpr int RB = K * (int)sizeof(ET);           // bytes of one q or k row
-    static constexpr int QK = kRecTok * RB;                  // q (or k) rows of a block
-    static constexpr int VB = kRecTok * kRecRows * (int)sizeof(ET);  // the block's values of the 32 rows
-    static constexpr int OFF_Q = 0, OFF_K = QK, OFF_V = 2 * QK, OFF_G = OFF_V + VB;
-    static constexpr int BUF = OFF_G + 256;                  // g at +0, beta at +64 (floats)
-    static constexpr int OFF_O = 2 * BUF;                    // outputs of a block, per wavefront [16][8]
-    static constexpr int BYTES = OFF_O + kRecWaves * kRecTok * 8 * (int)sizeof(ET);
-    static_assert(QK % 1024 == 0 && VB % 1024 == 0, "block parts are whole 1 KB loads");
+    static constexpr int OFF_Q = 0;                                  // float [16][K]
+    static constexpr int OFF_K = OFF_Q + kRecTok * K * 4;            // float [16][K]
+    static constexpr int OFF_V = OFF_K + kRecTok * K * 4;            // float [16][32]
+    static constexpr int OFF_G = OFF_V + kRecTok * kRecRows * 4;     // float g[16], beta[16]
+    static constexpr int OFF_O = OFF_G + 2 * kRecTok * 4;            // float outputs [wave][16][8]
+    static constexpr int BYTES = OFF_O + kRecWaves * kRecTok * 8 * 4;
 };
 
 template <typename ET, typename PT, int K>
@@ -171,20 +178,30 @@ __global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
     const float* __restrict__ beta, const float* __restrict__ h0, float* __restrict__ ht, PT* __restrict__ pool,
     long long slot_stride, int num_slots, const int32_t* __restrict__ state_indices,
     const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cu, int T, int H, int HK, int V, float scale,
-    ET* __restrict__ out) {
-    typedef RecLds<ET, K> SM;
+    ET* __restrict__ out, int n_pairs) {
+    typedef RecLds<K> SM;
     constexpr int CPL = K / kRecLpr;  // key columns per lane: lanes 8r .. 8r+7 hold state row r of the wavefront
     constexpr int NV = CPL / 4;       // four-column vectors per lane
-    constexpr int EB = (int)sizeof(ET);
+    constexpr int NT = 64 * kRecWaves;
+    constexpr int NQ = kRecTok * K / 4 / NT;  // four-element q (and k) vectors each thread moves per block
+    static_assert(NQ >= 1 && kRecTok * K % (4 * NT) == 0, "block split");
     typedef typename Raw<ET>::type RawT;
     __shared__ __align__(16) uint8_t smem[SM::BYTES];
-    typedef __attribute__((address_space(3))) uint8_t lds_u8;
-    lds_u8* const lds = (lds_u8*)smem;
+    typedef __attribute__((address_space(3))) float lds_f;
+    typedef __attribute__((address_space(3))) f32x4 lds_f4;
+    lds_f* const sQ = (lds_f*)(smem + SM::OFF_Q);
+    lds_f* const sK = (lds_f*)(smem + SM::OFF_K);
+    lds_f* const sV = (lds_f*)(smem + SM::OFF_V);
+    lds_f* const sG = (lds_f*)(smem + SM::OFF_G);
 
+    // the nvb workgroups of one (sequence, head) share its q and k: they run on one XCD (whose L2
+    // then fetches those rows once); workgroups past the last pair of a padded grid exit
     const int nvb = V / kRecRows;
-    const int vb = blockIdx.x % nvb, nh = blockIdx.x / nvb;
+    int nh, vb;
+    xcd_split(blockIdx.x, nvb, nh, vb);
+    if (nh >= n_pairs) return;
     const int n = nh / H, h = nh - n * H, hk = h / (H / HK);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int rl = 8 * w + lane / kRecLpr;     // row within the workgroup's 32
     const int r0 = kRecRows * vb, row = r0 + rl;
     const int c0 = CPL * (lane % kRecLpr);
@@ -202,8 +219,8 @@ __global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
     if (pool) {
         const int slot = state_indices[n];
         if (slot <= 0 || slot >= num_slots) {  // null sequence: zero output rows, no state access
-            for (int t = bos + (int)threadIdx.x / kRecRows; t < eos; t += 64 * kRecWaves / kRecRows)
-                Io<ET>::store1(out + ((size_t)(b * T + t) * H + h) * V + r0 + threadIdx.x % kRecRows, 0.f);
+            for (int t = bos + tid / kRecRows; t < eos; t += NT / kRecRows)
+                Io<ET>::store1(out + ((size_t)(b * T + t) * H + h) * V + r0 + tid % kRecRows, 0.f);
             return;
         }
         slot_p = pool + (size_t)slot * (size_t)slot_stride + (size_t)h * V * K;
@@ -219,79 +236,84 @@ __global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
         S[i] = load_slot ? Io<PT>::load4(slot_p + soff + 4 * i)
                          : (h0p ? Io<float>::load4(h0p + soff + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f});
 
-    // one token block [t0, t0 + 16) into buffer bf with 16-byte direct loads (4-byte for the gates);
-    // tokens past the sequence's end repeat its last token (their results are never stored)
-    auto load_block = [&](int t0, int bf) __attribute__((always_inline)) {
-        lds_u8* B = lds + bf * SM::BUF;
+    // one token block [t0, t0 + 16) into registers: thread tid moves q and k vectors tid + 256 i,
+    // two values and (threads 0..31) one gate; tokens past the end repeat the last token (their
+    // results are never stored)
+    struct Blk {
+        RawT q[NQ], k[NQ];
+        float v0, v1, gb;
+    };
+    auto fetch = [&](int t0, Blk& x) __attribute__((always_inline)) {
         const int last = eos - 1;
-        for (int m = w; m < SM::QK / 1024; m += kRecWaves) {
-            const int off = 1024 * m + 16 * lane, tt = min(t0 + off / SM::RB, last), pc = off % SM::RB;
-            const size_t src = ((size_t)(b * T + tt) * HK + hk) * K * EB + pc;
-            load_lds16(reinterpret_cast<const uint8_t*>(q) + src, (uint8_t*)(B + SM::OFF_Q + 1024 * m));
-            load_lds16(reinterpret_cast<const uint8_t*>(k) + src, (uint8_t*)(B + SM::OFF_K + 1024 * m));
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int e = 4 * (tid + NT * i), tt = min(t0 + e / K, last);
+            const size_t src = ((size_t)(b * T + tt) * HK + hk) * K + e % K;
+            x.q[i] = Raw<ET>::load(q + src);
+            x.k[i] = Raw<ET>::load(k + src);
         }
-        constexpr int VROW = kRecRows * EB;  // bytes of the 32 values of one token
-        for (int m = w; m * 1024 < SM::VB; m += kRecWaves) {
-            const int off = 1024 * m + 16 * lane, tt = min(t0 + off / VROW, last), pc = off % VROW;
-            load_lds16(reinterpret_cast<const uint8_t*>(v) + ((size_t)(b * T + tt) * H + h) * V * EB + r0 * EB + pc,
-                       (uint8_t*)(B + SM::OFF_V + 1024 * m));
+        const int tv = min(t0 + tid / 16, last), rv = 2 * (tid % 16);
+        const ET* vp = v + ((size_t)(b * T + tv) * H + h) * V + r0 + rv;
+        x.v0 = Io<ET>::load1(vp);
+        x.v1 = Io<ET>::load1(vp + 1);
+        x.gb = 0.f;
+        if (tid < 2 * kRecTok) x.gb = (tid < kRecTok ? g : beta)[(size_t)(b * T + min(t0 + tid % kRecTok, last)) * H + h];
+    };
+    auto stage = [&](const Blk& x) __attribute__((always_inline)) {  // widen into LDS
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            *(lds_f4*)(sQ + 4 * (tid + NT * i)) = Raw<ET>::cvt(x.q[i]);
+            *(lds_f4*)(sK + 4 * (tid + NT * i)) = Raw<ET>::cvt(x.k[i]);
         }
-        if (w == 0) {  // lanes 0..15 the gates, 16..31 beta, the rest repeat them
-            const int tt = min(t0 + (lane & 15), last);
-            const float* src = ((lane >> 4) & 1 ? beta : g) + (size_t)(b * T + tt) * H + h;
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(B + SM::OFF_G), 4, 0, 0);
-        }
+        sV[2 * tid] = x.v0;
+        sV[2 * tid + 1] = x.v1;
+        if (tid < 2 * kRecTok) sG[tid] = x.gb;
     };
     const int nblk = (eos - bos + kRecTok - 1) / kRecTok;
-    if (nblk > 0) load_block(bos, 0);
-    lds_u8* const obuf = lds + SM::OFF_O + w * (kRecTok * 8 * EB);
+    Blk nb;
+    if (nblk > 0) fetch(bos, nb);
+    lds_f* const obuf = (lds_f*)(smem + SM::OFF_O) + w * (kRecTok * 8);
     for (int blk = 0; blk < nblk; ++blk) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // block blk landed for every wavefront; block blk-1's buffer is free again
         const int t0 = bos + blk * kRecTok, nt = min(kRecTok, eos - t0);
-        if (blk + 1 < nblk) load_block(t0 + kRecTok, (blk + 1) & 1);
-        const lds_u8* B = lds + (blk & 1) * SM::BUF;
+        __syncthreads();  // every wavefront is done with the previous block's LDS
+        stage(nb);
+        if (blk + 1 < nblk) fetch(t0 + kRecTok, nb);
+        __syncthreads();  // the block is in LDS
         for (int tt = 0; tt < nt; ++tt) {
-            const lds_u8* qr = B + SM::OFF_Q + tt * SM::RB + c0 * EB;
-            const lds_u8* kr = B + SM::OFF_K + tt * SM::RB + c0 * EB;
-            const float gamma = expf(*(const __attribute__((address_space(3))) float*)(B + SM::OFF_G + 4 * tt));
-            const float bt = *(const __attribute__((address_space(3))) float*)(B + SM::OFF_G + 64 + 4 * tt);
-            const lds_u8* vp = B + SM::OFF_V + (tt * kRecRows + rl) * EB;
-            const float vv = EB == 2 ? bf2f(*(const __attribute__((address_space(3))) bf16_t*)vp)
-                                     : *(const __attribute__((address_space(3))) float*)vp;
+            const lds_f* qr = sQ + tt * K + c0;
+            const lds_f* kr = sK + tt * K + c0;
+            const float gamma = expf(sG[tt]), bt = sG[kRecTok + tt], vv = sV[tt * kRecRows + rl];
             f32x4 kf[NV];
-            float sk = 0.f;
+            float sk0 = 0.f, sk1 = 0.f;  // two accumulation chains
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                kf[i] = Raw<ET>::cvt(*(const __attribute__((address_space(3))) RawT*)(kr + 4 * i * EB));
-                sk += dot4(S[i], kf[i]);
-            }
-            const float r = bt * (vv - gamma * row_group_sum(sk));
-            float so = 0.f;
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                S[i] = S[i] * gamma + kf[i] * r;
-                so += dot4(S[i], Raw<ET>::cvt(*(const __attribute__((address_space(3))) RawT*)(qr + 4 * i * EB)));
-            }
-            so = row_group_sum(so);
-            if (lane % kRecLpr == 0) {
-                const float ov = scale * so;
-                if constexpr (EB == 2)
-                    *(__attribute__((address_space(3))) bf16_t*)(obuf + (tt * 8 + lane / kRecLpr) * EB) = f2bf(ov);
+                kf[i] = *(const lds_f4*)(kr + 4 * i);
+                if (i & 1)
+                    sk1 = fma4(S[i], kf[i], sk1);
                 else
-                    *(__attribute__((address_space(3))) float*)(obuf + (tt * 8 + lane / kRecLpr) * EB) = ov;
+                    sk0 = fma4(S[i], kf[i], sk0);
             }
+            const float r = bt * (vv - gamma * row_group_sum(sk0 + sk1));
+            float so0 = 0.f, so1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[i][e] = fmaf(kf[i][e], r, S[i][e] * gamma);
+                if (i & 1)
+                    so1 = fma4(S[i], *(const lds_f4*)(qr + 4 * i), so1);
+                else
+                    so0 = fma4(S[i], *(const lds_f4*)(qr + 4 * i), so0);
+            }
+            const float so = row_group_sum(so0 + so1);
+            if (lane % kRecLpr == 0) obuf[tt * 8 + lane / kRecLpr] = scale * so;
         }
         // the wavefront's 8 outputs of each token of the block: one row piece per lane
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (lane < nt) {
             ET* dst = out + ((size_t)(b * T + t0 + lane) * H + h) * V + r0 + 8 * w;
-            if constexpr (EB == 2)
-                *reinterpret_cast<u128*>(dst) = *(const __attribute__((address_space(3))) u128*)(obuf + lane * 16);
-            else {
-                *reinterpret_cast<u128*>(dst) = *(const __attribute__((address_space(3))) u128*)(obuf + lane * 32);
-                *reinterpret_cast<u128*>(dst + 4) = *(const __attribute__((address_space(3))) u128*)(obuf + lane * 32 + 16);
-            }
+            const f32x4 lo = *(const lds_f4*)(obuf + 8 * lane), hi = *(const lds_f4*)(obuf + 8 * lane + 4);
+            Io<ET>::store4(dst, lo);
+            Io<ET>::store4(dst + 4, hi);
         }
     }
 #pragma unroll
@@ -308,19 +330,20 @@ hipError_t launch_rec_typed(int K, const void* q, const void* k, const void* v, 
                             const float* h0, float* ht, void* pool, long long slot_stride, int num_slots,
                             const int32_t* idx, const uint8_t* has_init, const int32_t* cu, int N, int T, int H,
                             int HK, int V, float scale, void* out, hipStream_t s) {
-    const dim3 grid((unsigned)N * (unsigned)H * (unsigned)(V / kRecRows)), block(64 * kRecWaves);
+    const unsigned pairs = (unsigned)N * (unsigned)H;
+    const dim3 grid(((pairs + 7) / 8) * 8 * (unsigned)(V / kRecRows)), block(64 * kRecWaves);
     const ET *qq = static_cast<const ET*>(q), *kk = static_cast<const ET*>(k), *vv = static_cast<const ET*>(v);
     PT* p = static_cast<PT*>(pool);
     ET* o = static_cast<ET*>(out);
     if (K == 64)
         gdn_recurrent_kernel<ET, PT, 64><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride, num_slots,
-                                                                idx, has_init, cu, T, H, HK, V, scale, o);
+                                                                idx, has_init, cu, T, H, HK, V, scale, o, (int)pairs);
     else if (K == 128)
         gdn_recurrent_kernel<ET, PT, 128><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride,
-                                                                 num_slots, idx, has_init, cu, T, H, HK, V, scale, o);
+                                                                 num_slots, idx, has_init, cu, T, H, HK, V, scale, o, (int)pairs);
     else
         gdn_recurrent_kernel<ET, PT, 256><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride,
-                                                                 num_slots, idx, has_init, cu, T, H, HK, V, scale, o);
+                                                                 num_slots, idx, has_init, cu, T, H, HK, V, scale, o, (int)pairs);
     return hipGetLastError();
 }
 
