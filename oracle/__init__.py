@@ -25,6 +25,8 @@ What each function follows (pages by title and section):
   entry and the section "Gate Transforms" (``decode.py``, numpy float64).
 * ``gdn_recurrent_paged``  the ``recurrent_gdn`` entry with a paged state pool:
   slot gather and scatter around ``gdn_forward`` (``decode.py``).
+* ``gate_transform``  the section "Gate Transforms": both kinds, per-head and
+  per-channel gates (``decode.py``).
 
 Pins: tests/test_oracle.py checks every function against closed forms,
 brute-force products or invariants that do not reuse this code.
@@ -194,4 +196,4 @@ def chunked_forward(kind, q, k, v, g, beta=None, h0=None, cu_seqlens=None, scale
     return out, ht
 
 
-from .decode import gdn_decode, gdn_recurrent_paged  # noqa: E402  (numpy float64, no C part)
+from .decode import gate_transform, gdn_decode, gdn_recurrent_paged  # noqa: E402  (numpy float64, no C part)

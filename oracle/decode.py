@@ -126,3 +126,26 @@ def gdn_recurrent_paged(q, k, v, g, beta, state_pool, state_indices, has_initial
                 out[0, cu[n]:cu[n + 1]] = 0.0
     return out, pool
 
+
+def gate_transform(raw, A_log, dt_bias, kind, lower_bound=None):
+    """Raw gate projections to natural-log decays (attention-gym "Linear Attention", section "Gate
+    Transforms"), float64. raw [..., H] with dt_bias [H] (per-head gates) or raw [..., H, D] with
+    dt_bias [H, D] (per-channel gates); A_log [H].
+      "softplus": -exp(A_log) * softplus(raw + dt_bias)
+      "bounded":  lower_bound * sigmoid(exp(A_log) * (raw + dt_bias))"""
+    raw = np.asarray(raw, dtype=np.float64)
+    A_log = np.asarray(A_log, dtype=np.float64)
+    dt_bias = np.asarray(dt_bias, dtype=np.float64)
+    H = A_log.shape[0]
+    per_channel = dt_bias.ndim == 2
+    assert raw.shape[-2 if per_channel else -1] == H and dt_bias.shape[0] == H
+    amp = np.exp(A_log)[:, None] if per_channel else np.exp(A_log)
+    x = raw + dt_bias
+    if kind == "softplus":
+        assert lower_bound is None
+        return -amp * softplus(x)
+    if kind == "bounded":
+        assert lower_bound is not None and np.isfinite(lower_bound) and lower_bound <= 0
+        return lower_bound * write_gate(amp * x)
+    raise ValueError(kind)
+

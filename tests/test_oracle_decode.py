@@ -223,3 +223,31 @@ def test_paged_recurrent_packed_edge_cases():
         np.testing.assert_allclose(out[:, sl], o1, rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(new[slot], h1[0], rtol=1e-12, atol=1e-14)
 
+
+def test_gate_transform_pins():
+    """Closed forms of both kinds: softplus(0) = ln 2 and sigmoid(0) = 1/2; the bounded kind tends
+    to lower_bound and to 0 at the two ends; A_log scales the softplus kind's amplitude and the
+    bounded kind's slope; per-channel gates with D = 1 equal per-head gates."""
+    H = 3
+    A = np.log(np.array([1.0, 2.0, 4.0]))
+    raw = np.zeros((2, 5, H))
+    np.testing.assert_allclose(oracle.gate_transform(raw, A, np.zeros(H), "softplus"),
+                               np.broadcast_to(-np.array([1.0, 2.0, 4.0]) * math.log(2.0), raw.shape), rtol=1e-15)
+    np.testing.assert_allclose(oracle.gate_transform(raw, A, np.zeros(H), "bounded", lower_bound=-5.0),
+                               np.full(raw.shape, -2.5), rtol=1e-15)
+    big = np.full((1, 1, H), 60.0)
+    np.testing.assert_allclose(oracle.gate_transform(big, A, np.zeros(H), "bounded", lower_bound=-3.0), -3.0, rtol=1e-15)
+    assert np.all(np.abs(oracle.gate_transform(-big, A, np.zeros(H), "bounded", lower_bound=-3.0)) < 1e-20)
+    # the bias shifts the pre-activation: raw = ln 3, bias = -ln 3 gives the zero point again
+    np.testing.assert_allclose(oracle.gate_transform(np.full((1, 1, H), math.log(3.0)), np.zeros(H),
+                                                     np.full(H, -math.log(3.0)), "softplus"), -math.log(2.0), rtol=1e-15)
+    # the slope of the bounded kind is exp(A_log): sigmoid(2 * ln 3 / 2) = sigmoid(ln 3) = 3/4
+    np.testing.assert_allclose(oracle.gate_transform(np.full((1, 1, 1), 0.5 * math.log(3.0)), np.array([math.log(2.0)]),
+                                                     np.zeros(1), "bounded", lower_bound=-1.0), -0.75, rtol=1e-15)
+    rng = np.random.default_rng(9)
+    r = rng.standard_normal((2, 4, H))
+    bias = rng.standard_normal(H)
+    for kind, lb in (("softplus", None), ("bounded", -5.0)):
+        np.testing.assert_array_equal(oracle.gate_transform(r[..., None], A, bias[:, None], kind, lb)[..., 0],
+                                      oracle.gate_transform(r, A, bias, kind, lb))
+
