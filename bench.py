@@ -19,7 +19,8 @@ baseline, not a target). Beside the published HBM peak, the roofline objects
 carry measured_peak: the bandwidth a plain 1 GiB device-to-device copy reaches
 on the same GPU (read plus write bytes), and the fraction of that.
 
-Other workloads (--workload varlen_gdn | long_gdn | ssd_gla | tiny_gdn | decode_gdn | recurrent_gdn) are for
+Other workloads (--workload varlen_gdn | long_gdn | ssd_gla | tiny_gdn | decode_gdn | recurrent_gdn |
+gate_transform) are for
 measurement only; the headline line is the default one. decode_gdn times one sf_gdn_decode call
 (one token for each of 256 sequences against a 514 MB float32 state pool, which is larger than
 the last-level cache, so it runs on one input set).
@@ -67,6 +68,8 @@ def algorithmic_bytes(w, kernel):
     written, V*K float32 each."""
     if kernel in ("gdn_decode", "decode_path"):
         return decode_bytes(w)
+    if kernel in ("gate_transform", "gate_path"):   # raw in, float32 out, the per-head parameters
+        return w.raw.numel() * (w.raw.element_size() + 4) + (w.A_log.numel() + w.dt_bias.numel()) * 4
     eb = w.q.element_size()
     tok = w.tokens
     qk = 2 * tok * w.HK * w.K * eb
@@ -107,6 +110,8 @@ def traffic_from_profile(kernel, workload):
 def make_sets(w, dev, rotate):
     import torch
     import workloads as wl
+    if isinstance(w, wl.GateWorkload):
+        return [{n: getattr(w, n).to(dev).contiguous() for n in ("raw", "A_log", "dt_bias")} for _ in range(rotate)]
     if isinstance(w, wl.DecodeWorkload):
         s = {n: (None if getattr(w, n) is None else getattr(w, n).to(dev).contiguous())
              for n in ("packed_qkv", "raw_gate", "raw_beta", "A_log", "dt_bias", "pool", "state_indices",
@@ -128,7 +133,10 @@ def make_sets(w, dev, rotate):
 
 def step_fn(w):
     import chunked_linear_recurrence_amd as sf
-    if w.name == "decode_gdn":
+    if w.name == "gate_transform":
+        def step(s):
+            return sf.gate_transform(s["raw"], s["A_log"], s["dt_bias"], kind=w.kind, lower_bound=w.lower_bound)
+    elif w.name == "decode_gdn":
         def step(s):
             return sf.gdn_decode(s["packed_qkv"], s["raw_gate"], s["raw_beta"], s["A_log"], s["dt_bias"], s["pool"],
                                  s["state_indices"], has_initial_state=s["has_initial_state"], scale=w.scale,
@@ -161,6 +169,13 @@ def cpu_baseline(w):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     threads = min(threads, len(os.sched_getaffinity(0)))
     f = wl.to_f32
+    if isinstance(w, wl.GateWorkload):
+        log("cpu_baseline: float64 gate-transform oracle (numpy) ...")
+        t0 = time.perf_counter()
+        oracle.gate_transform(f(w.raw), f(w.A_log), f(w.dt_bias), w.kind, w.lower_bound)
+        dt = time.perf_counter() - t0
+        return {"value": w.tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"the whole {w.name} workload ({w.raw.numel()} gates), one float64 pass, {dt:.2f} s wall"}
     if isinstance(w, wl.DecodeWorkload):
         log("cpu_baseline: float64 decode oracle (numpy, one step) ...")
         t0 = time.perf_counter()
@@ -217,7 +232,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="input sets cycled through (cache defeat)")
     ap.add_argument("--workload", default="dense_gdn",
                     choices=["dense_gdn", "tiny_gdn", "varlen_gdn", "long_gdn", "ssd_gla", "decode_gdn",
-                             "recurrent_gdn"])
+                             "recurrent_gdn", "gate_transform"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the second pass, whose launches are bracketed with HIP events")
@@ -291,7 +306,8 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(dom, w.name),
                 "kernel": dom, "avg_us": round(avg_s * 1e6, 2), "algorithmic_bytes": ab}
     decode = isinstance(w, wl.DecodeWorkload)
-    path_bytes = algorithmic_bytes(w, "decode_path" if decode else "path")
+    gate = isinstance(w, wl.GateWorkload)
+    path_bytes = algorithmic_bytes(w, "decode_path" if decode else "gate_path" if gate else "path")
     path_ach = path_bytes / (elapsed / args.steps) / 1e9
     copy_gbs = None if args.no_copy_peak else measured_copy_gbs(dev)
     if roof is not None and copy_gbs:
@@ -302,9 +318,11 @@ def main():
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if (w.packed_qkv if decode else w.q).dtype == torch.bfloat16 else "f32",
+        "dtype": "bf16" if (w.packed_qkv if decode else w.raw if gate else w.q).dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
-        "config": ({"workload": w.name, "B": w.B, "H": w.H, "HK": w.HK, "K": w.K, "V": w.V,
+        "config": ({"workload": w.name, "shape": list(w.raw.shape), "kind": w.kind, "tokens": w.tokens,
+                    "rotate": len(sets)} if gate else
+                   {"workload": w.name, "B": w.B, "H": w.H, "HK": w.HK, "K": w.K, "V": w.V,
                     "pool": "f32" if w.pool.dtype == torch.float32 else "bf16", "num_slots": w.pool.shape[0],
                     "tokens": w.tokens, "rotate": len(sets)} if decode else
                    {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HK": w.HK, "K": w.K, "V": w.V,

@@ -24,6 +24,8 @@ Functions (same names as the C entry points, without the ``sf_`` prefix):
 * ``gdn_recurrent_fwd`` token-by-token Gated Delta Rule forward, optionally on a
                         paged state pool (attention-gym "Linear Attention",
                         recurrent_gdn).
+* ``gate_transform``    raw gate projections to float32 natural-log decays
+                        (attention-gym "Linear Attention", "Gate Transforms").
 """
 from __future__ import annotations
 
@@ -40,12 +42,14 @@ LIB_PATH = os.path.join(_HERE, "libsf.so")
 SF_OK, SF_ERR_INVALID, SF_ERR_UNSUPPORTED, SF_ERR_HIP, SF_ERR_WORKSPACE = range(5)
 SF_F32, SF_BF16 = 0, 1
 SF_KIND_GDN, SF_KIND_GLA = 0, 1
+SF_GATE_SOFTPLUS, SF_GATE_BOUNDED = 0, 1
+GATE_KINDS = {"softplus": SF_GATE_SOFTPLUS, "bounded": SF_GATE_BOUNDED}
 KINDS = {"gdn": SF_KIND_GDN, "gla": SF_KIND_GLA}
 
 EXPORTED = (
     "sf_version", "sf_last_error", "sf_gdn_chunk_fwd_workspace", "sf_gdn_chunk_fwd",
     "sf_gla_chunk_fwd", "sf_segment_summary_workspace", "sf_segment_summary",
-    "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_gdn_decode", "sf_gdn_recurrent_fwd",
+    "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_gdn_decode", "sf_gdn_recurrent_fwd", "sf_gate_transform",
     "sf_timing_enable", "sf_timing_collect",
 )
 
@@ -93,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.sf_gdn_recurrent_fwd.restype = I
     L.sf_gdn_recurrent_fwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, I, I,
                                        ctypes.c_longlong, P, P, P]
+    L.sf_gate_transform.restype = I
+    L.sf_gate_transform.argtypes = [I, P, P, P, ctypes.c_longlong, I, I, I, F, P, P]
     L.sf_timing_enable.restype = I
     L.sf_timing_enable.argtypes = [I]
     L.sf_timing_collect.restype = I
@@ -408,6 +414,39 @@ def gdn_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_cache, stat
     _check(lib().sf_gdn_decode(_dt(packed_qkv), _ptr(packed_qkv), _ptr(raw_gate), _ptr(raw_beta), _ptr(A_log),
                                _ptr(dt_bias), _ptr(state_cache), pool_dt, NS, stride0, _ptr(state_indices),
                                _ptr(has_initial_state), B, H, HK, K, V, float(scale), _ptr(out), _stream()))
+    return out
+
+
+def gate_transform(raw_gate, A_log, dt_bias, *, kind, lower_bound=None):
+    """Raw gate projections to float32 natural-log decays. raw_gate [..., H] with dt_bias [H]
+    (per-head) or [..., H, D] with dt_bias [H, D] (per-channel), bf16 or float32; A_log [H] float32.
+    kind "softplus": -exp(A_log) softplus(raw + dt_bias); "bounded": lower_bound sigmoid(exp(A_log)
+    (raw + dt_bias)), with a finite lower_bound <= 0 (required by "bounded", rejected by "softplus")."""
+    if kind not in GATE_KINDS:
+        raise ValueError(f"kind must be one of {sorted(GATE_KINDS)}, got {kind!r}")
+    if kind == "softplus" and lower_bound is not None:
+        raise ValueError("lower_bound is rejected by the softplus kind")
+    if kind == "bounded" and (lower_bound is None or not math.isfinite(lower_bound) or lower_bound > 0):
+        raise ValueError("the bounded kind needs a finite lower_bound <= 0")
+    _need(raw_gate, "raw_gate")
+    dev = raw_gate.device
+    _need(A_log, "A_log", dtype=torch.float32, ndim=1, device=dev)
+    _need(dt_bias, "dt_bias", dtype=torch.float32, device=dev)
+    H = A_log.numel()
+    if dt_bias.dim() == 1:
+        D = 1
+        if raw_gate.shape[-1] != H or dt_bias.numel() != H:
+            raise ValueError(f"per-head gates: raw_gate [..., {H}] and dt_bias [{H}]")
+    elif dt_bias.dim() == 2:
+        D = dt_bias.shape[1]
+        if raw_gate.dim() < 2 or tuple(raw_gate.shape[-2:]) != (H, D) or dt_bias.shape[0] != H:
+            raise ValueError(f"per-channel gates: raw_gate [..., {H}, {D}] and dt_bias [{H}, {D}]")
+    else:
+        raise ValueError("dt_bias must be [H] or [H, D]")
+    rows = raw_gate.numel() // (H * D)
+    out = torch.empty(raw_gate.shape, dtype=torch.float32, device=dev)
+    _check(lib().sf_gate_transform(_dt(raw_gate), _ptr(raw_gate), _ptr(A_log), _ptr(dt_bias), rows, H, D,
+                                   GATE_KINDS[kind], float(lower_bound or 0.0), _ptr(out), _stream()))
     return out
 
 

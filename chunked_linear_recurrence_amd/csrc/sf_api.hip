@@ -315,6 +315,26 @@ sf_status sf_state_scan(sf_kind kind, const float* M, const float* S_ext, const 
     return hip_status(e, "sf_state_scan launch");
 }
 
+sf_status sf_gate_transform(sf_dtype dt, const void* raw, const float* A_log, const float* dt_bias, long long rows,
+                            int H, int D, sf_gate_kind kind, float lower_bound, float* out, void* stream) {
+    if (dt != SF_F32 && dt != SF_BF16) return fail(SF_ERR_INVALID, "dtype must be SF_F32 or SF_BF16");
+    if (kind != SF_GATE_SOFTPLUS && kind != SF_GATE_BOUNDED)
+        return fail(SF_ERR_INVALID, "kind must be SF_GATE_SOFTPLUS or SF_GATE_BOUNDED");
+    if (rows < 0 || H <= 0 || D <= 0) return fail(SF_ERR_INVALID, "sizes must be positive (rows=%lld H=%d D=%d)", rows, H, D);
+    if (kind == SF_GATE_BOUNDED && !(lower_bound <= 0.f && lower_bound > -3.0e38f))
+        return fail(SF_ERR_INVALID, "the bounded kind needs a finite lower_bound <= 0 (got %g)", (double)lower_bound);
+    if ((long long)H * D > kMaxElems || rows > (1LL << 40) / ((long long)H * D))
+        return fail(SF_ERR_UNSUPPORTED, "too many elements");
+    if (rows == 0) return SF_OK;
+    if (!raw || !A_log || !dt_bias || !out) return fail(SF_ERR_INVALID, "raw, A_log, dt_bias and out must not be NULL");
+    if (reinterpret_cast<uintptr_t>(raw) % (dt == SF_BF16 ? 8 : 16) != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
+        return fail(SF_ERR_INVALID, "raw must be %d-byte and out 16-byte aligned", dt == SF_BF16 ? 8 : 16);
+    hipError_t e = sf::launch_gate_transform(dt == SF_BF16, kind == SF_GATE_BOUNDED, raw, A_log, dt_bias,
+                                             (long)(rows * H * D), H, D, lower_bound, out,
+                                             static_cast<hipStream_t>(stream));
+    return hip_status(e, "sf_gate_transform launch");
+}
+
 sf_status sf_gdn_recurrent_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
                                const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B, int T,
                                int H, int HK, int K, int V, float scale, void* out, float* ht, void* state_pool,

@@ -75,6 +75,10 @@ hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const v
                       float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages = 3,
                       int pre_w = -1);
 
+// Gate transform (gates.hip): n elements of raw [rows, H, D] -> float32 decays.
+hipError_t launch_gate_transform(bool bf16, bool bounded, const void* raw, const float* A_log, const float* dt_bias,
+                                 long n, int H, int D, float lower_bound, float* out, hipStream_t s);
+
 // Token-by-token delta-rule forward (decode.hip): the state from h0 (or zero) to ht, or, when
 // pool is non-null, from and back to the slots state_indices name (pool_bf16: its element type).
 hipError_t launch_gdn_recurrent(bool bf16, bool pool_bf16, const void* q, const void* k, const void* v,

@@ -195,6 +195,25 @@ sf_status sf_gdn_segmented_fwd(sf_dtype dt, const void *q, const void *k, const 
                                void *out, float *ht, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* Gate transform kinds (attention-gym "Linear Attention", section "Gate Transforms"). */
+typedef enum { SF_GATE_SOFTPLUS = 0, SF_GATE_BOUNDED = 1 } sf_gate_kind;
+
+/*
+ * Gate transform: raw gate projections to float32 natural-log decays
+ * (attention-gym "Linear Attention", section "Gate Transforms"). For element e
+ * of raw [rows, H, D] (D = 1: per-head gates [rows, H], dt_bias [H];
+ * D > 1: per-channel gates, dt_bias [H, D]), j = e mod (H*D), h = j / D:
+ *   SF_GATE_SOFTPLUS: out[e] = -exp(A_log[h]) * softplus(raw[e] + dt_bias[j])
+ *   SF_GATE_BOUNDED:  out[e] = lower_bound * sigmoid(exp(A_log[h]) * (raw[e] + dt_bias[j]))
+ * raw in dt (rows = the product of the leading dimensions, e.g. B*T), 8-byte
+ * (bf16) or 16-byte (float32) aligned; A_log [H] and dt_bias float32; out
+ * [rows, H, D] float32, 16-byte aligned. lower_bound is read by the bounded
+ * kind only and must be finite and <= 0 there. Arithmetic is float32.
+ */
+sf_status sf_gate_transform(sf_dtype dt, const void *raw, const float *A_log, const float *dt_bias,
+                            long long rows, int H, int D, sf_gate_kind kind, float lower_bound,
+                            float *out, void *stream);
+
 /*
  * Token-by-token Gated Delta Rule forward (attention-gym "Linear Attention":
  * the recurrent_gdn entry; the token rule of the section "Gated Delta Rule").

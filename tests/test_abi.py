@@ -196,6 +196,23 @@ def test_recurrent_rejects_invalid_arguments(L):
     assert st == sf.SF_ERR_INVALID and "NULL" in err
 
 
+def test_gate_transform_rejects_invalid_arguments(L):
+    call = lambda dt=sf.SF_BF16, kind=sf.SF_GATE_BOUNDED, lb=-5.0, raw=FAKE * 16, out=FAKE * 16, H=4, D=1: \
+        L.sf_gate_transform(dt, raw, FAKE, FAKE, 8, H, D, kind, lb, out, None)
+    assert call(kind=7) == sf.SF_ERR_INVALID
+    assert call(lb=1.0) == sf.SF_ERR_INVALID
+    assert call(lb=float("-inf")) == sf.SF_ERR_INVALID
+    assert call(lb=float("nan")) == sf.SF_ERR_INVALID
+    assert call(raw=FAKE * 16 + 4) == sf.SF_ERR_INVALID          # misaligned
+    assert call(raw=None) == sf.SF_ERR_INVALID
+    assert call(H=0) == sf.SF_ERR_INVALID
+    assert L.sf_gate_transform(sf.SF_F32, None, None, None, 0, 4, 1, sf.SF_GATE_SOFTPLUS, 0.0, None, None) == sf.SF_OK
+    with pytest.raises(ValueError, match="lower_bound"):
+        sf.gate_transform(None, None, None, kind="softplus", lower_bound=-1.0)
+    with pytest.raises(ValueError, match="kind"):
+        sf.gate_transform(None, None, None, kind="linear")
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 64, 2, 64)

@@ -26,6 +26,7 @@ and one decode workload (one token per sequence against a paged state pool):
                       slots (slot 0 the null slot), every row active.
 7. ``recurrent_gdn``  64 sequences of 16 tokens, H=HK=32, K=V=128, bf16, on a
                       float32 pool of 65 slots (token-by-token forward).
+8. ``gate_transform`` per-channel raw gates [2, 16384, 16, 128] bf16, softplus kind.
 
 Draw order inside one workload: q, k, v, gate noise, beta noise, h0, A, dt,
 sequence lengths.
@@ -39,7 +40,7 @@ import numpy as np
 import torch
 
 SEEDS = {"tiny_gdn": 101, "dense_gdn": 102, "varlen_gdn": 103, "long_gdn": 104, "ssd_gla": 105,
-         "decode_gdn": 106, "recurrent_gdn": 107}
+         "decode_gdn": 106, "recurrent_gdn": 107, "gate_transform": 108}
 
 
 @dataclass
@@ -293,9 +294,41 @@ def recurrent_gdn(seed=SEEDS["recurrent_gdn"], *, B=64, T=16, H=32, D=128):
                     meta={"pool": torch.from_numpy(pool), "state_indices": torch.from_numpy(idx)})
 
 
+@dataclass
+class GateWorkload:
+    name: str
+    raw: torch.Tensor       # [..., H] or [..., H, D]
+    A_log: torch.Tensor     # [H] float32
+    dt_bias: torch.Tensor   # [H] or [H, D] float32
+    kind: str
+    lower_bound: Optional[float] = None
+
+    @property
+    def tokens(self) -> int:
+        return int(np.prod(self.raw.shape[:-2 if self.dt_bias.dim() == 2 else -1]))
+
+
+def gate_inputs(*, shape, H, D=None, dtype=torch.bfloat16, seed=0):
+    """raw ~ N(0,1) of the given shape; A_log = log U(1, 16) per head; dt_bias ~ N(-3, 1) per head
+    (or per head and channel)."""
+    rng = np.random.default_rng(seed)
+    raw = _normal(rng, shape)
+    A_log = np.log(rng.uniform(1.0, 16.0, size=H)).astype(np.float32)
+    dt_bias = (rng.standard_normal(H if D is None else (H, D)) - 3.0).astype(np.float32)
+    return dict(raw=_cast(raw, dtype), A_log=torch.from_numpy(A_log), dt_bias=torch.from_numpy(dt_bias))
+
+
+def gate_transform(seed=SEEDS["gate_transform"], *, B=2, T=16384, H=16, D=128):
+    """Per-channel raw gates of a long bf16 batch through the softplus kind. The pages give no
+    standalone size for this step: the long scalar-gate batch's token count with the dense
+    workload's heads and head width is the reading taken."""
+    d = gate_inputs(shape=(B, T, H, D), H=H, D=D, seed=seed)
+    return GateWorkload("gate_transform", kind="softplus", **d)
+
+
 CONFIGS = {"tiny_gdn": tiny_gdn, "dense_gdn": dense_gdn, "varlen_gdn": varlen_gdn,
            "long_gdn": long_gdn, "ssd_gla": ssd_gla, "decode_gdn": decode_gdn,
-           "recurrent_gdn": recurrent_gdn}
+           "recurrent_gdn": recurrent_gdn, "gate_transform": gate_transform}
 
 
 def to_f32(t):
