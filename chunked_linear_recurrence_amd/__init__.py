@@ -24,6 +24,8 @@ Functions (same names as the C entry points, without the ``sf_`` prefix):
 * ``gdn_recurrent_fwd`` token-by-token Gated Delta Rule forward, optionally on a
                         paged state pool (attention-gym "Linear Attention",
                         recurrent_gdn).
+* ``paged_gdn_chunk_fwd`` chunk forward on a paged state cache (attention-gym
+                        "Linear Attention", paged_chunk_gdn).
 * ``gate_transform``    raw gate projections to float32 natural-log decays
                         (attention-gym "Linear Attention", "Gate Transforms").
 """
@@ -50,6 +52,7 @@ EXPORTED = (
     "sf_version", "sf_last_error", "sf_gdn_chunk_fwd_workspace", "sf_gdn_chunk_fwd",
     "sf_gla_chunk_fwd", "sf_segment_summary_workspace", "sf_segment_summary",
     "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_gdn_decode", "sf_gdn_recurrent_fwd", "sf_gate_transform",
+    "sf_paged_gdn_chunk_fwd_workspace", "sf_paged_gdn_chunk_fwd",
     "sf_timing_enable", "sf_timing_collect",
 )
 
@@ -97,6 +100,11 @@ def lib() -> ctypes.CDLL:
     L.sf_gdn_recurrent_fwd.restype = I
     L.sf_gdn_recurrent_fwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, I, I,
                                        ctypes.c_longlong, P, P, P]
+    L.sf_paged_gdn_chunk_fwd_workspace.restype = Z
+    L.sf_paged_gdn_chunk_fwd_workspace.argtypes = [I, I, I, I, I, I, I, I]
+    L.sf_paged_gdn_chunk_fwd.restype = I
+    L.sf_paged_gdn_chunk_fwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, I, I, ctypes.c_longlong,
+                                         P, P, P, Z, P]
     L.sf_gate_transform.restype = I
     L.sf_gate_transform.argtypes = [I, P, P, P, ctypes.c_longlong, I, I, I, F, P, P]
     L.sf_timing_enable.restype = I
@@ -359,6 +367,33 @@ def gdn_recurrent_fwd(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, 
                                       _ptr(initial_state), pool_dt, NS, stride0, _ptr(state_indices),
                                       _ptr(has_initial_state), _stream()))
     return out, None
+
+
+def paged_gdn_chunk_fwd(q, k, v, g, beta, state_cache, state_indices, *, cu_seqlens=None, has_initial_state=None,
+                        scale=None):
+    """Delta-rule chunk forward advancing a paged state cache in place (inference prefill). state_cache
+    [num_slots, H, V, K] float32 or bf16; state_indices [N] int32 (<= 0: zero output, cache untouched);
+    has_initial_state [N] bool or None. Returns the output [B, T, H, V] in q.dtype."""
+    B, T, H, HK, K, V, N = _token_args(q, k, v, g, beta, None, cu_seqlens)
+    dev = q.device
+    _need(state_indices, "state_indices", dtype=torch.int32, ndim=1, device=dev)
+    if state_indices.numel() != N:
+        raise ValueError(f"state_indices must have {N} entries")
+    if has_initial_state is not None:
+        _need(has_initial_state, "has_initial_state", dtype=torch.bool, ndim=1, device=dev)
+        if has_initial_state.numel() != N:
+            raise ValueError(f"has_initial_state must have {N} entries")
+    NS, stride0, pool_dt = _pool_layout(state_cache, H, V, K, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+    dt = _dt(q)
+    nbytes = lib().sf_paged_gdn_chunk_fwd_workspace(dt, B, T, H, K, V, N, int(cu_seqlens is not None))
+    ws = _workspace(nbytes, dev)
+    _check(lib().sf_paged_gdn_chunk_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, B, T,
+                                        H, HK, K, V, float(scale), _ptr(out), _ptr(state_cache), pool_dt, NS, stride0,
+                                        _ptr(state_indices), _ptr(has_initial_state), _ptr(ws), nbytes, _stream()))
+    return out
 
 
 def gdn_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_cache, state_indices, *,

@@ -315,6 +315,67 @@ sf_status sf_state_scan(sf_kind kind, const float* M, const float* S_ext, const 
     return hip_status(e, "sf_state_scan launch");
 }
 
+namespace {
+// paged chunk forward: the chunk path's workspace, then float32 entry and exit states
+struct PagedWorkspace {
+    sf::GdnWorkspace chunk;
+    float *h0, *ht;
+    size_t bytes;
+};
+PagedWorkspace paged_layout(void* base, int eb, int B, int T, int H, int K, int V, int N, bool packed) {
+    PagedWorkspace w{};
+    w.chunk = sf::gdn_workspace_layout(base, eb, B, T, H, N, packed);
+    size_t off = w.chunk.bytes;
+    uint8_t* p = static_cast<uint8_t*>(base);
+    const size_t st = sf::align256(sizeof(float) * (size_t)N * H * V * K);
+    w.h0 = reinterpret_cast<float*>(p ? p + off : nullptr);
+    off += st;
+    w.ht = reinterpret_cast<float*>(p ? p + off : nullptr);
+    off += st;
+    w.bytes = off;
+    return w;
+}
+}  // namespace
+
+size_t sf_paged_gdn_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N, int packed) {
+    if ((dt != SF_F32 && dt != SF_BF16) || B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0 || N < 0) return 0;
+    return paged_layout(nullptr, elem_bytes(dt), B, T, H, K, V, N, packed != 0).bytes;
+}
+
+sf_status sf_paged_gdn_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const int32_t* cu_seqlens, int N, int B, int T, int H, int HK, int K,
+                                 int V, float scale, void* out, void* state_pool, sf_dtype pool_dt, int num_slots,
+                                 long long slot_stride, const int32_t* state_indices, const uint8_t* has_initial_state,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
+    if (st != SF_OK) return st;
+    if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
+    if (K != V || (K != 64 && K != 128))
+        return fail(SF_ERR_UNSUPPORTED, "delta-rule kernels are built for K == V in {64, 128} (K=%d V=%d)", K, V);
+    if (pool_dt != SF_F32 && pool_dt != SF_BF16) return fail(SF_ERR_INVALID, "pool dtype must be SF_F32 or SF_BF16");
+    const long long blk = (long long)H * V * K;
+    if (num_slots < 0 || slot_stride < blk || slot_stride % 4 != 0)
+        return fail(SF_ERR_INVALID, "slot_stride %lld must be a multiple of 4 and at least H*V*K = %lld", slot_stride, blk);
+    if (!state_pool || !state_indices) return fail(SF_ERR_INVALID, "state_pool and state_indices must not be NULL");
+    if (reinterpret_cast<uintptr_t>(state_pool) % 16 != 0) return fail(SF_ERR_INVALID, "state_pool must be 16-byte aligned");
+    const PagedWorkspace need = paged_layout(nullptr, elem_bytes(dt), B, T, H, K, V, N, packed);
+    if (!workspace || workspace_bytes < need.bytes)
+        return fail(SF_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(SF_ERR_INVALID, "workspace must be 256-byte aligned");
+    const PagedWorkspace ws = paged_layout(workspace, elem_bytes(dt), B, T, H, K, V, N, packed);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool pb = pool_dt == SF_BF16;
+    hipError_t e = sf::launch_state_gather(pb, state_pool, slot_stride, num_slots, state_indices, has_initial_state, N,
+                                           (long)blk, ws.h0, s);
+    if (e == hipSuccess)
+        e = sf::launch_gdn(dt == SF_BF16, 0, q, k, v, g, beta, ws.h0, cu_seqlens, ws.chunk, N, B, T, H, HK, K, V, scale,
+                           out, ws.ht, nullptr, s);
+    if (e == hipSuccess) e = sf::launch_state_scatter(pb, state_pool, slot_stride, num_slots, state_indices, N, (long)blk, ws.ht, s);
+    if (e == hipSuccess) e = sf::launch_null_rows(dt == SF_BF16, state_indices, num_slots, cu_seqlens, N, T, H * V, out, s);
+    return hip_status(e, "sf_paged_gdn_chunk_fwd launch");
+}
+
 sf_status sf_gate_transform(sf_dtype dt, const void* raw, const float* A_log, const float* dt_bias, long long rows,
                             int H, int D, sf_gate_kind kind, float lower_bound, float* out, void* stream) {
     if (dt != SF_F32 && dt != SF_BF16) return fail(SF_ERR_INVALID, "dtype must be SF_F32 or SF_BF16");

@@ -75,6 +75,14 @@ hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const v
                       float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages = 3,
                       int pre_w = -1);
 
+// Paged state cache around the chunk path (paging.hip). block = H*V*K elements per slot.
+hipError_t launch_state_gather(bool pool_bf16, const void* pool, long long slot_stride, int num_slots, const int32_t* idx,
+                               const uint8_t* has_init, int N, long block, float* h0, hipStream_t s);
+hipError_t launch_state_scatter(bool pool_bf16, void* pool, long long slot_stride, int num_slots, const int32_t* idx,
+                                int N, long block, const float* ht, hipStream_t s);
+hipError_t launch_null_rows(bool bf16, const int32_t* idx, int num_slots, const int32_t* cu, int N, int T, int HV,
+                            void* out, hipStream_t s);
+
 // Gate transform (gates.hip): n elements of raw [rows, H, D] -> float32 decays.
 hipError_t launch_gate_transform(bool bf16, bool bounded, const void* raw, const float* A_log, const float* dt_bias,
                                  long n, int H, int D, float lower_bound, float* out, hipStream_t s);

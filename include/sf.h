@@ -195,6 +195,33 @@ sf_status sf_gdn_segmented_fwd(sf_dtype dt, const void *q, const void *k, const 
                                void *out, float *ht, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* Workspace bytes needed by sf_paged_gdn_chunk_fwd (0 for invalid sizes). */
+size_t sf_paged_gdn_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N,
+                                        int packed);
+
+/*
+ * Delta-rule chunk forward on a paged state cache (attention-gym "Linear
+ * Attention": the paged_chunk_gdn entry; inference prefill). As
+ * sf_gdn_chunk_fwd, but sequence n starts from slot state_indices[n] of
+ * state_pool (from zeros when has_initial_state is given and
+ * has_initial_state[n] == 0) and its final state overwrites that slot,
+ * even for an empty sequence; a non-positive index (or one >= num_slots)
+ * gives zero output rows and leaves the pool alone. The pool layout is as for
+ * sf_gdn_decode (pool_dt SF_F32 or SF_BF16; slot_stride elements between
+ * slots, a multiple of 4 and >= H*V*K; 16-byte aligned). Two sequences naming
+ * the same positive slot race. workspace: at least
+ * sf_paged_gdn_chunk_fwd_workspace(...) bytes, 256-byte aligned (the chunk
+ * path's records plus float32 entry and exit states). Supported shapes as
+ * for sf_gdn_chunk_fwd.
+ */
+sf_status sf_paged_gdn_chunk_fwd(sf_dtype dt, const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta, const int32_t *cu_seqlens, int N,
+                                 int B, int T, int H, int HK, int K, int V, float scale, void *out,
+                                 void *state_pool, sf_dtype pool_dt, int num_slots,
+                                 long long slot_stride, const int32_t *state_indices,
+                                 const uint8_t *has_initial_state, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
 /* Gate transform kinds (attention-gym "Linear Attention", section "Gate Transforms"). */
 typedef enum { SF_GATE_SOFTPLUS = 0, SF_GATE_BOUNDED = 1 } sf_gate_kind;
 

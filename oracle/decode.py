@@ -3,7 +3,8 @@ float64 (test infrastructure; same rules as the rest of ``oracle/``: only tests,
 and the bench's CPU baseline may use it).
 
 ``gdn_recurrent_paged`` follows the ``recurrent_gdn`` entry of attention-gym "Linear Attention"
-with ``state_indices``: every sequence starts from its slot of the pool (or from zero when its
+with ``state_indices`` (and serves the ``paged_chunk_gdn`` entry too: chunking changes only the
+floating-point order of the same recurrence, and the slot rules are the same): every sequence starts from its slot of the pool (or from zero when its
 ``has_initial_state`` entry is false), runs the token rule over its tokens, and its final state
 overwrites the slot; a non-positive index gives zero output and leaves the pool untouched. The
 token recurrence itself is ``oracle.gdn_forward`` (oracle.c); this function only gathers and

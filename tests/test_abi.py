@@ -213,6 +213,20 @@ def test_gate_transform_rejects_invalid_arguments(L):
         sf.gate_transform(None, None, None, kind="linear")
 
 
+def test_paged_chunk_rejects_invalid_arguments(L):
+    def call(stride=4 * 128 * 128, pool=FAKE * 16, idx=FAKE, K=128, V=128, ws=FAKE * 256, nbytes=1 << 40):
+        st = L.sf_paged_gdn_chunk_fwd(sf.SF_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 2, 128, 4, 4, K, V, 1.0, FAKE,
+                                      pool, sf.SF_F32, 9, stride, idx, None, ws, nbytes, None)
+        return st, L.sf_last_error().decode()
+    assert call(K=96, V=96)[0] == sf.SF_ERR_UNSUPPORTED
+    assert call(stride=100)[0] == sf.SF_ERR_INVALID
+    assert call(idx=None)[0] == sf.SF_ERR_INVALID
+    assert call(pool=FAKE * 16 + 4)[0] == sf.SF_ERR_INVALID
+    assert call(nbytes=16)[0] == sf.SF_ERR_WORKSPACE
+    need = L.sf_paged_gdn_chunk_fwd_workspace(sf.SF_BF16, 2, 128, 4, 128, 128, 2, 0)
+    assert need == L.sf_gdn_chunk_fwd_workspace(sf.SF_BF16, 2, 128, 4, 128, 128, 2, 0) + 2 * (2 * 4 * 128 * 128 * 4)
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 64, 2, 64)

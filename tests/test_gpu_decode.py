@@ -264,3 +264,63 @@ def test_recurrent_full_size(dev):
     say(f"recurrent_gdn: rel_rms o {eo:.3g}  S {ep:.3g}")
     assert eo <= BF16_RTOL and ep <= BF16_RTOL
     assert np.array_equal(pool[0].cpu().numpy(), f(w.meta["pool"])[0])
+
+
+# ---------------------------------------------------------------------------------------------
+# chunk forward on a paged state cache (sf_paged_gdn_chunk_fwd)
+# ---------------------------------------------------------------------------------------------
+
+PAGED_CHUNK_CASES = [
+    # name, dtype, pool dtype, K, B, T, lengths or None, nulls, fresh
+    ("bf16-dense", torch.bfloat16, torch.float32, 128, 3, 150, None, 1, 1),
+    ("f32-k64-dense", torch.float32, torch.float32, 64, 2, 70, None, 0, 1),
+    ("bf16-packed-bf16pool", torch.bfloat16, torch.bfloat16, 128, 1, 0, [70, 0, 129, 5, 0, 64], 1, 2),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CHUNK_CASES, ids=[c[0] for c in PAGED_CHUNK_CASES])
+def test_paged_chunk_vs_oracle(dev, case):
+    name, dt, pdt, K, B, T, lens, nulls, fresh_n = case
+    H, HK, V = 4, 2, K
+    cu = None
+    if lens is not None:
+        T = int(sum(lens))
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    N = B if lens is None else len(lens)
+    say(f"paged chunk {name}: N={N} T={T}")
+    seed = zlib.crc32(name.encode()) % 1000
+    d = wl.delta_rule_inputs(B=B, T=T, H=H, HK=HK, K=K, V=V, dtype=dt, seed=seed, gate_shift=1.0)
+    p = wl.decode_inputs(B=N, H=H, HK=HK, K=K, V=V, dtype=dt, pool_dtype=pdt, seed=seed + 1, num_slots=N + 3,
+                         n_null=nulls, n_fresh=fresh_n, pool_std=0.3)
+    pool = p["pool"].to(dev).contiguous()
+    g = {n: d[n].to(dev).contiguous() for n in ("q", "k", "v", "g", "beta")}
+    fresh = p["has_initial_state"]
+    o = sf.paged_gdn_chunk_fwd(g["q"], g["k"], g["v"], g["g"], g["beta"], pool, p["state_indices"].to(dev),
+                               cu_seqlens=None if cu is None else cu.to(dev),
+                               has_initial_state=None if fresh is None else fresh.to(dev), scale=0.25)
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    ref_o, ref_pool = oracle.gdn_recurrent_paged(f(d["q"]), f(d["k"]), f(d["v"]), f(d["g"]), f(d["beta"]),
+                                                 f(p["pool"]), p["state_indices"].numpy(),
+                                                 None if fresh is None else fresh.numpy(),
+                                                 cu_seqlens=None if cu is None else cu.numpy(), scale=0.25)
+    o = o.float().cpu().numpy()
+    got_pool = pool.float().cpu().numpy()
+    idx = p["state_indices"].numpy()
+    active = sorted(int(s) for s in idx if s > 0)
+    p0 = f(p["pool"])
+    for s in range(got_pool.shape[0]):
+        if s not in active:
+            assert np.array_equal(got_pool[s], p0[s]), f"slot {s} was written"
+    for n in range(N):
+        if idx[n] <= 0:
+            rows = o[n] if cu is None else o[0, cu[n]:cu[n + 1]]
+            assert np.all(rows == 0), f"null sequence {n} has nonzero output"
+    if dt == torch.float32:
+        eo, ep = float(np.max(np.abs(o - ref_o))), float(np.max(np.abs(got_pool[active] - ref_pool[active])))
+        say(f"{name}: max|o|err {eo:.3g}  max|S|err {ep:.3g}")
+        assert eo <= FP32_ATOL and ep <= FP32_ATOL
+    else:
+        eo, ep = rel_rms(o, ref_o), rel_rms(got_pool[active], ref_pool[active])
+        say(f"{name}: rel_rms o {eo:.3g}  S {ep:.3g}")
+        assert eo <= BF16_RTOL and ep <= BF16_RTOL

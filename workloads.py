@@ -27,6 +27,8 @@ and one decode workload (one token per sequence against a paged state pool):
 7. ``recurrent_gdn``  64 sequences of 16 tokens, H=HK=32, K=V=128, bf16, on a
                       float32 pool of 65 slots (token-by-token forward).
 8. ``gate_transform`` per-channel raw gates [2, 16384, 16, 128] bf16, softplus kind.
+9. ``paged_gdn``      the packed workload's stream on a float32 state pool (chunk
+                      forward advancing the cache in place).
 
 Draw order inside one workload: q, k, v, gate noise, beta noise, h0, A, dt,
 sequence lengths.
@@ -40,7 +42,8 @@ import numpy as np
 import torch
 
 SEEDS = {"tiny_gdn": 101, "dense_gdn": 102, "varlen_gdn": 103, "long_gdn": 104, "ssd_gla": 105,
-         "decode_gdn": 106, "recurrent_gdn": 107, "gate_transform": 108}
+         "decode_gdn": 106, "recurrent_gdn": 107, "gate_transform": 108,
+         "paged_gdn": 109}
 
 
 @dataclass
@@ -202,6 +205,19 @@ def varlen_gdn(seed=SEEDS["varlen_gdn"], *, T=32768, H=32, D=128, n_long=7):
                     meta={"lengths": [int(x) for x in lens]})
 
 
+def paged_gdn(seed=SEEDS["paged_gdn"], *, T=32768, H=32, D=128, n_long=7):
+    """varlen_gdn's stream and distributions, each sequence starting from its slot of a float32 pool
+    (N + 1 slots, every sequence loaded; pool ~ N(0, 0.02^2), slots a random permutation of 1..N)."""
+    w = varlen_gdn(seed=seed, T=T, H=H, D=D, n_long=n_long)
+    rng = np.random.default_rng(seed + 1000)
+    N = w.N
+    pool = _normal(rng, (N + 1, H, D, D)) * np.float32(0.02)
+    idx = rng.permutation(np.arange(1, N + 1)).astype(np.int32)
+    w.name = "paged_gdn"
+    w.meta.update(pool=torch.from_numpy(pool), state_indices=torch.from_numpy(idx))
+    return w
+
+
 def long_gdn(seed=SEEDS["long_gdn"], *, T=262144, H=16, D=128, n_seg=16):
     """bf16 delta rule on one long row cut into n_seg segments; g = -softplus(N(0,1) + 4) as the
     formula gives it (its decay is fast, whatever the label says); zero initial state; scale 1/sqrt(D)."""
@@ -328,7 +344,8 @@ def gate_transform(seed=SEEDS["gate_transform"], *, B=2, T=16384, H=16, D=128):
 
 CONFIGS = {"tiny_gdn": tiny_gdn, "dense_gdn": dense_gdn, "varlen_gdn": varlen_gdn,
            "long_gdn": long_gdn, "ssd_gla": ssd_gla, "decode_gdn": decode_gdn,
-           "recurrent_gdn": recurrent_gdn, "gate_transform": gate_transform}
+           "recurrent_gdn": recurrent_gdn, "gate_transform": gate_transform,
+           "paged_gdn": paged_gdn}
 
 
 def to_f32(t):
