@@ -26,6 +26,8 @@ Functions (same names as the C entry points, without the ``sf_`` prefix):
                         recurrent_gdn).
 * ``paged_gdn_chunk_fwd`` chunk forward on a paged state cache (attention-gym
                         "Linear Attention", paged_chunk_gdn).
+* ``gdn_chunk_fwd_raw_gate`` gdn_chunk_fwd with the gate transform fused into its
+                        Pre stage (raw gate projection in, no separate kernel).
 * ``gate_transform``    raw gate projections to float32 natural-log decays
                         (attention-gym "Linear Attention", "Gate Transforms").
 """
@@ -52,7 +54,7 @@ EXPORTED = (
     "sf_version", "sf_last_error", "sf_gdn_chunk_fwd_workspace", "sf_gdn_chunk_fwd",
     "sf_gla_chunk_fwd", "sf_segment_summary_workspace", "sf_segment_summary",
     "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_gdn_decode", "sf_gdn_recurrent_fwd", "sf_gate_transform",
-    "sf_paged_gdn_chunk_fwd_workspace", "sf_paged_gdn_chunk_fwd",
+    "sf_paged_gdn_chunk_fwd_workspace", "sf_paged_gdn_chunk_fwd", "sf_gdn_chunk_fwd_raw_gate",
     "sf_timing_enable", "sf_timing_collect",
 )
 
@@ -105,6 +107,8 @@ def lib() -> ctypes.CDLL:
     L.sf_paged_gdn_chunk_fwd.restype = I
     L.sf_paged_gdn_chunk_fwd.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, I, I, ctypes.c_longlong,
                                          P, P, P, Z, P]
+    L.sf_gdn_chunk_fwd_raw_gate.restype = I
+    L.sf_gdn_chunk_fwd_raw_gate.argtypes = [I, P, P, P, P, P, P, I, F, P, P, P, I, I, I, I, I, I, I, F, P, P, P, Z, P]
     L.sf_gate_transform.restype = I
     L.sf_gate_transform.argtypes = [I, P, P, P, ctypes.c_longlong, I, I, I, F, P, P]
     L.sf_timing_enable.restype = I
@@ -161,12 +165,12 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def _token_args(q, k, v, g, beta, initial_state, cu_seqlens):
+def _token_args(q, k, v, g, beta, initial_state, cu_seqlens, g_dtype=torch.float32):
     _need(q, "q", ndim=4)
     dev = q.device
     _need(k, "k", dtype=q.dtype, ndim=4, device=dev)
     _need(v, "v", dtype=q.dtype, ndim=4, device=dev)
-    _need(g, "g", dtype=torch.float32, ndim=3, device=dev)
+    _need(g, "g", dtype=g_dtype, ndim=3, device=dev)
     if beta is not None:
         _need(beta, "beta", dtype=torch.float32, ndim=3, device=dev)
     B, T, HK, K = q.shape
@@ -204,6 +208,36 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, scal
     _check(lib().sf_gdn_chunk_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                                   _ptr(cu_seqlens), N, B, T, H, HK, K, V, float(scale), _ptr(out), _ptr(ht),
                                   _ptr(ws), nbytes, _stream()))
+    return out, ht
+
+
+def gdn_chunk_fwd_raw_gate(q, k, v, raw_gate, A_log, dt_bias, beta, initial_state=None, *, kind,
+                           lower_bound=None, cu_seqlens=None, scale=None, output_final_state=False):
+    """gdn_chunk_fwd whose natural-log gate is formed inside the kernels from raw_gate [B,T,H] (q's dtype),
+    A_log [H] and dt_bias [H] (float32): kind "softplus" or "bounded" (with lower_bound), as gate_transform."""
+    if kind not in GATE_KINDS:
+        raise ValueError(f"kind must be one of {sorted(GATE_KINDS)}, got {kind!r}")
+    if kind == "softplus" and lower_bound is not None:
+        raise ValueError("lower_bound is rejected by the softplus kind")
+    if kind == "bounded" and (lower_bound is None or not math.isfinite(lower_bound) or lower_bound > 0):
+        raise ValueError("the bounded kind needs a finite lower_bound <= 0")
+    B, T, H, HK, K, V, N = _token_args(q, k, v, raw_gate, beta, initial_state, cu_seqlens, g_dtype=q.dtype)
+    _need(A_log, "A_log", dtype=torch.float32, ndim=1, device=q.device)
+    _need(dt_bias, "dt_bias", dtype=torch.float32, ndim=1, device=q.device)
+    if A_log.numel() != H or dt_bias.numel() != H:
+        raise ValueError(f"A_log and dt_bias must have {H} entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    dev = q.device
+    out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+    ht = torch.empty((N, H, V, K), dtype=torch.float32, device=dev) if output_final_state else None
+    dt = _dt(q)
+    nbytes = lib().sf_gdn_chunk_fwd_workspace(dt, B, T, H, K, V, N, int(cu_seqlens is not None))
+    ws = _workspace(nbytes, dev)
+    _check(lib().sf_gdn_chunk_fwd_raw_gate(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(A_log), _ptr(dt_bias),
+                                           GATE_KINDS[kind], float(lower_bound or 0.0), _ptr(beta), _ptr(initial_state),
+                                           _ptr(cu_seqlens), N, B, T, H, HK, K, V, float(scale), _ptr(out), _ptr(ht),
+                                           _ptr(ws), nbytes, _stream()))
     return out, ht
 
 

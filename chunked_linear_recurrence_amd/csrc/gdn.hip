@@ -119,6 +119,18 @@ __device__ __forceinline__ bool chunk_coords(int slot, const int2* table, const 
 //   [0,64) Gamma_t  [64,128) e_t  [128,192) beta_t  [192,256) G_t
 // (Gamma_L = Gamma_63: padded tokens of a partial chunk have zero gate)
 // ---------------------------------------------------------------------------
+// The natural-log gate of token row gi and head h: g as given, or the gate transform of the raw
+// projection (attention-gym "Linear Attention", "Gate Transforms"), in float32 with the accurate
+// exponential and log1p (Pre reads 64 gates per chunk and head, so their cost does not show).
+__device__ __forceinline__ float load_gate(const float* __restrict__ g, const GateSrc& gs, size_t gi, int h) {
+    if (gs.raw == nullptr) return g[gi];
+    const float x = (gs.raw_bf16 ? bf2f(static_cast<const bf16_t*>(gs.raw)[gi]) : static_cast<const float*>(gs.raw)[gi]) +
+                    gs.dt_bias[h];
+    const float amp = expf(gs.A_log[h]);
+    if (gs.bounded) return gs.lower_bound / (1.f + expf(-amp * x));
+    return -amp * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))));
+}
+
 template <typename ST, int KD>
 __global__ __launch_bounds__(256) void gdn_prep_kernel(const ST* __restrict__ q, const ST* __restrict__ k,
                                                        const float* __restrict__ g,
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const ST* __restrict__ q,
                                                        const int2* __restrict__ table,
                                                        const int32_t* __restrict__ cu, int T, int H,
                                                        int HK, int nc, float scale, int want_p,
-                                                       uint8_t* __restrict__ fac) {
+                                                       uint8_t* __restrict__ fac, GateSrc gs) {
     constexpr int E = 16 / sizeof(ST);  // elements per 16-byte unit
     constexpr int LDK = KD + E, LD = GC + E;
     constexpr int UPR = KD / E;
@@ -156,7 +168,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const ST* __restrict__ q,
     }
     if (tid < GC) {
         const size_t gi = (size_t)(b * T + t0 + tid) * H + h;
-        const float gv = tid < L ? g[gi] : 0.f;
+        const float gv = tid < L ? load_gate(g, gs, gi, h) : 0.f;
         sB[tid] = tid < L ? beta[gi] : 0.f;
         sG[tid] = wave_inclusive_scan(gv);
     }
@@ -320,7 +332,7 @@ __global__ __launch_bounds__(64 * NW, NW == 2 ? 4 : 1) void gdn_prep_wave_kernel
                                                             const int2* __restrict__ table,
                                                             const int32_t* __restrict__ cu, int T, int H,
                                                             int HK, int nc, int n_slots, float scale,
-                                                            uint8_t* __restrict__ fac, int want_w) {
+                                                            uint8_t* __restrict__ fac, int want_w, GateSrc gs) {
     constexpr int KP = KD / 32;
     static_assert(tri_off(GC) * 4 >= GC * GC * 2, "the T staging tile reuses the A area");
     __shared__ __align__(16) float sA[tri_off(GC)];  // A packed columns; then T diag(beta), bf16 [64][64]
@@ -343,7 +355,7 @@ __global__ __launch_bounds__(64 * NW, NW == 2 ? 4 : 1) void gdn_prep_wave_kernel
 
     // gates of the chunk (both wavefronts; padded tokens get g = 0)
     const size_t gi = (size_t)(b * T + t0 + min(lane, L - 1)) * H + h;
-    const float G = wave_inclusive_scan(lane < L ? g[gi] : 0.f);
+    const float G = wave_inclusive_scan(lane < L ? load_gate(g, gs, gi, h) : 0.f);
     float* sGw = sG[wave];
     sGw[lane] = G;
     uint8_t* rec = fac + ((size_t)slot * H + h) * gdn_factor_bytes(2);
@@ -1827,7 +1839,8 @@ template <typename ST, int KD>
 static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const float* g,
                           const float* beta, const float* h0, const int32_t* cu,
                           const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int V,
-                          float scale, ST* out, float* ht, float* Mout, hipStream_t s, int stages, int pre_w) {
+                          float scale, ST* out, float* ht, float* Mout, hipStream_t s, int stages, int pre_w,
+                          const GateSrc& gs) {
     // the key-key block W and the decay-masked query-key block P are read only by the per-slice bf16
     // chain kernel (the per-head one forms P itself from the K and Q rows it holds)
     const int want_w = pre_w >= 0 ? pre_w : (gdn_chain_per_slice(N * H, mode == 0 ? V : V + KD) ? 1 : 0);
@@ -1851,19 +1864,19 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
             const bool two = (long)H * slots <= 8L * device_cus();
             if (two) {
                 if (want_p)
-                    gdn_prep_wave_kernel<KD, true, 2><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
+                    gdn_prep_wave_kernel<KD, true, 2><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w, gs);
                 else
-                    gdn_prep_wave_kernel<KD, false, 2><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
+                    gdn_prep_wave_kernel<KD, false, 2><<<gx, 128, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w, gs);
             } else {
                 if (want_p)
-                    gdn_prep_wave_kernel<KD, true, 1><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
+                    gdn_prep_wave_kernel<KD, true, 1><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w, gs);
                 else
-                    gdn_prep_wave_kernel<KD, false, 1><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w);
+                    gdn_prep_wave_kernel<KD, false, 1><<<gx, 64, 0, s>>>(q, k, g, beta, tab, cu, T, H, HK, nc, (int)slots, scale, ws.factors, want_w, gs);
             }
         } else
             gdn_prep_kernel<ST, KD><<<dim3((unsigned)slots, H), 256, 0, s>>>(
                 q, k, g, beta, packed ? ws.table : nullptr, cu, T, H, HK, nc, scale, mode == 0 ? 1 : 0,
-                ws.factors);
+                ws.factors, gs);
         timing_end(s);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -1924,15 +1937,17 @@ static hipError_t run_gdn(int mode, const ST* q, const ST* k, const ST* v, const
 hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const float* h0, const int32_t* cu,
                       const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int K, int V,
-                      float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages, int pre_w) {
+                      float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages, int pre_w,
+                      const GateSrc* gate_src) {
+    const GateSrc gs = gate_src ? *gate_src : GateSrc{nullptr, 0, nullptr, nullptr, 0, 0.f};
     if (bf16) {
         const bf16_t *qq = (const bf16_t*)q, *kk = (const bf16_t*)k, *vv = (const bf16_t*)v;
-        if (K == 128) return run_gdn<bf16_t, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s, stages, pre_w);
-        return run_gdn<bf16_t, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s, stages, pre_w);
+        if (K == 128) return run_gdn<bf16_t, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s, stages, pre_w, gs);
+        return run_gdn<bf16_t, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (bf16_t*)out, ht, Mout, s, stages, pre_w, gs);
     }
     const float *qq = (const float*)q, *kk = (const float*)k, *vv = (const float*)v;
-    if (K == 128) return run_gdn<float, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s, stages, pre_w);
-    return run_gdn<float, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s, stages, pre_w);
+    if (K == 128) return run_gdn<float, 128>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s, stages, pre_w, gs);
+    return run_gdn<float, 64>(mode, qq, kk, vv, g, beta, h0, cu, ws, N, B, T, H, HK, V, scale, (float*)out, ht, Mout, s, stages, pre_w, gs);
 }
 
 }  // namespace sf

@@ -165,6 +165,34 @@ sf_status sf_gdn_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void
     return hip_status(e, "sf_gdn_chunk_fwd launch");
 }
 
+sf_status sf_gdn_chunk_fwd_raw_gate(sf_dtype dt, const void* q, const void* k, const void* v, const void* raw_gate,
+                                    const float* A_log, const float* dt_bias, sf_gate_kind kind, float lower_bound,
+                                    const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B, int T,
+                                    int H, int HK, int K, int V, float scale, void* out, float* ht, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
+    if (st != SF_OK) return st;
+    if (!q || !k || !v || !raw_gate || !A_log || !dt_bias || !beta || !out)
+        return fail(SF_ERR_INVALID, "q, k, v, raw_gate, A_log, dt_bias, beta and out must not be NULL");
+    if (kind != SF_GATE_SOFTPLUS && kind != SF_GATE_BOUNDED)
+        return fail(SF_ERR_INVALID, "kind must be SF_GATE_SOFTPLUS or SF_GATE_BOUNDED");
+    if (kind == SF_GATE_BOUNDED && !(lower_bound <= 0.f && lower_bound > -3.0e38f))
+        return fail(SF_ERR_INVALID, "the bounded kind needs a finite lower_bound <= 0 (got %g)", (double)lower_bound);
+    if (K != V || (K != 64 && K != 128))
+        return fail(SF_ERR_UNSUPPORTED, "delta-rule kernels are built for K == V in {64, 128} (K=%d V=%d)", K, V);
+    const sf::GdnWorkspace need = sf::gdn_workspace_layout(nullptr, elem_bytes(dt), B, T, H, N, packed);
+    if (!workspace || workspace_bytes < need.bytes)
+        return fail(SF_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                    need.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(SF_ERR_INVALID, "workspace must be 256-byte aligned");
+    const sf::GdnWorkspace ws = sf::gdn_workspace_layout(workspace, elem_bytes(dt), B, T, H, N, packed);
+    const sf::GateSrc gs{raw_gate, dt == SF_BF16 ? 1 : 0, A_log, dt_bias, kind == SF_GATE_BOUNDED ? 1 : 0, lower_bound};
+    hipError_t e = sf::launch_gdn(dt == SF_BF16, 0, q, k, v, nullptr, beta, h0, cu_seqlens, ws, N, B, T, H, HK, K, V,
+                                  scale, out, ht, nullptr, static_cast<hipStream_t>(stream), 3, -1, &gs);
+    return hip_status(e, "sf_gdn_chunk_fwd_raw_gate launch");
+}
+
 sf_status sf_gla_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
                            const float* h0, const int32_t* cu_seqlens, int N, int B, int T, int H, int HK,
                            int K, int V, int chunk, float scale, void* out, float* ht, void* stream) {

@@ -56,6 +56,18 @@ inline GdnWorkspace gdn_workspace_layout(void* base, int elem_bytes, int B, int 
     return w;
 }
 
+// Raw gate projection read by the delta-rule Pre stage in place of g (the gate transform fused
+// into its gate load): g = -exp(A_log[h]) softplus(raw + dt_bias[h]) or, bounded,
+// lower_bound sigmoid(exp(A_log[h]) (raw + dt_bias[h])). raw == nullptr: read g as given.
+struct GateSrc {
+    const void* raw;
+    int raw_bf16;
+    const float* A_log;
+    const float* dt_bias;
+    int bounded;
+    float lower_bound;
+};
+
 // Measurement hook (see sf_timing_enable): brackets one launch with events.
 void timing_begin(const char* name, hipStream_t s);
 void timing_end(hipStream_t s);
@@ -73,7 +85,7 @@ hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const v
                       const float* g, const float* beta, const float* h0, const int32_t* cu,
                       const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int K, int V,
                       float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages = 3,
-                      int pre_w = -1);
+                      int pre_w = -1, const GateSrc* gate_src = nullptr);
 
 // Paged state cache around the chunk path (paging.hip). block = H*V*K elements per slot.
 hipError_t launch_state_gather(bool pool_bf16, const void* pool, long long slot_stride, int num_slots, const int32_t* idx,

@@ -195,6 +195,25 @@ sf_status sf_gdn_segmented_fwd(sf_dtype dt, const void *q, const void *k, const 
                                void *out, float *ht, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* Gate transform kinds (attention-gym "Linear Attention", section "Gate Transforms"). */
+typedef enum { SF_GATE_SOFTPLUS = 0, SF_GATE_BOUNDED = 1 } sf_gate_kind;
+
+/*
+ * sf_gdn_chunk_fwd with the gate transform fused into the gate load of its
+ * Pre stage (attention-gym "Linear Attention", "Gate Transforms": no separate
+ * elementwise kernel runs): g[b, t, h] is formed from raw_gate [B, T, H] in dt
+ * as sf_gate_transform forms it for per-head gates (A_log [H], dt_bias [H],
+ * float32; kind SF_GATE_SOFTPLUS or SF_GATE_BOUNDED with a finite
+ * lower_bound <= 0), in float32. Every other argument, the workspace and the
+ * results are those of sf_gdn_chunk_fwd.
+ */
+sf_status sf_gdn_chunk_fwd_raw_gate(sf_dtype dt, const void *q, const void *k, const void *v,
+                                    const void *raw_gate, const float *A_log, const float *dt_bias,
+                                    sf_gate_kind kind, float lower_bound, const float *beta,
+                                    const float *h0, const int32_t *cu_seqlens, int N, int B, int T,
+                                    int H, int HK, int K, int V, float scale, void *out, float *ht,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Workspace bytes needed by sf_paged_gdn_chunk_fwd (0 for invalid sizes). */
 size_t sf_paged_gdn_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N,
                                         int packed);
@@ -221,9 +240,6 @@ sf_status sf_paged_gdn_chunk_fwd(sf_dtype dt, const void *q, const void *k, cons
                                  long long slot_stride, const int32_t *state_indices,
                                  const uint8_t *has_initial_state, void *workspace,
                                  size_t workspace_bytes, void *stream);
-
-/* Gate transform kinds (attention-gym "Linear Attention", section "Gate Transforms"). */
-typedef enum { SF_GATE_SOFTPLUS = 0, SF_GATE_BOUNDED = 1 } sf_gate_kind;
 
 /*
  * Gate transform: raw gate projections to float32 natural-log decays

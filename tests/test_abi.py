@@ -227,6 +227,16 @@ def test_paged_chunk_rejects_invalid_arguments(L):
     assert need == L.sf_gdn_chunk_fwd_workspace(sf.SF_BF16, 2, 128, 4, 128, 128, 2, 0) + 2 * (2 * 4 * 128 * 128 * 4)
 
 
+def test_raw_gate_chunk_rejects_invalid_arguments(L):
+    def call(kind=sf.SF_GATE_SOFTPLUS, lb=0.0, raw=FAKE, K=128):
+        return L.sf_gdn_chunk_fwd_raw_gate(sf.SF_BF16, FAKE, FAKE, FAKE, raw, FAKE, FAKE, kind, lb, FAKE, None, None, 2,
+                                           2, 128, 4, 4, K, K, 1.0, FAKE, None, FAKE * 256, 1 << 40, None)
+    assert call(raw=None) == sf.SF_ERR_INVALID
+    assert call(kind=5) == sf.SF_ERR_INVALID
+    assert call(kind=sf.SF_GATE_BOUNDED, lb=2.0) == sf.SF_ERR_INVALID
+    assert call(K=96) == sf.SF_ERR_UNSUPPORTED
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 64, 2, 64)

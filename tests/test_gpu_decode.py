@@ -324,3 +324,50 @@ def test_paged_chunk_vs_oracle(dev, case):
         eo, ep = rel_rms(o, ref_o), rel_rms(got_pool[active], ref_pool[active])
         say(f"{name}: rel_rms o {eo:.3g}  S {ep:.3g}")
         assert eo <= BF16_RTOL and ep <= BF16_RTOL
+
+
+# ---------------------------------------------------------------------------------------------
+# chunk forward with the gate transform fused into Pre (sf_gdn_chunk_fwd_raw_gate)
+# ---------------------------------------------------------------------------------------------
+
+RAW_GATE_CASES = [
+    # name, dtype, K, B, T, lengths or None, kind, lower bound
+    ("bf16-dense-softplus", torch.bfloat16, 128, 2, 300, None, "softplus", None),
+    ("bf16-packed-bounded", torch.bfloat16, 64, 1, 0, [100, 0, 37, 200], "bounded", -5.0),
+    ("f32-softplus", torch.float32, 64, 1, 130, None, "softplus", None),
+]
+
+
+@pytest.mark.parametrize("case", RAW_GATE_CASES, ids=[c[0] for c in RAW_GATE_CASES])
+def test_raw_gate_chunk_vs_oracle(dev, case):
+    """The fused path against oracle.gate_transform followed by the token recurrence."""
+    name, dt, K, B, T, lens, kind, lb = case
+    H, HK, V = 4, 2, K
+    cu = None
+    if lens is not None:
+        T = int(sum(lens))
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    N = B if lens is None else len(lens)
+    say(f"raw-gate chunk {name}: N={N} T={T}")
+    seed = zlib.crc32(name.encode()) % 1000
+    d = wl.delta_rule_inputs(B=B, T=T, H=H, HK=HK, K=K, V=V, dtype=dt, seed=seed, h0_std=0.1, N=N)
+    gi = wl.gate_inputs(shape=(B, T, H), H=H, dtype=dt, seed=seed + 1)
+    g = {n: d[n].to(dev).contiguous() for n in ("q", "k", "v", "beta", "h0")}
+    o, ht = sf.gdn_chunk_fwd_raw_gate(g["q"], g["k"], g["v"], gi["raw"].to(dev), gi["A_log"].to(dev),
+                                      gi["dt_bias"].to(dev), g["beta"], g["h0"], kind=kind, lower_bound=lb,
+                                      cu_seqlens=None if cu is None else cu.to(dev), scale=0.2,
+                                      output_final_state=True)
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    gate = oracle.gate_transform(f(gi["raw"]), f(gi["A_log"]), f(gi["dt_bias"]), kind, lb)
+    ref_o, ref_ht = oracle.gdn_forward(f(d["q"]), f(d["k"]), f(d["v"]), gate, f(d["beta"]), f(d["h0"]),
+                                       cu_seqlens=None if cu is None else cu.numpy(), scale=0.2)
+    o, ht = o.float().cpu().numpy(), ht.cpu().numpy()
+    if dt == torch.float32:
+        eo, eh = float(np.max(np.abs(o - ref_o))), float(np.max(np.abs(ht - ref_ht)))
+        say(f"{name}: max|o|err {eo:.3g}  max|ht|err {eh:.3g}")
+        assert eo <= FP32_ATOL and eh <= FP32_ATOL
+    else:
+        eo, eh = rel_rms(o, ref_o), rel_rms(ht, ref_ht)
+        say(f"{name}: rel_rms o {eo:.3g}  ht {eh:.3g}")
+        assert eo <= BF16_RTOL and eh <= BF16_RTOL
