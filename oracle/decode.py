@@ -150,3 +150,34 @@ def gate_transform(raw, A_log, dt_bias, kind, lower_bound=None):
         return lower_bound * write_gate(amp * x)
     raise ValueError(kind)
 
+
+def kda_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None):
+    """Kimi Delta Attention, token by token (attention-gym "Linear Attention", section "Kimi Delta
+    Attention": per-channel gate; at each token the previous state is multiplied channelwise by
+    exp(gate), then the delta rule's correction and update, then the read with q), float64.
+    q, k, g [B, T, H, K]; v [B, T, H, V]; beta [B, T, H]; h0 [N, H, V, K] or None.
+    Returns (out [B, T, H, V], ht [N, H, V, K]); rows outside every sequence are NaN."""
+    q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
+    B, T, H, K = q.shape
+    V = v.shape[3]
+    if scale is None:
+        scale = 1.0 / np.sqrt(K)
+    if cu_seqlens is None:
+        spans = [(n, 0, T) for n in range(B)]
+    else:
+        cu = np.asarray(cu_seqlens)
+        assert B == 1
+        spans = [(0, int(cu[n]), int(cu[n + 1])) for n in range(len(cu) - 1)]
+    N = len(spans)
+    out = np.full((B, T, H, V), np.nan)
+    ht = np.zeros((N, H, V, K))
+    for n, (b, bos, eos) in enumerate(spans):
+        S = np.zeros((H, V, K)) if h0 is None else np.array(h0[n], dtype=np.float64)
+        for t in range(bos, eos):
+            S = S * np.exp(g[b, t])[:, None, :]                      # channelwise decay of each key column
+            r = beta[b, t][:, None] * (v[b, t] - np.einsum("hvk,hk->hv", S, k[b, t]))
+            S = S + r[:, :, None] * k[b, t][:, None, :]
+            out[b, t] = scale * np.einsum("hvk,hk->hv", S, q[b, t])
+        ht[n] = S
+    return out, ht
+

@@ -251,3 +251,62 @@ def test_gate_transform_pins():
         np.testing.assert_array_equal(oracle.gate_transform(r[..., None], A, bias[:, None], kind, lb)[..., 0],
                                       oracle.gate_transform(r, A, bias, kind, lb))
 
+
+def _kda_inputs(rng, B, T, Hh, Kk, Vv):
+    q = rng.standard_normal((B, T, Hh, Kk))
+    k = rng.standard_normal((B, T, Hh, Kk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, Hh, Vv))
+    g = -np.logaddexp(0.0, rng.standard_normal((B, T, Hh, Kk)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, Hh))))
+    return q, k, v, g, beta
+
+
+def test_kda_with_uniform_channels_is_the_delta_rule():
+    """A per-channel gate equal across channels is the scalar gate: KDA reduces to oracle.gdn_forward."""
+    rng = np.random.default_rng(11)
+    B, T, Hh, Kk, Vv = 2, 9, 3, 5, 4
+    q, k, v, _, beta = _kda_inputs(rng, B, T, Hh, Kk, Vv)
+    gs = -np.logaddexp(0.0, rng.standard_normal((B, T, Hh)))
+    h0 = rng.standard_normal((B, Hh, Vv, Kk)) * 0.3
+    f32 = lambda x: np.asarray(x, np.float32).astype(np.float64)  # gdn_forward reads float32 inputs
+    q, k, v, gs, beta, h0 = map(f32, (q, k, v, gs, beta, h0))
+    o1, h1 = oracle.kda_forward(q, k, v, np.repeat(gs[..., None], Kk, axis=-1), beta, h0, scale=0.4)
+    o2, h2 = oracle.gdn_forward(q, k, v, gs, beta, h0=h0, scale=0.4)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(h1, h2, rtol=1e-12, atol=1e-13)
+
+
+def test_kda_closed_forms():
+    """beta = 0: every key column decays by the product of its own factors and the output reads the
+    decayed state; one token from zero: S = beta v k^T and o = scale beta v (k . q)."""
+    rng = np.random.default_rng(12)
+    B, T, Hh, Kk, Vv = 1, 6, 2, 4, 3
+    q, k, v, g, _ = _kda_inputs(rng, B, T, Hh, Kk, Vv)
+    h0 = rng.standard_normal((B, Hh, Vv, Kk))
+    out, ht = oracle.kda_forward(q, k, v, g, np.zeros((B, T, Hh)), h0, scale=0.5)
+    decay = np.exp(np.cumsum(g[0], axis=0))                          # [T, H, K]
+    for t in range(T):
+        St = h0[0] * decay[t][:, None, :]
+        np.testing.assert_allclose(out[0, t], 0.5 * np.einsum("hvk,hk->hv", St, q[0, t]), rtol=1e-12)
+    np.testing.assert_allclose(ht[0], h0[0] * decay[-1][:, None, :], rtol=1e-12)
+    b1 = np.full((1, 1, Hh), 0.7)
+    o1, h1 = oracle.kda_forward(q[:, :1], k[:, :1], v[:, :1], g[:, :1], b1, scale=0.5)
+    np.testing.assert_allclose(h1[0], 0.7 * v[0, 0][:, :, None] * k[0, 0][:, None, :], rtol=1e-14)
+    np.testing.assert_allclose(o1[0, 0], 0.5 * 0.7 * v[0, 0] * np.sum(k[0, 0] * q[0, 0], -1)[:, None], rtol=1e-13)
+
+
+def test_kda_packed_equals_separate():
+    rng = np.random.default_rng(13)
+    lens = [4, 0, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, g, beta = _kda_inputs(rng, 1, int(cu[-1]), 2, 4, 3)
+    h0 = rng.standard_normal((3, 2, 3, 4))
+    out, ht = oracle.kda_forward(q, k, v, g, beta, h0, cu_seqlens=cu)
+    for n in range(3):
+        sl = slice(cu[n], cu[n + 1])
+        o1, h1 = oracle.kda_forward(q[:, sl], k[:, sl], v[:, sl], g[:, sl], beta[:, sl], h0[n:n + 1])
+        np.testing.assert_array_equal(out[:, sl], o1)
+        np.testing.assert_array_equal(ht[n], h1[0])
+    np.testing.assert_array_equal(ht[1], h0[1])                     # the empty sequence passes its state
+
