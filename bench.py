@@ -20,7 +20,7 @@ carry measured_peak: the bandwidth a plain 1 GiB device-to-device copy reaches
 on the same GPU (read plus write bytes), and the fraction of that.
 
 Other workloads (--workload varlen_gdn | long_gdn | ssd_gla | tiny_gdn | decode_gdn | recurrent_gdn |
-gate_transform | paged_gdn) are for
+gate_transform | paged_gdn | recurrent_kda) are for
 measurement only; the headline line is the default one. decode_gdn times one sf_gdn_decode call
 (one token for each of 256 sequences against a 514 MB float32 state pool, which is larger than
 the last-level cache, so it runs on one input set).
@@ -76,7 +76,9 @@ def algorithmic_bytes(w, kernel):
     vo = 2 * tok * w.H * w.V * eb
     gb = tok * w.H * 4 * (2 if w.beta is not None else 1)
     states = w.N * w.H * w.V * w.K * 4 * (1 + (w.h0 is not None))
-    if w.name in ("recurrent_gdn", "paged_gdn"):   # every slot read and written (float32 pool)
+    if w.name == "recurrent_kda":   # per-channel gate: K floats per token and head
+        gb = tok * w.H * 4 * (w.K + 1)
+    if w.name in ("recurrent_gdn", "paged_gdn", "recurrent_kda"):   # every slot read and written (float32 pool)
         states = 2 * w.N * w.H * w.V * w.K * w.meta["pool"].element_size()
         return qk + vo + states + (0 if kernel == "gdn_chain" else gb)
     if kernel in ("gdn_chain", "gla_chain"):
@@ -124,7 +126,7 @@ def make_sets(w, dev, rotate):
         for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens"):
             t = getattr(w, n)
             s[n] = None if t is None else t.to(dev).contiguous()
-        if w.name in ("recurrent_gdn", "paged_gdn"):
+        if w.name in ("recurrent_gdn", "paged_gdn", "recurrent_kda"):
             s["pool"] = w.meta["pool"].to(dev).contiguous()
             s["state_indices"] = w.meta["state_indices"].to(dev)
         sets.append(s)
@@ -145,6 +147,10 @@ def step_fn(w):
         def step(s):
             return sf.paged_gdn_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["pool"], s["state_indices"],
                                           cu_seqlens=s["cu_seqlens"], scale=w.scale)
+    elif w.name == "recurrent_kda":
+        def step(s):
+            return sf.kda_recurrent_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["pool"],
+                                        state_indices=s["state_indices"], scale=w.scale)
     elif w.name == "recurrent_gdn":
         def step(s):
             return sf.gdn_recurrent_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["pool"],
@@ -193,7 +199,10 @@ def cpu_baseline(w):
     args = dict(q=f(w.q), k=f(w.k), v=f(w.v), g=f(w.g))
     log(f"cpu_baseline: float64 oracle on {threads} threads ...")
     t0 = time.perf_counter()
-    if w.name in ("recurrent_gdn", "paged_gdn"):
+    if w.name == "recurrent_kda":
+        pool, idx = f(w.meta["pool"]), w.meta["state_indices"].numpy()
+        oracle.kda_forward(args["q"], args["k"], args["v"], args["g"], f(w.beta), pool[idx], scale=w.scale)
+    elif w.name in ("recurrent_gdn", "paged_gdn"):
         oracle.gdn_recurrent_paged(args["q"], args["k"], args["v"], args["g"], f(w.beta), f(w.meta["pool"]),
                                    w.meta["state_indices"].numpy(),
                                    cu_seqlens=None if w.cu_seqlens is None else w.cu_seqlens.numpy(), scale=w.scale)
@@ -237,7 +246,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="input sets cycled through (cache defeat)")
     ap.add_argument("--workload", default="dense_gdn",
                     choices=["dense_gdn", "tiny_gdn", "varlen_gdn", "long_gdn", "ssd_gla", "decode_gdn",
-                             "recurrent_gdn", "gate_transform", "paged_gdn"])
+                             "recurrent_gdn", "gate_transform", "paged_gdn", "recurrent_kda"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the second pass, whose launches are bracketed with HIP events")

@@ -28,6 +28,8 @@ Functions (same names as the C entry points, without the ``sf_`` prefix):
                         "Linear Attention", paged_chunk_gdn).
 * ``gdn_chunk_fwd_raw_gate`` gdn_chunk_fwd with the gate transform fused into its
                         Pre stage (raw gate projection in, no separate kernel).
+* ``kda_recurrent_fwd`` Kimi Delta Attention token by token (per-channel gate),
+                        optionally on a paged state pool.
 * ``gate_transform``    raw gate projections to float32 natural-log decays
                         (attention-gym "Linear Attention", "Gate Transforms").
 """
@@ -55,6 +57,7 @@ EXPORTED = (
     "sf_gla_chunk_fwd", "sf_segment_summary_workspace", "sf_segment_summary",
     "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_gdn_decode", "sf_gdn_recurrent_fwd", "sf_gate_transform",
     "sf_paged_gdn_chunk_fwd_workspace", "sf_paged_gdn_chunk_fwd", "sf_gdn_chunk_fwd_raw_gate",
+    "sf_kda_recurrent_fwd",
     "sf_timing_enable", "sf_timing_collect",
 )
 
@@ -109,6 +112,9 @@ def lib() -> ctypes.CDLL:
                                          P, P, P, Z, P]
     L.sf_gdn_chunk_fwd_raw_gate.restype = I
     L.sf_gdn_chunk_fwd_raw_gate.argtypes = [I, P, P, P, P, P, P, I, F, P, P, P, I, I, I, I, I, I, I, F, P, P, P, Z, P]
+    L.sf_kda_recurrent_fwd.restype = I
+    L.sf_kda_recurrent_fwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, I, I,
+                                       ctypes.c_longlong, P, P, P]
     L.sf_gate_transform.restype = I
     L.sf_gate_transform.argtypes = [I, P, P, P, ctypes.c_longlong, I, I, I, F, P, P]
     L.sf_timing_enable.restype = I
@@ -428,6 +434,58 @@ def paged_gdn_chunk_fwd(q, k, v, g, beta, state_cache, state_indices, *, cu_seql
                                         H, HK, K, V, float(scale), _ptr(out), _ptr(state_cache), pool_dt, NS, stride0,
                                         _ptr(state_indices), _ptr(has_initial_state), _ptr(ws), nbytes, _stream()))
     return out
+
+
+def kda_recurrent_fwd(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, scale=None,
+                      output_final_state=False, state_indices=None, has_initial_state=None):
+    """Kimi Delta Attention token by token. q, k, g [B,T,H,K] (g float32, one decay per key channel);
+    v [B,T,H,V]; beta [B,T,H] float32. State modes as gdn_recurrent_fwd (initial_state [N,H,V,K] float32,
+    or a paged pool with state_indices). Returns (output, final state or None)."""
+    _need(q, "q", ndim=4)
+    dev = q.device
+    _need(g, "g", dtype=torch.float32, ndim=4, device=dev)
+    if g.shape != q.shape:
+        raise ValueError(f"the per-channel gate must be shaped like q {tuple(q.shape)}, got {tuple(g.shape)}")
+    B, T, H, K = q.shape
+    if k.shape != q.shape or v.dim() != 4 or v.shape[:3] != (B, T, H):
+        raise ValueError("q, k [B,T,H,K] and v [B,T,H,V] must share B, T and H (no grouped heads)")
+    V = v.shape[3]
+    _need(k, "k", dtype=q.dtype, device=dev)
+    _need(v, "v", dtype=q.dtype, device=dev)
+    _need(beta, "beta", dtype=torch.float32, ndim=3, device=dev)
+    if beta.shape != (B, T, H):
+        raise ValueError("beta must be [B, T, H]")
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1, device=dev)
+        N = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+    if state_indices is None:
+        if has_initial_state is not None:
+            raise ValueError("has_initial_state needs state_indices")
+        if initial_state is not None:
+            _need(initial_state, "initial_state", dtype=torch.float32, ndim=4, device=dev)
+            if tuple(initial_state.shape) != (N, H, V, K):
+                raise ValueError(f"initial_state must be [{N}, {H}, {V}, {K}]")
+        ht = torch.empty((N, H, V, K), dtype=torch.float32, device=dev) if output_final_state else None
+        _check(lib().sf_kda_recurrent_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                          _ptr(cu_seqlens), N, B, T, H, K, V, float(scale), _ptr(out), _ptr(ht), None,
+                                          SF_F32, 0, 0, None, None, _stream()))
+        return out, ht
+    if output_final_state:
+        raise ValueError("output_final_state is rejected with state_indices: the pool is advanced in place")
+    _need(state_indices, "state_indices", dtype=torch.int32, ndim=1, device=dev)
+    if state_indices.numel() != N:
+        raise ValueError(f"state_indices must have {N} entries")
+    if has_initial_state is not None:
+        _need(has_initial_state, "has_initial_state", dtype=torch.bool, ndim=1, device=dev)
+    NS, stride0, pool_dt = _pool_layout(initial_state, H, V, K, dev)
+    _check(lib().sf_kda_recurrent_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), None, _ptr(cu_seqlens), N,
+                                      B, T, H, K, V, float(scale), _ptr(out), None, _ptr(initial_state), pool_dt, NS,
+                                      stride0, _ptr(state_indices), _ptr(has_initial_state), _stream()))
+    return out, None
 
 
 def gdn_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_cache, state_indices, *,

@@ -162,24 +162,26 @@ __device__ __forceinline__ float fma4(f32x4 x, f32x4 y, float a) {
 }
 
 // LDS plan of one recurrent workgroup: one token block, widened to float32 once for all rows
-template <int K>
+// (CH: per-channel gates, whose decay factors exp(g) take one more [16][K] block)
+template <int K, bool CH>
 struct RecLds {
     static constexpr int OFF_Q = 0;                                  // float [16][K]
     static constexpr int OFF_K = OFF_Q + kRecTok * K * 4;            // float [16][K]
-    static constexpr int OFF_V = OFF_K + kRecTok * K * 4;            // float [16][32]
+    static constexpr int OFF_A = OFF_K + kRecTok * K * 4;            // float [16][K] exp(g) (CH only)
+    static constexpr int OFF_V = OFF_A + (CH ? kRecTok * K * 4 : 0); // float [16][32]
     static constexpr int OFF_G = OFF_V + kRecTok * kRecRows * 4;     // float g[16], beta[16]
     static constexpr int OFF_O = OFF_G + 2 * kRecTok * 4;            // float outputs [wave][16][8]
     static constexpr int BYTES = OFF_O + kRecWaves * kRecTok * 8 * 4;
 };
 
-template <typename ET, typename PT, int K>
+template <typename ET, typename PT, int K, bool CH>
 __global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
     const ET* __restrict__ q, const ET* __restrict__ k, const ET* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, const float* __restrict__ h0, float* __restrict__ ht, PT* __restrict__ pool,
     long long slot_stride, int num_slots, const int32_t* __restrict__ state_indices,
     const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cu, int T, int H, int HK, int V, float scale,
     ET* __restrict__ out, int n_pairs) {
-    typedef RecLds<K> SM;
+    typedef RecLds<K, CH> SM;
     constexpr int CPL = K / kRecLpr;  // key columns per lane: lanes 8r .. 8r+7 hold state row r of the wavefront
     constexpr int NV = CPL / 4;       // four-column vectors per lane
     constexpr int NT = 64 * kRecWaves;
@@ -191,6 +193,7 @@ __global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
     typedef __attribute__((address_space(3))) f32x4 lds_f4;
     lds_f* const sQ = (lds_f*)(smem + SM::OFF_Q);
     lds_f* const sK = (lds_f*)(smem + SM::OFF_K);
+    lds_f* const sA = (lds_f*)(smem + SM::OFF_A);
     lds_f* const sV = (lds_f*)(smem + SM::OFF_V);
     lds_f* const sG = (lds_f*)(smem + SM::OFF_G);
 
@@ -241,6 +244,7 @@ __global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
     // results are never stored)
     struct Blk {
         RawT q[NQ], k[NQ];
+        f32x4 a[CH ? NQ : 1];  // per-channel gates (CH)
         float v0, v1, gb;
     };
     auto fetch = [&](int t0, Blk& x) __attribute__((always_inline)) {
@@ -251,19 +255,27 @@ __global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
             const size_t src = ((size_t)(b * T + tt) * HK + hk) * K + e % K;
             x.q[i] = Raw<ET>::load(q + src);
             x.k[i] = Raw<ET>::load(k + src);
+            if constexpr (CH) x.a[i] = *reinterpret_cast<const f32x4*>(g + ((size_t)(b * T + tt) * H + h) * K + e % K);
         }
         const int tv = min(t0 + tid / 16, last), rv = 2 * (tid % 16);
         const ET* vp = v + ((size_t)(b * T + tv) * H + h) * V + r0 + rv;
         x.v0 = Io<ET>::load1(vp);
         x.v1 = Io<ET>::load1(vp + 1);
         x.gb = 0.f;
-        if (tid < 2 * kRecTok) x.gb = (tid < kRecTok ? g : beta)[(size_t)(b * T + min(t0 + tid % kRecTok, last)) * H + h];
+        if (tid < 2 * kRecTok && (!CH || tid >= kRecTok))
+            x.gb = (tid < kRecTok ? g : beta)[(size_t)(b * T + min(t0 + tid % kRecTok, last)) * H + h];
     };
     auto stage = [&](const Blk& x) __attribute__((always_inline)) {  // widen into LDS
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             *(lds_f4*)(sQ + 4 * (tid + NT * i)) = Raw<ET>::cvt(x.q[i]);
             *(lds_f4*)(sK + 4 * (tid + NT * i)) = Raw<ET>::cvt(x.k[i]);
+            if constexpr (CH) {
+                f32x4 d;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[e] = expf(x.a[i][e]);
+                *(lds_f4*)(sA + 4 * (tid + NT * i)) = d;
+            }
         }
         sV[2 * tid] = x.v0;
         sV[2 * tid + 1] = x.v1;
@@ -282,7 +294,15 @@ __global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
         for (int tt = 0; tt < nt; ++tt) {
             const lds_f* qr = sQ + tt * K + c0;
             const lds_f* kr = sK + tt * K + c0;
-            const float gamma = expf(sG[tt]), bt = sG[kRecTok + tt], vv = sV[tt * kRecRows + rl];
+            const float bt = sG[kRecTok + tt], vv = sV[tt * kRecRows + rl];
+            float gamma = 1.f;
+            if constexpr (CH) {  // decay each key column by its own factor first
+                const lds_f* ar = sA + tt * K + c0;
+#pragma unroll
+                for (int i = 0; i < NV; ++i) S[i] = S[i] * *(const lds_f4*)(ar + 4 * i);
+            } else {
+                gamma = expf(sG[tt]);
+            }
             f32x4 kf[NV];
             float sk0 = 0.f, sk1 = 0.f;  // two accumulation chains
 #pragma unroll
@@ -298,7 +318,7 @@ __global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) S[i][e] = fmaf(kf[i][e], r, S[i][e] * gamma);
+                for (int e = 0; e < 4; ++e) S[i][e] = CH ? fmaf(kf[i][e], r, S[i][e]) : fmaf(kf[i][e], r, S[i][e] * gamma);
                 if (i & 1)
                     so1 = fma4(S[i], *(const lds_f4*)(qr + 4 * i), so1);
                 else
@@ -325,7 +345,7 @@ __global__ __launch_bounds__(64 * kRecWaves) void gdn_recurrent_kernel(
     }
 }
 
-template <typename ET, typename PT>
+template <typename ET, typename PT, bool CH>
 hipError_t launch_rec_typed(int K, const void* q, const void* k, const void* v, const float* g, const float* beta,
                             const float* h0, float* ht, void* pool, long long slot_stride, int num_slots,
                             const int32_t* idx, const uint8_t* has_init, const int32_t* cu, int N, int T, int H,
@@ -336,13 +356,13 @@ hipError_t launch_rec_typed(int K, const void* q, const void* k, const void* v, 
     PT* p = static_cast<PT*>(pool);
     ET* o = static_cast<ET*>(out);
     if (K == 64)
-        gdn_recurrent_kernel<ET, PT, 64><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride, num_slots,
+        gdn_recurrent_kernel<ET, PT, 64, CH><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride, num_slots,
                                                                 idx, has_init, cu, T, H, HK, V, scale, o, (int)pairs);
     else if (K == 128)
-        gdn_recurrent_kernel<ET, PT, 128><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride,
+        gdn_recurrent_kernel<ET, PT, 128, CH><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride,
                                                                  num_slots, idx, has_init, cu, T, H, HK, V, scale, o, (int)pairs);
     else
-        gdn_recurrent_kernel<ET, PT, 256><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride,
+        gdn_recurrent_kernel<ET, PT, 256, CH><<<grid, block, 0, s>>>(qq, kk, vv, g, beta, h0, ht, p, slot_stride,
                                                                  num_slots, idx, has_init, cu, T, H, HK, V, scale, o, (int)pairs);
     return hipGetLastError();
 }
@@ -372,24 +392,34 @@ hipError_t launch_typed(int K, const void* qkv, const void* rg, const void* rb, 
 
 }  // namespace
 
+template <bool CH>
+hipError_t launch_rec(bool bf16, bool pool_bf16, const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, const float* h0, float* ht, void* pool, long long slot_stride, int num_slots,
+                      const int32_t* state_indices, const uint8_t* has_init, const int32_t* cu, int N, int T, int H,
+                      int HK, int K, int V, float scale, void* out, hipStream_t s) {
+    if (bf16)
+        return pool_bf16 ? launch_rec_typed<bf16_t, bf16_t, CH>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
+                                                                state_indices, has_init, cu, N, T, H, HK, V, scale, out, s)
+                         : launch_rec_typed<bf16_t, float, CH>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
+                                                               state_indices, has_init, cu, N, T, H, HK, V, scale, out, s);
+    return pool_bf16 ? launch_rec_typed<float, bf16_t, CH>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
+                                                           state_indices, has_init, cu, N, T, H, HK, V, scale, out, s)
+                     : launch_rec_typed<float, float, CH>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
+                                                          state_indices, has_init, cu, N, T, H, HK, V, scale, out, s);
+}
+
 hipError_t launch_gdn_recurrent(bool bf16, bool pool_bf16, const void* q, const void* k, const void* v,
                                 const float* g, const float* beta, const float* h0, float* ht, void* pool,
                                 long long slot_stride, int num_slots, const int32_t* state_indices,
                                 const uint8_t* has_init, const int32_t* cu, int N, int T, int H, int HK, int K,
-                                int V, float scale, void* out, hipStream_t s) {
+                                int V, float scale, void* out, hipStream_t s, bool per_channel) {
     if (N == 0) return hipSuccess;
-    timing_begin("gdn_recurrent", s);
-    hipError_t e;
-    if (bf16)
-        e = pool_bf16 ? launch_rec_typed<bf16_t, bf16_t>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
-                                                         state_indices, has_init, cu, N, T, H, HK, V, scale, out, s)
-                      : launch_rec_typed<bf16_t, float>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
-                                                        state_indices, has_init, cu, N, T, H, HK, V, scale, out, s);
-    else
-        e = pool_bf16 ? launch_rec_typed<float, bf16_t>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
-                                                        state_indices, has_init, cu, N, T, H, HK, V, scale, out, s)
-                      : launch_rec_typed<float, float>(K, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots,
-                                                       state_indices, has_init, cu, N, T, H, HK, V, scale, out, s);
+    timing_begin(per_channel ? "kda_recurrent" : "gdn_recurrent", s);
+    const hipError_t e = per_channel
+        ? launch_rec<true>(bf16, pool_bf16, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots, state_indices,
+                           has_init, cu, N, T, H, HK, K, V, scale, out, s)
+        : launch_rec<false>(bf16, pool_bf16, q, k, v, g, beta, h0, ht, pool, slot_stride, num_slots, state_indices,
+                            has_init, cu, N, T, H, HK, K, V, scale, out, s);
     timing_end(s);
     return e;
 }

@@ -424,11 +424,12 @@ sf_status sf_gate_transform(sf_dtype dt, const void* raw, const float* A_log, co
     return hip_status(e, "sf_gate_transform launch");
 }
 
-sf_status sf_gdn_recurrent_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B, int T,
-                               int H, int HK, int K, int V, float scale, void* out, float* ht, void* state_pool,
-                               sf_dtype pool_dt, int num_slots, long long slot_stride, const int32_t* state_indices,
-                               const uint8_t* has_initial_state, void* stream) {
+namespace {
+sf_status recurrent_fwd(bool per_channel, sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B, int T, int H,
+                        int HK, int K, int V, float scale, void* out, float* ht, void* state_pool, sf_dtype pool_dt,
+                        int num_slots, long long slot_stride, const int32_t* state_indices,
+                        const uint8_t* has_initial_state, void* stream) {
     const bool packed = cu_seqlens != nullptr;
     sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
     if (st != SF_OK) return st;
@@ -454,11 +455,33 @@ sf_status sf_gdn_recurrent_fwd(sf_dtype dt, const void* q, const void* k, const 
     if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
     if ((h0 && reinterpret_cast<uintptr_t>(h0) % 16 != 0) || (ht && reinterpret_cast<uintptr_t>(ht) % 16 != 0))
         return fail(SF_ERR_INVALID, "h0 and ht must be 16-byte aligned");
+    if (per_channel && (reinterpret_cast<uintptr_t>(g) % 16 != 0))
+        return fail(SF_ERR_INVALID, "the per-channel gate must be 16-byte aligned");
     hipError_t e = sf::launch_gdn_recurrent(dt == SF_BF16, paged && pool_dt == SF_BF16, q, k, v, g, beta, h0, ht,
                                             paged ? state_pool : nullptr, slot_stride, num_slots, state_indices,
                                             has_initial_state, cu_seqlens, N, T, H, HK, K, V, scale, out,
-                                            static_cast<hipStream_t>(stream));
-    return hip_status(e, "sf_gdn_recurrent_fwd launch");
+                                            static_cast<hipStream_t>(stream), per_channel);
+    return hip_status(e, per_channel ? "sf_kda_recurrent_fwd launch" : "sf_gdn_recurrent_fwd launch");
+}
+}  // namespace
+
+sf_status sf_gdn_recurrent_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B, int T,
+                               int H, int HK, int K, int V, float scale, void* out, float* ht, void* state_pool,
+                               sf_dtype pool_dt, int num_slots, long long slot_stride, const int32_t* state_indices,
+                               const uint8_t* has_initial_state, void* stream) {
+    return recurrent_fwd(false, dt, q, k, v, g, beta, h0, cu_seqlens, N, B, T, H, HK, K, V, scale, out, ht, state_pool,
+                         pool_dt, num_slots, slot_stride, state_indices, has_initial_state, stream);
+}
+
+sf_status sf_kda_recurrent_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B, int T,
+                               int H, int K, int V, float scale, void* out, float* ht, void* state_pool,
+                               sf_dtype pool_dt, int num_slots, long long slot_stride, const int32_t* state_indices,
+                               const uint8_t* has_initial_state, void* stream) {
+    if (!fits((long)B * T * H * K)) return fail(SF_ERR_UNSUPPORTED, "the gate has 2^31 or more elements");
+    return recurrent_fwd(true, dt, q, k, v, g, beta, h0, cu_seqlens, N, B, T, H, H, K, V, scale, out, ht, state_pool,
+                         pool_dt, num_slots, slot_stride, state_indices, has_initial_state, stream);
 }
 
 sf_status sf_gdn_decode(sf_dtype dt, const void* packed_qkv, const void* raw_gate, const void* raw_beta,

@@ -101,11 +101,12 @@ hipError_t launch_gate_transform(bool bf16, bool bounded, const void* raw, const
 
 // Token-by-token delta-rule forward (decode.hip): the state from h0 (or zero) to ht, or, when
 // pool is non-null, from and back to the slots state_indices name (pool_bf16: its element type).
+// per_channel: Kimi Delta Attention, g [B, T, H, K] (one decay per key channel), HK == H.
 hipError_t launch_gdn_recurrent(bool bf16, bool pool_bf16, const void* q, const void* k, const void* v,
                                 const float* g, const float* beta, const float* h0, float* ht, void* pool,
                                 long long slot_stride, int num_slots, const int32_t* state_indices,
                                 const uint8_t* has_init, const int32_t* cu, int N, int T, int H, int HK, int K,
-                                int V, float scale, void* out, hipStream_t s);
+                                int V, float scale, void* out, hipStream_t s, bool per_channel = false);
 
 // One-token paged delta-rule decode (decode.hip). pool_bf16: the pool's element type.
 hipError_t launch_gdn_decode(bool bf16, bool pool_bf16, const void* qkv, const void* raw_gate,

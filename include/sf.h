@@ -290,6 +290,22 @@ sf_status sf_gdn_recurrent_fwd(sf_dtype dt, const void *q, const void *k, const 
                                void *stream);
 
 /*
+ * Kimi Delta Attention, token by token (attention-gym "Linear Attention",
+ * section "Kimi Delta Attention": the per-channel gate; at each token the
+ * previous state is multiplied channelwise by exp(g), then the delta rule's
+ * correction and update and the read with q): decayed = S diag(exp(g_t)),
+ * r = beta_t (v_t - decayed k_t), S = decayed + r k_t^T, o_t = scale S q_t.
+ * Arguments, state modes and errors as sf_gdn_recurrent_fwd, except:
+ *   q, k, g [B, T, H, K] (no grouped heads; g float32, 16-byte aligned).
+ */
+sf_status sf_kda_recurrent_fwd(sf_dtype dt, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *h0,
+                               const int32_t *cu_seqlens, int N, int B, int T, int H, int K, int V,
+                               float scale, void *out, float *ht, void *state_pool, sf_dtype pool_dt,
+                               int num_slots, long long slot_stride, const int32_t *state_indices,
+                               const uint8_t *has_initial_state, void *stream);
+
+/*
  * One-token paged Gated Delta Rule decode (attention-gym "Linear Attention":
  * the recurrent_gdn_decode entry; section "Gate Transforms" for the gate).
  * For every sequence b < B and value head h < H, in float32:

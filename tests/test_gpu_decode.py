@@ -371,3 +371,64 @@ def test_raw_gate_chunk_vs_oracle(dev, case):
         eo, eh = rel_rms(o, ref_o), rel_rms(ht, ref_ht)
         say(f"{name}: rel_rms o {eo:.3g}  ht {eh:.3g}")
         assert eo <= BF16_RTOL and eh <= BF16_RTOL
+
+
+# ---------------------------------------------------------------------------------------------
+# Kimi Delta Attention token by token (sf_kda_recurrent_fwd)
+# ---------------------------------------------------------------------------------------------
+
+KDA_CASES = [
+    # name, dtype, B, T, H, K, V, h0, lengths (packed) or None
+    ("f32-k64-h0", torch.float32, 2, 37, 3, 64, 64, True, None),
+    ("bf16-k128-h0", torch.bfloat16, 2, 50, 4, 128, 128, True, None),
+    ("bf16-packed", torch.bfloat16, 1, 0, 2, 128, 64, True, [9, 0, 33, 17]),
+]
+
+
+@pytest.mark.parametrize("case", KDA_CASES, ids=[c[0] for c in KDA_CASES])
+def test_kda_recurrent_vs_oracle(dev, case):
+    name, dt, B, T, H, K, V, with_h0, lens = case
+    cu = None
+    if lens is not None:
+        T = int(sum(lens))
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    N = B if lens is None else len(lens)
+    say(f"kda {name}: B={B} T={T} H={H} K={K} V={V} N={N}")
+    d = wl.kda_inputs(B=B, T=T, H=H, K=K, V=V, dtype=dt, seed=zlib.crc32(name.encode()) % 1000, gate_shift=0.5,
+                      h0_std=0.3 if with_h0 else None, N=N)
+    g = {n: (None if d[n] is None else d[n].to(dev).contiguous()) for n in ("q", "k", "v", "g", "beta", "h0")}
+    o, ht = sf.kda_recurrent_fwd(g["q"], g["k"], g["v"], g["g"], g["beta"], g["h0"],
+                                 cu_seqlens=None if cu is None else cu.to(dev), scale=0.3, output_final_state=True)
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    ref_o, ref_ht = oracle.kda_forward(f(d["q"]), f(d["k"]), f(d["v"]), f(d["g"]), f(d["beta"]), f(d["h0"]),
+                                       cu_seqlens=None if cu is None else cu.numpy(), scale=0.3)
+    o, ht = o.float().cpu().numpy(), ht.cpu().numpy()
+    if dt == torch.float32:
+        eo, eh = float(np.max(np.abs(o - ref_o))), float(np.max(np.abs(ht - ref_ht)))
+        say(f"{name}: max|o|err {eo:.3g}  max|ht|err {eh:.3g}")
+        assert eo <= FP32_ATOL and eh <= FP32_ATOL
+    else:
+        eo, eh = rel_rms(o, ref_o), rel_rms(ht, ref_ht)
+        say(f"{name}: rel_rms o {eo:.3g}  ht {eh:.3g}")
+        assert eo <= BF16_RTOL and eh <= BF16_RTOL
+
+
+def test_kda_recurrent_paged_full_size(dev):
+    """The bench's KDA workload (64 sequences of 16 tokens, H=32, K=V=128, bf16, float32 pool), every
+    sequence and head against the oracle started from the same slots."""
+    w = wl.recurrent_kda()
+    say("kda: full-size workload")
+    pool = w.meta["pool"].to(dev).contiguous()
+    idx = w.meta["state_indices"]
+    o, _ = sf.kda_recurrent_fwd(w.q.to(dev), w.k.to(dev), w.v.to(dev), w.g.to(dev), w.beta.to(dev), pool,
+                                state_indices=idx.to(dev), scale=w.scale)
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    p0 = f(w.meta["pool"])
+    ref_o, ref_ht = oracle.kda_forward(f(w.q), f(w.k), f(w.v), f(w.g), f(w.beta), p0[idx.numpy()], scale=w.scale)
+    eo = rel_rms(o.float().cpu().numpy(), ref_o)
+    eh = rel_rms(pool.cpu().numpy()[idx.numpy()], ref_ht)
+    say(f"recurrent_kda: rel_rms o {eo:.3g}  S {eh:.3g}")
+    assert eo <= BF16_RTOL and eh <= BF16_RTOL
+    assert np.array_equal(pool[0].cpu().numpy(), p0[0])

@@ -29,6 +29,8 @@ and one decode workload (one token per sequence against a paged state pool):
 8. ``gate_transform`` per-channel raw gates [2, 16384, 16, 128] bf16, softplus kind.
 9. ``paged_gdn``      the packed workload's stream on a float32 state pool (chunk
                       forward advancing the cache in place).
+10. ``recurrent_kda`` recurrent_gdn's shapes with a per-channel gate (Kimi Delta
+                      Attention token by token).
 
 Draw order inside one workload: q, k, v, gate noise, beta noise, h0, A, dt,
 sequence lengths.
@@ -43,7 +45,7 @@ import torch
 
 SEEDS = {"tiny_gdn": 101, "dense_gdn": 102, "varlen_gdn": 103, "long_gdn": 104, "ssd_gla": 105,
          "decode_gdn": 106, "recurrent_gdn": 107, "gate_transform": 108,
-         "paged_gdn": 109}
+         "paged_gdn": 109, "recurrent_kda": 110}
 
 
 @dataclass
@@ -218,6 +220,31 @@ def paged_gdn(seed=SEEDS["paged_gdn"], *, T=32768, H=32, D=128, n_long=7):
     return w
 
 
+def kda_inputs(*, B, T, H, K, V, dtype=torch.bfloat16, seed=0, gate_shift=2.0, h0_std=None, N=None):
+    """q, k (unit rows), v ~ N(0,1); per-channel g = -softplus(N(0,1) + gate_shift) [B, T, H, K];
+    beta = sigmoid(N(0,1))."""
+    rng = np.random.default_rng(seed)
+    q = _l2rows(_normal(rng, (B, T, H, K)))
+    k = _l2rows(_normal(rng, (B, T, H, K)))
+    v = _normal(rng, (B, T, H, V))
+    g = -_softplus(_normal(rng, (B, T, H, K)) + np.float32(gate_shift))
+    beta = _sigmoid(_normal(rng, (B, T, H)))
+    h0 = None if h0_std is None else torch.from_numpy(_normal(rng, (N or B, H, V, K)) * np.float32(h0_std))
+    return dict(q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype), g=torch.from_numpy(g),
+                beta=torch.from_numpy(beta), h0=h0, rng=rng)
+
+
+def recurrent_kda(seed=SEEDS["recurrent_kda"], *, B=64, T=16, H=32, D=128):
+    """recurrent_gdn's shapes and pool with a per-channel gate (a reading, as there)."""
+    d = kda_inputs(B=B, T=T, H=H, K=D, V=D, seed=seed)
+    rng = d["rng"]
+    pool = _normal(rng, (B + 1, H, D, D)) * np.float32(0.02)
+    idx = rng.permutation(np.arange(1, B + 1)).astype(np.int32)
+    return Workload("recurrent_kda", "kda", d["q"], d["k"], d["v"], d["g"], d["beta"], None, None,
+                    scale=1.0 / np.sqrt(D), chunk=0,
+                    meta={"pool": torch.from_numpy(pool), "state_indices": torch.from_numpy(idx)})
+
+
 def long_gdn(seed=SEEDS["long_gdn"], *, T=262144, H=16, D=128, n_seg=16):
     """bf16 delta rule on one long row cut into n_seg segments; g = -softplus(N(0,1) + 4) as the
     formula gives it (its decay is fast, whatever the label says); zero initial state; scale 1/sqrt(D)."""
@@ -345,7 +372,7 @@ def gate_transform(seed=SEEDS["gate_transform"], *, B=2, T=16384, H=16, D=128):
 CONFIGS = {"tiny_gdn": tiny_gdn, "dense_gdn": dense_gdn, "varlen_gdn": varlen_gdn,
            "long_gdn": long_gdn, "ssd_gla": ssd_gla, "decode_gdn": decode_gdn,
            "recurrent_gdn": recurrent_gdn, "gate_transform": gate_transform,
-           "paged_gdn": paged_gdn}
+           "paged_gdn": paged_gdn, "recurrent_kda": recurrent_kda}
 
 
 def to_f32(t):
