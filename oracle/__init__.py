@@ -29,6 +29,7 @@ What each function follows (pages by title and section):
   per-channel gates (``decode.py``).
 * ``kda_forward``   the section "Kimi Delta Attention": the token rule with a
   per-channel decay (``decode.py``, numpy float64).
+* ``kda_decode``    the ``recurrent_kda_decode`` entry (``decode.py``).
 
 Pins: tests/test_oracle.py checks every function against closed forms,
 brute-force products or invariants that do not reuse this code.
@@ -198,4 +199,4 @@ def chunked_forward(kind, q, k, v, g, beta=None, h0=None, cu_seqlens=None, scale
     return out, ht
 
 
-from .decode import gate_transform, gdn_decode, gdn_recurrent_paged, kda_forward  # noqa: E402  (numpy float64, no C part)
+from .decode import gate_transform, gdn_decode, gdn_recurrent_paged, kda_decode, kda_forward  # noqa: E402  (numpy float64, no C part)

@@ -181,3 +181,39 @@ def kda_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None):
         ht[n] = S
     return out, ht
 
+
+def kda_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_pool, state_indices,
+               has_initial_state=None, *, H, K, V, kind="bounded", lower_bound=-5.0, scale=None):
+    """One-token paged KDA decode (attention-gym "Linear Attention", the recurrent_kda_decode entry):
+    packed_qkv [B, H (2K + V)] (all query heads, all key heads, all value heads); raw_gate [B, H, K]
+    (or [1, B, H, K]) through gate_transform with dt_bias [H, K] (per-channel); raw_beta [B, H] through
+    the sigmoid; q and k L2-normalised; then the KDA token rule on the slot's state. Slot rules as
+    gdn_decode. Returns (out [B, H, V], pool), float64."""
+    x = np.asarray(packed_qkv, dtype=np.float64)
+    B = x.shape[0]
+    assert x.shape[1] == H * (2 * K + V)
+    rg = np.asarray(raw_gate, dtype=np.float64).reshape(B, H, K)
+    rb = np.asarray(raw_beta, dtype=np.float64).reshape(B, H)
+    gate = gate_transform(rg, A_log, dt_bias, kind, lower_bound if kind == "bounded" else None)  # [B, H, K]
+    pool = np.array(state_pool, dtype=np.float64, copy=True)
+    idx = np.asarray(state_indices).astype(np.int64)
+    init = np.ones(B, dtype=bool) if has_initial_state is None else np.asarray(has_initial_state, dtype=bool)
+    if scale is None:
+        scale = 1.0 / np.sqrt(K)
+    out = np.zeros((B, H, V))
+    for b in range(B):
+        slot = int(idx[b])
+        if slot <= 0:
+            continue
+        for h in range(H):
+            q = l2_normalise(x[b, h * K:(h + 1) * K])
+            k = l2_normalise(x[b, H * K + h * K:H * K + (h + 1) * K])
+            v = x[b, 2 * H * K + h * V:2 * H * K + (h + 1) * V]
+            S = pool[slot, h].copy() if init[b] else np.zeros((V, K))
+            S = S * np.exp(gate[b, h])[None, :]      # channelwise decay of the key columns
+            r = write_gate(rb[b, h]) * (v - S @ k)
+            S = S + np.outer(r, k)
+            out[b, h] = scale * (S @ q)
+            pool[slot, h] = S
+    return out, pool
+

@@ -310,3 +310,45 @@ def test_kda_packed_equals_separate():
         np.testing.assert_array_equal(ht[n], h1[0])
     np.testing.assert_array_equal(ht[1], h0[1])                     # the empty sequence passes its state
 
+
+def test_kda_decode_pins():
+    """Uniform per-channel raw gates and biases with the softplus kind are GDN's per-head gate: the KDA
+    decode equals gdn_decode (H = HK); and T decode steps equal kda_forward on the normalised q, k
+    and the transformed gates (each prepared with the decode module's pinned helpers)."""
+    rng = np.random.default_rng(14)
+    B, Hh, Kk, Vv = 3, 2, 6, 5
+    pool = rng.standard_normal((5, Hh, Vv, Kk)) * 0.3
+    idx = np.array([4, 0, 2])
+    x = rng.standard_normal((B, Hh * (2 * Kk + Vv)))
+    rg = rng.standard_normal((B, Hh))
+    rb = rng.standard_normal((B, Hh))
+    A = rng.standard_normal(Hh) * 0.3
+    bias = rng.standard_normal(Hh)
+    o1, p1 = oracle.kda_decode(x, np.repeat(rg[..., None], Kk, -1), rb, A, np.repeat(bias[:, None], Kk, -1), pool, idx,
+                               H=Hh, K=Kk, V=Vv, kind="softplus", lower_bound=None, scale=0.4)
+    o2, p2 = oracle.gdn_decode(x, rg, rb, A, bias, pool, idx, H=Hh, HK=Hh, K=Kk, V=Vv, scale=0.4)
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(p1, p2, rtol=1e-13, atol=1e-15)
+    # T steps against the KDA token recurrence (bounded kind)
+    T = 4
+    xs = rng.standard_normal((T, B, Hh * (2 * Kk + Vv)))
+    rgs = rng.standard_normal((T, B, Hh, Kk))
+    rbs = rng.standard_normal((T, B, Hh))
+    dtb = rng.standard_normal((Hh, Kk))
+    cur, outs = pool, []
+    for t in range(T):
+        o, cur = oracle.kda_decode(xs[t], rgs[t], rbs[t], A, dtb, cur, idx, H=Hh, K=Kk, V=Vv, scale=0.4)
+        outs.append(o)
+    qn = np.apply_along_axis(dec.l2_normalise, -1, xs[..., :Hh * Kk].reshape(T, B, Hh, Kk))
+    kn = np.apply_along_axis(dec.l2_normalise, -1, xs[..., Hh * Kk:2 * Hh * Kk].reshape(T, B, Hh, Kk))
+    vv = xs[..., 2 * Hh * Kk:].reshape(T, B, Hh, Vv)
+    gate = dec.gate_transform(rgs, A, dtb, "bounded", -5.0)
+    beta = dec.write_gate(rbs)
+    tr = lambda a: np.swapaxes(a, 0, 1)   # [T, B, ...] -> [B, T, ...]
+    for b in (0, 2):
+        ref_o, ref_h = oracle.kda_forward(tr(qn)[b:b + 1], tr(kn)[b:b + 1], tr(vv)[b:b + 1], tr(gate)[b:b + 1],
+                                          tr(beta)[b:b + 1], pool[idx[b]][None], scale=0.4)
+        np.testing.assert_allclose(np.stack(outs)[:, b], ref_o[0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(cur[idx[b]], ref_h[0], rtol=1e-12, atol=1e-14)
+    assert np.all(np.stack(outs)[:, 1] == 0)
+
