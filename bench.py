@@ -20,7 +20,7 @@ carry measured_peak: the bandwidth a plain 1 GiB device-to-device copy reaches
 on the same GPU (read plus write bytes), and the fraction of that.
 
 Other workloads (--workload varlen_gdn | long_gdn | ssd_gla | tiny_gdn | decode_gdn | recurrent_gdn |
-gate_transform | paged_gdn | recurrent_kda) are for
+gate_transform | paged_gdn | recurrent_kda | decode_kda) are for
 measurement only; the headline line is the default one. decode_gdn times one sf_gdn_decode call
 (one token for each of 256 sequences against a 514 MB float32 state pool, which is larger than
 the last-level cache, so it runs on one input set).
@@ -55,8 +55,8 @@ def decode_bytes(w):
     active = w.state_indices > 0
     loaded = active if w.has_initial_state is None else active & w.has_initial_state
     states = (int(active.sum()) + int(loaded.sum())) * w.H * w.V * w.K * pe
-    rows = w.B * (w.packed_qkv.shape[1] + 2 * w.H) * eb + w.B * w.H * w.V * eb
-    return states + rows + 2 * w.H * 4 + w.B * 4
+    rows = (w.packed_qkv.numel() + w.raw_gate.numel() + w.raw_beta.numel()) * eb + w.B * w.H * w.V * eb
+    return states + rows + (w.A_log.numel() + w.dt_bias.numel()) * 4 + w.B * 4
 
 
 def algorithmic_bytes(w, kernel):
@@ -66,7 +66,7 @@ def algorithmic_bytes(w, kernel):
     (HK/H of q and k per value head), plus gate and beta in float32; per
     (sequence, head): the initial state read (when given) and the final state
     written, V*K float32 each."""
-    if kernel in ("gdn_decode", "decode_path"):
+    if kernel in ("gdn_decode", "kda_decode", "decode_path"):
         return decode_bytes(w)
     if kernel in ("gate_transform", "gate_path"):   # raw in, float32 out, the per-head parameters
         return w.raw.numel() * (w.raw.element_size() + 4) + (w.A_log.numel() + w.dt_bias.numel()) * 4
@@ -138,6 +138,11 @@ def step_fn(w):
     if w.name == "gate_transform":
         def step(s):
             return sf.gate_transform(s["raw"], s["A_log"], s["dt_bias"], kind=w.kind, lower_bound=w.lower_bound)
+    elif w.name == "decode_kda":
+        def step(s):
+            return sf.kda_decode(s["packed_qkv"], s["raw_gate"], s["raw_beta"], s["A_log"], s["dt_bias"], s["pool"],
+                                 s["state_indices"], has_initial_state=s["has_initial_state"],
+                                 gate_transform=w.gate_kind, lower_bound=w.lower_bound, scale=w.scale, out=s["out"])
     elif w.name == "decode_gdn":
         def step(s):
             return sf.gdn_decode(s["packed_qkv"], s["raw_gate"], s["raw_beta"], s["A_log"], s["dt_bias"], s["pool"],
@@ -189,9 +194,15 @@ def cpu_baseline(w):
     if isinstance(w, wl.DecodeWorkload):
         log("cpu_baseline: float64 decode oracle (numpy, one step) ...")
         t0 = time.perf_counter()
-        oracle.gdn_decode(f(w.packed_qkv), f(w.raw_gate), f(w.raw_beta), f(w.A_log), f(w.dt_bias), f(w.pool),
-                          w.state_indices.numpy(), None if w.has_initial_state is None else w.has_initial_state.numpy(),
-                          H=w.H, HK=w.HK, K=w.K, V=w.V, scale=w.scale)
+        if w.per_channel:
+            oracle.kda_decode(f(w.packed_qkv), f(w.raw_gate), f(w.raw_beta), f(w.A_log), f(w.dt_bias), f(w.pool),
+                              w.state_indices.numpy(), None, H=w.H, K=w.K, V=w.V, kind=w.gate_kind,
+                              lower_bound=w.lower_bound, scale=w.scale)
+        else:
+            oracle.gdn_decode(f(w.packed_qkv), f(w.raw_gate), f(w.raw_beta), f(w.A_log), f(w.dt_bias), f(w.pool),
+                              w.state_indices.numpy(),
+                              None if w.has_initial_state is None else w.has_initial_state.numpy(),
+                              H=w.H, HK=w.HK, K=w.K, V=w.V, scale=w.scale)
         dt = time.perf_counter() - t0
         return {"value": w.tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                 "sample": f"the whole {w.name} step ({w.tokens} rows x {w.H} heads), one float64 pass, "
@@ -246,7 +257,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="input sets cycled through (cache defeat)")
     ap.add_argument("--workload", default="dense_gdn",
                     choices=["dense_gdn", "tiny_gdn", "varlen_gdn", "long_gdn", "ssd_gla", "decode_gdn",
-                             "recurrent_gdn", "gate_transform", "paged_gdn", "recurrent_kda"])
+                             "recurrent_gdn", "gate_transform", "paged_gdn", "recurrent_kda", "decode_kda"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the second pass, whose launches are bracketed with HIP events")

@@ -30,6 +30,7 @@ Functions (same names as the C entry points, without the ``sf_`` prefix):
                         Pre stage (raw gate projection in, no separate kernel).
 * ``kda_recurrent_fwd`` Kimi Delta Attention token by token (per-channel gate),
                         optionally on a paged state pool.
+* ``kda_decode``        one-token paged KDA decode (recurrent_kda_decode).
 * ``gate_transform``    raw gate projections to float32 natural-log decays
                         (attention-gym "Linear Attention", "Gate Transforms").
 """
@@ -57,7 +58,7 @@ EXPORTED = (
     "sf_gla_chunk_fwd", "sf_segment_summary_workspace", "sf_segment_summary",
     "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_gdn_decode", "sf_gdn_recurrent_fwd", "sf_gate_transform",
     "sf_paged_gdn_chunk_fwd_workspace", "sf_paged_gdn_chunk_fwd", "sf_gdn_chunk_fwd_raw_gate",
-    "sf_kda_recurrent_fwd",
+    "sf_kda_recurrent_fwd", "sf_kda_decode",
     "sf_timing_enable", "sf_timing_collect",
 )
 
@@ -115,6 +116,8 @@ def lib() -> ctypes.CDLL:
     L.sf_kda_recurrent_fwd.restype = I
     L.sf_kda_recurrent_fwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, I, I,
                                        ctypes.c_longlong, P, P, P]
+    L.sf_kda_decode.restype = I
+    L.sf_kda_decode.argtypes = [I, P, P, P, P, P, I, F, P, I, I, ctypes.c_longlong, P, P, I, I, I, I, F, P, P]
     L.sf_gate_transform.restype = I
     L.sf_gate_transform.argtypes = [I, P, P, P, ctypes.c_longlong, I, I, I, F, P, P]
     L.sf_timing_enable.restype = I
@@ -574,6 +577,54 @@ def gate_transform(raw_gate, A_log, dt_bias, *, kind, lower_bound=None):
     out = torch.empty(raw_gate.shape, dtype=torch.float32, device=dev)
     _check(lib().sf_gate_transform(_dt(raw_gate), _ptr(raw_gate), _ptr(A_log), _ptr(dt_bias), rows, H, D,
                                    GATE_KINDS[kind], float(lower_bound or 0.0), _ptr(out), _stream()))
+    return out
+
+
+def kda_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_cache, state_indices, *,
+               has_initial_state=None, gate_transform="bounded", lower_bound=-5.0, scale=None, out=None):
+    """One KDA decode token per sequence; advances state_cache in place. packed_qkv [B, H*(2K + V)];
+    raw_gate [1, B, H, K] or [B, H, K]; raw_beta [1, B, H]; A_log [H]; dt_bias [H, K] (float32);
+    gate_transform "bounded" (lower_bound) or "softplus". Returns out [1, B, H, V]."""
+    if gate_transform not in GATE_KINDS:
+        raise ValueError(f"gate_transform must be one of {sorted(GATE_KINDS)}")
+    if gate_transform == "bounded" and (lower_bound is None or not math.isfinite(lower_bound) or lower_bound > 0):
+        raise ValueError("the bounded kind needs a finite lower_bound <= 0")
+    _need(packed_qkv, "packed_qkv", ndim=2)
+    dev = packed_qkv.device
+    B, W = packed_qkv.shape
+    if not isinstance(state_cache, torch.Tensor) or state_cache.dim() != 4:
+        raise ValueError("state_cache must be a [num_slots, H, V, K] GPU tensor")
+    NS, H, V, K = state_cache.shape
+    NS, stride0, pool_dt = _pool_layout(state_cache, H, V, K, dev)
+    if W != H * (2 * K + V):
+        raise ValueError(f"packed_qkv width {W} must be H*(2K + V) = {H * (2 * K + V)}")
+    _need(raw_gate, "raw_gate", dtype=packed_qkv.dtype, device=dev)
+    if raw_gate.numel() != B * H * K:
+        raise ValueError(f"raw_gate must hold [1, {B}, {H}, {K}] values")
+    _need(raw_beta, "raw_beta", dtype=packed_qkv.dtype, device=dev)
+    if raw_beta.numel() != B * H:
+        raise ValueError(f"raw_beta must hold [1, {B}, {H}] values")
+    _need(A_log, "A_log", dtype=torch.float32, ndim=1, device=dev)
+    _need(dt_bias, "dt_bias", dtype=torch.float32, ndim=2, device=dev)
+    if A_log.numel() != H or tuple(dt_bias.shape) != (H, K):
+        raise ValueError(f"A_log must be [{H}] and dt_bias [{H}, {K}]")
+    _need(state_indices, "state_indices", dtype=torch.int32, ndim=1, device=dev)
+    if state_indices.numel() != B:
+        raise ValueError(f"state_indices must have {B} entries")
+    if has_initial_state is not None:
+        _need(has_initial_state, "has_initial_state", dtype=torch.bool, ndim=1, device=dev)
+    if out is None:
+        out = torch.empty((1, B, H, V), dtype=packed_qkv.dtype, device=dev)
+    else:
+        _need(out, "out", dtype=packed_qkv.dtype, device=dev)
+        if out.numel() != B * H * V:
+            raise ValueError(f"out must hold [1, {B}, {H}, {V}] values")
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    _check(lib().sf_kda_decode(_dt(packed_qkv), _ptr(packed_qkv), _ptr(raw_gate), _ptr(raw_beta), _ptr(A_log),
+                               _ptr(dt_bias), GATE_KINDS[gate_transform], float(lower_bound or 0.0), _ptr(state_cache),
+                               pool_dt, NS, stride0, _ptr(state_indices), _ptr(has_initial_state), B, H, K, V,
+                               float(scale), _ptr(out), _stream()))
     return out
 
 

@@ -68,12 +68,16 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
 
-template <typename ET, typename PT, int K>
+// CH: Kimi Delta Attention (recurrent_kda_decode): raw_gate [B, H, K] and dt_bias [H, K] per key
+// channel through the bounded (lower_bound sigmoid(exp(A_log) a)) or softplus kind, each key column
+// decayed by its own factor; without CH the per-head softplus gate of the delta rule.
+template <typename ET, typename PT, int K, bool CH>
 __global__ __launch_bounds__(64 * kDecodeWaves) void gdn_decode_kernel(
     const ET* __restrict__ qkv, const ET* __restrict__ raw_gate, const ET* __restrict__ raw_beta,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias, PT* __restrict__ pool,
     long long slot_stride, int num_slots, const int32_t* __restrict__ state_indices,
-    const uint8_t* __restrict__ has_init, int H, int HK, int V, float scale, ET* __restrict__ out) {
+    const uint8_t* __restrict__ has_init, int H, int HK, int V, float scale, ET* __restrict__ out, int bounded,
+    float lower_bound) {
     constexpr int LPR = K / 4;      // lanes per state row
     constexpr int RPI = 64 / LPR;   // rows per wavefront instruction
     const int b = blockIdx.x / H, h = blockIdx.x - b * H;
@@ -94,9 +98,20 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gdn_decode_kernel(
     qv = qv * (1.f / sqrtf(group_sum<LPR>(dot4(qv, qv)) + kL2Eps));
     kv = kv * (1.f / sqrtf(group_sum<LPR>(dot4(kv, kv)) + kL2Eps));
     // gates: softplus(a) = max(a, 0) + log(1 + exp(-|a|)) never overflows
-    const float a = Io<ET>::load1(raw_gate + (size_t)b * H + h) + dt_bias[h];
-    const float sp = fmaxf(a, 0.f) + log1pf(expf(-fabsf(a)));
-    const float gamma = expf(-expf(A_log[h]) * sp);
+    float gamma = 1.f;
+    f32x4 alpha = {1.f, 1.f, 1.f, 1.f};  // per-channel decay of columns c0..c0+3 (CH)
+    if constexpr (CH) {
+        const f32x4 a = Io<ET>::load4(raw_gate + ((size_t)b * H + h) * K + c0) +
+                        *reinterpret_cast<const f32x4*>(dt_bias + (size_t)h * K + c0);
+        const float amp = expf(A_log[h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            alpha[e] = expf(bounded ? lower_bound / (1.f + expf(-amp * a[e]))
+                                    : -amp * (fmaxf(a[e], 0.f) + log1pf(expf(-fabsf(a[e])))));
+    } else {
+        const float a = Io<ET>::load1(raw_gate + (size_t)b * H + h) + dt_bias[h];
+        gamma = expf(-expf(A_log[h]) * (fmaxf(a, 0.f) + log1pf(expf(-fabsf(a)))));
+    }
     const float beta = 1.f / (1.f + expf(-Io<ET>::load1(raw_beta + (size_t)b * H + h)));
     const bool init = has_init == nullptr || has_init[b] != 0;
 
@@ -118,8 +133,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gdn_decode_kernel(
         for (int j = 0; j < kDecodeBatch; ++j) {
             if (i0 + j < nit) {  // uniform over the wavefront: the group sums run on full lanes
                 const int row = w * rows_w + (i0 + j) * RPI + rin;
-                const float r = beta * (vv[j] - gamma * group_sum<LPR>(dot4(S[j], kv)));
-                const f32x4 Sn = S[j] * gamma + kv * r;
+                const f32x4 Sd = CH ? S[j] * alpha : S[j];  // (the scalar decay is folded in below)
+                const float r = beta * (vv[j] - gamma * group_sum<LPR>(dot4(Sd, kv)));
+                const f32x4 Sn = CH ? Sd + kv * r : S[j] * gamma + kv * r;
                 const float ov = group_sum<LPR>(dot4(Sn, qv));
                 Io<PT>::store4(S0 + (size_t)row * K + c0, Sn);
                 if (lane % LPR == 0) Io<ET>::store1(o + row, scale * ov);
@@ -367,11 +383,11 @@ hipError_t launch_rec_typed(int K, const void* q, const void* k, const void* v, 
     return hipGetLastError();
 }
 
-template <typename ET, typename PT>
+template <typename ET, typename PT, bool CH>
 hipError_t launch_typed(int K, const void* qkv, const void* rg, const void* rb, const float* A_log,
                         const float* dt_bias, void* pool, long long slot_stride, int num_slots,
                         const int32_t* idx, const uint8_t* has_init, int B, int H, int HK, int V,
-                        float scale, void* out, hipStream_t s) {
+                        float scale, void* out, hipStream_t s, int bounded, float lb) {
     const dim3 grid((unsigned)B * (unsigned)H), block(64 * kDecodeWaves);
     const ET* q = static_cast<const ET*>(qkv);
     const ET* g = static_cast<const ET*>(rg);
@@ -379,14 +395,14 @@ hipError_t launch_typed(int K, const void* qkv, const void* rg, const void* rb, 
     PT* p = static_cast<PT*>(pool);
     ET* o = static_cast<ET*>(out);
     if (K == 64)
-        gdn_decode_kernel<ET, PT, 64><<<grid, block, 0, s>>>(q, g, bt, A_log, dt_bias, p, slot_stride, num_slots, idx,
-                                                             has_init, H, HK, V, scale, o);
+        gdn_decode_kernel<ET, PT, 64, CH><<<grid, block, 0, s>>>(q, g, bt, A_log, dt_bias, p, slot_stride, num_slots, idx,
+                                                             has_init, H, HK, V, scale, o, bounded, lb);
     else if (K == 128)
-        gdn_decode_kernel<ET, PT, 128><<<grid, block, 0, s>>>(q, g, bt, A_log, dt_bias, p, slot_stride, num_slots, idx,
-                                                              has_init, H, HK, V, scale, o);
+        gdn_decode_kernel<ET, PT, 128, CH><<<grid, block, 0, s>>>(q, g, bt, A_log, dt_bias, p, slot_stride, num_slots, idx,
+                                                              has_init, H, HK, V, scale, o, bounded, lb);
     else
-        gdn_decode_kernel<ET, PT, 256><<<grid, block, 0, s>>>(q, g, bt, A_log, dt_bias, p, slot_stride, num_slots, idx,
-                                                              has_init, H, HK, V, scale, o);
+        gdn_decode_kernel<ET, PT, 256, CH><<<grid, block, 0, s>>>(q, g, bt, A_log, dt_bias, p, slot_stride, num_slots, idx,
+                                                              has_init, H, HK, V, scale, o, bounded, lb);
     return hipGetLastError();
 }
 
@@ -424,24 +440,35 @@ hipError_t launch_gdn_recurrent(bool bf16, bool pool_bf16, const void* q, const 
     return e;
 }
 
+template <bool CH>
+hipError_t launch_dec(bool bf16, bool pool_bf16, const void* qkv, const void* raw_gate, const void* raw_beta,
+                      const float* A_log, const float* dt_bias, void* pool, long long slot_stride, int num_slots,
+                      const int32_t* idx, const uint8_t* has_init, int B, int H, int HK, int K, int V, float scale,
+                      void* out, hipStream_t s, int bounded, float lb) {
+    if (bf16)
+        return pool_bf16 ? launch_typed<bf16_t, bf16_t, CH>(K, qkv, raw_gate, raw_beta, A_log, dt_bias, pool, slot_stride,
+                                                            num_slots, idx, has_init, B, H, HK, V, scale, out, s, bounded, lb)
+                         : launch_typed<bf16_t, float, CH>(K, qkv, raw_gate, raw_beta, A_log, dt_bias, pool, slot_stride,
+                                                           num_slots, idx, has_init, B, H, HK, V, scale, out, s, bounded, lb);
+    return pool_bf16 ? launch_typed<float, bf16_t, CH>(K, qkv, raw_gate, raw_beta, A_log, dt_bias, pool, slot_stride,
+                                                       num_slots, idx, has_init, B, H, HK, V, scale, out, s, bounded, lb)
+                     : launch_typed<float, float, CH>(K, qkv, raw_gate, raw_beta, A_log, dt_bias, pool, slot_stride,
+                                                      num_slots, idx, has_init, B, H, HK, V, scale, out, s, bounded, lb);
+}
+
 hipError_t launch_gdn_decode(bool bf16, bool pool_bf16, const void* qkv, const void* raw_gate,
                              const void* raw_beta, const float* A_log, const float* dt_bias, void* pool,
                              long long slot_stride, int num_slots, const int32_t* state_indices,
                              const uint8_t* has_init, int B, int H, int HK, int K, int V, float scale,
-                             void* out, hipStream_t s) {
+                             void* out, hipStream_t s, bool per_channel, int bounded, float lower_bound) {
     if (B == 0) return hipSuccess;
-    timing_begin("gdn_decode", s);
-    hipError_t e;
-    if (bf16)
-        e = pool_bf16 ? launch_typed<bf16_t, bf16_t>(K, qkv, raw_gate, raw_beta, A_log, dt_bias, pool, slot_stride,
-                                                     num_slots, state_indices, has_init, B, H, HK, V, scale, out, s)
-                      : launch_typed<bf16_t, float>(K, qkv, raw_gate, raw_beta, A_log, dt_bias, pool, slot_stride,
-                                                    num_slots, state_indices, has_init, B, H, HK, V, scale, out, s);
-    else
-        e = pool_bf16 ? launch_typed<float, bf16_t>(K, qkv, raw_gate, raw_beta, A_log, dt_bias, pool, slot_stride,
-                                                    num_slots, state_indices, has_init, B, H, HK, V, scale, out, s)
-                      : launch_typed<float, float>(K, qkv, raw_gate, raw_beta, A_log, dt_bias, pool, slot_stride,
-                                                   num_slots, state_indices, has_init, B, H, HK, V, scale, out, s);
+    timing_begin(per_channel ? "kda_decode" : "gdn_decode", s);
+    const hipError_t e =
+        per_channel ? launch_dec<true>(bf16, pool_bf16, qkv, raw_gate, raw_beta, A_log, dt_bias, pool, slot_stride,
+                                       num_slots, state_indices, has_init, B, H, HK, K, V, scale, out, s, bounded,
+                                       lower_bound)
+                    : launch_dec<false>(bf16, pool_bf16, qkv, raw_gate, raw_beta, A_log, dt_bias, pool, slot_stride,
+                                        num_slots, state_indices, has_init, B, H, HK, K, V, scale, out, s, 0, 0.f);
     timing_end(s);
     return e;
 }

@@ -484,11 +484,12 @@ sf_status sf_kda_recurrent_fwd(sf_dtype dt, const void* q, const void* k, const 
                          pool_dt, num_slots, slot_stride, state_indices, has_initial_state, stream);
 }
 
-sf_status sf_gdn_decode(sf_dtype dt, const void* packed_qkv, const void* raw_gate, const void* raw_beta,
-                        const float* A_log, const float* dt_bias, void* state_pool, sf_dtype pool_dt,
-                        int num_slots, long long slot_stride, const int32_t* state_indices,
-                        const uint8_t* has_initial_state, int B, int H, int HK, int K, int V, float scale,
-                        void* out, void* stream) {
+namespace {
+sf_status decode_step(bool per_channel, int bounded, float lower_bound, sf_dtype dt, const void* packed_qkv,
+                      const void* raw_gate, const void* raw_beta, const float* A_log, const float* dt_bias,
+                      void* state_pool, sf_dtype pool_dt, int num_slots, long long slot_stride,
+                      const int32_t* state_indices, const uint8_t* has_initial_state, int B, int H, int HK, int K,
+                      int V, float scale, void* out, void* stream) {
     if (dt != SF_F32 && dt != SF_BF16) return fail(SF_ERR_INVALID, "dtype must be SF_F32 or SF_BF16");
     if (pool_dt != SF_F32 && pool_dt != SF_BF16) return fail(SF_ERR_INVALID, "pool dtype must be SF_F32 or SF_BF16");
     if (B < 0 || H <= 0 || HK <= 0 || K <= 0 || V <= 0 || num_slots < 0)
@@ -510,11 +511,38 @@ sf_status sf_gdn_decode(sf_dtype dt, const void* packed_qkv, const void* raw_gat
                                     "must not be NULL");
     if (reinterpret_cast<uintptr_t>(state_pool) % 16 != 0 || reinterpret_cast<uintptr_t>(packed_qkv) % 16 != 0)
         return fail(SF_ERR_INVALID, "state_pool and packed_qkv must be 16-byte aligned");
+    if (per_channel && (reinterpret_cast<uintptr_t>(dt_bias) % 16 != 0 ||
+                        reinterpret_cast<uintptr_t>(raw_gate) % (dt == SF_BF16 ? 8 : 16) != 0))
+        return fail(SF_ERR_INVALID, "dt_bias must be 16-byte and raw_gate %d-byte aligned", dt == SF_BF16 ? 8 : 16);
     hipError_t e = sf::launch_gdn_decode(dt == SF_BF16, pool_dt == SF_BF16, packed_qkv, raw_gate, raw_beta, A_log,
                                          dt_bias, state_pool, slot_stride, num_slots, state_indices,
                                          has_initial_state, B, H, HK, K, V, scale, out,
-                                         static_cast<hipStream_t>(stream));
-    return hip_status(e, "sf_gdn_decode launch");
+                                         static_cast<hipStream_t>(stream), per_channel, bounded, lower_bound);
+    return hip_status(e, per_channel ? "sf_kda_decode launch" : "sf_gdn_decode launch");
+}
+}  // namespace
+
+sf_status sf_gdn_decode(sf_dtype dt, const void* packed_qkv, const void* raw_gate, const void* raw_beta,
+                        const float* A_log, const float* dt_bias, void* state_pool, sf_dtype pool_dt,
+                        int num_slots, long long slot_stride, const int32_t* state_indices,
+                        const uint8_t* has_initial_state, int B, int H, int HK, int K, int V, float scale,
+                        void* out, void* stream) {
+    return decode_step(false, 0, 0.f, dt, packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_pool, pool_dt,
+                       num_slots, slot_stride, state_indices, has_initial_state, B, H, HK, K, V, scale, out, stream);
+}
+
+sf_status sf_kda_decode(sf_dtype dt, const void* packed_qkv, const void* raw_gate, const void* raw_beta,
+                        const float* A_log, const float* dt_bias, sf_gate_kind kind, float lower_bound,
+                        void* state_pool, sf_dtype pool_dt, int num_slots, long long slot_stride,
+                        const int32_t* state_indices, const uint8_t* has_initial_state, int B, int H, int K, int V,
+                        float scale, void* out, void* stream) {
+    if (kind != SF_GATE_SOFTPLUS && kind != SF_GATE_BOUNDED)
+        return fail(SF_ERR_INVALID, "kind must be SF_GATE_SOFTPLUS or SF_GATE_BOUNDED");
+    if (kind == SF_GATE_BOUNDED && !(lower_bound <= 0.f && lower_bound > -3.0e38f))
+        return fail(SF_ERR_INVALID, "the bounded kind needs a finite lower_bound <= 0 (got %g)", (double)lower_bound);
+    return decode_step(true, kind == SF_GATE_BOUNDED ? 1 : 0, lower_bound, dt, packed_qkv, raw_gate, raw_beta, A_log,
+                       dt_bias, state_pool, pool_dt, num_slots, slot_stride, state_indices, has_initial_state, B, H,
+                       H, K, V, scale, out, stream);
 }
 
 }  // extern "C"

@@ -113,7 +113,8 @@ hipError_t launch_gdn_decode(bool bf16, bool pool_bf16, const void* qkv, const v
                              const void* raw_beta, const float* A_log, const float* dt_bias, void* pool,
                              long long slot_stride, int num_slots, const int32_t* state_indices,
                              const uint8_t* has_init, int B, int H, int HK, int K, int V, float scale,
-                             void* out, hipStream_t s);
+                             void* out, hipStream_t s, bool per_channel = false, int bounded = 0,
+                             float lower_bound = 0.f);
 
 // Compute units of the current device, and whether a bf16 delta-rule chain over `chains`
 // (sequence, head) pairs of `rows` state rows runs per 16-row slice (else per head).

@@ -339,6 +339,24 @@ sf_status sf_gdn_decode(sf_dtype dt, const void *packed_qkv, const void *raw_gat
                         int H, int HK, int K, int V, float scale, void *out, void *stream);
 
 /*
+ * One-token paged Kimi Delta Attention decode (attention-gym "Linear
+ * Attention": the recurrent_kda_decode entry). As sf_gdn_decode, except:
+ *   packed_qkv [B, H*(2K + V)]: all H query heads, all H key heads, then the
+ *   H value heads (no grouped heads);
+ *   raw_gate [B, H, K] dt (the [1, B, H, K] projection) with dt_bias [H, K]
+ *   float32 (16-byte aligned): a per-key-channel gate through the kind's
+ *   transform (SF_GATE_BOUNDED, the entry's default with lower_bound -5, or
+ *   SF_GATE_SOFTPLUS), each key column of the state decayed by its own factor
+ *   exp(g) before the correction.
+ */
+sf_status sf_kda_decode(sf_dtype dt, const void *packed_qkv, const void *raw_gate,
+                        const void *raw_beta, const float *A_log, const float *dt_bias,
+                        sf_gate_kind kind, float lower_bound, void *state_pool, sf_dtype pool_dt,
+                        int num_slots, long long slot_stride, const int32_t *state_indices,
+                        const uint8_t *has_initial_state, int B, int H, int K, int V, float scale,
+                        void *out, void *stream);
+
+/*
  * Kernel timing hook for measurement. While enabled, every kernel the
  * library enqueues is bracketed by a pair of HIP events recorded on the same
  * stream (events come from a pool created by sf_timing_enable, so no

@@ -432,3 +432,52 @@ def test_kda_recurrent_paged_full_size(dev):
     say(f"recurrent_kda: rel_rms o {eo:.3g}  S {eh:.3g}")
     assert eo <= BF16_RTOL and eh <= BF16_RTOL
     assert np.array_equal(pool[0].cpu().numpy(), p0[0])
+
+
+# ---------------------------------------------------------------------------------------------
+# one-token paged KDA decode (sf_kda_decode)
+# ---------------------------------------------------------------------------------------------
+
+KDA_DEC_CASES = [
+    # name, dtype, pool dtype, B, H, K, V, nulls, fresh, kind, lower bound
+    ("bf16-bounded", torch.bfloat16, torch.float32, 21, 4, 128, 128, 2, 3, "bounded", -5.0),
+    ("f32-softplus-k64", torch.float32, torch.float32, 9, 3, 64, 64, 1, 1, "softplus", None),
+    ("bf16-bf16pool-k256", torch.bfloat16, torch.bfloat16, 6, 2, 256, 32, 1, 1, "bounded", -3.0),
+]
+
+
+@pytest.mark.parametrize("case", KDA_DEC_CASES, ids=[c[0] for c in KDA_DEC_CASES])
+def test_kda_decode_vs_oracle(dev, case):
+    name, dt, pdt, B, H, K, V, nulls, fresh, kind, lb = case
+    say(f"kda decode {name}: B={B} H={H} K={K} V={V}")
+    d = wl.kda_decode_inputs(B=B, H=H, K=K, V=V, dtype=dt, pool_dtype=pdt, seed=zlib.crc32(name.encode()) % 1000,
+                             num_slots=B + 4, n_null=nulls, n_fresh=fresh, pool_std=0.3)
+    g = {n: (None if d[n] is None else d[n].to(dev).contiguous()) for n in d}
+    out = sf.kda_decode(g["packed_qkv"], g["raw_gate"], g["raw_beta"], g["A_log"], g["dt_bias"], g["pool"],
+                        g["state_indices"], has_initial_state=g["has_initial_state"], gate_transform=kind,
+                        lower_bound=lb, scale=0.2)
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    fr = d["has_initial_state"]
+    ref_out, ref_pool = oracle.kda_decode(f(d["packed_qkv"]), f(d["raw_gate"]), f(d["raw_beta"]), f(d["A_log"]),
+                                          f(d["dt_bias"]), f(d["pool"]), d["state_indices"].numpy(),
+                                          None if fr is None else fr.numpy(), H=H, K=K, V=V, kind=kind,
+                                          lower_bound=lb, scale=0.2)
+    check(out.float().cpu().numpy()[0], g["pool"].float().cpu().numpy(), ref_out, ref_pool, d,
+          dt == torch.float32 and pdt == torch.float32, name)
+
+
+def test_kda_decode_full_size(dev):
+    w = wl.decode_kda()
+    say("kda decode: full-size workload")
+    d = {n: getattr(w, n) for n in ("packed_qkv", "raw_gate", "raw_beta", "A_log", "dt_bias", "pool",
+                                    "state_indices", "has_initial_state")}
+    g = {n: (None if d[n] is None else d[n].to(dev).contiguous()) for n in d}
+    out = sf.kda_decode(g["packed_qkv"], g["raw_gate"], g["raw_beta"], g["A_log"], g["dt_bias"], g["pool"],
+                        g["state_indices"], gate_transform=w.gate_kind, lower_bound=w.lower_bound, scale=w.scale)
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    ref_out, ref_pool = oracle.kda_decode(f(w.packed_qkv), f(w.raw_gate), f(w.raw_beta), f(w.A_log), f(w.dt_bias),
+                                          f(w.pool), w.state_indices.numpy(), None, H=w.H, K=w.K, V=w.V,
+                                          kind=w.gate_kind, lower_bound=w.lower_bound, scale=w.scale)
+    check(out.float().cpu().numpy()[0], g["pool"].cpu().numpy(), ref_out, ref_pool, d, False, "decode_kda")

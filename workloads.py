@@ -31,6 +31,8 @@ and one decode workload (one token per sequence against a paged state pool):
                       forward advancing the cache in place).
 10. ``recurrent_kda`` recurrent_gdn's shapes with a per-channel gate (Kimi Delta
                       Attention token by token).
+11. ``decode_kda``    decode_gdn's shapes for the KDA decode (per-channel raw gates,
+                      bounded kind with lower bound -5).
 
 Draw order inside one workload: q, k, v, gate noise, beta noise, h0, A, dt,
 sequence lengths.
@@ -45,7 +47,7 @@ import torch
 
 SEEDS = {"tiny_gdn": 101, "dense_gdn": 102, "varlen_gdn": 103, "long_gdn": 104, "ssd_gla": 105,
          "decode_gdn": 106, "recurrent_gdn": 107, "gate_transform": 108,
-         "paged_gdn": 109, "recurrent_kda": 110}
+         "paged_gdn": 109, "recurrent_kda": 110, "decode_kda": 111}
 
 
 @dataclass
@@ -277,6 +279,9 @@ class DecodeWorkload:
     K: int
     V: int
     scale: float
+    per_channel: bool = False          # Kimi Delta Attention: raw_gate [1, B, H, K], dt_bias [H, K]
+    gate_kind: str = "softplus"
+    lower_bound: Optional[float] = None
 
     @property
     def B(self):
@@ -314,6 +319,23 @@ def decode_inputs(*, B, H, HK, K, V, dtype=torch.bfloat16, pool_dtype=torch.floa
                 A_log=torch.from_numpy(A_log), dt_bias=torch.from_numpy(dt_bias), pool=_cast(pool, pool_dtype),
                 state_indices=torch.from_numpy(idx),
                 has_initial_state=None if fresh is None else torch.from_numpy(fresh))
+
+
+def kda_decode_inputs(*, B, H, K, V, dtype=torch.bfloat16, pool_dtype=torch.float32, seed=0, **kw):
+    """decode_inputs with HK = H, then per-channel raw gates ~ N(0,1) [1, B, H, K] and dt_bias ~
+    N(0, 1) [H, K] (drawn after the rest)."""
+    d = decode_inputs(B=B, H=H, HK=H, K=K, V=V, dtype=dtype, pool_dtype=pool_dtype, seed=seed, **kw)
+    rng = np.random.default_rng(seed + 7919)
+    d["raw_gate"] = _cast(_normal(rng, (1, B, H, K)), dtype)
+    d["dt_bias"] = torch.from_numpy(rng.standard_normal((H, K)).astype(np.float32))
+    return d
+
+
+def decode_kda(seed=SEEDS["decode_kda"], *, B=256, H=32, D=128):
+    """decode_gdn's shapes for the KDA decode, bounded kind with the entry's default lower bound -5."""
+    d = kda_decode_inputs(B=B, H=H, K=D, V=D, seed=seed)
+    return DecodeWorkload("decode_kda", H=H, HK=H, K=D, V=D, scale=1.0 / np.sqrt(D), per_channel=True,
+                          gate_kind="bounded", lower_bound=-5.0, **d)
 
 
 def decode_gdn(seed=SEEDS["decode_gdn"], *, B=256, H=32, HK=32, D=128):
@@ -372,7 +394,7 @@ def gate_transform(seed=SEEDS["gate_transform"], *, B=2, T=16384, H=16, D=128):
 CONFIGS = {"tiny_gdn": tiny_gdn, "dense_gdn": dense_gdn, "varlen_gdn": varlen_gdn,
            "long_gdn": long_gdn, "ssd_gla": ssd_gla, "decode_gdn": decode_gdn,
            "recurrent_gdn": recurrent_gdn, "gate_transform": gate_transform,
-           "paged_gdn": paged_gdn, "recurrent_kda": recurrent_kda}
+           "paged_gdn": paged_gdn, "recurrent_kda": recurrent_kda, "decode_kda": decode_kda}
 
 
 def to_f32(t):
