@@ -452,7 +452,8 @@ sf_status recurrent_fwd(bool per_channel, sf_dtype dt, const void* q, const void
         return fail(SF_ERR_INVALID, "state_pool and has_initial_state need state_indices");
     }
     if (N == 0) return SF_OK;
-    if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
+    if ((long)B * T > 0 && (!q || !k || !v || !g || !beta || !out))  // (no tokens: nothing of them is read)
+        return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
     if ((h0 && reinterpret_cast<uintptr_t>(h0) % 16 != 0) || (ht && reinterpret_cast<uintptr_t>(ht) % 16 != 0))
         return fail(SF_ERR_INVALID, "h0 and ht must be 16-byte aligned");
     if (per_channel && (reinterpret_cast<uintptr_t>(g) % 16 != 0))

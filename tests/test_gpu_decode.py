@@ -481,3 +481,47 @@ def test_kda_decode_full_size(dev):
                                           f(w.pool), w.state_indices.numpy(), None, H=w.H, K=w.K, V=w.V,
                                           kind=w.gate_kind, lower_bound=w.lower_bound, scale=w.scale)
     check(out.float().cpu().numpy()[0], g["pool"].cpu().numpy(), ref_out, ref_pool, d, False, "decode_kda")
+
+
+# ---------------------------------------------------------------------------------------------
+# degenerate cases of the token-by-token and paged entry points
+# ---------------------------------------------------------------------------------------------
+
+def test_degenerate_token_paths(dev):
+    """No rows, no tokens, every row null: the entry points return without touching anything they
+    should not, and the states pass through where the pages say so."""
+    say("degenerate: empty decode batch, zero-length sequences, all-null paged call")
+    H, K, V = 2, 64, 64
+    # a decode call with no rows
+    d = wl.decode_inputs(B=1, H=H, HK=H, K=K, V=V, dtype=torch.bfloat16, seed=3)
+    pool = d["pool"].to(dev)
+    before = pool.clone()
+    empty = torch.empty((0, 2 * H * K + H * V), dtype=torch.bfloat16, device=dev)
+    out = sf.gdn_decode(empty, torch.empty((1, 0, H), dtype=torch.bfloat16, device=dev),
+                        torch.empty((1, 0, H), dtype=torch.bfloat16, device=dev), d["A_log"].to(dev),
+                        d["dt_bias"].to(dev), pool, torch.empty(0, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert out.shape == (1, 0, H, V) and torch.equal(pool, before)
+    # zero-length sequences: the final state is the initial state, bit for bit
+    x = wl.delta_rule_inputs(B=2, T=0, H=H, K=K, V=V, dtype=torch.bfloat16, seed=4, h0_std=0.5)
+    h0 = x["h0"].to(dev)
+    o, ht = sf.gdn_recurrent_fwd(*(x[n].to(dev) for n in ("q", "k", "v", "g", "beta")), h0, output_final_state=True)
+    torch.cuda.synchronize()
+    assert o.shape[1] == 0 and torch.equal(ht, h0)
+    xk = wl.kda_inputs(B=2, T=0, H=H, K=K, V=V, seed=5, h0_std=0.5)
+    o, ht = sf.kda_recurrent_fwd(*(xk[n].to(dev) for n in ("q", "k", "v", "g", "beta")), xk["h0"].to(dev),
+                                 output_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ht, xk["h0"].to(dev))
+    # a paged chunk call whose rows are all null: zero outputs, the pool untouched
+    y = wl.delta_rule_inputs(B=3, T=70, H=H, K=K, V=V, dtype=torch.bfloat16, seed=6)
+    pool2 = torch.randn(5, H, V, K, device=dev)
+    before2 = pool2.clone()
+    o = sf.paged_gdn_chunk_fwd(*(y[n].to(dev) for n in ("q", "k", "v", "g", "beta")), pool2,
+                               torch.tensor([0, -1, 0], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.equal(pool2, before2)
+    # a gate transform of nothing
+    g = sf.gate_transform(torch.empty((0, H), dtype=torch.bfloat16, device=dev), d["A_log"].to(dev),
+                          d["dt_bias"].to(dev), kind="softplus")
+    assert g.shape == (0, H) and g.dtype == torch.float32
