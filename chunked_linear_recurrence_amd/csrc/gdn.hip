@@ -1519,7 +1519,21 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
         // V slice (row0 / 16 + sl) read transposed; transition rows read slice 0 and mask it
         const int off_v = SM::OFF_V + ((vrows ? row0 - 16 * grp * NS : 0) * GC + (4 * lg + (ln >> 2)) * 16 + 4 * (ln & 3)) * 2;
         barrier();
+        // Output rows of a step are held in registers and stored at the start of the next step,
+        // after its barrier: stores issued in the middle of a step compete with that step's
+        // global-to-LDS fill.
+        i16x4 po[4][SPW];
+        bf16_t* pa[4];
+        bool pv[4] = {false, false, false, false};
+        auto flush = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                if (pv[tt])
+#pragma unroll
+                    for (int sl = 0; sl < SPW; ++sl) *reinterpret_cast<i16x4*>(pa[tt] + 16 * sl) = po[tt][sl];
+        };
         for (int c = 0; c < nch; ++c) {
+            if constexpr (!SUMMARY) if (active) flush();
             if (active) {
                 lds_u8* B = buf(c);
                 lds_u8* KR = B + SM::OFF_K;
@@ -1604,11 +1618,10 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
                             for (int sl = 0; sl < SPW; ++sl) o[sl] = mma32(cat8(Rb[sl][2 * pp], Rb[sl][2 * pp + 1]), pf, pp == 0 ? o[sl] * gq : o[sl]);
                         }
                         const int t = 16 * tt + ln;
-                        if (t < L) {
+                        pa[tt] = out + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + 4 * lg;
+                        pv[tt] = t < L;
 #pragma unroll
-                            for (int sl = 0; sl < SPW; ++sl)
-                                *reinterpret_cast<i16x4*>(out + ((size_t)(b * T + t0 + t) * H + h) * V + row0 + 16 * sl + 4 * lg) = El::pack(o[sl]);
-                        }
+                        for (int sl = 0; sl < SPW; ++sl) po[tt][sl] = El::pack(o[sl]);
                     }
                 }
                 // S^T <- Gamma_L S^T + K^T (e R)
@@ -1641,6 +1654,7 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             barrier();
         }
+        if constexpr (!SUMMARY) if (active) flush();
         if (active) {
 #pragma unroll
             for (int sl = 0; sl < SPW; ++sl)
