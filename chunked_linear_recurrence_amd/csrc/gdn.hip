@@ -1414,8 +1414,8 @@ __global__ __launch_bounds__(512) void gdn_chain_1w_kernel(
 //    R = T diag(beta) Y, O = scale Gamma Q S^T + P R, S <- Gamma_L S + K^T (e R). Each fragment of
 //    the shared operands read from LDS feeds the wavefront's SPW slices.
 //  - Wavefronts 8 and 9 move chunk c+1 (K and Q rows, T, coefficients, the eight V slices) into
-//    the other of two LDS buffers with 16-byte direct loads while chunk c computes, and touch the
-//    lines of chunk c+2 so that those loads find them in L2.
+//    the other of two LDS buffers with 16-byte direct loads while chunk c computes and, in the
+//    summary pass, touch the lines of chunk c+2 so that those loads find them in L2.
 //  - Wavefront 10 (output pass only) forms P_c = scale (D o Q_c K_c^T) from the K and Q rows in
 //    LDS while the slice wavefronts form X, Y and R, once for the eight slices: Pre then neither
 //    reads Q nor writes P, and the chain does not read P back.
@@ -1751,18 +1751,21 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
         };
         // (loads complete in issue order: the wait after a step's loads and its warm-up leaves only
         // the warm-up in flight)
+        // The warm-up runs in summary mode only: in the output pass (Q and V rows as well, 32
+        // workgroups per XCD) the touched lines are evicted before their loads come, and on a
+        // long input the pass fetched 15 % more than it reads.
         if (nch > 0) issue(0);
-        if (nch > 1) warm(1);
+        if constexpr (SUMMARY) if (nch > 1) warm(1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         barrier();
         for (int c = 0; c < nch; ++c) {
             if (c + 1 < nch) {
                 issue(c + 1);
-                if (c + 2 < nch) warm(c + 2);
+                if constexpr (SUMMARY) if (c + 2 < nch) warm(c + 2);
             }
             if constexpr (!SUMMARY) barrier();  // the P_c barrier
             if (c + 1 < nch) {
-                if (c + 2 < nch)
+                if (SUMMARY && c + 2 < nch)
                     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
                 else
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
