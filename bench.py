@@ -13,9 +13,12 @@ Prints one JSON line with tokens/s (from the timed steps as a caller runs them),
 the roofline fraction of the dominant kernel (its average launch time from HIP
 events recorded on the launch stream around every launch, in a second timed
 pass over the same steps; the events add gaps between launches, so that pass's
-step time is reported apart as events_pass_ms_per_step) and the float64 oracle
-timed on the host cores on the same workload (cpu_baseline; a reported
-baseline, not a target). Beside the published HBM peak, the roofline objects
+step time is reported apart as events_pass_ms_per_step), p50_ms and min_ms of the
+per-step times (one event between consecutive steps on the launch stream), and the
+oracle's float32 token loops timed on the host cores on the same workload
+(cpu_baseline, with the core count and CPU model; a reported baseline, not a
+target). Segmented workloads also carry path_roofline_two_pass, the path's
+fraction on the byte count of the summary-scan-finalize method. Beside the published HBM peak, the roofline objects
 carry measured_peak: the bandwidth a plain 1 GiB device-to-device copy reaches
 on the same GPU (read plus write bytes), and the fraction of that.
 
@@ -86,6 +89,36 @@ def algorithmic_bytes(w, kernel):
     if kernel == "gdn_prep":
         return qk + gb
     return qk + vo + gb + states      # whole path
+
+
+def two_pass_bytes(w):
+    """Bytes of the segmented method (summary pass, scan, finalize pass), for workloads cut into
+    segments: pass 1 reads k, v, g (and beta) and writes every segment's summary (M or a_block, and
+    S_ext); the scan reads the summaries and writes the entry states S_in; pass 2 is the whole path
+    on the segment view with S_in read as its initial states. None for unsegmented workloads."""
+    if not getattr(w, "n_seg", None) or w.n_seg <= 1:
+        return None
+    eb = w.q.element_size()
+    tok = w.tokens
+    rows = w.B * w.n_seg
+    state = w.H * w.V * w.K * 4
+    delta = w.beta is not None
+    summ = rows * (state + (w.H * w.K * w.K * 4 if delta else w.H * 4))
+    pass1 = tok * w.HK * w.K * eb + tok * w.H * w.V * eb + tok * w.H * 4 * (2 if delta else 1) + summ
+    scan = summ + rows * state + w.B * state          # read summaries, write S_in and the final state
+    pass2 = algorithmic_bytes(w, "path") + rows * state
+    return pass1 + scan + pass2
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def traffic_from_profile(kernel, workload):
@@ -178,18 +211,22 @@ def step_fn(w):
 
 
 def cpu_baseline(w):
-    """The float64 oracle, as it stands, on the host cores: one pass over the workload."""
+    """The oracle, as it stands, on the host cores: its float32 build of the token loops (the CPU
+    throughput baseline; parity uses the float64 build) over one pass of the workload, or a bounded
+    head sample of it."""
     import oracle
     import workloads as wl
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     threads = min(threads, len(os.sched_getaffinity(0)))
+    model = cpu_model()
     f = wl.to_f32
     if isinstance(w, wl.GateWorkload):
         log("cpu_baseline: float64 gate-transform oracle (numpy) ...")
         t0 = time.perf_counter()
         oracle.gate_transform(f(w.raw), f(w.A_log), f(w.dt_bias), w.kind, w.lower_bound)
         dt = time.perf_counter() - t0
-        return {"value": w.tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": w.tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle", "precision": "f64",
+                "cpu_model": model,
                 "sample": f"the whole {w.name} workload ({w.raw.numel()} gates), one float64 pass, {dt:.2f} s wall"}
     if isinstance(w, wl.DecodeWorkload):
         log("cpu_baseline: float64 decode oracle (numpy, one step) ...")
@@ -204,29 +241,57 @@ def cpu_baseline(w):
                               None if w.has_initial_state is None else w.has_initial_state.numpy(),
                               H=w.H, HK=w.HK, K=w.K, V=w.V, scale=w.scale)
         dt = time.perf_counter() - t0
-        return {"value": w.tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": w.tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle", "precision": "f64",
+                "cpu_model": model,
                 "sample": f"the whole {w.name} step ({w.tokens} rows x {w.H} heads), one float64 pass, "
                           f"{dt:.2f} s wall"}
-    args = dict(q=f(w.q), k=f(w.k), v=f(w.v), g=f(w.g))
-    log(f"cpu_baseline: float64 oracle on {threads} threads ...")
-    t0 = time.perf_counter()
-    if w.name == "recurrent_kda":
-        pool, idx = f(w.meta["pool"]), w.meta["state_indices"].numpy()
-        oracle.kda_forward(args["q"], args["k"], args["v"], args["g"], f(w.beta), pool[idx], scale=w.scale)
-    elif w.name in ("recurrent_gdn", "paged_gdn"):
-        oracle.gdn_recurrent_paged(args["q"], args["k"], args["v"], args["g"], f(w.beta), f(w.meta["pool"]),
-                                   w.meta["state_indices"].numpy(),
-                                   cu_seqlens=None if w.cu_seqlens is None else w.cu_seqlens.numpy(), scale=w.scale)
-    elif w.kind == "gdn":
-        oracle.gdn_forward(args["q"], args["k"], args["v"], args["g"], f(w.beta), f(w.h0),
-                           cu_seqlens=None if w.cu_seqlens is None else w.cu_seqlens.numpy(), scale=w.scale,
-                           threads=threads)
-    else:
-        oracle.gla_forward(args["q"], args["k"], args["v"], args["g"], scale=w.scale, threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": w.tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole {w.name} workload ({w.tokens} tokens x {w.H} heads), one float64 pass, "
-                      f"{dt:.2f} s wall"}
+    if w.name in ("recurrent_kda", "recurrent_gdn", "paged_gdn"):
+        args = dict(q=f(w.q), k=f(w.k), v=f(w.v), g=f(w.g))
+        log(f"cpu_baseline: float64 oracle on {threads} threads ...")
+        t0 = time.perf_counter()
+        if w.name == "recurrent_kda":
+            pool, idx = f(w.meta["pool"]), w.meta["state_indices"].numpy()
+            oracle.kda_forward(args["q"], args["k"], args["v"], args["g"], f(w.beta), pool[idx], scale=w.scale)
+        else:
+            oracle.gdn_recurrent_paged(args["q"], args["k"], args["v"], args["g"], f(w.beta), f(w.meta["pool"]),
+                                       w.meta["state_indices"].numpy(),
+                                       cu_seqlens=None if w.cu_seqlens is None else w.cu_seqlens.numpy(),
+                                       scale=w.scale)
+        dt = time.perf_counter() - t0
+        return {"value": w.tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "precision": "f64",
+                "cpu_model": model,
+                "sample": f"the whole {w.name} workload ({w.tokens} tokens x {w.H} heads), one float64 pass, "
+                          f"{dt:.2f} s wall"}
+    # Chunk workloads: the float32 token loops. Whole workload when it is small; otherwise a sample
+    # of heads (each (sequence, head) chain costs the same per token, so tokens/s scales by H/heads)
+    # sized to stay within about half a minute on the host.
+    heads = w.H
+    if w.tokens * w.H > 40_000_000:
+        heads = max(w.H // w.HK, (w.H * 40_000_000) // (w.tokens * w.H) // (w.H // w.HK) * (w.H // w.HK))
+    grp = w.H // w.HK
+    hs = list(range(heads))
+    gs = sorted({h // grp for h in hs})
+    sub = lambda x, idx: x[:, :, idx]
+    q, k = f(sub(w.q, gs)), f(sub(w.k, gs))
+    v, g = f(sub(w.v, hs)), f(sub(w.g, hs))
+    beta = None if w.beta is None else f(sub(w.beta, hs))
+    h0 = None if w.h0 is None else f(w.h0[:, hs])
+    cu = None if w.cu_seqlens is None else w.cu_seqlens.numpy()
+    kind = "gdn" if w.kind == "gdn" else "gla"
+    log(f"cpu_baseline: float32 oracle token loops on {threads} threads, {heads}/{w.H} heads ...")
+    # whole passes until at least 3 s have run (one pass when a pass takes longer)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward_f32(kind, q, k, v, g, beta, h0, cu_seqlens=cu, scale=w.scale, threads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= 3.0:
+            break
+    frac = heads / w.H
+    return {"value": w.tokens * frac * passes / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "precision": "f32", "cpu_model": model,
+            "sample": f"{w.name}: {'all' if heads == w.H else heads} of {w.H} heads over all {w.tokens} tokens, "
+                      f"{passes} pass(es) of the float32 token loops, {dt:.2f} s wall; tokens/s scaled by heads/H"}
 
 
 def measured_copy_gbs(dev, nbytes=1 << 30, reps=10):
@@ -303,6 +368,19 @@ def main():
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # Pass 1b: the same steps with one event on torch's current stream (the launch stream) between
+    # consecutive steps: per-step durations for p50 and min.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    p50_ms = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (per_step[len(per_step) // 2 - 1] +
+                                                                          per_step[len(per_step) // 2])
+    min_ms = per_step[0]
     kt, ev_elapsed = {}, None
     if not args.no_events:
         log(f"bench: timing {args.steps} steps with per-launch events")
@@ -341,7 +419,8 @@ def main():
 
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "p50_ms": p50_ms, "min_ms": min_ms,
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if (w.packed_qkv if decode else w.raw if gate else w.q).dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
@@ -357,10 +436,17 @@ def main():
                           "frac": round(path_ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": path_bytes,
                           "measured_peak": copy_gbs,
                           "frac_of_measured": None if not copy_gbs else round(path_ach / copy_gbs, 4)},
+        "path_roofline_two_pass": None,
         "kernels": kernels,
         "events_pass_ms_per_step": None if ev_elapsed is None else 1e3 * ev_elapsed / args.steps,
         "cpu_baseline": None,
     }
+    tp = None if (decode or gate) else two_pass_bytes(w)
+    if tp:
+        tp_ach = tp / (elapsed / args.steps) / 1e9
+        out["path_roofline_two_pass"] = {"bound": "hbm", "achieved": round(tp_ach, 1), "peak": HBM_PEAK_GBS,
+                                         "unit": "GB/s", "frac": round(tp_ach / HBM_PEAK_GBS, 4),
+                                         "algorithmic_bytes": tp}
     if args.copy_calibration:
         n = 512 << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -59,7 +59,7 @@ EXPORTED = (
     "sf_state_scan", "sf_gdn_segmented_fwd_workspace", "sf_gdn_segmented_fwd", "sf_gdn_decode", "sf_gdn_recurrent_fwd", "sf_gate_transform",
     "sf_paged_gdn_chunk_fwd_workspace", "sf_paged_gdn_chunk_fwd", "sf_gdn_chunk_fwd_raw_gate",
     "sf_kda_recurrent_fwd", "sf_kda_decode",
-    "sf_timing_enable", "sf_timing_collect",
+    "sf_timing_enable", "sf_timing_collect", "sf_check_cu_seqlens", "sf_check_state_indices",
 )
 
 
@@ -120,6 +120,10 @@ def lib() -> ctypes.CDLL:
     L.sf_kda_decode.argtypes = [I, P, P, P, P, P, I, F, P, I, I, ctypes.c_longlong, P, P, I, I, I, I, F, P, P]
     L.sf_gate_transform.restype = I
     L.sf_gate_transform.argtypes = [I, P, P, P, ctypes.c_longlong, I, I, I, F, P, P]
+    L.sf_check_cu_seqlens.restype = I
+    L.sf_check_cu_seqlens.argtypes = [P, I, I]
+    L.sf_check_state_indices.restype = I
+    L.sf_check_state_indices.argtypes = [P, I, I]
     L.sf_timing_enable.restype = I
     L.sf_timing_enable.argtypes = [I]
     L.sf_timing_collect.restype = I
@@ -136,6 +140,24 @@ def version() -> str:
 def _check(status: int):
     if status != SF_OK:
         raise SfError(status, lib().sf_last_error().decode())
+
+
+def validate_cu_seqlens(cu_seqlens: torch.Tensor, T: int) -> None:
+    """Debug check of packed offsets (copies them to the host, which synchronises): starts at 0, never
+    decreases, ends at or before T. Raises SfError otherwise."""
+    h = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    _check(lib().sf_check_cu_seqlens(ctypes.c_void_p(h.data_ptr()), h.numel() - 1, int(T)))
+
+
+def validate_state_indices(state_indices: torch.Tensor, num_slots: int) -> None:
+    """Debug check of slot indices (copies them to the host): positive indices below num_slots and
+    unique. Raises SfError otherwise."""
+    h = state_indices.detach().to("cpu", torch.int32).contiguous()
+    _check(lib().sf_check_state_indices(ctypes.c_void_p(h.data_ptr()), h.numel(), int(num_slots)))
+
+
+def _validating() -> bool:
+    return os.environ.get("SF_VALIDATE", "0") == "1"
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -191,6 +213,8 @@ def _token_args(q, k, v, g, beta, initial_state, cu_seqlens, g_dtype=torch.float
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1, device=dev)
         N = cu_seqlens.numel() - 1
+        if _validating():
+            validate_cu_seqlens(cu_seqlens, T)
     else:
         N = B
     if initial_state is not None:
@@ -405,6 +429,8 @@ def gdn_recurrent_fwd(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, 
                                           None, SF_F32, 0, 0, None, None, _stream()))
         return out, ht
     NS, stride0, pool_dt = _pool_layout(initial_state, H, V, K, dev)
+    if _validating():
+        validate_state_indices(state_indices, NS)
     _check(lib().sf_gdn_recurrent_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), None,
                                       _ptr(cu_seqlens), N, B, T, H, HK, K, V, float(scale), _ptr(out), None,
                                       _ptr(initial_state), pool_dt, NS, stride0, _ptr(state_indices),
@@ -427,6 +453,8 @@ def paged_gdn_chunk_fwd(q, k, v, g, beta, state_cache, state_indices, *, cu_seql
         if has_initial_state.numel() != N:
             raise ValueError(f"has_initial_state must have {N} entries")
     NS, stride0, pool_dt = _pool_layout(state_cache, H, V, K, dev)
+    if _validating():
+        validate_state_indices(state_indices, NS)
     if scale is None:
         scale = 1.0 / math.sqrt(K)
     out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
@@ -462,6 +490,8 @@ def kda_recurrent_fwd(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, 
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1, device=dev)
         N = cu_seqlens.numel() - 1
+        if _validating():
+            validate_cu_seqlens(cu_seqlens, T)
     if scale is None:
         scale = 1.0 / math.sqrt(K)
     out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
@@ -485,6 +515,8 @@ def kda_recurrent_fwd(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, 
     if has_initial_state is not None:
         _need(has_initial_state, "has_initial_state", dtype=torch.bool, ndim=1, device=dev)
     NS, stride0, pool_dt = _pool_layout(initial_state, H, V, K, dev)
+    if _validating():
+        validate_state_indices(state_indices, NS)
     _check(lib().sf_kda_recurrent_fwd(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), None, _ptr(cu_seqlens), N,
                                       B, T, H, K, V, float(scale), _ptr(out), None, _ptr(initial_state), pool_dt, NS,
                                       stride0, _ptr(state_indices), _ptr(has_initial_state), _stream()))
@@ -531,6 +563,8 @@ def gdn_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_cache, stat
         _need(has_initial_state, "has_initial_state", dtype=torch.bool, ndim=1, device=dev)
         if has_initial_state.numel() != B:
             raise ValueError(f"has_initial_state must have {B} entries")
+    if _validating():
+        validate_state_indices(state_indices, NS)
     if out is None:
         out = torch.empty((1, B, H, V), dtype=packed_qkv.dtype, device=dev)
     else:
@@ -596,6 +630,8 @@ def kda_decode(packed_qkv, raw_gate, raw_beta, A_log, dt_bias, state_cache, stat
         raise ValueError("state_cache must be a [num_slots, H, V, K] GPU tensor")
     NS, H, V, K = state_cache.shape
     NS, stride0, pool_dt = _pool_layout(state_cache, H, V, K, dev)
+    if _validating():
+        validate_state_indices(state_indices, NS)
     if W != H * (2 * K + V):
         raise ValueError(f"packed_qkv width {W} must be H*(2K + V) = {H * (2 * K + V)}")
     _need(raw_gate, "raw_gate", dtype=packed_qkv.dtype, device=dev)

@@ -137,6 +137,32 @@ int sf_timing_collect(const char** names, double* total_ms, int* launches, int m
     return nk;
 }
 
+sf_status sf_check_cu_seqlens(const int32_t* cu, int N, int T) {
+    if (N < 0 || T < 0) return fail(SF_ERR_INVALID, "N and T must be nonnegative (N=%d T=%d)", N, T);
+    if (!cu) return fail(SF_ERR_INVALID, "cu_seqlens is NULL");
+    if (cu[0] != 0) return fail(SF_ERR_INVALID, "cu_seqlens[0] is %d, must be 0", (int)cu[0]);
+    for (int n = 0; n < N; ++n)
+        if (cu[n + 1] < cu[n])
+            return fail(SF_ERR_INVALID, "cu_seqlens decreases at %d: %d -> %d", n, (int)cu[n], (int)cu[n + 1]);
+    if (cu[N] > T) return fail(SF_ERR_INVALID, "cu_seqlens[%d] = %d is past T = %d", N, (int)cu[N], T);
+    return SF_OK;
+}
+
+sf_status sf_check_state_indices(const int32_t* idx, int N, int num_slots) {
+    if (N < 0 || num_slots < 0) return fail(SF_ERR_INVALID, "N and num_slots must be nonnegative");
+    if (N > 0 && !idx) return fail(SF_ERR_INVALID, "state_indices is NULL");
+    std::vector<int> owner((size_t)num_slots, -1);
+    for (int n = 0; n < N; ++n) {
+        const int s = idx[n];
+        if (s <= 0) continue;
+        if (s >= num_slots) return fail(SF_ERR_INVALID, "state_indices[%d] = %d is past num_slots = %d", n, s, num_slots);
+        if (owner[(size_t)s] >= 0)
+            return fail(SF_ERR_INVALID, "state_indices[%d] and [%d] both name slot %d (they would race)", owner[(size_t)s], n, s);
+        owner[(size_t)s] = n;
+    }
+    return SF_OK;
+}
+
 size_t sf_gdn_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N, int packed) {
     (void)K;
     (void)V;

@@ -359,6 +359,23 @@ sf_status sf_kda_decode(sf_dtype dt, const void *packed_qkv, const void *raw_gat
                         void *out, void *stream);
 
 /*
+ * Host-side argument checks for debugging. The entry points do not read device
+ * memory, so the value constraints on cu_seqlens and state_indices are the
+ * caller's (attention-gym "Linear Attention" states the same for its packed
+ * offsets and slot indices). These two functions check a HOST copy of those
+ * arrays and return SF_ERR_INVALID with a message naming the first violation;
+ * they enqueue nothing and touch no device memory. The Python binding calls them
+ * on every entry when the environment variable SF_VALIDATE is set to 1.
+ *   sf_check_cu_seqlens: cu_seqlens_host [N + 1] starts at 0, never decreases and
+ *     ends at or before T.
+ *   sf_check_state_indices: state_indices_host [N]; every positive index is below
+ *     num_slots and no positive index repeats (two sequences on one slot race).
+ *     Non-positive indices (padding / null rows) are allowed.
+ */
+sf_status sf_check_cu_seqlens(const int32_t *cu_seqlens_host, int N, int T);
+sf_status sf_check_state_indices(const int32_t *state_indices_host, int N, int num_slots);
+
+/*
  * Kernel timing hook for measurement. While enabled, every kernel the
  * library enqueues is bracketed by a pair of HIP events recorded on the same
  * stream (events come from a pool created by sf_timing_enable, so no

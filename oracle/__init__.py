@@ -21,6 +21,8 @@ What each function follows (pages by title and section):
 * ``state_scan``    the exclusive causal scan of the same page.
 * ``chunked_forward``  StateFlow Section 2.2 Eq. (2) chunk split, used only to
   check that the chunk algebra reproduces the token recurrence.
+* ``forward_f32``   the token loops of ``gdn_forward`` / ``gla_forward`` in float32:
+  the CPU throughput baseline of bench.py, never a parity reference.
 * ``gdn_decode``    attention-gym "Linear Attention", the ``recurrent_gdn_decode``
   entry and the section "Gate Transforms" (``decode.py``, numpy float64).
 * ``gdn_recurrent_paged``  the ``recurrent_gdn`` entry with a paged state pool:
@@ -76,6 +78,8 @@ def _load():
         lib.orc_gla_summary.argtypes = [P, P, P, P, I, I, I, I, I, I, I, P, P, I]
         lib.orc_state_scan.argtypes = [I, P, P, P, I, I, I, I, I, P, P]
         lib.orc_chunked_forward.argtypes = [I, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, P, P, I]
+        lib.orc_forward_f32.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_float, P, P, I]
+        lib.orc_forward_f32.restype = None
         lib.orc_max_threads.restype = I
         for f in (lib.orc_gdn_forward, lib.orc_gla_forward, lib.orc_gdn_summary,
                   lib.orc_gla_summary, lib.orc_state_scan, lib.orc_chunked_forward):
@@ -143,6 +147,22 @@ def gla_forward(q, k, v, g, h0=None, cu_seqlens=None, scale=1.0, threads=0):
     ht = np.zeros((N, H, V, K), dtype=np.float64)
     _load().orc_gla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(cu),
                             N, B, T, H, HK, K, V, float(scale), _ptr(out), _ptr(ht),
+                            int(threads))
+    return out, ht
+
+
+def forward_f32(kind, q, k, v, g, beta=None, h0=None, cu_seqlens=None, scale=None, threads=0):
+    """Float32 build of the token loops (kind "gdn" or "gla"): the same steps as gdn_forward /
+    gla_forward in float arithmetic. CPU throughput baseline only, never a parity reference.
+    Returns (out, ht) in float32."""
+    q, k, v, g, beta, h0 = map(_f32, (q, k, v, g, beta, h0))
+    B, T, H, HK, K, V, N, cu = _dims(q, v, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / np.sqrt(K) if kind == "gdn" else 1.0
+    out = np.full((B, T, H, V), np.nan, dtype=np.float32)
+    ht = np.zeros((N, H, V, K), dtype=np.float32)
+    _load().orc_forward_f32(1 if kind == "gdn" else 0, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(h0), _ptr(cu), N, B, T, H, HK, K, V, float(scale), _ptr(out), _ptr(ht),
                             int(threads))
     return out, ht
 

@@ -31,7 +31,9 @@
  *           (only used by the chunked self-check functions below).
  *
  * Precision: inputs arrive as float32 arrays (bf16 inputs are widened
- * exactly by the caller); all arithmetic and every output is float64.
+ * exactly by the caller); all arithmetic and every output is float64, except
+ * orc_forward_f32, a float32 build of the two token loops that serves only as
+ * the CPU throughput baseline (never as a parity reference).
  *
  * Parity pins: every exported function is pinned by tests/test_oracle.py
  * against closed forms, brute force or invariants that do not reuse this
@@ -480,6 +482,101 @@ void orc_chunked_forward(int delta, int C, const float *q, const float *k,
                           out + (tok0 * H + h) * V, (long)H * V);
             if (ht)
                 memcpy(ht + ((long)n * H + h) * V * K, S, sizeof(double) * V * K);
+            free(S);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Float32 builds of the two token loops above: the same steps in the same
+ * order with float arithmetic (expf). They are the CPU throughput baseline
+ * only; parity always uses the float64 functions.
+ * ------------------------------------------------------------------------- */
+static void gdn_chain_f32(float *S, int V, int K, const float *q, const float *k,
+                          const float *v, const float *g, const float *beta,
+                          long qs, long vs, long gs, int ntok, float scale,
+                          float *o, long os)
+{
+    float *r = (float *)malloc(sizeof(float) * (size_t)V);
+    for (int t = 0; t < ntok; ++t) {
+        const float *kt = k + (long)t * qs;
+        const float gam = expf(g[(long)t * gs]);
+        const float bt = beta[(long)t * gs];
+        for (long i = 0; i < (long)V * K; ++i)
+            S[i] *= gam;
+        for (int row = 0; row < V; ++row) {
+            float dk = 0.f;
+            for (int c = 0; c < K; ++c)
+                dk += S[(long)row * K + c] * kt[c];
+            r[row] = bt * (v[(long)t * vs + row] - dk);
+        }
+        for (int row = 0; row < V; ++row)
+            for (int c = 0; c < K; ++c)
+                S[(long)row * K + c] += r[row] * kt[c];
+        const float *qt = q + (long)t * qs;
+        for (int row = 0; row < V; ++row) {
+            float acc = 0.f;
+            for (int c = 0; c < K; ++c)
+                acc += S[(long)row * K + c] * qt[c];
+            o[(long)t * os + row] = scale * acc;
+        }
+    }
+    free(r);
+}
+
+static void gla_chain_f32(float *S, int V, int K, const float *q, const float *k,
+                          const float *v, const float *g, long qs, long vs, long gs,
+                          int ntok, float scale, float *o, long os)
+{
+    for (int t = 0; t < ntok; ++t) {
+        const float *kt = k + (long)t * qs;
+        const float *vt = v + (long)t * vs;
+        const float gam = expf(g[(long)t * gs]);
+        for (int row = 0; row < V; ++row)
+            for (int c = 0; c < K; ++c)
+                S[(long)row * K + c] = gam * S[(long)row * K + c] + vt[row] * kt[c];
+        const float *qt = q + (long)t * qs;
+        for (int row = 0; row < V; ++row) {
+            float acc = 0.f;
+            for (int c = 0; c < K; ++c)
+                acc += S[(long)row * K + c] * qt[c];
+            o[(long)t * os + row] = scale * acc;
+        }
+    }
+}
+
+/* kind 1: Gated Delta Rule (beta used), kind 0: scalar gate. Layouts as
+ * orc_gdn_forward, with float32 out [B, T, H, V] and ht [N, H, V, K]. */
+void orc_forward_f32(int delta, const float *q, const float *k, const float *v,
+                     const float *g, const float *beta, const float *h0,
+                     const int32_t *cu, int N, int B, int T, int H, int HK, int K,
+                     int V, float scale, float *out, float *ht, int nthreads)
+{
+    (void)B;
+    set_threads(nthreads);
+    const int grp = H / HK;
+    #pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int n = 0; n < N; ++n) {
+        for (int h = 0; h < H; ++h) {
+            int b, bos, eos;
+            seq_range(cu, n, T, &b, &bos, &eos);
+            const int hk = h / grp;
+            float *S = (float *)calloc((size_t)V * K, sizeof(float));
+            if (h0)
+                memcpy(S, h0 + ((long)n * H + h) * V * K, sizeof(float) * V * K);
+            const long tok0 = (long)b * T + bos;
+            if (delta)
+                gdn_chain_f32(S, V, K, q + (tok0 * HK + hk) * K, k + (tok0 * HK + hk) * K,
+                              v + (tok0 * H + h) * V, g + tok0 * H + h, beta + tok0 * H + h,
+                              (long)HK * K, (long)H * V, H, eos - bos, scale,
+                              out + (tok0 * H + h) * V, (long)H * V);
+            else
+                gla_chain_f32(S, V, K, q + (tok0 * HK + hk) * K, k + (tok0 * HK + hk) * K,
+                              v + (tok0 * H + h) * V, g + tok0 * H + h, (long)HK * K,
+                              (long)H * V, H, eos - bos, scale, out + (tok0 * H + h) * V,
+                              (long)H * V);
+            if (ht)
+                memcpy(ht + ((long)n * H + h) * V * K, S, sizeof(float) * V * K);
             free(S);
         }
     }

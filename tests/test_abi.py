@@ -255,3 +255,33 @@ def test_segment_view_indexing():
         for j in range(n_seg):
             assert torch.equal(sv[b * n_seg + j], x[b, j * L:(j + 1) * L])
             assert sv[b * n_seg + j].data_ptr() == x[b, j * L].data_ptr()
+
+
+def test_host_validators(L):
+    """The debug checks on host copies of cu_seqlens and slot indices (no GPU, nothing enqueued)."""
+    import numpy as np
+
+    def cu_ok(arr, T):
+        a = np.ascontiguousarray(np.asarray(arr, dtype=np.int32))
+        return L.sf_check_cu_seqlens(a.ctypes.data_as(ctypes.c_void_p), len(a) - 1, T)
+
+    assert cu_ok([0, 5, 5, 9], 9) == sf.SF_OK
+    assert cu_ok([0], 0) == sf.SF_OK
+    assert cu_ok([1, 5], 9) == sf.SF_ERR_INVALID and b"cu_seqlens[0]" in L.sf_last_error()
+    assert cu_ok([0, 5, 4], 9) == sf.SF_ERR_INVALID and b"decreases" in L.sf_last_error()
+    assert cu_ok([0, 5, 10], 9) == sf.SF_ERR_INVALID and b"past T" in L.sf_last_error()
+
+    def idx_ok(arr, ns):
+        a = np.ascontiguousarray(np.asarray(arr, dtype=np.int32))
+        return L.sf_check_state_indices(a.ctypes.data_as(ctypes.c_void_p), len(a), ns)
+
+    assert idx_ok([3, 0, -1, 1, 2], 4) == sf.SF_OK
+    assert idx_ok([3, 4], 4) == sf.SF_ERR_INVALID and b"past num_slots" in L.sf_last_error()
+    assert idx_ok([2, 0, 2], 4) == sf.SF_ERR_INVALID and b"race" in L.sf_last_error()
+    # the binding's helpers raise on the same cases (host tensors: no GPU needed)
+    import torch
+    sf.validate_cu_seqlens(torch.tensor([0, 3, 3], dtype=torch.int32), 3)
+    with pytest.raises(sf.SfError):
+        sf.validate_cu_seqlens(torch.tensor([0, 3, 2], dtype=torch.int32), 3)
+    with pytest.raises(sf.SfError):
+        sf.validate_state_indices(torch.tensor([1, 1], dtype=torch.int32), 4)

@@ -373,6 +373,70 @@ def test_raw_gate_chunk_vs_oracle(dev, case):
         assert eo <= BF16_RTOL and eh <= BF16_RTOL
 
 
+def test_paged_chunk_full_size(dev):
+    """The paged_gdn workload (the packed 32768-token stream, H = 32, a float32 pool) at full size: the
+    launch has more 16-row slices than two per CU and more Pre units than the GPU holds at once, so it runs
+    the per-head chain and the one-wavefront Pre, as bench.py's paged_gdn line does. Every sequence and
+    head of the output and every advanced slot against the oracle."""
+    w = wl.paged_gdn()
+    say(f"paged chunk full size: lengths {w.meta['lengths']}")
+    pool = w.meta["pool"].to(dev).contiguous()
+    idx = w.meta["state_indices"]
+    x = {n: getattr(w, n).to(dev).contiguous() for n in ("q", "k", "v", "g", "beta", "cu_seqlens")}
+    o = sf.paged_gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], pool, idx.to(dev),
+                               cu_seqlens=x["cu_seqlens"], scale=w.scale)
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    ref_o, ref_pool = oracle.gdn_recurrent_paged(f(w.q), f(w.k), f(w.v), f(w.g), f(w.beta), f(w.meta["pool"]),
+                                                 idx.numpy(), cu_seqlens=w.cu_seqlens.numpy(), scale=w.scale)
+    o = o.float().cpu().numpy()
+    got = pool.cpu().numpy()
+    cu = w.cu_seqlens.numpy()
+    worst = 0.0
+    for n in range(w.N):
+        for h in range(w.H):
+            e = rel_rms(got[idx[n], h], ref_pool[idx[n], h])
+            worst = max(worst, e)
+            assert e <= BF16_RTOL, ("slot", n, h, e)
+            if cu[n + 1] > cu[n]:
+                e = rel_rms(o[0, cu[n]:cu[n + 1], h], ref_o[0, cu[n]:cu[n + 1], h])
+                worst = max(worst, e)
+                assert e <= BF16_RTOL, ("out", n, h, e)
+    assert np.array_equal(got[0], f(w.meta["pool"])[0])  # the null slot is untouched
+    say(f"paged chunk full size: worst rel_rms over (sequence, head) {worst:.3g}")
+
+
+def test_raw_gate_chunk_full_size(dev):
+    """sf_gdn_chunk_fwd_raw_gate on the packed 32768-token stream with 32 heads (per-head chain,
+    one-wavefront Pre with the gate transform in its gate load), softplus kind, against the oracle's
+    gate transform followed by the token recurrence, per (sequence, head)."""
+    w = wl.varlen_gdn()
+    gi = wl.gate_inputs(shape=(1, w.T, w.H), H=w.H, dtype=torch.bfloat16, seed=123)
+    say(f"raw-gate chunk full size: lengths {w.meta['lengths']}")
+    x = {n: getattr(w, n).to(dev).contiguous() for n in ("q", "k", "v", "beta", "cu_seqlens")}
+    o, ht = sf.gdn_chunk_fwd_raw_gate(x["q"], x["k"], x["v"], gi["raw"].to(dev), gi["A_log"].to(dev),
+                                      gi["dt_bias"].to(dev), x["beta"], None, kind="softplus",
+                                      cu_seqlens=x["cu_seqlens"], scale=w.scale, output_final_state=True)
+    torch.cuda.synchronize()
+    f = wl.to_f32
+    gate = oracle.gate_transform(f(gi["raw"]), f(gi["A_log"]), f(gi["dt_bias"]), "softplus", None)
+    ref_o, ref_ht = oracle.gdn_forward(f(w.q), f(w.k), f(w.v), gate, f(w.beta), cu_seqlens=w.cu_seqlens.numpy(),
+                                       scale=w.scale)
+    o, ht = o.float().cpu().numpy(), ht.cpu().numpy()
+    cu = w.cu_seqlens.numpy()
+    worst = 0.0
+    for n in range(w.N):
+        if cu[n + 1] == cu[n]:
+            assert np.all(ht[n] == 0)
+            continue
+        for h in range(w.H):
+            for x_, r_ in ((o[0, cu[n]:cu[n + 1], h], ref_o[0, cu[n]:cu[n + 1], h]), (ht[n, h], ref_ht[n, h])):
+                e = rel_rms(x_, r_)
+                worst = max(worst, e)
+                assert e <= BF16_RTOL, (n, h, e)
+    say(f"raw-gate chunk full size: worst rel_rms over (sequence, head) {worst:.3g}")
+
+
 # ---------------------------------------------------------------------------------------------
 # Kimi Delta Attention token by token (sf_kda_recurrent_fwd)
 # ---------------------------------------------------------------------------------------------

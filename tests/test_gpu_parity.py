@@ -68,6 +68,21 @@ def heads_subset(w, heads):
                 beta=f32(sub(w.beta, hs)), h0=None if w.h0 is None else f32(w.h0[:, hs]), hs=hs)
 
 
+def check_units(name, units):
+    """Per-chain gate: units is a list of (label, x, ref); every unit's rel_rms must pass, so a wrong
+    head, short sequence or tail is not diluted by the rest of a large tensor."""
+    worst = ("", 0.0)
+    for label, x, ref in units:
+        if np.linalg.norm(ref) == 0:
+            assert np.array_equal(np.asarray(x, np.float64), ref), label
+            continue
+        e = rel_rms(x, ref)
+        if e > worst[1]:
+            worst = (label, e)
+        assert e <= BF16_RTOL, (name, label, e)
+    say(f"  {name}: {len(units)} units, worst rel_rms {worst[1]:.3e} ({worst[0]})")
+
+
 def check_bf16(name, o, ro, ht, rh):
     eo, eh = rel_rms(o, ro), rel_rms(ht, rh)
     say(f"  {name}: rel_rms(o)={eo:.3e} rel_rms(ht)={eh:.3e}")
@@ -169,17 +184,18 @@ def test_gdn_bf16_degenerate_gates(dev, oracle, case, H):
 
 
 def test_dense_gdn_full_size(dev, oracle):
-    say("case: dense GDN prefill B=2 T=4096 H=16 K=V=128 bf16 (full size, heads 0, 7, 15 vs oracle)")
+    say("case: dense GDN prefill B=2 T=4096 H=16 K=V=128 bf16 (full size, every head vs oracle)")
     w = wl.dense_gdn()
     o, ht = sf.gdn_chunk_fwd(cuda(w.q, dev), cuda(w.k, dev), cuda(w.v, dev), cuda(w.g, dev), cuda(w.beta, dev),
                              cuda(w.h0, dev), scale=w.scale, output_final_state=True)
     torch.cuda.synchronize()
     o, ht = f32(o), f32(ht)
     assert np.isfinite(o).all() and np.isfinite(ht).all()
-    heads = [0, 7, 15]
-    s = heads_subset(w, heads)
-    ro, rh = oracle.gdn_forward(s["q"], s["k"], s["v"], s["g"], s["beta"], s["h0"], scale=w.scale)
-    check_bf16("dense heads", o[:, :, s["hs"]], ro, ht[:, s["hs"]], rh)
+    ro, rh = oracle.gdn_forward(f32(w.q), f32(w.k), f32(w.v), f32(w.g), f32(w.beta), f32(w.h0), scale=w.scale)
+    check_bf16("dense, all heads", o, ro, ht, rh)
+    check_units("dense per (row, head)", [(f"o b{b} h{h}", o[b, :, h], ro[b, :, h]) for b in range(w.B)
+                                           for h in range(w.H)] +
+                [(f"ht b{b} h{h}", ht[b, h], rh[b, h]) for b in range(w.B) for h in range(w.H)])
 
 
 def host_chunk_table(cu, C=64):
@@ -193,23 +209,29 @@ def host_chunk_table(cu, C=64):
 def test_varlen_gdn_full_size(dev, oracle):
     w = wl.varlen_gdn()
     lens = w.meta["lengths"]
-    say(f"case: packed varlen GDN T=32768 H=32 K=V=128 bf16 lengths={lens}")
+    say(f"case: packed varlen GDN T=32768 H=32 K=V=128 bf16 lengths={lens} (every head and sequence)")
     cu = cuda(w.cu_seqlens, dev)
     h0 = torch.randn(w.N, w.H, w.V, w.K, generator=torch.Generator().manual_seed(5)) * 0.02
     q, k, v, g, beta = (cuda(x, dev) for x in (w.q, w.k, w.v, w.g, w.beta))
     o, ht = sf.gdn_chunk_fwd(q, k, v, g, beta, cuda(h0, dev), cu_seqlens=cu, scale=w.scale, output_final_state=True)
     torch.cuda.synchronize()
     o, ht = f32(o), f32(ht)
-    heads = [0, 13, 31]
-    s = heads_subset(w, heads)
-    ro, rh = oracle.gdn_forward(s["q"], s["k"], s["v"], s["g"], s["beta"], f32(h0[:, s["hs"]]),
+    ro, rh = oracle.gdn_forward(f32(w.q), f32(w.k), f32(w.v), f32(w.g), f32(w.beta), f32(h0),
                                 cu_seqlens=w.cu_seqlens.numpy(), scale=w.scale)
     end = int(w.cu_seqlens[-1])
-    check_bf16("varlen heads", o[:, :end, s["hs"]], ro[:, :end], ht[:, s["hs"]], rh)
-    # an empty sequence returns its initial state bitwise
+    check_bf16("varlen, all heads", o[:, :end], ro[:, :end], ht, rh)
+    cu_h = w.cu_seqlens.numpy()
+    units = []
     for n, L in enumerate(lens):
         if L == 0:
+            # an empty sequence returns its initial state bitwise
             assert np.array_equal(ht[n], f32(h0[n])), "empty sequence must pass its state through"
+            continue
+        a, b_ = int(cu_h[n]), int(cu_h[n + 1])
+        for h in range(w.H):
+            units.append((f"o seq{n}(L={L}) h{h}", o[0, a:b_, h], ro[0, a:b_, h]))
+            units.append((f"ht seq{n} h{h}", ht[n, h], rh[n, h]))
+    check_units("varlen per (sequence, head)", units)
 
 
 def test_varlen_chunk_table_is_exact(dev):
@@ -434,6 +456,77 @@ def test_gla_vs_oracle(dev, oracle, dtype, chunk, T, HK):
         check_bf16("gla", f32(o), ro, f32(ht), rh)
 
 
+def test_segmented_gla_nonzero_transitions(dev, oracle):
+    """Segmented scalar gate with a_block far from zero: the gates are slowed so that each segment's gate
+    sum is about -2 (a_block ~ 0.1), so the scan's a * S_in term carries real weight into every segment."""
+    say("case: segmented GLA B=2 T=4096 H=8 HK=2 K=128 V=64 chunk 128, 8 segments of 512, a_block ~ 0.1")
+    d = wl.scalar_gate_inputs(B=2, T=4096, H=8, HK=2, K=128, V=64, seed=91)
+    g = d["g"]
+    seg_sums = g.view(2, 8, 512, 8).sum(2)
+    d["g"] = (g * (-2.0 / float(seg_sums.median()))).float().contiguous()
+    h0 = (torch.randn(2, 8, 64, 128, generator=torch.Generator().manual_seed(91)) * 0.1).float()
+    x = {n: cuda(d[n], dev) for n in ("q", "k", "v", "g")}
+    o, hf = sf.segmented_gla_fwd(x["q"], x["k"], x["v"], x["g"], 8, cuda(h0, dev), scale=0.1, chunk=128,
+                                 output_final_state=True)
+    a, _ = sf.segment_summary("gla", sf.segment_view(x["k"], 8), sf.segment_view(x["v"], 8),
+                              sf.segment_view(x["g"], 8), chunk=128)
+    a = f32(a)
+    say(f"  a_block range [{a.min():.3f}, {a.max():.3f}]")
+    assert a.min() > 1e-3 and np.median(a) > 0.05  # the scan's a * S_in term is far from zero
+    ro, rh = oracle.gla_forward(f32(d["q"]), f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(h0), scale=0.1)
+    check_bf16("segmented vs unsegmented oracle", f32(o), ro, f32(hf), rh)
+    o_ = f32(o)
+    check_units("per (row, segment, head)", [(f"o b{b} seg{j} h{h}", o_[b, 512 * j:512 * (j + 1), h],
+                                              ro[b, 512 * j:512 * (j + 1), h])
+                                             for b in range(2) for j in range(8) for h in range(8)])
+
+
+# bf16 scalar-gate shapes the ABI accepts, each against the oracle: K, V in {64, 128}, chunk 64 and 128,
+# grouped heads, a ragged last chunk and an initial state.
+@pytest.mark.parametrize("K,V,chunk", [(64, 64, 64), (64, 64, 128), (128, 128, 64), (128, 128, 128),
+                                       (64, 128, 128), (128, 64, 64), (64, 128, 64)])
+def test_gla_bf16_shapes_vs_oracle(dev, oracle, K, V, chunk):
+    say(f"case: GLA bf16 K={K} V={V} chunk {chunk} B=2 T=300 H=4 HK=2 with h0")
+    d = wl.scalar_gate_inputs(B=2, T=300, H=4, HK=2, K=K, V=V, seed=K + V + chunk)
+    h0 = (torch.randn(2, 4, V, K, generator=torch.Generator().manual_seed(K + V)) * 0.3).float()
+    o, ht = sf.gla_chunk_fwd(cuda(d["q"], dev), cuda(d["k"], dev), cuda(d["v"], dev), cuda(d["g"], dev),
+                             cuda(h0, dev), chunk=chunk, scale=0.3, output_final_state=True)
+    ro, rh = oracle.gla_forward(f32(d["q"]), f32(d["k"]), f32(d["v"]), f32(d["g"]), f32(h0), scale=0.3)
+    check_bf16(f"gla K={K} V={V} chunk {chunk}", f32(o), ro, f32(ht), rh)
+
+
+def test_document_aligned_split_is_bitwise(dev):
+    """A packed stream cut at a document boundary into two calls gives, bit for bit, the results of the
+    single call (attention-gym "Context Parallelism", document-aligned fragments): each document's
+    arithmetic does not depend on which others share its launch. Delta rule and scalar gate."""
+    lens = [130, 0, 64, 7, 300, 91, 1]
+    cut = 3   # documents [0, 3) and [3, 7)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    H = 32
+    say(f"case: document-aligned split, lengths {lens}, cut before document {cut}, H={H} K=V=128")
+    d = wl.delta_rule_inputs(B=1, T=T, H=H, K=128, V=128, dtype=torch.bfloat16, seed=23, gate_shift=-1.0)
+    h0 = (torch.randn(len(lens), H, 128, 128, generator=torch.Generator().manual_seed(2)) * 0.1).float()
+    x = {n: cuda(d[n], dev) for n in ("q", "k", "v", "g", "beta")}
+    h0d = cuda(h0, dev)
+    t = int(cu[cut])
+    part = lambda a, b: {n: x[n][:, a:b].contiguous() for n in x}
+    cu_a = torch.from_numpy(cu[:cut + 1]).to(dev)
+    cu_b = torch.from_numpy(cu[cut:] - t).to(dev)
+    for kind in ("gdn", "gla"):
+        if kind == "gdn":
+            run = lambda y, hh, c: sf.gdn_chunk_fwd(y["q"], y["k"], y["v"], y["g"], y["beta"], hh, cu_seqlens=c,
+                                                    output_final_state=True)
+        else:
+            run = lambda y, hh, c: sf.gla_chunk_fwd(y["q"], y["k"], y["v"], y["g"], hh, cu_seqlens=c, chunk=64,
+                                                    scale=0.2, output_final_state=True)
+        o, ht = run(x, h0d, torch.from_numpy(cu).to(dev))
+        oa, ha = run(part(0, t), h0d[:cut].contiguous(), cu_a)
+        ob, hb = run(part(t, T), h0d[cut:].contiguous(), cu_b)
+        assert torch.equal(o[:, :t], oa) and torch.equal(o[:, t:T], ob), kind
+        assert torch.equal(ht[:cut], ha) and torch.equal(ht[cut:], hb), kind
+
+
 # Degenerate scalar gates: g = 0 is causal linear attention (no decay, the state grows), g = -60
 # per token underflows every decay past the diagonal and the carried state.
 @pytest.mark.parametrize("case", ["nodecay", "strongdecay"])
@@ -451,7 +544,7 @@ def test_gla_bf16_degenerate_gates(dev, oracle, case):
 
 
 def test_ssd_gla_full_size_segmented(dev, oracle):
-    say("case: SSD-shaped GLA B=2 T=16384 H=64 HK=8 K=128 V=64 chunk 128, 8 segments per row (full size)")
+    say("case: SSD-shaped GLA B=2 T=16384 H=64 HK=8 K=128 V=64 chunk 128, 8 segments per row (full size, all heads)")
     w = wl.ssd_gla()
     x = {n: cuda(getattr(w, n), dev) for n in ("q", "k", "v", "g")}
     o, hf = sf.segmented_gla_fwd(x["q"], x["k"], x["v"], x["g"], w.n_seg, scale=w.scale, chunk=w.chunk,
@@ -459,23 +552,26 @@ def test_ssd_gla_full_size_segmented(dev, oracle):
     ou, hu = sf.gla_chunk_fwd(x["q"], x["k"], x["v"], x["g"], scale=w.scale, chunk=w.chunk,
                               output_final_state=True)
     torch.cuda.synchronize()
-    heads = [0, 1, 37, 63]
-    s = heads_subset(w, heads)
-    ro, rh = oracle.gla_forward(s["q"], s["k"], s["v"], s["g"], scale=w.scale)
-    hs = s["hs"]
-    check_bf16("segmented", f32(o)[:, :, hs], ro, f32(hf)[:, hs], rh)
-    check_bf16("unsegmented", f32(ou)[:, :, hs], ro, f32(hu)[:, hs], rh)
+    ro, rh = oracle.gla_forward(f32(w.q), f32(w.k), f32(w.v), f32(w.g), scale=w.scale)
+    o, hf, ou, hu = f32(o), f32(hf), f32(ou), f32(hu)
+    check_bf16("segmented", o, ro, hf, rh)
+    check_bf16("unsegmented", ou, ro, hu, rh)
+    check_units("segmented per (row, head)", [(f"o b{b} h{h}", o[b, :, h], ro[b, :, h]) for b in range(w.B)
+                                               for h in range(w.H)])
 
 
 def test_long_gdn_full_size_segmented(dev, oracle):
-    say("case: long GDN B=1 T=262144 H=16 K=V=128 bf16, 16 segments of 16384 (full size; head 3 vs oracle)")
+    say("case: long GDN B=1 T=262144 H=16 K=V=128 bf16, 16 segments of 16384 (full size; every head vs oracle)")
     w = wl.long_gdn()
     x = {n: cuda(getattr(w, n), dev) for n in ("q", "k", "v", "g", "beta")}
     o, hf = sf.segmented_gdn_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], w.n_seg, scale=w.scale,
                                  output_final_state=True)
     torch.cuda.synchronize()
-    say("  GPU done; oracle on head 3 over 262144 tokens")
-    s = heads_subset(w, [3])
-    ro, rh = oracle.gdn_forward(s["q"], s["k"], s["v"], s["g"], s["beta"], scale=w.scale)
-    hs = s["hs"]
-    check_bf16("segmented head 3", f32(o[:, :, hs]), ro, f32(hf[:, hs]), rh)
+    o, hf = f32(o), f32(hf)
+    say("  GPU done; oracle on all 16 heads over 262144 tokens")
+    ro, rh = oracle.gdn_forward(f32(w.q), f32(w.k), f32(w.v), f32(w.g), f32(w.beta), scale=w.scale)
+    check_bf16("segmented, all heads", o, ro, hf, rh)
+    L = w.T // w.n_seg
+    check_units("segmented per (segment, head)", [(f"o seg{j} h{h}", o[0, j * L:(j + 1) * L, h],
+                                                   ro[0, j * L:(j + 1) * L, h])
+                                                  for j in range(w.n_seg) for h in range(w.H)])

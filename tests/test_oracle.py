@@ -370,3 +370,34 @@ def test_tiny_config_is_seeded_and_shaped():
         assert (x == y).all()
     assert float(a.g.max()) <= 0.0 and 0.0 < float(a.beta.min()) and float(a.beta.max()) < 1.0
     np.testing.assert_allclose(np.linalg.norm(wl.to_f32(a.k), axis=-1), 1.0, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# Float32 build (CPU throughput baseline only)
+# ---------------------------------------------------------------------------
+
+def test_float32_build_matches_general_recurrence(oracle):
+    """The float32 token loops against the dense Eq. (1) form in float64 (delta rule) and the
+    masked quadratic SSD form (scalar gate), at float32 rounding: a slip in those loops (a
+    dropped decay, the output read before the update) fails here even though they are never a
+    parity reference."""
+    lens = [40, 0, 17]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q, k, v, g, beta, _ = rand_gdn(T=int(cu[-1]), H=2, K=8, V=6, seed=41, gate_shift=-1.0)
+    h0 = (np.random.default_rng(3).standard_normal((3, 2, 6, 8)) * 0.3).astype(np.float32)
+    o32, h32 = oracle.forward_f32("gdn", q, k, v, g, beta, h0, cu_seqlens=cu, scale=0.4)
+    for n, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        sl = lambda x: x[:, a:b]
+        ro, rh = eq1_reference(sl(q), sl(k), sl(v), sl(g), sl(beta), h0[n:n + 1], 0.4)
+        np.testing.assert_allclose(o32[:, a:b], ro, rtol=0, atol=2e-5)
+        np.testing.assert_allclose(h32[n], rh[0], rtol=0, atol=2e-5)
+    # scalar gate, zero initial state: O = (D o Q K^T) V with D_ti = exp(G_t - G_i), i <= t
+    T = 37
+    rng = np.random.default_rng(5)
+    q2, k2, v2 = (rng.standard_normal((1, T, 1, 4)).astype(np.float32) for _ in range(3))
+    g2 = -np.abs(rng.standard_normal((1, T, 1))).astype(np.float32) * 0.3
+    o2, _ = oracle.forward_f32("gla", q2, k2, v2, g2, scale=1.0)
+    G = np.cumsum(g2[0, :, 0].astype(np.float64))
+    D = np.tril(np.exp(G[:, None] - G[None, :]))
+    ref = (D * (q2[0, :, 0].astype(np.float64) @ k2[0, :, 0].T.astype(np.float64))) @ v2[0, :, 0]
+    np.testing.assert_allclose(o2[0, :, 0], ref, rtol=0, atol=1e-4 * max(1.0, np.abs(ref).max()))
