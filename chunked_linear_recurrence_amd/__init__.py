@@ -60,6 +60,7 @@ EXPORTED = (
     "sf_paged_gdn_chunk_fwd_workspace", "sf_paged_gdn_chunk_fwd", "sf_gdn_chunk_fwd_raw_gate",
     "sf_kda_recurrent_fwd", "sf_kda_decode",
     "sf_timing_enable", "sf_timing_collect", "sf_check_cu_seqlens", "sf_check_state_indices",
+    "sf_gdn_chunk_fwd_noalloc", "sf_static_scratch_bytes",
 )
 
 
@@ -120,6 +121,10 @@ def lib() -> ctypes.CDLL:
     L.sf_kda_decode.argtypes = [I, P, P, P, P, P, I, F, P, I, I, ctypes.c_longlong, P, P, I, I, I, I, F, P, P]
     L.sf_gate_transform.restype = I
     L.sf_gate_transform.argtypes = [I, P, P, P, ctypes.c_longlong, I, I, I, F, P, P]
+    L.sf_gdn_chunk_fwd_noalloc.restype = I
+    L.sf_gdn_chunk_fwd_noalloc.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P]
+    L.sf_static_scratch_bytes.restype = Z
+    L.sf_static_scratch_bytes.argtypes = []
     L.sf_check_cu_seqlens.restype = I
     L.sf_check_cu_seqlens.argtypes = [P, I, I]
     L.sf_check_state_indices.restype = I

@@ -191,6 +191,63 @@ sf_status sf_gdn_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void
     return hip_status(e, "sf_gdn_chunk_fwd launch");
 }
 
+// ---------------------------------------------------------------------------
+// The chunk forward with its workspace in a static device array, for callers that cannot allocate.
+// ---------------------------------------------------------------------------
+namespace {
+// Every GPU the library runs on holds its own copy of this array (module globals are per device)
+// until the process ends. Host code never uses its name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sf_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(SF_ERR_UNSUPPORTED, "device ordinal %d is past %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(SF_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SF_OK;
+}
+}  // namespace
+
+size_t sf_static_scratch_bytes(void) { return kScratchBytes; }
+
+sf_status sf_gdn_chunk_fwd_noalloc(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B,
+                                   int T, int H, int HK, int K, int V, float scale, void* out, float* ht,
+                                   void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
+    if (st != SF_OK) return st;
+    if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
+    if (K != V || (K != 64 && K != 128))
+        return fail(SF_ERR_UNSUPPORTED, "delta-rule kernels are built for K == V in {64, 128} (K=%d V=%d)", K, V);
+    const sf::GdnWorkspace need = sf::gdn_workspace_layout(nullptr, elem_bytes(dt), B, T, H, N, packed);
+    if (need.bytes > kScratchBytes)
+        return fail(SF_ERR_WORKSPACE, "these sizes need %zu bytes of scratch, more than the static %zu", need.bytes,
+                    kScratchBytes);
+    void* base = nullptr;
+    if ((st = scratch_for_current_device(&base)) != SF_OK) return st;
+    // nothing in the scratch has to start at zero: every byte a kernel reads was written earlier in this call
+    const sf::GdnWorkspace ws = sf::gdn_workspace_layout(base, elem_bytes(dt), B, T, H, N, packed);
+    hipError_t e = sf::launch_gdn(dt == SF_BF16, 0, q, k, v, g, beta, h0, cu_seqlens, ws, N, B, T, H, HK, K, V,
+                                  scale, out, ht, nullptr, static_cast<hipStream_t>(stream));
+    return hip_status(e, "sf_gdn_chunk_fwd_noalloc launch");
+}
+
 sf_status sf_gdn_chunk_fwd_raw_gate(sf_dtype dt, const void* q, const void* k, const void* v, const void* raw_gate,
                                     const float* A_log, const float* dt_bias, sf_gate_kind kind, float lower_bound,
                                     const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B, int T,

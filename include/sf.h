@@ -114,6 +114,26 @@ sf_status sf_gdn_chunk_fwd(sf_dtype dt, const void *q, const void *k, const void
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sf_gdn_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and results as sf_gdn_chunk_fwd without the workspace: the
+ * workspace is a static device array of the library (sf_static_scratch_bytes()
+ * bytes, 64 MiB; each GPU holds its own copy from the first call on it until
+ * the process ends). Sizes whose workspace (sf_gdn_chunk_fwd_workspace) exceeds
+ * it return SF_ERR_WORKSPACE with nothing enqueued. The entry point calls no
+ * allocator. Every call on one GPU shares that GPU's array, so calls that
+ * overlap on one GPU (other streams, other threads) race: the caller orders
+ * them. Nothing in the array has to start at zero.
+ */
+sf_status sf_gdn_chunk_fwd_noalloc(sf_dtype dt, const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, const float *h0,
+                                   const int32_t *cu_seqlens, int N, int B, int T, int H, int HK,
+                                   int K, int V, float scale, void *out, float *ht, void *stream);
+
+/* Bytes of the static device array behind sf_gdn_chunk_fwd_noalloc. */
+size_t sf_static_scratch_bytes(void);
+
+/*
  * Scalar-gated linear attention chunk forward (StateFlow Section 2.1, Eq. (1)
  * with F_t = exp(g_t) I; the Megatron-LM "Mamba2 state-passing context
  * parallelism" SSD core): S_t = exp(g_t) S_{t-1} + v_t k_t^T,

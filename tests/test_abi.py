@@ -285,3 +285,11 @@ def test_host_validators(L):
         sf.validate_cu_seqlens(torch.tensor([0, 3, 2], dtype=torch.int32), 3)
     with pytest.raises(sf.SfError):
         sf.validate_state_indices(torch.tensor([1, 1], dtype=torch.int32), 4)
+
+
+def test_noalloc_rejects_sizes_past_its_scratch(L):
+    """sf_gdn_chunk_fwd_noalloc refuses, on the host, sizes whose workspace exceeds its static array."""
+    assert L.sf_static_scratch_bytes() == 64 << 20
+    st = L.sf_gdn_chunk_fwd_noalloc(sf.SF_BF16, *([ctypes.c_void_p(FAKE)] * 5), None, None, 1, 1, 1 << 18, 16, 16,
+                                    128, 128, ctypes.c_float(0.1), ctypes.c_void_p(FAKE), None, None)
+    assert st == sf.SF_ERR_WORKSPACE and b"static" in L.sf_last_error()
