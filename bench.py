@@ -83,8 +83,8 @@ def algorithmic_bytes(w, kernel):
         gb = tok * w.H * 4 * (w.K + 1)
     if w.name in ("recurrent_gdn", "paged_gdn", "recurrent_kda"):   # every slot read and written (float32 pool)
         states = 2 * w.N * w.H * w.V * w.K * w.meta["pool"].element_size()
-        return qk + vo + states + (0 if kernel == "gdn_chain" else gb)
-    if kernel in ("gdn_chain", "gla_chain"):
+        return qk + vo + states + (0 if kernel in ("gdn_chain", "gdn_chain_slice") else gb)
+    if kernel in ("gdn_chain", "gdn_chain_slice", "gla_chain"):
         return qk + vo + states
     if kernel == "gdn_prep":
         return qk + gb

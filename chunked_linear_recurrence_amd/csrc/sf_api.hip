@@ -272,7 +272,7 @@ sf_status sf_gdn_chunk_fwd_raw_gate(sf_dtype dt, const void* q, const void* k, c
     const sf::GdnWorkspace ws = sf::gdn_workspace_layout(workspace, elem_bytes(dt), B, T, H, N, packed);
     const sf::GateSrc gs{raw_gate, dt == SF_BF16 ? 1 : 0, A_log, dt_bias, kind == SF_GATE_BOUNDED ? 1 : 0, lower_bound};
     hipError_t e = sf::launch_gdn(dt == SF_BF16, 0, q, k, v, nullptr, beta, h0, cu_seqlens, ws, N, B, T, H, HK, K, V,
-                                  scale, out, ht, nullptr, static_cast<hipStream_t>(stream), 3, -1, &gs);
+                                  scale, out, ht, nullptr, static_cast<hipStream_t>(stream), 3, &gs);
     return hip_status(e, "sf_gdn_chunk_fwd_raw_gate launch");
 }
 
@@ -391,12 +391,10 @@ sf_status sf_gdn_segmented_fwd(sf_dtype dt, const void* q, const void* k, const 
     const SegWorkspace ws = seg_layout(workspace, elem_bytes(dt), n_rows, L_seg, H, K, V);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf = dt == SF_BF16;
-    // Pre once on the segment view (with P, so the records serve both passes), then the summary
-    // pass, the exclusive scan and the forward pass from the true entry states
-    // (the key-key block W only if one of the two chain passes runs per 16-row slice)
-    const int pre_w = (sf::gdn_chain_per_slice((long)n_rows * H, V + K) || sf::gdn_chain_per_slice((long)n_rows * H, V)) ? 1 : 0;
+    // Pre once on the segment view (its records serve both passes), then the summary pass, the exclusive
+    // scan and the forward pass from the true entry states
     hipError_t e = sf::launch_gdn(bf, 0, q, k, v, g, beta, nullptr, nullptr, ws.pre, n_rows, n_rows, L_seg, H, HK, K, V,
-                                  scale, nullptr, nullptr, nullptr, s, 1, pre_w);
+                                  scale, nullptr, nullptr, nullptr, s, 1);
     if (e == hipSuccess)
         e = sf::launch_gdn(bf, 1, nullptr, k, v, g, beta, nullptr, nullptr, ws.pre, n_rows, n_rows, L_seg, H, HK, K, V,
                            1.f, nullptr, ws.S_ext, ws.M, s, 2);

@@ -101,14 +101,20 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // values stay in registers.
 typedef unsigned int u128 __attribute__((ext_vector_type(4)));
 
-// Inclusive prefix sum over the 64 lanes of a wavefront.
+// Inclusive prefix sum over the 64 lanes of a wavefront, on DPP lane moves: within each row of 16 lanes by
+// shifts of 1, 2, 4 and 8, then the last lane of row 0 / 2 added to rows 1 / 3 and the last lane of row 1
+// added to rows 2 and 3 (the gfx9 row broadcasts). Lanes whose DPP source is out of range add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+    x += dpp_or_zero<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_or_zero<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_or_zero<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_or_zero<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_or_zero<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_or_zero<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
     return x;
 }
 

@@ -10,17 +10,15 @@ namespace sf {
 
 constexpr int kGdnChunk = 64;
 
-// Bytes of one per-(chunk, head) factor record of the delta-rule "Pre" stage:
-// the 64x64 solve factor T, the 64x64 decay-masked query-key block P (both in
-// the q/k/v element type) and 256 float coefficients; for bf16 also the 64x64
-// key-key block W = K_c K_{c-1}^T of the chunk and its predecessor, which lets
-// the chain form K_c S_c^T without waiting for the state update of chunk c-1.
+// Bytes of one per-(chunk, head) factor record of the delta-rule "Pre" stage. float32: the 64x64 solve
+// factor T, the 64x64 decay-masked query-key block P (row-major float32) and 256 float coefficients. bf16:
+// T diag(beta) as six 1 KB MFMA fragments of its lower-triangular blocks and the 256 coefficients (the bf16
+// chain kernels form P themselves).
+constexpr size_t kGdnRecordBf16 = 6 * 1024 + 256 * sizeof(float);
 __host__ __device__ inline size_t gdn_factor_bytes(int elem_bytes) {
-    return (size_t)2 * kGdnChunk * kGdnChunk * elem_bytes + 256 * sizeof(float) +
-           (elem_bytes == 2 ? (size_t)kGdnChunk * kGdnChunk * 2 : 0);
+    return elem_bytes == 2 ? kGdnRecordBf16
+                           : (size_t)2 * kGdnChunk * kGdnChunk * elem_bytes + 256 * sizeof(float);
 }
-// byte offset of W in a bf16 record (after T, P and the coefficients)
-constexpr size_t kGdnWOffset = (size_t)2 * kGdnChunk * kGdnChunk * 2 + 256 * sizeof(float);
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -78,14 +76,12 @@ hipError_t launch_chunk_table(const int32_t* cu, int N, int chunk, long cap, int
 
 // mode: 0 = forward (writes out/ht), 1 = summary (writes S_ext into ht, M into Mout).
 // stages: 1 = Pre (and the chunk table) into the workspace, 2 = the chain from the workspace's
-// records, 3 = both. Pre of mode 0 also forms P, so its records serve both modes. pre_w: whether
-// Pre forms the key-key block W (read only by the per-slice chain kernel); -1 = as this call's
-// chain needs.
+// records, 3 = both. Pre's records serve both modes.
 hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const float* h0, const int32_t* cu,
                       const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int K, int V,
                       float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages = 3,
-                      int pre_w = -1, const GateSrc* gate_src = nullptr);
+                      const GateSrc* gate_src = nullptr);
 
 // Paged state cache around the chunk path (paging.hip). block = H*V*K elements per slot.
 hipError_t launch_state_gather(bool pool_bf16, const void* pool, long long slot_stride, int num_slots, const int32_t* idx,
@@ -116,10 +112,10 @@ hipError_t launch_gdn_decode(bool bf16, bool pool_bf16, const void* qkv, const v
                              void* out, hipStream_t s, bool per_channel = false, int bounded = 0,
                              float lower_bound = 0.f);
 
-// Compute units of the current device, and whether a bf16 delta-rule chain over `chains`
-// (sequence, head) pairs of `rows` state rows runs per 16-row slice (else per head).
+// Compute units of the current device, and whether a bf16 delta-rule forward chain over `chains`
+// (sequence, head) pairs of V state rows runs per 16-row slice (else per head).
 int device_cus();
-bool gdn_chain_per_slice(long chains, int rows);
+bool gdn_chain_per_slice(long chains, int V);
 
 hipError_t launch_gla(bool bf16, int mode, const void* q, const void* k, const void* v,
                       const float* g, const float* h0, const int32_t* cu, int N, int B, int T,

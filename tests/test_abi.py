@@ -49,7 +49,7 @@ def test_version(L):
 
 
 def test_workspace_sizes(L):
-    rec = 3 * 64 * 64 * 2 + 1024  # bf16 factor record: T, P, coefficients, W
+    rec = 6 * 1024 + 1024  # bf16 factor record: T diag(beta) fragments, coefficients
     dense = L.sf_gdn_chunk_fwd_workspace(sf.SF_BF16, 2, 4096, 16, 128, 128, 2, 0)
     assert dense == 2 * 64 * 16 * rec
     # packed: chunk offsets (N+1 ints) and table (cap int2), each 256-aligned, then factors
@@ -66,7 +66,7 @@ def test_workspace_sizes(L):
 def test_segmented_workspace_size(L):
     # per segment row: the Pre records, then M [rows, H, K, K], S_ext and S_in [rows, H, V, K], float32,
     # each 256-aligned
-    rec = 3 * 64 * 64 * 2 + 1024
+    rec = 6 * 1024 + 1024
     al = lambda x: (x + 255) // 256 * 256
     B, n_seg, T, H, K = 1, 16, 262144, 16, 128
     rows, L_seg = B * n_seg, T // n_seg
