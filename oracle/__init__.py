@@ -19,6 +19,9 @@ What each function follows (pages by title and section):
 * ``gla_summary``   Megatron-LM "Mamba2 state-passing context parallelism"
   (a_block and S_ext).
 * ``state_scan``    the exclusive causal scan of the same page.
+* ``gdn_backward``  the gradients of ``gdn_forward``'s token rule by reverse-mode
+  through the token loop, the state cotangent carried backwards (StateFlow
+  Section 2.2, Eq. (6)-(7)).
 * ``chunked_forward``  StateFlow Section 2.2 Eq. (2) chunk split, used only to
   check that the chunk algebra reproduces the token recurrence.
 * ``forward_f32``   the token loops of ``gdn_forward`` / ``gla_forward`` in float32:
@@ -79,6 +82,8 @@ def _load():
         lib.orc_state_scan.argtypes = [I, P, P, P, I, I, I, I, I, P, P]
         lib.orc_chunked_forward.argtypes = [I, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, P, P, I]
         lib.orc_forward_f32.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_float, P, P, I]
+        lib.orc_gdn_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D, P, P, P, P, P, P, I]
+        lib.orc_gdn_backward.restype = None
         lib.orc_forward_f32.restype = None
         lib.orc_max_threads.restype = I
         for f in (lib.orc_gdn_forward, lib.orc_gla_forward, lib.orc_gdn_summary,
@@ -137,6 +142,26 @@ def gdn_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, threads=
                             _ptr(cu), N, B, T, H, HK, K, V, float(scale), _ptr(out),
                             _ptr(ht), int(threads))
     return out, ht
+
+
+def gdn_backward(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None, threads=0):
+    """Gradients of the token-by-token Gated Delta Rule (reverse-mode through the token loop).
+
+    do [B,T,H,V] and dht [N,H,V,K] (None: zero) are the upstream gradients of the outputs and final
+    states. Returns a dict of float64 arrays dq, dk [B,T,HK,K] (summed over the value heads of each q/k
+    head), dv [B,T,H,V], dg, dbeta [B,T,H], dh0 [N,H,V,K]. Entries of tokens outside every sequence are
+    NaN."""
+    q, k, v, g, beta, do, h0, dht = map(_f32, (q, k, v, g, beta, do, h0, dht))
+    B, T, H, HK, K, V, N, cu = _dims(q, v, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / np.sqrt(K)
+    r = dict(dq=np.full((B, T, HK, K), np.nan), dk=np.full((B, T, HK, K), np.nan),
+             dv=np.full((B, T, H, V), np.nan), dg=np.full((B, T, H), np.nan),
+             dbeta=np.full((B, T, H), np.nan), dh0=np.zeros((N, H, V, K)))
+    _load().orc_gdn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dht),
+                             _ptr(cu), N, B, T, H, HK, K, V, float(scale), _ptr(r["dq"]), _ptr(r["dk"]),
+                             _ptr(r["dv"]), _ptr(r["dg"]), _ptr(r["dbeta"]), _ptr(r["dh0"]), int(threads))
+    return r
 
 
 def gla_forward(q, k, v, g, h0=None, cu_seqlens=None, scale=1.0, threads=0):

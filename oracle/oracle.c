@@ -582,6 +582,167 @@ void orc_forward_f32(int delta, const float *q, const float *k, const float *v,
     }
 }
 
+/* ---------------------------------------------------------------------------
+ * Gated Delta Rule backward ([GDN] token rule, differentiated by reverse-mode
+ * through the token loop; the state cotangent is carried from the last token
+ * back to the entry state, as StateFlow Section 2.2, Eq. (6)-(7) carries the
+ * gradient of the recurrence backwards through the chunks).
+ *
+ * Loss convention: the caller's upstream gradients are do = dLoss/do_t
+ * [B, T, H, V] and dht = dLoss/dht [N, H, V, K] (NULL: zero). The outputs are
+ * the gradients of the same loss with respect to every input:
+ *   dq, dk [B, T, HK, K] (summed over the H/HK value heads of a q/k head),
+ *   dv [B, T, H, V], dg, dbeta [B, T, H], dh0 [N, H, V, K] (NULL: skipped),
+ * all float64; entries of tokens outside every sequence are left as given.
+ *
+ * For one token, with gamma = exp(g) and the forward rule
+ *   D = gamma S_prev;  u = v - D k;  r = beta u;  S = D + r k^T;  o = scale S q,
+ * and dS the gradient with respect to S (all later use of S included):
+ *   dS += scale do q^T;   dq = scale S^T do
+ *   dr = dS k;            dk = dS^T r
+ *   du = beta dr;         dbeta = dr . u;   dv = du
+ *   dD = dS - du k^T;     dk -= D^T du
+ *   dg = gamma <dD, S_prev>;  and the gradient of S_prev is gamma dD.
+ * The states S_prev of the reverse sweep are recomputed with the forward rule
+ * from a checkpoint every BWD_BLOCK tokens.
+ * ------------------------------------------------------------------------- */
+#define BWD_BLOCK 64
+
+/* One token of the [GDN] rule on S [V][K] (in place). */
+static void gdn_token(double *S, int V, int K, const float *kt, const float *vt,
+                      double gam, double bt)
+{
+    for (long i = 0; i < (long)V * K; ++i)
+        S[i] *= gam;
+    for (int row = 0; row < V; ++row) {
+        double dk = 0.0;
+        for (int c = 0; c < K; ++c)
+            dk += S[(long)row * K + c] * (double)kt[c];
+        const double rr = bt * ((double)vt[row] - dk);
+        for (int c = 0; c < K; ++c)
+            S[(long)row * K + c] += rr * (double)kt[c];
+    }
+}
+
+void orc_gdn_backward(const float *q, const float *k, const float *v,
+                      const float *g, const float *beta, const float *h0,
+                      const float *dout, const float *dht, const int32_t *cu,
+                      int N, int B, int T, int H, int HK, int K, int V,
+                      double scale, double *dq, double *dk, double *dv,
+                      double *dg, double *dbeta, double *dh0, int nthreads)
+{
+    (void)B;
+    set_threads(nthreads);
+    const int grp = H / HK;
+    /* one (sequence, q/k head) per task: its value heads accumulate into the
+     * same dq, dk rows one after the other */
+    #pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int n = 0; n < N; ++n) {
+        for (int hk = 0; hk < HK; ++hk) {
+            int b, bos, eos;
+            seq_range(cu, n, T, &b, &bos, &eos);
+            const int ntok = eos - bos;
+            const long tok0 = (long)b * T + bos;
+            const long VK = (long)V * K;
+            const int nblk = (ntok + BWD_BLOCK - 1) / BWD_BLOCK;
+            double *ck = (double *)malloc(sizeof(double) * VK * (size_t)(nblk + 1));
+            double *Sb = (double *)malloc(sizeof(double) * VK * (BWD_BLOCK + 1));
+            double *dS = (double *)malloc(sizeof(double) * VK);
+            double *dD = (double *)malloc(sizeof(double) * VK);
+            double *u = (double *)malloc(sizeof(double) * V);
+            double *dr = (double *)malloc(sizeof(double) * V);
+            for (int t = 0; t < ntok; ++t)
+                for (int c = 0; c < K; ++c) {
+                    dq[((tok0 + t) * HK + hk) * K + c] = 0.0;
+                    dk[((tok0 + t) * HK + hk) * K + c] = 0.0;
+                }
+            for (int h = hk * grp; h < (hk + 1) * grp; ++h) {
+                const float *kp = k + (tok0 * HK + hk) * K, *qp = q + (tok0 * HK + hk) * K;
+                const float *vp = v + (tok0 * H + h) * V, *dop = dout + (tok0 * H + h) * V;
+                const float *gp = g + tok0 * H + h, *bp = beta + tok0 * H + h;
+                const long qs = (long)HK * K, vs = (long)H * V;
+                /* checkpoints: the state before tokens 0, BWD_BLOCK, 2 BWD_BLOCK, ... */
+                for (long i = 0; i < VK; ++i)
+                    ck[i] = h0 ? (double)h0[((long)n * H + h) * VK + i] : 0.0;
+                for (int bl = 0; bl < nblk; ++bl) {
+                    memcpy(ck + VK * (bl + 1), ck + VK * bl, sizeof(double) * VK);
+                    for (int t = bl * BWD_BLOCK; t < ntok && t < (bl + 1) * BWD_BLOCK; ++t)
+                        gdn_token(ck + VK * (bl + 1), V, K, kp + t * qs, vp + t * vs,
+                                  exp((double)gp[(long)t * H]), (double)bp[(long)t * H]);
+                }
+                for (long i = 0; i < VK; ++i)
+                    dS[i] = dht ? (double)dht[((long)n * H + h) * VK + i] : 0.0;
+                for (int bl = nblk - 1; bl >= 0; --bl) {
+                    const int t0 = bl * BWD_BLOCK;
+                    const int nt = (ntok - t0 < BWD_BLOCK) ? ntok - t0 : BWD_BLOCK;
+                    /* Sb[i] = state before token t0 + i */
+                    memcpy(Sb, ck + VK * bl, sizeof(double) * VK);
+                    for (int i = 0; i < nt; ++i) {
+                        memcpy(Sb + VK * (i + 1), Sb + VK * i, sizeof(double) * VK);
+                        gdn_token(Sb + VK * (i + 1), V, K, kp + (t0 + i) * qs, vp + (t0 + i) * vs,
+                                  exp((double)gp[(long)(t0 + i) * H]), (double)bp[(long)(t0 + i) * H]);
+                    }
+                    for (int i = nt - 1; i >= 0; --i) {
+                        const int t = t0 + i;
+                        const double *Sp = Sb + VK * i, *Sn = Sb + VK * (i + 1);
+                        const float *kt = kp + t * qs, *qt = qp + t * qs, *vt = vp + t * vs, *dot = dop + t * vs;
+                        const double gam = exp((double)gp[(long)t * H]), bt = (double)bp[(long)t * H];
+                        double *dqt = dq + ((tok0 + t) * HK + hk) * K, *dkt = dk + ((tok0 + t) * HK + hk) * K;
+                        /* o = scale S q */
+                        for (int row = 0; row < V; ++row)
+                            for (int c = 0; c < K; ++c) {
+                                dS[(long)row * K + c] += scale * (double)dot[row] * (double)qt[c];
+                                dqt[c] += scale * Sn[(long)row * K + c] * (double)dot[row];
+                            }
+                        /* S = D + r k^T with D = gamma S_prev, u = v - D k, r = beta u */
+                        for (int row = 0; row < V; ++row) {
+                            double dk_row = 0.0, acc = 0.0;
+                            for (int c = 0; c < K; ++c) {
+                                dk_row += gam * Sp[(long)row * K + c] * (double)kt[c];
+                                acc += dS[(long)row * K + c] * (double)kt[c];
+                            }
+                            u[row] = (double)vt[row] - dk_row;
+                            dr[row] = acc;
+                        }
+                        double db = 0.0;
+                        for (int row = 0; row < V; ++row) {
+                            db += dr[row] * u[row];
+                            dv[(tok0 + t) * H * V + (long)h * V + row] = bt * dr[row];
+                        }
+                        dbeta[(tok0 + t) * H + h] = db;
+                        for (int c = 0; c < K; ++c) {
+                            double a1 = 0.0, a2 = 0.0;
+                            for (int row = 0; row < V; ++row) {
+                                a1 += dS[(long)row * K + c] * bt * u[row];          /* dS^T r */
+                                a2 += gam * Sp[(long)row * K + c] * bt * dr[row];   /* D^T du */
+                            }
+                            dkt[c] += a1 - a2;
+                        }
+                        double dgam = 0.0;
+                        for (int row = 0; row < V; ++row)
+                            for (int c = 0; c < K; ++c) {
+                                const long i2 = (long)row * K + c;
+                                dD[i2] = dS[i2] - bt * dr[row] * (double)kt[c];
+                                dgam += dD[i2] * Sp[i2];
+                            }
+                        dg[(tok0 + t) * H + h] = dgam * gam;
+                        for (long i2 = 0; i2 < VK; ++i2)
+                            dS[i2] = gam * dD[i2];
+                    }
+                }
+                if (dh0)
+                    memcpy(dh0 + ((long)n * H + h) * VK, dS, sizeof(double) * VK);
+            }
+            free(ck);
+            free(Sb);
+            free(dS);
+            free(dD);
+            free(u);
+            free(dr);
+        }
+    }
+}
+
 int orc_max_threads(void)
 {
 #ifdef _OPENMP
