@@ -11,6 +11,9 @@ Functions (same names as the C entry points, without the ``sf_`` prefix):
 
 * ``gdn_chunk_fwd``     Gated Delta Rule forward, 64-token chunks
                         (attention-gym "Linear Attention", "Gated Delta Rule").
+* ``gdn_chunk_bwd``     its gradients (dq, dk, dv, dg, dbeta, dh0), the state
+                        gradient carried from the last chunk back to the first
+                        (StateFlow Section 2.2, Eq. (6)-(7)).
 * ``gla_chunk_fwd``     scalar-gated linear attention forward
                         (StateFlow Eq. (1), scalar-identity transition).
 * ``segment_summary``   affine summary per segment row (attention-gym
@@ -60,7 +63,7 @@ EXPORTED = (
     "sf_paged_gdn_chunk_fwd_workspace", "sf_paged_gdn_chunk_fwd", "sf_gdn_chunk_fwd_raw_gate",
     "sf_kda_recurrent_fwd", "sf_kda_decode",
     "sf_timing_enable", "sf_timing_collect", "sf_check_cu_seqlens", "sf_check_state_indices",
-    "sf_gdn_chunk_fwd_noalloc", "sf_static_scratch_bytes",
+    "sf_gdn_chunk_fwd_noalloc", "sf_static_scratch_bytes", "sf_gdn_chunk_bwd_workspace", "sf_gdn_chunk_bwd",
 )
 
 
@@ -125,6 +128,10 @@ def lib() -> ctypes.CDLL:
     L.sf_gdn_chunk_fwd_noalloc.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P]
     L.sf_static_scratch_bytes.restype = Z
     L.sf_static_scratch_bytes.argtypes = []
+    L.sf_gdn_chunk_bwd_workspace.restype = Z
+    L.sf_gdn_chunk_bwd_workspace.argtypes = [I, I, I, I, I, I, I, I]
+    L.sf_gdn_chunk_bwd.restype = I
+    L.sf_gdn_chunk_bwd.argtypes = [I, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, P, P, P, P, Z, P]
     L.sf_check_cu_seqlens.restype = I
     L.sf_check_cu_seqlens.argtypes = [P, I, I]
     L.sf_check_state_indices.restype = I
@@ -247,6 +254,37 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, scal
                                   _ptr(cu_seqlens), N, B, T, H, HK, K, V, float(scale), _ptr(out), _ptr(ht),
                                   _ptr(ws), nbytes, _stream()))
     return out, ht
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, *, cu_seqlens=None, scale=None):
+    """Gated Delta Rule chunk backward: the gradients of sum(do * o) + sum(dht * ht) for the forward of
+    gdn_chunk_fwd with the same arguments. do [B,T,H,V] in q.dtype; dht [N,H,V,K] float32 or None.
+    Returns (dq, dk, dv in q.dtype, dg, dbeta float32 [B,T,H], dh0 float32 [N,H,V,K]). Entries of tokens at
+    or past cu_seqlens[-1] are left uninitialised. Needs HK == H."""
+    B, T, H, HK, K, V, N = _token_args(q, k, v, g, beta, initial_state, cu_seqlens)
+    dev = q.device
+    _need(do, "do", dtype=q.dtype, ndim=4, device=dev)
+    if tuple(do.shape) != (B, T, H, V):
+        raise ValueError(f"do must be [{B}, {T}, {H}, {V}], got {tuple(do.shape)}")
+    if dht is not None:
+        _need(dht, "dht", dtype=torch.float32, ndim=4, device=dev)
+        if tuple(dht.shape) != (N, H, V, K):
+            raise ValueError(f"dht must be [{N}, {H}, {V}, {K}], got {tuple(dht.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dg = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    dbeta = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((N, H, V, K), dtype=torch.float32, device=dev)
+    dt = _dt(q)
+    nbytes = lib().sf_gdn_chunk_bwd_workspace(dt, B, T, H, K, V, N, int(cu_seqlens is not None))
+    ws = _workspace(nbytes, dev)
+    _check(lib().sf_gdn_chunk_bwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(do),
+                                  _ptr(dht), _ptr(cu_seqlens), N, B, T, H, HK, K, V, float(scale), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(ws), nbytes, _stream()))
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def gdn_chunk_fwd_raw_gate(q, k, v, raw_gate, A_log, dt_bias, beta, initial_state=None, *, kind,

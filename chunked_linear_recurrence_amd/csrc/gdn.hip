@@ -95,31 +95,6 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
     }
 }
 
-// Locate chunk `slot`: batch row, first token, length, index of the chunk in
-// its sequence. false past the end.
-__device__ __forceinline__ bool chunk_coords(int slot, const int2* table, const int32_t* cu, int T,
-                                             int nc, int& b, int& t0, int& L, int& ci) {
-    if (table) {
-        const int2 e = table[slot];
-        if (e.x < 0) return false;
-        b = 0;
-        t0 = cu[e.x] + GC * e.y;
-        L = min(GC, cu[e.x + 1] - t0);
-        ci = e.y;
-    } else {
-        b = slot / nc;
-        ci = slot % nc;
-        t0 = ci * GC;
-        L = min(GC, T - t0);
-    }
-    return true;
-}
-__device__ __forceinline__ bool chunk_coords(int slot, const int2* table, const int32_t* cu, int T,
-                                             int nc, int& b, int& t0, int& L) {
-    int ci;
-    return chunk_coords(slot, table, cu, T, nc, b, t0, L, ci);
-}
-
 // ---------------------------------------------------------------------------
 // Pre: per (chunk slot, head) -> T, P, coefficients.
 // Record layout: T [64][64] ST | P [64][64] ST | coef float[256]:

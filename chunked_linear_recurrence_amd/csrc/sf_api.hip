@@ -192,6 +192,39 @@ sf_status sf_gdn_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void
 }
 
 // ---------------------------------------------------------------------------
+// Chunk backward
+// ---------------------------------------------------------------------------
+size_t sf_gdn_chunk_bwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N, int packed) {
+    if ((dt != SF_F32 && dt != SF_BF16) || B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0 || N < 0) return 0;
+    return sf::gdn_bwd_workspace_layout(nullptr, B, T, H, K, V, N, packed != 0).bytes;
+}
+
+sf_status sf_gdn_chunk_bwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* h0, const void* dout, const float* dht,
+                           const int32_t* cu_seqlens, int N, int B, int T, int H, int HK, int K, int V,
+                           float scale, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
+    if (st != SF_OK) return st;
+    if (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta)
+        return fail(SF_ERR_INVALID, "q, k, v, g, beta, dout, dq, dk, dv, dg and dbeta must not be NULL");
+    if (HK != H) return fail(SF_ERR_UNSUPPORTED, "the chunk backward needs one q/k head per value head (HK=%d H=%d)", HK, H);
+    if ((K != 64 && K != 128) || (V != 64 && V != 128))
+        return fail(SF_ERR_UNSUPPORTED, "the chunk backward is built for K, V in {64, 128} (K=%d V=%d)", K, V);
+    if (H > 65535) return fail(SF_ERR_UNSUPPORTED, "H=%d is past the 65535 heads of a launch", H);
+    const sf::GdnBwdWorkspace need = sf::gdn_bwd_workspace_layout(nullptr, B, T, H, K, V, N, packed);
+    if (!workspace || workspace_bytes < need.bytes)
+        return fail(SF_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                    need.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(SF_ERR_INVALID, "workspace must be 256-byte aligned");
+    const sf::GdnBwdWorkspace ws = sf::gdn_bwd_workspace_layout(workspace, B, T, H, K, V, N, packed);
+    hipError_t e = sf::launch_gdn_bwd(dt == SF_BF16, q, k, v, g, beta, h0, dout, dht, cu_seqlens, ws, N, B, T, H, K, V,
+                                      scale, dq, dk, dv, dg, dbeta, dh0, static_cast<hipStream_t>(stream));
+    return hip_status(e, "sf_gdn_chunk_bwd launch");
+}
+
+// ---------------------------------------------------------------------------
 // The chunk forward with its workspace in a static device array, for callers that cannot allocate.
 // ---------------------------------------------------------------------------
 namespace {

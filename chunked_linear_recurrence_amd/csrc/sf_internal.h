@@ -20,6 +20,31 @@ __host__ __device__ inline size_t gdn_factor_bytes(int elem_bytes) {
                            : (size_t)2 * kGdnChunk * kGdnChunk * elem_bytes + 256 * sizeof(float);
 }
 
+// Locate chunk `slot`: batch row, first token, length, index of the chunk in
+// its sequence. false past the end.
+__device__ __forceinline__ bool chunk_coords(int slot, const int2* table, const int32_t* cu, int T,
+                                             int nc, int& b, int& t0, int& L, int& ci) {
+    if (table) {
+        const int2 e = table[slot];
+        if (e.x < 0) return false;
+        b = 0;
+        t0 = cu[e.x] + kGdnChunk * e.y;
+        L = min(kGdnChunk, cu[e.x + 1] - t0);
+        ci = e.y;
+    } else {
+        b = slot / nc;
+        ci = slot % nc;
+        t0 = ci * kGdnChunk;
+        L = min(kGdnChunk, T - t0);
+    }
+    return true;
+}
+__device__ __forceinline__ bool chunk_coords(int slot, const int2* table, const int32_t* cu, int T,
+                                             int nc, int& b, int& t0, int& L) {
+    int ci;
+    return chunk_coords(slot, table, cu, T, nc, b, t0, L, ci);
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace carve-up for the delta-rule path (packed: chunk offsets + table).
@@ -54,6 +79,41 @@ inline GdnWorkspace gdn_workspace_layout(void* base, int elem_bytes, int B, int 
     return w;
 }
 
+// Workspace of the delta-rule chunk backward (float32 throughout): the chunk table of packed inputs, one
+// record per (chunk slot, head) (T [64][64], W and Qt [64][K], 256 coefficients), every chunk's entry
+// state and the gradient of every chunk's exit state ([slots][H][V][K] each).
+struct GdnBwdWorkspace {
+    int* chunk_off;
+    int2* table;
+    float* rec;
+    float* states;
+    float* dstates;
+    size_t bytes;
+};
+inline size_t gdn_bwd_record_floats(int K) {
+    return (size_t)kGdnChunk * kGdnChunk + 2 * (size_t)kGdnChunk * K + 256;
+}
+inline GdnBwdWorkspace gdn_bwd_workspace_layout(void* base, int B, int T, int H, int K, int V, int N, bool packed) {
+    GdnBwdWorkspace w{};
+    size_t off = 0;
+    uint8_t* p = static_cast<uint8_t*>(base);
+    const long slots = gdn_slots(B, T, N, packed);
+    auto take = [&](size_t bytes) {
+        uint8_t* r = p ? p + off : nullptr;
+        off += align256(bytes);
+        return r;
+    };
+    if (packed) {
+        w.chunk_off = reinterpret_cast<int*>(take(sizeof(int) * (size_t)(N + 1)));
+        w.table = reinterpret_cast<int2*>(take(sizeof(int2) * (size_t)slots));
+    }
+    w.rec = reinterpret_cast<float*>(take(sizeof(float) * gdn_bwd_record_floats(K) * (size_t)slots * H));
+    w.states = reinterpret_cast<float*>(take(sizeof(float) * (size_t)slots * H * V * K));
+    w.dstates = reinterpret_cast<float*>(take(sizeof(float) * (size_t)slots * H * V * K));
+    w.bytes = off;
+    return w;
+}
+
 // Raw gate projection read by the delta-rule Pre stage in place of g (the gate transform fused
 // into its gate load): g = -exp(A_log[h]) softplus(raw + dt_bias[h]) or, bounded,
 // lower_bound sigmoid(exp(A_log[h]) (raw + dt_bias[h])). raw == nullptr: read g as given.
@@ -82,6 +142,15 @@ hipError_t launch_gdn(bool bf16, int mode, const void* q, const void* k, const v
                       const GdnWorkspace& ws, int N, int B, int T, int H, int HK, int K, int V,
                       float scale, void* out, float* ht, float* Mout, hipStream_t s, int stages = 3,
                       const GateSrc* gate_src = nullptr);
+
+// Delta-rule chunk backward (gdn_bwd.hip): dq, dk, dv in the input type, dg, dbeta float32 [B, T, H], dh0
+// float32 [N, H, V, K] (or null) for upstream gradients dout [B, T, H, V] (input type) and dht (or null:
+// zero). Needs HK == H.
+hipError_t launch_gdn_bwd(bool bf16, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* h0, const void* dout, const float* dht,
+                          const int32_t* cu, const GdnBwdWorkspace& ws, int N, int B, int T, int H, int K,
+                          int V, float scale, void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                          float* dh0, hipStream_t s);
 
 // Paged state cache around the chunk path (paging.hip). block = H*V*K elements per slot.
 hipError_t launch_state_gather(bool pool_bf16, const void* pool, long long slot_stride, int num_slots, const int32_t* idx,

@@ -83,14 +83,11 @@ const char *sf_last_error(void);
  * Workspace bytes needed by sf_gdn_chunk_fwd for these sizes (packed != 0
  * when cu_seqlens is passed; then B must be 1). The workspace holds the
  * per-chunk factors of the chunk decomposition (StateFlow Section 2.2,
- * Eq. (2), "Pre"): the unit-lower-triangular WY/UT solve factor, the
- * per-token decay coefficients and the decay-masked query-key block, plus
- * for bf16 the key-key block of each chunk with its predecessor, which lets
- * the chain overlap consecutive chunk steps (for bf16 launches with more
- * than two 16-row state slices per compute unit, the chain forms the
- * query-key block itself and does without the key-key block, so those two
- * parts are left unwritten), and the device chunk table of packed inputs.
- * The size does not depend on that choice. Returns 0 for invalid sizes.
+ * Eq. (2), "Pre"), one record per (64-token chunk, head): for bf16 the
+ * unit-lower-triangular WY/UT solve factor scaled by beta (as MFMA fragments)
+ * and the per-token decay coefficients; for float32 the solve factor, the
+ * decay-masked query-key block and the coefficients. Packed inputs add the
+ * device chunk table. Returns 0 for invalid sizes.
  */
 size_t sf_gdn_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N,
                                   int packed);
@@ -111,6 +108,40 @@ sf_status sf_gdn_chunk_fwd(sf_dtype dt, const void *q, const void *k, const void
                            const float *g, const float *beta, const float *h0,
                            const int32_t *cu_seqlens, int N, int B, int T, int H, int HK,
                            int K, int V, float scale, void *out, float *ht,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes needed by sf_gdn_chunk_bwd for these sizes (packed != 0 when
+ * cu_seqlens is passed). It holds, in float32, one record per (64-token chunk,
+ * head) with the chunk's solve factor T, its WY factor W = T diag(beta Gamma) K,
+ * Qt = scale diag(Gamma) Q - P W and decay coefficients, every chunk's entry
+ * state and the gradient of every chunk's exit state ([chunks, H, V, K] each),
+ * and the device chunk table of packed inputs. Returns 0 for invalid sizes. */
+size_t sf_gdn_chunk_bwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N,
+                                  int packed);
+
+/*
+ * Gated Delta Rule chunk backward: the gradients of sf_gdn_chunk_fwd's loss
+ * sum(dout * out) + sum(dht * ht) with respect to its inputs (the token rule of
+ * attention-gym "Linear Attention", section "Gated Delta Rule", differentiated
+ * through the chunk form of StateFlow Section 2.2, Eq. (2); the state gradient
+ * runs from the last chunk back to the first as in its Eq. (6)-(7)).
+ *   q, k, v, g, beta, h0, cu_seqlens, N, B, T, H, HK, K, V, scale
+ *          as sf_gdn_chunk_fwd (h0 NULL: zero initial states)
+ *   dout   [B, T, H, V] dt, the gradient of the output
+ *   dht    [N, H, V, K] float32, the gradient of the final states, or NULL (zero)
+ *   dq, dk [B, T, HK, K] dt;  dv [B, T, H, V] dt;  dg, dbeta [B, T, H] float32;
+ *   dh0    [N, H, V, K] float32 or NULL (not written)
+ *          Entries of tokens at or past cu_seqlens[N] are not written.
+ *   workspace  at least sf_gdn_chunk_bwd_workspace(...) bytes, 256-byte aligned
+ * All arithmetic is float32. Supported: HK == H, K and V in {64, 128}; others
+ * return SF_ERR_UNSUPPORTED. Caller-owned device memory throughout; enqueued on
+ * stream, no synchronisation.
+ */
+sf_status sf_gdn_chunk_bwd(sf_dtype dt, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const float *h0,
+                           const void *dout, const float *dht, const int32_t *cu_seqlens,
+                           int N, int B, int T, int H, int HK, int K, int V, float scale,
+                           void *dq, void *dk, void *dv, float *dg, float *dbeta, float *dh0,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*

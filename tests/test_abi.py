@@ -293,3 +293,42 @@ def test_noalloc_rejects_sizes_past_its_scratch(L):
     st = L.sf_gdn_chunk_fwd_noalloc(sf.SF_BF16, *([ctypes.c_void_p(FAKE)] * 5), None, None, 1, 1, 1 << 18, 16, 16,
                                     128, 128, ctypes.c_float(0.1), ctypes.c_void_p(FAKE), None, None)
     assert st == sf.SF_ERR_WORKSPACE and b"static" in L.sf_last_error()
+
+
+def test_bwd_workspace_size(L):
+    # float32 records (T [64][64], W and Qt [64][K], 256 coefficients), entry states and exit-state gradients
+    B, T, H, K, V = 2, 4096, 16, 128, 128
+    slots = B * (T // 64)
+    rec = 4 * (64 * 64 + 2 * 64 * K + 256)
+    al = lambda x: (x + 255) // 256 * 256
+    want = al(slots * H * rec) + 2 * al(slots * H * V * K * 4)
+    assert L.sf_gdn_chunk_bwd_workspace(sf.SF_BF16, B, T, H, K, V, B, 0) == want
+    assert L.sf_gdn_chunk_bwd_workspace(7, B, T, H, K, V, B, 0) == 0
+
+
+def bwd_call(L, **kw):
+    a = dict(dt=sf.SF_BF16, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, dout=FAKE, dht=None, cu=None,
+             N=1, B=1, T=128, H=4, HK=4, K=128, V=128, scale=ctypes.c_float(0.1), dq=FAKE, dk=FAKE, dv=FAKE,
+             dg=FAKE, dbeta=FAKE, dh0=None, ws=FAKE * 256, wsb=1 << 40, s=None)
+    a.update(kw)
+    st = L.sf_gdn_chunk_bwd(a["dt"], a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["dout"], a["dht"], a["cu"],
+                            a["N"], a["B"], a["T"], a["H"], a["HK"], a["K"], a["V"], a["scale"], a["dq"], a["dk"],
+                            a["dv"], a["dg"], a["dbeta"], a["dh0"], a["ws"], a["wsb"], a["s"])
+    return st, L.sf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(HK=2), sf.SF_ERR_UNSUPPORTED, "one q/k head per value head"),
+    (dict(HK=3), sf.SF_ERR_INVALID, "divide"),
+    (dict(dout=None), sf.SF_ERR_INVALID, "NULL"),
+    (dict(dbeta=None), sf.SF_ERR_INVALID, "NULL"),
+    (dict(K=96), sf.SF_ERR_UNSUPPORTED, "{64, 128}"),
+    (dict(V=32), sf.SF_ERR_UNSUPPORTED, "{64, 128}"),
+    (dict(wsb=16), sf.SF_ERR_WORKSPACE, "smaller"),
+    (dict(ws=FAKE * 256 + 8), sf.SF_ERR_INVALID, "aligned"),
+    (dict(N=3), sf.SF_ERR_INVALID, "N (3) must equal B"),
+])
+def test_bwd_rejects_invalid_arguments(L, kw, status, msg):
+    st, err = bwd_call(L, **kw)
+    assert st == status, err
+    assert msg in err

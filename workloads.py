@@ -144,6 +144,14 @@ def delta_rule_inputs(*, B, T, H, K, V, HK=None, dtype=torch.bfloat16, seed=0,
                 g=torch.from_numpy(g), beta=torch.from_numpy(beta), h0=h0, rng=rng)
 
 
+def upstream_grads(rng, *, B, T, H, V, K, N, dtype=torch.bfloat16, dht=True):
+    """Upstream gradients for the backward: do ~ N(0,1) [B,T,H,V] in the input type, dht ~ N(0,1) float32
+    [N,H,V,K] (or None)."""
+    do = _normal(rng, (B, T, H, V))
+    dh = torch.from_numpy(_normal(rng, (N, H, V, K))) if dht else None
+    return dict(do=_cast(do, dtype), dht=dh)
+
+
 def scalar_gate_inputs(*, B, T, H, HK, K, V, dtype=torch.bfloat16, seed=0):
     """q, k, v ~ N(0,1) (not normalised); per-head A = -softplus(N(0,1)) [H];
     dt = softplus(N(0,1)) [B, T, H]; g = A * dt."""
