@@ -23,7 +23,7 @@ carry measured_peak: the bandwidth a plain 1 GiB device-to-device copy reaches
 on the same GPU (read plus write bytes), and the fraction of that.
 
 Other workloads (--workload varlen_gdn | long_gdn | ssd_gla | tiny_gdn | decode_gdn | recurrent_gdn |
-gate_transform | paged_gdn | recurrent_kda | decode_kda) are for
+gate_transform | paged_gdn | recurrent_kda | decode_kda | dense_gdn_bwd) are for
 measurement only; the headline line is the default one. decode_gdn times one sf_gdn_decode call
 (one token for each of 256 sequences against a 514 MB float32 state pool, which is larger than
 the last-level cache, so it runs on one input set).
@@ -41,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GDN chunk-fwd tokens/s (bf16, K=V=128) + % of MFMA/HBM roofline, 1 MI355X"
+METRIC_BWD = "GDN chunk-bwd tokens/s (bf16, K=V=128) + % of HBM roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 
@@ -71,6 +72,8 @@ def algorithmic_bytes(w, kernel):
     written, V*K float32 each."""
     if kernel in ("gdn_decode", "kda_decode", "decode_path"):
         return decode_bytes(w)
+    if w.name == "dense_gdn_bwd":
+        return bwd_bytes(w, kernel)
     if kernel in ("gate_transform", "gate_path"):   # raw in, float32 out, the per-head parameters
         return w.raw.numel() * (w.raw.element_size() + 4) + (w.A_log.numel() + w.dt_bias.numel()) * 4
     eb = w.q.element_size()
@@ -89,6 +92,24 @@ def algorithmic_bytes(w, kernel):
     if kernel == "gdn_prep":
         return qk + gb
     return qk + vo + gb + states      # whole path
+
+
+def bwd_bytes(w, kernel):
+    """Chunk backward, by definition of the computation: reads q, k, v, do (element type), g and beta
+    (float32), h0 and dht; writes dq, dk, dv (element type), dg and dbeta (float32) and dh0. Per kernel,
+    the share each one reads or writes of those (its intermediates excluded)."""
+    eb = w.q.element_size()
+    tok = w.tokens
+    row = tok * w.H * w.K * eb            # one of q, k, v, do, dq, dk, dv (K == V)
+    gate = tok * w.H * 4                  # one of g, beta, dg, dbeta
+    state = w.N * w.H * w.V * w.K * 4     # one of h0, dht, dh0
+    parts = {"gdn_bwd_prep": 2 * row + 2 * gate,          # q, k, g, beta
+             "gdn_bwd_states": 2 * row + state,           # k, v, h0
+             "gdn_bwd_dstate": 2 * row + 2 * state,       # k, do, dht, dh0
+             "gdn_bwd_grad": 4 * row + 3 * row + 2 * gate}  # q, k, v, do; dq, dk, dv, dg, dbeta
+    if kernel in parts:
+        return parts[kernel]
+    return 7 * row + 4 * gate + 3 * state
 
 
 def two_pass_bytes(w):
@@ -159,6 +180,9 @@ def make_sets(w, dev, rotate):
         for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens"):
             t = getattr(w, n)
             s[n] = None if t is None else t.to(dev).contiguous()
+        if w.name == "dense_gdn_bwd":
+            s["do"] = w.meta["do"].to(dev).contiguous()
+            s["dht"] = w.meta["dht"].to(dev).contiguous()
         if w.name in ("recurrent_gdn", "paged_gdn", "recurrent_kda"):
             s["pool"] = w.meta["pool"].to(dev).contiguous()
             s["state_indices"] = w.meta["state_indices"].to(dev)
@@ -193,6 +217,10 @@ def step_fn(w):
         def step(s):
             return sf.gdn_recurrent_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["pool"],
                                         state_indices=s["state_indices"], scale=w.scale)
+    elif w.name == "dense_gdn_bwd":
+        def step(s):
+            return sf.gdn_chunk_bwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["do"], s["h0"], s["dht"],
+                                    scale=w.scale)
     elif w.name in ("dense_gdn", "tiny_gdn", "varlen_gdn"):
         def step(s):
             return sf.gdn_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["h0"], cu_seqlens=s["cu_seqlens"],
@@ -245,6 +273,16 @@ def cpu_baseline(w):
                 "cpu_model": model,
                 "sample": f"the whole {w.name} step ({w.tokens} rows x {w.H} heads), one float64 pass, "
                           f"{dt:.2f} s wall"}
+    if w.name == "dense_gdn_bwd":
+        log(f"cpu_baseline: float64 backward oracle on {threads} threads ...")
+        t0 = time.perf_counter()
+        oracle.gdn_backward(f(w.q), f(w.k), f(w.v), f(w.g), f(w.beta), f(w.meta["do"]), f(w.h0), f(w.meta["dht"]),
+                            scale=w.scale, threads=threads)
+        dt = time.perf_counter() - t0
+        return {"value": w.tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "precision": "f64",
+                "cpu_model": model,
+                "sample": f"the whole {w.name} workload ({w.tokens} tokens x {w.H} heads), one float64 pass of the "
+                          f"reverse-mode token loop, {dt:.2f} s wall"}
     if w.name in ("recurrent_kda", "recurrent_gdn", "paged_gdn"):
         args = dict(q=f(w.q), k=f(w.k), v=f(w.v), g=f(w.g))
         log(f"cpu_baseline: float64 oracle on {threads} threads ...")
@@ -322,7 +360,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="input sets cycled through (cache defeat)")
     ap.add_argument("--workload", default="dense_gdn",
                     choices=["dense_gdn", "tiny_gdn", "varlen_gdn", "long_gdn", "ssd_gla", "decode_gdn",
-                             "recurrent_gdn", "gate_transform", "paged_gdn", "recurrent_kda", "decode_kda"])
+                             "recurrent_gdn", "gate_transform", "paged_gdn", "recurrent_kda", "decode_kda",
+                             "dense_gdn_bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the second pass, whose launches are bracketed with HIP events")
@@ -418,7 +457,7 @@ def main():
         roof["frac_of_measured"] = round(roof["achieved"] / copy_gbs, 4)
 
     out = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_BWD if w.name == "dense_gdn_bwd" else METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "p50_ms": p50_ms, "min_ms": min_ms,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,

@@ -44,15 +44,47 @@ struct BwdRec {
 template <typename ST>
 __device__ __forceinline__ float ld(const ST* p) { return Elem<ST>::to_f(*p); }
 
-// Rows [t0, t0 + L) of one head of a [rows][heads][D] tensor into LDS as float [64][D + 1], zero past L.
-template <typename ST, int D>
-__device__ __forceinline__ void load_rows(const ST* __restrict__ src, long row0, int L, int heads, int head,
-                                          float* dst) {
-    for (int i = threadIdx.x; i < BC * D; i += NT) {
-        const int t = i / D, c = i % D;
-        dst[t * (D + 1) + c] = t < L ? ld(src + ((row0 + t) * heads + head) * (long)D + c) : 0.f;
+// element e of a 16-byte piece holding 8 bf16 or 4 float
+template <typename ST>
+__device__ __forceinline__ ST unit_of(const u128& u, int e) {
+    if constexpr (sizeof(ST) == 2) {
+        const uint32_t w = u[e >> 1];
+        return (ST)((e & 1) ? (w >> 16) : (w & 0xffffu));
+    } else {
+        return __uint_as_float(u[e]);
     }
 }
+
+// A [ROWS][COLS] tile of ST (row stride ld elements; rows at or past rows_valid read as zero) moved to LDS as
+// float [ROWS][COLS + 1] through registers in 16-byte pieces: load() puts every piece of the thread in flight
+// at once, store() writes them to LDS, so a tile costs one load latency, and a chain can load the next
+// chunk's tiles while it computes on the current ones.
+template <typename ST, int ROWS, int COLS>
+struct Tile {
+    static constexpr int E = 16 / (int)sizeof(ST);
+    static constexpr int PPR = COLS / E;                     // pieces per row
+    static constexpr int PIECES = ROWS * PPR;
+    static constexpr int PER = (PIECES + NT - 1) / NT;
+    static_assert(COLS % E == 0, "tile rows are whole 16-byte pieces");
+    u128 r[PER];
+    __device__ __forceinline__ void load(const ST* __restrict__ base, long ld, int rows_valid) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
+            r[p] = u128{0u, 0u, 0u, 0u};
+            if (idx < PIECES && row < rows_valid) r[p] = *reinterpret_cast<const u128*>(base + row * ld + col);
+        }
+    }
+    __device__ __forceinline__ void store(float* dst) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
+            if (idx < PIECES)
+#pragma unroll
+                for (int e = 0; e < E; ++e) dst[row * (COLS + 1) + col + e] = Elem<ST>::to_f(unit_of<ST>(r[p], e));
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------------------------------------
 // Prep: per (chunk slot, head). G by a wave prefix sum, A and P from the raw products with the decay masks,
@@ -67,17 +99,25 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     constexpr int LK = KD + 1, LL = BC + 1;
     __shared__ float sK[BC * LK], sQ[BC * LK], sW[BC * LK];
     __shared__ float sA[BC * LL], sT[BC * LL], sP[BC * LL];
-    __shared__ float sG[BC], sB[BC];
+    __shared__ float sG[BC], sB[BC], sBG[BC];
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     int b, t0, L;
     if (!chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
     const long row0 = (long)b * T + t0;
-    load_rows<ST, KD>(k, row0, L, H, h, sK);
-    load_rows<ST, KD>(q, row0, L, H, h, sQ);
+    {
+        Tile<ST, BC, KD> tk, tq;
+        tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tk.store(sK);
+        tq.store(sQ);
+    }
     if (tid < BC) {
         const float gv = tid < L ? g[(row0 + tid) * H + h] : 0.f;
-        sB[tid] = tid < L ? beta[(row0 + tid) * H + h] : 0.f;
-        sG[tid] = wave_inclusive_scan(gv);
+        const float bv = tid < L ? beta[(row0 + tid) * H + h] : 0.f;
+        const float G = wave_inclusive_scan(gv);
+        sB[tid] = bv;
+        sG[tid] = G;
+        sBG[tid] = bv * expf(G);
     }
     __syncthreads();
     // A = diag(beta) (D_strict o K K^T) and P = scale (D o Q K^T)
@@ -111,7 +151,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     for (int m = 0; m < KD / 4; ++m) {
         const int c = (tid & 3) + 4 * m;
         float w = 0.f;
-        for (int s2 = 0; s2 <= t; ++s2) w += sT[t * LL + s2] * (sB[s2] * expf(sG[s2])) * sK[s2 * LK + c];
+        for (int s2 = 0; s2 <= t; ++s2) w += sT[t * LL + s2] * sBG[s2] * sK[s2 * LK + c];
         sW[t * LK + c] = w;
         R[RL::W_OFF + t * KD + c] = w;
     }
@@ -177,10 +217,22 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states_kernel(const ST* __restrict
         S[m] = h0 ? h0[(((size_t)n * H + h) * V + v0 + r) * KD + c] : 0.f;
     }
     const int t = tid >> 2, v4 = (tid & 3) * 4;
-    for (int ci = 0; ci < nch; ++ci) {
+    // chunk ci's K rows, T, coefficients and V slice, loaded one chunk ahead
+    Tile<ST, BC, KD> tk;
+    Tile<float, BC, BC> tt;
+    Tile<ST, BC, 16> tv;
+    float cf = 0.f;
+    auto issue = [&](int ci) __attribute__((always_inline)) {
         const long row0 = (long)b * T + bos + (long)ci * BC;
         const int L = min(BC, eos - (bos + ci * BC));
         const float* R = rec + ((size_t)(slot0 + ci) * H + h) * RL::FLOATS;
+        tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tt.load(R + RL::T_OFF, BC, BC);
+        tv.load(v + (row0 * H + h) * (long)V + v0, (long)H * V, L);
+        cf = R[RL::C_OFF + tid];
+    };
+    if (nch > 0) issue(0);
+    for (int ci = 0; ci < nch; ++ci) {
         float* Sout = states + (((size_t)(slot0 + ci) * H + h) * V + v0) * KD;
 #pragma unroll
         for (int m = 0; m < NE; ++m) {
@@ -188,14 +240,12 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states_kernel(const ST* __restrict
             Sout[(e / KD) * KD + e % KD] = S[m];
             sS[(e / KD) * LK + e % KD] = S[m];
         }
-        load_rows<ST, KD>(k, row0, L, H, h, sK);
-        for (int i = tid; i < BC * BC; i += NT) sT[(i / BC) * LL + i % BC] = R[RL::T_OFF + i];
-        sC[tid] = R[RL::C_OFF + tid];
-        for (int i = tid; i < BC * 16; i += NT) {
-            const int tt = i / 16, j = i % 16;
-            sV[tt * LV + j] = tt < L ? ld(v + ((row0 + tt) * H + h) * (long)V + v0 + j) : 0.f;
-        }
+        tk.store(sK);
+        tt.store(sT);
+        tv.store(sV);
+        sC[tid] = cf;
         __syncthreads();
+        if (ci + 1 < nch) issue(ci + 1);
         // Z = diag(beta) (V - diag(Gamma) K S^T) on (token t, values v4 .. v4 + 3)
         {
             float x[4] = {0.f, 0.f, 0.f, 0.f};
@@ -262,10 +312,23 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate_kernel(const ST* __restrict
         const int e = tid + NT * m;
         dS[m] = dht ? dht[(((size_t)n * H + h) * V + v0 + e / KD) * KD + e % KD] : 0.f;
     }
-    for (int ci = nch - 1; ci >= 0; --ci) {
+    // chunk ci's K rows, W, Qt, coefficients and dO slice, loaded one chunk ahead (chunks run backwards)
+    Tile<ST, BC, KD> tk;
+    Tile<float, BC, KD> tw, tq;
+    Tile<ST, BC, 16> to;
+    float cf = 0.f;
+    auto issue = [&](int ci) __attribute__((always_inline)) {
         const long row0 = (long)b * T + bos + (long)ci * BC;
         const int L = min(BC, eos - (bos + ci * BC));
         const float* R = rec + ((size_t)(slot0 + ci) * H + h) * RL::FLOATS;
+        tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tw.load(R + RL::W_OFF, KD, BC);
+        tq.load(R + RL::QT_OFF, KD, BC);
+        to.load(dout + (row0 * H + h) * (long)V + v0, (long)H * V, L);
+        cf = R[RL::C_OFF + tid];
+    };
+    if (nch > 0) issue(nch - 1);
+    for (int ci = nch - 1; ci >= 0; --ci) {
         float* Dout = dstates + (((size_t)(slot0 + ci) * H + h) * V + v0) * KD;
 #pragma unroll
         for (int m = 0; m < NE; ++m) {
@@ -273,17 +336,13 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate_kernel(const ST* __restrict
             Dout[(e / KD) * KD + e % KD] = dS[m];
             sD[(e / KD) * LK + e % KD] = dS[m];
         }
-        load_rows<ST, KD>(k, row0, L, H, h, sK);
-        for (int i = tid; i < BC * KD; i += NT) {
-            sW[(i / KD) * LK + i % KD] = R[RL::W_OFF + i];
-            sQt[(i / KD) * LK + i % KD] = R[RL::QT_OFF + i];
-        }
-        sC[tid] = R[RL::C_OFF + tid];
-        for (int i = tid; i < BC * 16; i += NT) {
-            const int tt = i / 16, j = i % 16;
-            sO[tt * LV + j] = tt < L ? ld(dout + ((row0 + tt) * H + h) * (long)V + v0 + j) : 0.f;
-        }
+        tk.store(sK);
+        tw.store(sW);
+        tq.store(sQt);
+        to.store(sO);
+        sC[tid] = cf;
         __syncthreads();
+        if (ci > 0) issue(ci - 1);
         // Z[r][t] = e_t (dS' K^T)[r][t]; thread: row r = tid / 16, tokens 4 (tid % 16) .. + 3
         {
             const int r = tid >> 4, t4 = (tid & 15) * 4;
@@ -351,10 +410,17 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
     if (!chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
     const long row0 = (long)b * T + t0;
     const float* Rc = rec + ((size_t)slot * H + h) * RL::FLOATS;
-    load_rows<ST, KD>(k, row0, L, H, h, sK);
-    load_rows<ST, KD>(q, row0, L, H, h, sQ);
-    for (int i = tid; i < BC * BC; i += NT) sT[(i / BC) * LL + i % BC] = Rc[RL::T_OFF + i];
-    sC[tid] = Rc[RL::C_OFF + tid];
+    {
+        Tile<ST, BC, KD> tk, tq;
+        Tile<float, BC, BC> tt;
+        tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tt.load(Rc + RL::T_OFF, BC, BC);
+        sC[tid] = Rc[RL::C_OFF + tid];
+        tk.store(sK);
+        tq.store(sQ);
+        tt.store(sT);
+    }
     __syncthreads();
     const int t = tid >> 2, q4 = tid & 3, v4 = 4 * q4;
     // raw Q K^T and K K^T on the thread's (t, s) entries
@@ -377,18 +443,22 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
     float pGam = 0.f, pE = 0.f, pB = 0.f, pGL = 0.f;  // partial sums of dGamma_t, de_t, dbeta_t, dGamma_L
     const int nvs = V / 16;
     __syncthreads();
+    // the slice's entry state, exit-state gradient and dO, loaded one slice ahead
+    Tile<float, 16, KD> ts, td;
+    Tile<ST, BC, 16> to;
+    auto issue = [&](int vs) __attribute__((always_inline)) {
+        const int v0 = 16 * vs;
+        ts.load(states + (((size_t)slot * H + h) * V + v0) * KD, KD, 16);
+        td.load(dstates + (((size_t)slot * H + h) * V + v0) * KD, KD, 16);
+        to.load(dout + (row0 * H + h) * (long)V + v0, (long)H * V, L);
+    };
+    issue(0);
     for (int vs = 0; vs < nvs; ++vs) {
         const int v0 = 16 * vs;
-        const float* Sg = states + (((size_t)slot * H + h) * V + v0) * KD;
-        const float* Dg = dstates + (((size_t)slot * H + h) * V + v0) * KD;
-        for (int i = tid; i < 16 * KD; i += NT) {
-            sS[(i / KD) * LK + i % KD] = Sg[i];
-            sD[(i / KD) * LK + i % KD] = Dg[i];
-        }
-        for (int i = tid; i < BC * 16; i += NT) {
-            const int tt = i / 16, j = i % 16;
-            sO[tt * LV + j] = tt < L ? ld(dout + ((row0 + tt) * H + h) * (long)V + v0 + j) : 0.f;
-        }
+        ts.store(sS);
+        td.store(sD);
+        to.store(sO);
+        if (vs + 1 < nvs) issue(vs + 1);
         float vv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) vv[j] = t < L ? ld(v + ((row0 + t) * H + h) * (long)V + v0 + v4 + j) : 0.f;

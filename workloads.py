@@ -47,7 +47,7 @@ import torch
 
 SEEDS = {"tiny_gdn": 101, "dense_gdn": 102, "varlen_gdn": 103, "long_gdn": 104, "ssd_gla": 105,
          "decode_gdn": 106, "recurrent_gdn": 107, "gate_transform": 108,
-         "paged_gdn": 109, "recurrent_kda": 110, "decode_kda": 111}
+         "paged_gdn": 109, "recurrent_kda": 110, "decode_kda": 111, "dense_gdn_bwd": 112}
 
 
 @dataclass
@@ -204,6 +204,16 @@ def dense_gdn(seed=SEEDS["dense_gdn"], *, B=2, T=4096, H=16, D=128):
                           gate_shift=2.0, h0_std=0.02)
     return Workload("dense_gdn", "gdn", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], None,
                     scale=1.0 / np.sqrt(D), chunk=64)
+
+
+def dense_gdn_bwd(seed=SEEDS["dense_gdn_bwd"], *, B=2, T=4096, H=16, D=128):
+    """The dense prefill inputs (dense_gdn's generator and seed) and, for the backward, upstream gradients
+    do ~ N(0,1) (bf16) and dht ~ N(0,1) (float32) drawn with this seed."""
+    w = dense_gdn(B=B, T=T, H=H, D=D)
+    u = upstream_grads(np.random.default_rng(seed), B=B, T=T, H=H, V=D, K=D, N=B)
+    w.name = "dense_gdn_bwd"
+    w.meta.update(do=u["do"], dht=u["dht"])
+    return w
 
 
 def varlen_gdn(seed=SEEDS["varlen_gdn"], *, T=32768, H=32, D=128, n_long=7):
@@ -402,7 +412,8 @@ def gate_transform(seed=SEEDS["gate_transform"], *, B=2, T=16384, H=16, D=128):
 CONFIGS = {"tiny_gdn": tiny_gdn, "dense_gdn": dense_gdn, "varlen_gdn": varlen_gdn,
            "long_gdn": long_gdn, "ssd_gla": ssd_gla, "decode_gdn": decode_gdn,
            "recurrent_gdn": recurrent_gdn, "gate_transform": gate_transform,
-           "paged_gdn": paged_gdn, "recurrent_kda": recurrent_kda, "decode_kda": decode_kda}
+           "paged_gdn": paged_gdn, "recurrent_kda": recurrent_kda, "decode_kda": decode_kda,
+           "dense_gdn_bwd": dense_gdn_bwd}
 
 
 def to_f32(t):
