@@ -23,7 +23,7 @@ carry measured_peak: the bandwidth a plain 1 GiB device-to-device copy reaches
 on the same GPU (read plus write bytes), and the fraction of that.
 
 Other workloads (--workload varlen_gdn | long_gdn | ssd_gla | tiny_gdn | decode_gdn | recurrent_gdn |
-gate_transform | paged_gdn | recurrent_kda | decode_kda | dense_gdn_bwd) are for
+gate_transform | paged_gdn | recurrent_kda | decode_kda | dense_gdn_bwd | dense_kda) are for
 measurement only; the headline line is the default one. decode_gdn times one sf_gdn_decode call
 (one token for each of 256 sequences against a 514 MB float32 state pool, which is larger than
 the last-level cache, so it runs on one input set).
@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GDN chunk-fwd tokens/s (bf16, K=V=128) + % of MFMA/HBM roofline, 1 MI355X"
 METRIC_BWD = "GDN chunk-bwd tokens/s (bf16, K=V=128) + % of HBM roofline, 1 MI355X"
+METRIC_KDA = "KDA chunk-fwd tokens/s (bf16, K=V=128) + % of HBM roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 
@@ -82,8 +83,14 @@ def algorithmic_bytes(w, kernel):
     vo = 2 * tok * w.H * w.V * eb
     gb = tok * w.H * 4 * (2 if w.beta is not None else 1)
     states = w.N * w.H * w.V * w.K * 4 * (1 + (w.h0 is not None))
-    if w.name == "recurrent_kda":   # per-channel gate: K floats per token and head
+    if w.name in ("recurrent_kda", "dense_kda"):   # per-channel gate: K floats per token and head
         gb = tok * w.H * 4 * (w.K + 1)
+    if w.name == "dense_kda":
+        # kda_prep reads q, k, v, g, beta; kda_chain reads h0 and writes o and ht
+        if kernel == "kda_prep":
+            return qk + vo // 2 + gb
+        if kernel == "kda_chain":
+            return vo // 2 + states
     if w.name in ("recurrent_gdn", "paged_gdn", "recurrent_kda"):   # every slot read and written (float32 pool)
         states = 2 * w.N * w.H * w.V * w.K * w.meta["pool"].element_size()
         return qk + vo + states + (0 if kernel in ("gdn_chain", "gdn_chain_slice") else gb)
@@ -221,6 +228,10 @@ def step_fn(w):
         def step(s):
             return sf.gdn_chunk_bwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["do"], s["h0"], s["dht"],
                                     scale=w.scale)
+    elif w.name == "dense_kda":
+        def step(s):
+            return sf.kda_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["h0"], scale=w.scale,
+                                    output_final_state=True)
     elif w.name in ("dense_gdn", "tiny_gdn", "varlen_gdn"):
         def step(s):
             return sf.gdn_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["h0"], cu_seqlens=s["cu_seqlens"],
@@ -283,6 +294,15 @@ def cpu_baseline(w):
                 "cpu_model": model,
                 "sample": f"the whole {w.name} workload ({w.tokens} tokens x {w.H} heads), one float64 pass of the "
                           f"reverse-mode token loop, {dt:.2f} s wall"}
+    if w.name == "dense_kda":
+        log("cpu_baseline: float64 KDA oracle (numpy token loop) ...")
+        t0 = time.perf_counter()
+        oracle.kda_forward(f(w.q), f(w.k), f(w.v), f(w.g), f(w.beta), f(w.h0), scale=w.scale)
+        dt = time.perf_counter() - t0
+        return {"value": w.tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle", "precision": "f64",
+                "cpu_model": model,
+                "sample": f"the whole {w.name} workload ({w.tokens} tokens x {w.H} heads), one float64 pass of the "
+                          f"numpy token loop, {dt:.2f} s wall"}
     if w.name in ("recurrent_kda", "recurrent_gdn", "paged_gdn"):
         args = dict(q=f(w.q), k=f(w.k), v=f(w.v), g=f(w.g))
         log(f"cpu_baseline: float64 oracle on {threads} threads ...")
@@ -361,7 +381,7 @@ def main():
     ap.add_argument("--workload", default="dense_gdn",
                     choices=["dense_gdn", "tiny_gdn", "varlen_gdn", "long_gdn", "ssd_gla", "decode_gdn",
                              "recurrent_gdn", "gate_transform", "paged_gdn", "recurrent_kda", "decode_kda",
-                             "dense_gdn_bwd"])
+                             "dense_gdn_bwd", "dense_kda"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true",
                     help="skip the second pass, whose launches are bracketed with HIP events")
@@ -457,7 +477,7 @@ def main():
         roof["frac_of_measured"] = round(roof["achieved"] / copy_gbs, 4)
 
     out = {
-        "metric": METRIC_BWD if w.name == "dense_gdn_bwd" else METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": {"dense_gdn_bwd": METRIC_BWD, "dense_kda": METRIC_KDA}.get(w.name, METRIC), "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "p50_ms": p50_ms, "min_ms": min_ms,
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,

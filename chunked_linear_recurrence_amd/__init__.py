@@ -31,6 +31,8 @@ Functions (same names as the C entry points, without the ``sf_`` prefix):
                         "Linear Attention", paged_chunk_gdn).
 * ``gdn_chunk_fwd_raw_gate`` gdn_chunk_fwd with the gate transform fused into its
                         Pre stage (raw gate projection in, no separate kernel).
+* ``kda_chunk_fwd``     Kimi Delta Attention forward in 64-token chunks
+                        (attention-gym "Linear Attention", chunk_kda).
 * ``kda_recurrent_fwd`` Kimi Delta Attention token by token (per-channel gate),
                         optionally on a paged state pool.
 * ``kda_decode``        one-token paged KDA decode (recurrent_kda_decode).
@@ -64,6 +66,7 @@ EXPORTED = (
     "sf_kda_recurrent_fwd", "sf_kda_decode",
     "sf_timing_enable", "sf_timing_collect", "sf_check_cu_seqlens", "sf_check_state_indices",
     "sf_gdn_chunk_fwd_noalloc", "sf_static_scratch_bytes", "sf_gdn_chunk_bwd_workspace", "sf_gdn_chunk_bwd",
+    "sf_kda_chunk_fwd_workspace", "sf_kda_chunk_fwd",
 )
 
 
@@ -128,6 +131,10 @@ def lib() -> ctypes.CDLL:
     L.sf_gdn_chunk_fwd_noalloc.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P]
     L.sf_static_scratch_bytes.restype = Z
     L.sf_static_scratch_bytes.argtypes = []
+    L.sf_kda_chunk_fwd_workspace.restype = Z
+    L.sf_kda_chunk_fwd_workspace.argtypes = [I, I, I, I, I, I, I, I]
+    L.sf_kda_chunk_fwd.restype = I
+    L.sf_kda_chunk_fwd.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, P]
     L.sf_gdn_chunk_bwd_workspace.restype = Z
     L.sf_gdn_chunk_bwd_workspace.argtypes = [I, I, I, I, I, I, I, I]
     L.sf_gdn_chunk_bwd.restype = I
@@ -285,6 +292,45 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, initial_state=None, dht=None, *, cu_seql
                                   _ptr(dht), _ptr(cu_seqlens), N, B, T, H, HK, K, V, float(scale), _ptr(dq), _ptr(dk),
                                   _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(ws), nbytes, _stream()))
     return dq, dk, dv, dg, dbeta, dh0
+
+
+def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, cu_seqlens=None, scale=None, output_final_state=False):
+    """Kimi Delta Attention chunk forward: q, k, g [B,T,H,K] (g float32, per-channel natural-log decay),
+    v [B,T,H,V], beta [B,T,H] float32, initial_state [N,H,V,K] float32. Returns (output [B,T,H,V] in q.dtype,
+    final state or None). Output rows at or past cu_seqlens[-1] are left uninitialised."""
+    _need(q, "q", ndim=4)
+    dev = q.device
+    _need(k, "k", dtype=q.dtype, ndim=4, device=dev)
+    _need(v, "v", dtype=q.dtype, ndim=4, device=dev)
+    _need(g, "g", dtype=torch.float32, ndim=4, device=dev)
+    _need(beta, "beta", dtype=torch.float32, ndim=3, device=dev)
+    B, T, H, K = q.shape
+    V = v.shape[3]
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} g {tuple(g.shape)} v {tuple(v.shape)} "
+                         f"beta {tuple(beta.shape)}")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=1, device=dev)
+        N = cu_seqlens.numel() - 1
+        if _validating():
+            validate_cu_seqlens(cu_seqlens, T)
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", dtype=torch.float32, ndim=4, device=dev)
+        if tuple(initial_state.shape) != (N, H, V, K):
+            raise ValueError(f"initial_state must be [{N}, {H}, {V}, {K}], got {tuple(initial_state.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    out = torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+    ht = torch.empty((N, H, V, K), dtype=torch.float32, device=dev) if output_final_state else None
+    dt = _dt(q)
+    nbytes = lib().sf_kda_chunk_fwd_workspace(dt, B, T, H, K, V, N, int(cu_seqlens is not None))
+    ws = _workspace(nbytes, dev)
+    _check(lib().sf_kda_chunk_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                  _ptr(cu_seqlens), N, B, T, H, K, V, float(scale), _ptr(out), _ptr(ht), _ptr(ws),
+                                  nbytes, _stream()))
+    return out, ht
 
 
 def gdn_chunk_fwd_raw_gate(q, k, v, raw_gate, A_log, dt_bias, beta, initial_state=None, *, kind,

@@ -192,6 +192,39 @@ sf_status sf_gdn_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void
 }
 
 // ---------------------------------------------------------------------------
+// KDA chunk forward
+// ---------------------------------------------------------------------------
+size_t sf_kda_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N, int packed) {
+    if ((dt != SF_F32 && dt != SF_BF16) || B < 0 || T < 0 || H <= 0 || N < 0) return 0;
+    if (!((K == 128 && (V == 128 || V == 64)) || (K == 64 && V == 64))) return 0;
+    return sf::kda_workspace_layout(nullptr, B, T, H, K, V, N, packed != 0).bytes;
+}
+
+sf_status sf_kda_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* h0, const int32_t* cu_seqlens, int N, int B, int T,
+                           int H, int K, int V, float scale, void* out, float* ht, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    sf_status st = check_tokens(dt, B, T, H, H, K, V, N, packed);
+    if (st != SF_OK) return st;
+    if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
+    if (!((K == 128 && (V == 128 || V == 64)) || (K == 64 && V == 64)))
+        return fail(SF_ERR_UNSUPPORTED, "the KDA chunk forward is built for (K, V) in {(128, 128), (128, 64), (64, 64)} "
+                    "(K=%d V=%d)", K, V);
+    if (!fits((long)B * T * H * K)) return fail(SF_ERR_UNSUPPORTED, "the gate has 2^31 or more elements");
+    if (H > 65535) return fail(SF_ERR_UNSUPPORTED, "H=%d is past the 65535 heads of a launch", H);
+    const sf::KdaWorkspace need = sf::kda_workspace_layout(nullptr, B, T, H, K, V, N, packed);
+    if (!workspace || workspace_bytes < need.bytes)
+        return fail(SF_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                    need.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(SF_ERR_INVALID, "workspace must be 256-byte aligned");
+    const sf::KdaWorkspace ws = sf::kda_workspace_layout(workspace, B, T, H, K, V, N, packed);
+    hipError_t e = sf::launch_kda_chunk(dt == SF_BF16, q, k, v, g, beta, h0, cu_seqlens, ws, N, B, T, H, K, V, scale,
+                                        out, ht, static_cast<hipStream_t>(stream));
+    return hip_status(e, "sf_kda_chunk_fwd launch");
+}
+
+// ---------------------------------------------------------------------------
 // Chunk backward
 // ---------------------------------------------------------------------------
 size_t sf_gdn_chunk_bwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N, int packed) {

@@ -114,6 +114,32 @@ inline GdnBwdWorkspace gdn_bwd_workspace_layout(void* base, int B, int T, int H,
     return w;
 }
 
+// Workspace of the KDA chunk forward: the chunk table of packed inputs and one float32 record per (chunk
+// slot, head) (W, U, P, Qg, Kh, Gamma_L; kda_record_floats floats).
+struct KdaWorkspace {
+    int* chunk_off;
+    int2* table;
+    float* rec;
+    size_t bytes;
+};
+size_t kda_record_floats(int K, int V);
+inline KdaWorkspace kda_workspace_layout(void* base, int B, int T, int H, int K, int V, int N, bool packed) {
+    KdaWorkspace w{};
+    size_t off = 0;
+    uint8_t* p = static_cast<uint8_t*>(base);
+    const long slots = gdn_slots(B, T, N, packed);
+    if (packed) {
+        w.chunk_off = reinterpret_cast<int*>(p ? p + off : nullptr);
+        off += align256(sizeof(int) * (size_t)(N + 1));
+        w.table = reinterpret_cast<int2*>(p ? p + off : nullptr);
+        off += align256(sizeof(int2) * (size_t)slots);
+    }
+    w.rec = reinterpret_cast<float*>(p ? p + off : nullptr);
+    off += align256(sizeof(float) * kda_record_floats(K, V) * (size_t)slots * H);
+    w.bytes = off;
+    return w;
+}
+
 // Raw gate projection read by the delta-rule Pre stage in place of g (the gate transform fused
 // into its gate load): g = -exp(A_log[h]) softplus(raw + dt_bias[h]) or, bounded,
 // lower_bound sigmoid(exp(A_log[h]) (raw + dt_bias[h])). raw == nullptr: read g as given.
@@ -151,6 +177,12 @@ hipError_t launch_gdn_bwd(bool bf16, const void* q, const void* k, const void* v
                           const int32_t* cu, const GdnBwdWorkspace& ws, int N, int B, int T, int H, int K,
                           int V, float scale, void* dq, void* dk, void* dv, float* dg, float* dbeta,
                           float* dh0, hipStream_t s);
+
+// KDA chunk forward (kda.hip): q, k, g [B, T, H, K], v and out [B, T, H, V] (g float32), beta [B, T, H].
+// (K, V) in {(128, 128), (128, 64), (64, 64)}.
+hipError_t launch_kda_chunk(bool bf16, const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const float* h0, const int32_t* cu, const KdaWorkspace& ws, int N,
+                            int B, int T, int H, int K, int V, float scale, void* out, float* ht, hipStream_t s);
 
 // Paged state cache around the chunk path (paging.hip). block = H*V*K elements per slot.
 hipError_t launch_state_gather(bool pool_bf16, const void* pool, long long slot_stride, int num_slots, const int32_t* idx,

@@ -110,6 +110,35 @@ sf_status sf_gdn_chunk_fwd(sf_dtype dt, const void *q, const void *k, const void
                            int K, int V, float scale, void *out, float *ht,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace bytes needed by sf_kda_chunk_fwd (packed != 0 when cu_seqlens is
+ * passed): one float32 record per (64-token chunk, head) with the chunk's WY
+ * factors W = T diag(beta) (Gamma o K) and U = T diag(beta) V, the decayed
+ * query-key block P, the decayed queries and keys and the chunk's total decay,
+ * and the device chunk table of packed inputs. 0 for invalid or unsupported
+ * sizes. */
+size_t sf_kda_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V, int N,
+                                  int packed);
+
+/*
+ * Kimi Delta Attention chunk forward (attention-gym "Linear Attention",
+ * section "Kimi Delta Attention", chunk_kda with 64-token chunks): the delta
+ * rule whose state decays key channel by key channel, with g the per-token,
+ * per-channel natural-log decay (finite and <= 0, a caller responsibility),
+ * as sf_kda_recurrent_fwd computes token by token.
+ *   q, k, g [B, T, H, K] (g float32);  v [B, T, H, V];  beta [B, T, H] float32
+ *   h0, cu_seqlens, N, scale, out, ht as sf_gdn_chunk_fwd (no grouped heads)
+ *   workspace  at least sf_kda_chunk_fwd_workspace(...) bytes, 256-byte aligned
+ * The within-chunk decay between two tokens is applied per pair and channel,
+ * so the chunk form is exact for any nonpositive gate (no lower bound is
+ * assumed). float32 arithmetic. Supported: (K, V) in {(128, 128), (128, 64),
+ * (64, 64)}; others return SF_ERR_UNSUPPORTED.
+ */
+sf_status sf_kda_chunk_fwd(sf_dtype dt, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const float *h0,
+                           const int32_t *cu_seqlens, int N, int B, int T, int H, int K, int V,
+                           float scale, void *out, float *ht, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Workspace bytes needed by sf_gdn_chunk_bwd for these sizes (packed != 0 when
  * cu_seqlens is passed). It holds, in float32, one record per (64-token chunk,
  * head) with the chunk's solve factor T, its WY factor W = T diag(beta Gamma) K,

@@ -332,3 +332,36 @@ def test_bwd_rejects_invalid_arguments(L, kw, status, msg):
     st, err = bwd_call(L, **kw)
     assert st == status, err
     assert msg in err
+
+
+def test_kda_chunk_workspace_size(L):
+    B, T, H, K, V = 2, 4096, 16, 128, 128
+    slots = B * (T // 64)
+    rec = 4 * (3 * 64 * K + 64 * V + 64 * 64 + K)   # W, Qg, Kh [64][K]; U [64][V]; P [64][64]; Gamma_L [K]
+    al = lambda x: (x + 255) // 256 * 256
+    assert L.sf_kda_chunk_fwd_workspace(sf.SF_BF16, B, T, H, K, V, B, 0) == al(slots * H * rec)
+    assert L.sf_kda_chunk_fwd_workspace(sf.SF_BF16, B, T, H, 64, 128, B, 0) == 0
+
+
+def kda_call(L, **kw):
+    a = dict(dt=sf.SF_BF16, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, N=1, B=1, T=128, H=4,
+             K=128, V=128, scale=ctypes.c_float(0.1), out=FAKE, ht=None, ws=FAKE * 256, wsb=1 << 40, s=None)
+    a.update(kw)
+    st = L.sf_kda_chunk_fwd(a["dt"], a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"], a["N"], a["B"],
+                            a["T"], a["H"], a["K"], a["V"], a["scale"], a["out"], a["ht"], a["ws"], a["wsb"], a["s"])
+    return st, L.sf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(K=64, V=128), sf.SF_ERR_UNSUPPORTED, "(K, V)"),
+    (dict(K=96, V=96), sf.SF_ERR_UNSUPPORTED, "(K, V)"),
+    (dict(g=None), sf.SF_ERR_INVALID, "NULL"),
+    (dict(out=None), sf.SF_ERR_INVALID, "NULL"),
+    (dict(wsb=16), sf.SF_ERR_WORKSPACE, "smaller"),
+    (dict(ws=FAKE * 256 + 8), sf.SF_ERR_INVALID, "aligned"),
+    (dict(cu=FAKE, B=2, N=2), sf.SF_ERR_INVALID, "batch-one"),
+])
+def test_kda_chunk_rejects_invalid_arguments(L, kw, status, msg):
+    st, err = kda_call(L, **kw)
+    assert st == status, err
+    assert msg in err

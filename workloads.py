@@ -47,7 +47,7 @@ import torch
 
 SEEDS = {"tiny_gdn": 101, "dense_gdn": 102, "varlen_gdn": 103, "long_gdn": 104, "ssd_gla": 105,
          "decode_gdn": 106, "recurrent_gdn": 107, "gate_transform": 108,
-         "paged_gdn": 109, "recurrent_kda": 110, "decode_kda": 111, "dense_gdn_bwd": 112}
+         "paged_gdn": 109, "recurrent_kda": 110, "decode_kda": 111, "dense_gdn_bwd": 112, "dense_kda": 113}
 
 
 @dataclass
@@ -254,6 +254,15 @@ def kda_inputs(*, B, T, H, K, V, dtype=torch.bfloat16, seed=0, gate_shift=2.0, h
                 beta=torch.from_numpy(beta), h0=h0, rng=rng)
 
 
+def dense_kda(seed=SEEDS["dense_kda"], *, B=2, T=4096, H=16, D=128):
+    """KDA chunk prefill at the dense prefill shape: q, k (unit rows), v ~ N(0,1) bf16; per-channel
+    g = -softplus(N(0,1) + 2) float32 [B, T, H, D]; beta = sigmoid(N(0,1)); initial state N(0, 0.02);
+    scale 1/sqrt(D)."""
+    d = kda_inputs(B=B, T=T, H=H, K=D, V=D, seed=seed, h0_std=0.02)
+    return Workload("dense_kda", "kda", d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], None,
+                    scale=1.0 / np.sqrt(D), chunk=64)
+
+
 def recurrent_kda(seed=SEEDS["recurrent_kda"], *, B=64, T=16, H=32, D=128):
     """recurrent_gdn's shapes and pool with a per-channel gate (a reading, as there)."""
     d = kda_inputs(B=B, T=T, H=H, K=D, V=D, seed=seed)
@@ -413,7 +422,7 @@ CONFIGS = {"tiny_gdn": tiny_gdn, "dense_gdn": dense_gdn, "varlen_gdn": varlen_gd
            "long_gdn": long_gdn, "ssd_gla": ssd_gla, "decode_gdn": decode_gdn,
            "recurrent_gdn": recurrent_gdn, "gate_transform": gate_transform,
            "paged_gdn": paged_gdn, "recurrent_kda": recurrent_kda, "decode_kda": decode_kda,
-           "dense_gdn_bwd": dense_gdn_bwd}
+           "dense_gdn_bwd": dense_gdn_bwd, "dense_kda": dense_kda}
 
 
 def to_f32(t):
