@@ -373,10 +373,9 @@ sf_status sf_gdn_recurrent_fwd(sf_dtype dt, const void *q, const void *k, const 
 
 /*
  * Kimi Delta Attention, token by token (attention-gym "Linear Attention",
- * section "Kimi Delta Attention": the per-channel gate; at each token the
- * previous state is multiplied channelwise by exp(g), then the delta rule's
- * correction and update and the read with q): decayed = S diag(exp(g_t)),
- * r = beta_t (v_t - decayed k_t), S = decayed + r k_t^T, o_t = scale S q_t.
+ * section "Kimi Delta Attention"), with a per-channel gate g_t in R^K:
+ * decayed = S diag(exp(g_t)), r = beta_t (v_t - decayed k_t),
+ * S = decayed + r k_t^T, o_t = scale S q_t.
  * Arguments, state modes and errors as sf_gdn_recurrent_fwd, except:
  *   q, k, g [B, T, H, K] (no grouped heads; g float32, 16-byte aligned).
  */

@@ -153,8 +153,8 @@ def gate_transform(raw, A_log, dt_bias, kind, lower_bound=None):
 
 def kda_forward(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None):
     """Kimi Delta Attention, token by token (attention-gym "Linear Attention", section "Kimi Delta
-    Attention": per-channel gate; at each token the previous state is multiplied channelwise by
-    exp(gate), then the delta rule's correction and update, then the read with q), float64.
+    Attention"), float64, with a per-channel gate g_t in R^K: D = S diag(exp(g_t)),
+    r = beta_t (v_t - D k_t), S = D + r k_t^T, o_t = scale S q_t.
     q, k, g [B, T, H, K]; v [B, T, H, V]; beta [B, T, H]; h0 [N, H, V, K] or None.
     Returns (out [B, T, H, V], ht [N, H, V, K]); rows outside every sequence are NaN."""
     q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
