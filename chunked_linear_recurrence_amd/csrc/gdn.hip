@@ -941,7 +941,7 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
             barrier();
             for (int c = 0; c < nch; ++c) {
                 lds_u8* B = buf(c);
-                form_p<KD, 2>(B + SM::OFF_K, B + SM::OFF_Q, (const lds_f32*)(B + SM::OFF_C), scale, B + SM::OFF_P);
+                form_p<KD, 0xF>(B + SM::OFF_K, B + SM::OFF_Q, (const lds_f32*)(B + SM::OFF_C), scale, B + SM::OFF_P);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 barrier();  // P_c complete
                 barrier();  // end of the step
@@ -1189,9 +1189,9 @@ __global__ __launch_bounds__(704) void gdn_chain_slice_kernel(
         for (int s = -2; s <= nch; ++s) {
             if (s >= 0 && s < nch) {
                 if (wave == 5)
-                    form_p<KD, 0>(kbuf(s), qbuf(s), cbuf(s), scale, pbuf(s));
+                    form_p<KD, 0x9>(kbuf(s), qbuf(s), cbuf(s), scale, pbuf(s));
                 else
-                    form_p<KD, 1>(kbuf(s), qbuf(s), cbuf(s), scale, pbuf(s));
+                    form_p<KD, 0x6>(kbuf(s), qbuf(s), cbuf(s), scale, pbuf(s));
                 wave_lds_sync();
             }
             barrier();

@@ -87,8 +87,26 @@ struct Tile {
 };
 
 // ---------------------------------------------------------------------------------------------------------
-// Prep: per (chunk slot, head). G by a wave prefix sum, A and P from the raw products with the decay masks,
-// T by forward substitution (one column per thread), then W and Qt.
+// Float32 MFMA tile over LDS operands: acc += A(i, k) B(k, j) for one 16x16 tile, k in [k0, k1) (a multiple of 4
+// apart), with A(i, k) = A[i * ars + k * acs] and B(k, j) = B[k * brs + j * bcs] (pointers at the tile origin;
+// the strides give transposed reads for free). Lane (ln, lg) brings A(ln, k + lg) times as (the scale of its A
+// row) and B(k + lg, ln); the C tile holds rows 4 lg + r, column ln (v_mfma_f32_16x16x4_f32).
+// ---------------------------------------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mm4(const float* A, int ars, int acs, const float* B, int brs, int bcs, int k0, int k1,
+                                     f32x4 acc, float as = 1.f) {
+    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
+    const float* a = A + ln * ars + lg * acs;
+    const float* b = B + lg * brs + ln * bcs;
+    for (int kk = k0; kk < k1; kk += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as * a[kk * acs], b[kk * brs], acc, 0, 0, 0);
+    return acc;
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// Prep: per (chunk slot, head), on float32 MFMA tiles (wavefront w owns token rows 16 w .. 16 w + 15). G by a wave
+// prefix sum; A and P from the raw products with the decay masks; T by 16x16 blocks (the four diagonal blocks by
+// column substitution, one wavefront each, then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj block diagonal by block
+// diagonal); then W = T diag(beta Gamma) K and Qt = scale Gamma Q - P W.
 // ---------------------------------------------------------------------------------------------------------
 template <typename ST, int KD>
 __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__ q, const ST* __restrict__ k,
@@ -96,10 +114,10 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
                                                           const int2* __restrict__ table, const int32_t* __restrict__ cu,
                                                           int T, int H, int nc, float scale, float* __restrict__ rec) {
     typedef BwdRec<KD> RL;
-    constexpr int LK = KD + 1, LL = BC + 1;
+    constexpr int LK = KD + 1, LL = BC + 1, LU = 17, NJ = KD / 16;
     __shared__ float sK[BC * LK], sQ[BC * LK], sW[BC * LK];
     __shared__ float sA[BC * LL], sT[BC * LL], sP[BC * LL];
-    __shared__ float sG[BC], sB[BC], sBG[BC];
+    __shared__ float sG[BC], sB[BC], sU[4 * 16 * LU];
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     int b, t0, L;
     if (!chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
@@ -113,56 +131,86 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     }
     if (tid < BC) {
         const float gv = tid < L ? g[(row0 + tid) * H + h] : 0.f;
-        const float bv = tid < L ? beta[(row0 + tid) * H + h] : 0.f;
-        const float G = wave_inclusive_scan(gv);
-        sB[tid] = bv;
-        sG[tid] = G;
-        sBG[tid] = bv * expf(G);
+        sB[tid] = tid < L ? beta[(row0 + tid) * H + h] : 0.f;
+        sG[tid] = wave_inclusive_scan(gv);
     }
     __syncthreads();
-    // A = diag(beta) (D_strict o K K^T) and P = scale (D o Q K^T)
-    for (int i = tid; i < BC * BC; i += NT) {
-        const int t = i / BC, s = i % BC;
-        float kk = 0.f, qk = 0.f;
-        if (s <= t)
-            for (int c = 0; c < KD; ++c) {
-                kk += sK[t * LK + c] * sK[s * LK + c];
-                qk += sQ[t * LK + c] * sK[s * LK + c];
-            }
-        const float d = s <= t ? expf(sG[t] - sG[s]) : 0.f;
-        sA[t * LL + s] = s < t ? sB[t] * d * kk : 0.f;
-        sP[t * LL + s] = scale * d * qk;
-    }
-    __syncthreads();
-    if (tid < BC) {
-        // column j = tid of T = (I + A)^-1 (unit lower triangular): x_j = 1, x_t = -sum_{j<=s<t} A_ts x_s
-        const int j = tid;
-        for (int t = 0; t < BC; ++t) {
-            float x = t == j ? 1.f : 0.f;
-            if (t > j)
-                for (int s2 = j; s2 < t; ++s2) x -= sA[t * LL + s2] * sT[s2 * LL + j];
-            sT[t * LL + j] = x;
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    int tr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tr[r] = 16 * w + 4 * lg + r;
+    // A = diag(beta) (D_strict o K K^T) and P = scale (D o Q K^T) on the wavefront's row tile
+    for (int j = 0; j < 4; ++j) {
+        f32x4 kk = zero4(), qk = zero4();
+        if (j <= w) {
+            kk = mm4(sK + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, kk);
+            qk = mm4(sQ + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, qk);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = tr[r], s2 = 16 * j + ln;
+            const float d = s2 <= t ? expf(sG[t] - sG[s2]) : 0.f;
+            sA[t * LL + s2] = s2 < t ? sB[t] * d * kk[r] : 0.f;
+            sP[t * LL + s2] = scale * d * qk[r];
+            sT[t * LL + s2] = 0.f;
         }
     }
     __syncthreads();
-    float* R = rec + ((size_t)slot * H + h) * RL::FLOATS;
-    // W[t][c] = sum_{s<=t} T[t][s] beta_s Gamma_s K[s][c]; thread owns row t = tid / 4, columns tid % 4 + 4 m
-    const int t = tid >> 2;
-    for (int m = 0; m < KD / 4; ++m) {
-        const int c = (tid & 3) + 4 * m;
-        float w = 0.f;
-        for (int s2 = 0; s2 <= t; ++s2) w += sT[t * LL + s2] * sBG[s2] * sK[s2 * LK + c];
-        sW[t * LK + c] = w;
-        R[RL::W_OFF + t * KD + c] = w;
+    // diagonal blocks: wavefront w inverts block w, lane j < 16 solving column j: x_j = 1,
+    // x_i = -sum_{j<=s<i} A_ii[i][s] x_s
+    if (lane < 16) {
+        const int o = 16 * w, j = lane;
+        for (int i = 0; i < 16; ++i) {
+            float x = i == j ? 1.f : 0.f;
+            if (i > j)
+                for (int s2 = j; s2 < i; ++s2) x -= sA[(o + i) * LL + o + s2] * sT[(o + s2) * LL + o + j];
+            sT[(o + i) * LL + o + j] = x;
+        }
+    }
+    // (K scaled by beta Gamma per token, for W: K is not read again as itself)
+    for (int i = tid; i < BC * KD; i += NT) {
+        const int t = i / KD, c = i % KD;
+        sK[t * LK + c] *= sB[t] * expf(sG[t]);
     }
     __syncthreads();
-    // Qt[t][c] = scale Gamma_t Q[t][c] - sum_{s<=t} P[t][s] W[s][c]
-    const float gq = scale * expf(sG[t]);
-    for (int m = 0; m < KD / 4; ++m) {
-        const int c = (tid & 3) + 4 * m;
-        float acc = 0.f;
-        for (int s2 = 0; s2 <= t; ++s2) acc += sP[t * LL + s2] * sW[s2 * LK + c];
-        R[RL::QT_OFF + t * KD + c] = gq * sQ[t * LK + c] - acc;
+    // off-diagonal blocks, one block diagonal dd at a time: block (i, j = i - dd) by wavefront i
+    for (int dd = 1; dd < 4; ++dd) {
+        const int i = w, j = w - dd;
+        if (j >= 0) {
+            // U = sum_{kb=j}^{i-1} A_i,kb T_kb,j (16 x 16, k over the tokens of blocks j .. i-1)
+            const f32x4 Uv = mm4(sA + 16 * i * LL + 16 * j, LL, 1, sT + 16 * j * LL + 16 * j, LL, 1, 0, 16 * (i - j), zero4());
+            float* Ub = sU + w * 16 * LU;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ub[(4 * lg + r) * LU + ln] = Uv[r];
+            // T_ij = -T_ii U (same wavefront: its own LDS writes precede its reads)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the U tile is in LDS
+            const f32x4 Tv = mm4(sT + 16 * i * LL + 16 * i, LL, 1, Ub, LU, 1, 0, 16, zero4());
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sT[(16 * i + 4 * lg + r) * LL + 16 * j + ln] = -Tv[r];
+        }
+        __syncthreads();
+    }
+    float* R = rec + ((size_t)slot * H + h) * RL::FLOATS;
+    // W = T (beta Gamma K) on the wavefront's row tile (T is zero past column 16 w + 15)
+#pragma unroll
+    for (int jc = 0; jc < NJ; ++jc) {
+        const f32x4 Wv = mm4(sT + 16 * w * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sW[tr[r] * LK + 16 * jc + ln] = Wv[r];
+            R[RL::W_OFF + tr[r] * KD + 16 * jc + ln] = Wv[r];
+        }
+    }
+    __syncthreads();
+    // Qt = scale Gamma Q - P W
+#pragma unroll
+    for (int jc = 0; jc < NJ; ++jc) {
+        const f32x4 PW = mm4(sP + 16 * w * LL, LL, 1, sW + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = tr[r], c = 16 * jc + ln;
+            R[RL::QT_OFF + t * KD + c] = scale * expf(sG[t]) * sQ[t * LK + c] - PW[r];
+        }
     }
     for (int i = tid; i < BC * BC; i += NT) R[RL::T_OFF + i] = sT[(i / BC) * LL + i % BC];
     if (tid < BC) {
@@ -192,7 +240,8 @@ __device__ __forceinline__ void seq_of(int n, const int32_t* cu, const int* chun
 
 // ---------------------------------------------------------------------------------------------------------
 // States: the forward chain of one 16-row slice of one (sequence, head), storing the entry state of every
-// chunk (float32 [slot][H][V][K]). Thread owns state entries e = tid + 256 m (row e / KD, column e % KD).
+// chunk (float32 [slot][H][V][K]), on float32 MFMA tiles. Wavefront w holds key tiles JPW w .. JPW w + JPW - 1
+// of the slice's state (lane: rows 4 lg + r, key 16 jc + ln) and forms token tile w of X and R.
 // ---------------------------------------------------------------------------------------------------------
 template <typename ST, int KD>
 __global__ __launch_bounds__(NT) void gdn_bwd_states_kernel(const ST* __restrict__ k, const ST* __restrict__ v,
@@ -201,23 +250,22 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states_kernel(const ST* __restrict
                                                             int T, int H, int V, int n_seq, int nc, int nvs,
                                                             float* __restrict__ states) {
     typedef BwdRec<KD> RL;
-    constexpr int LK = KD + 1, LL = BC + 1, LV = 17, NE = 16 * KD / NT;
+    constexpr int LK = KD + 1, LL = BC + 1, LV = 17, JPW = KD / 64;
     __shared__ float sK[BC * LK], sS[16 * LK], sT[BC * LL], sV[BC * LV], sZ[BC * LV], sC[256];
     int chain, vs;
     xcd_split(blockIdx.x, nvs, chain, vs);
     if (chain >= n_seq * H) return;
     const int n = chain / H, h = chain % H, tid = threadIdx.x, v0 = 16 * vs;
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     int b, bos, eos, slot0;
     seq_of(n, cu, chunk_off, T, nc, b, bos, eos, slot0);
     const int nch = (eos - bos + BC - 1) / BC;
-    float S[NE];
+    f32x4 S[JPW];
 #pragma unroll
-    for (int m = 0; m < NE; ++m) {
-        const int e = tid + NT * m, r = e / KD, c = e % KD;
-        S[m] = h0 ? h0[(((size_t)n * H + h) * V + v0 + r) * KD + c] : 0.f;
-    }
-    const int t = tid >> 2, v4 = (tid & 3) * 4;
-    // chunk ci's K rows, T, coefficients and V slice, loaded one chunk ahead
+    for (int i = 0; i < JPW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[i][r] = h0 ? h0[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] : 0.f;
     Tile<ST, BC, KD> tk;
     Tile<float, BC, BC> tt;
     Tile<ST, BC, 16> tv;
@@ -235,60 +283,47 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states_kernel(const ST* __restrict
     for (int ci = 0; ci < nch; ++ci) {
         float* Sout = states + (((size_t)(slot0 + ci) * H + h) * V + v0) * KD;
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + NT * m;
-            Sout[(e / KD) * KD + e % KD] = S[m];
-            sS[(e / KD) * LK + e % KD] = S[m];
-        }
+        for (int i = 0; i < JPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * lg + r, c = 16 * (JPW * w + i) + ln;
+                Sout[row * KD + c] = S[i][r];
+                sS[row * LK + c] = S[i][r];
+            }
         tk.store(sK);
         tt.store(sT);
         tv.store(sV);
         sC[tid] = cf;
         __syncthreads();
         if (ci + 1 < nch) issue(ci + 1);
-        // Z = diag(beta) (V - diag(Gamma) K S^T) on (token t, values v4 .. v4 + 3)
-        {
-            float x[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int c = 0; c < KD; ++c) {
-                const float kt = sK[t * LK + c];
+        // Z = diag(beta) (V - diag(Gamma) K S^T) on token tile w
+        const f32x4 X = mm4(sK + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] += kt * sS[(v4 + j) * LK + c];
-            }
-            const float gam = sC[64 + t], bt = sC[192 + t];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sZ[t * LV + v4 + j] = bt * (sV[t * LV + v4 + j] - gam * x[j]);
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * lg + r;
+            sZ[t * LV + ln] = sC[192 + t] * (sV[t * LV + ln] - sC[64 + t] * X[r]);
         }
         __syncthreads();
         // e R = e T Z (into sV, no longer needed)
-        {
-            float r[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int s2 = 0; s2 <= t; ++s2) {
-                const float ts = sT[t * LL + s2];
+        const f32x4 Rv = mm4(sT + 16 * w * LL, LL, 1, sZ, LV, 1, 0, 16 * (w + 1), zero4());
 #pragma unroll
-                for (int j = 0; j < 4; ++j) r[j] += ts * sZ[s2 * LV + v4 + j];
-            }
-            const float et = sC[128 + t];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sV[t * LV + v4 + j] = et * r[j];
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * lg + r;
+            sV[t * LV + ln] = sC[128 + t] * Rv[r];
         }
         __syncthreads();
-        // S <- Gamma_L S + (e R)^T K
+        // S <- Gamma_L S + (e R)^T K on the wavefront's key tiles
         const float gl = sC[64 + BC - 1];
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + NT * m, r = e / KD, c = e % KD;
-            float acc = gl * S[m];
-            for (int tt = 0; tt < BC; ++tt) acc += sV[tt * LV + r] * sK[tt * LK + c];
-            S[m] = acc;
-        }
+        for (int i = 0; i < JPW; ++i) S[i] = mm4(sV, 1, LV, sK + 16 * (JPW * w + i), LK, 1, 0, BC, S[i] * gl);
         __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Reverse chain: one 16-row slice of one (sequence, head), from dht (or zero) backwards. Before chunk c's
-// step the slice holds the gradient of chunk c's exit state, stored as float32 [slot][H][V][K]; after chunk
-// 0 it is dh0.
+// Reverse chain: one 16-row slice of one (sequence, head), from dht (or zero) backwards, on float32 MFMA tiles.
+// Before chunk c's step the slice holds the gradient of chunk c's exit state, stored as float32 [slot][H][V][K];
+// after chunk 0 it is dh0. Wavefront w holds key tiles JPW w .. of the gradient and forms token tile w of Z.
 // ---------------------------------------------------------------------------------------------------------
 template <typename ST, int KD>
 __global__ __launch_bounds__(NT) void gdn_bwd_dstate_kernel(const ST* __restrict__ k, const ST* __restrict__ dout,
@@ -297,21 +332,22 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate_kernel(const ST* __restrict
                                                             int T, int H, int V, int n_seq, int nc, int nvs,
                                                             float* __restrict__ dstates, float* __restrict__ dh0) {
     typedef BwdRec<KD> RL;
-    constexpr int LK = KD + 1, LV = 17, NE = 16 * KD / NT, LZ = BC + 1;
+    constexpr int LK = KD + 1, LV = 17, LZ = BC + 1, JPW = KD / 64;
     __shared__ float sK[BC * LK], sW[BC * LK], sQt[BC * LK], sD[16 * LK], sO[BC * LV], sZ[16 * LZ], sC[256];
     int chain, vs;
     xcd_split(blockIdx.x, nvs, chain, vs);
     if (chain >= n_seq * H) return;
     const int n = chain / H, h = chain % H, tid = threadIdx.x, v0 = 16 * vs;
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     int b, bos, eos, slot0;
     seq_of(n, cu, chunk_off, T, nc, b, bos, eos, slot0);
     const int nch = (eos - bos + BC - 1) / BC;
-    float dS[NE];
+    f32x4 dS[JPW];
 #pragma unroll
-    for (int m = 0; m < NE; ++m) {
-        const int e = tid + NT * m;
-        dS[m] = dht ? dht[(((size_t)n * H + h) * V + v0 + e / KD) * KD + e % KD] : 0.f;
-    }
+    for (int i = 0; i < JPW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dS[i][r] = dht ? dht[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] : 0.f;
     // chunk ci's K rows, W, Qt, coefficients and dO slice, loaded one chunk ahead (chunks run backwards)
     Tile<ST, BC, KD> tk;
     Tile<float, BC, KD> tw, tq;
@@ -331,11 +367,13 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate_kernel(const ST* __restrict
     for (int ci = nch - 1; ci >= 0; --ci) {
         float* Dout = dstates + (((size_t)(slot0 + ci) * H + h) * V + v0) * KD;
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + NT * m;
-            Dout[(e / KD) * KD + e % KD] = dS[m];
-            sD[(e / KD) * LK + e % KD] = dS[m];
-        }
+        for (int i = 0; i < JPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * lg + r, c = 16 * (JPW * w + i) + ln;
+                Dout[row * KD + c] = dS[i][r];
+                sD[row * LK + c] = dS[i][r];
+            }
         tk.store(sK);
         tw.store(sW);
         tq.store(sQt);
@@ -343,45 +381,38 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate_kernel(const ST* __restrict
         sC[tid] = cf;
         __syncthreads();
         if (ci > 0) issue(ci - 1);
-        // Z[r][t] = e_t (dS' K^T)[r][t]; thread: row r = tid / 16, tokens 4 (tid % 16) .. + 3
-        {
-            const int r = tid >> 4, t4 = (tid & 15) * 4;
-            float z[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int c = 0; c < KD; ++c) {
-                const float d = sD[r * LK + c];
+        // Z[r][t] = e_t (dS' K^T)[r][t] on token tile w
+        const f32x4 Zt = mm4(sD, LK, 1, sK + 16 * w * LK, 1, LK, 0, KD, zero4());
+        const float et = sC[128 + 16 * w + ln];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) z[j] += d * sK[(t4 + j) * LK + c];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sZ[r * LZ + t4 + j] = sC[128 + t4 + j] * z[j];
-        }
+        for (int r = 0; r < 4; ++r) sZ[(4 * lg + r) * LZ + 16 * w + ln] = et * Zt[r];
         __syncthreads();
-        // dS = Gamma_L dS' - Z W + dO^T Qt
+        // dS = Gamma_L dS' + dO^T Qt - Z W on the wavefront's key tiles
         const float gl = sC[64 + BC - 1];
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + NT * m, r = e / KD, c = e % KD;
-            float acc = gl * dS[m];
-            for (int tt = 0; tt < BC; ++tt) acc += sO[tt * LV + r] * sQt[tt * LK + c] - sZ[r * LZ + tt] * sW[tt * LK + c];
-            dS[m] = acc;
+        for (int i = 0; i < JPW; ++i) {
+            const int jc = JPW * w + i;
+            const f32x4 a = mm4(sO, 1, LV, sQt + 16 * jc, LK, 1, 0, BC, dS[i] * gl);
+            const f32x4 zw = mm4(sZ, LZ, 1, sW + 16 * jc, LK, 1, 0, BC, zero4());
+            dS[i] = a - zw;
         }
         __syncthreads();
     }
     if (dh0) {
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + NT * m;
-            dh0[(((size_t)n * H + h) * V + v0 + e / KD) * KD + e % KD] = dS[m];
-        }
+        for (int i = 0; i < JPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dh0[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] = dS[i][r];
     }
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Gradients of one (chunk slot, head): the value dimension in 16-row slices (entry state, exit-state
-// gradient, dO and V of the slice), dP, dT, dq and dk accumulated over the slices in registers, then the
-// solve and gate terms. Thread ownership: token t = tid / 4 of every [64 x 16] slice matrix (values
-// v4 .. v4 + 3, v4 = 4 (tid % 4)), of dP and dT (columns tid % 4 + 4 j) and of dq, dk (columns
-// tid % 4 + 4 m).
+// Gradients of one (chunk slot, head), on float32 MFMA tiles: wavefront w owns token rows 16 w .. 16 w + 15 of
+// every product. The value dimension runs in 16-row slices (entry state, exit-state gradient and dO of the
+// slice, the next slice's loading ahead); dP, dT, dq and dk accumulate over the slices in registers; then the
+// solve's and the gate's terms. P (scale D o Q K^T) is kept rather than the raw Q K^T: the gate term
+// scale dP D Q K^T is dP o P.
 // ---------------------------------------------------------------------------------------------------------
 template <typename ST, int KD>
 __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
@@ -390,20 +421,21 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
     const int2* __restrict__ table, const int32_t* __restrict__ cu, int T, int H, int V, int nc, float scale,
     ST* __restrict__ dq, ST* __restrict__ dk, ST* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta) {
     typedef BwdRec<KD> RL;
-    constexpr int LK = KD + 1, LL = BC + 1, LV = 17, NM = KD / 4;
-    __shared__ float sK[BC * LK], sQ[BC * LK], sT[BC * LL], sQK[BC * LL], sKK[BC * LL], sC[256];
-    // per-slice region; after the slices it holds dP | dT (two [64][65] blocks)
-    constexpr int SLICE_FLOATS = 2 * 16 * LK + 4 * BC * LV > 2 * BC * LL ? 2 * 16 * LK + 4 * BC * LV : 2 * BC * LL;
+    constexpr int LK = KD + 1, LL = BC + 1, LV = 17, NJ = KD / 16;
+    __shared__ float sK[BC * LK], sQ[BC * LK], sT[BC * LL], sP[BC * LL], sKK[BC * LL], sC[256];
+    // per-slice region; after the slices it holds dT (then U, then F) and scale D o dP
+    constexpr int SLICE_FLOATS = 2 * 16 * LK + 5 * BC * LV > 2 * BC * LL ? 2 * 16 * LK + 5 * BC * LV : 2 * BC * LL;
     __shared__ float sX[SLICE_FLOATS];
-    float* const sS = sX;                 // [16][LK] entry state of the slice
-    float* const sD = sX + 16 * LK;       // [16][LK] exit-state gradient of the slice
-    float* const sO = sX + 32 * LK;       // [64][LV] dO of the slice
-    float* const sZ = sO + BC * LV;       // [64][LV] Z = diag(beta) Y
-    float* const sR = sZ + BC * LV;       // [64][LV] R
-    float* const sdR = sR + BC * LV;      // [64][LV] dR, later dX
-    float* const sdP = sX;                // [64][LL] after the slices
-    float* const sdT = sX + BC * LL;      // [64][LL] after the slices
-    __shared__ float sDG[BC];
+    float* const sS = sX;               // [16][LK] entry state of the slice
+    float* const sD = sX + 16 * LK;     // [16][LK] exit-state gradient of the slice
+    float* const sO = sX + 32 * LK;     // [64][LV] dO of the slice
+    float* const sZ = sO + BC * LV;     // [64][LV] Z = diag(beta) Y
+    float* const sR = sZ + BC * LV;     // [64][LV] R
+    float* const sdR = sR + BC * LV;    // [64][LV] dR
+    float* const sdX = sdR + BC * LV;   // [64][LV] dX
+    float* const sdT = sX;              // [64][LL] after the slices: dT, then U = dT T^T, then F
+    float* const sDP = sX + BC * LL;    // [64][LL] after the slices: scale D o dP
+    __shared__ float sDG[BC], sEE[BC], sRed[NT / 64];
 
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     int b, t0, L;
@@ -422,28 +454,41 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
         tt.store(sT);
     }
     __syncthreads();
-    const int t = tid >> 2, q4 = tid & 3, v4 = 4 * q4;
-    // raw Q K^T and K K^T on the thread's (t, s) entries
-    for (int j = 0; j < 16; ++j) {
-        const int s2 = q4 + 4 * j;
-        float qk = 0.f, kk = 0.f;
-        for (int c = 0; c < KD; ++c) {
-            qk += sQ[t * LK + c] * sK[s2 * LK + c];
-            kk += sK[t * LK + c] * sK[s2 * LK + c];
-        }
-        sQK[t * LL + s2] = qk;
-        sKK[t * LL + s2] = kk;
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    // the lane's C-tile rows: tokens tr[r] = 16 w + 4 lg + r; its A-operand row: token 16 w + ln
+    int tr[4];
+    float Gr[4], gam[4], ee[4], bb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        tr[r] = 16 * w + 4 * lg + r;
+        Gr[r] = sC[tr[r]];
+        gam[r] = sC[64 + tr[r]];
+        ee[r] = sC[128 + tr[r]];
+        bb[r] = sC[192 + tr[r]];
     }
-    const float Gt = sC[t], gamt = sC[64 + t], et = sC[128 + t], bt = sC[192 + t], gl = sC[64 + BC - 1];
-    float aP[16], aT[16], aQ[NM], aK[NM];
+    const float gq_a = scale * sC[64 + 16 * w + ln], e_a = sC[128 + 16 * w + ln];
+    const float gl = sC[64 + BC - 1];
+    // P = scale (D o Q K^T) (s <= t) and the raw K K^T (s < t) on the wavefront's row tile
+    for (int j = 0; j < 4; ++j) {
+        f32x4 qk = zero4(), kk = zero4();
+        if (j <= w) {
+            qk = mm4(sQ + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, qk);
+            kk = mm4(sK + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, kk);
+        }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) aP[j] = aT[j] = 0.f;
+        for (int r = 0; r < 4; ++r) {
+            const int t = tr[r], s2 = 16 * j + ln;
+            sP[t * LL + s2] = s2 <= t ? scale * expf(Gr[r] - sC[s2]) * qk[r] : 0.f;
+            sKK[t * LL + s2] = s2 < t ? kk[r] : 0.f;
+        }
+    }
+    f32x4 aP[4], aT[4], aQ[NJ], aK[NJ];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) aQ[m] = aK[m] = 0.f;
-    float pGam = 0.f, pE = 0.f, pB = 0.f, pGL = 0.f;  // partial sums of dGamma_t, de_t, dbeta_t, dGamma_L
+    for (int j = 0; j < 4; ++j) aP[j] = aT[j] = zero4();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) aQ[j] = aK[j] = zero4();
+    float pGam[4] = {0.f, 0.f, 0.f, 0.f}, pE[4] = {0.f, 0.f, 0.f, 0.f}, pB[4] = {0.f, 0.f, 0.f, 0.f}, pGL = 0.f;
     const int nvs = V / 16;
-    __syncthreads();
-    // the slice's entry state, exit-state gradient and dO, loaded one slice ahead
     Tile<float, 16, KD> ts, td;
     Tile<ST, BC, 16> to;
     auto issue = [&](int vs) __attribute__((always_inline)) {
@@ -453,186 +498,147 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
         to.load(dout + (row0 * H + h) * (long)V + v0, (long)H * V, L);
     };
     issue(0);
+    __syncthreads();
     for (int vs = 0; vs < nvs; ++vs) {
         const int v0 = 16 * vs;
         ts.store(sS);
         td.store(sD);
         to.store(sO);
-        if (vs + 1 < nvs) issue(vs + 1);
         float vv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vv[j] = t < L ? ld(v + ((row0 + t) * H + h) * (long)V + v0 + v4 + j) : 0.f;
+        for (int r = 0; r < 4; ++r) vv[r] = tr[r] < L ? ld(v + ((row0 + tr[r]) * H + h) * (long)V + v0 + ln) : 0.f;
+        if (vs + 1 < nvs) issue(vs + 1);
         __syncthreads();
-        // X = K S^T, QS = Q S^T, KdS = K dS'^T on (t, v4 .. v4 + 3)
-        float X[4] = {0.f, 0.f, 0.f, 0.f}, QS[4] = {0.f, 0.f, 0.f, 0.f}, KdS[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < KD; ++c) {
-            const float kt = sK[t * LK + c], qt = sQ[t * LK + c];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float sv = sS[(v4 + j) * LK + c], dv_ = sD[(v4 + j) * LK + c];
-                X[j] += kt * sv;
-                QS[j] += qt * sv;
-                KdS[j] += kt * dv_;
-            }
-        }
+        // X = K S^T, QS = Q S^T, KdS = K dS'^T on (token tile w, the slice's 16 values)
+        const f32x4 X = mm4(sK + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
+        const f32x4 QS = mm4(sQ + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
+        const f32x4 KdS = mm4(sK + 16 * w * LK, LK, 1, sD, 1, LK, 0, KD, zero4());
         float Y[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            Y[j] = vv[j] - gamt * X[j];
-            sZ[t * LV + v4 + j] = bt * Y[j];
-            pGam += scale * sO[t * LV + v4 + j] * QS[j];
+        for (int r = 0; r < 4; ++r) {
+            Y[r] = vv[r] - gam[r] * X[r];
+            sZ[tr[r] * LV + ln] = bb[r] * Y[r];
+            pGam[r] += scale * sO[tr[r] * LV + ln] * QS[r];
         }
         __syncthreads();
-        // R = T Z;  dR = P^T dO + e KdS with P[s][t] = scale exp(G_s - G_t) QK[s][t], s >= t
-        float Rv[4] = {0.f, 0.f, 0.f, 0.f}, dR[4];
-        for (int s2 = 0; s2 <= t; ++s2) {
-            const float ts = sT[t * LL + s2];
+        // R = T Z;  dR = P^T dO + e KdS
+        const f32x4 R = mm4(sT + 16 * w * LL, LL, 1, sZ, LV, 1, 0, 16 * (w + 1), zero4());
+        const f32x4 dRp = mm4(sP + 16 * w, 1, LL, sO, LV, 1, 16 * w, BC, zero4());
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Rv[j] += ts * sZ[s2 * LV + v4 + j];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dR[j] = et * KdS[j];
-        for (int s2 = t; s2 < BC; ++s2) {
-            const float p = scale * expf(sC[s2] - Gt) * sQK[s2 * LL + t];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dR[j] += p * sO[s2 * LV + v4 + j];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sR[t * LV + v4 + j] = Rv[j];
-            sdR[t * LV + v4 + j] = dR[j];
-            pE += Rv[j] * KdS[j];
+        for (int r = 0; r < 4; ++r) {
+            const float dr = dRp[r] + ee[r] * KdS[r];
+            sR[tr[r] * LV + ln] = R[r];
+            sdR[tr[r] * LV + ln] = dr;
+            pE[r] += R[r] * KdS[r];
         }
         __syncthreads();
-        // dZ = T^T dR; dbeta, dY = dV, dX = -Gamma dY; dP += dO R^T, dT += dR Z^T on the thread's entries
-        float dZ[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int s2 = t; s2 < BC; ++s2) {
-            const float ts = sT[s2 * LL + t];
+        // dZ = T^T dR; dbeta, dY = dV, dX = -Gamma dY; dP += dO R^T, dT += dR Z^T
+        const f32x4 dZ = mm4(sT + 16 * w, 1, LL, sdR, LV, 1, 16 * w, BC, zero4());
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dZ[j] += ts * sdR[s2 * LV + v4 + j];
+        for (int r = 0; r < 4; ++r) {
+            pB[r] += Y[r] * dZ[r];
+            const float dY = bb[r] * dZ[r];
+            if (tr[r] < L) dv[((row0 + tr[r]) * H + h) * (long)V + v0 + ln] = Elem<ST>::from_f(dY);
+            sdX[tr[r] * LV + ln] = -gam[r] * dY;
+            pGam[r] -= dY * X[r];
         }
-#pragma unroll 1
-        for (int vv2 = 0; vv2 < 16; ++vv2) {
-            const float o = sO[t * LV + vv2], r = sdR[t * LV + vv2];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int s2 = q4 + 4 * j;
-                aP[j] += o * sR[s2 * LV + vv2];
-                aT[j] += r * sZ[s2 * LV + vv2];
-            }
-        }
-        float dX[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            pB += Y[j] * dZ[j];
-            const float dY = bt * dZ[j];
-            if (t < L) dv[((row0 + t) * H + h) * (long)V + v0 + v4 + j] = Elem<ST>::from_f(dY);
-            dX[j] = -gamt * dY;
-            pGam -= dY * X[j];
+            aP[j] = mm4(sO + 16 * w * LV, LV, 1, sR + 16 * j * LV, 1, LV, 0, 16, aP[j]);
+            aT[j] = mm4(sdR + 16 * w * LV, LV, 1, sZ + 16 * j * LV, 1, LV, 0, 16, aT[j]);
         }
         for (int i = tid; i < 16 * KD; i += NT) pGL += sS[(i / KD) * LK + i % KD] * sD[(i / KD) * LK + i % KD];
-        __syncthreads();  // every read of dR is done: it becomes dX
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sdR[t * LV + v4 + j] = dX[j];
         __syncthreads();
-        // dq += scale Gamma_t dO S;  dk += dX S + e R dS'
-#pragma unroll 1
-        for (int vv2 = 0; vv2 < 16; ++vv2) {
-            const float o = scale * gamt * sO[t * LV + vv2], x = sdR[t * LV + vv2], r = et * sR[t * LV + vv2];
+        // dq += scale Gamma dO S;  dk += dX S + e R dS'
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const int c = q4 + 4 * m;
-                const float sv = sS[vv2 * LK + c];
-                aQ[m] += o * sv;
-                aK[m] += x * sv + r * sD[vv2 * LK + c];
-            }
+        for (int j = 0; j < NJ; ++j) {
+            aQ[j] = mm4(sO + 16 * w * LV, LV, 1, sS + 16 * j, LK, 1, 0, 16, aQ[j], gq_a);
+            aK[j] = mm4(sdX + 16 * w * LV, LV, 1, sS + 16 * j, LK, 1, 0, 16, aK[j]);
+            aK[j] = mm4(sR + 16 * w * LV, LV, 1, sD + 16 * j, LK, 1, 0, 16, aK[j], e_a);
         }
         __syncthreads();
     }
-    // dP and dT to LDS; U = dT T^T on the thread's entries (T lower: j <= s)
+    // dT to LDS, U = dT T^T (T[s][j] is zero past j = s)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int s2 = q4 + 4 * j;
-        sdP[t * LL + s2] = aP[j];
-        sdT[t * LL + s2] = aT[j];
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sdT[tr[r] * LL + 16 * j + ln] = aT[j][r];
     __syncthreads();
-    float U[16];
+    f32x4 U[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int s2 = q4 + 4 * j;
-        float u = 0.f;
-        for (int jj = 0; jj <= s2; ++jj) u += sdT[t * LL + jj] * sT[s2 * LL + jj];
-        U[j] = u;
-    }
+    for (int j = 0; j < 4; ++j) U[j] = mm4(sdT + 16 * w * LL, LL, 1, sT + 16 * j * LL, 1, LL, 0, 16 * (j + 1), zero4());
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sdT[t * LL + q4 + 4 * j] = U[j];
-    __syncthreads();
-    // dA[t][s] = -sum_{j >= t} T[j][t] U[j][s] for s < t; then the gate terms, F and (scale D o dP)
-    float rowc = 0.f;
-    float Fv[16], DP[16];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int s2 = q4 + 4 * j;
-        float dA = 0.f;
-        if (s2 < t)
-            for (int jj = t; jj < BC; ++jj) dA -= sT[jj * LL + t] * sdT[jj * LL + s2];
-        const float d = s2 <= t ? expf(Gt - sC[s2]) : 0.f;
-        const float kk = sKK[t * LL + s2];
-        pB += dA * d * kk;                       // (dA is zero unless s < t)
-        Fv[j] = dA * bt * d;
-        DP[j] = s2 <= t ? scale * d * aP[j] : 0.f;
-        const float c = DP[j] * sQK[t * LL + s2] + Fv[j] * kk;
-        rowc += c;
-        sKK[t * LL + s2] = c;                    // own entry: K K^T is not read again
-    }
+        for (int r = 0; r < 4; ++r) sdT[tr[r] * LL + 16 * j + ln] = U[j][r];
     __syncthreads();
-    // (scale D o dP) into sdP, F into sdT (own entries; U is no longer read)
+    // dA = -T^T U on s < t (T[j][t] is zero below j = t); then the gate terms, F and scale D o dP
+    float rowc[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 Fv[4], DPv[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        sdP[t * LL + q4 + 4 * j] = DP[j];
-        sdT[t * LL + q4 + 4 * j] = Fv[j];
+    for (int j = 0; j < 4; ++j) {
+        f32x4 dA = zero4();
+        if (j <= w) dA = mm4(sT + 16 * w, 1, LL, sdT + 16 * j, LL, 1, 16 * w, BC, dA);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = tr[r], s2 = 16 * j + ln;
+            const float d = s2 <= t ? expf(Gr[r] - sC[s2]) : 0.f;
+            const float a = s2 < t ? -dA[r] : 0.f;
+            const float kk = sKK[t * LL + s2];
+            pB[r] += a * d * kk;
+            Fv[j][r] = a * bb[r] * d;
+            DPv[j][r] = s2 <= t ? scale * d * aP[j][r] : 0.f;
+            const float c = (s2 <= t ? aP[j][r] * sP[t * LL + s2] : 0.f) + Fv[j][r] * kk;
+            rowc[r] += c;
+            sKK[t * LL + s2] = c;  // own entry: K K^T is not read again
+        }
     }
+    __syncthreads();  // U is no longer read
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sdT[tr[r] * LL + 16 * j + ln] = Fv[j][r];
+            sDP[tr[r] * LL + 16 * j + ln] = DPv[j][r];
+        }
     __syncthreads();
     // dq += (scale D o dP) K;  dk += (scale D o dP)^T Q + F K + F^T K
-#pragma unroll 1
-    for (int s2 = 0; s2 < BC; ++s2) {
-        const float p = sdP[t * LL + s2], pt = sdP[s2 * LL + t], f = sdT[t * LL + s2] + sdT[s2 * LL + t];
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const int c = q4 + 4 * m;
-            const float ks = sK[s2 * LK + c];
-            aQ[m] += p * ks;
-            aK[m] += pt * sQ[s2 * LK + c] + f * ks;
+    for (int j = 0; j < NJ; ++j) {
+        aQ[j] = mm4(sDP + 16 * w * LL, LL, 1, sK + 16 * j, LK, 1, 0, 16 * (w + 1), aQ[j]);
+        aK[j] = mm4(sDP + 16 * w, 1, LL, sQ + 16 * j, LK, 1, 16 * w, BC, aK[j]);
+        aK[j] = mm4(sdT + 16 * w * LL, LL, 1, sK + 16 * j, LK, 1, 0, 16 * (w + 1), aK[j]);
+        aK[j] = mm4(sdT + 16 * w, 1, LL, sK + 16 * j, LK, 1, 16 * w, BC, aK[j]);
+    }
+    // row sums over the 16 lanes of each row group; <dS', S> over the workgroup
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pGam[r] += __shfl_xor(pGam[r], o, 64);
+            pE[r] += __shfl_xor(pE[r], o, 64);
+            pB[r] += __shfl_xor(pB[r], o, 64);
+            rowc[r] += __shfl_xor(rowc[r], o, 64);
         }
-    }
-    // the four threads of token t hold quarters of its row sums
-#pragma unroll
-    for (int o = 1; o <= 2; o <<= 1) {
-        pGam += __shfl_xor(pGam, o, 64);
-        pE += __shfl_xor(pE, o, 64);
-        pB += __shfl_xor(pB, o, 64);
-        rowc += __shfl_xor(rowc, o, 64);
-    }
-    // <dS', S> over the workgroup
     for (int o = 1; o < 64; o <<= 1) pGL += __shfl_xor(pGL, o, 64);
-    __shared__ float sRed[NT / 64], sEE[BC];
-    if ((tid & 63) == 0) sRed[tid >> 6] = pGL;
-    // dG_t = dGamma_t Gamma_t - de_t e_t + (row sum - column sum of the gate terms of D)
-    if (q4 == 0) {
-        sDG[t] = pGam * gamt - pE * et + rowc;
-        sEE[t] = pE * et;
-    }
-    if (t < L) {
+    if (lane == 0) sRed[w] = pGL;
+    if (ln == 0)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const int c = q4 + 4 * m;
-            dq[((row0 + t) * H + h) * (long)KD + c] = Elem<ST>::from_f(aQ[m]);
-            dk[((row0 + t) * H + h) * (long)KD + c] = Elem<ST>::from_f(aK[m]);
+        for (int r = 0; r < 4; ++r) {
+            sDG[tr[r]] = pGam[r] * gam[r] - pE[r] * ee[r] + rowc[r];
+            sEE[tr[r]] = pE[r] * ee[r];
+            if (tr[r] < L) dbeta[(row0 + tr[r]) * H + h] = pB[r];
         }
-        if (q4 == 0) dbeta[(row0 + t) * H + h] = pB;
-    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (tr[r] < L) {
+                const long o = ((row0 + tr[r]) * H + h) * (long)KD + 16 * j + ln;
+                dq[o] = Elem<ST>::from_f(aQ[j][r]);
+                dk[o] = Elem<ST>::from_f(aK[j][r]);
+            }
     __syncthreads();
     if (tid < BC) {
         float col = 0.f;
@@ -644,7 +650,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
             for (int tt = 0; tt < BC; ++tt) se += sEE[tt];
             float gsum = 0.f;
 #pragma unroll
-            for (int w = 0; w < NT / 64; ++w) gsum += sRed[w];
+            for (int ww = 0; ww < NT / 64; ++ww) gsum += sRed[ww];
             dG += se + gsum * gl;
         }
         // dg = the reverse cumulative sum of dG over the chunk: lane l scans dG of token 63 - l

@@ -270,10 +270,10 @@ __device__ __forceinline__ void pre_all(const bf16x8 (&kf)[4][KP], float G, floa
 
 // ---------------------------------------------------------------------------------------------------------
 // P = scale (D o Q K^T) of one chunk from the K and Q rows in LDS (RowBlock layout), in fragment order, for the
-// block rows ROWS: 0 for {0, 3}, 1 for {1, 2}, 2 for all four (five tiles each way). P^T tiles with K rows as A
-// (rows s) and Q rows as B (columns t): the C tile holds, for lane (ln, lg), P[16 ti + ln][16 tj + 4 lg + r],
-// which is fragment (ti, tj / 2)'s lane content (first or second half), the B operand that pairs with the R
-// fragments of the same tokens. G (in log2 units) is coefficients [192, 256).
+// block rows set in ROWS (bit ti: block row ti; every tile the same code, whichever call forms it). P^T tiles
+// with K rows as A (rows s) and Q rows as B (columns t): the C tile holds, for lane (ln, lg),
+// P[16 ti + ln][16 tj + 4 lg + r], which is fragment (ti, tj / 2)'s lane content (first or second half), the B
+// operand that pairs with the R fragments of the same tokens. G (in log2 units) is coefficients [192, 256).
 // ---------------------------------------------------------------------------------------------------------
 template <int KD, int ROWS>
 __device__ __forceinline__ void form_p(const lds_u8* KR, const lds_u8* QR, const lds_f32* cf, float scale, lds_u8* P) {
@@ -281,6 +281,7 @@ __device__ __forceinline__ void form_p(const lds_u8* KR, const lds_u8* QR, const
     typedef Elem<bf16_t> El;
     constexpr int KP = KD / 32;
     constexpr int UST = (16 / RBk::RPB) * 1024;
+    constexpr int TOP = (ROWS & 8) ? 3 : (ROWS & 4) ? 2 : (ROWS & 2) ? 1 : 0;  // highest block row formed
     const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
     int orow[KP];
 #pragma unroll
@@ -290,11 +291,10 @@ __device__ __forceinline__ void form_p(const lds_u8* KR, const lds_u8* QR, const
     for (int R = 0; R < 4; ++R)
 #pragma unroll
         for (int p = 0; p < KP; ++p)
-            if (ROWS != 1 || R < 3) kf[R][p] = *(const lds_bf16x8*)(KR + orow[p] + R * UST);
+            if (R <= TOP) kf[R][p] = *(const lds_bf16x8*)(KR + orow[p] + R * UST);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
-        if (ROWS == 0 && (ti == 1 || ti == 2)) continue;
-        if (ROWS == 1 && (ti == 0 || ti == 3)) continue;
+        if (!((ROWS >> ti) & 1)) continue;
         bf16x8 qf[KP];
 #pragma unroll
         for (int p = 0; p < KP; ++p) qf[p] = *(const lds_bf16x8*)(QR + orow[p] + ti * UST);
