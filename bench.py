@@ -41,10 +41,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GDN chunk-fwd tokens/s (bf16, K=V=128) + % of MFMA/HBM roofline, 1 MI355X"
-METRIC_BWD = "GDN chunk-bwd tokens/s (bf16, K=V=128) + % of HBM roofline, 1 MI355X"
+METRIC_BWD = "GDN chunk-bwd tokens/s (bf16, K=V=128) + % of roofline, 1 MI355X"
 METRIC_KDA = "KDA chunk-fwd tokens/s (bf16, K=V=128) + % of HBM roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+F32_PEAK_TFLOPS = 157.3        # MI355X dense float32 MFMA, published
 
 
 def log(*a):
@@ -117,6 +118,18 @@ def bwd_bytes(w, kernel):
     if kernel in parts:
         return parts[kernel]
     return 7 * row + 4 * gate + 3 * state
+
+
+def bwd_grad_flops(w):
+    """Contraction flops the chunk backward's per-chunk gradients need (2 per multiply-add), by the
+    formulas of the chunk backward, triangular factors counted on their lower-triangular pairs only:
+    X, Q S, K dS', dO S, dX S, R dS' (C K V each); Q K^T, K K^T, dP K, dP^T Q, dT K, dT^T K (C(C+1)/2 K
+    each); T Z, P^T dO, T^T dR, dO R^T, dR Z^T (C(C+1)/2 V each); dT T and the dA product (C^3/6 each)."""
+    C = w.chunk
+    c2 = C * (C + 1) // 2
+    mac = 6 * C * w.K * w.V + 6 * c2 * w.K + 5 * c2 * w.V + C ** 3 // 3
+    chunks = (w.tokens // C) * w.H
+    return 2 * mac * chunks
 
 
 def two_pass_bytes(w):
@@ -467,12 +480,19 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(dom, w.name),
                 "kernel": dom, "avg_us": round(avg_s * 1e6, 2), "algorithmic_bytes": ab}
+        if dom == "gdn_bwd_grad":
+            # float32 contractions bind this kernel before HBM does: report that roofline, the HBM one beside it
+            fl = bwd_grad_flops(w)
+            tf = fl / avg_s / 1e12
+            roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / F32_PEAK_TFLOPS, 4), "traffic": roof["traffic"], "kernel": dom,
+                    "avg_us": roof["avg_us"], "algorithmic_flops": fl, "dtype": "f32", "hbm": roof}
     decode = isinstance(w, wl.DecodeWorkload)
     gate = isinstance(w, wl.GateWorkload)
     path_bytes = algorithmic_bytes(w, "decode_path" if decode else "gate_path" if gate else "path")
     path_ach = path_bytes / (elapsed / args.steps) / 1e9
     copy_gbs = None if args.no_copy_peak else measured_copy_gbs(dev)
-    if roof is not None and copy_gbs:
+    if roof is not None and copy_gbs and roof["bound"] == "hbm":
         roof["measured_peak"] = copy_gbs
         roof["frac_of_measured"] = round(roof["achieved"] / copy_gbs, 4)
 
