@@ -956,23 +956,22 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
 // head) chain, for launches with at most two slices per CU. Pre (gdn_prep_bf16_kernel) has written every
 // chunk's T diag(beta) and coefficients; the workgroup streams them with the chunk's K, Q and V rows into LDS
 // rings, two chunks ahead of the step that uses them, and forms P itself.
-// Eleven wavefronts with fixed roles, one workgroup barrier per step; in step s:
-//   0, 1  state:     key tiles [0, KB/2) / [KB/2, KB) of the slice's float32 state: once both residual
-//                    wavefronts have published e R of chunk s (LDS flags), S <- Gamma_L S + K_s^T (e R); the
-//                    bf16 state of chunk s+1 goes to LDS
-//   2, 7  residual:  chunk s, token tiles {0, 1} / {2, 3}: X = K S^T from the bf16 entry state, Y = V - Gamma X
-//                    and R = T diag(beta) Y on their tiles (wavefront 7 also forms Y of tiles 0, 1, which R of
-//                    tiles 2, 3 needs, T being lower triangular), e R for the state wavefronts and R for the output
-//   3, 4  output:    O of chunk s-1 for token tiles {0, 3} / {1, 2} (its Q rows, Gamma and entry state were
-//                    read into registers in step s-1); then reads chunk s's
-//   5, 6  P:         P = scale (D o Q K^T) of chunk s, block rows {0, 3} / {1, 2}
-//   8     records:   T diag(beta) and the coefficients of chunk s+2
-//   9     feeder:    K rows of chunk s+2 (16-byte direct loads into LDS)
-//   10    feeder:    Q rows and the V slice of chunk s+2
+// Eight wavefronts with fixed roles, one workgroup barrier per step; in step s:
+//   0     chain:     the slice's float32 state in registers and the whole step of chunk s: X = K S^T from the
+//                    bf16 entry state, Y = V - Gamma X, R = T diag(beta) Y, e R and S <- Gamma_L S + K_s^T (e R),
+//                    each product's C tile the next one's B operand; the K^T reads of the update are issued
+//                    behind the residual's own reads; R of chunk s and the bf16 entry state of chunk s+1 go to
+//                    LDS for the output wavefronts
+//   1, 2  output:    O of chunk s-1 for token tiles {0, 3} / {1, 2} (its Q rows and Gamma were read into
+//                    registers in step s-1, its entry state, R and P come from LDS); then reads chunk s's
+//   3, 5  P:         P = scale (D o Q K^T) of chunk s, block rows {0, 3} / {1, 2}
+//   4     records:   T diag(beta) and the coefficients of chunk s+2
+//   6     feeder:    K rows of chunk s+2 (16-byte direct loads into LDS)
+//   7     feeder:    Q rows and the V slice of chunk s+2
 // The loading wavefronts wait, before the barrier of step s, only for the loads they issued in step s-1, so
-// that a load has a whole step to land. Wavefront w runs on SIMD w % 4: the two state wavefronts and the two
-// residual wavefronts sit on four different SIMDs. Every per-chunk product comes from gdn_steps.h, as in Pre
-// and the per-head kernel.
+// that a load has a whole step to land. Wavefront w runs on SIMD w % 4: the chain wavefront shares its SIMD
+// only with the record loader. Every per-chunk product comes from gdn_steps.h, as in Pre and the per-head
+// kernel.
 // ---------------------------------------------------------------------------
 template <int KD>
 struct SliceLds {
@@ -985,17 +984,14 @@ struct SliceLds {
     static constexpr int OFF_C = OFF_V + 3 * 2048;               // coefficients float[256], ring of 3
     static constexpr int OFF_T = OFF_C + 3 * 1024;               // T diag(beta) fragments, ring of 3
     static constexpr int OFF_P = OFF_T + 3 * kTriFrags * 1024;   // P fragments, ring of 2
-    static constexpr int OFF_SF = OFF_P + 2 * kTriFrags * 1024;  // bf16 entry state [KB][64 lanes] x 8 B, ring of 2
-    static constexpr int OFF_R = OFF_SF + 2 * KB * 512;          // bf16 R [4][64 lanes] x 8 B, ring of 2
-    static constexpr int OFF_ER = OFF_R + 2 * 2048;              // bf16 e R [4][64 lanes] x 8 B
-    static constexpr int OFF_FLAG = OFF_ER + 2048;               // int[2]: the last chunk whose e R of token
-                                                                 // tiles {0, 1} / {2, 3} is in LDS
-    static constexpr int BYTES = OFF_FLAG + 64;
+    static constexpr int OFF_SF = OFF_P + 2 * kTriFrags * 1024;  // bf16 entry state [KB][64 lanes] x 8 B, ring of 3
+    static constexpr int OFF_R = OFF_SF + 3 * KB * 512;          // bf16 R [4][64 lanes] x 8 B, ring of 2
+    static constexpr int BYTES = OFF_R + 2 * 2048;
     static_assert(BYTES <= 160 * 1024, "LDS plan exceeds the CU's 160 KB");
 };
 
 template <int KD>
-__global__ __launch_bounds__(704) void gdn_chain_slice_kernel(
+__global__ __launch_bounds__(512) void gdn_chain_slice_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ h0, const int32_t* __restrict__ cu, const int* __restrict__ chunk_off,
     const uint8_t* __restrict__ fac, int nc, int T, int H, int HK, int V, int n_seq, int nvb, float scale,
@@ -1038,123 +1034,75 @@ __global__ __launch_bounds__(704) void gdn_chain_slice_kernel(
     auto cbuf = [&](int c) __attribute__((always_inline)) { return (lds_f32*)(lds0 + SM::OFF_C + (c % 3) * 1024); };
     auto tbuf = [&](int c) __attribute__((always_inline)) { return lds0 + SM::OFF_T + (c % 3) * kTriFrags * 1024; };
     auto pbuf = [&](int c) __attribute__((always_inline)) { return lds0 + SM::OFF_P + (c & 1) * kTriFrags * 1024; };
-    auto sfbuf = [&](int c) __attribute__((always_inline)) { return lds0 + SM::OFF_SF + (c & 1) * KB * 512; };
+    auto sfbuf = [&](int c) __attribute__((always_inline)) { return lds0 + SM::OFF_SF + (c % 3) * KB * 512; };
     auto rbuf = [&](int c) __attribute__((always_inline)) { return lds0 + SM::OFF_R + (c & 1) * 2048; };
     auto chunk_len = [&](int c) __attribute__((always_inline)) { return min(GC, eos - (bos + c * GC)); };
     auto barrier = [] __attribute__((always_inline)) () { asm volatile("s_barrier" ::: "memory"); };
-    typedef __attribute__((address_space(3))) int lds_int;
-    volatile lds_int* const flag = (volatile lds_int*)(lds0 + SM::OFF_FLAG);  // [0] e R lo, [1] e R hi
-    // bounded wait for flag[i] >= s (set within the same step by another wavefront; polled without a sleep,
-    // as the wait is on the critical path)
-    auto wait_flag = [&](int i, int s) __attribute__((always_inline)) {
-        for (int spin = 0; spin < (1 << 24) && flag[i] < s; ++spin) {
-        }
-    };
     // Every wavefront passes one barrier before the steps and one at the end of each step s = -2 .. nch.
 
-    if (wave <= 1) {
-        // ================= state: key tiles [KT0, KT0 + KB/2) of the slice =================
-        __builtin_amdgcn_s_setprio(2);  // the chain is the critical path: first pick of their SIMDs
-        auto state_role = [&](auto HH) __attribute__((always_inline)) {
-            constexpr int NKT = KB / 2, KT0 = decltype(HH)::value * NKT;
-            f32x4 S[NKT];
-#pragma unroll
-            for (int i = 0; i < NKT; ++i) {
-                const int kt = KT0 + i;
-                const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
-                S[i] = h0 ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + row) * KD + kk) : zero4();
-            }
-            auto put_state = [&](int c) __attribute__((always_inline)) {  // bf16 entry state of chunk c, own tiles
-#pragma unroll
-                for (int i = 0; i < NKT; ++i) *(lds_i16x4*)(sfbuf(c) + (KT0 + i) * 512 + lane * 8) = El::pack(S[i]);
-            };
-            if (nch > 0) put_state(0);
-            wave_lds_sync();
-            barrier();
-            for (int s = -2; s <= nch; ++s) {
-                if (s >= 0 && s < nch) {
-                    i16x4 Ka[NKT][4];
-                    Ops::template read_kt<KT0, NKT>(kbuf(s), Ka);
-                    const float gl = cbuf(s)[63];
-                    wait_flag(0, s);
-                    wait_flag(1, s);
-                    i16x4 ER[4];
-#pragma unroll
-                    for (int ti = 0; ti < 4; ++ti) ER[ti] = *(const lds_i16x4*)(lds0 + SM::OFF_ER + ti * 512 + lane * 8);
-                    Ops::template update_with<NKT>(S, ER, Ka, gl);
-                    if (s + 1 < nch) put_state(s + 1);
-                    wave_lds_sync();
-                }
-                barrier();
-            }
-            if (ht) {
-#pragma unroll
-                for (int i = 0; i < NKT; ++i) {
-                    const int kt = KT0 + i;
-                    const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
-                    *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + row) * KD + kk) = S[i];
-                }
-            }
-        };
-        if (wave == 0)
-            state_role(std::integral_constant<int, 0>());
-        else
-            state_role(std::integral_constant<int, 1>());
-    } else if (wave == 2 || wave == 7) {
-        // ================= residual of chunk s: wavefront 2 token tiles {0, 1}, wavefront 7 tiles {2, 3} =================
-        __builtin_amdgcn_s_setprio(2);
+    if (wave == 0) {
+        // ================= chain: the slice's float32 state and the whole chunk step =================
+        __builtin_amdgcn_s_setprio(2);  // the chain is the critical path: first pick of its SIMD
         const int off_v = ((4 * lg + (ln >> 2)) * 16 + 4 * (ln & 3)) * 2;  // transposed V reads
-        const int half = wave == 2 ? 0 : 1;
-        if (lane == 0) flag[half] = -1;
+        f32x4 S[KB];
+        i16x4 Sf[KB];
+#pragma unroll
+        for (int kt = 0; kt < KB; ++kt) {
+            const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
+            S[kt] = h0 ? *reinterpret_cast<const f32x4*>(h0 + (((size_t)n * H + h) * V + row) * KD + kk) : zero4();
+            Sf[kt] = El::pack(S[kt]);
+        }
+        auto put_state = [&](int c) __attribute__((always_inline)) {  // bf16 entry state of chunk c
+#pragma unroll
+            for (int kt = 0; kt < KB; ++kt) *(lds_i16x4*)(sfbuf(c) + kt * 512 + lane * 8) = Sf[kt];
+        };
+        if (nch > 0) put_state(0);
         wave_lds_sync();
         barrier();
         for (int s = -2; s <= nch; ++s) {
             if (s >= 0 && s < nch) {
-                i16x4 Sf[KB];
+                // the K^T fragments of the update are read while the residual computes, half of the key tiles
+                // after each half of X
+                i16x4 Ka[KB / 2][4], Kb[KB / 2][4];
+                f32x4 R[4];
+                i16x4 ER[4];
+                Ops::residual_ahead(Sf, kbuf(s), vbuf(s) + off_v, 0xffffffffu, cbuf(s), tbuf(s), R, ER,
+                                    [&]() __attribute__((always_inline)) { Ops::template read_kt<0, KB / 2>(kbuf(s), Ka); },
+                                    [&]() __attribute__((always_inline)) { Ops::template read_kt<KB / 2, KB / 2>(kbuf(s), Kb); });
 #pragma unroll
-                for (int kt = 0; kt < KB; ++kt) Sf[kt] = *(const lds_i16x4*)(sfbuf(s) + kt * 512 + lane * 8);
-                f32x4 R[2];
-                i16x4 ER[2];
-                if (half == 0) {
-                    const auto in = Ops::template residual_r_in<0>(cbuf(s), tbuf(s));
-                    i16x4 Y[2];
-                    Ops::template residual_y<0>(Sf, kbuf(s), vbuf(s) + off_v, 0xffffffffu, cbuf(s), Y);
-                    Ops::template residual_r<0>(cat8(Y[0], Y[1]), bf16x8{}, in, R, ER);
-                } else {
-                    // Y of tiles 0, 1 as well (the same code as wavefront 2, so the same bits), rather than
-                    // waiting for it
-                    const auto in = Ops::template residual_r_in<2>(cbuf(s), tbuf(s));
-                    i16x4 Ylo[2], Yhi[2];
-                    Ops::template residual_y<0>(Sf, kbuf(s), vbuf(s) + off_v, 0xffffffffu, cbuf(s), Ylo);
-                    Ops::template residual_y<2>(Sf, kbuf(s), vbuf(s) + off_v, 0xffffffffu, cbuf(s), Yhi);
-                    Ops::template residual_r<2>(cat8(Ylo[0], Ylo[1]), cat8(Yhi[0], Yhi[1]), in, R, ER);
-                }
+                for (int ti = 0; ti < 4; ++ti) *(lds_i16x4*)(rbuf(s) + ti * 512 + lane * 8) = El::pack(R[ti]);
+                Ops::template update_halves<KB>(S, ER, Ka, Kb, cbuf(s)[63]);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int ti = 2 * half + i;
-                    *(lds_i16x4*)(lds0 + SM::OFF_ER + ti * 512 + lane * 8) = ER[i];
-                    *(lds_i16x4*)(rbuf(s) + ti * 512 + lane * 8) = El::pack(R[i]);
-                }
+                for (int kt = 0; kt < KB; ++kt) Sf[kt] = El::pack(S[kt]);
+                // R of chunk s and the entry state of chunk s (written in step s - 1) are in LDS; the entry state
+                // of chunk s + 1 is written now and waited for at the end of the next step
                 wave_lds_sync();
-                if (lane == 0) flag[half] = s;
-                wave_lds_sync();
+                if (s + 1 < nch) put_state(s + 1);
             }
             barrier();
         }
-    } else if (wave <= 4) {
-        // ================= output: wavefront 3 token tiles {0, 3}, wavefront 4 tiles {1, 2} =================
-        auto tile_of = [&](int i) __attribute__((always_inline)) { return wave == 3 ? 3 * i : 1 + i; };
+        if (ht) {
+#pragma unroll
+            for (int kt = 0; kt < KB; ++kt) {
+                const int kk = 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1), row = row0 + ln;
+                *reinterpret_cast<f32x4*>(ht + (((size_t)n * H + h) * V + row) * KD + kk) = S[kt];
+            }
+        }
+    } else if (wave <= 2) {
+        // ================= output: wavefront 1 token tiles {0, 3}, wavefront 2 tiles {1, 2} =================
+        auto tile_of = [&](int i) __attribute__((always_inline)) { return wave == 1 ? 3 * i : 1 + i; };
         bf16x8 Qf[2][KP];
         float gq[2];
-        i16x4 Sf[KB];
         barrier();
         for (int s = -2; s <= nch; ++s) {
             const int c = s - 1;  // chunk whose output is formed now
             if (c >= 0 && c < nch) {
                 const int t0 = bos + c * GC, L = chunk_len(c);
-                i16x4 Rb[4];
+                i16x4 Rb[4], Sf[KB];
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) Rb[ti] = *(const lds_i16x4*)(rbuf(c) + ti * 512 + lane * 8);
+#pragma unroll
+                for (int kt = 0; kt < KB; ++kt) Sf[kt] = *(const lds_i16x4*)(sfbuf(c) + kt * 512 + lane * 8);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int tt = tile_of(i);
@@ -1168,7 +1116,8 @@ __global__ __launch_bounds__(704) void gdn_chain_slice_kernel(
                 }
             }
             if (s >= 0 && s < nch) {
-                // chunk s's Q row fragments of the own tiles, scale Gamma of the lane's token, the bf16 entry state
+                // chunk s's Q row fragments of the own tiles and scale Gamma of the lane's token (the Q ring
+                // slot is refilled in step s + 1)
                 const lds_f32* cf = cbuf(s);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
@@ -1177,18 +1126,16 @@ __global__ __launch_bounds__(704) void gdn_chain_slice_kernel(
                     for (int p = 0; p < KP; ++p) Qf[i][p] = *(const lds_bf16x8*)(qbuf(s) + Ops::orow(p) + tt * UST);
                     gq[i] = cf[16 * tt + ln] * scale;
                 }
-#pragma unroll
-                for (int kt = 0; kt < KB; ++kt) Sf[kt] = *(const lds_i16x4*)(sfbuf(s) + kt * 512 + lane * 8);
             }
             wave_lds_sync();
             barrier();
         }
-    } else if (wave <= 6) {
-        // ================= P of chunk s: wavefront 5 block rows {0, 3}, wavefront 6 rows {1, 2} =================
+    } else if (wave == 3 || wave == 5) {
+        // ================= P of chunk s: wavefront 3 block rows {0, 3}, wavefront 5 rows {1, 2} =================
         barrier();
         for (int s = -2; s <= nch; ++s) {
             if (s >= 0 && s < nch) {
-                if (wave == 5)
+                if (wave == 3)
                     form_p<KD, 0x9>(kbuf(s), qbuf(s), cbuf(s), scale, pbuf(s));
                 else
                     form_p<KD, 0x6>(kbuf(s), qbuf(s), cbuf(s), scale, pbuf(s));
@@ -1197,7 +1144,7 @@ __global__ __launch_bounds__(704) void gdn_chain_slice_kernel(
             barrier();
         }
     } else {
-        // ================= loaders of chunk s+2: wavefront 8 the records, 9 the K rows, 10 the Q rows and V slice =================
+        // ================= loaders of chunk s+2: wavefront 4 the records, 6 the K rows, 7 the Q rows and V slice =================
         // Rows past the end of a partial chunk repeat its last token (finite values that the zero beta,
         // T diag(beta) columns and e of padded tokens keep out of every stored result).
         const size_t krs = (size_t)HK * KD * 2, vrs = (size_t)H * V * 2;  // token strides (bytes)
@@ -1233,9 +1180,9 @@ __global__ __launch_bounds__(704) void gdn_chain_slice_kernel(
             const int c = s + 2;
             const bool more = c < nch;
             if (more) {
-                if (wave == 8)
+                if (wave == 4)
                     feed_rec(c);
-                else if (wave == 9)
+                else if (wave == 6)
                     feed_rows(k, c, kbuf(c));
                 else {
                     feed_rows(q, c, qbuf(c));
@@ -1245,9 +1192,9 @@ __global__ __launch_bounds__(704) void gdn_chain_slice_kernel(
             // chunk s+1's loads (issued in step s-1) have landed; chunk s+2's stay in flight
             if (!more)
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            else if (wave == 8)
+            else if (wave == 4)
                 asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NREC) : "memory");
-            else if (wave == 9)
+            else if (wave == 6)
                 asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK) : "memory");
             else
                 asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NQV) : "memory");
@@ -1312,7 +1259,7 @@ static hipError_t run_gdn_bf16(int mode, const bf16_t* q, const bf16_t* k, const
     if (per_slice) {
         const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * nvb);
         timing_begin("gdn_chain_slice", s);
-        gdn_chain_slice_kernel<KD><<<grid, 704, 0, s>>>(q, k, v, h0, cu, ws.chunk_off, ws.factors, nc, T, H, HK, V, N, nvb,
+        gdn_chain_slice_kernel<KD><<<grid, 512, 0, s>>>(q, k, v, h0, cu, ws.chunk_off, ws.factors, nc, T, H, HK, V, N, nvb,
                                                   scale, out, ht);
         timing_end(s);
         return hipGetLastError();

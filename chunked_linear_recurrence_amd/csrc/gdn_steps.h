@@ -32,6 +32,14 @@ typedef __attribute__((address_space(3))) float lds_f32;
 // wavefront-local order of LDS traffic: later LDS reads see the lanes' earlier writes
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// An LDS address formed in a register as it stands: the reads that follow add their constant parts in the
+// instruction's offset field, instead of the compiler keeping one precomputed address per read alive.
+__device__ __forceinline__ const __attribute__((address_space(3))) uint8_t* lds_base(
+    const __attribute__((address_space(3))) uint8_t* p) {
+    asm volatile("" : "+v"(p));
+    return p;
+}
+
 // 16-byte loads of four floats and 16-byte stores, LDS or global memory
 __device__ __forceinline__ f32x4 ld4(const lds_f32* p) { return *(const lds_f32x4*)p; }
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
@@ -340,40 +348,71 @@ struct SliceOps {
         return RBk::off(4 * lg + (ln >> 2), 4 * p + (ln & 3));
     }
 
-    // The residual in two halves over the token tiles, so that two wavefronts can share it with the same
-    // arithmetic as one. Each step first issues all of its LDS reads and only then its products, so that the
-    // reads' latency is paid once.
-    // residual_y<U0>: X = K S^T on the token tiles U0, U0 + 1 from the bf16 entry state Sf, and Y = V - Gamma X
-    // there in bf16. KR: K rows; vtr: this slice's V block [64][16] bf16 at the lane's transposed-read offset;
-    // vmask zeroes V for transition rows; cf: coefficients.
+    // The residual, by halves over the token tiles: for the token tiles U0, U0 + 1, x_in issues the LDS reads
+    // (K row fragments, the Gamma coefficients, the V block) and x_mul forms X = K S^T from the bf16 entry state
+    // Sf; residual_yx forms Y = V - Gamma X in bf16. KR: K rows; vtr: this slice's V block [64][16] bf16 at the
+    // lane's transposed-read offset; cf: coefficients. The two schedules below (residual, residual_ahead) call
+    // the same pieces, so they give the same bits.
     template <int U0>
-    __device__ static void residual_y(const i16x4 (&Sf)[KB], const lds_u8* KR, const lds_u8* vtr, uint32_t vmask,
-                                      const lds_f32* cf, i16x4 (&Yf)[2]) {
-        const int lg = lane_id() >> 4;
+    struct XIn {
         bf16x8 kr[2][KP];
         f32x4 gam[2];
         i16x4 vx[2];
+    };
+    template <int U0>
+    struct XOut {
+        f32x4 X[2], gam[2];
+        i16x4 vx[2];
+    };
+    template <int U0>
+    __device__ static XIn<U0> x_in(const lds_u8* KR, const lds_u8* vtr, const lds_f32* cf) {
+        const int lg = lane_id() >> 4;
+        XIn<U0> in;
 #pragma unroll
-        for (int p = 0; p < KP; ++p)
+        for (int p = 0; p < KP; ++p) {
+            const lds_u8* kb = lds_base(KR + orow(p));
 #pragma unroll
-            for (int u = 0; u < 2; ++u) kr[u][p] = *(const lds_bf16x8*)(KR + orow(p) + (U0 + u) * UST);
+            for (int u = 0; u < 2; ++u) in.kr[u][p] = *(const lds_bf16x8*)(kb + (U0 + u) * UST);
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            gam[u] = *(const lds_f32x4*)(cf + 16 * (U0 + u) + 4 * lg);
-            vx[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vtr + 16 * (U0 + u) * 16 * 2));
+            in.gam[u] = *(const lds_f32x4*)(cf + 16 * (U0 + u) + 4 * lg);
+            in.vx[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vtr + 16 * (U0 + u) * 16 * 2));
         }
-        __builtin_amdgcn_sched_barrier(0);
+        return in;
+    }
+    template <int U0>
+    __device__ static XOut<U0> x_mul(const XIn<U0>& in, const i16x4 (&Sf)[KB]) {
+        XOut<U0> o;
         // (the two token tiles' accumulations interleaved, each summed over p in order)
-        f32x4 X[2] = {zero4(), zero4()};
+        o.X[0] = zero4();
+        o.X[1] = zero4();
 #pragma unroll
         for (int p = 0; p < KP; ++p)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) X[u] = mma32(kr[u][p], cat8(Sf[2 * p], Sf[2 * p + 1]), X[u]);
+            for (int u = 0; u < 2; ++u) o.X[u] = mma32(in.kr[u][p], cat8(Sf[2 * p], Sf[2 * p + 1]), o.X[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            o.gam[u] = in.gam[u];
+            o.vx[u] = in.vx[u];
+        }
+        return o;
+    }
+    // reads, then products (the reads' latency paid once per half)
+    template <int U0>
+    __device__ static XOut<U0> residual_x(const i16x4 (&Sf)[KB], const lds_u8* KR, const lds_u8* vtr, const lds_f32* cf) {
+        const XIn<U0> in = x_in<U0>(KR, vtr, cf);
+        __builtin_amdgcn_sched_barrier(0);
+        return x_mul<U0>(in, Sf);
+    }
+    // Y = V - Gamma X on those tiles in bf16; vmask zeroes V for transition rows
+    template <int U0>
+    __device__ static void residual_yx(const XOut<U0>& x, uint32_t vmask, i16x4 (&Yf)[2]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-            const i16x4 Vf = __builtin_bit_cast(i16x4, __builtin_bit_cast(u32x2, vx[u]) & vmask);
-            Yf[u] = El::pack(El::unpack(Vf) - gam[u] * X[u]);
+            const i16x4 Vf = __builtin_bit_cast(i16x4, __builtin_bit_cast(u32x2, x.vx[u]) & vmask);
+            Yf[u] = El::pack(El::unpack(Vf) - x.gam[u] * x.X[u]);
         }
     }
     // The T diag(beta) fragments and the e coefficients that residual_r<U0> needs (they do not depend on Y):
@@ -383,13 +422,14 @@ struct SliceOps {
         bf16x8 tf[U0 == 0 ? 2 : 4];
         f32x4 ec[2];
     };
+    __device__ static bf16x8 tri_in(const lds_u8* Tfr, int ti, int p) {
+        return *(const lds_bf16x8*)(Tfr + tri_frag(ti, p) * 1024 + lane_id() * 16);
+    }
     template <int U0>
     __device__ static RIn<U0> residual_r_in(const lds_f32* cf, const lds_u8* Tfr) {
-        const int lane = lane_id(), lg = lane >> 4;
+        const int lg = lane_id() >> 4;
         RIn<U0> in;
-        auto tf = [&](int ti, int p) __attribute__((always_inline)) {
-            return *(const lds_bf16x8*)(Tfr + tri_frag(ti, p) * 1024 + lane * 16);
-        };
+        auto tf = [&](int ti, int p) __attribute__((always_inline)) { return tri_in(Tfr, ti, p); };
         if constexpr (U0 == 0) {
             in.tf[0] = tf(0, 0);
             in.tf[1] = tf(1, 0);
@@ -417,14 +457,44 @@ struct SliceOps {
 #pragma unroll
         for (int i = 0; i < 2; ++i) ER[i] = El::pack(R[i] * in.ec[i]);
     }
-    // R = T diag(beta) (V - diag(Gamma) K S^T) from the bf16 entry state Sf; ER = e o R in bf16 (both halves)
+    // R = T diag(beta) (V - diag(Gamma) K S^T) from the bf16 entry state Sf; ER = e o R in bf16.
+    // residual: one half after the other, for callers short of registers.
     __device__ static void residual(const i16x4 (&Sf)[KB], const lds_u8* KR, const lds_u8* vtr, uint32_t vmask,
                                     const lds_f32* cf, const lds_u8* Tfr, f32x4 (&R)[4], i16x4 (&ER)[4]) {
         const RIn<0> in0 = residual_r_in<0>(cf, Tfr);
         const RIn<2> in2 = residual_r_in<2>(cf, Tfr);
         i16x4 Ylo[2], Yhi[2];
-        residual_y<0>(Sf, KR, vtr, vmask, cf, Ylo);
-        residual_y<2>(Sf, KR, vtr, vmask, cf, Yhi);
+        residual_yx<0>(residual_x<0>(Sf, KR, vtr, cf), vmask, Ylo);
+        residual_yx<2>(residual_x<2>(Sf, KR, vtr, cf), vmask, Yhi);
+        residual_ry(Ylo, Yhi, in0, in2, R, ER);
+    }
+    // residual_ahead: every read of both halves issued first; ahead0() runs once the first half's products are
+    // issued and ahead1() once the second half's are (a caller's own reads, which then land while the rest of
+    // the residual computes).
+    template <typename Ahead0, typename Ahead1>
+    __device__ static void residual_ahead(const i16x4 (&Sf)[KB], const lds_u8* KR, const lds_u8* vtr, uint32_t vmask,
+                                          const lds_f32* cf, const lds_u8* Tfr, f32x4 (&R)[4], i16x4 (&ER)[4],
+                                          Ahead0&& ahead0, Ahead1&& ahead1) {
+        const RIn<0> in0 = residual_r_in<0>(cf, Tfr);
+        const RIn<2> in2 = residual_r_in<2>(cf, Tfr);
+        const XIn<0> a0 = x_in<0>(KR, vtr, cf);
+        const XIn<2> a2 = x_in<2>(KR, vtr, cf);
+        __builtin_amdgcn_sched_barrier(0);
+        const XOut<0> x0 = x_mul<0>(a0, Sf);
+        __builtin_amdgcn_sched_barrier(0);
+        ahead0();
+        __builtin_amdgcn_sched_barrier(0);
+        const XOut<2> x2 = x_mul<2>(a2, Sf);
+        __builtin_amdgcn_sched_barrier(0);
+        ahead1();
+        __builtin_amdgcn_sched_barrier(0);
+        i16x4 Ylo[2], Yhi[2];
+        residual_yx<0>(x0, vmask, Ylo);
+        residual_yx<2>(x2, vmask, Yhi);
+        residual_ry(Ylo, Yhi, in0, in2, R, ER);
+    }
+    __device__ static void residual_ry(const i16x4 (&Ylo)[2], const i16x4 (&Yhi)[2], const RIn<0>& in0,
+                                       const RIn<2>& in2, f32x4 (&R)[4], i16x4 (&ER)[4]) {
         const bf16x8 Y01 = cat8(Ylo[0], Ylo[1]), Y23 = cat8(Yhi[0], Yhi[1]);
         f32x4 Rlo[2], Rhi[2];
         i16x4 Elo[2], Ehi[2];
@@ -448,9 +518,10 @@ struct SliceOps {
         for (int i = 0; i < NKT; ++i) {
             const int kt = KT0 + i;
             const int p = kt >> 1, hh = kt & 1;
+            const lds_u8* kb = lds_base(KR + otr(p));
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                Ka[i][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(KR + otr(p) + 8 * hh + u * UST));
+                Ka[i][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kb + 8 * hh + u * UST));
         }
     }
     template <int NKT>
@@ -461,6 +532,18 @@ struct SliceOps {
         for (int i = 0; i < NKT; ++i) acc[i] = mma32(cat8(Ka[i][0], Ka[i][1]), E01, S[i] * gl);
 #pragma unroll
         for (int i = 0; i < NKT; ++i) S[i] = mma32(cat8(Ka[i][2], Ka[i][3]), E23, acc[i]);
+    }
+    // the same, with the K^T fragments of the first and second half of the key tiles in Ka and Kb
+    template <int NKT>
+    __device__ static void update_halves(f32x4 (&S)[NKT], const i16x4 (&ER)[4], const i16x4 (&Ka)[NKT / 2][4],
+                                         const i16x4 (&Kb)[NKT / 2][4], float gl) {
+        const bf16x8 E01 = cat8(ER[0], ER[1]), E23 = cat8(ER[2], ER[3]);
+        auto kf = [&](int i, int u) __attribute__((always_inline)) { return i < NKT / 2 ? Ka[i][u] : Kb[i - NKT / 2][u]; };
+        f32x4 acc[NKT];
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) acc[i] = mma32(cat8(kf(i, 0), kf(i, 1)), E01, S[i] * gl);
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) S[i] = mma32(cat8(kf(i, 2), kf(i, 3)), E23, acc[i]);
     }
     template <int KT0, int NKT>
     __device__ static void update_tiles(f32x4 (&S)[NKT], const i16x4 (&ER)[4], const lds_u8* KR, float gl) {
