@@ -24,6 +24,7 @@
 //   gdn_bwd_dstate_kernel  per (sequence, head, 16-row slice): the reverse chain, storing every chunk's
 //                          exit-state gradient, and dh0
 //   gdn_bwd_grad_kernel    per (chunk, head): dq, dk, dv, dg, dbeta of the chunk
+#include "f32_tiles.h"
 #include "sf_device.h"
 #include "sf_internal.h"
 
@@ -31,7 +32,7 @@ namespace sf {
 namespace {
 
 constexpr int BC = kGdnChunk;
-constexpr int NT = 256;  // threads per workgroup of every backward kernel
+constexpr int NT = f32t::NT;  // threads per workgroup of every backward kernel
 
 // Record of one (chunk, head), floats: T [64][64] | W [64][KD] | Qt [64][KD] | coef [256]:
 // [0,64) G, [64,128) Gamma, [128,192) e, [192,256) beta (padded tokens: g = beta = 0).
@@ -44,63 +45,8 @@ struct BwdRec {
 template <typename ST>
 __device__ __forceinline__ float ld(const ST* p) { return Elem<ST>::to_f(*p); }
 
-// element e of a 16-byte piece holding 8 bf16 or 4 float
-template <typename ST>
-__device__ __forceinline__ ST unit_of(const u128& u, int e) {
-    if constexpr (sizeof(ST) == 2) {
-        const uint32_t w = u[e >> 1];
-        return (ST)((e & 1) ? (w >> 16) : (w & 0xffffu));
-    } else {
-        return __uint_as_float(u[e]);
-    }
-}
-
-// A [ROWS][COLS] tile of ST (row stride ld elements; rows at or past rows_valid read as zero) moved to LDS as
-// float [ROWS][COLS + 1] through registers in 16-byte pieces: load() puts every piece of the thread in flight
-// at once, store() writes them to LDS, so a tile costs one load latency, and a chain can load the next
-// chunk's tiles while it computes on the current ones.
-template <typename ST, int ROWS, int COLS>
-struct Tile {
-    static constexpr int E = 16 / (int)sizeof(ST);
-    static constexpr int PPR = COLS / E;                     // pieces per row
-    static constexpr int PIECES = ROWS * PPR;
-    static constexpr int PER = (PIECES + NT - 1) / NT;
-    static_assert(COLS % E == 0, "tile rows are whole 16-byte pieces");
-    u128 r[PER];
-    __device__ __forceinline__ void load(const ST* __restrict__ base, long ld, int rows_valid) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
-            r[p] = u128{0u, 0u, 0u, 0u};
-            if (idx < PIECES && row < rows_valid) r[p] = *reinterpret_cast<const u128*>(base + row * ld + col);
-        }
-    }
-    __device__ __forceinline__ void store(float* dst) const {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
-            if (idx < PIECES)
-#pragma unroll
-                for (int e = 0; e < E; ++e) dst[row * (COLS + 1) + col + e] = Elem<ST>::to_f(unit_of<ST>(r[p], e));
-        }
-    }
-};
-
-// ---------------------------------------------------------------------------------------------------------
-// Float32 MFMA tile over LDS operands: acc += A(i, k) B(k, j) for one 16x16 tile, k in [k0, k1) (a multiple of 4
-// apart), with A(i, k) = A[i * ars + k * acs] and B(k, j) = B[k * brs + j * bcs] (pointers at the tile origin;
-// the strides give transposed reads for free). Lane (ln, lg) brings A(ln, k + lg) times as (the scale of its A
-// row) and B(k + lg, ln); the C tile holds rows 4 lg + r, column ln (v_mfma_f32_16x16x4_f32).
-// ---------------------------------------------------------------------------------------------------------
-__device__ __forceinline__ f32x4 mm4(const float* A, int ars, int acs, const float* B, int brs, int bcs, int k0, int k1,
-                                     f32x4 acc, float as = 1.f) {
-    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
-    const float* a = A + ln * ars + lg * acs;
-    const float* b = B + lg * brs + ln * bcs;
-    for (int kk = k0; kk < k1; kk += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as * a[kk * acs], b[kk * brs], acc, 0, 0, 0);
-    return acc;
-}
+using f32t::Tile;
+using f32t::mm4;
 
 // ---------------------------------------------------------------------------------------------------------
 // Prep: per (chunk slot, head), on float32 MFMA tiles (wavefront w owns token rows 16 w .. 16 w + 15). G by a wave

@@ -18,6 +18,7 @@
 // Kernels (float32 arithmetic; q, k, v and the output in the input type):
 //   kda_prep_kernel   per (chunk, head): W, U, P, Qg, Kh and Gamma_L into a record
 //   kda_chain_kernel  per (sequence, head, 16-row slice of the state): the state chain and the output
+#include "f32_tiles.h"
 #include "sf_device.h"
 #include "sf_internal.h"
 
@@ -25,7 +26,9 @@ namespace sf {
 namespace {
 
 constexpr int BC = kGdnChunk;
-constexpr int NT = 256;
+constexpr int NT = f32t::NT;
+using f32t::Tile;
+using f32t::mm4;
 
 // Record of one (chunk, head), floats: W [64][KD] | U [64][VD] | P [64][64] | Qg [64][KD] | Kh [64][KD] | Gamma_L [KD]
 template <int KD>
@@ -39,49 +42,16 @@ struct KdaRec {
     static __host__ __device__ size_t floats(int V) { return gl_off(V) + KD; }
 };
 
-// element e of a 16-byte piece holding 8 bf16 or 4 float
-template <typename ST>
-__device__ __forceinline__ ST unit_of(const u128& u, int e) {
-    if constexpr (sizeof(ST) == 2) {
-        const uint32_t w = u[e >> 1];
-        return (ST)((e & 1) ? (w >> 16) : (w & 0xffffu));
-    } else {
-        return __uint_as_float(u[e]);
-    }
-}
-
-// A [ROWS][COLS] tile of ST (row stride ld elements; rows at or past rows_valid read as zero) moved to LDS as
-// float [ROWS][COLS + 1] through registers in 16-byte pieces, all of a thread's pieces in flight at once.
-template <typename ST, int ROWS, int COLS>
-struct Tile {
-    static constexpr int E = 16 / (int)sizeof(ST);
-    static constexpr int PPR = COLS / E;
-    static constexpr int PIECES = ROWS * PPR;
-    static constexpr int PER = (PIECES + NT - 1) / NT;
-    static_assert(COLS % E == 0, "tile rows are whole 16-byte pieces");
-    u128 r[PER];
-    __device__ __forceinline__ void load(const ST* __restrict__ base, long ld, int rows_valid) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
-            r[p] = u128{0u, 0u, 0u, 0u};
-            if (idx < PIECES && row < rows_valid) r[p] = *reinterpret_cast<const u128*>(base + row * ld + col);
-        }
-    }
-    __device__ __forceinline__ void store(float* dst) const {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
-            if (idx < PIECES)
-#pragma unroll
-                for (int e = 0; e < E; ++e) dst[row * (COLS + 1) + col + e] = Elem<ST>::to_f(unit_of<ST>(r[p], e));
-        }
-    }
-};
-
 // ---------------------------------------------------------------------------------------------------------
-// Prep: per (chunk slot, head). The per-channel cumulative gate (one thread per channel), A and P with the
-// pairwise per-channel decays, T by forward substitution (one column per thread), then W, U, Qg, Kh.
+// Prep: per (chunk slot, head), wavefront w owning token rows 16 w .. 16 w + 15; float32 throughout.
+//   G: the per-channel cumulative gate (one thread per channel).
+//   A and P, block row w: the blocks left of the diagonal as float32 MFMA tiles, through the split
+//     exp(G_t - G_s) = exp(G_t - G_r) exp(G_r - G_s) at the last token r of block w - 1 (s <= r < t, so both
+//     factors are at most 1: no overflow for any nonpositive gate); the diagonal block with the pairwise
+//     per-channel decays as they stand.
+//   T = (I + A)^-1 by 16x16 blocks (the four diagonal blocks by column substitution, one wavefront each, then
+//     T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj block diagonal by block diagonal).
+//   W = T diag(beta) (Gamma o K) and U = T diag(beta) V as tiles; Qg, Kh and Gamma_L elementwise.
 // ---------------------------------------------------------------------------------------------------------
 template <typename ST, int KD, int VD>
 __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, const ST* __restrict__ k,
@@ -90,25 +60,29 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
                                                       const int32_t* __restrict__ cu, int T, int H, int nc, float scale,
                                                       float* __restrict__ rec) {
     typedef KdaRec<KD> RL;
-    constexpr int LK = KD + 1, LL = BC + 1, LV = VD + 1;
-    __shared__ float sK[BC * LK], sQ[BC * LK], sG[BC * LK];
-    __shared__ float sA[BC * LL], sT[BC * LL];
-    __shared__ float sB[BC];
-    float* const sV = sQ;  // V rows replace Q rows once Qg and P are formed (VD <= KD)
+    constexpr int LK = KD + 4, LL = BC + 1, LU = 17, NJ = KD / 16, NV = VD / 16;
+    __shared__ __align__(16) float sK[BC * LK];
+    __shared__ __align__(16) float sQ[BC * LK];
+    __shared__ __align__(16) float sG[BC * LK];
+    __shared__ float sA[BC * LL], sT[BC * LL], sP[BC * LL];
+    __shared__ float sB[BC], sU[4 * 16 * LU];
+    float* const sV = sQ;  // V rows (scaled by beta) replace Q rows once Qg is formed (VD <= KD)
     static_assert(VD <= KD, "V rows reuse the Q buffer");
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     int b, t0, L;
     if (!chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
     const long row0 = (long)b * T + t0;
+    Tile<ST, BC, VD> tv;  // V rows: loaded now, stored once the Q rows are no longer read
     {
         Tile<ST, BC, KD> tk, tq;
         Tile<float, BC, KD> tg;
         tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tg.load(g + (row0 * H + h) * (long)KD, (long)H * KD, L);  // padded tokens: g = 0
-        tk.store(sK);
-        tq.store(sQ);
-        tg.store(sG);
+        tv.load(v + (row0 * H + h) * (long)VD, (long)H * VD, L);
+        tk.store(sK, LK);
+        tq.store(sQ, LK);
+        tg.store(sG, LK);
     }
     if (tid < BC) sB[tid] = tid < L ? beta[(row0 + tid) * H + h] : 0.f;
     __syncthreads();
@@ -121,76 +95,165 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
         }
     }
     __syncthreads();
-    float* R = rec + ((size_t)slot * H + h) * RL::floats(VD);
-    // A (strictly lower) into sA and P (lower with the diagonal) into the record; thread's entries (t, s) with
-    // t = tid / 4, s = tid % 4 + 4 j
-    const int t = tid >> 2, q4 = tid & 3;
-    for (int j = 0; j < 16; ++j) {
-        const int s2 = q4 + 4 * j;
-        float a = 0.f, p = 0.f;
-        if (s2 <= t)
-            for (int c = 0; c < KD; ++c) {
-                const float d = __expf(sG[t * LK + c] - sG[s2 * LK + c]) * sK[s2 * LK + c];
-                a += sK[t * LK + c] * d;
-                p += sQ[t * LK + c] * d;
-            }
-        sA[t * LL + s2] = s2 < t ? sB[t] * a : 0.f;
-        R[RL::p_off(VD) + t * BC + s2] = s2 <= t ? scale * p : 0.f;
-    }
-    __syncthreads();
-    // Qg = scale Gamma o Q and Kh = exp(G_L - G) o K to the record, then V rows into the Q buffer
-    for (int i = tid; i < BC * KD; i += NT) {
-        const int tt = i / KD, c = i % KD;
-        const float G = sG[tt * LK + c], GL = sG[(BC - 1) * LK + c];
-        R[RL::q_off(VD) + i] = scale * __expf(G) * sQ[tt * LK + c];
-        R[RL::kh_off(VD) + i] = __expf(GL - G) * sK[tt * LK + c];
-    }
-    if (tid < KD) R[RL::gl_off(VD) + tid] = __expf(sG[(BC - 1) * LK + tid]);
-    if (tid < BC) {
-        // column j = tid of T = (I + A)^-1 (unit lower triangular): x_j = 1, x_t = -sum_{j<=s<t} A_ts x_s
-        const int j = tid;
-        for (int tt = 0; tt < BC; ++tt) {
-            float x = tt == j ? 1.f : 0.f;
-            if (tt > j)
-                for (int s2 = j; s2 < tt; ++s2) x -= sA[tt * LL + s2] * sT[s2 * LL + j];
-            sT[tt * LL + j] = x;
-        }
-    }
-    __syncthreads();
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    // A (strictly lower, beta applied) and P (lower with the diagonal, scale applied), block row w, with the
+    // reference token b = 16 w: exp(G_t - G_s) = exp(G_t - G_b) exp(G_b - G_s). For the blocks left of the
+    // diagonal (s < b <= t) both factors are at most 1. For the diagonal block (b <= s, t) the second factor is
+    // at least 1; it is used when the block's decay range G_b - G_{b+15} is at most 64 on every channel (the
+    // factor then stays below e^64), else the diagonal block takes the pairwise per-channel decays as they stand.
     {
-        Tile<ST, BC, VD> tv;
-        tv.load(v + (row0 * H + h) * (long)VD, (long)H * VD, L);
-        // (the Q rows are no longer read: Qg and P are in the record)
-        float* dst = sV;
+        const int b0 = 16 * w;
+        const float* Gb = sG + b0 * LK;
+        bool wide = false;
+        for (int c = lane; c < KD; c += 64) wide |= Gb[c] - sG[(b0 + 15) * LK + c] > 64.f;
+        const bool fast = __ballot(wide) == 0;  // the same on every lane of the wavefront
+        // All four blocks (w, j) as float32 MFMA tiles, without branches (the blocks right of the diagonal, and
+        // the diagonal one when its range is wide, are formed and dropped; the exponent is clamped at 80 so that
+        // they stay finite). Lane (ln, lg) brings A(t = b + ln, c) and B(c, s = 16 j + ln), c = kk + lg; four
+        // reduction steps per pass, their reads issued together.
+        f32x4 accA[4] = {zero4(), zero4(), zero4(), zero4()}, accP[4] = {zero4(), zero4(), zero4(), zero4()};
+        const float* Kt = sK + (b0 + ln) * LK;
+        const float* Qt = sQ + (b0 + ln) * LK;
+        const float* Gt = sG + (b0 + ln) * LK;
+        for (int k0 = 0; k0 < KD; k0 += 16) {
+            float gb[4], ak[4], aq[4], gt[4], ks[4][4], gs[4][4];
 #pragma unroll
-        for (int p = 0; p < Tile<ST, BC, VD>::PER; ++p) {
-            const int idx = threadIdx.x + NT * p, row = idx / Tile<ST, BC, VD>::PPR,
-                      col = (idx % Tile<ST, BC, VD>::PPR) * Tile<ST, BC, VD>::E;
-            if (idx < Tile<ST, BC, VD>::PIECES)
+            for (int u = 0; u < 4; ++u) {
+                const int c = k0 + 4 * u + lg;
+                gb[u] = Gb[c];
+                ak[u] = Kt[c];
+                aq[u] = Qt[c];
+                gt[u] = Gt[c];
 #pragma unroll
-                for (int e = 0; e < Tile<ST, BC, VD>::E; ++e)
-                    dst[row * LV + col + e] = Elem<ST>::to_f(unit_of<ST>(tv.r[p], e));
+                for (int j = 0; j < 4; ++j) {
+                    ks[j][u] = sK[(16 * j + ln) * LK + c];
+                    gs[j][u] = sG[(16 * j + ln) * LK + c];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float ft = __expf(gt[u] - gb[u]);
+                const float a1 = ak[u] * ft, a2 = aq[u] * ft;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float bs = ks[j][u] * __expf(fminf(gb[u] - gs[j][u], 80.f));
+                    accA[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bs, accA[j], 0, 0, 0);
+                    accP[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, bs, accP[j], 0, 0, 0);
+                }
+            }
         }
+        // the diagonal block with the pairwise decays: lane (ln = s, lg) forms rows t = b + 4 lg + r, four
+        // channels at a time
+        f32x4 da = zero4(), dp = zero4();
+        if (!fast) {
+            const int sd = b0 + ln;
+#pragma unroll 2
+            for (int c = 0; c < KD; c += 4) {
+                const f32x4 ks = *(const f32x4*)(sK + sd * LK + c), gs = *(const f32x4*)(sG + sd * LK + c);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = b0 + 4 * lg + r;
+                    const f32x4 kt = *(const f32x4*)(sK + t * LK + c), qt = *(const f32x4*)(sQ + t * LK + c),
+                                gt = *(const f32x4*)(sG + t * LK + c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // (clamped: only s <= t is kept, where G_t - G_s <= 0)
+                        const float d = __expf(fminf(gt[e] - gs[e], 0.f)) * ks[e];
+                        da[r] += kt[e] * d;
+                        dp[r] += qt[e] * d;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = b0 + 4 * lg + r, s2 = 16 * j + ln;
+                float a = 0.f, pv = 0.f;
+                if (j < w) {
+                    a = accA[j][r];
+                    pv = accP[j][r];
+                } else if (j == w) {
+                    a = s2 < t ? (fast ? accA[j][r] : da[r]) : 0.f;
+                    pv = s2 <= t ? (fast ? accP[j][r] : dp[r]) : 0.f;
+                }
+                sA[t * LL + s2] = sB[t] * a;
+                sP[t * LL + s2] = scale * pv;
+                sT[t * LL + s2] = 0.f;
+            }
     }
     __syncthreads();
-    // W[t][c] = sum_{s<=t} T[t][s] beta_s Gamma_s[c] K[s][c];  U[t][v] = sum_{s<=t} T[t][s] beta_s V[s][v]
-    for (int m = 0; m < KD / 4; ++m) {
-        const int c = q4 + 4 * m;
-        float w = 0.f;
-        for (int s2 = 0; s2 <= t; ++s2) w += sT[t * LL + s2] * sB[s2] * __expf(sG[s2 * LK + c]) * sK[s2 * LK + c];
-        R[RL::w_off() + t * KD + c] = w;
+    float* R = rec + ((size_t)slot * H + h) * RL::floats(VD);
+    if (w == 0) {
+        // T: the four diagonal blocks at once, lane 16 bb + j solving column j of block bb: x_j = 1,
+        // x_i = -sum_{j<=s<i} A_bb[i][s] x_s
+        const int o = 16 * (lane >> 4), j = lane & 15;
+        for (int i = 0; i < 16; ++i) {
+            float x = i == j ? 1.f : 0.f;
+            if (i > j)
+                for (int s2 = j; s2 < i; ++s2) x -= sA[(o + i) * LL + o + s2] * sT[(o + s2) * LL + o + j];
+            sT[(o + i) * LL + o + j] = x;
+        }
+    } else {
+        // wavefronts 1-3: Qg = scale Gamma o Q and Kh = exp(G_L - G) o K to the record, K scaled by beta Gamma
+        // in place (for W), Gamma_L and P to the record
+        const int i0 = tid - 64, NS = NT - 64;
+#pragma unroll 4
+        for (int i = i0; i < BC * KD; i += NS) {
+            const int tt = i / KD, c = i % KD;
+            const float G = sG[tt * LK + c], GL = sG[(BC - 1) * LK + c], kv = sK[tt * LK + c];
+            const float eg = __expf(G);
+            R[RL::q_off(VD) + i] = scale * eg * sQ[tt * LK + c];
+            R[RL::kh_off(VD) + i] = __expf(GL - G) * kv;
+            sK[tt * LK + c] = sB[tt] * eg * kv;
+        }
+        if (i0 < KD) R[RL::gl_off(VD) + i0] = __expf(sG[(BC - 1) * LK + i0]);
+        for (int i = i0; i < BC * BC; i += NS) R[RL::p_off(VD) + i] = sP[(i / BC) * LL + i % BC];
     }
-    for (int m = 0; m < VD / 4; ++m) {
-        const int c = q4 + 4 * m;
-        float u = 0.f;
-        for (int s2 = 0; s2 <= t; ++s2) u += sT[t * LL + s2] * sB[s2] * sV[s2 * LV + c];
-        R[RL::u_off() + t * VD + c] = u;
+    __syncthreads();
+    tv.store(sV, LK);  // (visible after the first barrier below)
+    // T: off-diagonal blocks, one block diagonal dd at a time, block (i, j = i - dd) by wavefront i
+    for (int dd = 1; dd < 4; ++dd) {
+        const int i = w, j = w - dd;
+        if (j >= 0) {
+            // Ub = sum_{kb=j}^{i-1} A_i,kb T_kb,j (16 x 16, k over the tokens of blocks j .. i-1)
+            const f32x4 Uv = mm4(sA + 16 * i * LL + 16 * j, LL, 1, sT + 16 * j * LL + 16 * j, LL, 1, 0, 16 * (i - j), zero4());
+            float* Ub = sU + w * 16 * LU;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ub[(4 * lg + r) * LU + ln] = Uv[r];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wavefront's own Ub tile is in LDS
+            const f32x4 Tv = mm4(sT + 16 * i * LL + 16 * i, LL, 1, Ub, LU, 1, 0, 16, zero4());
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sT[(16 * i + 4 * lg + r) * LL + 16 * j + ln] = -Tv[r];
+        }
+        __syncthreads();
+    }
+    // V rows scaled by beta
+    for (int i = tid; i < BC * VD; i += NT) sV[(i / VD) * LK + i % VD] *= sB[i / VD];
+    __syncthreads();
+    // W = T (beta Gamma o K), U = T (beta V) on the wavefront's row tile (T is zero past column 16 w + 15)
+    const int tr0 = 16 * w + 4 * lg;
+#pragma unroll
+    for (int jc = 0; jc < NJ; ++jc) {
+        const f32x4 Wv = mm4(sT + 16 * w * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[RL::w_off() + (tr0 + r) * KD + 16 * jc + ln] = Wv[r];
+    }
+#pragma unroll
+    for (int jc = 0; jc < NV; ++jc) {
+        const f32x4 Uv = mm4(sT + 16 * w * LL, LL, 1, sV + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[RL::u_off() + (tr0 + r) * VD + 16 * jc + ln] = Uv[r];
     }
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Chain: one 16-row slice of the state of one (sequence, head) through its chunks; the next chunk's record
-// tiles load while the current one computes. Thread owns state entries e = tid + 256 m.
+// Chain: one 16-row slice of the state of one (sequence, head) through its chunks, on float32 MFMA tiles; the
+// next chunk's record tiles load (into registers) while the current one computes. Wavefront w forms token tile w
+// of R = U - W S^T, of Qg S^T and of O = Qg S^T + P R, and holds key tiles JPW w .. JPW w + JPW - 1 of the
+// slice's state S [16][KD] (lane: rows 4 lg + r, key 16 jc + ln) for S <- S diag(Gamma_L) + R^T Kh; the state
+// goes to LDS after each update as the B operand of the next chunk's products.
 // ---------------------------------------------------------------------------------------------------------
 template <typename ST, int KD, int VD>
 __global__ __launch_bounds__(NT) void kda_chain_kernel(const float* __restrict__ h0, const int32_t* __restrict__ cu,
@@ -198,13 +261,17 @@ __global__ __launch_bounds__(NT) void kda_chain_kernel(const float* __restrict__
                                                        int T, int H, int n_seq, int nc, int nvs, ST* __restrict__ out,
                                                        float* __restrict__ ht) {
     typedef KdaRec<KD> RL;
-    constexpr int LK = KD + 1, LL = BC + 1, LV = 17, NE = 16 * KD / NT;
-    __shared__ float sW[BC * LK], sQg[BC * LK], sKh[BC * LK], sP[BC * LL], sU[BC * LV], sR[BC * LV], sS[16 * LK];
-    __shared__ float sGL[KD];
+    constexpr int LK = KD + 4, LL = BC + 1, LV = 17, JPW = KD / 64;
+    __shared__ __align__(16) float sW[BC * LK];
+    __shared__ __align__(16) float sQg[BC * LK];
+    __shared__ __align__(16) float sKh[BC * LK];
+    __shared__ __align__(16) float sS[16 * LK];
+    __shared__ float sP[BC * LL], sU[BC * LV], sR[BC * LV], sGL[KD];
     int chain, vs;
     xcd_split(blockIdx.x, nvs, chain, vs);
     if (chain >= n_seq * H) return;
     const int n = chain / H, h = chain % H, tid = threadIdx.x, v0 = 16 * vs;
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     int b, bos, eos, slot0;
     if (cu) {
         b = 0;
@@ -218,11 +285,14 @@ __global__ __launch_bounds__(NT) void kda_chain_kernel(const float* __restrict__
         slot0 = n * nc;
     }
     const int nch = (eos - bos + BC - 1) / BC;
-    float S[NE];
+    // the wavefront's key tiles of the state, C-tile layout
+    f32x4 S[JPW];
 #pragma unroll
-    for (int m = 0; m < NE; ++m) {
-        const int e = tid + NT * m;
-        S[m] = h0 ? h0[(((size_t)n * H + h) * VD + v0 + e / KD) * KD + e % KD] : 0.f;
+    for (int i = 0; i < JPW; ++i) {
+        const int c = 16 * (JPW * w + i) + ln;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[i][r] = h0 ? h0[(((size_t)n * H + h) * VD + v0 + 4 * lg + r) * KD + c] : 0.f;
     }
     Tile<float, BC, KD> tw, tq, tk;
     Tile<float, BC, BC> tp;
@@ -238,67 +308,47 @@ __global__ __launch_bounds__(NT) void kda_chain_kernel(const float* __restrict__
         gl = tid < KD ? R[RL::gl_off(VD) + tid] : 0.f;
     };
     if (nch > 0) issue(0);
-    const int t = tid >> 2, v4 = (tid & 3) * 4;
+    const int tr0 = 16 * w + 4 * lg;
     for (int ci = 0; ci < nch; ++ci) {
         const long row0 = (long)b * T + bos + (long)ci * BC;
         const int L = min(BC, eos - (bos + ci * BC));
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + NT * m;
-            sS[(e / KD) * LK + e % KD] = S[m];
-        }
-        tw.store(sW);
-        tq.store(sQg);
-        tk.store(sKh);
+        for (int i = 0; i < JPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sS[(4 * lg + r) * LK + 16 * (JPW * w + i) + ln] = S[i][r];
+        tw.store(sW, LK);
+        tq.store(sQg, LK);
+        tk.store(sKh, LK);
         tp.store(sP);
         tu.store(sU);
         if (tid < KD) sGL[tid] = gl;
         __syncthreads();
         if (ci + 1 < nch) issue(ci + 1);
-        // R = U - W S^T and QS = Qg S^T on (token t, values v4 .. v4 + 3)
-        float r[4], qs[4];
+        // token tile w: R = U - W S^T and QS = Qg S^T (B(c, v) = S[v][c])
+        const f32x4 WS = mm4(sW + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
+        const f32x4 QS = mm4(sQg + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            r[j] = sU[t * LV + v4 + j];
-            qs[j] = 0.f;
-        }
-        for (int c = 0; c < KD; ++c) {
-            const float w = sW[t * LK + c], qg = sQg[t * LK + c];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float sv = sS[(v4 + j) * LK + c];
-                r[j] -= w * sv;
-                qs[j] += qg * sv;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sR[t * LV + v4 + j] = r[j];
+        for (int r = 0; r < 4; ++r) sR[(tr0 + r) * LV + ln] = sU[(tr0 + r) * LV + ln] - WS[r];
         __syncthreads();
-        // O = Qg S^T + P R
-        float o[4] = {qs[0], qs[1], qs[2], qs[3]};
-        for (int s2 = 0; s2 <= t; ++s2) {
-            const float p = sP[t * LL + s2];
+        // O = QS + P R on token tile w (P is zero past column 16 w + 15)
+        const f32x4 o = mm4(sP + 16 * w * LL, LL, 1, sR, LV, 1, 0, 16 * (w + 1), QS);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] += p * sR[s2 * LV + v4 + j];
-        }
-        if (t < L)
+        for (int r = 0; r < 4; ++r)
+            if (tr0 + r < L) out[((row0 + tr0 + r) * H + h) * (long)VD + v0 + ln] = Elem<ST>::from_f(o[r]);
+        // S <- S diag(Gamma_L) + R^T Kh on the wavefront's key tiles: A(v, t) = R[t][v], B(t, c) = Kh[t][c]
 #pragma unroll
-            for (int j = 0; j < 4; ++j) out[((row0 + t) * H + h) * (long)VD + v0 + v4 + j] = Elem<ST>::from_f(o[j]);
-        // S <- S diag(Gamma_L) + R^T Kh
-#pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + NT * m, rr = e / KD, c = e % KD;
-            float acc = S[m] * sGL[c];
-            for (int tt = 0; tt < BC; ++tt) acc += sR[tt * LV + rr] * sKh[tt * LK + c];
-            S[m] = acc;
+        for (int i = 0; i < JPW; ++i) {
+            const int jc = JPW * w + i;
+            S[i] = mm4(sR, 1, LV, sKh + 16 * jc, LK, 1, 0, BC, S[i] * sGL[16 * jc + ln]);
         }
         __syncthreads();
     }
     if (ht) {
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            const int e = tid + NT * m;
-            ht[(((size_t)n * H + h) * VD + v0 + e / KD) * KD + e % KD] = S[m];
+        for (int i = 0; i < JPW; ++i) {
+            const int c = 16 * (JPW * w + i) + ln;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ht[(((size_t)n * H + h) * VD + v0 + 4 * lg + r) * KD + c] = S[i][r];
         }
     }
 }

@@ -92,6 +92,19 @@ def test_kda_chunk_strong_decay_fp32(dev, oracle):
     check(o, ht, ro, rh, False, "strong-decay", 1, 300, 2)
 
 
+@pytest.mark.parametrize("shift,label", [(30.0, "every diagonal block pairwise"), (3.6, "mixed")])
+def test_kda_chunk_decay_range_paths(dev, oracle, shift, label):
+    # The prep forms a diagonal 16-token block through a reference token when the block's per-channel decay
+    # range is at most 64 and with the pairwise decays otherwise: g around -30 per token sends every block to
+    # the pairwise form; g around -3.6 puts a block's 15-step ranges near 55, past 64 on some channels of
+    # some blocks, so both forms run within one launch.
+    say(f"case: KDA chunk float32, g = -softplus(N(0,1) + {shift}) ({label})")
+    d = wl.kda_inputs(B=1, T=256, H=2, K=128, V=64, dtype=torch.float32, seed=308 + int(shift), gate_shift=shift,
+                      h0_std=0.1)
+    o, ht, ro, rh = run(dev, oracle, d)
+    check(o, ht, ro, rh, False, f"decay-range {shift}", 1, 256, 2)
+
+
 def test_kda_chunk_packed_bf16(dev, oracle):
     lens = [0, 1, 64, 130, 5, 700, 0, 63]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
