@@ -51,6 +51,23 @@ struct Tile {
                 for (int e = 0; e < E; ++e) dst[row * lds + col + e] = Elem<ST>::to_f(unit_of<ST>(r[p], e));
         }
     }
+    // into rows of stride LDS, a multiple of four floats (dst 16-byte aligned): 16-byte LDS writes
+    template <int LDS>
+    __device__ __forceinline__ void store_rows(float* dst) const {
+        static_assert(LDS % 4 == 0, "16-byte row starts");
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
+            if (idx < PIECES)
+#pragma unroll
+                for (int e = 0; e < E; e += 4) {
+                    f32x4 f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) f[i] = Elem<ST>::to_f(unit_of<ST>(r[p], e + i));
+                    *reinterpret_cast<f32x4*>(dst + row * LDS + col + e) = f;
+                }
+        }
+    }
 };
 
 // Float32 MFMA tile over LDS operands: acc += A(i, k) B(k, j) for one 16x16 tile, k in [k0, k1) (a multiple of 4

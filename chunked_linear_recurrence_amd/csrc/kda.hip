@@ -80,9 +80,9 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
         tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tg.load(g + (row0 * H + h) * (long)KD, (long)H * KD, L);  // padded tokens: g = 0
         tv.load(v + (row0 * H + h) * (long)VD, (long)H * VD, L);
-        tk.store(sK, LK);
-        tq.store(sQ, LK);
-        tg.store(sG, LK);
+        tk.template store_rows<LK>(sK);
+        tq.template store_rows<LK>(sQ);
+        tg.template store_rows<LK>(sG);
     }
     if (tid < BC) sB[tid] = tid < L ? beta[(row0 + tid) * H + h] : 0.f;
     __syncthreads();
@@ -188,13 +188,18 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
     if (w == 0) {
         // T: the four diagonal blocks at once, lane 16 bb + j solving column j of block bb: x_j = 1,
         // x_i = -sum_{j<=s<i} A_bb[i][s] x_s
+        // (the column in registers; x_s = 0 for s < j, so the sums may start at 0)
         const int o = 16 * (lane >> 4), j = lane & 15;
+        float x[16];
+#pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float x = i == j ? 1.f : 0.f;
-            if (i > j)
-                for (int s2 = j; s2 < i; ++s2) x -= sA[(o + i) * LL + o + s2] * sT[(o + s2) * LL + o + j];
-            sT[(o + i) * LL + o + j] = x;
+            float acc = i == j ? 1.f : 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < i; ++s2) acc -= sA[(o + i) * LL + o + s2] * x[s2];
+            x[i] = acc;
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sT[(o + i) * LL + o + j] = x[i];
     } else {
         // wavefronts 1-3: Qg = scale Gamma o Q and Kh = exp(G_L - G) o K to the record, K scaled by beta Gamma
         // in place (for W), Gamma_L and P to the record
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
         for (int i = i0; i < BC * BC; i += NS) R[RL::p_off(VD) + i] = sP[(i / BC) * LL + i % BC];
     }
     __syncthreads();
-    tv.store(sV, LK);  // (visible after the first barrier below)
+    tv.template store_rows<LK>(sV);  // (visible after the first barrier below)
     // T: off-diagonal blocks, one block diagonal dd at a time, block (i, j = i - dd) by wavefront i
     for (int dd = 1; dd < 4; ++dd) {
         const int i = w, j = w - dd;
@@ -232,20 +237,24 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
     // V rows scaled by beta
     for (int i = tid; i < BC * VD; i += NT) sV[(i / VD) * LK + i % VD] *= sB[i / VD];
     __syncthreads();
-    // W = T (beta Gamma o K), U = T (beta V) on the wavefront's row tile (T is zero past column 16 w + 15)
-    const int tr0 = 16 * w + 4 * lg;
+    // W = T (beta Gamma o K), U = T (beta V): wavefront w forms column tiles w, w + 4, .. of every row tile (T is
+    // zero past column 16 ti + 15 of row tile ti), so the four wavefronts share the triangle evenly
 #pragma unroll
-    for (int jc = 0; jc < NJ; ++jc) {
-        const f32x4 Wv = mm4(sT + 16 * w * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+    for (int jc = w; jc < NJ; jc += 4)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) R[RL::w_off() + (tr0 + r) * KD + 16 * jc + ln] = Wv[r];
-    }
+        for (int ti = 0; ti < 4; ++ti) {
+            const f32x4 Wv = mm4(sT + 16 * ti * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (ti + 1), zero4());
 #pragma unroll
-    for (int jc = 0; jc < NV; ++jc) {
-        const f32x4 Uv = mm4(sT + 16 * w * LL, LL, 1, sV + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+            for (int r = 0; r < 4; ++r) R[RL::w_off() + (16 * ti + 4 * lg + r) * KD + 16 * jc + ln] = Wv[r];
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) R[RL::u_off() + (tr0 + r) * VD + 16 * jc + ln] = Uv[r];
-    }
+    for (int jc = w; jc < NV; jc += 4)
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            const f32x4 Uv = mm4(sT + 16 * ti * LL, LL, 1, sV + 16 * jc, LK, 1, 0, 16 * (ti + 1), zero4());
+#pragma unroll
+            for (int r = 0; r < 4; ++r) R[RL::u_off() + (16 * ti + 4 * lg + r) * VD + 16 * jc + ln] = Uv[r];
+        }
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -298,16 +307,26 @@ __global__ __launch_bounds__(NT) void kda_chain_kernel(const float* __restrict__
     Tile<float, BC, BC> tp;
     Tile<float, BC, 16> tu;
     float gl = 0.f;
-    auto issue = [&](int ci) __attribute__((always_inline)) {
-        const float* R = rec + ((size_t)(slot0 + ci) * H + h) * RL::floats(VD);
+    auto recp = [&](int ci) __attribute__((always_inline)) { return rec + ((size_t)(slot0 + ci) * H + h) * RL::floats(VD); };
+    // the next chunk's loads are issued in three groups spread over the step, each ahead of a stretch of
+    // products, so that their issue (throttled by the memory pipeline) overlaps the computation
+    auto issue_w = [&](int ci) __attribute__((always_inline)) {
+        const float* R = recp(ci);
         tw.load(R + RL::w_off(), KD, BC);
-        tq.load(R + RL::q_off(VD), KD, BC);
-        tk.load(R + RL::kh_off(VD), KD, BC);
-        tp.load(R + RL::p_off(VD), BC, BC);
         tu.load(R + RL::u_off() + v0, VD, BC);
         gl = tid < KD ? R[RL::gl_off(VD) + tid] : 0.f;
     };
-    if (nch > 0) issue(0);
+    auto issue_q = [&](int ci) __attribute__((always_inline)) {
+        const float* R = recp(ci);
+        tq.load(R + RL::q_off(VD), KD, BC);
+        tp.load(R + RL::p_off(VD), BC, BC);
+    };
+    auto issue_k = [&](int ci) __attribute__((always_inline)) { tk.load(recp(ci) + RL::kh_off(VD), KD, BC); };
+    if (nch > 0) {
+        issue_w(0);
+        issue_q(0);
+        issue_k(0);
+    }
     const int tr0 = 16 * w + 4 * lg;
     for (int ci = 0; ci < nch; ++ci) {
         const long row0 = (long)b * T + bos + (long)ci * BC;
@@ -316,20 +335,23 @@ __global__ __launch_bounds__(NT) void kda_chain_kernel(const float* __restrict__
         for (int i = 0; i < JPW; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) sS[(4 * lg + r) * LK + 16 * (JPW * w + i) + ln] = S[i][r];
-        tw.store(sW, LK);
-        tq.store(sQg, LK);
-        tk.store(sKh, LK);
+        tw.template store_rows<LK>(sW);
+        tq.template store_rows<LK>(sQg);
+        tk.template store_rows<LK>(sKh);
         tp.store(sP);
         tu.store(sU);
         if (tid < KD) sGL[tid] = gl;
         __syncthreads();
-        if (ci + 1 < nch) issue(ci + 1);
+        const bool more = ci + 1 < nch;
+        if (more) issue_w(ci + 1);
         // token tile w: R = U - W S^T and QS = Qg S^T (B(c, v) = S[v][c])
         const f32x4 WS = mm4(sW + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
+        if (more) issue_q(ci + 1);
         const f32x4 QS = mm4(sQg + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) sR[(tr0 + r) * LV + ln] = sU[(tr0 + r) * LV + ln] - WS[r];
         __syncthreads();
+        if (more) issue_k(ci + 1);
         // O = QS + P R on token tile w (P is zero past column 16 w + 15)
         const f32x4 o = mm4(sP + 16 * w * LL, LL, 1, sR, LV, 1, 0, 16 * (w + 1), QS);
 #pragma unroll
