@@ -481,12 +481,21 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(dom, w.name),
                 "kernel": dom, "avg_us": round(avg_s * 1e6, 2), "algorithmic_bytes": ab}
         if dom == "gdn_bwd_grad":
-            # float32 contractions bind this kernel before HBM does: report that roofline, the HBM one beside it
+            # the gradient kernel's contractions take operands of the input type (float32 or bf16 MFMA): its
+            # roofline is whichever floor is higher, the contractions' at that type's peak or the HBM bytes',
+            # and the other one is reported beside it
             fl = bwd_grad_flops(w)
             tf = fl / avg_s / 1e12
-            roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": F32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / F32_PEAK_TFLOPS, 4), "traffic": roof["traffic"], "kernel": dom,
-                    "avg_us": roof["avg_us"], "algorithmic_flops": fl, "dtype": "f32", "hbm": roof}
+            bf = w.q.dtype == torch.bfloat16
+            peak = BF16_PEAK_TFLOPS if bf else F32_PEAK_TFLOPS
+            mf = {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
+                  "frac": round(tf / peak, 4), "traffic": roof["traffic"], "kernel": dom, "avg_us": roof["avg_us"],
+                  "algorithmic_flops": fl, "dtype": "bf16" if bf else "f32"}
+            if fl / (peak * 1e12) > ab / (HBM_PEAK_GBS * 1e9):
+                mf["hbm"] = roof
+                roof = mf
+            else:
+                roof["mfma"] = mf
     decode = isinstance(w, wl.DecodeWorkload)
     gate = isinstance(w, wl.GateWorkload)
     path_bytes = algorithmic_bytes(w, "decode_path" if decode else "gate_path" if gate else "path")

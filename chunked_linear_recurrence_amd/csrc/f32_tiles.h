@@ -108,5 +108,64 @@ __device__ __forceinline__ f32x4 mm4(const float* A, int ars, int acs, const flo
     return acc;
 }
 
+// The same tile product with bf16 operands (float32 accumulation): the float32 LDS operands are rounded to bf16
+// in registers, 32 reduction steps per v_mfma_f32_16x16x32_bf16 (lane (ln, lg) brings A(ln, k + 8 lg + j) and
+// B(k + 8 lg + j, ln), j = 0..7) and a last 16 by v_mfma_f32_16x16x16_bf16 (A(ln, k + 4 lg + j), j = 0..3). The
+// C tile layout is mm4's. k1 - k0 is a multiple of 16.
+__device__ __forceinline__ f32x4 mm32(const float* A, int ars, int acs, const float* B, int brs, int bcs, int k0,
+                                      int k1, f32x4 acc, float as = 1.f) {
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
+    const float* a = A + ln * ars;
+    const float* b = B + ln * bcs;
+    int kk = k0;
+    for (; kk + 64 <= k1; kk += 64) {
+        f32x8 av[2], bv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                av[u][j] = a[(kk + 32 * u + 8 * lg + j) * acs];
+                bv[u][j] = b[(kk + 32 * u + 8 * lg + j) * brs];
+            }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_convertvector(av[u] * as, bf16x8),
+                                                          __builtin_convertvector(bv[u], bf16x8), acc, 0, 0, 0);
+    }
+    if (kk + 32 <= k1) {
+        f32x8 av, bv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            av[j] = a[(kk + 8 * lg + j) * acs];
+            bv[j] = b[(kk + 8 * lg + j) * brs];
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_convertvector(av * as, bf16x8),
+                                                      __builtin_convertvector(bv, bf16x8), acc, 0, 0, 0);
+        kk += 32;
+    }
+    if (kk + 16 <= k1) {
+        f32x4 av, bv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            av[j] = a[(kk + 4 * lg + j) * acs];
+            bv[j] = b[(kk + 4 * lg + j) * brs];
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Elem<bf16_t>::pack(av * as), Elem<bf16_t>::pack(bv), acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// The tile product in the arithmetic of the input type ST: float32 operands for float32 inputs, bf16 operands
+// for bf16 inputs.
+template <typename ST>
+__device__ __forceinline__ f32x4 mmx(const float* A, int ars, int acs, const float* B, int brs, int bcs, int k0, int k1,
+                                     f32x4 acc, float as = 1.f) {
+    if constexpr (sizeof(ST) == 2)
+        return mm32(A, ars, acs, B, brs, bcs, k0, k1, acc, as);
+    else
+        return mm4(A, ars, acs, B, brs, bcs, k0, k1, acc, as);
+}
+
 }  // namespace f32t
 }  // namespace sf

@@ -47,6 +47,7 @@ __device__ __forceinline__ float ld(const ST* p) { return Elem<ST>::to_f(*p); }
 
 using f32t::Tile;
 using f32t::mm4;
+using f32t::mmx;
 
 // ---------------------------------------------------------------------------------------------------------
 // Prep: per (chunk slot, head), on float32 MFMA tiles (wavefront w owns token rows 16 w .. 16 w + 15). G by a wave
@@ -89,8 +90,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     for (int j = 0; j < 4; ++j) {
         f32x4 kk = zero4(), qk = zero4();
         if (j <= w) {
-            kk = mm4(sK + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, kk);
-            qk = mm4(sQ + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, qk);
+            kk = mmx<ST>(sK + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, kk);
+            qk = mmx<ST>(sQ + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, qk);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     // W = T (beta Gamma K) on the wavefront's row tile (T is zero past column 16 w + 15)
 #pragma unroll
     for (int jc = 0; jc < NJ; ++jc) {
-        const f32x4 Wv = mm4(sT + 16 * w * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+        const f32x4 Wv = mmx<ST>(sT + 16 * w * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             sW[tr[r] * LK + 16 * jc + ln] = Wv[r];
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     // Qt = scale Gamma Q - P W
 #pragma unroll
     for (int jc = 0; jc < NJ; ++jc) {
-        const f32x4 PW = mm4(sP + 16 * w * LL, LL, 1, sW + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+        const f32x4 PW = mmx<ST>(sP + 16 * w * LL, LL, 1, sW + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tr[r], c = 16 * jc + ln;
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states_kernel(const ST* __restrict
         __syncthreads();
         if (ci + 1 < nch) issue(ci + 1);
         // Z = diag(beta) (V - diag(Gamma) K S^T) on token tile w
-        const f32x4 X = mm4(sK + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
+        const f32x4 X = mmx<ST>(sK + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * w + 4 * lg + r;
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states_kernel(const ST* __restrict
         }
         __syncthreads();
         // e R = e T Z (into sV, no longer needed)
-        const f32x4 Rv = mm4(sT + 16 * w * LL, LL, 1, sZ, LV, 1, 0, 16 * (w + 1), zero4());
+        const f32x4 Rv = mmx<ST>(sT + 16 * w * LL, LL, 1, sZ, LV, 1, 0, 16 * (w + 1), zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * w + 4 * lg + r;
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states_kernel(const ST* __restrict
         // S <- Gamma_L S + (e R)^T K on the wavefront's key tiles
         const float gl = sC[64 + BC - 1];
 #pragma unroll
-        for (int i = 0; i < JPW; ++i) S[i] = mm4(sV, 1, LV, sK + 16 * (JPW * w + i), LK, 1, 0, BC, S[i] * gl);
+        for (int i = 0; i < JPW; ++i) S[i] = mmx<ST>(sV, 1, LV, sK + 16 * (JPW * w + i), LK, 1, 0, BC, S[i] * gl);
         __syncthreads();
     }
 }
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate_kernel(const ST* __restrict
         __syncthreads();
         if (ci > 0) issue(ci - 1);
         // Z[r][t] = e_t (dS' K^T)[r][t] on token tile w
-        const f32x4 Zt = mm4(sD, LK, 1, sK + 16 * w * LK, 1, LK, 0, KD, zero4());
+        const f32x4 Zt = mmx<ST>(sD, LK, 1, sK + 16 * w * LK, 1, LK, 0, KD, zero4());
         const float et = sC[128 + 16 * w + ln];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sZ[(4 * lg + r) * LZ + 16 * w + ln] = et * Zt[r];
@@ -338,8 +339,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate_kernel(const ST* __restrict
 #pragma unroll
         for (int i = 0; i < JPW; ++i) {
             const int jc = JPW * w + i;
-            const f32x4 a = mm4(sO, 1, LV, sQt + 16 * jc, LK, 1, 0, BC, dS[i] * gl);
-            const f32x4 zw = mm4(sZ, LZ, 1, sW + 16 * jc, LK, 1, 0, BC, zero4());
+            const f32x4 a = mmx<ST>(sO, 1, LV, sQt + 16 * jc, LK, 1, 0, BC, dS[i] * gl);
+            const f32x4 zw = mmx<ST>(sZ, LZ, 1, sW + 16 * jc, LK, 1, 0, BC, zero4());
             dS[i] = a - zw;
         }
         __syncthreads();
@@ -418,8 +419,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
     for (int j = 0; j < 4; ++j) {
         f32x4 qk = zero4(), kk = zero4();
         if (j <= w) {
-            qk = mm4(sQ + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, qk);
-            kk = mm4(sK + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, kk);
+            qk = mmx<ST>(sQ + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, qk);
+            kk = mmx<ST>(sK + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, kk);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -456,9 +457,9 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
         if (vs + 1 < nvs) issue(vs + 1);
         __syncthreads();
         // X = K S^T, QS = Q S^T, KdS = K dS'^T on (token tile w, the slice's 16 values)
-        const f32x4 X = mm4(sK + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
-        const f32x4 QS = mm4(sQ + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
-        const f32x4 KdS = mm4(sK + 16 * w * LK, LK, 1, sD, 1, LK, 0, KD, zero4());
+        const f32x4 X = mmx<ST>(sK + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
+        const f32x4 QS = mmx<ST>(sQ + 16 * w * LK, LK, 1, sS, 1, LK, 0, KD, zero4());
+        const f32x4 KdS = mmx<ST>(sK + 16 * w * LK, LK, 1, sD, 1, LK, 0, KD, zero4());
         float Y[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -468,8 +469,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
         }
         __syncthreads();
         // R = T Z;  dR = P^T dO + e KdS
-        const f32x4 R = mm4(sT + 16 * w * LL, LL, 1, sZ, LV, 1, 0, 16 * (w + 1), zero4());
-        const f32x4 dRp = mm4(sP + 16 * w, 1, LL, sO, LV, 1, 16 * w, BC, zero4());
+        const f32x4 R = mmx<ST>(sT + 16 * w * LL, LL, 1, sZ, LV, 1, 0, 16 * (w + 1), zero4());
+        const f32x4 dRp = mmx<ST>(sP + 16 * w, 1, LL, sO, LV, 1, 16 * w, BC, zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float dr = dRp[r] + ee[r] * KdS[r];
@@ -479,7 +480,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
         }
         __syncthreads();
         // dZ = T^T dR; dbeta, dY = dV, dX = -Gamma dY; dP += dO R^T, dT += dR Z^T
-        const f32x4 dZ = mm4(sT + 16 * w, 1, LL, sdR, LV, 1, 16 * w, BC, zero4());
+        const f32x4 dZ = mmx<ST>(sT + 16 * w, 1, LL, sdR, LV, 1, 16 * w, BC, zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             pB[r] += Y[r] * dZ[r];
@@ -490,17 +491,17 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            aP[j] = mm4(sO + 16 * w * LV, LV, 1, sR + 16 * j * LV, 1, LV, 0, 16, aP[j]);
-            aT[j] = mm4(sdR + 16 * w * LV, LV, 1, sZ + 16 * j * LV, 1, LV, 0, 16, aT[j]);
+            aP[j] = mmx<ST>(sO + 16 * w * LV, LV, 1, sR + 16 * j * LV, 1, LV, 0, 16, aP[j]);
+            aT[j] = mmx<ST>(sdR + 16 * w * LV, LV, 1, sZ + 16 * j * LV, 1, LV, 0, 16, aT[j]);
         }
         for (int i = tid; i < 16 * KD; i += NT) pGL += sS[(i / KD) * LK + i % KD] * sD[(i / KD) * LK + i % KD];
         __syncthreads();
         // dq += scale Gamma dO S;  dk += dX S + e R dS'
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            aQ[j] = mm4(sO + 16 * w * LV, LV, 1, sS + 16 * j, LK, 1, 0, 16, aQ[j], gq_a);
-            aK[j] = mm4(sdX + 16 * w * LV, LV, 1, sS + 16 * j, LK, 1, 0, 16, aK[j]);
-            aK[j] = mm4(sR + 16 * w * LV, LV, 1, sD + 16 * j, LK, 1, 0, 16, aK[j], e_a);
+            aQ[j] = mmx<ST>(sO + 16 * w * LV, LV, 1, sS + 16 * j, LK, 1, 0, 16, aQ[j], gq_a);
+            aK[j] = mmx<ST>(sdX + 16 * w * LV, LV, 1, sS + 16 * j, LK, 1, 0, 16, aK[j]);
+            aK[j] = mmx<ST>(sR + 16 * w * LV, LV, 1, sD + 16 * j, LK, 1, 0, 16, aK[j], e_a);
         }
         __syncthreads();
     }
@@ -512,7 +513,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
     __syncthreads();
     f32x4 U[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) U[j] = mm4(sdT + 16 * w * LL, LL, 1, sT + 16 * j * LL, 1, LL, 0, 16 * (j + 1), zero4());
+    for (int j = 0; j < 4; ++j) U[j] = mmx<ST>(sdT + 16 * w * LL, LL, 1, sT + 16 * j * LL, 1, LL, 0, 16 * (j + 1), zero4());
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         f32x4 dA = zero4();
-        if (j <= w) dA = mm4(sT + 16 * w, 1, LL, sdT + 16 * j, LL, 1, 16 * w, BC, dA);
+        if (j <= w) dA = mmx<ST>(sT + 16 * w, 1, LL, sdT + 16 * j, LL, 1, 16 * w, BC, dA);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tr[r], s2 = 16 * j + ln;
@@ -552,10 +553,10 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
     // dq += (scale D o dP) K;  dk += (scale D o dP)^T Q + F K + F^T K
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        aQ[j] = mm4(sDP + 16 * w * LL, LL, 1, sK + 16 * j, LK, 1, 0, 16 * (w + 1), aQ[j]);
-        aK[j] = mm4(sDP + 16 * w, 1, LL, sQ + 16 * j, LK, 1, 16 * w, BC, aK[j]);
-        aK[j] = mm4(sdT + 16 * w * LL, LL, 1, sK + 16 * j, LK, 1, 0, 16 * (w + 1), aK[j]);
-        aK[j] = mm4(sdT + 16 * w, 1, LL, sK + 16 * j, LK, 1, 16 * w, BC, aK[j]);
+        aQ[j] = mmx<ST>(sDP + 16 * w * LL, LL, 1, sK + 16 * j, LK, 1, 0, 16 * (w + 1), aQ[j]);
+        aK[j] = mmx<ST>(sDP + 16 * w, 1, LL, sQ + 16 * j, LK, 1, 16 * w, BC, aK[j]);
+        aK[j] = mmx<ST>(sdT + 16 * w * LL, LL, 1, sK + 16 * j, LK, 1, 0, 16 * (w + 1), aK[j]);
+        aK[j] = mmx<ST>(sdT + 16 * w, 1, LL, sK + 16 * j, LK, 1, 16 * w, BC, aK[j]);
     }
     // row sums over the 16 lanes of each row group; <dS', S> over the workgroup
 #pragma unroll
