@@ -92,13 +92,15 @@ def algorithmic_bytes(w, kernel):
             return qk + vo // 2 + gb
         if kernel == "kda_chain":
             return vo // 2 + states
+    if kernel == "gdn_prep":                      # Pre reads k, the gate and beta
+        return qk // 2 + gb
+    if kernel == "gdn_summary_chain":             # k, v in; each segment's M [K][K] and S_ext [V][K] out
+        return qk // 2 + vo // 2 + w.B * w.n_seg * w.H * (w.K * w.K + w.V * w.K) * 4
     if w.name in ("recurrent_gdn", "paged_gdn", "recurrent_kda"):   # every slot read and written (float32 pool)
         states = 2 * w.N * w.H * w.V * w.K * w.meta["pool"].element_size()
         return qk + vo + states + (0 if kernel in ("gdn_chain", "gdn_chain_slice") else gb)
     if kernel in ("gdn_chain", "gdn_chain_slice", "gla_chain"):
         return qk + vo + states
-    if kernel == "gdn_prep":
-        return qk + gb
     return qk + vo + gb + states      # whole path
 
 
