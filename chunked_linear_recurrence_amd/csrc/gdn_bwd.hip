@@ -382,7 +382,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
     float* const sdX = sdR + BC * LV;   // [64][LV] dX
     float* const sdT = sX;              // [64][LL] after the slices: dT, then U = dT T^T, then F
     float* const sDP = sX + BC * LL;    // [64][LL] after the slices: scale D o dP
-    __shared__ float sDG[BC], sEE[BC], sRed[NT / 64];
+    __shared__ float sDG[BC], sEE[BC], sRed[NT / 64], sCol[NT];
 
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     int b, t0, L;
@@ -587,14 +587,21 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
                 dk[o] = Elem<ST>::from_f(aK[j][r]);
             }
     __syncthreads();
+    {
+        // column sums of the gate terms: wavefront w over rows 16 w .. 16 w + 15, lane = column
+        float part = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) part += sKK[(16 * w + tt) * LL + lane];
+        sCol[tid] = part;
+    }
+    __syncthreads();
     if (tid < BC) {
-        float col = 0.f;
-        for (int tt = 0; tt < BC; ++tt) col += sKK[tt * LL + tid];
+        const float col = (sCol[tid] + sCol[64 + tid]) + (sCol[128 + tid] + sCol[192 + tid]);
         float dG = sDG[tid] - col;
+        // G_L (token 63: padded tokens repeat the last real G) also carries e's and Gamma_L's terms
+        float se = sEE[tid];
+        for (int o = 1; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
         if (tid == BC - 1) {
-            // G_L (token 63: padded tokens repeat the last real G) also carries e's and Gamma_L's terms
-            float se = 0.f;
-            for (int tt = 0; tt < BC; ++tt) se += sEE[tt];
             float gsum = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NT / 64; ++ww) gsum += sRed[ww];
