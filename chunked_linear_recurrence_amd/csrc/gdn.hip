@@ -27,8 +27,9 @@
 //         gdn_chain_slice_kernel       the chain and the output, one workgroup per
 //                                16-row state slice, P formed on chip
 //                                (launches with at most two slices per CU)
-//         gdn_chain_head_kernel  the same per (sequence, head) (larger
-//                                launches, and the summary pass)
+//         gdn_chain_head_kernel  the same per (sequence, head) and group of 4
+//                                or 8 slices (larger launches, and the
+//                                summary pass)
 //   f32   gdn_prep_kernel + gdn_chain_kernel
 // The bf16 kernels take every per-chunk step from gdn_steps.h, so a
 // sequence's results are the same bits whichever of them runs it.
@@ -587,14 +588,16 @@ __global__ __launch_bounds__(64 * NW) void gdn_chain_kernel(
 //    LDS (gdn_steps.h form_p) while the slice wavefronts form X, Y and R, once for the eight slices.
 // One workgroup barrier per chunk (two in the output pass: P_c is complete before the outputs).
 // ---------------------------------------------------------------------------
-template <int KD, bool SUMMARY>
+template <int KD, bool SUMMARY, int NCW_ = 8>
 struct HeadLds {
     typedef RowBlock<KD> RBk;
     static constexpr int KP = KD / 32, KB = KD / 16;
     static constexpr int SPW = SUMMARY ? 2 : 1;                        // slices per slice wavefront
-    static constexpr int NCW = 8;                                      // slice wavefronts
+    static constexpr int NCW = SUMMARY ? 8 : NCW_;                     // slice wavefronts
+    static constexpr int NPW = SUMMARY ? 0 : 2;                        // wavefronts forming P
     static constexpr int NS = NCW * SPW;                               // slices per workgroup
-    static constexpr int NVS = 8;                                      // V slices held (V <= 128)
+    static constexpr int NVS = SUMMARY ? 8 : NS;                       // V slices held (V <= 128)
+    static constexpr int THREADS = 64 * (NCW + 2 + NPW);
     static constexpr int OFF_K = 0;                                    // K rows (RowBlock)
     static constexpr int OFF_Q = OFF_K + RBk::BYTES;                   // Q rows (RowBlock)
     static constexpr int OFF_T = OFF_Q + (SUMMARY ? 0 : RBk::BYTES);   // kTriFrags fragments of 1 KB
@@ -607,13 +610,13 @@ struct HeadLds {
     static_assert(BYTES <= 160 * 1024, "LDS plan exceeds the CU's 160 KB");
 };
 
-template <int KD, bool SUMMARY>
-__global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
+template <int KD, bool SUMMARY, int NCW_>
+__global__ __launch_bounds__((HeadLds<KD, SUMMARY, NCW_>::THREADS)) void gdn_chain_head_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ h0, const int32_t* __restrict__ cu, const int* __restrict__ chunk_off,
     const uint8_t* __restrict__ fac, int T, int H, int HK, int V, int n_seq, int nc, int ngrp,
     float scale, bf16_t* __restrict__ out, float* __restrict__ ht, float* __restrict__ Mout) {
-    typedef HeadLds<KD, SUMMARY> SM;
+    typedef HeadLds<KD, SUMMARY, NCW_> SM;
     typedef RowBlock<KD> RBk;
     typedef Elem<bf16_t> El;
     constexpr int KP = SM::KP, KB = SM::KB, NS = SM::NS, SPW = SM::SPW, NCW = SM::NCW;
@@ -708,7 +711,7 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
                     f32x4 R[4];
                     i16x4 ER[4];
                     Ops::residual(Sf, KR, B + off_v, vmask, cf, B + SM::OFF_T, R, ER);
-                    barrier();  // P_c complete (wavefront 10)
+                    barrier();  // P_c complete (the P wavefronts)
                     const int t0 = bos + c * GC, L = min(GC, eos - t0);
                     i16x4 Rb[4];
 #pragma unroll
@@ -932,7 +935,7 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
             barrier();
         }
     } else {
-        // ================= P_c for the output pass: one wavefront =================
+        // ================= P_c for the output pass: two wavefronts, block rows {0, 3} and {1, 2} =================
         // P^T tiles with K rows as A (rows s) and Q rows as B (columns t): the C tile holds, for lane
         // (ln, lg), P[16 ti + ln][16 tj + 4 lg + r], which is fragment (ti, tj / 2)'s lane content
         // (first or second half), the B operand that pairs with the R fragments of the same tokens.
@@ -941,7 +944,10 @@ __global__ __launch_bounds__(SUMMARY ? 640 : 704) void gdn_chain_head_kernel(
             barrier();
             for (int c = 0; c < nch; ++c) {
                 lds_u8* B = buf(c);
-                form_p<KD, 0xF>(B + SM::OFF_K, B + SM::OFF_Q, (const lds_f32*)(B + SM::OFF_C), scale, B + SM::OFF_P);
+                if (wave == NCW + 2)
+                    form_p<KD, 0x9>(B + SM::OFF_K, B + SM::OFF_Q, (const lds_f32*)(B + SM::OFF_C), scale, B + SM::OFF_P);
+                else
+                    form_p<KD, 0x6>(B + SM::OFF_K, B + SM::OFF_Q, (const lds_f32*)(B + SM::OFF_C), scale, B + SM::OFF_P);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 barrier();  // P_c complete
                 barrier();  // end of the step
@@ -1264,18 +1270,25 @@ static hipError_t run_gdn_bf16(int mode, const bf16_t* q, const bf16_t* k, const
         timing_end(s);
         return hipGetLastError();
     }
-    // slices per workgroup: the output pass's 8, the summary pass's 16 (all of a head's V + K rows)
+    // slices per workgroup: the summary pass's 16 (all of a head's V + K rows); the output pass's 4 for packed
+    // input, whose longest sequences set the time (smaller workgroups step faster), else 8 (one workgroup per
+    // head keeps equal-length chains to one pass over the CUs). Every slice runs the same steps either way.
     const int rows = mode == 0 ? V : V + KD;
-    const int ns = mode == 0 ? HeadLds<KD, false>::NS : HeadLds<KD, true>::NS;
+    const bool four = mode == 0 && cu != nullptr;
+    const int ns = mode != 0 ? HeadLds<KD, true>::NS : four ? HeadLds<KD, false, 4>::NS : HeadLds<KD, false, 8>::NS;
     const int ngrp = (rows / 16 + ns - 1) / ns;
     const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * ngrp);
     if (mode == 0) {
         timing_begin("gdn_chain", s);
-        gdn_chain_head_kernel<KD, false><<<grid, 704, 0, s>>>(q, k, v, h0, cu, ws.chunk_off, ws.factors, T, H, HK, V, N,
-                                                              nc, ngrp, scale, out, ht, nullptr);
+        if (four)
+            gdn_chain_head_kernel<KD, false, 4><<<grid, HeadLds<KD, false, 4>::THREADS, 0, s>>>(
+                q, k, v, h0, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, ngrp, scale, out, ht, nullptr);
+        else
+            gdn_chain_head_kernel<KD, false, 8><<<grid, HeadLds<KD, false, 8>::THREADS, 0, s>>>(
+                q, k, v, h0, cu, ws.chunk_off, ws.factors, T, H, HK, V, N, nc, ngrp, scale, out, ht, nullptr);
     } else {
         timing_begin("gdn_summary_chain", s);
-        gdn_chain_head_kernel<KD, true><<<grid, 640, 0, s>>>(q, k, v, nullptr, cu, ws.chunk_off, ws.factors, T, H, HK,
+        gdn_chain_head_kernel<KD, true, 8><<<grid, HeadLds<KD, true>::THREADS, 0, s>>>(q, k, v, nullptr, cu, ws.chunk_off, ws.factors, T, H, HK,
                                                              V, N, nc, ngrp, scale, nullptr, ht, Mout);
     }
     timing_end(s);
