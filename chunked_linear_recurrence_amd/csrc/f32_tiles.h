@@ -51,6 +51,16 @@ struct Tile {
                 for (int e = 0; e < E; ++e) dst[row * lds + col + e] = Elem<ST>::to_f(unit_of<ST>(r[p], e));
         }
     }
+    // the pieces as they are (no conversion) into rows of stride LDS elements of ST, a multiple of 16 bytes
+    template <int LDS>
+    __device__ __forceinline__ void store_raw(ST* dst) const {
+        static_assert(LDS * sizeof(ST) % 16 == 0, "16-byte row starts");
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
+            if (idx < PIECES) *reinterpret_cast<u128*>(dst + row * LDS + col) = r[p];
+        }
+    }
     // into rows of stride LDS, a multiple of four floats (dst 16-byte aligned): 16-byte LDS writes
     template <int LDS>
     __device__ __forceinline__ void store_rows(float* dst) const {
@@ -153,6 +163,23 @@ __device__ __forceinline__ f32x4 mm32(const float* A, int ars, int acs, const fl
         }
         acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Elem<bf16_t>::pack(av * as), Elem<bf16_t>::pack(bv), acc, 0, 0, 0);
     }
+    return acc;
+}
+
+// bf16 tile product from bf16 LDS operands: acc += A(i, k) B(k, j), A row-major (A[i * lda + k]) and B given by
+// its transpose (Bt[j * ldb + k]); k in [k0, k1), k1 - k0 a multiple of 16, lda and ldb multiples of 8. Lane
+// (ln, lg) reads 8 consecutive k of its A row and of its Bt row with one 16-byte read each.
+__device__ __forceinline__ f32x4 mmb(const bf16_t* A, int lda, const bf16_t* Bt, int ldb, int k0, int k1, f32x4 acc) {
+    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
+    const bf16_t* a = A + ln * lda;
+    const bf16_t* b = Bt + ln * ldb;
+    int kk = k0;
+    for (; kk + 32 <= k1; kk += 32)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(a + kk + 8 * lg),
+                                                      *reinterpret_cast<const bf16x8*>(b + kk + 8 * lg), acc, 0, 0, 0);
+    if (kk + 16 <= k1)
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(*reinterpret_cast<const i16x4*>(a + kk + 4 * lg),
+                                                        *reinterpret_cast<const i16x4*>(b + kk + 4 * lg), acc, 0, 0, 0);
     return acc;
 }
 

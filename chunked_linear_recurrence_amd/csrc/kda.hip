@@ -42,6 +42,20 @@ struct KdaRec {
     static __host__ __device__ size_t floats(int V) { return gl_off(V) + KD; }
 };
 
+// Record of one (chunk, head) for bf16 input, bytes, inside the float32 record's footprint: W [64][KD] bf16 |
+// Qg [64][KD] bf16 | Kh^T [KD][64] bf16 | P [64][64] bf16 | U [64][VD] float | Gamma_L [KD] float. The chain's
+// products take bf16 operands, so the factors are stored as such (U stays float32: it enters R as it is).
+template <int KD>
+struct KdaRec16 {
+    static constexpr size_t W_OFF = 0;
+    static constexpr size_t Q_OFF = W_OFF + (size_t)BC * KD * 2;
+    static constexpr size_t KT_OFF = Q_OFF + (size_t)BC * KD * 2;
+    static constexpr size_t P_OFF = KT_OFF + (size_t)KD * BC * 2;
+    static constexpr size_t U_OFF = P_OFF + (size_t)BC * BC * 2;
+    static constexpr __host__ __device__ size_t gl_off(int V) { return U_OFF + (size_t)BC * V * 4; }
+    static constexpr __host__ __device__ size_t bytes(int V) { return gl_off(V) + (size_t)KD * 4; }
+};
+
 // ---------------------------------------------------------------------------------------------------------
 // Prep: per (chunk slot, head), wavefront w owning token rows 16 w .. 16 w + 15; float32 throughout.
 //   G: the per-channel cumulative gate (one thread per channel).
@@ -115,6 +129,54 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
         const float* Kt = sK + (b0 + ln) * LK;
         const float* Qt = sQ + (b0 + ln) * LK;
         const float* Gt = sG + (b0 + ln) * LK;
+        if constexpr (sizeof(ST) == 2) {
+            // bf16 input: the decayed factors rounded to bf16, 32 channels per v_mfma_f32_16x16x32_bf16 (lane
+            // (ln, lg) brings channels k0 + 8 lg .. + 7)
+            typedef float f32x8 __attribute__((ext_vector_type(8)));
+            for (int k0 = 0; k0 < KD; k0 += 32) {
+                const int c0 = k0 + 8 * lg;
+                f32x8 gb, ak, aq, gt, ks[4], gs[4];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const f32x4 g4 = *(const f32x4*)(Gb + c0 + 4 * hf), k4 = *(const f32x4*)(Kt + c0 + 4 * hf),
+                                q4 = *(const f32x4*)(Qt + c0 + 4 * hf), t4 = *(const f32x4*)(Gt + c0 + 4 * hf);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        gb[4 * hf + e] = g4[e];
+                        ak[4 * hf + e] = k4[e];
+                        aq[4 * hf + e] = q4[e];
+                        gt[4 * hf + e] = t4[e];
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x4 kk4 = *(const f32x4*)(sK + (16 * j + ln) * LK + c0 + 4 * hf),
+                                    gg4 = *(const f32x4*)(sG + (16 * j + ln) * LK + c0 + 4 * hf);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            ks[j][4 * hf + e] = kk4[e];
+                            gs[j][4 * hf + e] = gg4[e];
+                        }
+                    }
+                }
+                f32x8 a1, a2;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float ft = __expf(gt[e] - gb[e]);
+                    a1[e] = ak[e] * ft;
+                    a2[e] = aq[e] * ft;
+                }
+                const bf16x8 A1 = __builtin_convertvector(a1, bf16x8), A2 = __builtin_convertvector(a2, bf16x8);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f32x8 bs;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bs[e] = ks[j][e] * __expf(fminf(gb[e] - gs[j][e], 80.f));
+                    const bf16x8 Bs = __builtin_convertvector(bs, bf16x8);
+                    accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Bs, accA[j], 0, 0, 0);
+                    accP[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, Bs, accP[j], 0, 0, 0);
+                }
+            }
+        } else
         for (int k0 = 0; k0 < KD; k0 += 16) {
             float gb[4], ak[4], aq[4], gt[4], ks[4][4], gs[4][4];
 #pragma unroll
@@ -184,7 +246,12 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
             }
     }
     __syncthreads();
+    constexpr bool B16 = sizeof(ST) == 2;
+    typedef KdaRec16<KD> R16;
     float* R = rec + ((size_t)slot * H + h) * RL::floats(VD);
+    uint8_t* const Rb = reinterpret_cast<uint8_t*>(R);  // the bf16 record's bytes
+    static_assert(KdaRec16<KD>::bytes(VD) <= (3 * BC * KD + BC * VD + BC * BC + KD) * sizeof(float),
+                  "the bf16 record fits in the float32 record's footprint");
     if (w == 0) {
         // T: the four diagonal blocks at once, lane 16 bb + j solving column j of block bb: x_j = 1,
         // x_i = -sum_{j<=s<i} A_bb[i][s] x_s
@@ -204,17 +271,29 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
         // wavefronts 1-3: Qg = scale Gamma o Q and Kh = exp(G_L - G) o K to the record, K scaled by beta Gamma
         // in place (for W), Gamma_L and P to the record
         const int i0 = tid - 64, NS = NT - 64;
+        if constexpr (B16) {
+            // (Kh^T and the scaled K follow once the solve no longer holds the wavefronts apart)
 #pragma unroll 4
-        for (int i = i0; i < BC * KD; i += NS) {
-            const int tt = i / KD, c = i % KD;
-            const float G = sG[tt * LK + c], GL = sG[(BC - 1) * LK + c], kv = sK[tt * LK + c];
-            const float eg = __expf(G);
-            R[RL::q_off(VD) + i] = scale * eg * sQ[tt * LK + c];
-            R[RL::kh_off(VD) + i] = __expf(GL - G) * kv;
-            sK[tt * LK + c] = sB[tt] * eg * kv;
+            for (int i = i0; i < BC * KD; i += NS) {
+                const int tt = i / KD, c = i % KD;
+                reinterpret_cast<bf16_t*>(Rb + R16::Q_OFF)[i] = f2bf(scale * __expf(sG[tt * LK + c]) * sQ[tt * LK + c]);
+            }
+            if (i0 < KD) reinterpret_cast<float*>(Rb + R16::gl_off(VD))[i0] = __expf(sG[(BC - 1) * LK + i0]);
+            for (int i = i0; i < BC * BC; i += NS)
+                reinterpret_cast<bf16_t*>(Rb + R16::P_OFF)[i] = f2bf(sP[(i / BC) * LL + i % BC]);
+        } else {
+#pragma unroll 4
+            for (int i = i0; i < BC * KD; i += NS) {
+                const int tt = i / KD, c = i % KD;
+                const float G = sG[tt * LK + c], GL = sG[(BC - 1) * LK + c], kv = sK[tt * LK + c];
+                const float eg = __expf(G);
+                R[RL::q_off(VD) + i] = scale * eg * sQ[tt * LK + c];
+                R[RL::kh_off(VD) + i] = __expf(GL - G) * kv;
+                sK[tt * LK + c] = sB[tt] * eg * kv;
+            }
+            if (i0 < KD) R[RL::gl_off(VD) + i0] = __expf(sG[(BC - 1) * LK + i0]);
+            for (int i = i0; i < BC * BC; i += NS) R[RL::p_off(VD) + i] = sP[(i / BC) * LL + i % BC];
         }
-        if (i0 < KD) R[RL::gl_off(VD) + i0] = __expf(sG[(BC - 1) * LK + i0]);
-        for (int i = i0; i < BC * BC; i += NS) R[RL::p_off(VD) + i] = sP[(i / BC) * LL + i % BC];
     }
     __syncthreads();
     tv.template store_rows<LK>(sV);  // (visible after the first barrier below)
@@ -236,6 +315,22 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
     }
     // V rows scaled by beta
     for (int i = tid; i < BC * VD; i += NT) sV[(i / VD) * LK + i % VD] *= sB[i / VD];
+    if constexpr (B16) {
+        // Kh^T = (exp(G_L - G) o K)^T, consecutive threads along the tokens of one channel (contiguous stores)
+#pragma unroll 4
+        for (int i = tid; i < BC * KD; i += NT) {
+            const int c = i / BC, tt = i % BC;
+            reinterpret_cast<bf16_t*>(Rb + R16::KT_OFF)[i] =
+                f2bf(__expf(sG[(BC - 1) * LK + c] - sG[tt * LK + c]) * sK[tt * LK + c]);
+        }
+        __syncthreads();
+        // K scaled by beta Gamma in place, for W
+#pragma unroll 4
+        for (int i = tid; i < BC * KD; i += NT) {
+            const int tt = i / KD, c = i % KD;
+            sK[tt * LK + c] *= sB[tt] * __expf(sG[tt * LK + c]);
+        }
+    }
     __syncthreads();
     // W = T (beta Gamma o K), U = T (beta V): wavefront w forms column tiles w, w + 4, .. of every row tile (T is
     // zero past column 16 ti + 15 of row tile ti), so the four wavefronts share the triangle evenly
@@ -243,17 +338,29 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
     for (int jc = w; jc < NJ; jc += 4)
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
-            const f32x4 Wv = mm4(sT + 16 * ti * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (ti + 1), zero4());
+            const f32x4 Wv = f32t::mmx<ST>(sT + 16 * ti * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (ti + 1), zero4());
 #pragma unroll
-            for (int r = 0; r < 4; ++r) R[RL::w_off() + (16 * ti + 4 * lg + r) * KD + 16 * jc + ln] = Wv[r];
+            for (int r = 0; r < 4; ++r) {
+                const int o = (16 * ti + 4 * lg + r) * KD + 16 * jc + ln;
+                if constexpr (B16)
+                    reinterpret_cast<bf16_t*>(Rb + R16::W_OFF)[o] = f2bf(Wv[r]);
+                else
+                    R[RL::w_off() + o] = Wv[r];
+            }
         }
 #pragma unroll
     for (int jc = w; jc < NV; jc += 4)
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
-            const f32x4 Uv = mm4(sT + 16 * ti * LL, LL, 1, sV + 16 * jc, LK, 1, 0, 16 * (ti + 1), zero4());
+            const f32x4 Uv = f32t::mmx<ST>(sT + 16 * ti * LL, LL, 1, sV + 16 * jc, LK, 1, 0, 16 * (ti + 1), zero4());
 #pragma unroll
-            for (int r = 0; r < 4; ++r) R[RL::u_off() + (16 * ti + 4 * lg + r) * VD + 16 * jc + ln] = Uv[r];
+            for (int r = 0; r < 4; ++r) {
+                const int o = (16 * ti + 4 * lg + r) * VD + 16 * jc + ln;
+                if constexpr (B16)
+                    reinterpret_cast<float*>(Rb + R16::U_OFF)[o] = Uv[r];
+                else
+                    R[RL::u_off() + o] = Uv[r];
+            }
         }
 }
 
@@ -375,6 +482,129 @@ __global__ __launch_bounds__(NT) void kda_chain_kernel(const float* __restrict__
     }
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// Chain for bf16 input: the same steps as kda_chain_kernel with bf16 operands and float32 accumulation, from the
+// bf16 record. The slice's state stays float32 in C-tile layout (rows v, key columns); its bf16 copy S_b [16][KD]
+// and R^T in bf16 [16][64] go through LDS as the operands (every operand read is a 16-byte row read: W, Qg and P
+// by token rows, S_b and R^T by value rows, Kh^T by key rows).
+// ---------------------------------------------------------------------------------------------------------
+template <int KD, int VD>
+__global__ __launch_bounds__(NT) void kda_chain16_kernel(const float* __restrict__ h0, const int32_t* __restrict__ cu,
+                                                         const int* __restrict__ chunk_off, const float* __restrict__ rec,
+                                                         int T, int H, int n_seq, int nc, int nvs, bf16_t* __restrict__ out,
+                                                         float* __restrict__ ht) {
+    typedef KdaRec<KD> RL;
+    typedef KdaRec16<KD> R16;
+    constexpr int LW = KD + 8, LT = BC + 8, LV = 17, JPW = KD / 64;
+    __shared__ __align__(16) bf16_t sW[BC * LW];
+    __shared__ __align__(16) bf16_t sQg[BC * LW];
+    __shared__ __align__(16) bf16_t sKt[KD * LT];
+    __shared__ __align__(16) bf16_t sP[BC * LT];
+    __shared__ __align__(16) bf16_t sSb[16 * LW];
+    __shared__ __align__(16) bf16_t sRt[16 * LT];
+    __shared__ float sU[BC * LV], sGL[KD];
+    int chain, vs;
+    xcd_split(blockIdx.x, nvs, chain, vs);
+    if (chain >= n_seq * H) return;
+    const int n = chain / H, h = chain % H, tid = threadIdx.x, v0 = 16 * vs;
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    int b, bos, eos, slot0;
+    if (cu) {
+        b = 0;
+        bos = cu[n];
+        eos = cu[n + 1];
+        slot0 = chunk_off[n];
+    } else {
+        b = n;
+        bos = 0;
+        eos = T;
+        slot0 = n * nc;
+    }
+    const int nch = (eos - bos + BC - 1) / BC;
+    f32x4 S[JPW];
+#pragma unroll
+    for (int i = 0; i < JPW; ++i) {
+        const int c = 16 * (JPW * w + i) + ln;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[i][r] = h0 ? h0[(((size_t)n * H + h) * VD + v0 + 4 * lg + r) * KD + c] : 0.f;
+    }
+    Tile<bf16_t, BC, KD> tw, tq;
+    Tile<bf16_t, KD, BC> tk;
+    Tile<bf16_t, BC, BC> tp;
+    Tile<float, BC, 16> tu;
+    float gl = 0.f;
+    auto recb = [&](int ci) __attribute__((always_inline)) {
+        return reinterpret_cast<const uint8_t*>(rec + ((size_t)(slot0 + ci) * H + h) * RL::floats(VD));
+    };
+    // the next chunk's loads in three groups spread over the step
+    auto issue_w = [&](int ci) __attribute__((always_inline)) {
+        const uint8_t* R = recb(ci);
+        tw.load(reinterpret_cast<const bf16_t*>(R + R16::W_OFF), KD, BC);
+        tu.load(reinterpret_cast<const float*>(R + R16::U_OFF) + v0, VD, BC);
+        gl = tid < KD ? reinterpret_cast<const float*>(R + R16::gl_off(VD))[tid] : 0.f;
+    };
+    auto issue_q = [&](int ci) __attribute__((always_inline)) {
+        const uint8_t* R = recb(ci);
+        tq.load(reinterpret_cast<const bf16_t*>(R + R16::Q_OFF), KD, BC);
+        tp.load(reinterpret_cast<const bf16_t*>(R + R16::P_OFF), BC, BC);
+    };
+    auto issue_k = [&](int ci) __attribute__((always_inline)) {
+        tk.load(reinterpret_cast<const bf16_t*>(recb(ci) + R16::KT_OFF), BC, KD);
+    };
+    if (nch > 0) {
+        issue_w(0);
+        issue_q(0);
+        issue_k(0);
+    }
+    const int tr0 = 16 * w + 4 * lg;
+    for (int ci = 0; ci < nch; ++ci) {
+        const long row0 = (long)b * T + bos + (long)ci * BC;
+        const int L = min(BC, eos - (bos + ci * BC));
+#pragma unroll
+        for (int i = 0; i < JPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sSb[(4 * lg + r) * LW + 16 * (JPW * w + i) + ln] = f2bf(S[i][r]);
+        tw.template store_raw<LW>(sW);
+        tq.template store_raw<LW>(sQg);
+        tk.template store_raw<LT>(sKt);
+        tp.template store_raw<LT>(sP);
+        tu.store(sU);
+        if (tid < KD) sGL[tid] = gl;
+        __syncthreads();
+        const bool more = ci + 1 < nch;
+        if (more) issue_w(ci + 1);
+        // token tile w: R = U - W S^T and QS = Qg S^T
+        const f32x4 WS = f32t::mmb(sW + 16 * w * LW, LW, sSb, LW, 0, KD, zero4());
+        if (more) issue_q(ci + 1);
+        const f32x4 QS = f32t::mmb(sQg + 16 * w * LW, LW, sSb, LW, 0, KD, zero4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sRt[ln * LT + tr0 + r] = f2bf(sU[(tr0 + r) * LV + ln] - WS[r]);
+        __syncthreads();
+        if (more) issue_k(ci + 1);
+        // O = QS + P R on token tile w (P is zero past column 16 w + 15)
+        const f32x4 o = f32t::mmb(sP + 16 * w * LT, LT, sRt, LT, 0, 16 * (w + 1), QS);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (tr0 + r < L) out[((row0 + tr0 + r) * H + h) * (long)VD + v0 + ln] = f2bf(o[r]);
+        // S <- S diag(Gamma_L) + R^T Kh on the wavefront's key tiles: A(v, t) = R^T[v][t], B(t, c) = Kh^T[c][t]
+#pragma unroll
+        for (int i = 0; i < JPW; ++i) {
+            const int jc = JPW * w + i;
+            S[i] = f32t::mmb(sRt, LT, sKt + 16 * jc * LT, LT, 0, BC, S[i] * sGL[16 * jc + ln]);
+        }
+        __syncthreads();
+    }
+    if (ht) {
+#pragma unroll
+        for (int i = 0; i < JPW; ++i) {
+            const int c = 16 * (JPW * w + i) + ln;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ht[(((size_t)n * H + h) * VD + v0 + 4 * lg + r) * KD + c] = S[i][r];
+        }
+    }
+}
+
 template <typename ST, int KD, int VD>
 hipError_t run_kda(const ST* q, const ST* k, const ST* v, const float* g, const float* beta, const float* h0,
                    const int32_t* cu, const KdaWorkspace& ws, int N, int B, int T, int H, float scale, ST* out,
@@ -399,7 +629,10 @@ hipError_t run_kda(const ST* q, const ST* k, const ST* v, const float* g, const 
     const int nvs = VD / 16;
     const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * nvs);
     timing_begin("kda_chain", s);
-    kda_chain_kernel<ST, KD, VD><<<grid, NT, 0, s>>>(h0, cu, ws.chunk_off, ws.rec, T, H, N, nc, nvs, out, ht);
+    if constexpr (sizeof(ST) == 2)
+        kda_chain16_kernel<KD, VD><<<grid, NT, 0, s>>>(h0, cu, ws.chunk_off, ws.rec, T, H, N, nc, nvs, out, ht);
+    else
+        kda_chain_kernel<ST, KD, VD><<<grid, NT, 0, s>>>(h0, cu, ws.chunk_off, ws.rec, T, H, N, nc, nvs, out, ht);
     timing_end(s);
     return hipGetLastError();
 }

@@ -84,6 +84,18 @@ def test_kda_chunk_fp32_small(dev, oracle, K, V):
     check(o, ht, ro, rh, False, "fp32", 2, 200, 2)
 
 
+@pytest.mark.parametrize("K,V", [(64, 64), (128, 64), (128, 128)])
+def test_kda_chunk_bf16_shapes(dev, oracle, K, V):
+    # every (K, V) the bf16 path accepts, packed with partial chunks and an empty sequence
+    lens = [200, 0, 37, 64, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    say(f"case: KDA chunk bf16 packed K={K} V={V} H=2 lengths {lens}, h0")
+    d = wl.kda_inputs(B=1, T=T, H=2, K=K, V=V, seed=310 + K + V, h0_std=0.1, N=len(lens))
+    o, ht, ro, rh = run(dev, oracle, d, cu=cu)
+    check(o, ht, ro, rh, True, f"bf16 K={K} V={V}", 1, T, 2, cu=cu)
+
+
 def test_kda_chunk_strong_decay_fp32(dev, oracle):
     # per-channel gates around -4 per token (decays to e^-256 within a chunk): no overflow, no NaN
     say("case: KDA chunk float32, strong per-channel decay (g = -softplus(N(0,1) + 4))")
