@@ -52,10 +52,16 @@ template <> struct Elem<bf16_t> {
                                                        acc, 0, 0, 0);
     }
     // float32 -> bf16 with the hardware converter (v_cvt_pk_bf16_f32, round to
-    // nearest even), two values per instruction.
+    // nearest even), two values per instruction. Converted as two 2-wide vectors:
+    // a 4-wide conversion is sometimes split into one value per instruction plus
+    // byte permutes (three times the instructions, in the chain's step too).
     static __device__ __forceinline__ frag pack(f32x4 x) {
-        const bf16x4 b = __builtin_convertvector(x, bf16x4);
-        return __builtin_bit_cast(frag, b);
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 lo = __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2);
+        const bf16x2 hi = __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2);
+        return __builtin_bit_cast(frag, u32x2{__builtin_bit_cast(unsigned int, lo), __builtin_bit_cast(unsigned int, hi)});
     }
     static __device__ __forceinline__ f32x4 unpack(frag x) {
         f32x4 r;
