@@ -1067,17 +1067,23 @@ __global__ __launch_bounds__(512) void gdn_chain_slice_kernel(
         barrier();
         for (int s = -2; s <= nch; ++s) {
             if (s >= 0 && s < nch) {
-                // the K^T fragments of the update are read while the residual computes, half of the key tiles
-                // after each half of X
+                // Gamma_L is read ahead of everything; the K^T fragments of the update are read while the residual
+                // computes, half of the key tiles after X (with Gamma_L S formed then) and half after Y
                 i16x4 Ka[KB / 2][4], Kb[KB / 2][4];
                 f32x4 R[4];
                 i16x4 ER[4];
-                Ops::residual_ahead(Sf, kbuf(s), vbuf(s) + off_v, 0xffffffffu, cbuf(s), tbuf(s), R, ER,
-                                    [&]() __attribute__((always_inline)) { Ops::template read_kt<0, KB / 2>(kbuf(s), Ka); },
+                float gl;
+                Ops::residual_split(Sf, kbuf(s), vbuf(s) + off_v, 0xffffffffu, cbuf(s), tbuf(s), R, ER,
+                                    [&]() __attribute__((always_inline)) { gl = cbuf(s)[63]; },
+                                    [&]() __attribute__((always_inline)) {
+                                        Ops::template read_kt<0, KB / 2>(kbuf(s), Ka);
+#pragma unroll
+                                        for (int kt = 0; kt < KB; ++kt) S[kt] = S[kt] * gl;
+                                    },
                                     [&]() __attribute__((always_inline)) { Ops::template read_kt<KB / 2, KB / 2>(kbuf(s), Kb); });
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) *(lds_i16x4*)(rbuf(s) + ti * 512 + lane * 8) = El::pack(R[ti]);
-                Ops::template update_halves<KB>(S, ER, Ka, Kb, cbuf(s)[63]);
+                Ops::template update_halves<KB>(S, ER, Ka, Kb, 1.f);  // S holds Gamma_L S already
 #pragma unroll
                 for (int kt = 0; kt < KB; ++kt) Sf[kt] = El::pack(S[kt]);
                 // R of chunk s and the entry state of chunk s (written in step s - 1) are in LDS; the entry state

@@ -17,6 +17,8 @@
 // sequence's results do not depend on which kernel ran it or on what else shared its launch.
 #pragma once
 
+#include <type_traits>
+
 #include "sf_device.h"
 #include "sf_internal.h"
 
@@ -109,16 +111,21 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 
 // Pre, gates (one wavefront, lane t = token t of the chunk): G, the inclusive gate sum (padded tokens repeat
 // the last one), and the 256 coefficients [0,64) Gamma_t = exp(G_t), [64,128) e_t = exp(G_L - G_t) (hardware
-// exponential; both exponents are <= 0), [128,192)
-// beta_t (0 on padded tokens), [192,256) G_t log2(e), into coef (LDS or global).
-template <typename CoefPtr>
+// exponential; both exponents are <= 0), [128,192) beta_t (0 on padded tokens) in Pre's own copy (LDS), and in
+// the record the decay from token t to the last token of its 16-token tile, w_t = exp(G_end - G_t) <= 1, which
+// the off-diagonal tiles of P take (p_row), [192,256) G_t log2(e); into coef (LDS or global).
+template <bool RECORD, typename CoefPtr>
 __device__ __forceinline__ void pre_coefs(float G, float bv, CoefPtr coef) {
     const int lane = lane_id();
     const float GL = __shfl(G, 63, 64);
+    const float G2 = G * 1.4426950408889634f;  // log2 units: every decay mask is one hardware exp2
     coef[lane] = __expf(G);
     coef[64 + lane] = __expf(GL - G);
-    coef[128 + lane] = bv;
-    coef[192 + lane] = G * 1.4426950408889634f;  // log2 units: every decay mask is one hardware exp2
+    if constexpr (RECORD)
+        coef[128 + lane] = hw_exp2(fminf(__shfl(G2, lane | 15, 64) - G2, 0.f));
+    else
+        coef[128 + lane] = bv;
+    coef[192 + lane] = G2;
 }
 
 // Pre, first part, one half of the tiles (one wavefront): A = diag(beta) (strictly lower D o K K^T) on five of
@@ -267,8 +274,8 @@ __device__ __forceinline__ void pre_part_t(lds_u8* sc, BetaPtr beta, DstPtr dst)
 template <int KP, typename CoefPtr, typename DstPtr>
 __device__ __forceinline__ void pre_all(const bf16x8 (&kf)[4][KP], float G, float bv, lds_f32* scf, CoefPtr coef,
                                         lds_u8* sc, DstPtr dst) {
-    pre_coefs(G, bv, scf);
-    pre_coefs(G, bv, coef);
+    pre_coefs<false>(G, bv, scf);
+    pre_coefs<true>(G, bv, coef);
     wave_lds_sync();
     pre_tiles<0, KP>(kf, scf, sc);
     pre_tiles<1, KP>(kf, scf, sc);
@@ -277,16 +284,56 @@ __device__ __forceinline__ void pre_all(const bf16x8 (&kf)[4][KP], float G, floa
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// P = scale (D o Q K^T) of one chunk from the K and Q rows in LDS (RowBlock layout), in fragment order, for the
-// block rows set in ROWS (bit ti: block row ti; every tile the same code, whichever call forms it). P^T tiles
-// with K rows as A (rows s) and Q rows as B (columns t): the C tile holds, for lane (ln, lg),
-// P[16 ti + ln][16 tj + 4 lg + r], which is fragment (ti, tj / 2)'s lane content (first or second half), the B
-// operand that pairs with the R fragments of the same tokens. G (in log2 units) is coefficients [192, 256).
+// Block row TI of P^T = scale (D o Q K^T)^T in registers: kf[tj][p] the K row fragments of token tiles
+// tj <= TI, qf[p] the Q row fragments of token tile TI; pf[p], p <= TI / 2, gets fragment (TI, p)'s lane
+// content. P^T tiles with K rows as A (rows s) and Q rows as B (columns t): the C tile holds, for lane (ln, lg),
+// P[16 TI + ln][16 tj + 4 lg + r], which is fragment (TI, tj / 2)'s lane content (first or second half), the B
+// operand that pairs with the R fragments of the same tokens. cf: the record's coefficients (G in log2 units
+// at [192, 256), w at [128, 192)). The decay exp(G_t - G_s) of a diagonal tile is one exponential per element;
+// an off-diagonal tile (s in an earlier tile tj) splits it at the last token e of tile tj into exp(G_t - G_e)
+// per row and w_s = exp(G_e - G_s) per column, both <= 1, so neither factor overflows where the product is
+// finite.
 // ---------------------------------------------------------------------------------------------------------
+template <int TI, int KP>
+__device__ __forceinline__ void p_row(const bf16x8 (&kf)[4][KP], const bf16x8 (&qf)[KP], const lds_f32* cf, float scale,
+                                      bf16x8 (&pf)[2]) {
+    typedef Elem<bf16_t> El;
+    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
+    const float Gt = cf[192 + 16 * TI + ln];
+    f32x4 PT[4];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+        PT[tj] = zero4();
+        if (tj <= TI) {
+#pragma unroll
+            for (int p = 0; p < KP; ++p) PT[tj] = mma32(kf[tj][p], qf[p], PT[tj]);
+        }
+    }
+#pragma unroll
+    for (int tj = 0; tj < TI; ++tj) {
+        const float a = scale * hw_exp2(fminf(Gt - cf[192 + 16 * tj + 15], 0.f));
+        const f32x4 w = *(const lds_f32x4*)(cf + 128 + 16 * tj + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) PT[tj][r] = PT[tj][r] * a * w[r];
+    }
+    {
+        const f32x4 Gs = *(const lds_f32x4*)(cf + 192 + 16 * TI + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            // token s = 16 TI + 4 lg + r against t = 16 TI + ln: only s <= t, where G_t - G_s <= 0
+            const bool keep = 4 * lg + r <= ln;
+            PT[TI][r] = keep ? PT[TI][r] * (scale * hw_exp2(fminf(Gt - Gs[r], 0.f))) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p <= TI / 2; ++p) pf[p] = cat8(El::pack(PT[2 * p]), El::pack(PT[2 * p + 1]));
+}
+
+// P of one chunk from the K and Q rows in LDS (RowBlock layout) into LDS in fragment order, for the block rows
+// set in ROWS (bit ti: block row ti), each row by p_row.
 template <int KD, int ROWS>
 __device__ __forceinline__ void form_p(const lds_u8* KR, const lds_u8* QR, const lds_f32* cf, float scale, lds_u8* P) {
     typedef RowBlock<KD> RBk;
-    typedef Elem<bf16_t> El;
     constexpr int KP = KD / 32;
     constexpr int UST = (16 / RBk::RPB) * 1024;
     constexpr int TOP = (ROWS & 8) ? 3 : (ROWS & 4) ? 2 : (ROWS & 2) ? 1 : 0;  // highest block row formed
@@ -300,33 +347,21 @@ __device__ __forceinline__ void form_p(const lds_u8* KR, const lds_u8* QR, const
 #pragma unroll
         for (int p = 0; p < KP; ++p)
             if (R <= TOP) kf[R][p] = *(const lds_bf16x8*)(KR + orow[p] + R * UST);
+    auto row = [&](auto ti_c) __attribute__((always_inline)) {
+        constexpr int ti = decltype(ti_c)::value;
+        if constexpr ((ROWS >> ti) & 1) {
+            bf16x8 qf[KP], pf[2];
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-        if (!((ROWS >> ti) & 1)) continue;
-        bf16x8 qf[KP];
+            for (int p = 0; p < KP; ++p) qf[p] = *(const lds_bf16x8*)(QR + orow[p] + ti * UST);
+            p_row<ti, KP>(kf, qf, cf, scale, pf);
 #pragma unroll
-        for (int p = 0; p < KP; ++p) qf[p] = *(const lds_bf16x8*)(QR + orow[p] + ti * UST);
-        const float Gt = cf[192 + 16 * ti + ln];
-        f32x4 PT[4];
-#pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
-            PT[tj] = zero4();
-            if (tj <= ti) {
-#pragma unroll
-                for (int p = 0; p < KP; ++p) PT[tj] = mma32(kf[tj][p], qf[p], PT[tj]);
-                const f32x4 Gs = *(const lds_f32x4*)(cf + 192 + 16 * tj + 4 * lg);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    // token s = 16 tj + 4 lg + r against t = 16 ti + ln: only s <= t, where G_t - G_s <= 0
-                    const bool keep = tj < ti || 4 * lg + r <= ln;
-                    PT[tj][r] = keep ? PT[tj][r] * (scale * hw_exp2(fminf(Gt - Gs[r], 0.f))) : 0.f;
-                }
-            }
+            for (int p = 0; p <= ti / 2; ++p) *(lds_bf16x8*)(P + tri_frag(ti, p) * 1024 + lane * 16) = pf[p];
         }
-#pragma unroll
-        for (int p = 0; p <= ti / 2; ++p)
-            *(lds_bf16x8*)(P + tri_frag(ti, p) * 1024 + lane * 16) = cat8(El::pack(PT[2 * p]), El::pack(PT[2 * p + 1]));
-    }
+    };
+    row(std::integral_constant<int, 0>{});
+    row(std::integral_constant<int, 1>{});
+    row(std::integral_constant<int, 2>{});
+    row(std::integral_constant<int, 3>{});
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -351,8 +386,8 @@ struct SliceOps {
     // The residual, by halves over the token tiles: for the token tiles U0, U0 + 1, x_in issues the LDS reads
     // (K row fragments, the Gamma coefficients, the V block) and x_mul forms X = K S^T from the bf16 entry state
     // Sf; residual_yx forms Y = V - Gamma X in bf16. KR: K rows; vtr: this slice's V block [64][16] bf16 at the
-    // lane's transposed-read offset; cf: coefficients. The two schedules below (residual, residual_ahead) call
-    // the same pieces, so they give the same bits.
+    // lane's transposed-read offset; cf: coefficients. The two schedules below (residual, residual_split) make
+    // the same products in the same order, so they give the same bits.
     template <int U0>
     struct XIn {
         bf16x8 kr[2][KP];
@@ -381,16 +416,20 @@ struct SliceOps {
         }
         return in;
     }
-    template <int U0>
-    __device__ static XOut<U0> x_mul(const XIn<U0>& in, const i16x4 (&Sf)[KB]) {
-        XOut<U0> o;
-        // (the two token tiles' accumulations interleaved, each summed over p in order)
-        o.X[0] = zero4();
-        o.X[1] = zero4();
+    // X = K S^T on the two token tiles from their K row fragments kr (the two tiles' accumulations interleaved,
+    // each summed over p in order)
+    __device__ static void x_prod(const bf16x8 (&kr)[2][KP], const i16x4 (&Sf)[KB], f32x4 (&X)[2]) {
+        X[0] = zero4();
+        X[1] = zero4();
 #pragma unroll
         for (int p = 0; p < KP; ++p)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) o.X[u] = mma32(in.kr[u][p], cat8(Sf[2 * p], Sf[2 * p + 1]), o.X[u]);
+            for (int u = 0; u < 2; ++u) X[u] = mma32(kr[u][p], cat8(Sf[2 * p], Sf[2 * p + 1]), X[u]);
+    }
+    template <int U0>
+    __device__ static XOut<U0> x_mul(const XIn<U0>& in, const i16x4 (&Sf)[KB]) {
+        XOut<U0> o;
+        x_prod(in.kr, Sf, o.X);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             o.gam[u] = in.gam[u];
@@ -468,29 +507,60 @@ struct SliceOps {
         residual_yx<2>(residual_x<2>(Sf, KR, vtr, cf), vmask, Yhi);
         residual_ry(Ylo, Yhi, in0, in2, R, ER);
     }
-    // residual_ahead: every read of both halves issued first; ahead0() runs once the first half's products are
-    // issued and ahead1() once the second half's are (a caller's own reads, which then land while the rest of
-    // the residual computes).
-    template <typename Ahead0, typename Ahead1>
-    __device__ static void residual_ahead(const i16x4 (&Sf)[KB], const lds_u8* KR, const lds_u8* vtr, uint32_t vmask,
+    // residual_split: the schedule of one wavefront that runs the whole step. The LDS reads return in order and
+    // the wait counter reaches back 15 reads only, so the reads go out in the order of their use, each batch
+    // behind products that cover its latency: the K row fragments of all four tiles (first() issues a caller's
+    // early reads ahead of them), the first half's products, the Gamma, V, T diag(beta) and e reads, the second
+    // half's products, after_x() (a caller's reads and arithmetic that need none of these), Y, after_y(), R.
+    template <typename First, typename AfterX, typename AfterY>
+    __device__ static void residual_split(const i16x4 (&Sf)[KB], const lds_u8* KR, const lds_u8* vtr, uint32_t vmask,
                                           const lds_f32* cf, const lds_u8* Tfr, f32x4 (&R)[4], i16x4 (&ER)[4],
-                                          Ahead0&& ahead0, Ahead1&& ahead1) {
+                                          First&& first, AfterX&& after_x, AfterY&& after_y) {
+        const int lg = lane_id() >> 4;
+        first();
+        bf16x8 kr0[2][KP], kr2[2][KP];
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            const lds_u8* kb = lds_base(KR + orow(p));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) kr0[u][p] = *(const lds_bf16x8*)(kb + u * UST);
+        }
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            const lds_u8* kb = lds_base(KR + orow(p));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) kr2[u][p] = *(const lds_bf16x8*)(kb + (2 + u) * UST);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        XOut<0> x0;
+        XOut<2> x2;
+        x_prod(kr0, Sf, x0.X);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 gam = *(const lds_f32x4*)(cf + 16 * u + 4 * lg);
+            const i16x4 vx = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vtr + 16 * u * 16 * 2));
+            if (u < 2) {
+                x0.gam[u] = gam;
+                x0.vx[u] = vx;
+            } else {
+                x2.gam[u - 2] = gam;
+                x2.vx[u - 2] = vx;
+            }
+        }
         const RIn<0> in0 = residual_r_in<0>(cf, Tfr);
         const RIn<2> in2 = residual_r_in<2>(cf, Tfr);
-        const XIn<0> a0 = x_in<0>(KR, vtr, cf);
-        const XIn<2> a2 = x_in<2>(KR, vtr, cf);
         __builtin_amdgcn_sched_barrier(0);
-        const XOut<0> x0 = x_mul<0>(a0, Sf);
+        x_prod(kr2, Sf, x2.X);
         __builtin_amdgcn_sched_barrier(0);
-        ahead0();
-        __builtin_amdgcn_sched_barrier(0);
-        const XOut<2> x2 = x_mul<2>(a2, Sf);
-        __builtin_amdgcn_sched_barrier(0);
-        ahead1();
+        after_x();
         __builtin_amdgcn_sched_barrier(0);
         i16x4 Ylo[2], Yhi[2];
         residual_yx<0>(x0, vmask, Ylo);
         residual_yx<2>(x2, vmask, Yhi);
+        __builtin_amdgcn_sched_barrier(0);
+        after_y();
+        __builtin_amdgcn_sched_barrier(0);
         residual_ry(Ylo, Yhi, in0, in2, R, ER);
     }
     __device__ static void residual_ry(const i16x4 (&Ylo)[2], const i16x4 (&Yhi)[2], const RIn<0>& in0,
