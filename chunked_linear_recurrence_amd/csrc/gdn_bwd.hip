@@ -41,6 +41,20 @@ struct BwdRec {
     static constexpr int T_OFF = 0, W_OFF = BC * BC, QT_OFF = W_OFF + BC * KD, C_OFF = QT_OFF + BC * KD;
     static constexpr int FLOATS = C_OFF + 256;
 };
+// T, W and Qt are stored in the input type at their offsets (for bf16 inputs half of each region): they enter
+// only products, whose tiles round their operands to the input type in any case (unscaled).
+template <typename ST, int KD>
+__device__ __forceinline__ ST* rec_t(float* R) { return reinterpret_cast<ST*>(R + BwdRec<KD>::T_OFF); }
+template <typename ST, int KD>
+__device__ __forceinline__ const ST* rec_t(const float* R) { return reinterpret_cast<const ST*>(R + BwdRec<KD>::T_OFF); }
+template <typename ST, int KD>
+__device__ __forceinline__ ST* rec_w(float* R) { return reinterpret_cast<ST*>(R + BwdRec<KD>::W_OFF); }
+template <typename ST, int KD>
+__device__ __forceinline__ ST* rec_qt(float* R) { return reinterpret_cast<ST*>(R + BwdRec<KD>::QT_OFF); }
+template <typename ST, int KD>
+__device__ __forceinline__ const ST* rec_w(const float* R) { return reinterpret_cast<const ST*>(R + BwdRec<KD>::W_OFF); }
+template <typename ST, int KD>
+__device__ __forceinline__ const ST* rec_qt(const float* R) { return reinterpret_cast<const ST*>(R + BwdRec<KD>::QT_OFF); }
 
 template <typename ST>
 __device__ __forceinline__ float ld(const ST* p) { return Elem<ST>::to_f(*p); }
@@ -138,6 +152,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
         __syncthreads();
     }
     float* R = rec + ((size_t)slot * H + h) * RL::FLOATS;
+    ST* const RW = rec_w<ST, KD>(R);
+    ST* const RQ = rec_qt<ST, KD>(R);
     // W = T (beta Gamma K) on the wavefront's row tile (T is zero past column 16 w + 15)
 #pragma unroll
     for (int jc = 0; jc < NJ; ++jc) {
@@ -145,7 +161,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             sW[tr[r] * LK + 16 * jc + ln] = Wv[r];
-            R[RL::W_OFF + tr[r] * KD + 16 * jc + ln] = Wv[r];
+            RW[tr[r] * KD + 16 * jc + ln] = Elem<ST>::from_f(Wv[r]);
         }
     }
     __syncthreads();
@@ -156,10 +172,10 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tr[r], c = 16 * jc + ln;
-            R[RL::QT_OFF + t * KD + c] = scale * expf(sG[t]) * sQ[t * LK + c] - PW[r];
+            RQ[t * KD + c] = Elem<ST>::from_f(scale * expf(sG[t]) * sQ[t * LK + c] - PW[r]);
         }
     }
-    for (int i = tid; i < BC * BC; i += NT) R[RL::T_OFF + i] = sT[(i / BC) * LL + i % BC];
+    for (int i = tid; i < BC * BC; i += NT) rec_t<ST, KD>(R)[i] = Elem<ST>::from_f(sT[(i / BC) * LL + i % BC]);
     if (tid < BC) {
         const float G = sG[tid], GL = sG[BC - 1];
         R[RL::C_OFF + tid] = G;
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states_kernel(const ST* __restrict
         for (int r = 0; r < 4; ++r)
             S[i][r] = h0 ? h0[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] : 0.f;
     Tile<ST, BC, KD> tk;
-    Tile<float, BC, BC> tt;
+    Tile<ST, BC, BC> tt;
     Tile<ST, BC, 16> tv;
     float cf = 0.f;
     auto issue = [&](int ci) __attribute__((always_inline)) {
@@ -222,7 +238,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states_kernel(const ST* __restrict
         const int L = min(BC, eos - (bos + ci * BC));
         const float* R = rec + ((size_t)(slot0 + ci) * H + h) * RL::FLOATS;
         tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
-        tt.load(R + RL::T_OFF, BC, BC);
+        tt.load(rec_t<ST, KD>(R), BC, BC);
         tv.load(v + (row0 * H + h) * (long)V + v0, (long)H * V, L);
         cf = R[RL::C_OFF + tid];
     };
@@ -296,8 +312,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate_kernel(const ST* __restrict
         for (int r = 0; r < 4; ++r)
             dS[i][r] = dht ? dht[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] : 0.f;
     // chunk ci's K rows, W, Qt, coefficients and dO slice, loaded one chunk ahead (chunks run backwards)
-    Tile<ST, BC, KD> tk;
-    Tile<float, BC, KD> tw, tq;
+    Tile<ST, BC, KD> tk, tw, tq;
     Tile<ST, BC, 16> to;
     float cf = 0.f;
     auto issue = [&](int ci) __attribute__((always_inline)) {
@@ -305,8 +320,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate_kernel(const ST* __restrict
         const int L = min(BC, eos - (bos + ci * BC));
         const float* R = rec + ((size_t)(slot0 + ci) * H + h) * RL::FLOATS;
         tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
-        tw.load(R + RL::W_OFF, KD, BC);
-        tq.load(R + RL::QT_OFF, KD, BC);
+        tw.load(rec_w<ST, KD>(R), KD, BC);
+        tq.load(rec_qt<ST, KD>(R), KD, BC);
         to.load(dout + (row0 * H + h) * (long)V + v0, (long)H * V, L);
         cf = R[RL::C_OFF + tid];
     };
@@ -391,10 +406,10 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
     const float* Rc = rec + ((size_t)slot * H + h) * RL::FLOATS;
     {
         Tile<ST, BC, KD> tk, tq;
-        Tile<float, BC, BC> tt;
+        Tile<ST, BC, BC> tt;
         tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
-        tt.load(Rc + RL::T_OFF, BC, BC);
+        tt.load(rec_t<ST, KD>(Rc), BC, BC);
         sC[tid] = Rc[RL::C_OFF + tid];
         tk.store(sK);
         tq.store(sQ);

@@ -79,9 +79,10 @@ inline GdnWorkspace gdn_workspace_layout(void* base, int elem_bytes, int B, int 
     return w;
 }
 
-// Workspace of the delta-rule chunk backward (float32 throughout): the chunk table of packed inputs, one
-// record per (chunk slot, head) (T [64][64], W and Qt [64][K], 256 coefficients), every chunk's entry
-// state and the gradient of every chunk's exit state ([slots][H][V][K] each).
+// Workspace of the delta-rule chunk backward: the chunk table of packed inputs, one record per (chunk slot,
+// head) (T [64][64], W and Qt [64][K] in the input type in float32-sized regions, 256 float32
+// coefficients), every chunk's float32 entry state and the gradient of every chunk's exit state ([slots][H][V][K]
+// each).
 struct GdnBwdWorkspace {
     int* chunk_off;
     int2* table;
