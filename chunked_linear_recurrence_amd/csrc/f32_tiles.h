@@ -183,6 +183,52 @@ __device__ __forceinline__ f32x4 mmb(const bf16_t* A, int lda, const bf16_t* Bt,
     return acc;
 }
 
+// Eight (four) elements p[0], p[stride], ... as bf16: float elements rounded to nearest even, bf16 elements as
+// they are.
+__device__ __forceinline__ bf16x8 bf8_of(const float* p, int stride) {
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    f32x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = p[j * stride];
+    return __builtin_convertvector(v, bf16x8);
+}
+__device__ __forceinline__ bf16x8 bf8_of(const bf16_t* p, int stride) {
+    i16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (short)p[j * stride];
+    return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ i16x4 bf4_of(const float* p, int stride) {
+    f32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = p[j * stride];
+    return Elem<bf16_t>::pack(v);
+}
+__device__ __forceinline__ i16x4 bf4_of(const bf16_t* p, int stride) {
+    i16x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (short)p[j * stride];
+    return v;
+}
+
+// mm32 (unscaled) with each operand in LDS as float or as bf16: for the same operand values, the same products in
+// the same order, so the same bits.
+template <typename TA, typename TB>
+__device__ __forceinline__ f32x4 mmg(const TA* A, int ars, int acs, const TB* B, int brs, int bcs, int k0, int k1,
+                                     f32x4 acc) {
+    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
+    const TA* a = A + ln * ars;
+    const TB* b = B + ln * bcs;
+    int kk = k0;
+    for (; kk + 32 <= k1; kk += 32)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8_of(a + (kk + 8 * lg) * acs, acs),
+                                                      bf8_of(b + (kk + 8 * lg) * brs, brs), acc, 0, 0, 0);
+    if (kk + 16 <= k1)
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bf4_of(a + (kk + 4 * lg) * acs, acs),
+                                                        bf4_of(b + (kk + 4 * lg) * brs, brs), acc, 0, 0, 0);
+    return acc;
+}
+
 // The tile product in the arithmetic of the input type ST: float32 operands for float32 inputs, bf16 operands
 // for bf16 inputs.
 template <typename ST>

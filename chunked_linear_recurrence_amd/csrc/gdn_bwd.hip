@@ -61,7 +61,10 @@ __device__ __forceinline__ float ld(const ST* p) { return Elem<ST>::to_f(*p); }
 
 using f32t::Tile;
 using f32t::mm4;
+using f32t::mmb;
+using f32t::mmg;
 using f32t::mmx;
+using f32t::unit_of;
 
 // ---------------------------------------------------------------------------------------------------------
 // Prep: per (chunk slot, head), on float32 MFMA tiles (wavefront w owns token rows 16 w .. 16 w + 15). G by a wave
@@ -175,7 +178,11 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
             RQ[t * KD + c] = Elem<ST>::from_f(scale * expf(sG[t]) * sQ[t * LK + c] - PW[r]);
         }
     }
-    for (int i = tid; i < BC * BC; i += NT) rec_t<ST, KD>(R)[i] = Elem<ST>::from_f(sT[(i / BC) * LL + i % BC]);
+    for (int i = tid; i < BC * BC; i += NT) {
+        rec_t<ST, KD>(R)[i] = Elem<ST>::from_f(sT[(i / BC) * LL + i % BC]);
+        // bf16 inputs: T^T follows T in the float32-sized region (the gradient kernel reads T by columns from it)
+        if constexpr (sizeof(ST) == 2) rec_t<ST, KD>(R)[BC * BC + i] = Elem<ST>::from_f(sT[(i % BC) * LL + i / BC]);
+    }
     if (tid < BC) {
         const float G = sG[tid], GL = sG[BC - 1];
         R[RL::C_OFF + tid] = G;
@@ -630,6 +637,368 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// The gradient kernel for bf16 inputs, per (chunk slot, head): the products of gdn_bwd_grad_kernel on bf16 LDS
+// operands. K, Q, T, T^T (from the record), P and the slices' state rows are kept in bf16, so every operand reaches
+// its product by a 16-byte read of eight consecutive reduction elements (row form: A rows and B^T rows, k
+// contiguous) or by two transposing reads (ds_read_b64_tr_b16) of a row-major block, which give a lane four
+// consecutive rows of one column, the C-tile shape (column form: both operands indexed [k][m] and [k][n]). The
+// value dimension goes in slices of 32, so the per-slice products (dP, dT, dq, dk) reduce 32 values per
+// 16x16x32 MFMA. The products after the slices take their float operands as before and the bf16 ones from
+// these arrays (mmg, the same bits as mm32).
+// ---------------------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) uint8_t lds8;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
+
+// column form: lane (ln, lg) gets M[r0 + 4 lg + i][c0 + ln], i = 0..3, of the row-major bf16 block M (pitch P
+// elements, a multiple of 4; c0 a multiple of 4)
+__device__ __forceinline__ i16x4 col4(const bf16_t* M, int P, int r0, int c0) {
+    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
+    const bf16_t* a = M + (r0 + 4 * lg + (ln >> 2)) * P + c0 + 4 * (ln & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds8*)a);
+}
+// the 32-deep column-form operand: rows r0 + 4 lg + i, then r0 + 16 + 4 lg + i
+__device__ __forceinline__ bf16x8 col8(const bf16_t* M, int P, int r0, int c0) {
+    return cat8(col4(M, P, r0, c0), col4(M, P, r0 + 16, c0));
+}
+// row form: lane (ln, lg) gets M[r0 + ln][k0 + 8 lg .. + 7] (pitch P a multiple of 8, k0 of 8)
+__device__ __forceinline__ bf16x8 row8(const bf16_t* M, int P, int r0, int k0) {
+    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
+    return *(const lds_bf16x8_t*)(lds8*)(M + (r0 + ln) * P + k0 + 8 * lg);
+}
+// C tile (rows r0 + 4 lg + i, column c0 + ln) into a row-major bf16 block, and transposed (row c0 + ln, columns
+// r0 + 4 lg .. + 3: one 8-byte write)
+__device__ __forceinline__ void put_rows(bf16_t* M, int P, int r0, int c0, f32x4 c) {
+    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) M[(r0 + 4 * lg + i) * P + c0 + ln] = f2bf(c[i]);
+}
+__device__ __forceinline__ void put_cols(bf16_t* M, int P, int r0, int c0, f32x4 c) {
+    const int lane = lane_id(), ln = lane & 15, lg = lane >> 4;
+    *(lds_i16x4_t*)(lds8*)(M + (c0 + ln) * P + r0 + 4 * lg) = Elem<bf16_t>::pack(c);
+}
+
+template <int KD>
+__global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ rec, const float* __restrict__ states,
+    const float* __restrict__ dstates, const int2* __restrict__ table, const int32_t* __restrict__ cu, int T, int H,
+    int V, int nc, float scale, bf16_t* __restrict__ dq, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
+    float* __restrict__ dg, float* __restrict__ dbeta) {
+    typedef BwdRec<KD> RL;
+    typedef Elem<bf16_t> El;
+    constexpr int KP = KD + 8;   // bf16 pitch of K, Q and the state rows
+    constexpr int CP = BC + 8;   // bf16 pitch of 64-wide rows (T, T^T, P, and the slices' transposed blocks)
+    constexpr int SW = 32;       // values per slice
+    constexpr int VP = SW + 8;   // bf16 pitch of a slice's token rows
+    constexpr int LL = BC + 1;   // float pitch of P, K K^T, dT, D o dP
+    constexpr int NJ = KD / 16;
+    __shared__ __align__(16) bf16_t sK[BC * KP], sQ[BC * KP], sT[BC * CP], sTt[BC * CP], sPb[BC * CP];
+    __shared__ float sP[BC * LL], sKK[BC * LL], sC[256];
+    // per-slice region (bf16); after the slices it holds dT (then U, then F) and scale D o dP (float)
+    constexpr int SLICE_BYTES = (2 * SW * KP + 5 * BC * VP + 3 * SW * CP) * 2, POST_BYTES = 2 * BC * LL * 4;
+    __shared__ __align__(16) uint8_t sX[SLICE_BYTES > POST_BYTES ? SLICE_BYTES : POST_BYTES];
+    bf16_t* const sS = reinterpret_cast<bf16_t*>(sX);  // [SW][KP] entry state rows of the slice
+    bf16_t* const sD = sS + SW * KP;                    // [SW][KP] exit-state gradient rows
+    bf16_t* const sO = sD + SW * KP;                    // [BC][VP] dO
+    bf16_t* const sV = sO + BC * VP;                    // [BC][VP] V
+    bf16_t* const sZ = sV + BC * VP;                    // [BC][VP] Z = diag(beta) Y
+    bf16_t* const sR = sZ + BC * VP;                    // [BC][VP] R
+    bf16_t* const sdR = sR + BC * VP;                   // [BC][VP] dR
+    bf16_t* const sOt = sdR + BC * VP;                  // [SW][CP] dO^T
+    bf16_t* const sRt = sOt + SW * CP;                  // [SW][CP] R^T
+    bf16_t* const sXt = sRt + SW * CP;                  // [SW][CP] dX^T
+    float* const sdT = reinterpret_cast<float*>(sX);   // [64][LL] after the slices: dT, then U = dT T^T, then F
+    float* const sDP = sdT + BC * LL;                   // [64][LL] after the slices: scale D o dP
+    __shared__ float sDG[BC], sEE[BC], sRed[NT / 64], sCol[NT];
+
+    const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    int b, t0, L;
+    if (!chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
+    const long row0 = (long)b * T + t0;
+    const float* Rc = rec + ((size_t)slot * H + h) * RL::FLOATS;
+    {
+        Tile<bf16_t, BC, KD> tk, tq;
+        Tile<bf16_t, BC, BC> tt, ttt;
+        tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tt.load(rec_t<bf16_t, KD>(Rc), BC, BC);
+        ttt.load(rec_t<bf16_t, KD>(Rc) + BC * BC, BC, BC);
+        sC[tid] = Rc[RL::C_OFF + tid];
+        tk.template store_raw<KP>(sK);
+        tq.template store_raw<KP>(sQ);
+        tt.template store_raw<CP>(sT);
+        ttt.template store_raw<CP>(sTt);
+    }
+    __syncthreads();
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    // the lane's C-tile rows: tokens tr[r] = 16 w + 4 lg + r
+    int tr[4];
+    float Gr[4], gam[4], ee[4], bb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        tr[r] = 16 * w + 4 * lg + r;
+        Gr[r] = sC[tr[r]];
+        gam[r] = sC[64 + tr[r]];
+        ee[r] = sC[128 + tr[r]];
+        bb[r] = sC[192 + tr[r]];
+    }
+    const float gl = sC[64 + BC - 1];
+    // P = scale (D o Q K^T) (s <= t) and the raw K K^T (s < t) on the wavefront's row tile
+    for (int j = 0; j < 4; ++j) {
+        f32x4 qk = zero4(), kk = zero4();
+        if (j <= w) {
+            qk = mmb(sQ + 16 * w * KP, KP, sK + 16 * j * KP, KP, 0, KD, qk);
+            kk = mmb(sK + 16 * w * KP, KP, sK + 16 * j * KP, KP, 0, KD, kk);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = tr[r], s2 = 16 * j + ln;
+            const float pv = s2 <= t ? scale * expf(Gr[r] - sC[s2]) * qk[r] : 0.f;
+            sP[t * LL + s2] = pv;
+            sPb[t * CP + s2] = f2bf(pv);
+            sKK[t * LL + s2] = s2 < t ? kk[r] : 0.f;
+        }
+    }
+    f32x4 aP[4], aT[4], aQ[NJ], aK[NJ], aK2[NJ];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) aP[j] = aT[j] = zero4();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) aQ[j] = aK[j] = aK2[j] = zero4();
+    float pGam[4] = {0.f, 0.f, 0.f, 0.f}, pE[4] = {0.f, 0.f, 0.f, 0.f}, pB[4] = {0.f, 0.f, 0.f, 0.f}, pGL = 0.f;
+    const int nvs = V / SW;
+    Tile<float, SW, KD> ts, td;
+    Tile<bf16_t, BC, SW> to, tv;
+    auto issue = [&](int vs) __attribute__((always_inline)) {
+        const int v0 = SW * vs;
+        ts.load(states + (((size_t)slot * H + h) * V + v0) * KD, KD, SW);
+        td.load(dstates + (((size_t)slot * H + h) * V + v0) * KD, KD, SW);
+        to.load(dout + (row0 * H + h) * (long)V + v0, (long)H * V, L);
+        tv.load(v + (row0 * H + h) * (long)V + v0, (long)H * V, L);
+    };
+    issue(0);
+    __syncthreads();
+    for (int vs = 0; vs < nvs; ++vs) {
+        const int v0 = SW * vs;
+        // the slice's operands to LDS: state rows in bf16 (<S, dS'> in float32 from the same registers), dO and V
+        // rows, dO^T
+#pragma unroll
+        for (int p = 0; p < decltype(ts)::PER; ++p) {
+            const int idx = tid + NT * p, row = idx / decltype(ts)::PPR, col = (idx % decltype(ts)::PPR) * 4;
+            if (idx < decltype(ts)::PIECES) {
+                const f32x4 sv = __builtin_bit_cast(f32x4, ts.r[p]), dv4 = __builtin_bit_cast(f32x4, td.r[p]);
+                pGL += (sv[0] * dv4[0] + sv[1] * dv4[1]) + (sv[2] * dv4[2] + sv[3] * dv4[3]);
+                *(lds_i16x4_t*)(lds8*)(sS + row * KP + col) = El::pack(sv);
+                *(lds_i16x4_t*)(lds8*)(sD + row * KP + col) = El::pack(dv4);
+            }
+        }
+        to.template store_raw<VP>(sO);
+        tv.template store_raw<VP>(sV);
+#pragma unroll
+        for (int p = 0; p < decltype(to)::PER; ++p) {
+            const int idx = tid + NT * p, row = idx / decltype(to)::PPR, col = (idx % decltype(to)::PPR) * 8;
+            if (idx < decltype(to)::PIECES)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sOt[(col + e) * CP + row] = unit_of<bf16_t>(to.r[p], e);
+        }
+        if (vs + 1 < nvs) issue(vs + 1);
+        __syncthreads();
+        // X = K S^T, QS = Q S^T, KdS = K dS'^T on (token tile w, the slice's two value tiles): row form
+        f32x4 X[2], QS[2], KdS[2], Y[2];
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) {
+            X[vt] = mmb(sK + 16 * w * KP, KP, sS + 16 * vt * KP, KP, 0, KD, zero4());
+            QS[vt] = mmb(sQ + 16 * w * KP, KP, sS + 16 * vt * KP, KP, 0, KD, zero4());
+            KdS[vt] = mmb(sK + 16 * w * KP, KP, sD + 16 * vt * KP, KP, 0, KD, zero4());
+        }
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) {
+            const f32x4 vv = El::unpack(col4(sV, VP, 16 * w, 16 * vt)), oo = El::unpack(col4(sO, VP, 16 * w, 16 * vt));
+            f32x4 z;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Y[vt][r] = vv[r] - gam[r] * X[vt][r];
+                z[r] = bb[r] * Y[vt][r];
+                pGam[r] += scale * oo[r] * QS[vt][r];
+            }
+            put_rows(sZ, VP, 16 * w, 16 * vt, z);
+        }
+        __syncthreads();
+        // R = T Z (column form: T^T rows give T by columns); dR = P^T dO + e KdS (column form, P rows)
+        f32x4 R[2], dR[2];
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) {
+            R[vt] = zero4();
+            f32x4 dRp = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < BC; k0 += 32) {
+                if (k0 < 16 * (w + 1)) R[vt] = mma32(col8(sTt, CP, k0, 16 * w), col8(sZ, VP, k0, 16 * vt), R[vt]);
+                if (k0 + 32 > 16 * w) dRp = mma32(col8(sPb, CP, k0, 16 * w), col8(sO, VP, k0, 16 * vt), dRp);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                dR[vt][r] = dRp[r] + ee[r] * KdS[vt][r];
+                pE[r] += R[vt][r] * KdS[vt][r];
+            }
+            put_rows(sR, VP, 16 * w, 16 * vt, R[vt]);
+            put_cols(sRt, CP, 16 * w, 16 * vt, R[vt]);
+            put_rows(sdR, VP, 16 * w, 16 * vt, dR[vt]);
+        }
+        __syncthreads();
+        // dZ = T^T dR (column form, T rows); dbeta, dY = dV, dX = -Gamma dY
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) {
+            f32x4 dZ = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < BC; k0 += 32)
+                if (k0 + 32 > 16 * w) dZ = mma32(col8(sT, CP, k0, 16 * w), col8(sdR, VP, k0, 16 * vt), dZ);
+            f32x4 dX;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pB[r] += Y[vt][r] * dZ[r];
+                const float dY = bb[r] * dZ[r];
+                if (tr[r] < L) dv[((row0 + tr[r]) * H + h) * (long)V + v0 + 16 * vt + ln] = f2bf(dY);
+                dX[r] = -gam[r] * dY;
+                pGam[r] -= dY * X[vt][r];
+            }
+            put_cols(sXt, CP, 16 * w, 16 * vt, dX);
+        }
+        // dP += dO R^T, dT += dR Z^T (row form over the slice's 32 values)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            aP[j] = mmb(sO + 16 * w * VP, VP, sR + 16 * j * VP, VP, 0, SW, aP[j]);
+            aT[j] = mmb(sdR + 16 * w * VP, VP, sZ + 16 * j * VP, VP, 0, SW, aT[j]);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's dX^T columns are in LDS
+        // dq += dO S, dk += dX S, dk2 += R dS' (column form: dO^T, dX^T, R^T by rows, S and dS' rows)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const bf16x8 s8 = col8(sS, KP, 0, 16 * j), d8 = col8(sD, KP, 0, 16 * j);
+            aQ[j] = mma32(col8(sOt, CP, 0, 16 * w), s8, aQ[j]);
+            aK[j] = mma32(col8(sXt, CP, 0, 16 * w), s8, aK[j]);
+            aK2[j] = mma32(col8(sRt, CP, 0, 16 * w), d8, aK2[j]);
+        }
+        __syncthreads();
+    }
+    // dq = scale Gamma (dO S), dk = dX S + e (R dS')
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            aQ[j][r] *= scale * gam[r];
+            aK[j][r] += ee[r] * aK2[j][r];
+        }
+    // dT to LDS, U = dT T^T (T[s][j] is zero past j = s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sdT[tr[r] * LL + 16 * j + ln] = aT[j][r];
+    __syncthreads();
+    f32x4 U[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) U[j] = mmg(sdT + 16 * w * LL, LL, 1, sT + 16 * j * CP, 1, CP, 0, 16 * (j + 1), zero4());
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sdT[tr[r] * LL + 16 * j + ln] = U[j][r];
+    __syncthreads();
+    // dA = -T^T U on s < t (T[j][t] is zero below j = t); then the gate terms, F and scale D o dP
+    float rowc[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 Fv[4], DPv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f32x4 dA = zero4();
+        if (j <= w) dA = mmg(sT + 16 * w, 1, CP, sdT + 16 * j, LL, 1, 16 * w, BC, dA);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = tr[r], s2 = 16 * j + ln;
+            const float d = s2 <= t ? expf(Gr[r] - sC[s2]) : 0.f;
+            const float a = s2 < t ? -dA[r] : 0.f;
+            const float kk = sKK[t * LL + s2];
+            pB[r] += a * d * kk;
+            Fv[j][r] = a * bb[r] * d;
+            DPv[j][r] = s2 <= t ? scale * d * aP[j][r] : 0.f;
+            const float c = (s2 <= t ? aP[j][r] * sP[t * LL + s2] : 0.f) + Fv[j][r] * kk;
+            rowc[r] += c;
+            sKK[t * LL + s2] = c;  // own entry: K K^T is not read again
+        }
+    }
+    __syncthreads();  // U is no longer read
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sdT[tr[r] * LL + 16 * j + ln] = Fv[j][r];
+            sDP[tr[r] * LL + 16 * j + ln] = DPv[j][r];
+        }
+    __syncthreads();
+    // dq += (scale D o dP) K;  dk += (scale D o dP)^T Q + F K + F^T K
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        aQ[j] = mmg(sDP + 16 * w * LL, LL, 1, sK + 16 * j, KP, 1, 0, 16 * (w + 1), aQ[j]);
+        aK[j] = mmg(sDP + 16 * w, 1, LL, sQ + 16 * j, KP, 1, 16 * w, BC, aK[j]);
+        aK[j] = mmg(sdT + 16 * w * LL, LL, 1, sK + 16 * j, KP, 1, 0, 16 * (w + 1), aK[j]);
+        aK[j] = mmg(sdT + 16 * w, 1, LL, sK + 16 * j, KP, 1, 16 * w, BC, aK[j]);
+    }
+    // row sums over the 16 lanes of each row group; <dS', S> over the workgroup
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pGam[r] += __shfl_xor(pGam[r], o, 64);
+            pE[r] += __shfl_xor(pE[r], o, 64);
+            pB[r] += __shfl_xor(pB[r], o, 64);
+            rowc[r] += __shfl_xor(rowc[r], o, 64);
+        }
+    for (int o = 1; o < 64; o <<= 1) pGL += __shfl_xor(pGL, o, 64);
+    if (lane == 0) sRed[w] = pGL;
+    if (ln == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sDG[tr[r]] = pGam[r] * gam[r] - pE[r] * ee[r] + rowc[r];
+            sEE[tr[r]] = pE[r] * ee[r];
+            if (tr[r] < L) dbeta[(row0 + tr[r]) * H + h] = pB[r];
+        }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (tr[r] < L) {
+                const long o = ((row0 + tr[r]) * H + h) * (long)KD + 16 * j + ln;
+                dq[o] = f2bf(aQ[j][r]);
+                dk[o] = f2bf(aK[j][r]);
+            }
+    __syncthreads();
+    {
+        // column sums of the gate terms: wavefront w over rows 16 w .. 16 w + 15, lane = column
+        float part = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) part += sKK[(16 * w + tt) * LL + lane];
+        sCol[tid] = part;
+    }
+    __syncthreads();
+    if (tid < BC) {
+        const float col = (sCol[tid] + sCol[64 + tid]) + (sCol[128 + tid] + sCol[192 + tid]);
+        float dG = sDG[tid] - col;
+        // G_L (token 63: padded tokens repeat the last real G) also carries e's and Gamma_L's terms
+        float se = sEE[tid];
+        for (int o = 1; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
+        if (tid == BC - 1) {
+            float gsum = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NT / 64; ++ww) gsum += sRed[ww];
+            dG += se + gsum * gl;
+        }
+        // dg = the reverse cumulative sum of dG over the chunk: lane l scans dG of token 63 - l
+        const float rev = __shfl(dG, BC - 1 - tid, 64);
+        const float cs = wave_inclusive_scan(rev);
+        const float dgt = __shfl(cs, BC - 1 - tid, 64);
+        if (tid < L) dg[(row0 + tid) * H + h] = dgt;
+    }
+}
+
 template <typename ST, int KD>
 hipError_t run_bwd(const ST* q, const ST* k, const ST* v, const float* g, const float* beta, const float* h0,
                    const ST* dout, const float* dht, const int32_t* cu, const GdnBwdWorkspace& ws, int N, int B,
@@ -666,9 +1035,19 @@ hipError_t run_bwd(const ST* q, const ST* k, const ST* v, const float* g, const 
     }
     if (slots > 0) {
         timing_begin("gdn_bwd_grad", s);
-        gdn_bwd_grad_kernel<ST, KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, v, dout, ws.rec, ws.states, ws.dstates,
-                                                                          table, cu, T, H, V, nc, scale, dq, dk, dv, dg,
-                                                                          dbeta);
+        // bf16 inputs with whole 32-value slices: the bf16-operand kernel
+        bool wide = false;
+        if constexpr (sizeof(ST) == 2) {
+            wide = V % 32 == 0;
+            if (wide)
+                gdn_bwd_grad16_kernel<KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, v, dout, ws.rec, ws.states,
+                                                                                  ws.dstates, table, cu, T, H, V, nc,
+                                                                                  scale, dq, dk, dv, dg, dbeta);
+        }
+        if (!wide)
+            gdn_bwd_grad_kernel<ST, KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, v, dout, ws.rec, ws.states,
+                                                                              ws.dstates, table, cu, T, H, V, nc, scale,
+                                                                              dq, dk, dv, dg, dbeta);
         timing_end(s);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
