@@ -999,6 +999,179 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// The two chains for bf16 inputs, on the operand forms of gdn_bwd_grad16_kernel (bf16 LDS rows; row-form and
+// column-form products): the same steps as gdn_bwd_states_kernel and gdn_bwd_dstate_kernel.
+// ---------------------------------------------------------------------------------------------------------
+template <int KD>
+__global__ __launch_bounds__(NT) void gdn_bwd_states16_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                                              const float* __restrict__ h0, const int32_t* __restrict__ cu,
+                                                              const int* __restrict__ chunk_off, const float* __restrict__ rec,
+                                                              int T, int H, int V, int n_seq, int nc, int nvs,
+                                                              float* __restrict__ states) {
+    typedef BwdRec<KD> RL;
+    typedef Elem<bf16_t> El;
+    constexpr int KP = KD + 8, CP = BC + 8, VP = 16 + 8, JPW = KD / 64;
+    __shared__ __align__(16) bf16_t sK[BC * KP], sS[16 * KP], sTt[BC * CP], sV[BC * VP], sZ[BC * VP], sE[BC * VP];
+    __shared__ float sC[256];
+    int chain, vs;
+    xcd_split(blockIdx.x, nvs, chain, vs);
+    if (chain >= n_seq * H) return;
+    const int n = chain / H, h = chain % H, tid = threadIdx.x, v0 = 16 * vs;
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    int b, bos, eos, slot0;
+    seq_of(n, cu, chunk_off, T, nc, b, bos, eos, slot0);
+    const int nch = (eos - bos + BC - 1) / BC;
+    f32x4 S[JPW];
+#pragma unroll
+    for (int i = 0; i < JPW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[i][r] = h0 ? h0[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] : 0.f;
+    Tile<bf16_t, BC, KD> tk;
+    Tile<bf16_t, BC, BC> tt;
+    Tile<bf16_t, BC, 16> tv;
+    float cf = 0.f;
+    auto issue = [&](int ci) __attribute__((always_inline)) {
+        const long row0 = (long)b * T + bos + (long)ci * BC;
+        const int L = min(BC, eos - (bos + ci * BC));
+        const float* R = rec + ((size_t)(slot0 + ci) * H + h) * RL::FLOATS;
+        tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tt.load(rec_t<bf16_t, KD>(R) + BC * BC, BC, BC);  // T^T
+        tv.load(v + (row0 * H + h) * (long)V + v0, (long)H * V, L);
+        cf = R[RL::C_OFF + tid];
+    };
+    if (nch > 0) issue(0);
+    for (int ci = 0; ci < nch; ++ci) {
+        float* Sout = states + (((size_t)(slot0 + ci) * H + h) * V + v0) * KD;
+#pragma unroll
+        for (int i = 0; i < JPW; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sout[(4 * lg + r) * KD + 16 * (JPW * w + i) + ln] = S[i][r];
+            put_rows(sS, KP, 0, 16 * (JPW * w + i), S[i]);
+        }
+        tk.template store_raw<KP>(sK);
+        tt.template store_raw<CP>(sTt);
+        tv.template store_raw<VP>(sV);
+        sC[tid] = cf;
+        __syncthreads();
+        if (ci + 1 < nch) issue(ci + 1);
+        // Z = diag(beta) (V - diag(Gamma) K S^T) on token tile w (row form)
+        const f32x4 X = mmb(sK + 16 * w * KP, KP, sS, KP, 0, KD, zero4());
+        const f32x4 vv = El::unpack(col4(sV, VP, 16 * w, 0));
+        f32x4 z;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * w + 4 * lg + r;
+            z[r] = sC[192 + t] * (vv[r] - sC[64 + t] * X[r]);
+        }
+        put_rows(sZ, VP, 16 * w, 0, z);
+        __syncthreads();
+        // e R = e T Z (column form, T^T rows)
+        f32x4 Rv = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < BC; k0 += 32)
+            if (k0 < 16 * (w + 1)) Rv = mma32(col8(sTt, CP, k0, 16 * w), col8(sZ, VP, k0, 0), Rv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Rv[r] *= sC[128 + 16 * w + 4 * lg + r];
+        put_rows(sE, VP, 16 * w, 0, Rv);
+        __syncthreads();
+        // S <- Gamma_L S + (e R)^T K on the wavefront's key tiles (column form)
+        const float gl = sC[64 + BC - 1];
+#pragma unroll
+        for (int i = 0; i < JPW; ++i) {
+            f32x4 acc = S[i] * gl;
+#pragma unroll
+            for (int k0 = 0; k0 < BC; k0 += 32) acc = mma32(col8(sE, VP, k0, 0), col8(sK, KP, k0, 16 * (JPW * w + i)), acc);
+            S[i] = acc;
+        }
+        __syncthreads();
+    }
+}
+
+template <int KD>
+__global__ __launch_bounds__(NT) void gdn_bwd_dstate16_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ dout,
+                                                              const float* __restrict__ dht, const int32_t* __restrict__ cu,
+                                                              const int* __restrict__ chunk_off, const float* __restrict__ rec,
+                                                              int T, int H, int V, int n_seq, int nc, int nvs,
+                                                              float* __restrict__ dstates, float* __restrict__ dh0) {
+    typedef BwdRec<KD> RL;
+    constexpr int KP = KD + 8, VP = 16 + 8, JPW = KD / 64;
+    __shared__ __align__(16) bf16_t sK[BC * KP], sW[BC * KP], sQt[BC * KP], sD[16 * KP], sO[BC * VP], sZt[BC * VP];
+    __shared__ float sC[256];
+    int chain, vs;
+    xcd_split(blockIdx.x, nvs, chain, vs);
+    if (chain >= n_seq * H) return;
+    const int n = chain / H, h = chain % H, tid = threadIdx.x, v0 = 16 * vs;
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    int b, bos, eos, slot0;
+    seq_of(n, cu, chunk_off, T, nc, b, bos, eos, slot0);
+    const int nch = (eos - bos + BC - 1) / BC;
+    f32x4 dS[JPW];
+#pragma unroll
+    for (int i = 0; i < JPW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dS[i][r] = dht ? dht[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] : 0.f;
+    // chunk ci's K rows, W, Qt, coefficients and dO slice, loaded one chunk ahead (chunks run backwards)
+    Tile<bf16_t, BC, KD> tk, tw, tq;
+    Tile<bf16_t, BC, 16> to;
+    float cf = 0.f;
+    auto issue = [&](int ci) __attribute__((always_inline)) {
+        const long row0 = (long)b * T + bos + (long)ci * BC;
+        const int L = min(BC, eos - (bos + ci * BC));
+        const float* R = rec + ((size_t)(slot0 + ci) * H + h) * RL::FLOATS;
+        tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tw.load(rec_w<bf16_t, KD>(R), KD, BC);
+        tq.load(rec_qt<bf16_t, KD>(R), KD, BC);
+        to.load(dout + (row0 * H + h) * (long)V + v0, (long)H * V, L);
+        cf = R[RL::C_OFF + tid];
+    };
+    if (nch > 0) issue(nch - 1);
+    for (int ci = nch - 1; ci >= 0; --ci) {
+        float* Dout = dstates + (((size_t)(slot0 + ci) * H + h) * V + v0) * KD;
+#pragma unroll
+        for (int i = 0; i < JPW; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Dout[(4 * lg + r) * KD + 16 * (JPW * w + i) + ln] = dS[i][r];
+            put_rows(sD, KP, 0, 16 * (JPW * w + i), dS[i]);
+        }
+        tk.template store_raw<KP>(sK);
+        tw.template store_raw<KP>(sW);
+        tq.template store_raw<KP>(sQt);
+        to.template store_raw<VP>(sO);
+        sC[tid] = cf;
+        __syncthreads();
+        if (ci > 0) issue(ci - 1);
+        // Z[v][t] = e_t (dS' K^T)[v][t] on token tile w (row form), kept by token rows for the column form
+        f32x4 Zt = mmb(sD, KP, sK + 16 * w * KP, KP, 0, KD, zero4());
+        Zt = Zt * sC[128 + 16 * w + ln];
+        put_cols(sZt, VP, 0, 16 * w, Zt);
+        __syncthreads();
+        // dS = Gamma_L dS' + dO^T Qt - Z W on the wavefront's key tiles (column form)
+        const float gl = sC[64 + BC - 1];
+#pragma unroll
+        for (int i = 0; i < JPW; ++i) {
+            const int jc = JPW * w + i;
+            f32x4 a = dS[i] * gl, zw = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < BC; k0 += 32) {
+                a = mma32(col8(sO, VP, k0, 0), col8(sQt, KP, k0, 16 * jc), a);
+                zw = mma32(col8(sZt, VP, k0, 0), col8(sW, KP, k0, 16 * jc), zw);
+            }
+            dS[i] = a - zw;
+        }
+        __syncthreads();
+    }
+    if (dh0) {
+#pragma unroll
+        for (int i = 0; i < JPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dh0[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] = dS[i][r];
+    }
+}
+
 template <typename ST, int KD>
 hipError_t run_bwd(const ST* q, const ST* k, const ST* v, const float* g, const float* beta, const float* h0,
                    const ST* dout, const float* dht, const int32_t* cu, const GdnBwdWorkspace& ws, int N, int B,
@@ -1024,12 +1197,19 @@ hipError_t run_bwd(const ST* q, const ST* k, const ST* v, const float* g, const 
         const int nvs = V / 16;
         const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * nvs);
         timing_begin("gdn_bwd_states", s);
-        gdn_bwd_states_kernel<ST, KD><<<grid, NT, 0, s>>>(k, v, h0, cu, ws.chunk_off, ws.rec, T, H, V, N, nc, nvs, ws.states);
+        if constexpr (sizeof(ST) == 2)
+            gdn_bwd_states16_kernel<KD><<<grid, NT, 0, s>>>(k, v, h0, cu, ws.chunk_off, ws.rec, T, H, V, N, nc, nvs, ws.states);
+        else
+            gdn_bwd_states_kernel<ST, KD><<<grid, NT, 0, s>>>(k, v, h0, cu, ws.chunk_off, ws.rec, T, H, V, N, nc, nvs, ws.states);
         timing_end(s);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         timing_begin("gdn_bwd_dstate", s);
-        gdn_bwd_dstate_kernel<ST, KD><<<grid, NT, 0, s>>>(k, dout, dht, cu, ws.chunk_off, ws.rec, T, H, V, N, nc, nvs,
-                                                          ws.dstates, dh0);
+        if constexpr (sizeof(ST) == 2)
+            gdn_bwd_dstate16_kernel<KD><<<grid, NT, 0, s>>>(k, dout, dht, cu, ws.chunk_off, ws.rec, T, H, V, N, nc, nvs,
+                                                            ws.dstates, dh0);
+        else
+            gdn_bwd_dstate_kernel<ST, KD><<<grid, NT, 0, s>>>(k, dout, dht, cu, ws.chunk_off, ws.rec, T, H, V, N, nc, nvs,
+                                                              ws.dstates, dh0);
         timing_end(s);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
