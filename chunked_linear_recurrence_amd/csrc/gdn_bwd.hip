@@ -81,7 +81,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     constexpr int LK = KD + 1, LL = BC + 1, LU = 17, NJ = KD / 16;
     __shared__ float sK[BC * LK], sQ[BC * LK], sW[BC * LK];
     __shared__ float sA[BC * LL], sT[BC * LL], sP[BC * LL];
-    __shared__ float sG[BC], sB[BC], sU[4 * 16 * LU];
+    __shared__ float sG[BC], sB[BC], sGam[BC], sU[4 * 16 * LU];
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     int b, t0, L;
     if (!chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
@@ -96,7 +96,9 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     if (tid < BC) {
         const float gv = tid < L ? g[(row0 + tid) * H + h] : 0.f;
         sB[tid] = tid < L ? beta[(row0 + tid) * H + h] : 0.f;
-        sG[tid] = wave_inclusive_scan(gv);
+        const float G = wave_inclusive_scan(gv);
+        sG[tid] = G;
+        sGam[tid] = expf(G);
     }
     __syncthreads();
     const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
@@ -122,19 +124,24 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     __syncthreads();
     // diagonal blocks: wavefront w inverts block w, lane j < 16 solving column j: x_j = 1,
     // x_i = -sum_{j<=s<i} A_ii[i][s] x_s
+    // (the column in registers; its entries above the diagonal are zero, so the terms s2 < j change nothing)
     if (lane < 16) {
         const int o = 16 * w, j = lane;
+        float xs[16];
+#pragma unroll
         for (int i = 0; i < 16; ++i) {
             float x = i == j ? 1.f : 0.f;
-            if (i > j)
-                for (int s2 = j; s2 < i; ++s2) x -= sA[(o + i) * LL + o + s2] * sT[(o + s2) * LL + o + j];
-            sT[(o + i) * LL + o + j] = x;
+#pragma unroll
+            for (int s2 = 0; s2 < i; ++s2) x -= sA[(o + i) * LL + o + s2] * xs[s2];
+            xs[i] = x;
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sT[(o + i) * LL + o + j] = xs[i];
     }
     // (K scaled by beta Gamma per token, for W: K is not read again as itself)
     for (int i = tid; i < BC * KD; i += NT) {
         const int t = i / KD, c = i % KD;
-        sK[t * LK + c] *= sB[t] * expf(sG[t]);
+        sK[t * LK + c] *= sB[t] * sGam[t];
     }
     __syncthreads();
     // off-diagonal blocks, one block diagonal dd at a time: block (i, j = i - dd) by wavefront i
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tr[r], c = 16 * jc + ln;
-            RQ[t * KD + c] = Elem<ST>::from_f(scale * expf(sG[t]) * sQ[t * LK + c] - PW[r]);
+            RQ[t * KD + c] = Elem<ST>::from_f(scale * sGam[t] * sQ[t * LK + c] - PW[r]);
         }
     }
     for (int i = tid; i < BC * BC; i += NT) {
