@@ -24,6 +24,8 @@
 //   gdn_bwd_dstate_kernel  per (sequence, head, 16-row slice): the reverse chain, storing every chunk's
 //                          exit-state gradient, and dh0
 //   gdn_bwd_grad_kernel    per (chunk, head): dq, dk, dv, dg, dbeta of the chunk
+#include <type_traits>
+
 #include "f32_tiles.h"
 #include "sf_device.h"
 #include "sf_internal.h"
@@ -78,8 +80,12 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
                                                           const int2* __restrict__ table, const int32_t* __restrict__ cu,
                                                           int T, int H, int nc, float scale, float* __restrict__ rec) {
     typedef BwdRec<KD> RL;
-    constexpr int LK = KD + 1, LL = BC + 1, LU = 17, NJ = KD / 16;
-    __shared__ float sK[BC * LK], sQ[BC * LK], sW[BC * LK];
+    // K, Q and W in LDS in the input type (bf16 rows of 16-byte pieces: the products read them as they are, the
+    // same bf16 values the float32 tiles would round them to)
+    constexpr bool B16 = sizeof(ST) == 2;
+    typedef typename std::conditional<B16, bf16_t, float>::type LT;
+    constexpr int LK = B16 ? KD + 8 : KD + 1, LL = BC + 1, LU = 17, NJ = KD / 16;
+    __shared__ __align__(16) LT sK[BC * LK], sQ[BC * LK], sW[BC * LK];
     __shared__ float sA[BC * LL], sT[BC * LL], sP[BC * LL];
     __shared__ float sG[BC], sB[BC], sGam[BC], sU[4 * 16 * LU];
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
@@ -90,8 +96,13 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
         Tile<ST, BC, KD> tk, tq;
         tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
-        tk.store(sK);
-        tq.store(sQ);
+        if constexpr (B16) {
+            tk.template store_raw<LK>(sK);
+            tq.template store_raw<LK>(sQ);
+        } else {
+            tk.store(sK);
+            tq.store(sQ);
+        }
     }
     if (tid < BC) {
         const float gv = tid < L ? g[(row0 + tid) * H + h] : 0.f;
@@ -109,8 +120,13 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     for (int j = 0; j < 4; ++j) {
         f32x4 kk = zero4(), qk = zero4();
         if (j <= w) {
-            kk = mmx<ST>(sK + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, kk);
-            qk = mmx<ST>(sQ + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, qk);
+            if constexpr (B16) {
+                kk = mmb(sK + 16 * w * LK, LK, sK + 16 * j * LK, LK, 0, KD, kk);
+                qk = mmb(sQ + 16 * w * LK, LK, sK + 16 * j * LK, LK, 0, KD, qk);
+            } else {
+                kk = mmx<ST>(sK + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, kk);
+                qk = mmx<ST>(sQ + 16 * w * LK, LK, 1, sK + 16 * j * LK, 1, LK, 0, KD, qk);
+            }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -141,7 +157,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     // (K scaled by beta Gamma per token, for W: K is not read again as itself)
     for (int i = tid; i < BC * KD; i += NT) {
         const int t = i / KD, c = i % KD;
-        sK[t * LK + c] *= sB[t] * sGam[t];
+        sK[t * LK + c] = Elem<ST>::from_f(Elem<ST>::to_f(sK[t * LK + c]) * (sB[t] * sGam[t]));
     }
     __syncthreads();
     // off-diagonal blocks, one block diagonal dd at a time: block (i, j = i - dd) by wavefront i
@@ -167,10 +183,14 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     // W = T (beta Gamma K) on the wavefront's row tile (T is zero past column 16 w + 15)
 #pragma unroll
     for (int jc = 0; jc < NJ; ++jc) {
-        const f32x4 Wv = mmx<ST>(sT + 16 * w * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+        f32x4 Wv;
+        if constexpr (B16)
+            Wv = mmg(sT + 16 * w * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+        else
+            Wv = mmx<ST>(sT + 16 * w * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            sW[tr[r] * LK + 16 * jc + ln] = Wv[r];
+            sW[tr[r] * LK + 16 * jc + ln] = Elem<ST>::from_f(Wv[r]);
             RW[tr[r] * KD + 16 * jc + ln] = Elem<ST>::from_f(Wv[r]);
         }
     }
@@ -178,11 +198,15 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     // Qt = scale Gamma Q - P W
 #pragma unroll
     for (int jc = 0; jc < NJ; ++jc) {
-        const f32x4 PW = mmx<ST>(sP + 16 * w * LL, LL, 1, sW + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+        f32x4 PW;
+        if constexpr (B16)
+            PW = mmg(sP + 16 * w * LL, LL, 1, sW + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
+        else
+            PW = mmx<ST>(sP + 16 * w * LL, LL, 1, sW + 16 * jc, LK, 1, 0, 16 * (w + 1), zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tr[r], c = 16 * jc + ln;
-            RQ[t * KD + c] = Elem<ST>::from_f(scale * sGam[t] * sQ[t * LK + c] - PW[r]);
+            RQ[t * KD + c] = Elem<ST>::from_f(scale * sGam[t] * Elem<ST>::to_f(sQ[t * LK + c]) - PW[r]);
         }
     }
     for (int i = tid; i < BC * BC; i += NT) {
