@@ -100,11 +100,15 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
     }
     if (tid < BC) sB[tid] = tid < L ? beta[(row0 + tid) * H + h] : 0.f;
     __syncthreads();
-    // cumulative gate per channel, in place
+    // cumulative gate per channel, in place (the channel's 64 gates read into registers first)
     if (tid < KD) {
+        float gv[BC];
+#pragma unroll
+        for (int t = 0; t < BC; ++t) gv[t] = sG[t * LK + tid];
         float acc = 0.f;
+#pragma unroll
         for (int t = 0; t < BC; ++t) {
-            acc += sG[t * LK + tid];
+            acc += gv[t];
             sG[t * LK + tid] = acc;
         }
     }
