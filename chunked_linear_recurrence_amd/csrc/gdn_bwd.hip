@@ -727,8 +727,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
     constexpr int NJ = KD / 16;
     __shared__ __align__(16) bf16_t sK[BC * KP], sQ[BC * KP], sT[BC * CP], sTt[BC * CP], sPb[BC * CP];
     __shared__ float sP[BC * LL], sKK[BC * LL], sC[256];
-    // per-slice region (bf16); after the slices it holds dT (then U, then F) and scale D o dP (float)
-    constexpr int SLICE_BYTES = (2 * SW * KP + 5 * BC * VP + 3 * SW * CP) * 2, POST_BYTES = 2 * BC * LL * 4;
+    // per-slice region (bf16); after the slices it holds dT (then U, then F), F^T and scale D o dP both ways
+    constexpr int SLICE_BYTES = (2 * SW * KP + 5 * BC * VP + 3 * SW * CP) * 2, POST_BYTES = 4 * BC * CP * 2;
     __shared__ __align__(16) uint8_t sX[SLICE_BYTES > POST_BYTES ? SLICE_BYTES : POST_BYTES];
     bf16_t* const sS = reinterpret_cast<bf16_t*>(sX);  // [SW][KP] entry state rows of the slice
     bf16_t* const sD = sS + SW * KP;                    // [SW][KP] exit-state gradient rows
@@ -740,8 +740,6 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
     bf16_t* const sOt = sdR + BC * VP;                  // [SW][CP] dO^T
     bf16_t* const sRt = sOt + SW * CP;                  // [SW][CP] R^T
     bf16_t* const sXt = sRt + SW * CP;                  // [SW][CP] dX^T
-    float* const sdT = reinterpret_cast<float*>(sX);   // [64][LL] after the slices: dT, then U = dT T^T, then F
-    float* const sDP = sdT + BC * LL;                   // [64][LL] after the slices: scale D o dP
     __shared__ float sDG[BC], sEE[BC], sRed[NT / 64], sCol[NT];
 
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
@@ -920,28 +918,36 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
             aQ[j][r] *= scale * gam[r];
             aK[j][r] += ee[r] * aK2[j][r];
         }
-    // dT to LDS, U = dT T^T (T[s][j] is zero past j = s)
+    // after the slices, bf16 blocks in the slice region: dT, then U, then F by rows; F^T; scale D o dP by rows
+    // and transposed
+    bf16_t* const bF = reinterpret_cast<bf16_t*>(sX);  // [64][CP]
+    bf16_t* const bFt = bF + BC * CP;
+    bf16_t* const bD = bFt + BC * CP;
+    bf16_t* const bDt = bD + BC * CP;
+    static_assert(4 * BC * CP * 2 <= sizeof(sX), "post-slice blocks fit the slice region");
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sdT[tr[r] * LL + 16 * j + ln] = aT[j][r];
+    for (int j = 0; j < 4; ++j) put_rows(bF, CP, 16 * w, 16 * j, aT[j]);
     __syncthreads();
+    // U = dT T^T (row form; T[s][j] is zero past j = s)
     f32x4 U[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) U[j] = mmg(sdT + 16 * w * LL, LL, 1, sT + 16 * j * CP, 1, CP, 0, 16 * (j + 1), zero4());
+    for (int j = 0; j < 4; ++j) U[j] = mmb(bF + 16 * w * CP, CP, sT + 16 * j * CP, CP, 0, 16 * (j + 1), zero4());
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sdT[tr[r] * LL + 16 * j + ln] = U[j][r];
+    for (int j = 0; j < 4; ++j) put_rows(bF, CP, 16 * w, 16 * j, U[j]);
     __syncthreads();
-    // dA = -T^T U on s < t (T[j][t] is zero below j = t); then the gate terms, F and scale D o dP
+    // dA = -T^T U on s < t (column form over the rows of T and U; T[k][t] is zero for k < t); then the gate
+    // terms, F and scale D o dP
     float rowc[4] = {0.f, 0.f, 0.f, 0.f};
     f32x4 Fv[4], DPv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         f32x4 dA = zero4();
-        if (j <= w) dA = mmg(sT + 16 * w, 1, CP, sdT + 16 * j, LL, 1, 16 * w, BC, dA);
+        if (j <= w) {
+#pragma unroll
+            for (int k0 = 0; k0 < BC; k0 += 32)
+                if (k0 + 32 > 16 * w) dA = mma32(col8(sT, CP, k0, 16 * w), col8(bF, CP, k0, 16 * j), dA);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tr[r], s2 = 16 * j + ln;
@@ -958,20 +964,28 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
     }
     __syncthreads();  // U is no longer read
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            sdT[tr[r] * LL + 16 * j + ln] = Fv[j][r];
-            sDP[tr[r] * LL + 16 * j + ln] = DPv[j][r];
-        }
+    for (int j = 0; j < 4; ++j) {
+        put_rows(bF, CP, 16 * w, 16 * j, Fv[j]);
+        put_cols(bFt, CP, 16 * w, 16 * j, Fv[j]);
+        put_rows(bD, CP, 16 * w, 16 * j, DPv[j]);
+        put_cols(bDt, CP, 16 * w, 16 * j, DPv[j]);
+    }
     __syncthreads();
-    // dq += (scale D o dP) K;  dk += (scale D o dP)^T Q + F K + F^T K
+    // dq += (scale D o dP) K;  dk += (scale D o dP)^T Q + F K + F^T K (column form over the tokens)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        aQ[j] = mmg(sDP + 16 * w * LL, LL, 1, sK + 16 * j, KP, 1, 0, 16 * (w + 1), aQ[j]);
-        aK[j] = mmg(sDP + 16 * w, 1, LL, sQ + 16 * j, KP, 1, 16 * w, BC, aK[j]);
-        aK[j] = mmg(sdT + 16 * w * LL, LL, 1, sK + 16 * j, KP, 1, 0, 16 * (w + 1), aK[j]);
-        aK[j] = mmg(sdT + 16 * w, 1, LL, sK + 16 * j, KP, 1, 16 * w, BC, aK[j]);
+#pragma unroll
+        for (int k0 = 0; k0 < BC; k0 += 32) {
+            const bf16x8 kcol = col8(sK, KP, k0, 16 * j);
+            if (k0 < 16 * (w + 1)) {
+                aQ[j] = mma32(col8(bDt, CP, k0, 16 * w), kcol, aQ[j]);
+                aK[j] = mma32(col8(bFt, CP, k0, 16 * w), kcol, aK[j]);
+            }
+            if (k0 + 32 > 16 * w) {
+                aK[j] = mma32(col8(bD, CP, k0, 16 * w), col8(sQ, KP, k0, 16 * j), aK[j]);
+                aK[j] = mma32(col8(bF, CP, k0, 16 * w), kcol, aK[j]);
+            }
+        }
     }
     // row sums over the 16 lanes of each row group; <dS', S> over the workgroup
 #pragma unroll
