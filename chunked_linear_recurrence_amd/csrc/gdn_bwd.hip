@@ -17,13 +17,17 @@
 //   dbeta = rowsum(Y o dZ) + rowsum(dA o D_strict o K K^T),
 //   dG_t from the gate's four places (Gamma, e, D in P, D in A), dg = the reverse cumulative sum of dG.
 //
-// Kernels (float32 arithmetic throughout; q, k, v, do and the gradients dq, dk, dv in the input type):
+// Kernels (float32 accumulation and elementwise arithmetic; q, k, v, do and the gradients dq, dk, dv in the
+// input type; the products in the input type's arithmetic):
 //   gdn_bwd_prep_kernel    per (chunk, head): T, W, Qt and the coefficients into a record
 //   gdn_bwd_states_kernel  per (sequence, head, 16-row slice): the forward chain, storing every chunk's
-//                          entry state
+//                          entry state (gdn_bwd_states16_kernel for bf16 inputs)
 //   gdn_bwd_dstate_kernel  per (sequence, head, 16-row slice): the reverse chain, storing every chunk's
-//                          exit-state gradient, and dh0
-//   gdn_bwd_grad_kernel    per (chunk, head): dq, dk, dv, dg, dbeta of the chunk
+//                          exit-state gradient, and dh0 (gdn_bwd_dstate16_kernel for bf16 inputs)
+//   gdn_bwd_grad_kernel    per (chunk, head): dq, dk, dv, dg, dbeta of the chunk (gdn_bwd_grad16_kernel for
+//                          bf16 inputs)
+// The float32-input kernels keep their operands in float32 in LDS; the bf16 ones keep bf16 operands and
+// read them in the row and column forms described at gdn_bwd_grad16_kernel.
 #include <type_traits>
 
 #include "f32_tiles.h"
@@ -1260,16 +1264,11 @@ hipError_t run_bwd(const ST* q, const ST* k, const ST* v, const float* g, const 
     }
     if (slots > 0) {
         timing_begin("gdn_bwd_grad", s);
-        // bf16 inputs with whole 32-value slices: the bf16-operand kernel
-        bool wide = false;
-        if constexpr (sizeof(ST) == 2) {
-            wide = V % 32 == 0;
-            if (wide)
-                gdn_bwd_grad16_kernel<KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, v, dout, ws.rec, ws.states,
-                                                                                  ws.dstates, table, cu, T, H, V, nc,
-                                                                                  scale, dq, dk, dv, dg, dbeta);
-        }
-        if (!wide)
+        if constexpr (sizeof(ST) == 2)
+            gdn_bwd_grad16_kernel<KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, v, dout, ws.rec, ws.states,
+                                                                              ws.dstates, table, cu, T, H, V, nc, scale,
+                                                                              dq, dk, dv, dg, dbeta);
+        else
             gdn_bwd_grad_kernel<ST, KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, v, dout, ws.rec, ws.states,
                                                                               ws.dstates, table, cu, T, H, V, nc, scale,
                                                                               dq, dk, dv, dg, dbeta);
