@@ -1077,21 +1077,24 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states16_kernel(const bf16_t* __re
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             S[i][r] = h0 ? h0[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] : 0.f;
-    Tile<bf16_t, BC, KD> tk;
-    Tile<bf16_t, BC, BC> tt;
-    Tile<bf16_t, BC, 16> tv;
-    float cf = 0.f;
-    auto issue = [&](int ci) __attribute__((always_inline)) {
+    // the operands of a chunk in registers (two sets: chunk c's load is issued two steps before its step,
+    // and the loop takes two steps per pass so that each set has fixed registers)
+    struct Ops16 {
+        Tile<bf16_t, BC, KD> tk;
+        Tile<bf16_t, BC, BC> tt;
+        Tile<bf16_t, BC, 16> tv;
+        float cf;
+    } opA, opB;
+    auto issue = [&](int ci, Ops16& o) __attribute__((always_inline)) {
         const long row0 = (long)b * T + bos + (long)ci * BC;
         const int L = min(BC, eos - (bos + ci * BC));
         const float* R = rec + ((size_t)(slot0 + ci) * H + h) * RL::FLOATS;
-        tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
-        tt.load(rec_t<bf16_t, KD>(R) + BC * BC, BC, BC);  // T^T
-        tv.load(v + (row0 * H + h) * (long)V + v0, (long)H * V, L);
-        cf = R[RL::C_OFF + tid];
+        o.tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        o.tt.load(rec_t<bf16_t, KD>(R) + BC * BC, BC, BC);  // T^T
+        o.tv.load(v + (row0 * H + h) * (long)V + v0, (long)H * V, L);
+        o.cf = R[RL::C_OFF + tid];
     };
-    if (nch > 0) issue(0);
-    for (int ci = 0; ci < nch; ++ci) {
+    auto step = [&](int ci, Ops16& o) __attribute__((always_inline)) {
         float* Sout = states + (((size_t)(slot0 + ci) * H + h) * V + v0) * KD;
 #pragma unroll
         for (int i = 0; i < JPW; ++i) {
@@ -1099,12 +1102,12 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states16_kernel(const bf16_t* __re
             for (int r = 0; r < 4; ++r) Sout[(4 * lg + r) * KD + 16 * (JPW * w + i) + ln] = S[i][r];
             put_rows(sS, KP, 0, 16 * (JPW * w + i), S[i]);
         }
-        tk.template store_raw<KP>(sK);
-        tt.template store_raw<CP>(sTt);
-        tv.template store_raw<VP>(sV);
-        sC[tid] = cf;
+        o.tk.template store_raw<KP>(sK);
+        o.tt.template store_raw<CP>(sTt);
+        o.tv.template store_raw<VP>(sV);
+        sC[tid] = o.cf;
         __syncthreads();
-        if (ci + 1 < nch) issue(ci + 1);
+        if (ci + 2 < nch) issue(ci + 2, o);
         // Z = diag(beta) (V - diag(Gamma) K S^T) on token tile w (row form)
         const f32x4 X = mmb(sK + 16 * w * KP, KP, sS, KP, 0, KD, zero4());
         const f32x4 vv = El::unpack(col4(sV, VP, 16 * w, 0));
@@ -1135,6 +1138,12 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states16_kernel(const bf16_t* __re
             S[i] = acc;
         }
         __syncthreads();
+    };
+    if (nch > 0) issue(0, opA);
+    if (nch > 1) issue(1, opB);
+    for (int ci = 0; ci < nch; ci += 2) {
+        step(ci, opA);
+        if (ci + 1 < nch) step(ci + 1, opB);
     }
 }
 
@@ -1162,22 +1171,25 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate16_kernel(const bf16_t* __re
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             dS[i][r] = dht ? dht[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] : 0.f;
-    // chunk ci's K rows, W, Qt, coefficients and dO slice, loaded one chunk ahead (chunks run backwards)
-    Tile<bf16_t, BC, KD> tk, tw, tq;
-    Tile<bf16_t, BC, 16> to;
-    float cf = 0.f;
-    auto issue = [&](int ci) __attribute__((always_inline)) {
+    // chunk ci's K rows, W, Qt, coefficients and dO slice in registers (two sets: a chunk's load is issued two
+    // steps before its step, chunks running backwards, and the loop takes two steps per pass so that each set
+    // has fixed registers)
+    struct Ops16 {
+        Tile<bf16_t, BC, KD> tk, tw, tq;
+        Tile<bf16_t, BC, 16> to;
+        float cf;
+    } opA, opB;
+    auto issue = [&](int ci, Ops16& o) __attribute__((always_inline)) {
         const long row0 = (long)b * T + bos + (long)ci * BC;
         const int L = min(BC, eos - (bos + ci * BC));
         const float* R = rec + ((size_t)(slot0 + ci) * H + h) * RL::FLOATS;
-        tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
-        tw.load(rec_w<bf16_t, KD>(R), KD, BC);
-        tq.load(rec_qt<bf16_t, KD>(R), KD, BC);
-        to.load(dout + (row0 * H + h) * (long)V + v0, (long)H * V, L);
-        cf = R[RL::C_OFF + tid];
+        o.tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        o.tw.load(rec_w<bf16_t, KD>(R), KD, BC);
+        o.tq.load(rec_qt<bf16_t, KD>(R), KD, BC);
+        o.to.load(dout + (row0 * H + h) * (long)V + v0, (long)H * V, L);
+        o.cf = R[RL::C_OFF + tid];
     };
-    if (nch > 0) issue(nch - 1);
-    for (int ci = nch - 1; ci >= 0; --ci) {
+    auto step = [&](int ci, Ops16& o) __attribute__((always_inline)) {
         float* Dout = dstates + (((size_t)(slot0 + ci) * H + h) * V + v0) * KD;
 #pragma unroll
         for (int i = 0; i < JPW; ++i) {
@@ -1185,13 +1197,13 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate16_kernel(const bf16_t* __re
             for (int r = 0; r < 4; ++r) Dout[(4 * lg + r) * KD + 16 * (JPW * w + i) + ln] = dS[i][r];
             put_rows(sD, KP, 0, 16 * (JPW * w + i), dS[i]);
         }
-        tk.template store_raw<KP>(sK);
-        tw.template store_raw<KP>(sW);
-        tq.template store_raw<KP>(sQt);
-        to.template store_raw<VP>(sO);
-        sC[tid] = cf;
+        o.tk.template store_raw<KP>(sK);
+        o.tw.template store_raw<KP>(sW);
+        o.tq.template store_raw<KP>(sQt);
+        o.to.template store_raw<VP>(sO);
+        sC[tid] = o.cf;
         __syncthreads();
-        if (ci > 0) issue(ci - 1);
+        if (ci >= 2) issue(ci - 2, o);
         // Z[v][t] = e_t (dS' K^T)[v][t] on token tile w (row form), kept by token rows for the column form
         f32x4 Zt = mmb(sD, KP, sK + 16 * w * KP, KP, 0, KD, zero4());
         Zt = Zt * sC[128 + 16 * w + ln];
@@ -1211,6 +1223,12 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate16_kernel(const bf16_t* __re
             dS[i] = a - zw;
         }
         __syncthreads();
+    };
+    if (nch > 0) issue(nch - 1, opA);
+    if (nch > 1) issue(nch - 2, opB);
+    for (int ci = nch - 1; ci >= 0; ci -= 2) {
+        step(ci, opA);
+        if (ci >= 1) step(ci - 1, opB);
     }
     if (dh0) {
 #pragma unroll
