@@ -533,64 +533,63 @@ __global__ __launch_bounds__(NT) void kda_chain16_kernel(const float* __restrict
         for (int r = 0; r < 4; ++r)
             S[i][r] = h0 ? h0[(((size_t)n * H + h) * VD + v0 + 4 * lg + r) * KD + c] : 0.f;
     }
-    Tile<bf16_t, BC, KD> tw, tq;
-    Tile<bf16_t, KD, BC> tk;
-    Tile<bf16_t, BC, BC> tp;
-    Tile<float, BC, 16> tu;
-    float gl = 0.f;
+    // a chunk's record tiles in registers (two sets: a chunk's loads are issued two steps before its step, in
+    // three groups spread over the step, and the loop takes two steps per pass so that each set has fixed
+    // registers)
+    struct Ops16 {
+        Tile<bf16_t, BC, KD> tw, tq;
+        Tile<bf16_t, KD, BC> tk;
+        Tile<bf16_t, BC, BC> tp;
+        Tile<float, BC, 16> tu;
+        float gl;
+    } opA, opB;
     auto recb = [&](int ci) __attribute__((always_inline)) {
         return reinterpret_cast<const uint8_t*>(rec + ((size_t)(slot0 + ci) * H + h) * RL::floats(VD));
     };
-    // the next chunk's loads in three groups spread over the step
-    auto issue_w = [&](int ci) __attribute__((always_inline)) {
+    auto issue_w = [&](int ci, Ops16& o) __attribute__((always_inline)) {
         const uint8_t* R = recb(ci);
-        tw.load(reinterpret_cast<const bf16_t*>(R + R16::W_OFF), KD, BC);
-        tu.load(reinterpret_cast<const float*>(R + R16::U_OFF) + v0, VD, BC);
-        gl = tid < KD ? reinterpret_cast<const float*>(R + R16::gl_off(VD))[tid] : 0.f;
+        o.tw.load(reinterpret_cast<const bf16_t*>(R + R16::W_OFF), KD, BC);
+        o.tu.load(reinterpret_cast<const float*>(R + R16::U_OFF) + v0, VD, BC);
+        o.gl = tid < KD ? reinterpret_cast<const float*>(R + R16::gl_off(VD))[tid] : 0.f;
     };
-    auto issue_q = [&](int ci) __attribute__((always_inline)) {
+    auto issue_q = [&](int ci, Ops16& o) __attribute__((always_inline)) {
         const uint8_t* R = recb(ci);
-        tq.load(reinterpret_cast<const bf16_t*>(R + R16::Q_OFF), KD, BC);
-        tp.load(reinterpret_cast<const bf16_t*>(R + R16::P_OFF), BC, BC);
+        o.tq.load(reinterpret_cast<const bf16_t*>(R + R16::Q_OFF), KD, BC);
+        o.tp.load(reinterpret_cast<const bf16_t*>(R + R16::P_OFF), BC, BC);
     };
-    auto issue_k = [&](int ci) __attribute__((always_inline)) {
-        tk.load(reinterpret_cast<const bf16_t*>(recb(ci) + R16::KT_OFF), BC, KD);
+    auto issue_k = [&](int ci, Ops16& o) __attribute__((always_inline)) {
+        o.tk.load(reinterpret_cast<const bf16_t*>(recb(ci) + R16::KT_OFF), BC, KD);
     };
-    if (nch > 0) {
-        issue_w(0);
-        issue_q(0);
-        issue_k(0);
-    }
     const int tr0 = 16 * w + 4 * lg;
-    for (int ci = 0; ci < nch; ++ci) {
+    auto step = [&](int ci, Ops16& o) __attribute__((always_inline)) {
         const long row0 = (long)b * T + bos + (long)ci * BC;
         const int L = min(BC, eos - (bos + ci * BC));
 #pragma unroll
         for (int i = 0; i < JPW; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) sSb[(4 * lg + r) * LW + 16 * (JPW * w + i) + ln] = f2bf(S[i][r]);
-        tw.template store_raw<LW>(sW);
-        tq.template store_raw<LW>(sQg);
-        tk.template store_raw<LT>(sKt);
-        tp.template store_raw<LT>(sP);
-        tu.store(sU);
-        if (tid < KD) sGL[tid] = gl;
+        o.tw.template store_raw<LW>(sW);
+        o.tq.template store_raw<LW>(sQg);
+        o.tk.template store_raw<LT>(sKt);
+        o.tp.template store_raw<LT>(sP);
+        o.tu.store(sU);
+        if (tid < KD) sGL[tid] = o.gl;
         __syncthreads();
-        const bool more = ci + 1 < nch;
-        if (more) issue_w(ci + 1);
+        const bool more = ci + 2 < nch;
+        if (more) issue_w(ci + 2, o);
         // token tile w: R = U - W S^T and QS = Qg S^T
         const f32x4 WS = f32t::mmb(sW + 16 * w * LW, LW, sSb, LW, 0, KD, zero4());
-        if (more) issue_q(ci + 1);
+        if (more) issue_q(ci + 2, o);
         const f32x4 QS = f32t::mmb(sQg + 16 * w * LW, LW, sSb, LW, 0, KD, zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) sRt[ln * LT + tr0 + r] = f2bf(sU[(tr0 + r) * LV + ln] - WS[r]);
         __syncthreads();
-        if (more) issue_k(ci + 1);
+        if (more) issue_k(ci + 2, o);
         // O = QS + P R on token tile w (P is zero past column 16 w + 15)
-        const f32x4 o = f32t::mmb(sP + 16 * w * LT, LT, sRt, LT, 0, 16 * (w + 1), QS);
+        const f32x4 ov = f32t::mmb(sP + 16 * w * LT, LT, sRt, LT, 0, 16 * (w + 1), QS);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            if (tr0 + r < L) out[((row0 + tr0 + r) * H + h) * (long)VD + v0 + ln] = f2bf(o[r]);
+            if (tr0 + r < L) out[((row0 + tr0 + r) * H + h) * (long)VD + v0 + ln] = f2bf(ov[r]);
         // S <- S diag(Gamma_L) + R^T Kh on the wavefront's key tiles: A(v, t) = R^T[v][t], B(t, c) = Kh^T[c][t]
 #pragma unroll
         for (int i = 0; i < JPW; ++i) {
@@ -598,6 +597,18 @@ __global__ __launch_bounds__(NT) void kda_chain16_kernel(const float* __restrict
             S[i] = f32t::mmb(sRt, LT, sKt + 16 * jc * LT, LT, 0, BC, S[i] * sGL[16 * jc + ln]);
         }
         __syncthreads();
+    };
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+        if (c < nch) {
+            Ops16& o = c == 0 ? opA : opB;
+            issue_w(c, o);
+            issue_q(c, o);
+            issue_k(c, o);
+        }
+    for (int ci = 0; ci < nch; ci += 2) {
+        step(ci, opA);
+        if (ci + 1 < nch) step(ci + 1, opB);
     }
     if (ht) {
 #pragma unroll
