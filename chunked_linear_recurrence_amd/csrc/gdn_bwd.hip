@@ -227,6 +227,148 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
     }
 }
 
+// The prep for bf16 inputs, in 79 KB of LDS so that two workgroups share a CU: K and Q rows in bf16; the Q rows'
+// block holds the U tiles of the off-diagonal solve once Q K^T is formed, then W; P in bf16 (it enters only P W);
+// scale Gamma Q of the lane's own Q~ entries kept in registers from the start. The same steps as
+// gdn_bwd_prep_kernel.
+template <int KD>
+__global__ __launch_bounds__(NT) void gdn_bwd_prep16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                            const float* __restrict__ g, const float* __restrict__ beta,
+                                                            const int2* __restrict__ table, const int32_t* __restrict__ cu,
+                                                            int T, int H, int nc, float scale, float* __restrict__ rec) {
+    typedef BwdRec<KD> RL;
+    typedef Elem<bf16_t> El;
+    constexpr int KP = KD + 8, CP = BC + 8, LL = BC + 1, LU = 17, NJ = KD / 16;
+    constexpr int OFF_K = 0, OFF_QW = OFF_K + BC * KP * 2, OFF_A = OFF_QW + BC * KP * 2, OFF_T = OFF_A + BC * LL * 4,
+                  OFF_P = OFF_T + BC * LL * 4, OFF_S = OFF_P + BC * CP * 2, BYTES = OFF_S + 3 * BC * 4;
+    static_assert(4 * 16 * LU * 4 <= BC * KP * 2, "the U tiles fit the Q rows' block");
+    static_assert(BYTES <= 80 * 1024, "two workgroups per CU");
+    __shared__ __align__(16) uint8_t smem[BYTES];
+    bf16_t* const sK = reinterpret_cast<bf16_t*>(smem + OFF_K);
+    bf16_t* const sQ = reinterpret_cast<bf16_t*>(smem + OFF_QW);  // Q rows, then (float) U tiles, then W rows
+    bf16_t* const sW = sQ;
+    float* const sU = reinterpret_cast<float*>(smem + OFF_QW);
+    float* const sA = reinterpret_cast<float*>(smem + OFF_A);
+    float* const sT = reinterpret_cast<float*>(smem + OFF_T);
+    bf16_t* const sP = reinterpret_cast<bf16_t*>(smem + OFF_P);
+    float* const sG = reinterpret_cast<float*>(smem + OFF_S);
+    float* const sB = sG + BC;
+    float* const sGam = sB + BC;
+    const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    int b, t0, L;
+    if (!chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
+    const long row0 = (long)b * T + t0;
+    {
+        Tile<bf16_t, BC, KD> tk, tq;
+        tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
+        tk.template store_raw<KP>(sK);
+        tq.template store_raw<KP>(sQ);
+    }
+    if (tid < BC) {
+        const float gv = tid < L ? g[(row0 + tid) * H + h] : 0.f;
+        sB[tid] = tid < L ? beta[(row0 + tid) * H + h] : 0.f;
+        const float G = wave_inclusive_scan(gv);
+        sG[tid] = G;
+        sGam[tid] = expf(G);
+    }
+    __syncthreads();
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    int tr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tr[r] = 16 * w + 4 * lg + r;
+    // scale Gamma Q at the lane's Q~ entries (rows tr[r], columns 16 jc + ln)
+    float qg[NJ][4];
+#pragma unroll
+    for (int jc = 0; jc < NJ; ++jc)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qg[jc][r] = scale * sGam[tr[r]] * bf2f(sQ[tr[r] * KP + 16 * jc + ln]);
+    // A = diag(beta) (D_strict o K K^T) and P = scale (D o Q K^T) on the wavefront's row tile
+    for (int j = 0; j < 4; ++j) {
+        f32x4 kk = zero4(), qk = zero4();
+        if (j <= w) {
+            kk = mmb(sK + 16 * w * KP, KP, sK + 16 * j * KP, KP, 0, KD, kk);
+            qk = mmb(sQ + 16 * w * KP, KP, sK + 16 * j * KP, KP, 0, KD, qk);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = tr[r], s2 = 16 * j + ln;
+            const float d = s2 <= t ? expf(sG[t] - sG[s2]) : 0.f;
+            sA[t * LL + s2] = s2 < t ? sB[t] * d * kk[r] : 0.f;
+            sP[t * CP + s2] = f2bf(scale * d * qk[r]);
+            sT[t * LL + s2] = 0.f;
+        }
+    }
+    __syncthreads();
+    // diagonal blocks: wavefront w inverts block w, lane j < 16 solving column j in registers
+    if (lane < 16) {
+        const int o = 16 * w, j = lane;
+        float xs[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float x = i == j ? 1.f : 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < i; ++s2) x -= sA[(o + i) * LL + o + s2] * xs[s2];
+            xs[i] = x;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sT[(o + i) * LL + o + j] = xs[i];
+    }
+    // (K scaled by beta Gamma per token, for W: K is not read again as itself)
+    for (int i = tid; i < BC * KD; i += NT) {
+        const int t = i / KD, c = i % KD;
+        sK[t * KP + c] = f2bf(bf2f(sK[t * KP + c]) * (sB[t] * sGam[t]));
+    }
+    __syncthreads();
+    // off-diagonal blocks, one block diagonal dd at a time: block (i, j = i - dd) by wavefront i
+    for (int dd = 1; dd < 4; ++dd) {
+        const int i = w, j = w - dd;
+        if (j >= 0) {
+            const f32x4 Uv = mm4(sA + 16 * i * LL + 16 * j, LL, 1, sT + 16 * j * LL + 16 * j, LL, 1, 0, 16 * (i - j), zero4());
+            float* Ub = sU + w * 16 * LU;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ub[(4 * lg + r) * LU + ln] = Uv[r];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the U tile is in LDS
+            const f32x4 Tv = mm4(sT + 16 * i * LL + 16 * i, LL, 1, Ub, LU, 1, 0, 16, zero4());
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sT[(16 * i + 4 * lg + r) * LL + 16 * j + ln] = -Tv[r];
+        }
+        __syncthreads();
+    }
+    float* R = rec + ((size_t)slot * H + h) * RL::FLOATS;
+    bf16_t* const RW = rec_w<bf16_t, KD>(R);
+    bf16_t* const RQ = rec_qt<bf16_t, KD>(R);
+    // W = T (beta Gamma K) on the wavefront's row tile (T is zero past column 16 w + 15)
+#pragma unroll
+    for (int jc = 0; jc < NJ; ++jc) {
+        const f32x4 Wv = mmg(sT + 16 * w * LL, LL, 1, sK + 16 * jc, KP, 1, 0, 16 * (w + 1), zero4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sW[tr[r] * KP + 16 * jc + ln] = f2bf(Wv[r]);
+            RW[tr[r] * KD + 16 * jc + ln] = f2bf(Wv[r]);
+        }
+    }
+    __syncthreads();
+    // Qt = scale Gamma Q - P W
+#pragma unroll
+    for (int jc = 0; jc < NJ; ++jc) {
+        const f32x4 PW = mmg(sP + 16 * w * CP, CP, 1, sW + 16 * jc, KP, 1, 0, 16 * (w + 1), zero4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) RQ[tr[r] * KD + 16 * jc + ln] = f2bf(qg[jc][r] - PW[r]);
+    }
+    for (int i = tid; i < BC * BC; i += NT) {
+        rec_t<bf16_t, KD>(R)[i] = f2bf(sT[(i / BC) * LL + i % BC]);
+        rec_t<bf16_t, KD>(R)[BC * BC + i] = f2bf(sT[(i % BC) * LL + i / BC]);  // T^T (read by columns)
+    }
+    if (tid < BC) {
+        const float G = sG[tid], GL = sG[BC - 1];
+        R[RL::C_OFF + tid] = G;
+        R[RL::C_OFF + 64 + tid] = expf(G);
+        R[RL::C_OFF + 128 + tid] = expf(GL - G);
+        R[RL::C_OFF + 192 + tid] = sB[tid];
+    }
+}
+
 // Sequence n of a (sequence, head) chain: batch row, token range, first chunk slot.
 __device__ __forceinline__ void seq_of(int n, const int32_t* cu, const int* chunk_off, int T, int nc, int& b,
                                        int& bos, int& eos, int& slot0) {
@@ -1255,7 +1397,10 @@ hipError_t run_bwd(const ST* q, const ST* k, const ST* v, const float* g, const 
     const int2* table = packed ? ws.table : nullptr;
     if (slots > 0) {
         timing_begin("gdn_bwd_prep", s);
-        gdn_bwd_prep_kernel<ST, KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, g, beta, table, cu, T, H, nc, scale, ws.rec);
+        if constexpr (sizeof(ST) == 2)
+            gdn_bwd_prep16_kernel<KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, g, beta, table, cu, T, H, nc, scale, ws.rec);
+        else
+            gdn_bwd_prep_kernel<ST, KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, g, beta, table, cu, T, H, nc, scale, ws.rec);
         timing_end(s);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
