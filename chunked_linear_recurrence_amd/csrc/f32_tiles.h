@@ -24,19 +24,19 @@ __device__ __forceinline__ ST unit_of(const u128& u, int e) {
 // A [ROWS][COLS] tile of ST (row stride ld elements; rows at or past rows_valid read as zero) moved to LDS as
 // float [ROWS][COLS + 1] through registers in 16-byte pieces: load() puts every piece of the thread in flight
 // at once, store() writes them to LDS, so a tile costs one load latency, and a chain can load the next
-// chunk's tiles while it computes on the current ones.
-template <typename ST, int ROWS, int COLS>
+// chunk's tiles while it computes on the current ones. NTH threads share the pieces.
+template <typename ST, int ROWS, int COLS, int NTH = NT>
 struct Tile {
     static constexpr int E = 16 / (int)sizeof(ST);
     static constexpr int PPR = COLS / E;                     // pieces per row
     static constexpr int PIECES = ROWS * PPR;
-    static constexpr int PER = (PIECES + NT - 1) / NT;
+    static constexpr int PER = (PIECES + NTH - 1) / NTH;
     static_assert(COLS % E == 0, "tile rows are whole 16-byte pieces");
     u128 r[PER];
     __device__ __forceinline__ void load(const ST* __restrict__ base, long ld, int rows_valid) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
+            const int idx = threadIdx.x + NTH * p, row = idx / PPR, col = (idx % PPR) * E;
             r[p] = u128{0u, 0u, 0u, 0u};
             if (idx < PIECES && row < rows_valid) r[p] = *reinterpret_cast<const u128*>(base + row * ld + col);
         }
@@ -45,7 +45,7 @@ struct Tile {
     __device__ __forceinline__ void store(float* dst, int lds = COLS + 1) const {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
+            const int idx = threadIdx.x + NTH * p, row = idx / PPR, col = (idx % PPR) * E;
             if (idx < PIECES)
 #pragma unroll
                 for (int e = 0; e < E; ++e) dst[row * lds + col + e] = Elem<ST>::to_f(unit_of<ST>(r[p], e));
@@ -57,7 +57,7 @@ struct Tile {
         static_assert(LDS * sizeof(ST) % 16 == 0, "16-byte row starts");
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
+            const int idx = threadIdx.x + NTH * p, row = idx / PPR, col = (idx % PPR) * E;
             if (idx < PIECES) *reinterpret_cast<u128*>(dst + row * LDS + col) = r[p];
         }
     }
@@ -67,7 +67,7 @@ struct Tile {
         static_assert(LDS % 4 == 0, "16-byte row starts");
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int idx = threadIdx.x + NT * p, row = idx / PPR, col = (idx % PPR) * E;
+            const int idx = threadIdx.x + NTH * p, row = idx / PPR, col = (idx % PPR) * E;
             if (idx < PIECES)
 #pragma unroll
                 for (int e = 0; e < E; e += 4) {

@@ -857,7 +857,7 @@ __device__ __forceinline__ void put_cols(bf16_t* M, int P, int r0, int c0, f32x4
 }
 
 template <int KD>
-__global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
+__global__ __launch_bounds__(2 * NT) void gdn_bwd_grad16_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ rec, const float* __restrict__ states,
     const float* __restrict__ dstates, const int2* __restrict__ table, const int32_t* __restrict__ cu, int T, int H,
@@ -865,12 +865,13 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
     float* __restrict__ dg, float* __restrict__ dbeta) {
     typedef BwdRec<KD> RL;
     typedef Elem<bf16_t> El;
+    constexpr int NG = 2 * NT;   // eight wavefronts: two per token tile
     constexpr int KP = KD + 8;   // bf16 pitch of K, Q and the state rows
     constexpr int CP = BC + 8;   // bf16 pitch of 64-wide rows (T, T^T, P, and the slices' transposed blocks)
     constexpr int SW = 32;       // values per slice
     constexpr int VP = SW + 8;   // bf16 pitch of a slice's token rows
-    constexpr int LL = BC + 1;   // float pitch of P, K K^T, dT, D o dP
-    constexpr int NJ = KD / 16;
+    constexpr int LL = BC + 1;   // float pitch of P, K K^T, D o dP terms
+    constexpr int NJ = KD / 16, HJ = NJ / 2;
     __shared__ __align__(16) bf16_t sK[BC * KP], sQ[BC * KP], sT[BC * CP], sTt[BC * CP], sPb[BC * CP];
     __shared__ float sP[BC * LL], sKK[BC * LL], sC[256];
     // per-slice region (bf16); after the slices it holds dT (then U, then F), F^T and scale D o dP both ways
@@ -886,7 +887,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
     bf16_t* const sOt = sdR + BC * VP;                  // [SW][CP] dO^T
     bf16_t* const sRt = sOt + SW * CP;                  // [SW][CP] R^T
     bf16_t* const sXt = sRt + SW * CP;                  // [SW][CP] dX^T
-    __shared__ float sDG[BC], sEE[BC], sRed[NT / 64], sCol[NT];
+    // per-token partial sums of the two wavefronts of a token tile; the workgroup's column sums and <dS', S>
+    __shared__ float sDG[2][BC], sEE[2][BC], sDB[2][BC], sRed[NG / 64], sCol[NG];
 
     const int slot = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     int b, t0, L;
@@ -894,20 +896,23 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
     const long row0 = (long)b * T + t0;
     const float* Rc = rec + ((size_t)slot * H + h) * RL::FLOATS;
     {
-        Tile<bf16_t, BC, KD> tk, tq;
-        Tile<bf16_t, BC, BC> tt, ttt;
+        Tile<bf16_t, BC, KD, NG> tk, tq;
+        Tile<bf16_t, BC, BC, NG> tt, ttt;
         tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tt.load(rec_t<bf16_t, KD>(Rc), BC, BC);
         ttt.load(rec_t<bf16_t, KD>(Rc) + BC * BC, BC, BC);
-        sC[tid] = Rc[RL::C_OFF + tid];
+        if (tid < 256) sC[tid] = Rc[RL::C_OFF + tid];
         tk.template store_raw<KP>(sK);
         tq.template store_raw<KP>(sQ);
         tt.template store_raw<CP>(sT);
         ttt.template store_raw<CP>(sTt);
     }
     __syncthreads();
-    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    // wavefront wi: token tile w and half hv (the slice's value tile hv, the key tiles HJ hv .. HJ hv + HJ - 1,
+    // the token column tiles 2 hv, 2 hv + 1); a light and a heavy token tile share each SIMD
+    const int wi = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int w = wi < 4 ? (wi & 1) : 3 - (wi & 1), hv = (wi >> 1) & 1;
     // the lane's C-tile rows: tokens tr[r] = 16 w + 4 lg + r
     int tr[4];
     float Gr[4], gam[4], ee[4], bb[4];
@@ -920,8 +925,10 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
         bb[r] = sC[192 + tr[r]];
     }
     const float gl = sC[64 + BC - 1];
-    // P = scale (D o Q K^T) (s <= t) and the raw K K^T (s < t) on the wavefront's row tile
-    for (int j = 0; j < 4; ++j) {
+    // P = scale (D o Q K^T) (s <= t) and the raw K K^T (s < t) on the wavefront's two tiles
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * hv + jj;
         f32x4 qk = zero4(), kk = zero4();
         if (j <= w) {
             qk = mmb(sQ + 16 * w * KP, KP, sK + 16 * j * KP, KP, 0, KD, qk);
@@ -936,15 +943,15 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
             sKK[t * LL + s2] = s2 < t ? kk[r] : 0.f;
         }
     }
-    f32x4 aP[4], aT[4], aQ[NJ], aK[NJ], aK2[NJ];
+    f32x4 aP[2], aT[2], aQ[HJ], aK[HJ], aK2[HJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) aP[j] = aT[j] = zero4();
+    for (int j = 0; j < 2; ++j) aP[j] = aT[j] = zero4();
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) aQ[j] = aK[j] = aK2[j] = zero4();
+    for (int j = 0; j < HJ; ++j) aQ[j] = aK[j] = aK2[j] = zero4();
     float pGam[4] = {0.f, 0.f, 0.f, 0.f}, pE[4] = {0.f, 0.f, 0.f, 0.f}, pB[4] = {0.f, 0.f, 0.f, 0.f}, pGL = 0.f;
     const int nvs = V / SW;
-    Tile<float, SW, KD> ts, td;
-    Tile<bf16_t, BC, SW> to, tv;
+    Tile<float, SW, KD, NG> ts, td;
+    Tile<bf16_t, BC, SW, NG> to, tv;
     auto issue = [&](int vs) __attribute__((always_inline)) {
         const int v0 = SW * vs;
         ts.load(states + (((size_t)slot * H + h) * V + v0) * KD, KD, SW);
@@ -954,13 +961,14 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
     };
     issue(0);
     __syncthreads();
+    const int vt = hv;  // the wavefront's value tile of the slice
     for (int vs = 0; vs < nvs; ++vs) {
         const int v0 = SW * vs;
         // the slice's operands to LDS: state rows in bf16 (<S, dS'> in float32 from the same registers), dO and V
         // rows, dO^T
 #pragma unroll
         for (int p = 0; p < decltype(ts)::PER; ++p) {
-            const int idx = tid + NT * p, row = idx / decltype(ts)::PPR, col = (idx % decltype(ts)::PPR) * 4;
+            const int idx = tid + NG * p, row = idx / decltype(ts)::PPR, col = (idx % decltype(ts)::PPR) * 4;
             if (idx < decltype(ts)::PIECES) {
                 const f32x4 sv = __builtin_bit_cast(f32x4, ts.r[p]), dv4 = __builtin_bit_cast(f32x4, td.r[p]);
                 pGL += (sv[0] * dv4[0] + sv[1] * dv4[1]) + (sv[2] * dv4[2] + sv[3] * dv4[3]);
@@ -972,93 +980,90 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
         tv.template store_raw<VP>(sV);
 #pragma unroll
         for (int p = 0; p < decltype(to)::PER; ++p) {
-            const int idx = tid + NT * p, row = idx / decltype(to)::PPR, col = (idx % decltype(to)::PPR) * 8;
+            const int idx = tid + NG * p, row = idx / decltype(to)::PPR, col = (idx % decltype(to)::PPR) * 8;
             if (idx < decltype(to)::PIECES)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sOt[(col + e) * CP + row] = unit_of<bf16_t>(to.r[p], e);
         }
         if (vs + 1 < nvs) issue(vs + 1);
         __syncthreads();
-        // X = K S^T, QS = Q S^T, KdS = K dS'^T on (token tile w, the slice's two value tiles): row form
-        f32x4 X[2], QS[2], KdS[2], Y[2];
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
-            X[vt] = mmb(sK + 16 * w * KP, KP, sS + 16 * vt * KP, KP, 0, KD, zero4());
-            QS[vt] = mmb(sQ + 16 * w * KP, KP, sS + 16 * vt * KP, KP, 0, KD, zero4());
-            KdS[vt] = mmb(sK + 16 * w * KP, KP, sD + 16 * vt * KP, KP, 0, KD, zero4());
-        }
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
+        // X = K S^T, QS = Q S^T, KdS = K dS'^T on (token tile w, value tile vt): row form
+        const f32x4 X = mmb(sK + 16 * w * KP, KP, sS + 16 * vt * KP, KP, 0, KD, zero4());
+        const f32x4 QS = mmb(sQ + 16 * w * KP, KP, sS + 16 * vt * KP, KP, 0, KD, zero4());
+        const f32x4 KdS = mmb(sK + 16 * w * KP, KP, sD + 16 * vt * KP, KP, 0, KD, zero4());
+        f32x4 Y;
+        {
             const f32x4 vv = El::unpack(col4(sV, VP, 16 * w, 16 * vt)), oo = El::unpack(col4(sO, VP, 16 * w, 16 * vt));
             f32x4 z;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                Y[vt][r] = vv[r] - gam[r] * X[vt][r];
-                z[r] = bb[r] * Y[vt][r];
-                pGam[r] += scale * oo[r] * QS[vt][r];
+                Y[r] = vv[r] - gam[r] * X[r];
+                z[r] = bb[r] * Y[r];
+                pGam[r] += scale * oo[r] * QS[r];
             }
             put_rows(sZ, VP, 16 * w, 16 * vt, z);
         }
         __syncthreads();
         // R = T Z (column form: T^T rows give T by columns); dR = P^T dO + e KdS (column form, P rows)
-        f32x4 R[2], dR[2];
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
-            R[vt] = zero4();
-            f32x4 dRp = zero4();
+        {
+            f32x4 R = zero4(), dRp = zero4(), dR;
 #pragma unroll
             for (int k0 = 0; k0 < BC; k0 += 32) {
-                if (k0 < 16 * (w + 1)) R[vt] = mma32(col8(sTt, CP, k0, 16 * w), col8(sZ, VP, k0, 16 * vt), R[vt]);
+                if (k0 < 16 * (w + 1)) R = mma32(col8(sTt, CP, k0, 16 * w), col8(sZ, VP, k0, 16 * vt), R);
                 if (k0 + 32 > 16 * w) dRp = mma32(col8(sPb, CP, k0, 16 * w), col8(sO, VP, k0, 16 * vt), dRp);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                dR[vt][r] = dRp[r] + ee[r] * KdS[vt][r];
-                pE[r] += R[vt][r] * KdS[vt][r];
+                dR[r] = dRp[r] + ee[r] * KdS[r];
+                pE[r] += R[r] * KdS[r];
             }
-            put_rows(sR, VP, 16 * w, 16 * vt, R[vt]);
-            put_cols(sRt, CP, 16 * w, 16 * vt, R[vt]);
-            put_rows(sdR, VP, 16 * w, 16 * vt, dR[vt]);
+            put_rows(sR, VP, 16 * w, 16 * vt, R);
+            put_cols(sRt, CP, 16 * w, 16 * vt, R);
+            put_rows(sdR, VP, 16 * w, 16 * vt, dR);
         }
         __syncthreads();
         // dZ = T^T dR (column form, T rows); dbeta, dY = dV, dX = -Gamma dY
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
-            f32x4 dZ = zero4();
+        {
+            f32x4 dZ = zero4(), dX;
 #pragma unroll
             for (int k0 = 0; k0 < BC; k0 += 32)
                 if (k0 + 32 > 16 * w) dZ = mma32(col8(sT, CP, k0, 16 * w), col8(sdR, VP, k0, 16 * vt), dZ);
-            f32x4 dX;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pB[r] += Y[vt][r] * dZ[r];
+                pB[r] += Y[r] * dZ[r];
                 const float dY = bb[r] * dZ[r];
                 if (tr[r] < L) dv[((row0 + tr[r]) * H + h) * (long)V + v0 + 16 * vt + ln] = f2bf(dY);
                 dX[r] = -gam[r] * dY;
-                pGam[r] -= dY * X[vt][r];
+                pGam[r] -= dY * X[r];
             }
             put_cols(sXt, CP, 16 * w, 16 * vt, dX);
         }
         // dP += dO R^T, dT += dR Z^T (row form over the slice's 32 values)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            aP[j] = mmb(sO + 16 * w * VP, VP, sR + 16 * j * VP, VP, 0, SW, aP[j]);
-            aT[j] = mmb(sdR + 16 * w * VP, VP, sZ + 16 * j * VP, VP, 0, SW, aT[j]);
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * hv + jj;
+            aP[jj] = mmb(sO + 16 * w * VP, VP, sR + 16 * j * VP, VP, 0, SW, aP[jj]);
+            aT[jj] = mmb(sdR + 16 * w * VP, VP, sZ + 16 * j * VP, VP, 0, SW, aT[jj]);
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's dX^T columns are in LDS
-        // dq += dO S, dk += dX S, dk2 += R dS' (column form: dO^T, dX^T, R^T by rows, S and dS' rows)
+        // dq += dO S, dk2 += R dS' (column form: dO^T, R^T by rows, S and dS' rows)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const bf16x8 s8 = col8(sS, KP, 0, 16 * j), d8 = col8(sD, KP, 0, 16 * j);
-            aQ[j] = mma32(col8(sOt, CP, 0, 16 * w), s8, aQ[j]);
-            aK[j] = mma32(col8(sXt, CP, 0, 16 * w), s8, aK[j]);
-            aK2[j] = mma32(col8(sRt, CP, 0, 16 * w), d8, aK2[j]);
+        for (int jj = 0; jj < HJ; ++jj) {
+            const int j = HJ * hv + jj;
+            aQ[jj] = mma32(col8(sOt, CP, 0, 16 * w), col8(sS, KP, 0, 16 * j), aQ[jj]);
+            aK2[jj] = mma32(col8(sRt, CP, 0, 16 * w), col8(sD, KP, 0, 16 * j), aK2[jj]);
+        }
+        __syncthreads();  // both value tiles of dX^T are in LDS
+        // dk += dX S
+#pragma unroll
+        for (int jj = 0; jj < HJ; ++jj) {
+            const int j = HJ * hv + jj;
+            aK[jj] = mma32(col8(sXt, CP, 0, 16 * w), col8(sS, KP, 0, 16 * j), aK[jj]);
         }
         __syncthreads();
     }
     // dq = scale Gamma (dO S), dk = dX S + e (R dS')
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < HJ; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             aQ[j][r] *= scale * gam[r];
@@ -1072,22 +1077,26 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
     bf16_t* const bDt = bD + BC * CP;
     static_assert(4 * BC * CP * 2 <= sizeof(sX), "post-slice blocks fit the slice region");
 #pragma unroll
-    for (int j = 0; j < 4; ++j) put_rows(bF, CP, 16 * w, 16 * j, aT[j]);
+    for (int jj = 0; jj < 2; ++jj) put_rows(bF, CP, 16 * w, 16 * (2 * hv + jj), aT[jj]);
     __syncthreads();
     // U = dT T^T (row form; T[s][j] is zero past j = s)
-    f32x4 U[4];
+    f32x4 U[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) U[j] = mmb(bF + 16 * w * CP, CP, sT + 16 * j * CP, CP, 0, 16 * (j + 1), zero4());
+    for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * hv + jj;
+        U[jj] = mmb(bF + 16 * w * CP, CP, sT + 16 * j * CP, CP, 0, 16 * (j + 1), zero4());
+    }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) put_rows(bF, CP, 16 * w, 16 * j, U[j]);
+    for (int jj = 0; jj < 2; ++jj) put_rows(bF, CP, 16 * w, 16 * (2 * hv + jj), U[jj]);
     __syncthreads();
     // dA = -T^T U on s < t (column form over the rows of T and U; T[k][t] is zero for k < t); then the gate
     // terms, F and scale D o dP
     float rowc[4] = {0.f, 0.f, 0.f, 0.f};
-    f32x4 Fv[4], DPv[4];
+    f32x4 Fv[2], DPv[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * hv + jj;
         f32x4 dA = zero4();
         if (j <= w) {
 #pragma unroll
@@ -1101,39 +1110,42 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
             const float a = s2 < t ? -dA[r] : 0.f;
             const float kk = sKK[t * LL + s2];
             pB[r] += a * d * kk;
-            Fv[j][r] = a * bb[r] * d;
-            DPv[j][r] = s2 <= t ? scale * d * aP[j][r] : 0.f;
-            const float c = (s2 <= t ? aP[j][r] * sP[t * LL + s2] : 0.f) + Fv[j][r] * kk;
+            Fv[jj][r] = a * bb[r] * d;
+            DPv[jj][r] = s2 <= t ? scale * d * aP[jj][r] : 0.f;
+            const float c = (s2 <= t ? aP[jj][r] * sP[t * LL + s2] : 0.f) + Fv[jj][r] * kk;
             rowc[r] += c;
             sKK[t * LL + s2] = c;  // own entry: K K^T is not read again
         }
     }
     __syncthreads();  // U is no longer read
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        put_rows(bF, CP, 16 * w, 16 * j, Fv[j]);
-        put_cols(bFt, CP, 16 * w, 16 * j, Fv[j]);
-        put_rows(bD, CP, 16 * w, 16 * j, DPv[j]);
-        put_cols(bDt, CP, 16 * w, 16 * j, DPv[j]);
+    for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * hv + jj;
+        put_rows(bF, CP, 16 * w, 16 * j, Fv[jj]);
+        put_cols(bFt, CP, 16 * w, 16 * j, Fv[jj]);
+        put_rows(bD, CP, 16 * w, 16 * j, DPv[jj]);
+        put_cols(bDt, CP, 16 * w, 16 * j, DPv[jj]);
     }
     __syncthreads();
     // dq += (scale D o dP) K;  dk += (scale D o dP)^T Q + F K + F^T K (column form over the tokens)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    for (int jj = 0; jj < HJ; ++jj) {
+        const int j = HJ * hv + jj;
 #pragma unroll
         for (int k0 = 0; k0 < BC; k0 += 32) {
             const bf16x8 kcol = col8(sK, KP, k0, 16 * j);
             if (k0 < 16 * (w + 1)) {
-                aQ[j] = mma32(col8(bDt, CP, k0, 16 * w), kcol, aQ[j]);
-                aK[j] = mma32(col8(bFt, CP, k0, 16 * w), kcol, aK[j]);
+                aQ[jj] = mma32(col8(bDt, CP, k0, 16 * w), kcol, aQ[jj]);
+                aK[jj] = mma32(col8(bFt, CP, k0, 16 * w), kcol, aK[jj]);
             }
             if (k0 + 32 > 16 * w) {
-                aK[j] = mma32(col8(bD, CP, k0, 16 * w), col8(sQ, KP, k0, 16 * j), aK[j]);
-                aK[j] = mma32(col8(bF, CP, k0, 16 * w), kcol, aK[j]);
+                aK[jj] = mma32(col8(bD, CP, k0, 16 * w), col8(sQ, KP, k0, 16 * j), aK[jj]);
+                aK[jj] = mma32(col8(bF, CP, k0, 16 * w), kcol, aK[jj]);
             }
         }
     }
-    // row sums over the 16 lanes of each row group; <dS', S> over the workgroup
+    // row sums over the 16 lanes of each row group (each wavefront's share of the token's terms); <dS', S> over
+    // the workgroup
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1)
 #pragma unroll
@@ -1144,42 +1156,45 @@ __global__ __launch_bounds__(NT) void gdn_bwd_grad16_kernel(
             rowc[r] += __shfl_xor(rowc[r], o, 64);
         }
     for (int o = 1; o < 64; o <<= 1) pGL += __shfl_xor(pGL, o, 64);
-    if (lane == 0) sRed[w] = pGL;
+    if (lane == 0) sRed[wi] = pGL;
     if (ln == 0)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            sDG[tr[r]] = pGam[r] * gam[r] - pE[r] * ee[r] + rowc[r];
-            sEE[tr[r]] = pE[r] * ee[r];
-            if (tr[r] < L) dbeta[(row0 + tr[r]) * H + h] = pB[r];
+            sDG[hv][tr[r]] = pGam[r] * gam[r] - pE[r] * ee[r] + rowc[r];
+            sEE[hv][tr[r]] = pE[r] * ee[r];
+            sDB[hv][tr[r]] = pB[r];
         }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int jj = 0; jj < HJ; ++jj)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (tr[r] < L) {
-                const long o = ((row0 + tr[r]) * H + h) * (long)KD + 16 * j + ln;
-                dq[o] = f2bf(aQ[j][r]);
-                dk[o] = f2bf(aK[j][r]);
+                const long o = ((row0 + tr[r]) * H + h) * (long)KD + 16 * (HJ * hv + jj) + ln;
+                dq[o] = f2bf(aQ[jj][r]);
+                dk[o] = f2bf(aK[jj][r]);
             }
     __syncthreads();
     {
-        // column sums of the gate terms: wavefront w over rows 16 w .. 16 w + 15, lane = column
+        // column sums of the gate terms: wavefront wi over rows 8 wi .. 8 wi + 7, lane = column
         float part = 0.f;
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) part += sKK[(16 * w + tt) * LL + lane];
+        for (int tt = 0; tt < 8; ++tt) part += sKK[(8 * wi + tt) * LL + lane];
         sCol[tid] = part;
     }
     __syncthreads();
     if (tid < BC) {
-        const float col = (sCol[tid] + sCol[64 + tid]) + (sCol[128 + tid] + sCol[192 + tid]);
-        float dG = sDG[tid] - col;
+        float col = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NG / 64; ++ww) col += sCol[64 * ww + tid];
+        float dG = (sDG[0][tid] + sDG[1][tid]) - col;
+        if (tid < L) dbeta[(row0 + tid) * H + h] = sDB[0][tid] + sDB[1][tid];
         // G_L (token 63: padded tokens repeat the last real G) also carries e's and Gamma_L's terms
-        float se = sEE[tid];
+        float se = sEE[0][tid] + sEE[1][tid];
         for (int o = 1; o < 64; o <<= 1) se += __shfl_xor(se, o, 64);
         if (tid == BC - 1) {
             float gsum = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < NT / 64; ++ww) gsum += sRed[ww];
+            for (int ww = 0; ww < NG / 64; ++ww) gsum += sRed[ww];
             dG += se + gsum * gl;
         }
         // dg = the reverse cumulative sum of dG over the chunk: lane l scans dG of token 63 - l
@@ -1428,7 +1443,7 @@ hipError_t run_bwd(const ST* q, const ST* k, const ST* v, const float* g, const 
     if (slots > 0) {
         timing_begin("gdn_bwd_grad", s);
         if constexpr (sizeof(ST) == 2)
-            gdn_bwd_grad16_kernel<KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, v, dout, ws.rec, ws.states,
+            gdn_bwd_grad16_kernel<KD><<<dim3((unsigned)slots, H), 2 * NT, 0, s>>>(q, k, v, dout, ws.rec, ws.states,
                                                                               ws.dstates, table, cu, T, H, V, nc, scale,
                                                                               dq, dk, dv, dg, dbeta);
         else
