@@ -27,6 +27,7 @@ namespace {
 
 constexpr int BC = kGdnChunk;
 constexpr int NT = f32t::NT;
+constexpr int NTP = 2 * NT;  // threads of the prep: eight wavefronts
 using f32t::Tile;
 using f32t::mm4;
 
@@ -68,7 +69,7 @@ struct KdaRec16 {
 //   W = T diag(beta) (Gamma o K) and U = T diag(beta) V as tiles; Qg, Kh and Gamma_L elementwise.
 // ---------------------------------------------------------------------------------------------------------
 template <typename ST, int KD, int VD>
-__global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, const ST* __restrict__ k,
+__global__ __launch_bounds__(NTP) void kda_prep_kernel(const ST* __restrict__ q, const ST* __restrict__ k,
                                                       const ST* __restrict__ v, const float* __restrict__ g,
                                                       const float* __restrict__ beta, const int2* __restrict__ table,
                                                       const int32_t* __restrict__ cu, int T, int H, int nc, float scale,
@@ -86,10 +87,10 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
     int b, t0, L;
     if (!chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
     const long row0 = (long)b * T + t0;
-    Tile<ST, BC, VD> tv;  // V rows: loaded now, stored once the Q rows are no longer read
+    Tile<ST, BC, VD, NTP> tv;  // V rows: loaded now, stored once the Q rows are no longer read
     {
-        Tile<ST, BC, KD> tk, tq;
-        Tile<float, BC, KD> tg;
+        Tile<ST, BC, KD, NTP> tk, tq;
+        Tile<float, BC, KD, NTP> tg;
         tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tg.load(g + (row0 * H + h) * (long)KD, (long)H * KD, L);  // padded tokens: g = 0
@@ -113,7 +114,8 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
         }
     }
     __syncthreads();
-    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    // wavefronts w and w + 4 share block row w: each forms two of its four blocks (j = 2 hv, 2 hv + 1)
+    const int wi = tid >> 6, w = wi & 3, hv = wi >> 2, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     // A (strictly lower, beta applied) and P (lower with the diagonal, scale applied), block row w, with the
     // reference token b = 16 w: exp(G_t - G_s) = exp(G_t - G_b) exp(G_b - G_s). For the blocks left of the
     // diagonal (s < b <= t) both factors are at most 1. For the diagonal block (b <= s, t) the second factor is
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
         // the diagonal one when its range is wide, are formed and dropped; the exponent is clamped at 80 so that
         // they stay finite). Lane (ln, lg) brings A(t = b + ln, c) and B(c, s = 16 j + ln), c = kk + lg; four
         // reduction steps per pass, their reads issued together.
-        f32x4 accA[4] = {zero4(), zero4(), zero4(), zero4()}, accP[4] = {zero4(), zero4(), zero4(), zero4()};
+        f32x4 accA[2] = {zero4(), zero4()}, accP[2] = {zero4(), zero4()};
         const float* Kt = sK + (b0 + ln) * LK;
         const float* Qt = sQ + (b0 + ln) * LK;
         const float* Gt = sG + (b0 + ln) * LK;
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
             typedef float f32x8 __attribute__((ext_vector_type(8)));
             for (int k0 = 0; k0 < KD; k0 += 32) {
                 const int c0 = k0 + 8 * lg;
-                f32x8 gb, ak, aq, gt, ks[4], gs[4];
+                f32x8 gb, ak, aq, gt, ks[2], gs[2];
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const f32x4 g4 = *(const f32x4*)(Gb + c0 + 4 * hf), k4 = *(const f32x4*)(Kt + c0 + 4 * hf),
@@ -152,13 +154,14 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
                         gt[4 * hf + e] = t4[e];
                     }
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int j = 2 * hv + jj;
                         const f32x4 kk4 = *(const f32x4*)(sK + (16 * j + ln) * LK + c0 + 4 * hf),
                                     gg4 = *(const f32x4*)(sG + (16 * j + ln) * LK + c0 + 4 * hf);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            ks[j][4 * hf + e] = kk4[e];
-                            gs[j][4 * hf + e] = gg4[e];
+                            ks[jj][4 * hf + e] = kk4[e];
+                            gs[jj][4 * hf + e] = gg4[e];
                         }
                     }
                 }
@@ -171,18 +174,18 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
                 }
                 const bf16x8 A1 = __builtin_convertvector(a1, bf16x8), A2 = __builtin_convertvector(a2, bf16x8);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int jj = 0; jj < 2; ++jj) {
                     f32x8 bs;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bs[e] = ks[j][e] * __expf(fminf(gb[e] - gs[j][e], 80.f));
+                    for (int e = 0; e < 8; ++e) bs[e] = ks[jj][e] * __expf(fminf(gb[e] - gs[jj][e], 80.f));
                     const bf16x8 Bs = __builtin_convertvector(bs, bf16x8);
-                    accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Bs, accA[j], 0, 0, 0);
-                    accP[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, Bs, accP[j], 0, 0, 0);
+                    accA[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Bs, accA[jj], 0, 0, 0);
+                    accP[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, Bs, accP[jj], 0, 0, 0);
                 }
             }
         } else
         for (int k0 = 0; k0 < KD; k0 += 16) {
-            float gb[4], ak[4], aq[4], gt[4], ks[4][4], gs[4][4];
+            float gb[4], ak[4], aq[4], gt[4], ks[2][4], gs[2][4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int c = k0 + 4 * u + lg;
@@ -191,9 +194,9 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
                 aq[u] = Qt[c];
                 gt[u] = Gt[c];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    ks[j][u] = sK[(16 * j + ln) * LK + c];
-                    gs[j][u] = sG[(16 * j + ln) * LK + c];
+                for (int jj = 0; jj < 2; ++jj) {
+                    ks[jj][u] = sK[(16 * (2 * hv + jj) + ln) * LK + c];
+                    gs[jj][u] = sG[(16 * (2 * hv + jj) + ln) * LK + c];
                 }
             }
 #pragma unroll
@@ -201,17 +204,17 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
                 const float ft = __expf(gt[u] - gb[u]);
                 const float a1 = ak[u] * ft, a2 = aq[u] * ft;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float bs = ks[j][u] * __expf(fminf(gb[u] - gs[j][u], 80.f));
-                    accA[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bs, accA[j], 0, 0, 0);
-                    accP[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, bs, accP[j], 0, 0, 0);
+                for (int jj = 0; jj < 2; ++jj) {
+                    const float bs = ks[jj][u] * __expf(fminf(gb[u] - gs[jj][u], 80.f));
+                    accA[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bs, accA[jj], 0, 0, 0);
+                    accP[jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, bs, accP[jj], 0, 0, 0);
                 }
             }
         }
         // the diagonal block with the pairwise decays: lane (ln = s, lg) forms rows t = b + 4 lg + r, four
         // channels at a time
         f32x4 da = zero4(), dp = zero4();
-        if (!fast) {
+        if (!fast && hv == (w >> 1)) {  // (the wavefront holding the diagonal block)
             const int sd = b0 + ln;
 #pragma unroll 2
             for (int c = 0; c < KD; c += 4) {
@@ -232,17 +235,17 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = b0 + 4 * lg + r, s2 = 16 * j + ln;
+                const int j = 2 * hv + jj, t = b0 + 4 * lg + r, s2 = 16 * j + ln;
                 float a = 0.f, pv = 0.f;
                 if (j < w) {
-                    a = accA[j][r];
-                    pv = accP[j][r];
+                    a = accA[jj][r];
+                    pv = accP[jj][r];
                 } else if (j == w) {
-                    a = s2 < t ? (fast ? accA[j][r] : da[r]) : 0.f;
-                    pv = s2 <= t ? (fast ? accP[j][r] : dp[r]) : 0.f;
+                    a = s2 < t ? (fast ? accA[jj][r] : da[r]) : 0.f;
+                    pv = s2 <= t ? (fast ? accP[jj][r] : dp[r]) : 0.f;
                 }
                 sA[t * LL + s2] = sB[t] * a;
                 sP[t * LL + s2] = scale * pv;
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
     uint8_t* const Rb = reinterpret_cast<uint8_t*>(R);  // the bf16 record's bytes
     static_assert(KdaRec16<KD>::bytes(VD) <= (3 * BC * KD + BC * VD + BC * BC + KD) * sizeof(float),
                   "the bf16 record fits in the float32 record's footprint");
-    if (w == 0) {
+    if (wi == 0) {
         // T: the four diagonal blocks at once, lane 16 bb + j solving column j of block bb: x_j = 1,
         // x_i = -sum_{j<=s<i} A_bb[i][s] x_s
         // (the column in registers; x_s = 0 for s < j, so the sums may start at 0)
@@ -272,9 +275,9 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
 #pragma unroll
         for (int i = 0; i < 16; ++i) sT[(o + i) * LL + o + j] = x[i];
     } else {
-        // wavefronts 1-3: Qg = scale Gamma o Q and Kh = exp(G_L - G) o K to the record, K scaled by beta Gamma
+        // wavefronts 1-7: Qg = scale Gamma o Q and Kh = exp(G_L - G) o K to the record, K scaled by beta Gamma
         // in place (for W), Gamma_L and P to the record
-        const int i0 = tid - 64, NS = NT - 64;
+        const int i0 = tid - 64, NS = NTP - 64;
         if constexpr (B16) {
             // (Kh^T and the scaled K follow once the solve no longer holds the wavefronts apart)
 #pragma unroll 4
@@ -301,10 +304,10 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
     }
     __syncthreads();
     tv.template store_rows<LK>(sV);  // (visible after the first barrier below)
-    // T: off-diagonal blocks, one block diagonal dd at a time, block (i, j = i - dd) by wavefront i
+    // T: off-diagonal blocks, one block diagonal dd at a time, block (i, j = i - dd) by wavefront i < 4
     for (int dd = 1; dd < 4; ++dd) {
         const int i = w, j = w - dd;
-        if (j >= 0) {
+        if (hv == 0 && j >= 0) {
             // Ub = sum_{kb=j}^{i-1} A_i,kb T_kb,j (16 x 16, k over the tokens of blocks j .. i-1)
             const f32x4 Uv = mm4(sA + 16 * i * LL + 16 * j, LL, 1, sT + 16 * j * LL + 16 * j, LL, 1, 0, 16 * (i - j), zero4());
             float* Ub = sU + w * 16 * LU;
@@ -318,11 +321,11 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
         __syncthreads();
     }
     // V rows scaled by beta
-    for (int i = tid; i < BC * VD; i += NT) sV[(i / VD) * LK + i % VD] *= sB[i / VD];
+    for (int i = tid; i < BC * VD; i += NTP) sV[(i / VD) * LK + i % VD] *= sB[i / VD];
     if constexpr (B16) {
         // Kh^T = (exp(G_L - G) o K)^T, consecutive threads along the tokens of one channel (contiguous stores)
 #pragma unroll 4
-        for (int i = tid; i < BC * KD; i += NT) {
+        for (int i = tid; i < BC * KD; i += NTP) {
             const int c = i / BC, tt = i % BC;
             reinterpret_cast<bf16_t*>(Rb + R16::KT_OFF)[i] =
                 f2bf(__expf(sG[(BC - 1) * LK + c] - sG[tt * LK + c]) * sK[tt * LK + c]);
@@ -330,16 +333,16 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
         __syncthreads();
         // K scaled by beta Gamma in place, for W
 #pragma unroll 4
-        for (int i = tid; i < BC * KD; i += NT) {
+        for (int i = tid; i < BC * KD; i += NTP) {
             const int tt = i / KD, c = i % KD;
             sK[tt * LK + c] *= sB[tt] * __expf(sG[tt * LK + c]);
         }
     }
     __syncthreads();
-    // W = T (beta Gamma o K), U = T (beta V): wavefront w forms column tiles w, w + 4, .. of every row tile (T is
-    // zero past column 16 ti + 15 of row tile ti), so the four wavefronts share the triangle evenly
+    // W = T (beta Gamma o K), U = T (beta V): wavefront wi forms column tiles wi, wi + 8, .. of every row tile (T
+    // is zero past column 16 ti + 15 of row tile ti), so the wavefronts share the triangle evenly
 #pragma unroll
-    for (int jc = w; jc < NJ; jc += 4)
+    for (int jc = wi; jc < NJ; jc += 8)
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
             const f32x4 Wv = f32t::mmx<ST>(sT + 16 * ti * LL, LL, 1, sK + 16 * jc, LK, 1, 0, 16 * (ti + 1), zero4());
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(NT) void kda_prep_kernel(const ST* __restrict__ q, 
             }
         }
 #pragma unroll
-    for (int jc = w; jc < NV; jc += 4)
+    for (int jc = wi; jc < NV; jc += 8)
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
             const f32x4 Uv = f32t::mmx<ST>(sT + 16 * ti * LL, LL, 1, sV + 16 * jc, LK, 1, 0, 16 * (ti + 1), zero4());
@@ -634,7 +637,7 @@ hipError_t run_kda(const ST* q, const ST* k, const ST* v, const float* g, const 
     }
     if (slots > 0) {
         timing_begin("kda_prep", s);
-        kda_prep_kernel<ST, KD, VD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, v, g, beta, packed ? ws.table : nullptr,
+        kda_prep_kernel<ST, KD, VD><<<dim3((unsigned)slots, H), NTP, 0, s>>>(q, k, v, g, beta, packed ? ws.table : nullptr,
                                                                            cu, T, H, nc, scale, ws.rec);
         timing_end(s);
         if ((err = hipGetLastError()) != hipSuccess) return err;
