@@ -1234,14 +1234,14 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states16_kernel(const bf16_t* __re
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             S[i][r] = h0 ? h0[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] : 0.f;
-    // the operands of a chunk in registers (two sets: chunk c's load is issued two steps before its step,
-    // and the loop takes two steps per pass so that each set has fixed registers)
+    // the operands of a chunk in registers (three sets: chunk c's load is issued three steps before its step,
+    // and the loop takes three steps per pass so that each set has fixed registers)
     struct Ops16 {
         Tile<bf16_t, BC, KD> tk;
         Tile<bf16_t, BC, BC> tt;
         Tile<bf16_t, BC, 16> tv;
         float cf;
-    } opA, opB;
+    } opA, opB, opC;
     auto issue = [&](int ci, Ops16& o) __attribute__((always_inline)) {
         const long row0 = (long)b * T + bos + (long)ci * BC;
         const int L = min(BC, eos - (bos + ci * BC));
@@ -1264,7 +1264,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states16_kernel(const bf16_t* __re
         o.tv.template store_raw<VP>(sV);
         sC[tid] = o.cf;
         __syncthreads();
-        if (ci + 2 < nch) issue(ci + 2, o);
+        if (ci + 3 < nch) issue(ci + 3, o);
         // Z = diag(beta) (V - diag(Gamma) K S^T) on token tile w (row form)
         const f32x4 X = mmb(sK + 16 * w * KP, KP, sS, KP, 0, KD, zero4());
         const f32x4 vv = El::unpack(col4(sV, VP, 16 * w, 0));
@@ -1298,9 +1298,11 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states16_kernel(const bf16_t* __re
     };
     if (nch > 0) issue(0, opA);
     if (nch > 1) issue(1, opB);
-    for (int ci = 0; ci < nch; ci += 2) {
+    if (nch > 2) issue(2, opC);
+    for (int ci = 0; ci < nch; ci += 3) {
         step(ci, opA);
         if (ci + 1 < nch) step(ci + 1, opB);
+        if (ci + 2 < nch) step(ci + 2, opC);
     }
 }
 
