@@ -1307,12 +1307,13 @@ __global__ __launch_bounds__(NT) void gdn_bwd_states16_kernel(const bf16_t* __re
 }
 
 template <int KD>
-__global__ __launch_bounds__(NT) void gdn_bwd_dstate16_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ dout,
-                                                              const float* __restrict__ dht, const int32_t* __restrict__ cu,
-                                                              const int* __restrict__ chunk_off, const float* __restrict__ rec,
-                                                              int T, int H, int V, int n_seq, int nc, int nvs,
-                                                              float* __restrict__ dstates, float* __restrict__ dh0) {
+__global__ __launch_bounds__(2 * NT) void gdn_bwd_dstate16_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ dout,
+                                                                  const float* __restrict__ dht, const int32_t* __restrict__ cu,
+                                                                  const int* __restrict__ chunk_off, const float* __restrict__ rec,
+                                                                  int T, int H, int V, int n_seq, int nc, int nvs,
+                                                                  float* __restrict__ dstates, float* __restrict__ dh0) {
     typedef BwdRec<KD> RL;
+    constexpr int NG = 2 * NT;  // eight wavefronts: (token tile w, half hv)
     constexpr int KP = KD + 8, VP = 16 + 8, JPW = KD / 64;
     __shared__ __align__(16) bf16_t sK[BC * KP], sW[BC * KP], sQt[BC * KP], sD[16 * KP], sO[BC * VP], sZt[BC * VP];
     __shared__ float sC[256];
@@ -1320,24 +1321,26 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate16_kernel(const bf16_t* __re
     xcd_split(blockIdx.x, nvs, chain, vs);
     if (chain >= n_seq * H) return;
     const int n = chain / H, h = chain % H, tid = threadIdx.x, v0 = 16 * vs;
-    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    // wavefront wi: token tile w for Z (half 0), key tile JPW w + hv of the state gradient (for K = 64 the
+    // wavefronts of half 1 hold none)
+    const int wi = tid >> 6, w = wi & 3, hv = wi >> 2, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const bool own = hv < JPW;
+    const int jc = JPW * w + hv;
     int b, bos, eos, slot0;
     seq_of(n, cu, chunk_off, T, nc, b, bos, eos, slot0);
     const int nch = (eos - bos + BC - 1) / BC;
-    f32x4 dS[JPW];
+    f32x4 dS = zero4();
+    if (own && dht)
 #pragma unroll
-    for (int i = 0; i < JPW; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dS[i][r] = dht ? dht[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] : 0.f;
-    // chunk ci's K rows, W, Qt, coefficients and dO slice in registers (two sets: a chunk's load is issued two
-    // steps before its step, chunks running backwards, and the loop takes two steps per pass so that each set
-    // has fixed registers)
+        for (int r = 0; r < 4; ++r) dS[r] = dht[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * jc + ln];
+    // chunk ci's K rows, W, Qt, coefficients and dO slice in registers (three sets: a chunk's load is issued
+    // three steps before its step, chunks running backwards, and the loop takes three steps per pass so that
+    // each set has fixed registers)
     struct Ops16 {
-        Tile<bf16_t, BC, KD> tk, tw, tq;
-        Tile<bf16_t, BC, 16> to;
+        Tile<bf16_t, BC, KD, NG> tk, tw, tq;
+        Tile<bf16_t, BC, 16, NG> to;
         float cf;
-    } opA, opB;
+    } opA, opB, opC;
     auto issue = [&](int ci, Ops16& o) __attribute__((always_inline)) {
         const long row0 = (long)b * T + bos + (long)ci * BC;
         const int L = min(BC, eos - (bos + ci * BC));
@@ -1346,55 +1349,56 @@ __global__ __launch_bounds__(NT) void gdn_bwd_dstate16_kernel(const bf16_t* __re
         o.tw.load(rec_w<bf16_t, KD>(R), KD, BC);
         o.tq.load(rec_qt<bf16_t, KD>(R), KD, BC);
         o.to.load(dout + (row0 * H + h) * (long)V + v0, (long)H * V, L);
-        o.cf = R[RL::C_OFF + tid];
+        o.cf = tid < 256 ? R[RL::C_OFF + tid] : 0.f;
     };
     auto step = [&](int ci, Ops16& o) __attribute__((always_inline)) {
-        float* Dout = dstates + (((size_t)(slot0 + ci) * H + h) * V + v0) * KD;
+        if (own) {
+            float* Dout = dstates + (((size_t)(slot0 + ci) * H + h) * V + v0) * KD;
 #pragma unroll
-        for (int i = 0; i < JPW; ++i) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Dout[(4 * lg + r) * KD + 16 * (JPW * w + i) + ln] = dS[i][r];
-            put_rows(sD, KP, 0, 16 * (JPW * w + i), dS[i]);
+            for (int r = 0; r < 4; ++r) Dout[(4 * lg + r) * KD + 16 * jc + ln] = dS[r];
+            put_rows(sD, KP, 0, 16 * jc, dS);
         }
         o.tk.template store_raw<KP>(sK);
         o.tw.template store_raw<KP>(sW);
         o.tq.template store_raw<KP>(sQt);
         o.to.template store_raw<VP>(sO);
-        sC[tid] = o.cf;
+        if (tid < 256) sC[tid] = o.cf;
         __syncthreads();
-        if (ci >= 2) issue(ci - 2, o);
-        // Z[v][t] = e_t (dS' K^T)[v][t] on token tile w (row form), kept by token rows for the column form
-        f32x4 Zt = mmb(sD, KP, sK + 16 * w * KP, KP, 0, KD, zero4());
-        Zt = Zt * sC[128 + 16 * w + ln];
-        put_cols(sZt, VP, 0, 16 * w, Zt);
+        if (ci >= 3) issue(ci - 3, o);
+        // Z[v][t] = e_t (dS' K^T)[v][t] on token tile w (row form), kept by token rows for the column form; with
+        // it, Gamma_L dS' + dO^T Qt on the wavefront's key tile (column form: it does not wait for Z)
+        if (hv == 0) {
+            f32x4 Zt = mmb(sD, KP, sK + 16 * w * KP, KP, 0, KD, zero4());
+            Zt = Zt * sC[128 + 16 * w + ln];
+            put_cols(sZt, VP, 0, 16 * w, Zt);
+        }
+        f32x4 a = zero4();
+        if (own) {
+            a = dS * sC[64 + BC - 1];
+#pragma unroll
+            for (int k0 = 0; k0 < BC; k0 += 32) a = mma32(col8(sO, VP, k0, 0), col8(sQt, KP, k0, 16 * jc), a);
+        }
         __syncthreads();
-        // dS = Gamma_L dS' + dO^T Qt - Z W on the wavefront's key tiles (column form)
-        const float gl = sC[64 + BC - 1];
+        // dS = Gamma_L dS' + dO^T Qt - Z W (column form)
+        if (own) {
+            f32x4 zw = zero4();
 #pragma unroll
-        for (int i = 0; i < JPW; ++i) {
-            const int jc = JPW * w + i;
-            f32x4 a = dS[i] * gl, zw = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < BC; k0 += 32) {
-                a = mma32(col8(sO, VP, k0, 0), col8(sQt, KP, k0, 16 * jc), a);
-                zw = mma32(col8(sZt, VP, k0, 0), col8(sW, KP, k0, 16 * jc), zw);
-            }
-            dS[i] = a - zw;
+            for (int k0 = 0; k0 < BC; k0 += 32) zw = mma32(col8(sZt, VP, k0, 0), col8(sW, KP, k0, 16 * jc), zw);
+            dS = a - zw;
         }
         __syncthreads();
     };
     if (nch > 0) issue(nch - 1, opA);
     if (nch > 1) issue(nch - 2, opB);
-    for (int ci = nch - 1; ci >= 0; ci -= 2) {
+    if (nch > 2) issue(nch - 3, opC);
+    for (int ci = nch - 1; ci >= 0; ci -= 3) {
         step(ci, opA);
         if (ci >= 1) step(ci - 1, opB);
+        if (ci >= 2) step(ci - 2, opC);
     }
-    if (dh0) {
+    if (own && dh0) {
 #pragma unroll
-        for (int i = 0; i < JPW; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dh0[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * (JPW * w + i) + ln] = dS[i][r];
+        for (int r = 0; r < 4; ++r) dh0[(((size_t)n * H + h) * V + v0 + 4 * lg + r) * KD + 16 * jc + ln] = dS[r];
     }
 }
 
@@ -1434,7 +1438,7 @@ hipError_t run_bwd(const ST* q, const ST* k, const ST* v, const float* g, const 
         if ((err = hipGetLastError()) != hipSuccess) return err;
         timing_begin("gdn_bwd_dstate", s);
         if constexpr (sizeof(ST) == 2)
-            gdn_bwd_dstate16_kernel<KD><<<grid, NT, 0, s>>>(k, dout, dht, cu, ws.chunk_off, ws.rec, T, H, V, N, nc, nvs,
+            gdn_bwd_dstate16_kernel<KD><<<grid, 2 * NT, 0, s>>>(k, dout, dht, cu, ws.chunk_off, ws.rec, T, H, V, N, nc, nvs,
                                                             ws.dstates, dh0);
         else
             gdn_bwd_dstate_kernel<ST, KD><<<grid, NT, 0, s>>>(k, dout, dht, cu, ws.chunk_off, ws.rec, T, H, V, N, nc, nvs,
