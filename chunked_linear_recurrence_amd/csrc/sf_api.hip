@@ -246,6 +246,10 @@ sf_status sf_gdn_chunk_bwd(sf_dtype dt, const void* q, const void* k, const void
     if ((K != 64 && K != 128) || (V != 64 && V != 128))
         return fail(SF_ERR_UNSUPPORTED, "the chunk backward is built for K, V in {64, 128} (K=%d V=%d)", K, V);
     if (H > 65535) return fail(SF_ERR_UNSUPPORTED, "H=%d is past the 65535 heads of a launch", H);
+    for (const void* p : {q, k, v, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                          static_cast<const void*>(dv)})
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+            return fail(SF_ERR_INVALID, "q, k, v, dout, dq, dk and dv must be 16-byte aligned (read and written in 16-byte pieces)");
     const sf::GdnBwdWorkspace need = sf::gdn_bwd_workspace_layout(nullptr, B, T, H, K, V, N, packed);
     if (!workspace || workspace_bytes < need.bytes)
         return fail(SF_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,

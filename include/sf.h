@@ -159,6 +159,7 @@ size_t sf_gdn_chunk_bwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V
  *   dout   [B, T, H, V] dt, the gradient of the output
  *   dht    [N, H, V, K] float32, the gradient of the final states, or NULL (zero)
  *   dq, dk [B, T, HK, K] dt;  dv [B, T, H, V] dt;  dg, dbeta [B, T, H] float32;
+ *          q, k, v, dout, dq, dk and dv 16-byte aligned (SF_ERR_INVALID otherwise);
  *   dh0    [N, H, V, K] float32 or NULL (not written)
  *          Entries of tokens at or past cu_seqlens[N] are not written.
  *   workspace  at least sf_gdn_chunk_bwd_workspace(...) bytes, 256-byte aligned

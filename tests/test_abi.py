@@ -326,6 +326,8 @@ def bwd_call(L, **kw):
     (dict(V=32), sf.SF_ERR_UNSUPPORTED, "{64, 128}"),
     (dict(wsb=16), sf.SF_ERR_WORKSPACE, "smaller"),
     (dict(ws=FAKE * 256 + 8), sf.SF_ERR_INVALID, "aligned"),
+    (dict(dq=FAKE + 2), sf.SF_ERR_INVALID, "16-byte aligned"),
+    (dict(v=FAKE + 8), sf.SF_ERR_INVALID, "16-byte aligned"),
     (dict(N=3), sf.SF_ERR_INVALID, "N (3) must equal B"),
 ])
 def test_bwd_rejects_invalid_arguments(L, kw, status, msg):
