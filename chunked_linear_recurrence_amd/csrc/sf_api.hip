@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -38,6 +39,14 @@ bool fits(long a) { return a >= 0 && a <= kMaxElems; }
 int elem_bytes(sf_dtype dt) { return dt == SF_BF16 ? 2 : 4; }
 
 // Common shape checks for token-major inputs.
+// The chunk kernels move q, k, v and the output rows in 16-byte pieces.
+sf_status check_rows16(std::initializer_list<const void*> ps, const char* names) {
+    for (const void* p : ps)
+        if (p && reinterpret_cast<uintptr_t>(p) % 16 != 0)
+            return fail(SF_ERR_INVALID, "%s must be 16-byte aligned (moved in 16-byte pieces)", names);
+    return SF_OK;
+}
+
 sf_status check_tokens(sf_dtype dt, int B, int T, int H, int HK, int K, int V, int N,
                        bool packed) {
     if (dt != SF_F32 && dt != SF_BF16) return fail(SF_ERR_INVALID, "dtype must be SF_F32 or SF_BF16");
@@ -177,6 +186,7 @@ sf_status sf_gdn_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void
     const bool packed = cu_seqlens != nullptr;
     sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
     if (st != SF_OK) return st;
+    if ((st = check_rows16({q, k, v, out}, "q, k, v and out")) != SF_OK) return st;
     if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
     if (K != V || (K != 64 && K != 128))
         return fail(SF_ERR_UNSUPPORTED, "delta-rule kernels are built for K == V in {64, 128} (K=%d V=%d)", K, V);
@@ -207,6 +217,7 @@ sf_status sf_kda_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void
     const bool packed = cu_seqlens != nullptr;
     sf_status st = check_tokens(dt, B, T, H, H, K, V, N, packed);
     if (st != SF_OK) return st;
+    if ((st = check_rows16({q, k, v, out}, "q, k, v and out")) != SF_OK) return st;
     if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
     if (!((K == 128 && (V == 128 || V == 64)) || (K == 64 && V == 64)))
         return fail(SF_ERR_UNSUPPORTED, "the KDA chunk forward is built for (K, V) in {(128, 128), (128, 64), (64, 64)} "
@@ -302,6 +313,7 @@ sf_status sf_gdn_chunk_fwd_noalloc(sf_dtype dt, const void* q, const void* k, co
     const bool packed = cu_seqlens != nullptr;
     sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
     if (st != SF_OK) return st;
+    if ((st = check_rows16({q, k, v, out}, "q, k, v and out")) != SF_OK) return st;
     if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
     if (K != V || (K != 64 && K != 128))
         return fail(SF_ERR_UNSUPPORTED, "delta-rule kernels are built for K == V in {64, 128} (K=%d V=%d)", K, V);
@@ -326,6 +338,7 @@ sf_status sf_gdn_chunk_fwd_raw_gate(sf_dtype dt, const void* q, const void* k, c
     const bool packed = cu_seqlens != nullptr;
     sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
     if (st != SF_OK) return st;
+    if ((st = check_rows16({q, k, v, out}, "q, k, v and out")) != SF_OK) return st;
     if (!q || !k || !v || !raw_gate || !A_log || !dt_bias || !beta || !out)
         return fail(SF_ERR_INVALID, "q, k, v, raw_gate, A_log, dt_bias, beta and out must not be NULL");
     if (kind != SF_GATE_SOFTPLUS && kind != SF_GATE_BOUNDED)
@@ -352,6 +365,7 @@ sf_status sf_gla_chunk_fwd(sf_dtype dt, const void* q, const void* k, const void
     const bool packed = cu_seqlens != nullptr;
     sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
     if (st != SF_OK) return st;
+    if ((st = check_rows16({q, k, v, out}, "q, k, v and out")) != SF_OK) return st;
     if (!q || !k || !v || !g || !out) return fail(SF_ERR_INVALID, "q, k, v, g and out must not be NULL");
     if (chunk != 64 && chunk != 128) return fail(SF_ERR_UNSUPPORTED, "chunk must be 64 or 128 (got %d)", chunk);
     if (dt == SF_F32 && chunk != 64) return fail(SF_ERR_UNSUPPORTED, "float32 inputs use chunk 64");
@@ -377,6 +391,7 @@ sf_status sf_segment_summary(sf_kind kind, sf_dtype dt, const void* k, const voi
                              float* M, float* S_ext, void* workspace, size_t workspace_bytes, void* stream) {
     sf_status st = check_tokens(dt, n_rows, L_seg, H, HK, K, V, n_rows, false);
     if (st != SF_OK) return st;
+    if ((st = check_rows16({k, v}, "k and v")) != SF_OK) return st;
     if (!k || !v || !g || !M || !S_ext) return fail(SF_ERR_INVALID, "k, v, g, M and S_ext must not be NULL");
     if (!fits((long)n_rows * H * K * K)) return fail(SF_ERR_UNSUPPORTED, "M has 2^31 or more elements");
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -449,6 +464,7 @@ sf_status sf_gdn_segmented_fwd(sf_dtype dt, const void* q, const void* k, const 
         return fail(SF_ERR_INVALID, "the segment length %d must be a multiple of the chunk (%d)", L_seg, sf::kGdnChunk);
     sf_status st = check_tokens(dt, n_rows, L_seg, H, HK, K, V, n_rows, false);
     if (st != SF_OK) return st;
+    if ((st = check_rows16({q, k, v, out}, "q, k, v and out")) != SF_OK) return st;
     if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
     if (K != V || (K != 64 && K != 128))
         return fail(SF_ERR_UNSUPPORTED, "delta-rule kernels are built for K == V in {64, 128} (K=%d V=%d)", K, V);
@@ -529,6 +545,7 @@ sf_status sf_paged_gdn_chunk_fwd(sf_dtype dt, const void* q, const void* k, cons
     const bool packed = cu_seqlens != nullptr;
     sf_status st = check_tokens(dt, B, T, H, HK, K, V, N, packed);
     if (st != SF_OK) return st;
+    if ((st = check_rows16({q, k, v, out}, "q, k, v and out")) != SF_OK) return st;
     if (!q || !k || !v || !g || !beta || !out) return fail(SF_ERR_INVALID, "q, k, v, g, beta and out must not be NULL");
     if (K != V || (K != 64 && K != 128))
         return fail(SF_ERR_UNSUPPORTED, "delta-rule kernels are built for K == V in {64, 128} (K=%d V=%d)", K, V);

@@ -101,6 +101,8 @@ size_t sf_gdn_chunk_fwd_workspace(sf_dtype dt, int B, int T, int H, int K, int V
  *   cu_seqlens  int32 [N + 1] or NULL; without it N must equal B
  *   scale  query scale (the usual choice is 1 / sqrt(K), chosen by the caller)
  *   out    [B, T, H, V] dt           ht [N, H, V, K] float32 final states, or NULL
+ *   q, k, v and out 16-byte aligned (SF_ERR_INVALID otherwise; the kernels move
+ *          their rows in 16-byte pieces), as for every chunk-form entry point here
  *   workspace  at least sf_gdn_chunk_fwd_workspace(...) bytes, 256-byte aligned
  * Supported: K == V, K in {64, 128}.
  */

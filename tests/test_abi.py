@@ -117,6 +117,8 @@ def gdn_call(L, **kw):
     (dict(ws=FAKE * 256 + 8), sf.SF_ERR_INVALID, "aligned"),
     (dict(T=1 << 20, H=128, HK=128, B=2, N=2), sf.SF_ERR_UNSUPPORTED, "2^31"),
     (dict(H=-1), sf.SF_ERR_INVALID, "positive"),
+    (dict(q=FAKE + 2), sf.SF_ERR_INVALID, "16-byte aligned"),
+    (dict(out=FAKE + 8), sf.SF_ERR_INVALID, "16-byte aligned"),
 ])
 def test_gdn_rejects_invalid_arguments(L, kw, status, msg):
     st, err = gdn_call(L, **kw)
@@ -362,6 +364,7 @@ def kda_call(L, **kw):
     (dict(wsb=16), sf.SF_ERR_WORKSPACE, "smaller"),
     (dict(ws=FAKE * 256 + 8), sf.SF_ERR_INVALID, "aligned"),
     (dict(cu=FAKE, B=2, N=2), sf.SF_ERR_INVALID, "batch-one"),
+    (dict(k=FAKE + 4), sf.SF_ERR_INVALID, "16-byte aligned"),
 ])
 def test_kda_chunk_rejects_invalid_arguments(L, kw, status, msg):
     st, err = kda_call(L, **kw)
