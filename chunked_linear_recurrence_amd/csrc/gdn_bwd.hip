@@ -232,12 +232,13 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep_kernel(const ST* __restrict__
 // scale Gamma Q of the lane's own Q~ entries kept in registers from the start. The same steps as
 // gdn_bwd_prep_kernel.
 template <int KD>
-__global__ __launch_bounds__(NT) void gdn_bwd_prep16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+__global__ __launch_bounds__(2 * NT) void gdn_bwd_prep16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                             const float* __restrict__ g, const float* __restrict__ beta,
                                                             const int2* __restrict__ table, const int32_t* __restrict__ cu,
                                                             int T, int H, int nc, float scale, float* __restrict__ rec) {
     typedef BwdRec<KD> RL;
     typedef Elem<bf16_t> El;
+    constexpr int NG = 2 * NT;  // eight wavefronts: (token tile w, half hv)
     constexpr int KP = KD + 8, CP = BC + 8, LL = BC + 1, LU = 17, NJ = KD / 16;
     constexpr int OFF_K = 0, OFF_QW = OFF_K + BC * KP * 2, OFF_A = OFF_QW + BC * KP * 2, OFF_T = OFF_A + BC * LL * 4,
                   OFF_P = OFF_T + BC * LL * 4, OFF_S = OFF_P + BC * CP * 2, BYTES = OFF_S + 3 * BC * 4;
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep16_kernel(const bf16_t* __rest
     if (!chunk_coords(slot, table, cu, T, nc, b, t0, L)) return;
     const long row0 = (long)b * T + t0;
     {
-        Tile<bf16_t, BC, KD> tk, tq;
+        Tile<bf16_t, BC, KD, NG> tk, tq;
         tk.load(k + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tq.load(q + (row0 * H + h) * (long)KD, (long)H * KD, L);
         tk.template store_raw<KP>(sK);
@@ -273,18 +274,22 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep16_kernel(const bf16_t* __rest
         sGam[tid] = expf(G);
     }
     __syncthreads();
-    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    // wavefront wi: token tile w; half hv takes the column tiles j = 2 hv, 2 hv + 1 of A and P and the key tiles
+    // HJ hv .. HJ hv + HJ - 1 of W and Qt
+    const int wi = tid >> 6, w = wi & 3, hv = wi >> 2, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    constexpr int HJ = NJ / 2;
     int tr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) tr[r] = 16 * w + 4 * lg + r;
     // scale Gamma Q at the lane's Q~ entries (rows tr[r], columns 16 jc + ln)
-    float qg[NJ][4];
+    float qg[HJ][4];
 #pragma unroll
-    for (int jc = 0; jc < NJ; ++jc)
+    for (int jj = 0; jj < HJ; ++jj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) qg[jc][r] = scale * sGam[tr[r]] * bf2f(sQ[tr[r] * KP + 16 * jc + ln]);
+        for (int r = 0; r < 4; ++r) qg[jj][r] = scale * sGam[tr[r]] * bf2f(sQ[tr[r] * KP + 16 * (HJ * hv + jj) + ln]);
     // A = diag(beta) (D_strict o K K^T) and P = scale (D o Q K^T) on the wavefront's row tile
-    for (int j = 0; j < 4; ++j) {
+    for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * hv + jj;
         f32x4 kk = zero4(), qk = zero4();
         if (j <= w) {
             kk = mmb(sK + 16 * w * KP, KP, sK + 16 * j * KP, KP, 0, KD, kk);
@@ -300,8 +305,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep16_kernel(const bf16_t* __rest
         }
     }
     __syncthreads();
-    // diagonal blocks: wavefront w inverts block w, lane j < 16 solving column j in registers
-    if (lane < 16) {
+    // diagonal blocks: wavefront w of half 0 inverts block w, lane j < 16 solving column j in registers
+    if (hv == 0 && lane < 16) {
         const int o = 16 * w, j = lane;
         float xs[16];
 #pragma unroll
@@ -315,15 +320,15 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep16_kernel(const bf16_t* __rest
         for (int i = 0; i < 16; ++i) sT[(o + i) * LL + o + j] = xs[i];
     }
     // (K scaled by beta Gamma per token, for W: K is not read again as itself)
-    for (int i = tid; i < BC * KD; i += NT) {
+    for (int i = tid; i < BC * KD; i += NG) {
         const int t = i / KD, c = i % KD;
         sK[t * KP + c] = f2bf(bf2f(sK[t * KP + c]) * (sB[t] * sGam[t]));
     }
     __syncthreads();
-    // off-diagonal blocks, one block diagonal dd at a time: block (i, j = i - dd) by wavefront i
+    // off-diagonal blocks, one block diagonal dd at a time: block (i, j = i - dd) by wavefront i of half 0
     for (int dd = 1; dd < 4; ++dd) {
         const int i = w, j = w - dd;
-        if (j >= 0) {
+        if (hv == 0 && j >= 0) {
             const f32x4 Uv = mm4(sA + 16 * i * LL + 16 * j, LL, 1, sT + 16 * j * LL + 16 * j, LL, 1, 0, 16 * (i - j), zero4());
             float* Ub = sU + w * 16 * LU;
 #pragma unroll
@@ -340,7 +345,8 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep16_kernel(const bf16_t* __rest
     bf16_t* const RQ = rec_qt<bf16_t, KD>(R);
     // W = T (beta Gamma K) on the wavefront's row tile (T is zero past column 16 w + 15)
 #pragma unroll
-    for (int jc = 0; jc < NJ; ++jc) {
+    for (int jj = 0; jj < HJ; ++jj) {
+        const int jc = HJ * hv + jj;
         const f32x4 Wv = mmg(sT + 16 * w * LL, LL, 1, sK + 16 * jc, KP, 1, 0, 16 * (w + 1), zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -351,12 +357,13 @@ __global__ __launch_bounds__(NT) void gdn_bwd_prep16_kernel(const bf16_t* __rest
     __syncthreads();
     // Qt = scale Gamma Q - P W
 #pragma unroll
-    for (int jc = 0; jc < NJ; ++jc) {
+    for (int jj = 0; jj < HJ; ++jj) {
+        const int jc = HJ * hv + jj;
         const f32x4 PW = mmg(sP + 16 * w * CP, CP, 1, sW + 16 * jc, KP, 1, 0, 16 * (w + 1), zero4());
 #pragma unroll
-        for (int r = 0; r < 4; ++r) RQ[tr[r] * KD + 16 * jc + ln] = f2bf(qg[jc][r] - PW[r]);
+        for (int r = 0; r < 4; ++r) RQ[tr[r] * KD + 16 * jc + ln] = f2bf(qg[jj][r] - PW[r]);
     }
-    for (int i = tid; i < BC * BC; i += NT) {
+    for (int i = tid; i < BC * BC; i += NG) {
         rec_t<bf16_t, KD>(R)[i] = f2bf(sT[(i / BC) * LL + i % BC]);
         rec_t<bf16_t, KD>(R)[BC * BC + i] = f2bf(sT[(i % BC) * LL + i / BC]);  // T^T (read by columns)
     }
@@ -1419,7 +1426,7 @@ hipError_t run_bwd(const ST* q, const ST* k, const ST* v, const float* g, const 
     if (slots > 0) {
         timing_begin("gdn_bwd_prep", s);
         if constexpr (sizeof(ST) == 2)
-            gdn_bwd_prep16_kernel<KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, g, beta, table, cu, T, H, nc, scale, ws.rec);
+            gdn_bwd_prep16_kernel<KD><<<dim3((unsigned)slots, H), 2 * NT, 0, s>>>(q, k, g, beta, table, cu, T, H, nc, scale, ws.rec);
         else
             gdn_bwd_prep_kernel<ST, KD><<<dim3((unsigned)slots, H), NT, 0, s>>>(q, k, g, beta, table, cu, T, H, nc, scale, ws.rec);
         timing_end(s);
