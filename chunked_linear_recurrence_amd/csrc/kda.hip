@@ -496,7 +496,7 @@ __global__ __launch_bounds__(NT) void kda_chain_kernel(const float* __restrict__
 // by token rows, S_b and R^T by value rows, Kh^T by key rows).
 // ---------------------------------------------------------------------------------------------------------
 template <int KD, int VD>
-__global__ __launch_bounds__(NT) void kda_chain16_kernel(const float* __restrict__ h0, const int32_t* __restrict__ cu,
+__global__ __launch_bounds__(NTP) void kda_chain16_kernel(const float* __restrict__ h0, const int32_t* __restrict__ cu,
                                                          const int* __restrict__ chunk_off, const float* __restrict__ rec,
                                                          int T, int H, int n_seq, int nc, int nvs, bf16_t* __restrict__ out,
                                                          float* __restrict__ ht) {
@@ -514,7 +514,11 @@ __global__ __launch_bounds__(NT) void kda_chain16_kernel(const float* __restrict
     xcd_split(blockIdx.x, nvs, chain, vs);
     if (chain >= n_seq * H) return;
     const int n = chain / H, h = chain % H, tid = threadIdx.x, v0 = 16 * vs;
-    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    // wavefront wi: token tile w, half hv (half 0 forms R, half 1 Qg S^T and the output of the tile); key tile
+    // JPW w + hv of the state (for K = 64 the wavefronts of half 1 hold none)
+    const int wi = tid >> 6, w = wi & 3, hv = wi >> 2, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const bool own = hv < JPW;
+    const int jc = JPW * w + hv;
     int b, bos, eos, slot0;
     if (cu) {
         b = 0;
@@ -528,22 +532,18 @@ __global__ __launch_bounds__(NT) void kda_chain16_kernel(const float* __restrict
         slot0 = n * nc;
     }
     const int nch = (eos - bos + BC - 1) / BC;
-    f32x4 S[JPW];
+    f32x4 S = zero4();
+    if (own && h0)
 #pragma unroll
-    for (int i = 0; i < JPW; ++i) {
-        const int c = 16 * (JPW * w + i) + ln;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[i][r] = h0 ? h0[(((size_t)n * H + h) * VD + v0 + 4 * lg + r) * KD + c] : 0.f;
-    }
+        for (int r = 0; r < 4; ++r) S[r] = h0[(((size_t)n * H + h) * VD + v0 + 4 * lg + r) * KD + 16 * jc + ln];
     // a chunk's record tiles in registers (two sets: a chunk's loads are issued two steps before its step, in
     // three groups spread over the step, and the loop takes two steps per pass so that each set has fixed
     // registers)
     struct Ops16 {
-        Tile<bf16_t, BC, KD> tw, tq;
-        Tile<bf16_t, KD, BC> tk;
-        Tile<bf16_t, BC, BC> tp;
-        Tile<float, BC, 16> tu;
+        Tile<bf16_t, BC, KD, NTP> tw, tq;
+        Tile<bf16_t, KD, BC, NTP> tk;
+        Tile<bf16_t, BC, BC, NTP> tp;
+        Tile<float, BC, 16, NTP> tu;
         float gl;
     } opA, opB;
     auto recb = [&](int ci) __attribute__((always_inline)) {
@@ -567,10 +567,9 @@ __global__ __launch_bounds__(NT) void kda_chain16_kernel(const float* __restrict
     auto step = [&](int ci, Ops16& o) __attribute__((always_inline)) {
         const long row0 = (long)b * T + bos + (long)ci * BC;
         const int L = min(BC, eos - (bos + ci * BC));
+        if (own)
 #pragma unroll
-        for (int i = 0; i < JPW; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sSb[(4 * lg + r) * LW + 16 * (JPW * w + i) + ln] = f2bf(S[i][r]);
+            for (int r = 0; r < 4; ++r) sSb[(4 * lg + r) * LW + 16 * jc + ln] = f2bf(S[r]);
         o.tw.template store_raw<LW>(sW);
         o.tq.template store_raw<LW>(sQg);
         o.tk.template store_raw<LT>(sKt);
@@ -580,25 +579,27 @@ __global__ __launch_bounds__(NT) void kda_chain16_kernel(const float* __restrict
         __syncthreads();
         const bool more = ci + 2 < nch;
         if (more) issue_w(ci + 2, o);
-        // token tile w: R = U - W S^T and QS = Qg S^T
-        const f32x4 WS = f32t::mmb(sW + 16 * w * LW, LW, sSb, LW, 0, KD, zero4());
+        // token tile w: R = U - W S^T (half 0) and QS = Qg S^T (half 1)
         if (more) issue_q(ci + 2, o);
-        const f32x4 QS = f32t::mmb(sQg + 16 * w * LW, LW, sSb, LW, 0, KD, zero4());
+        f32x4 QS = zero4();
+        if (hv == 0) {
+            const f32x4 WS = f32t::mmb(sW + 16 * w * LW, LW, sSb, LW, 0, KD, zero4());
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sRt[ln * LT + tr0 + r] = f2bf(sU[(tr0 + r) * LV + ln] - WS[r]);
+            for (int r = 0; r < 4; ++r) sRt[ln * LT + tr0 + r] = f2bf(sU[(tr0 + r) * LV + ln] - WS[r]);
+        } else {
+            QS = f32t::mmb(sQg + 16 * w * LW, LW, sSb, LW, 0, KD, zero4());
+        }
         __syncthreads();
         if (more) issue_k(ci + 2, o);
-        // O = QS + P R on token tile w (P is zero past column 16 w + 15)
-        const f32x4 ov = f32t::mmb(sP + 16 * w * LT, LT, sRt, LT, 0, 16 * (w + 1), QS);
+        // O = QS + P R on token tile w (P is zero past column 16 w + 15), by half 1
+        if (hv == 1) {
+            const f32x4 ov = f32t::mmb(sP + 16 * w * LT, LT, sRt, LT, 0, 16 * (w + 1), QS);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (tr0 + r < L) out[((row0 + tr0 + r) * H + h) * (long)VD + v0 + ln] = f2bf(ov[r]);
-        // S <- S diag(Gamma_L) + R^T Kh on the wavefront's key tiles: A(v, t) = R^T[v][t], B(t, c) = Kh^T[c][t]
-#pragma unroll
-        for (int i = 0; i < JPW; ++i) {
-            const int jc = JPW * w + i;
-            S[i] = f32t::mmb(sRt, LT, sKt + 16 * jc * LT, LT, 0, BC, S[i] * sGL[16 * jc + ln]);
+            for (int r = 0; r < 4; ++r)
+                if (tr0 + r < L) out[((row0 + tr0 + r) * H + h) * (long)VD + v0 + ln] = f2bf(ov[r]);
         }
+        // S <- S diag(Gamma_L) + R^T Kh on the wavefront's key tile: A(v, t) = R^T[v][t], B(t, c) = Kh^T[c][t]
+        if (own) S = f32t::mmb(sRt, LT, sKt + 16 * jc * LT, LT, 0, BC, S * sGL[16 * jc + ln]);
         __syncthreads();
     };
 #pragma unroll
@@ -613,14 +614,9 @@ __global__ __launch_bounds__(NT) void kda_chain16_kernel(const float* __restrict
         step(ci, opA);
         if (ci + 1 < nch) step(ci + 1, opB);
     }
-    if (ht) {
+    if (own && ht)
 #pragma unroll
-        for (int i = 0; i < JPW; ++i) {
-            const int c = 16 * (JPW * w + i) + ln;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ht[(((size_t)n * H + h) * VD + v0 + 4 * lg + r) * KD + c] = S[i][r];
-        }
-    }
+        for (int r = 0; r < 4; ++r) ht[(((size_t)n * H + h) * VD + v0 + 4 * lg + r) * KD + 16 * jc + ln] = S[r];
 }
 
 template <typename ST, int KD, int VD>
@@ -648,7 +644,7 @@ hipError_t run_kda(const ST* q, const ST* k, const ST* v, const float* g, const 
     const unsigned grid = (unsigned)(((chains + 7) / 8) * 8 * nvs);
     timing_begin("kda_chain", s);
     if constexpr (sizeof(ST) == 2)
-        kda_chain16_kernel<KD, VD><<<grid, NT, 0, s>>>(h0, cu, ws.chunk_off, ws.rec, T, H, N, nc, nvs, out, ht);
+        kda_chain16_kernel<KD, VD><<<grid, NTP, 0, s>>>(h0, cu, ws.chunk_off, ws.rec, T, H, N, nc, nvs, out, ht);
     else
         kda_chain_kernel<ST, KD, VD><<<grid, NT, 0, s>>>(h0, cu, ws.chunk_off, ws.rec, T, H, N, nc, nvs, out, ht);
     timing_end(s);
