@@ -20,6 +20,7 @@
 // Kernels (float32 accumulation and elementwise arithmetic; q, k, v, do and the gradients dq, dk, dv in the
 // input type; the products in the input type's arithmetic):
 //   gdn_bwd_prep_kernel    per (chunk, head): T, W, Qt and the coefficients into a record
+//                          (gdn_bwd_prep16_kernel for bf16 inputs)
 //   gdn_bwd_states_kernel  per (sequence, head, 16-row slice): the forward chain, storing every chunk's
 //                          entry state (gdn_bwd_states16_kernel for bf16 inputs)
 //   gdn_bwd_dstate_kernel  per (sequence, head, 16-row slice): the reverse chain, storing every chunk's
@@ -27,7 +28,8 @@
 //   gdn_bwd_grad_kernel    per (chunk, head): dq, dk, dv, dg, dbeta of the chunk (gdn_bwd_grad16_kernel for
 //                          bf16 inputs)
 // The float32-input kernels keep their operands in float32 in LDS; the bf16 ones keep bf16 operands and
-// read them in the row and column forms described at gdn_bwd_grad16_kernel.
+// read them in the row and column forms described at gdn_bwd_grad16_kernel. The bf16 prep, gradient and
+// state-gradient kernels run eight wavefronts, two per 16-token tile (or per key tile pair).
 #include <type_traits>
 
 #include "f32_tiles.h"
